@@ -1,0 +1,109 @@
+"""Pins for the 2D Lloyd-Max codebook trainer and the stored codebooks (CPU).
+
+Lloyd's algorithm must not increase the distortion, its fixed points satisfy
+the centroid condition and the energy identity E|x|^2 = E|Q(x)|^2 + D, the
+four-level quantiser of N(0, I_2) is the quadrant quantiser with centroids
+of radius sqrt(4/pi) and D = 2 - 4/pi, and at high rate the distortion
+approaches the Zador/Gersho value with the hexagonal cell,
+D ~ G_hex * 8 pi * 2 / K = 4.03 / K (G_hex = 5 / (36 sqrt 3)).
+"""
+import hashlib
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import lloyd
+import workloads
+
+CB_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "vector_codebook_codec_amd", "codebooks")
+
+
+def _load(K):
+    with open(os.path.join(CB_DIR, f"qamw_K{K}.json")) as f:
+        meta = json.load(f)
+    with open(os.path.join(CB_DIR, f"qamw_K{K}.f32"), "rb") as f:
+        raw = f.read()
+    return np.frombuffer(raw, dtype="<f4").reshape(K, 2), meta, raw
+
+
+def test_live_training_invariants():
+    X = workloads.gaussian_samples(1 << 14, 123)
+    K = 16
+    C49, h49 = lloyd.train(X, K, 49)
+    C50, h50 = lloyd.train(X, K, 50)
+    assert h50[:49] == h49[:49]
+    assert all(b <= a + 1e-15 for a, b in zip(h50, h50[1:]))      # non-increasing
+    # centroid condition: round 50 moves every centroid to its cell mean
+    idx, _ = lloyd.assign(X, C49)
+    mean, cnt = lloyd.cell_means(X, idx, K)
+    assert np.all(cnt > 0)
+    assert np.array_equal(C50, mean)
+    # energy identity: with every centroid at its cell mean the quantisation
+    # error is orthogonal to the reproduction, E|x|^2 = E|Q(x)|^2 + E|x - Q(x)|^2
+    q = C50[idx]
+    err = ((X - q) ** 2).sum(1)
+    assert abs(np.mean((X ** 2).sum(1)) - np.mean((q ** 2).sum(1)) - err.mean()) < 1e-12
+
+
+def test_empty_cell_keeps_centroid():
+    # two identical initial centroids: every tie goes to index 0, so cell 1 is
+    # empty after the first assignment and its centroid must not move
+    X = np.array([[0.0, 0.0], [0.0, 0.0], [1.0, 0.0], [0.0, 1.0]])
+    C, h = lloyd.train(X, 2, 1)
+    assert np.array_equal(C, [[0.25, 0.25], [0.0, 0.0]])
+    assert h[0] == 0.5
+
+
+@pytest.mark.parametrize("K", [2, 4, 16, 128, 256, 1024, 2048, 4096])
+def test_stored_codebook_files(K):
+    C, meta, raw = _load(K)
+    assert meta["K"] == K and meta["seed"] == 1 and meta["n_samples"] == 65536 and meta["iters"] == 50
+    assert hashlib.sha256(raw).hexdigest() == meta["sha256"]
+    h = meta["distortion_history"]
+    assert len(h) == 51
+    assert all(b <= a * (1 + 1e-12) for a, b in zip(h, h[1:]))
+    assert np.all(np.isfinite(C))
+    assert len(np.unique(C, axis=0)) == K
+
+
+def test_k4_quadrant_quantizer():
+    C, meta, _ = _load(4)
+    assert np.allclose(np.hypot(C[:, 0], C[:, 1]), math.sqrt(4 / math.pi), atol=0.02)
+    ang = np.sort(np.mod(np.arctan2(C[:, 1], C[:, 0]), 2 * math.pi))
+    gaps = np.diff(np.concatenate([ang, ang[:1] + 2 * math.pi]))
+    assert np.allclose(gaps, math.pi / 2, atol=0.03)
+    assert abs(meta["distortion_history"][-1] - (2 - 4 / math.pi)) < 0.01
+
+
+@pytest.mark.parametrize("K", [128, 256, 1024, 2048, 4096])
+def test_high_rate_distortion(K):
+    """Within [0.8, 1.6] of the high-rate value: 50 rounds from a
+    first-K-samples start leave large codebooks short of convergence (above),
+    and with 2^16 samples the training-set distortion is biased low."""
+    _, meta, _ = _load(K)
+    g_hex = 5 / (36 * math.sqrt(3))
+    zador = g_hex * 8 * math.pi * 2 / K
+    assert abs(zador * K - 4.03) < 0.01
+    assert 0.8 < meta["distortion_history"][-1] / zador < 1.6
+
+
+def test_stored_k256_near_fixed_point():
+    """Recompute the cells of the stored K=256 codebook on its own training
+    samples.  Fifty rounds leave K=256 still moving (the distortion falls
+    ~0.2% per round at the end), so the fixed-point conditions hold only
+    approximately: cell means within 0.05 of the centroids (cells are ~0.13
+    wide) and the energy-identity residual 2 E[(x - Q(x)) . Q(x)] below half of D."""
+    C, meta, _ = _load(256)
+    X = workloads.gaussian_samples(1 << 16, 1)
+    idx, dmin = lloyd.assign(X, C.astype(np.float64))
+    q = C.astype(np.float64)[idx]
+    gap = np.mean((X ** 2).sum(1)) - np.mean((q ** 2).sum(1)) - dmin.mean()
+    assert abs(gap) < 0.5 * dmin.mean()
+    assert abs(dmin.mean() - meta["distortion_history"][-1]) < 1e-6
+    mean, cnt = lloyd.cell_means(X, idx, 256)
+    assert np.all(cnt > 0)
+    assert np.max(np.abs(mean - C)) < 0.05
