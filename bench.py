@@ -1,0 +1,194 @@
+"""Throughput of the QAM-W codec on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = the whole codec path over one matrix already resident in HBM:
+qamw_calibrate (s, sigma) -> qamw_encode (row norms, nearest centroid, pack)
+-> qamw_decode (fp32 output).  The default workload is the 4096 x 11008 bf16
+down-projection-shaped matrix (Student-t(5) entries, std 0.02; K = 2048,
+Hadamard block 256).  Prints one JSON line.
+
+value         weights per second of the whole step (Gweights/s)
+roofline      the dominant kernel (encode): algorithmic fp32 flops
+              (pairs x K x 4 per launch) / its mean launch time, against the
+              MI355X fp32 vector peak (157.3 TFLOP/s)
+cpu_baseline  the fp64 NumPy oracle, single-threaded, on a 160-row sample of
+              the same workload (calibrate + encode + decode of those rows)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3t_4096x11008")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-decode-reps", type=int, default=10,
+                    help="decode-only reps timed after overwriting a 1 GiB buffer")
+    ap.add_argument("--copy-reference", type=int, default=0,
+                    help="also run N copies of a 1 GiB buffer (counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, C, rows=160):
+    """The oracle as it stands, one thread, on the first ``rows`` rows."""
+    from threadpoolctl import threadpool_limits
+    from oracle import qamw_ref as O
+
+    Wf = wl.W_f32()[:rows]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        s, sig, _ = O.calibrate(Wf, wl.r, wl.alpha, wl.block, wl.sign_seed)
+        enc = O.encode(Wf, s, sig, wl.block, wl.sign_seed, C)
+        O.decode(enc["packed"], enc["rho_hat_bits"], s, sig, wl.block, wl.sign_seed, C, wl.d)
+        dt = time.perf_counter() - t0
+    n = rows * wl.d
+    return {"value": n / dt / 1e9, "unit": "Gweights/s", "cores": 1, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of {wl.name} ({n} weights): calibrate over the sample, "
+                      f"encode, decode; fp64 NumPy, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the codec shards by rows or by matrix, but no multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import vector_codebook_codec_amd as q
+
+    dev = torch.device("cuda:0")
+    wl = workloads.get(args.workload)
+    C = q.load_codebook(wl.K)
+    N, d, K, b = wl.N, wl.d, wl.K, wl.block
+    if wl.wdtype == "bf16":
+        W = torch.from_numpy(wl.W.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        W = torch.from_numpy(wl.W).to(dev)
+    r = torch.from_numpy(wl.r).to(dev)
+    Ct = torch.from_numpy(C).to(dev)
+    s = torch.empty(d, dtype=torch.float32, device=dev)
+    sigma = torch.empty(d // 2, dtype=torch.float32, device=dev)
+    rw = q.qamw_packed_row_words(d, K)
+    packed = torch.empty((N, rw), dtype=torch.int32, device=dev)
+    rn = torch.empty(N, dtype=torch.int16, device=dev)
+    out = torch.empty((N, d), dtype=torch.float32, device=dev)
+    ws_cal = torch.empty(q.qamw_calibrate_workspace_bytes(N, d, b), dtype=torch.uint8, device=dev)
+    ws_enc = torch.empty(max(256, q.qamw_encode_workspace_bytes(N)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(marks=None):
+        if marks is not None:
+            marks[0].record(stream)
+        q.qamw_calibrate(W, r, wl.alpha, b, wl.sign_seed, s, sigma, ws_cal, stream)
+        if marks is not None:
+            marks[1].record(stream)
+        q.qamw_encode(W, s, sigma, b, wl.sign_seed, Ct, packed, rn, ws_enc, stream)
+        if marks is not None:
+            marks[2].record(stream)
+        q.qamw_decode(packed, rn, d, s, sigma, b, wl.sign_seed, Ct, out=out, stream=stream)
+        if marks is not None:
+            marks[3].record(stream)
+
+    for i in range(args.warmup):
+        step()
+        print(f"warmup step {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+
+    marks = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(marks[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    cal_ms = float(np.mean([m[0].elapsed_time(m[1]) for m in marks]))
+    enc_ms = float(np.mean([m[1].elapsed_time(m[2]) for m in marks]))
+    dec_ms = float(np.mean([m[2].elapsed_time(m[3]) for m in marks]))
+    step_ms = wall * 1e3 / args.steps
+
+    # decode alone, with HBM caches (L2, MALL) flushed by a 1 GiB write before each rep
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(args.cold_decode_reps):
+        flush.fill_(1.0)
+        a, z = ev(), ev()
+        a.record(stream)
+        q.qamw_decode(packed, rn, d, s, sigma, b, wl.sign_seed, Ct, out=out, stream=stream)
+        z.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(z))
+    dec_cold_ms = float(np.median(cold)) if cold else None
+
+    for _ in range(args.copy_reference):
+        flush2 = torch.empty_like(flush)
+        flush2.copy_(flush)
+        torch.cuda.synchronize()
+
+    B = q.qamw_index_bits(K)
+    P = N * d // 2
+    enc_flops = P * K * 4.0
+    achieved_tflops = enc_flops / (enc_ms * 1e-3) / 1e12
+    dec_bytes = N * d * 4 + N * rw * 4 + N * 2            # fp32 out + packed + row norms
+    weights = N * d
+    res = {
+        "metric": "QAM-W encode & decode Gweights/s at 4096x11008; % VALU peak / % HBM BW",
+        "value": weights / (step_ms * 1e-3) / 1e9,
+        "unit": "Gweights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {N}x{d} {wl.wdtype} Student-t(5) std 0.02, "
+                               f"r~LogNormal(0,1.2), alpha={wl.alpha}, block={b}, K={K}, fp32 decode",
+                   "N": N, "d": d, "K": K, "block": b, "bits_per_index": B, "in_dtype": wl.wdtype,
+                   "out_dtype": "f32"},
+        "roofline": {"bound": "alu", "kernel": "encode_kernel (qamw_encode; includes its row-norm pre-pass)",
+                     "achieved": achieved_tflops, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tflops / PEAK_FP32_TFLOPS, "traffic": None,
+                     "algorithmic": f"{P} pairs x {K} centroids x 4 flops = {enc_flops:.4g} per launch"},
+        "per_entry_ms": {"calibrate": cal_ms, "encode": enc_ms, "decode": dec_ms},
+        "encode_gweights_s": weights / ((cal_ms + enc_ms) * 1e-3) / 1e9,
+        "decode_gweights_s": weights / (dec_ms * 1e-3) / 1e9,
+        "decode_cold": None if dec_cold_ms is None else {
+            "ms": dec_cold_ms, "algorithmic_bytes": dec_bytes,
+            "GB_s": dec_bytes / (dec_cold_ms * 1e-3) / 1e9,
+            "frac_hbm": dec_bytes / (dec_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "achieved_bpw": B / 2 + 16.0 / d,
+    }
+    if not args.no_cpu_baseline:
+        print("timing the CPU oracle on a 160-row sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, C)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * qamw.h -- C ABI of the QAM-W weight codec on AMD Instinct MI355X (gfx950).
+ *
+ * QAM-W ("QAM-W: Joint 2D Codebook Quantization for LLM Weights via Hadamard
+ * Rotation and Activation-Aware Scaling"; cited below as "QAM-W, <section>")
+ * codes an LLM weight matrix row by row (QAM-W, Methodology: The QAM-W Codec):
+ *
+ *   s_j      = r_j ^ alpha                       activation-aware channel scale
+ *   W'       = W diag(s)
+ *   rho_n    = ||W'_n||_2,  u_n = W'_n / rho_n   scale / direction split
+ *   y_n      = R_fwd u_n,   R_fwd = (I (x) H_b / sqrt(b)) diag(eps)
+ *   z_{n,k}  = (y_{n,2k}, y_{n,2k+1})            pairing
+ *   sigma_k  = mean_n |z_{n,k}| / sqrt(pi/2)     per-pair calibration
+ *   idx_{n,k}= nearest centroid of z_{n,k}/sigma_k in a 2D Lloyd-Max codebook
+ *   packed   = idx at B = ceil(log2 K) bits each, LSB-first per row
+ *   decode   : unpack -> C[idx] * sigma_k -> R_fwd^T -> * rho_hat_n -> / s_j
+ *
+ * Conventions shared by every entry point
+ *   - W is row-major [N][ldw]: a row is an output channel, column j is input
+ *     channel j (s_j scales columns).  ldw >= d, in elements.
+ *   - H_b is the Sylvester-order Hadamard matrix H[i][k] = (-1)^popcount(i&k)
+ *     applied to each contiguous block [beta*b, beta*b + b) of a row.
+ *   - eps_j = -1 exactly when bit 63 of the j-th output (0-based) of
+ *     SplitMix64 seeded with sign_seed is set; one mask per matrix.
+ *   - The codebook is K x 2 float32, interleaved (cx, cy).
+ *   - Packed indices: row-major [N][qamw_packed_row_words(d, K)] uint32;
+ *     bit t of a row's stream is bit (t mod 32) of word t/32; index k holds
+ *     bits [k*B, k*B + B); unused bits are 0; rows start on 16-byte boundaries.
+ *   - Row norms are stored as IEEE binary16 bits, round-to-nearest-even of the
+ *     exact norm.
+ *   - Ties between equally distant centroids (equal fp32 scores) go to the
+ *     lowest index.
+ *
+ * Memory and streams
+ *   - Every array argument is a DEVICE pointer unless stated otherwise; the
+ *     caller allocates and owns all of them, including workspaces.  The
+ *     library never allocates, frees or synchronises, and keeps no global
+ *     mutable state: calls on different streams are independent.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every compute
+ *     call only enqueues kernels on it and returns; results are valid once
+ *     the stream has reached that point.  In-place calls are not supported
+ *     (outputs must not alias inputs).
+ *   - W, W_out and packed must be 16-byte aligned, and ldw / ldo rows must keep
+ *     16-byte alignment (ldw * element size % 16 == 0).
+ *
+ * Errors
+ *   Arguments are validated on the host before anything is launched; on a
+ *   failure nothing is enqueued or written and the status is returned.  A
+ *   failed kernel launch returns QAMW_EHIP.  qamw_last_error() gives a
+ *   message for the calling thread's last failure.  Device-side contracts the
+ *   host cannot check (r_j > 0, finite inputs) are the caller's: violating
+ *   them gives unspecified values but no out-of-bounds access.
+ */
+#ifndef QAMW_H
+#define QAMW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QAMW_OK = 0,
+  QAMW_EINVAL = -1,        /* bad argument (null pointer, size, stride, alignment) */
+  QAMW_EUNSUPPORTED = -2,  /* valid but unsupported (block, K, d, dtype) */
+  QAMW_EHIP = -3,          /* HIP runtime error on launch */
+  QAMW_EWORKSPACE = -4     /* workspace missing or too small */
+} qamw_status;
+
+typedef enum { QAMW_F32 = 0, QAMW_BF16 = 1, QAMW_F16 = 2 } qamw_dtype;
+
+/* ---------------- host-only helpers (pure, no device access) ---------------- */
+
+/* B = ceil(log2 K) for 2 <= K <= 4096; -1 otherwise. */
+int32_t qamw_index_bits(int32_t K);
+
+/* uint32 words per packed row: ceil((d/2) * B / 32) rounded up to a multiple
+ * of 4; -1 for invalid d or K. */
+int64_t qamw_packed_row_words(int64_t d, int32_t K);
+
+/* Bytes of device workspace qamw_calibrate needs for an N x d matrix
+ * (row norms in fp64 and per-row-tile partial sums of pair amplitudes). */
+size_t qamw_calibrate_workspace_bytes(int64_t N, int64_t d, int32_t block);
+
+/* Bytes of device workspace qamw_encode needs (fp64 row norms). */
+size_t qamw_encode_workspace_bytes(int64_t N);
+
+const char* qamw_status_string(int32_t status);
+const char* qamw_last_error(void);
+const char* qamw_version(void);
+
+/* ---------------- device entry points ---------------- */
+
+/*
+ * Calibration (QAM-W, Methodology: Activation-Aware Scaling; Pairing and
+ * Calibration).
+ *   W         [N][ldw] of wdtype (QAMW_F32 or QAMW_BF16)
+ *   chan_rms  [d] float32, r_j > 0: RMS of input channel j's activations
+ *   alpha     finite exponent; s_j = r_j ^ alpha (alpha = 0 gives s = 1)
+ *   block     Hadamard block b: power of two, 16 <= b <= 1024, d % b == 0
+ *   s_out     [d] float32 out: s_j
+ *   sigma_out [d/2] float32 out: sigma_k = sum_n |z_{n,k}| / (N sqrt(pi/2)),
+ *             |z_{n,k}| taken on the normalised rotated row u_n (0 for rho_n = 0)
+ *   workspace >= qamw_calibrate_workspace_bytes(N, d, block), 256-byte aligned
+ * Deterministic: the column sums use a fixed order, no atomics.
+ */
+int32_t qamw_calibrate(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
+                       const float* chan_rms, float alpha, int32_t block, uint64_t sign_seed,
+                       float* s_out, float* sigma_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Encode (QAM-W, Methodology: Separation of Scale and Direction; Deterministic
+ * Rotation; Pairing and Calibration; Joint 2D Quantization).
+ *   W, wdtype, N, d, ldw, block, sign_seed  as for qamw_calibrate
+ *   s          [d] float32: channel scales (normally s_out of qamw_calibrate)
+ *   sigma      [d/2] float32: pair scales; sigma_k = 0 codes z~ = 0
+ *   codebook   [K][2] float32, 2 <= K <= 4096
+ *   packed     [N][qamw_packed_row_words(d, K)] uint32 out
+ *   rownorm_f16[N] uint16 out: binary16 bits of rho_n (RNE)
+ *   workspace  >= qamw_encode_workspace_bytes(N), 256-byte aligned
+ * The nearest centroid is decided in fp32 on the expanded score
+ * |c|^2/2 - z~ . c (equal to |z~ - c|^2/2 - |z~|^2/2); equal scores go to the
+ * lowest index.
+ */
+int32_t qamw_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
+                    const float* s, const float* sigma, int32_t block, uint64_t sign_seed,
+                    const float* codebook, int32_t K,
+                    uint32_t* packed, uint16_t* rownorm_f16,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode (QAM-W, Methodology: Decoding).
+ *   packed, rownorm_f16, N, d, block, sign_seed, codebook, K  as produced by
+ *             qamw_encode; indices >= K (never produced) are clamped to K - 1
+ *   s          [d] float32 or NULL.  With s the output approximates W; with
+ *              NULL it approximates W' = W diag(s) (scales folded elsewhere)
+ *   sigma      [d/2] float32
+ *   W_out      [N][ldo] of out_dtype (QAMW_F32, QAMW_BF16 or QAMW_F16; the
+ *              16-bit types are rounded to nearest even from fp32)
+ * Arithmetic is fp32.
+ */
+int32_t qamw_decode(const uint32_t* packed, const uint16_t* rownorm_f16, int64_t N, int64_t d,
+                    const float* s, const float* sigma, int32_t block, uint64_t sign_seed,
+                    const float* codebook, int32_t K,
+                    void* W_out, int32_t out_dtype, int64_t ldo, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QAMW_H */

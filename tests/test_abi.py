@@ -1,0 +1,125 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/qamw.h declares, its host helpers return the documented values, and
+invalid arguments are rejected on the host before anything is launched."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qamw.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from vector_codebook_codec_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libqamw.so not built")
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qamw_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("qamw_calibrate", "qamw_encode", "qamw_decode", "qamw_packed_row_words"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from vector_codebook_codec_amd import _lib
+
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"{name} has no Python binding"
+
+
+def test_host_helpers(lib):
+    for K in (2, 3, 4, 256, 257, 2048, 4096):
+        assert lib.qamw_index_bits(K) == math.ceil(math.log2(K))
+    assert lib.qamw_index_bits(1) == -1 and lib.qamw_index_bits(4097) == -1
+    assert lib.qamw_packed_row_words(11008, 2048) == 1892
+    assert lib.qamw_packed_row_words(4096, 2048) == 704
+    assert lib.qamw_packed_row_words(13824, 4096) == 2592
+    assert lib.qamw_packed_row_words(12, 2048) == 4
+    assert lib.qamw_packed_row_words(13, 2048) == -1
+    assert lib.qamw_encode_workspace_bytes(4096) == 4096 * 8
+    assert lib.qamw_encode_workspace_bytes(5) == 256
+    # rho (fp64, 256-byte padded) + ceil(N / 16) tiles x d/2 fp32
+    assert lib.qamw_calibrate_workspace_bytes(4096, 11008, 256) == 4096 * 8 + 256 * 5504 * 4
+    assert lib.qamw_calibrate_workspace_bytes(0, 16, 16) == 0
+    assert lib.qamw_status_string(-4) == b"workspace missing or too small"
+
+
+# Fake, never-dereferenced device addresses: every call below must fail in
+# host-side validation, before any HIP call.
+A = 1 << 20           # 16-byte aligned
+MIS = A + 4           # misaligned
+WS = 1 << 24
+
+
+def _encode(lib, **kw):
+    args = dict(W=A, wdt=1, N=8, d=256, ldw=256, s=A, sigma=A, block=128, seed=0, cb=A, K=256,
+                packed=A, rn=A, ws=WS, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return lib.qamw_encode(args["W"], args["wdt"], args["N"], args["d"], args["ldw"], args["s"], args["sigma"],
+                           args["block"], args["seed"], args["cb"], args["K"], args["packed"], args["rn"],
+                           args["ws"], args["ws_bytes"], args["stream"])
+
+
+def _calibrate(lib, **kw):
+    args = dict(W=A, wdt=0, N=8, d=256, ldw=256, r=A, alpha=0.5, block=128, seed=0, s=A, sigma=A,
+                ws=WS, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return lib.qamw_calibrate(args["W"], args["wdt"], args["N"], args["d"], args["ldw"], args["r"],
+                              args["alpha"], args["block"], args["seed"], args["s"], args["sigma"], args["ws"],
+                              args["ws_bytes"], args["stream"])
+
+
+def _decode(lib, **kw):
+    args = dict(packed=A, rn=A, N=8, d=256, s=A, sigma=A, block=128, seed=0, cb=A, K=256, out=A, odt=0,
+                ldo=256, stream=None)
+    args.update(kw)
+    return lib.qamw_decode(args["packed"], args["rn"], args["N"], args["d"], args["s"], args["sigma"],
+                           args["block"], args["seed"], args["cb"], args["K"], args["out"], args["odt"],
+                           args["ldo"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block=3), -2), (dict(block=8), -2), (dict(block=2048), -2), (dict(block=128, d=320), -1),
+    (dict(N=0), -1), (dict(d=-16), -1), (dict(K=1), -2), (dict(K=4097), -2), (dict(ldw=128), -1),
+    (dict(W=None), -1), (dict(cb=None), -1), (dict(s=None), -1), (dict(packed=None), -1),
+    (dict(W=MIS), -1), (dict(packed=MIS), -1), (dict(wdt=2), -2), (dict(ldw=260), -1),
+    (dict(ws=None), -4), (dict(ws_bytes=8), -4), (dict(ws=WS + 16), -4),
+])
+def test_encode_rejects(lib, kw, status):
+    assert _encode(lib, **kw) == status
+    assert lib.qamw_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(alpha=float("nan")), -1), (dict(alpha=float("inf")), -1), (dict(r=None), -1),
+    (dict(sigma=None), -1), (dict(s=MIS), -1), (dict(ws_bytes=500), -4), (dict(block=32, d=48), -1),
+])
+def test_calibrate_rejects(lib, kw, status):
+    assert _calibrate(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(odt=3), -2), (dict(ldo=100), -1), (dict(out=MIS), -1), (dict(rn=None), -1),
+    (dict(K=5000), -2), (dict(block=64, d=96), -1), (dict(odt=1, ldo=260), -1),
+])
+def test_decode_rejects(lib, kw, status):
+    assert _decode(lib, **kw) == status
+
+
+def test_workspace_size_is_enforced(lib):
+    need = lib.qamw_calibrate_workspace_bytes(8, 256, 128)
+    assert _calibrate(lib, ws_bytes=need - 1) == -4

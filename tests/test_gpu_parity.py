@@ -1,0 +1,330 @@
+"""GPU parity of the QAM-W kernels against the CPU oracle (needs an MI355X).
+
+Criteria (the tolerances the codec's target sets, written out here):
+  * s_j: relative error <= 5e-7 (fp32 powf vs fp64 r^alpha).
+  * sigma_k: relative error <= 1e-5 (fp32 amplitudes, fp64 tile sums).
+  * row norms (fp16 bits): identical, except a one-ulp difference where the
+    oracle's norm lies within 1e-9 (relative) of an fp16 rounding boundary.
+  * indices: identical, except near-ties -- pairs where the GPU's centroid is
+    within 1e-6 |z~|^2 of the oracle's in fp64 squared distance; near-ties are
+    counted and printed.
+    "mode C": the oracle encodes with the GPU's s and sigma (isolates the
+    per-row rotation and the nearest-centroid search);
+    "mode I": the oracle uses its own s and sigma (fully independent).
+  * decode: max |GPU - oracle| <= 1e-5 in fp32 output; fp16/bf16 outputs
+    within half an output ulp of the oracle's fp64 value plus 2e-6.
+Full-size workloads are checked on sampled rows (sigma always over all rows).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import qamw_ref as O
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vector_codebook_codec_amd as pkg
+    from vector_codebook_codec_amd import _lib
+
+    _lib.load()
+    return pkg
+
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(W, wdtype):
+    if wdtype == "bf16":
+        return torch.from_numpy(W.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(W).to(DEV)
+
+
+def f16_boundary_ok(gpu_bits, ora_bits, rho):
+    """Equal, or one ulp apart with rho within 1e-9 of a rounding boundary."""
+    gpu_bits = gpu_bits.astype(np.int64)
+    ora_bits = ora_bits.astype(np.int64)
+    same = gpu_bits == ora_bits
+    lo = np.minimum(gpu_bits, ora_bits).astype(np.uint16)
+    hi = np.maximum(gpu_bits, ora_bits).astype(np.uint16)
+    mid = (O.f16_bits_to_f64(lo) + O.f16_bits_to_f64(hi)) / 2
+    near = (np.abs(gpu_bits - ora_bits) == 1) & (np.abs(rho - mid) <= 1e-9 * np.abs(rho))
+    return same | near
+
+
+def run_gpu(q, wl, C, stream_sync=True):
+    W = to_dev(wl.W, wl.wdtype)
+    r = torch.from_numpy(wl.r).to(DEV)
+    Ct = torch.from_numpy(C).to(DEV)
+    s, sigma = q.qamw_calibrate(W, r, wl.alpha, wl.block, wl.sign_seed)
+    packed, rn = q.qamw_encode(W, s, sigma, wl.block, wl.sign_seed, Ct)
+    torch.cuda.synchronize()
+    return dict(W=W, r=r, C=Ct, s=s, sigma=sigma, packed=packed, rn=rn)
+
+
+def check_encode_rows(wl, C, g, rows, mode, s_ref=None, sig_ref=None):
+    """Compare GPU indices / row norms of ``rows`` with the oracle."""
+    Wf = wl.W_f32()
+    s_g = g["s"].cpu().numpy()
+    sig_g = g["sigma"].cpu().numpy()
+    s_use, sig_use = (s_g, sig_g) if mode == "C" else (s_ref, sig_ref)
+    enc = O.encode(Wf, s_use, sig_use, wl.block, wl.sign_seed, C, rows=rows)
+    K = C.shape[0]
+    packed = g["packed"].cpu().numpy().view(np.uint32)[rows]
+    idx_g = O.unpack(packed, K, wl.d)
+    ok = O.accept_index(enc["zt"].reshape(-1, 2), C, enc["idx"].reshape(-1), idx_g.reshape(-1))
+    n_diff = int((idx_g != enc["idx"]).sum())
+    say(f"  mode {mode}: {len(rows)} rows, {idx_g.size} pairs, {n_diff} differ, "
+        f"{int((~ok).sum())} beyond near-tie tolerance")
+    assert ok.all(), f"{int((~ok).sum())} indices differ beyond the near-tie tolerance"
+    rn = g["rn"].cpu().numpy().view(np.uint16)[rows]
+    if mode == "C":
+        assert f16_boundary_ok(rn, enc["rho_hat_bits"], enc["rho"]).all()
+    # padding words after the last index are zero
+    B = O.index_bits(K)
+    used = (wl.d // 2) * B
+    if used % 32:
+        assert not (packed[:, used // 32] >> np.uint32(used % 32)).any()
+    assert not packed[:, -(-used // 32):].any()
+    return enc, idx_g
+
+
+def check_decode_rows(q, wl, C, g, rows, out_dtype=torch.float32, use_s=True):
+    s_g = g["s"].cpu().numpy()
+    sig_g = g["sigma"].cpu().numpy()
+    Wh = q.qamw_decode(g["packed"], g["rn"], wl.d, g["s"] if use_s else None, g["sigma"], wl.block,
+                       wl.sign_seed, g["C"], out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    packed = g["packed"].cpu().numpy().view(np.uint32)[rows]
+    rn = g["rn"].cpu().numpy().view(np.uint16)[rows]
+    ref = O.decode(packed, rn, s_g if use_s else None, sig_g, wl.block, wl.sign_seed, C, wl.d)
+    got = Wh[rows].float().cpu().numpy().astype(np.float64)
+    if out_dtype == torch.float32:
+        err = float(np.max(np.abs(got - ref)))
+        say(f"  decode fp32 rows={len(rows)} max abs err {err:.3e}")
+        assert err <= 1e-5
+    else:
+        if out_dtype == torch.float16:
+            ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+            bits_ref = O.to_f16_bits(ref)
+            bits_got = Wh[rows].cpu().view(torch.int16).numpy().view(np.uint16)
+        else:
+            e = np.floor(np.log2(np.maximum(np.abs(ref), 1e-38)))
+            ulp = 2.0 ** (e - 7)
+            bits_ref = O.to_bf16_bits(ref)
+            bits_got = Wh[rows].cpu().view(torch.int16).numpy().view(np.uint16)
+        err = np.abs(got - ref)
+        assert np.all(err <= 0.5 * ulp + 2e-6), float(np.max(err - 0.5 * ulp))
+        same = float((bits_ref == bits_got).mean())
+        say(f"  decode {out_dtype} identical to oracle rounding: {same:.6f}")
+        assert same >= 0.999
+    return Wh
+
+
+# ---------------------------------------------------------------- full c1
+def test_c1_full(q):
+    wl = workloads.get("c1_256x512")
+    C = q.load_codebook(wl.K)
+    say(f"case c1 {wl.N}x{wl.d} K={wl.K} b={wl.block}: calibrate/encode")
+    g = run_gpu(q, wl, C)
+    s_o, sig_o, _ = O.calibrate(wl.W_f32(), wl.r, wl.alpha, wl.block, wl.sign_seed)
+    s_g, sig_g = g["s"].cpu().numpy(), g["sigma"].cpu().numpy()
+    assert np.max(np.abs(s_g / s_o - 1)) <= 5e-7
+    assert np.max(np.abs(sig_g / sig_o - 1)) <= 1e-5
+    rows = np.arange(wl.N)
+    check_encode_rows(wl, C, g, rows, "C")
+    check_encode_rows(wl, C, g, rows, "I", s_o, sig_o)
+    say("case c1: decode")
+    check_decode_rows(q, wl, C, g, rows)
+    check_decode_rows(q, wl, C, g, rows, torch.float16)
+    check_decode_rows(q, wl, C, g, rows, torch.bfloat16)
+    check_decode_rows(q, wl, C, g, rows, use_s=False)
+
+
+# ---------------------------------------------------------------- shapes, blocks, K
+SHAPES = [
+    # (N, d, block, K, wdtype, alpha, seed)
+    (3, 16, 16, 2, "f32", 0.5, 1),          # one chunk, one lane, binary codebook
+    (5, 48, 16, 4, "bf16", 0.0, 2),          # ragged window, alpha = 0
+    (7, 96, 32, 16, "f32", 1.0, 3),
+    (9, 1088, 64, 128, "bf16", 0.5, 4),      # two windows, second ragged
+    (17, 2560, 128, 1024, "f32", 0.5, 5),
+    (6, 3072, 256, 2048, "bf16", 0.5, 6),
+    (4, 1536, 512, 4096, "f32", 0.5, 7),
+    (3, 2048, 1024, 256, "bf16", 0.5, 8),
+    (1, 1024, 1024, 2048, "f32", 0.5, 9),    # a single row
+]
+
+
+@pytest.mark.parametrize("N,d,block,K,wdtype,alpha,seed", SHAPES)
+def test_shapes(q, N, d, block, K, wdtype, alpha, seed):
+    rng = np.random.default_rng(1000 + seed)
+    W = (rng.standard_normal((N, d)) * 0.02).astype(np.float32)
+    r = rng.lognormal(0.0, 1.0, d).astype(np.float32)
+    if wdtype == "bf16":
+        W = workloads.bf16_bits_from_f32(W)
+    wl = workloads.Workload(f"shape{seed}", W, wdtype, r, alpha, block, seed * 12345, K)
+    C = q.load_codebook(K)
+    say(f"case shapes N={N} d={d} b={block} K={K} {wdtype} alpha={alpha}")
+    g = run_gpu(q, wl, C)
+    s_o, sig_o, _ = O.calibrate(wl.W_f32(), wl.r, alpha, block, wl.sign_seed)
+    assert np.max(np.abs(g["s"].cpu().numpy() / s_o - 1)) <= 5e-7
+    assert np.max(np.abs(g["sigma"].cpu().numpy() / sig_o - 1)) <= 1e-5
+    rows = np.arange(N)
+    check_encode_rows(wl, C, g, rows, "C")
+    check_decode_rows(q, wl, C, g, rows)
+
+
+def test_strided_rows(q):
+    """ldw > d on input and ldo > d on output."""
+    rng = np.random.default_rng(77)
+    N, d, ld, K, b = 10, 512, 640, 256, 128
+    big = (rng.standard_normal((N, ld)) * 0.02).astype(np.float32)
+    r = rng.lognormal(0, 1, d).astype(np.float32)
+    C = q.load_codebook(K)
+    Wbig = torch.from_numpy(big).to(DEV)
+    W = Wbig[:, :d]
+    s, sigma = q.qamw_calibrate(W, torch.from_numpy(r).to(DEV), 0.5, b, 3)
+    packed, rn = q.qamw_encode(W, s, sigma, b, 3, torch.from_numpy(C).to(DEV))
+    Wc = W.contiguous()
+    s2, sigma2 = q.qamw_calibrate(Wc, torch.from_numpy(r).to(DEV), 0.5, b, 3)
+    packed2, rn2 = q.qamw_encode(Wc, s2, sigma2, b, 3, torch.from_numpy(C).to(DEV))
+    out_big = torch.zeros((N, ld), device=DEV)
+    q.qamw_decode(packed, rn, d, s, sigma, b, 3, torch.from_numpy(C).to(DEV), out=out_big[:, :d])
+    ref = q.qamw_decode(packed2, rn2, d, s2, sigma2, b, 3, torch.from_numpy(C).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(s, s2) and torch.equal(sigma, sigma2)
+    assert torch.equal(packed, packed2) and torch.equal(rn, rn2)
+    assert torch.equal(out_big[:, :d], ref)
+    assert torch.count_nonzero(out_big[:, d:]) == 0
+
+
+# ---------------------------------------------------------------- degenerate inputs
+def test_zero_rows_and_zero_sigma(q):
+    rng = np.random.default_rng(5)
+    N, d, b, K = 8, 256, 128, 256
+    W = (rng.standard_normal((N, d)) * 0.02).astype(np.float32)
+    W[3] = 0.0
+    C = q.load_codebook(K)
+    Wt = torch.from_numpy(W).to(DEV)
+    s = torch.ones(d, device=DEV)
+    sig_np = (np.abs(rng.standard_normal(d // 2)) * 0.05 + 0.01).astype(np.float32)
+    sig_np[[0, 17, 127]] = 0.0
+    sigma = torch.from_numpy(sig_np).to(DEV)
+    Ct = torch.from_numpy(C).to(DEV)
+    say("case degenerate: zero row, sigma_k = 0")
+    packed, rn = q.qamw_encode(Wt, s, sigma, b, 9, Ct)
+    Wh = q.qamw_decode(packed, rn, d, s, sigma, b, 9, Ct)
+    torch.cuda.synchronize()
+    enc = O.encode(W, np.ones(d), sig_np, b, 9, C)
+    idx_g = O.unpack(packed.cpu().numpy().view(np.uint32), K, d)
+    ok = O.accept_index(enc["zt"].reshape(-1, 2), C, enc["idx"].reshape(-1), idx_g.reshape(-1))
+    assert ok.all()
+    origin, *_ = O.nearest_centroid(np.zeros((1, 2)), C)
+    assert np.all(idx_g[:, [0, 17, 127]] == origin[0])
+    assert np.all(idx_g[3] == origin[0])
+    assert rn.cpu().numpy()[3] == 0
+    assert torch.count_nonzero(Wh[3]) == 0
+
+
+def test_all_zero_matrix(q):
+    N, d, b, K = 4, 128, 128, 16
+    Wt = torch.zeros((N, d), device=DEV)
+    C = q.load_codebook(K)
+    s, sigma = q.qamw_calibrate(Wt, torch.ones(d, device=DEV), 0.5, b, 0)
+    packed, rn = q.qamw_encode(Wt, s, sigma, b, 0, torch.from_numpy(C).to(DEV))
+    Wh = q.qamw_decode(packed, rn, d, s, sigma, b, 0, torch.from_numpy(C).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(sigma) == 0
+    assert torch.count_nonzero(rn) == 0 and torch.count_nonzero(Wh) == 0
+    origin, *_ = O.nearest_centroid(np.zeros((1, 2)), C)
+    assert np.all(O.unpack(packed.cpu().numpy().view(np.uint32), K, d) == origin[0])
+
+
+def test_out_of_range_indices_clamp(q):
+    """A hand-made stream with indices >= K decodes as K - 1."""
+    N, d, b, K = 2, 64, 32, 5          # B = 3, so 5..7 are representable
+    C = q.load_codebook(16)[:K].copy()
+    rng = np.random.default_rng(3)
+    idx = rng.integers(0, 8, size=(N, d // 2))
+    packed = O.pack(idx, K, d)
+    rn = O.to_f16_bits(np.array([1.0, 0.5]))
+    sig = np.full(d // 2, 0.1, np.float32)
+    s = np.ones(d, np.float32)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    Wh = q.qamw_decode(dev(packed.view(np.int32)), dev(rn.view(np.int16)), d, dev(s), dev(sig), b, 4, dev(C))
+    torch.cuda.synchronize()
+    ref = O.decode(packed, rn, s, sig, b, 4, C, d)
+    assert float(np.max(np.abs(Wh.cpu().numpy() - ref))) <= 1e-6
+
+
+def test_exact_ties_lowest_index(q):
+    """Duplicated centroids: every index must be the first copy."""
+    rng = np.random.default_rng(11)
+    N, d, b = 4, 256, 64
+    base = q.load_codebook(16)
+    C = np.concatenate([base, base]).astype(np.float32)          # K = 32, second half duplicates
+    W = (rng.standard_normal((N, d)) * 0.02).astype(np.float32)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    s, sigma = q.qamw_calibrate(dev(W), dev(np.ones(d, np.float32)), 0.0, b, 1)
+    packed, rn = q.qamw_encode(dev(W), s, sigma, b, 1, dev(C))
+    torch.cuda.synchronize()
+    idx = O.unpack(packed.cpu().numpy().view(np.uint32), 32, d)
+    assert idx.max() < 16
+    enc = O.encode(W, s.cpu().numpy(), sigma.cpu().numpy(), b, 1, C)
+    assert O.accept_index(enc["zt"].reshape(-1, 2), C, enc["idx"].reshape(-1), idx.reshape(-1)).all()
+
+
+# ---------------------------------------------------------------- determinism
+def test_repeatable_bitwise(q):
+    wl = workloads.get("c1_256x512")
+    C = q.load_codebook(wl.K)
+    outs = []
+    for _ in range(3):
+        g = run_gpu(q, wl, C)
+        Wh = q.qamw_decode(g["packed"], g["rn"], wl.d, g["s"], g["sigma"], wl.block, wl.sign_seed, g["C"])
+        torch.cuda.synchronize()
+        outs.append((g["s"].cpu(), g["sigma"].cpu(), g["packed"].cpu(), g["rn"].cpu(), Wh.cpu()))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- full-size workloads
+FULL = ["c2_4096x4096", "c3_11008x4096", "c3t_4096x11008", "c4_5120x13824_K256_a0",
+        "c4_5120x13824_K4096_a0.5"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(q, name):
+    wl = workloads.get(name)
+    C = q.load_codebook(wl.K)
+    say(f"case {name} {wl.N}x{wl.d} K={wl.K} b={wl.block}: GPU calibrate/encode")
+    g = run_gpu(q, wl, C)
+    s_o, sig_o, _ = O.calibrate(wl.W_f32(), wl.r, wl.alpha, wl.block, wl.sign_seed)
+    s_g, sig_g = g["s"].cpu().numpy(), g["sigma"].cpu().numpy()
+    assert np.max(np.abs(s_g / s_o - 1)) <= 5e-7
+    err = np.max(np.abs(sig_g / sig_o - 1))
+    say(f"  sigma max rel err {err:.3e}")
+    assert err <= 1e-5
+    rng = np.random.default_rng(hash(name) % (1 << 32))
+    rows = np.sort(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, 10, replace=False)]))
+    check_encode_rows(wl, C, g, rows, "C")
+    check_encode_rows(wl, C, g, rows[:4], "I", s_o, sig_o)
+    say(f"case {name}: GPU decode")
+    check_decode_rows(q, wl, C, g, rows)
+    if name.startswith("c3"):
+        check_decode_rows(q, wl, C, g, rows, torch.float16)

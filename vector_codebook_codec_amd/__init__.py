@@ -1,0 +1,19 @@
+"""QAM-W weight codec on AMD Instinct MI355X (gfx950).
+
+The codec's work runs in hand-written HIP kernels behind the C ABI of
+include/qamw.h (libqamw.so, built in-tree by ``_build.build()``).  This
+package binds that ABI for torch device tensors; see ``codec`` for the entry
+points ``qamw_calibrate``, ``qamw_encode`` and ``qamw_decode``.
+"""
+from .codec import (  # noqa: F401
+    load_codebook,
+    qamw_calibrate,
+    qamw_calibrate_workspace_bytes,
+    qamw_decode,
+    qamw_encode,
+    qamw_encode_workspace_bytes,
+    qamw_index_bits,
+    qamw_packed_row_words,
+)
+
+__version__ = "0.1.0"

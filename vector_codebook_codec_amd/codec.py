@@ -1,0 +1,170 @@
+"""Python binding of the QAM-W C ABI over torch device tensors.
+
+Each function has the name of the C entry point it calls and only marshals
+arguments: it checks devices, dtypes and shapes, allocates the outputs and
+workspace with torch when the caller passes none, and hands raw pointers plus
+the current HIP stream to libqamw.so.  Every step of the codec runs in the
+library's kernels.
+"""
+from __future__ import annotations
+
+import json
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+
+CODEBOOK_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "codebooks")
+
+_WDT = {torch.float32: _lib.QAMW_F32, torch.bfloat16: _lib.QAMW_BF16}
+_ODT = {torch.float32: _lib.QAMW_F32, torch.bfloat16: _lib.QAMW_BF16, torch.float16: _lib.QAMW_F16}
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _vec(t: torch.Tensor, name: str, n: int, dtype=torch.float32) -> None:
+    _dev(t, name)
+    if t.dtype != dtype or t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor with {n} elements")
+
+
+def _rows(W: torch.Tensor, name: str):
+    _dev(W, name)
+    if W.dim() != 2 or W.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return W.shape[0], W.shape[1], W.stride(0)
+
+
+# ---------------------------------------------------------------- host helpers
+def qamw_index_bits(K: int) -> int:
+    return int(_lib.load().qamw_index_bits(K))
+
+
+def qamw_packed_row_words(d: int, K: int) -> int:
+    return int(_lib.load().qamw_packed_row_words(d, K))
+
+
+def qamw_calibrate_workspace_bytes(N: int, d: int, block: int) -> int:
+    return int(_lib.load().qamw_calibrate_workspace_bytes(N, d, block))
+
+
+def qamw_encode_workspace_bytes(N: int) -> int:
+    return int(_lib.load().qamw_encode_workspace_bytes(N))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 256-byte aligned blocks
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def load_codebook(K: int) -> np.ndarray:
+    """The stored K x 2 float32 codebook (2D Lloyd-Max, unit circular Gaussian)."""
+    path = os.path.join(CODEBOOK_DIR, f"qamw_K{K}.f32")
+    with open(path, "rb") as f:
+        C = np.frombuffer(f.read(), dtype="<f4").reshape(K, 2).copy()
+    with open(os.path.join(CODEBOOK_DIR, f"qamw_K{K}.json")) as f:
+        meta = json.load(f)
+    if meta["K"] != K:
+        raise ValueError(f"codebook metadata mismatch for K={K}")
+    return C
+
+
+# ---------------------------------------------------------------- entry points
+def qamw_calibrate(W: torch.Tensor, chan_rms: torch.Tensor, alpha: float, block: int, sign_seed: int,
+                   s_out: Optional[torch.Tensor] = None, sigma_out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """Returns (s [d] fp32, sigma [d/2] fp32)."""
+    N, d, ldw = _rows(W, "W")
+    if W.dtype not in _WDT:
+        raise ValueError("W must be float32 or bfloat16")
+    _vec(chan_rms, "chan_rms", d)
+    if s_out is None:
+        s_out = torch.empty(d, dtype=torch.float32, device=W.device)
+    if sigma_out is None:
+        sigma_out = torch.empty(d // 2, dtype=torch.float32, device=W.device)
+    _vec(s_out, "s_out", d)
+    _vec(sigma_out, "sigma_out", d // 2)
+    need = qamw_calibrate_workspace_bytes(N, d, block)
+    if workspace is None:
+        workspace = _workspace(need, W.device)
+    _lib.check("qamw_calibrate", _lib.load().qamw_calibrate(
+        W.data_ptr(), _WDT[W.dtype], N, d, ldw, chan_rms.data_ptr(), float(alpha), int(block),
+        int(sign_seed), s_out.data_ptr(), sigma_out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return s_out, sigma_out
+
+
+def qamw_encode(W: torch.Tensor, s: torch.Tensor, sigma: torch.Tensor, block: int, sign_seed: int,
+                codebook: torch.Tensor, packed: Optional[torch.Tensor] = None,
+                rownorm_f16: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None):
+    """Returns (packed [N][row_words] int32 holding uint32 words, rownorm [N] int16 holding fp16 bits)."""
+    N, d, ldw = _rows(W, "W")
+    if W.dtype not in _WDT:
+        raise ValueError("W must be float32 or bfloat16")
+    _vec(s, "s", d)
+    _vec(sigma, "sigma", d // 2)
+    _dev(codebook, "codebook")
+    if codebook.dtype != torch.float32 or codebook.dim() != 2 or codebook.shape[1] != 2 or not codebook.is_contiguous():
+        raise ValueError("codebook must be a contiguous K x 2 float32 tensor")
+    K = codebook.shape[0]
+    rw = qamw_packed_row_words(d, K)
+    if rw < 0:
+        raise ValueError(f"unsupported K={K} or d={d}")
+    if packed is None:
+        packed = torch.empty((N, rw), dtype=torch.int32, device=W.device)
+    if rownorm_f16 is None:
+        rownorm_f16 = torch.empty(N, dtype=torch.int16, device=W.device)
+    _dev(packed, "packed")
+    if packed.dtype != torch.int32 or tuple(packed.shape) != (N, rw) or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous int32 tensor of shape ({N}, {rw})")
+    _vec(rownorm_f16, "rownorm_f16", N, torch.int16)
+    need = qamw_encode_workspace_bytes(N)
+    if workspace is None:
+        workspace = _workspace(need, W.device)
+    _lib.check("qamw_encode", _lib.load().qamw_encode(
+        W.data_ptr(), _WDT[W.dtype], N, d, ldw, s.data_ptr(), sigma.data_ptr(), int(block), int(sign_seed),
+        codebook.data_ptr(), K, packed.data_ptr(), rownorm_f16.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return packed, rownorm_f16
+
+
+def qamw_decode(packed: torch.Tensor, rownorm_f16: torch.Tensor, d: int, s: Optional[torch.Tensor],
+                sigma: torch.Tensor, block: int, sign_seed: int, codebook: torch.Tensor,
+                out_dtype=torch.float32, out: Optional[torch.Tensor] = None, stream=None):
+    """Returns the decoded [N][d] matrix in out_dtype (fp32, bf16 or fp16)."""
+    _dev(packed, "packed")
+    N = packed.shape[0]
+    _dev(codebook, "codebook")
+    if codebook.dtype != torch.float32 or codebook.dim() != 2 or codebook.shape[1] != 2 or not codebook.is_contiguous():
+        raise ValueError("codebook must be a contiguous K x 2 float32 tensor")
+    K = codebook.shape[0]
+    rw = qamw_packed_row_words(d, K)
+    if packed.dtype != torch.int32 or tuple(packed.shape) != (N, rw) or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous int32 tensor of shape ({N}, {rw})")
+    _vec(rownorm_f16, "rownorm_f16", N, torch.int16)
+    if s is not None:
+        _vec(s, "s", d)
+    _vec(sigma, "sigma", d // 2)
+    if out is None:
+        out = torch.empty((N, d), dtype=out_dtype, device=packed.device)
+    n2, d2, ldo = _rows(out, "out")
+    if (n2, d2) != (N, d) or out.dtype not in _ODT:
+        raise ValueError("out must be N x d of float32, bfloat16 or float16")
+    _lib.check("qamw_decode", _lib.load().qamw_decode(
+        packed.data_ptr(), rownorm_f16.data_ptr(), N, d, None if s is None else s.data_ptr(),
+        sigma.data_ptr(), int(block), int(sign_seed), codebook.data_ptr(), K, out.data_ptr(),
+        _ODT[out.dtype], ldo, _stream(stream)))
+    return out
