@@ -33,6 +33,29 @@ import workloads  # noqa: E402
 
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_kernel_4096x11008_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "vector_codebook_codec_amd", "csrc", f)
+                  for f in ("qamw_kernels.hip", "qamw_device.h")]
+
+
+def measured_traffic(workload):
+    """Encode-kernel HBM bytes per launch from the committed counter passes,
+    or None when they were taken on other kernel sources or another workload."""
+    import hashlib
+
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        sha = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()
+    except OSError:
+        return None
+    if kv.get("source_sha256") != sha or kv.get("workload") != workload:
+        return None
+    return 1024.0 * (float(kv["fetch_kib"]) * float(kv["fetch_scale"]) +
+                     float(kv["write_kib"]) * float(kv["write_scale"]))
 
 
 def parse():
@@ -173,7 +196,7 @@ def main():
                    "out_dtype": "f32"},
         "roofline": {"bound": "alu", "kernel": "encode_kernel (qamw_encode; includes its row-norm pre-pass)",
                      "achieved": achieved_tflops, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tflops / PEAK_FP32_TFLOPS, "traffic": None,
+                     "frac": achieved_tflops / PEAK_FP32_TFLOPS, "traffic": measured_traffic(wl.name),
                      "algorithmic": f"{P} pairs x {K} centroids x 4 flops = {enc_flops:.4g} per launch"},
         "per_entry_ms": {"calibrate": cal_ms, "encode": enc_ms, "decode": dec_ms},
         "encode_gweights_s": weights / ((cal_ms + enc_ms) * 1e-3) / 1e9,

@@ -12,11 +12,16 @@ Criteria (the tolerances the codec's target sets, written out here):
     per-row rotation and the nearest-centroid search);
     "mode I": the oracle uses its own s and sigma (fully independent).
   * decode: max |GPU - oracle| <= 1e-5 in fp32 output; fp16/bf16 outputs
-    within half an output ulp of the oracle's fp64 value plus 2e-6.
+    within half an output ulp of the oracle's fp64 value plus 2e-6.  The
+    GPU rounds its fp32 value, so it lands on the other neighbour whenever a
+    rounding midpoint lies between that value and the fp64 one: with a
+    relative decode error of ~2e-6 that happens for ~2e-6 * 2^10 = 0.2% of
+    fp16 outputs; at least 99% must be identical to the oracle's rounding.
 Full-size workloads are checked on sampled rows (sigma always over all rows).
 """
 import math
 import sys
+import zlib
 
 import numpy as np
 import pytest
@@ -130,7 +135,7 @@ def check_decode_rows(q, wl, C, g, rows, out_dtype=torch.float32, use_s=True):
         assert np.all(err <= 0.5 * ulp + 2e-6), float(np.max(err - 0.5 * ulp))
         same = float((bits_ref == bits_got).mean())
         say(f"  decode {out_dtype} identical to oracle rounding: {same:.6f}")
-        assert same >= 0.999
+        assert same >= 0.99
     return Wh
 
 
@@ -320,7 +325,7 @@ def test_full_size_sampled(q, name):
     err = np.max(np.abs(sig_g / sig_o - 1))
     say(f"  sigma max rel err {err:.3e}")
     assert err <= 1e-5
-    rng = np.random.default_rng(hash(name) % (1 << 32))
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
     rows = np.sort(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, 10, replace=False)]))
     check_encode_rows(wl, C, g, rows, "C")
     check_encode_rows(wl, C, g, rows[:4], "I", s_o, sig_o)

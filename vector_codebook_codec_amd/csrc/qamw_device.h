@@ -74,55 +74,217 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
-struct OutF32 {
+// ---------------------------------------------------------------------------
+// Window-contiguous stores.  After the rotation lane l holds the 16 outputs
+// of chunk co_l of its window.  Storing them straight from registers makes
+// every store instruction scatter 16-byte pieces over the window; instead the
+// wave writes its window (64 chunks) to an LDS buffer and reads it back so
+// that store instruction v writes the window's v-th contiguous 64 x 16 bytes.
+// 16-byte slots are XOR-swizzled so that both LDS passes spread over all bank
+// groups.  The buffer is private to the wave; LDS operations of one wave
+// complete in order, and the fences keep the compiler from reordering the
+// cross-lane accesses.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int stage_slot(int chunk, int q) {  // q: 16-byte piece of the chunk (0..3)
+  return chunk * 4 + (q ^ ((chunk >> 2) & 3));
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Stage 16 fp32 outputs of chunk `co_local`, store the window contiguously.
+// buf: 256 x 16 bytes of LDS private to the wave.  Columns at or beyond
+// `valid_cols` (relative to the window start) are not written.
+__device__ __forceinline__ void store_window_f32(uint4* buf, int lane, int co_local, const float x[16],
+                                                float* __restrict__ dst, int valid_cols) {
+  wave_lds_fence();
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    buf[stage_slot(co_local, q)] = make_uint4(__float_as_uint(x[4 * q]), __float_as_uint(x[4 * q + 1]),
+                                              __float_as_uint(x[4 * q + 2]), __float_as_uint(x[4 * q + 3]));
+  wave_lds_fence();
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int e = v * 256 + lane * 4;          // first column of this lane's piece
+    const uint4 t = buf[stage_slot(e >> 4, (e >> 2) & 3)];
+    if (e < valid_cols) reinterpret_cast<uint4*>(dst + e)[0] = t;
+  }
+}
+
+// Same for 16-bit outputs (already packed two per word): 32 bytes per lane.
+__device__ __forceinline__ void store_window_b16(uint4* buf, int lane, int co_local, const uint32_t w[8],
+                                                 uint16_t* __restrict__ dst, int valid_cols) {
+  wave_lds_fence();
+  buf[stage_slot(co_local, 0)] = make_uint4(w[0], w[1], w[2], w[3]);
+  buf[stage_slot(co_local, 1)] = make_uint4(w[4], w[5], w[6], w[7]);
+  wave_lds_fence();
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int e = v * 512 + lane * 8;          // first column of this lane's piece
+    const uint4 t = buf[stage_slot(e >> 4, (e >> 3) & 1)];
+    if (e < valid_cols) reinterpret_cast<uint4*>(dst + e)[0] = t;
+  }
+}
+
+struct StageF32 {
   using T = float;
-  static __device__ __forceinline__ void store(float* __restrict__ p, const float x[16]) {
-    float4* q = reinterpret_cast<float4*>(p);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) q[v] = make_float4(x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]);
+  static __device__ __forceinline__ void store(uint4* buf, int lane, int co_local, const float x[16], float* dst,
+                                               int valid_cols) {
+    store_window_f32(buf, lane, co_local, x, dst, valid_cols);
   }
 };
 
-struct OutBF16 {
+struct StageBF16 {
   using T = uint16_t;
-  static __device__ __forceinline__ void store(uint16_t* __restrict__ p, const float x[16]) {
-    uint4* q = reinterpret_cast<uint4*>(p);
+  static __device__ __forceinline__ void store(uint4* buf, int lane, int co_local, const float x[16], uint16_t* dst,
+                                               int valid_cols) {
+    uint32_t w[8];
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = f32_to_bf16_bits(x[8 * v + 2 * i]) | (f32_to_bf16_bits(x[8 * v + 2 * i + 1]) << 16);
-      q[v] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
+    for (int i = 0; i < 8; ++i) w[i] = f32_to_bf16_bits(x[2 * i]) | (f32_to_bf16_bits(x[2 * i + 1]) << 16);
+    store_window_b16(buf, lane, co_local, w, dst, valid_cols);
   }
 };
 
-struct OutF16 {
+struct StageF16 {
   using T = uint16_t;
-  static __device__ __forceinline__ void store(uint16_t* __restrict__ p, const float x[16]) {
-    uint4* q = reinterpret_cast<uint4*>(p);
+  static __device__ __forceinline__ void store(uint4* buf, int lane, int co_local, const float x[16], uint16_t* dst,
+                                               int valid_cols) {
+    uint32_t w[8];
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = f32_to_f16_bits(x[8 * v + 2 * i]) | (f32_to_f16_bits(x[8 * v + 2 * i + 1]) << 16);
-      q[v] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
+    for (int i = 0; i < 8; ++i) w[i] = f32_to_f16_bits(x[2 * i]) | (f32_to_f16_bits(x[2 * i + 1]) << 16);
+    store_window_b16(buf, lane, co_local, w, dst, valid_cols);
   }
 };
 
 // ---------------------------------------------------------------------------
 // Unnormalised Walsh-Hadamard transform (Sylvester order) of every block of
-// 2^L elements held by the wavefront, block = b/16 adjacent lanes x 16
-// registers.  Element i of a block lives in lane (i >> 4) of its lane group,
-// register (i & 15); the result keeps that placement.  Requires 4 <= L <= 10.
+// b = 2^L elements held by the wavefront: a block is 2^(L-4) adjacent lanes
+// x 16 registers, element i in lane (i >> 4) of the group, register i & 15.
 //
-// In-lane stages pair registers r and r ^ h.  Cross-lane stages pair lanes a
-// and a ^ m; the lane whose bit m is set takes (partner - own), the other
-// (own + partner), both as one fma with a +-1 factor.
+// Register bits: four in-lane butterfly stages (registers r and r ^ h).
+// Lane bits: one butterfly stage per lane bit, each a single DPP-fed FMA.
+// DPP on gfx9 has no xor-4 / xor-8 lane pattern, so the lane stages pair
+// lanes a and a ^ m for m in {1, 2, 7, 15} (quad_perm, quad_perm,
+// row_half_mirror, row_mirror), then 16 and 32 (ds_bpermute) for b >= 512.
+// These masks form a basis of the lane-index space; with "lower/upper"
+// decided by the dual functionals lambda_i (parity(a & D_i), where
+// parity(D_i & m_j) = [i == j]) each stage is an exact Walsh-Hadamard
+// butterfly along one coordinate, so the network computes the Sylvester
+// transform up to a known relabelling of lanes and a per-lane sign:
+//
+//   lane a ends up holding  sign(a) * out[16 * G(a) + r],  r = 0..15,
+//   G(a) = XOR of D_i over the i with parity(a & D_i) = 1,
+//   sign(a) = (-1)^parity(a & (D_0 ^ D_1 ^ ...)).
+//
+// Stage i computes own + c_a * partner with c_a = (-1)^lambda_i(a); the
+// lanes with lambda_i(a) = 1 then hold the negated difference, which the
+// per-lane sign above accounts for.
 // ---------------------------------------------------------------------------
+constexpr int kLaneMasks[6] = {1, 2, 7, 15, 16, 32};
+
+constexpr int parity(int v) {
+  int p = 0;
+  while (v) { p ^= v & 1; v >>= 1; }
+  return p;
+}
+
+// D_i for a network over NB lane bits (brute force over the 2^NB functionals).
+constexpr int lane_dual(int NB, int i) {
+  for (int D = 0; D < (1 << NB); ++D) {
+    bool ok = true;
+    for (int j = 0; j < NB; ++j) ok = ok && (parity(D & kLaneMasks[j]) == (i == j ? 1 : 0));
+    if (ok) return D;
+  }
+  return -1;
+}
+
+constexpr int lane_sign_mask(int NB) {
+  int m = 0;
+  for (int i = 0; i < NB; ++i) m ^= lane_dual(NB, i);
+  return m;
+}
+
+// G(a): index (in 16-element chunks, within the block) of the outputs lane a holds.
+template <int NB, int I = 0>
+__device__ __forceinline__ int lane_out_chunk(int a) {
+  if constexpr (I < NB) {
+    constexpr int D = lane_dual(NB, I);
+    static_assert(D >= 0, "lane masks must form a basis");
+    return ((__builtin_popcount(a & D) & 1) ? D : 0) ^ lane_out_chunk<NB, I + 1>(a);
+  } else {
+    return 0;
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ float lane_out_sign(int a) {
+  constexpr int M = lane_sign_mask(NB);
+  return (__builtin_popcount(a & M) & 1) ? -1.0f : 1.0f;
+}
+
+// Partner value across lane bit 4 or 5 (b >= 512): ds_bpermute.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  static_assert(M == 16 || M == 32, "DPP covers the other masks");
+  return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, v), M));
+}
+
+// x[r] += c * x[r] of the partner lane, for all 16 registers, as single
+// v_fmac_f32 instructions with a DPP-routed src0.  The compiler does not fuse
+// a DPP move into v_fmac, hence the inline assembly (ALU only).  A VALU write
+// followed by a DPP read of the same VGPR needs two wait states: the leading
+// s_nop covers the previous stage; inside the block each instruction reads a
+// register last written 16 instructions earlier.
+#define QAMW_DPP_FMAC16(CTRL, x, c)                                                                      \
+  asm("s_nop 1\n"                                                                                         \
+      "v_fmac_f32_dpp %0, %0, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %1, %1, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %2, %2, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %3, %3, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %4, %4, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %5, %5, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %6, %6, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %7, %7, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %8, %8, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %9, %9, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %10, %10, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %11, %11, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %12, %12, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %13, %13, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %14, %14, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      "v_fmac_f32_dpp %15, %15, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"  \
+      : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),  \
+        "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]), "+v"(x[12]), "+v"(x[13]), "+v"(x[14]),         \
+        "+v"(x[15])                                                                                       \
+      : "v"(c))
+
+template <int I, int NB>
+__device__ __forceinline__ void lane_stage(float x[16], int a) {
+  if constexpr (I < NB) {
+    constexpr int D = lane_dual(NB, I);
+    constexpr int M = kLaneMasks[I];
+    const float c = (__builtin_popcount(a & D) & 1) ? -1.0f : 1.0f;
+    if constexpr (M == 1) {
+      QAMW_DPP_FMAC16("quad_perm:[1,0,3,2]", x, c);
+    } else if constexpr (M == 2) {
+      QAMW_DPP_FMAC16("quad_perm:[2,3,0,1]", x, c);
+    } else if constexpr (M == 7) {
+      QAMW_DPP_FMAC16("row_half_mirror", x, c);
+    } else if constexpr (M == 15) {
+      QAMW_DPP_FMAC16("row_mirror", x, c);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = __builtin_fmaf(lane_xor<M>(x[r]), c, x[r]);
+    }
+    lane_stage<I + 1, NB>(x, a);
+  }
+}
+
+// In-register stages plus the lane network; BlockOut says where each lane's
+// outputs land.  `lane` is the lane index in the wavefront.
 template <int L>
 __device__ __forceinline__ void fwht_block(float x[16], int lane) {
   static_assert(L >= 4 && L <= 10, "block size must be 16..1024");
@@ -137,17 +299,20 @@ __device__ __forceinline__ void fwht_block(float x[16], int lane) {
       }
     }
   }
-#pragma unroll
-  for (int t = 0; t < L - 4; ++t) {
-    const int m = 1 << t;
-    const float sgn = (lane & m) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p = __shfl_xor(x[i], m);
-      x[i] = __builtin_fmaf(x[i], sgn, p);
-    }
-  }
+  lane_stage<0, L - 4>(x, lane & ((1 << (L - 4)) - 1));
 }
+
+// Block-relative placement of a lane's outputs after fwht_block<L>.
+template <int L>
+struct BlockOut {
+  static constexpr int NB = L - 4;
+  // chunk index (within the wavefront window) holding this lane's outputs
+  static __device__ __forceinline__ int chunk(int lane) {
+    const int a = lane & ((1 << NB) - 1);
+    return (lane - a) + lane_out_chunk<NB>(a);
+  }
+  static __device__ __forceinline__ float sign(int lane) { return lane_out_sign<NB>(lane & ((1 << NB) - 1)); }
+};
 
 // fp64 -> IEEE binary16 bits with one round-to-nearest-even step.
 __device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {

@@ -121,7 +121,8 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
   const int win = gw % nwin;
   const int tile = gw / nwin;
   const int c = win * kWinChunks + lane;
-  const bool active = c < nchunks;
+  const bool active = c < nchunks;   // whole Hadamard blocks are active or not
+  const int co = win * kWinChunks + BlockOut<L>::chunk(lane);
   const double sqrt_b = sqrt((double)(1 << L));
 
   float f[16];
@@ -132,16 +133,13 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
 
   const int n0 = tile * kCalibRowsPerTile;
   const int n1 = min(N, n0 + kCalibRowsPerTile);
+  float nxt[16];
+  if (active) load_chunk(W + (int64_t)n0 * ldw + c * kChunk, nxt);
   for (int n = n0; n < n1; ++n) {
     float x[16];
-    if (active) {
-      load_chunk(W + (int64_t)n * ldw + c * kChunk, x);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] *= f[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = 0.0f;
-    }
+    for (int i = 0; i < 16; ++i) x[i] = active ? nxt[i] * f[i] : 0.0f;
+    if (active && n + 1 < n1) load_chunk(W + (int64_t)(n + 1) * ldw + c * kChunk, nxt);
     fwht_block<L>(x, lane);
     const double r = rho[n];
     const float inv = r > 0.0 ? (float)(1.0 / (sqrt_b * r)) : 0.0f;
@@ -152,20 +150,33 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
     }
   }
   if (active) {
-    float4* out = reinterpret_cast<float4*>(partial + (int64_t)tile * (d >> 1) + c * kPairsPerLane);
+    float4* out = reinterpret_cast<float4*>(partial + (int64_t)tile * (d >> 1) + co * kPairsPerLane);
     out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
 }
 
-// sigma_k = (sum over tiles, in tile order, fp64) / (N sqrt(pi/2)).
+// sigma_k = (sum over tiles, fp64, fixed order) / (N sqrt(pi/2)).  A
+// workgroup owns 16 columns; thread (column, slice) sums tiles slice,
+// slice + 16, ... and the 16 slice sums are then added in slice order.
+constexpr int kSigmaSlices = 16;
 __global__ __launch_bounds__(kBlockThreads) void sigma_kernel(const float* __restrict__ partial, int ntiles,
                                                               int half_d, int N, float* __restrict__ sigma) {
-  const int k = blockIdx.x * kBlockThreads + threadIdx.x;
-  if (k >= half_d) return;
+  __shared__ double part[kSigmaSlices][kBlockThreads / kSigmaSlices];
+  const int col_in = threadIdx.x % (kBlockThreads / kSigmaSlices);
+  const int slice = threadIdx.x / (kBlockThreads / kSigmaSlices);
+  const int k = blockIdx.x * (kBlockThreads / kSigmaSlices) + col_in;
   double acc = 0.0;
-  for (int t = 0; t < ntiles; ++t) acc += (double)partial[(int64_t)t * half_d + k];
-  sigma[k] = (float)(acc / ((double)N * 1.2533141373155002512078826));  // sqrt(pi/2)
+  if (k < half_d)
+    for (int t = slice; t < ntiles; t += kSigmaSlices) acc += (double)partial[(int64_t)t * half_d + k];
+  part[slice][col_in] = acc;
+  __syncthreads();
+  if (slice == 0 && k < half_d) {
+    double tot = 0.0;
+#pragma unroll
+    for (int q = 0; q < kSigmaSlices; ++q) tot += part[q][col_in];
+    sigma[k] = (float)(tot / ((double)N * 1.2533141373155002512078826));  // sqrt(pi/2)
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -184,7 +195,7 @@ __global__ __launch_bounds__(kBlockThreads) void sigma_kernel(const float* __res
 // minimum bit for bit is taken.
 // ---------------------------------------------------------------------------
 template <int L, typename Tin>
-__global__ __launch_bounds__(kBlockThreads) void encode_kernel(
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void encode_kernel(
     const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ s,
     const float* __restrict__ sigma, uint64_t seed, const float* __restrict__ codebook, int K, int Kpad,
     int B, int row_words, const double* __restrict__ rho, uint32_t* __restrict__ packed) {
@@ -233,15 +244,19 @@ __global__ __launch_bounds__(kBlockThreads) void encode_kernel(
     for (int i = 0; i < 16; ++i) x[i] = 0.0f;
   }
   fwht_block<L>(x, lane);
+  // the lane now holds (sign * ) the rotated pairs of chunk co_local of the window
+  const int co_local = BlockOut<L>::chunk(lane);
+  const int co = win * kWinChunks + co_local;
 
   // ---- z~ = y / sigma_k with y = x / (sqrt(b) rho)
   float zx[8], zy[8];
   {
     const double r = has_work ? rho[n] : 0.0;
     const double sqrt_b = sqrt((double)(1 << L));
+    const float osign = BlockOut<L>::sign(lane);
     float sg[8];
     if (active) {
-      const float4* sp = reinterpret_cast<const float4*>(sigma + c * kPairsPerLane);
+      const float4* sp = reinterpret_cast<const float4*>(sigma + co * kPairsPerLane);
       const float4 s0 = sp[0], s1 = sp[1];
       sg[0] = s0.x; sg[1] = s0.y; sg[2] = s0.z; sg[3] = s0.w;
       sg[4] = s1.x; sg[5] = s1.y; sg[6] = s1.z; sg[7] = s1.w;
@@ -251,7 +266,7 @@ __global__ __launch_bounds__(kBlockThreads) void encode_kernel(
     }
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-      const float inv = pair_normaliser(r, sg[p], sqrt_b);
+      const float inv = pair_normaliser(r, sg[p], sqrt_b) * osign;
       zx[p] = x[2 * p] * inv;
       zy[p] = x[2 * p + 1] * inv;
     }
@@ -303,7 +318,7 @@ __global__ __launch_bounds__(kBlockThreads) void encode_kernel(
 
   // ---- pack: the window's pairs own whole words [16*B*win, 16*B*(win+1))
 #pragma unroll
-  for (int p = 0; p < 8; ++p) stage[lane * kPairsPerLane + p] = (uint16_t)idx[p];
+  for (int p = 0; p < 8; ++p) stage[co_local * kPairsPerLane + p] = (uint16_t)idx[p];
   __syncthreads();
   if (!has_work) return;
   const int half_d = d >> 1;
@@ -326,90 +341,129 @@ __global__ __launch_bounds__(kBlockThreads) void encode_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Decode.  One wavefront per (window, group of rows_per_wave rows); the
-// lane's column factors g_j = eps_j / (sqrt(b) s_j) and sigma_k are formed
-// once and reused for every row of the group.
+// Decode.  A workgroup owns one 1024-column window and 4 * rows_per_wave
+// rows; each wavefront walks rows_per_wave consecutive rows.  The workgroup
+// stages the codebook (K x float2) and the window's column factors
+// g_j = eps_j / (sqrt(b) s_j) in LDS once; each lane keeps its 8 sigma_k and
+// its 16 factors in registers, and prefetches the next row's packed words
+// while it decodes the current row.  BT > 0 fixes the index width at compile
+// time (BT = 0: width B from the argument).
 // ---------------------------------------------------------------------------
-template <int L, typename Out>
+template <int BT>
+__device__ __forceinline__ void unpack8(const uint32_t w[4], uint32_t sh, int Bdyn, uint32_t idx[8]) {
+  const int B = BT ? BT : Bdyn;
+  const uint32_t mask = (1u << B) - 1u;
+  // the lane's 8*B bits, starting at bit 0 of a[0]
+  const uint32_t a[3] = {__builtin_amdgcn_alignbit(w[1], w[0], sh), __builtin_amdgcn_alignbit(w[2], w[1], sh),
+                         __builtin_amdgcn_alignbit(w[3], w[2], sh)};
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int o = p * B;
+    const int q = o >> 5;
+    const uint32_t lo = (q == 0) ? a[0] : ((q == 1) ? a[1] : a[2]);
+    const uint32_t hi = (q == 0) ? a[1] : ((q == 1) ? a[2] : 0u);
+    idx[p] = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(o & 31)) & mask;
+  }
+}
+
+template <int L, int BT, typename Out>
 __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
     const uint32_t* __restrict__ packed, const uint16_t* __restrict__ rho_f16, int N, int d,
     const float* __restrict__ s, const float* __restrict__ sigma, uint64_t seed,
-    const float* __restrict__ codebook, int K, int B, int row_words, int rows_per_wave,
+    const float* __restrict__ codebook, int K, int Bdyn, int row_words, int rows_per_wave,
     typename Out::T* __restrict__ out, int64_t ldo) {
   extern __shared__ float4 lds4[];
-  float2* cb = reinterpret_cast<float2*>(lds4);
+  uint4* stage_all = reinterpret_cast<uint4*>(lds4);    // 4 waves x 256 x 16 bytes
+  float* gwin = reinterpret_cast<float*>(stage_all + kWavesPerBlock * 256);  // kWinChunks * kChunk factors
+  float2* cb = reinterpret_cast<float2*>(gwin + kWinChunks * kChunk);
+
+  const int nchunks = d >> 4;
+  const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
+  const int win = blockIdx.x % nwin;
+  const int rblk = blockIdx.x / nwin;
+
   for (int c = threadIdx.x; c < K; c += kBlockThreads)
     cb[c] = make_float2(codebook[2 * c], codebook[2 * c + 1]);
+  {
+    const float inv_sqrt_b = (float)(1.0 / sqrt((double)(1 << L)));
+    for (int t = threadIdx.x; t < kWinChunks * kChunk; t += kBlockThreads) {
+      const int j = win * kWinChunks * kChunk + t;
+      gwin[t] = (j < d) ? sign_eps(seed, j) * (inv_sqrt_b / (s ? s[j] : 1.0f)) : 0.0f;
+    }
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int nchunks = d >> 4;
-  const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
-  const int ngroups = (N + rows_per_wave - 1) / rows_per_wave;
-  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (gw >= nwin * ngroups) return;
-  const int win = gw % nwin;
-  const int grp = gw / nwin;
+  const int wave = threadIdx.x >> 6;
+  uint4* stage = stage_all + wave * 256;
   const int c = win * kWinChunks + lane;
+  const int valid_cols = d - win * kWinChunks * kChunk;
+  // Lanes past the row end hold zeros but stay: the window store reads back
+  // columns for every lane of the wave.
   const bool active = c < nchunks;
+  const int co_local = BlockOut<L>::chunk(lane);
+  const int co = win * kWinChunks + co_local;
 
-  float g[16], sg[8];
-  if (active) {
-    const float inv_sqrt_b = (float)(1.0 / sqrt((double)(1 << L)));
+  float g[16];
+  {
+    const float osign = BlockOut<L>::sign(lane);
+    const float4* gp = reinterpret_cast<const float4*>(gwin + co_local * kChunk);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = c * kChunk + i;
-      const float sj = s ? s[j] : 1.0f;
-      g[i] = sign_eps(seed, j) * (inv_sqrt_b / sj);
+    for (int v = 0; v < 4; ++v) {
+      const float4 t = gp[v];
+      g[4 * v + 0] = t.x * osign; g[4 * v + 1] = t.y * osign;
+      g[4 * v + 2] = t.z * osign; g[4 * v + 3] = t.w * osign;
     }
-#pragma unroll
-    for (int p = 0; p < 8; ++p) sg[p] = sigma[c * kPairsPerLane + p];
+  }
+  float sg[8];
+  if (active) {
+    const float4* sp = reinterpret_cast<const float4*>(sigma + c * kPairsPerLane);
+    const float4 s0 = sp[0], s1 = sp[1];
+    sg[0] = s0.x; sg[1] = s0.y; sg[2] = s0.z; sg[3] = s0.w;
+    sg[4] = s1.x; sg[5] = s1.y; sg[6] = s1.z; sg[7] = s1.w;
   } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) g[i] = 0.0f;
 #pragma unroll
     for (int p = 0; p < 8; ++p) sg[p] = 0.0f;
   }
 
+  const int B = BT ? BT : Bdyn;
   const int64_t bitstart = (int64_t)c * kPairsPerLane * B;
   const int wstart = (int)(bitstart >> 5);
   const uint32_t sh = (uint32_t)(bitstart & 31);
-  const uint32_t mask = (1u << B) - 1u;
-  const int n0 = grp * rows_per_wave;
+  int widx[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) widx[i] = min(wstart + i, row_words - 1);
+
+  const int n0 = (rblk * kWavesPerBlock + wave) * rows_per_wave;
   const int n1 = min(N, n0 + rows_per_wave);
+  if (n0 >= n1) return;
+  uint32_t wn[4] = {0u, 0u, 0u, 0u};
+  if (active) {
+    const uint32_t* rw = packed + (int64_t)n0 * row_words;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wn[i] = rw[widx[i]];
+  }
   for (int n = n0; n < n1; ++n) {
+    uint32_t w[4] = {wn[0], wn[1], wn[2], wn[3]};
+    if (active && n + 1 < n1) {
+      const uint32_t* rw = packed + (int64_t)(n + 1) * row_words;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wn[i] = rw[widx[i]];
+    }
+    uint32_t idx[8];
+    unpack8<BT>(w, sh, Bdyn, idx);
     float x[16];
-    if (active) {
-      const uint32_t* rw = packed + (int64_t)n * row_words;
-      uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = rw[min(wstart + i, row_words - 1)];
-      // the lane's 8*B bits, starting at bit 0 of a[0]
-      const uint32_t a[3] = {__builtin_amdgcn_alignbit(w[1], w[0], sh),
-                             __builtin_amdgcn_alignbit(w[2], w[1], sh),
-                             __builtin_amdgcn_alignbit(w[3], w[2], sh)};
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const int o = p * B;
-        const int q = o >> 5;
-        const uint32_t lo = (q == 0) ? a[0] : ((q == 1) ? a[1] : a[2]);
-        const uint32_t hi = (q == 0) ? a[1] : ((q == 1) ? a[2] : 0u);
-        const uint32_t v = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(o & 31)) & mask;
-        const float2 cc = cb[min((int)v, K - 1)];
-        x[2 * p] = cc.x * sg[p];
-        x[2 * p + 1] = cc.y * sg[p];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = 0.0f;
+    for (int p = 0; p < 8; ++p) {
+      const float2 cc = cb[min((int)idx[p], K - 1)];
+      x[2 * p] = cc.x * sg[p];
+      x[2 * p + 1] = cc.y * sg[p];
     }
     fwht_block<L>(x, lane);
-    if (active) {
-      const float rh = f16_bits_to_f32(rho_f16[n]);
+    const float rh = f16_bits_to_f32(rho_f16[n]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = (x[i] * rh) * g[i];
-      Out::store(out + (int64_t)n * ldo + c * kChunk, x);
-    }
+    for (int i = 0; i < 16; ++i) x[i] = (x[i] * rh) * g[i];
+    Out::store(stage, lane, co_local, x, out + (int64_t)n * ldo + win * kWinChunks * kChunk, valid_cols);
   }
 }
 
@@ -514,29 +568,48 @@ struct LaunchEncode {
   }
 };
 
+template <int L, int BT>
+int launch_decode_bt(const uint32_t* packed, const uint16_t* rho_f16, int N, int d, const float* s,
+                     const float* sigma, uint64_t seed, const float* cb, int K, int B, int row_words, void* out,
+                     int32_t odt, int64_t ldo, hipStream_t st) {
+  const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
+  // about 32 wavefronts of work per CU on 256 CUs; each walks rows_per_wave rows
+  const int64_t target = 256 * 32;
+  int rows_per_wave = (int)(((int64_t)N * nwin + target - 1) / target);
+  rows_per_wave = rows_per_wave < 1 ? 1 : (rows_per_wave > 64 ? 64 : rows_per_wave);
+  const int64_t rows_per_block = (int64_t)rows_per_wave * kWavesPerBlock;
+  const int64_t blocks = (int64_t)nwin * ((N + rows_per_block - 1) / rows_per_block);
+  const size_t lds = (size_t)kWavesPerBlock * 256 * 16 + (size_t)kWinChunks * kChunk * sizeof(float) +
+                     (size_t)K * sizeof(float2);
+  const dim3 grid((unsigned)blocks), blk(kBlockThreads);
+  if (odt == QAMW_F32)
+    hipLaunchKernelGGL((decode_kernel<L, BT, StageF32>), grid, blk, lds, st, packed, rho_f16, N, d, s, sigma, seed,
+                       cb, K, B, row_words, rows_per_wave, (float*)out, ldo);
+  else if (odt == QAMW_BF16)
+    hipLaunchKernelGGL((decode_kernel<L, BT, StageBF16>), grid, blk, lds, st, packed, rho_f16, N, d, s, sigma,
+                       seed, cb, K, B, row_words, rows_per_wave, (uint16_t*)out, ldo);
+  else
+    hipLaunchKernelGGL((decode_kernel<L, BT, StageF16>), grid, blk, lds, st, packed, rho_f16, N, d, s, sigma, seed,
+                       cb, K, B, row_words, rows_per_wave, (uint16_t*)out, ldo);
+  return check_launch("decode_kernel");
+}
+
 template <int L>
 struct LaunchDecode {
   static int run(const uint32_t* packed, const uint16_t* rho_f16, int N, int d, const float* s, const float* sigma,
                  uint64_t seed, const float* cb, int K, int B, int row_words, void* out, int32_t odt, int64_t ldo,
                  hipStream_t st) {
-    const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
-    // about 16 wavefronts per CU on 256 CUs; each walks rows_per_wave rows
-    const int64_t target = 256 * 16;
-    int rows_per_wave = (int)(((int64_t)N * nwin + target - 1) / target);
-    rows_per_wave = rows_per_wave < 1 ? 1 : (rows_per_wave > 64 ? 64 : rows_per_wave);
-    const int64_t waves = (int64_t)nwin * ((N + rows_per_wave - 1) / rows_per_wave);
-    const size_t lds = (size_t)K * sizeof(float2);
-    const dim3 grid(grid_for_waves(waves)), blk(kBlockThreads);
-    if (odt == QAMW_F32)
-      hipLaunchKernelGGL((decode_kernel<L, OutF32>), grid, blk, lds, st, packed, rho_f16, N, d, s, sigma, seed, cb,
-                         K, B, row_words, rows_per_wave, (float*)out, ldo);
-    else if (odt == QAMW_BF16)
-      hipLaunchKernelGGL((decode_kernel<L, OutBF16>), grid, blk, lds, st, packed, rho_f16, N, d, s, sigma, seed, cb,
-                         K, B, row_words, rows_per_wave, (uint16_t*)out, ldo);
-    else
-      hipLaunchKernelGGL((decode_kernel<L, OutF16>), grid, blk, lds, st, packed, rho_f16, N, d, s, sigma, seed, cb,
-                         K, B, row_words, rows_per_wave, (uint16_t*)out, ldo);
-    return check_launch("decode_kernel");
+    // compile-time index widths for the common rates (K = 256, 1024, 2048, 4096)
+    if constexpr (L == 7 || L == 8) {
+      switch (B) {
+        case 8: return launch_decode_bt<L, 8>(packed, rho_f16, N, d, s, sigma, seed, cb, K, B, row_words, out, odt, ldo, st);
+        case 10: return launch_decode_bt<L, 10>(packed, rho_f16, N, d, s, sigma, seed, cb, K, B, row_words, out, odt, ldo, st);
+        case 11: return launch_decode_bt<L, 11>(packed, rho_f16, N, d, s, sigma, seed, cb, K, B, row_words, out, odt, ldo, st);
+        case 12: return launch_decode_bt<L, 12>(packed, rho_f16, N, d, s, sigma, seed, cb, K, B, row_words, out, odt, ldo, st);
+        default: break;
+      }
+    }
+    return launch_decode_bt<L, 0>(packed, rho_f16, N, d, s, sigma, seed, cb, K, B, row_words, out, odt, ldo, st);
   }
 };
 
@@ -641,7 +714,8 @@ int32_t qamw_calibrate(const void* W, int32_t wdtype, int64_t N, int64_t d, int6
                                          partial, st)))
     return rc;
   const int half_d = dd / 2;
-  hipLaunchKernelGGL(sigma_kernel, dim3((half_d + kBlockThreads - 1) / kBlockThreads), dim3(kBlockThreads), 0, st,
+  const int sigma_cols = kBlockThreads / kSigmaSlices;
+  hipLaunchKernelGGL(sigma_kernel, dim3((half_d + sigma_cols - 1) / sigma_cols), dim3(kBlockThreads), 0, st,
                      (const float*)partial, (int)calib_tiles(N), half_d, n, sigma_out);
   return check_launch("sigma_kernel");
 }
