@@ -40,8 +40,8 @@
  *     call only enqueues kernels on it and returns; results are valid once
  *     the stream has reached that point.  In-place calls are not supported
  *     (outputs must not alias inputs).
- *   - W, W_out and packed must be 16-byte aligned, and ldw / ldo rows must keep
- *     16-byte alignment (ldw * element size % 16 == 0).
+ *   - W, W_out, packed, codebook, s and sigma must be 16-byte aligned, and
+ *     ldw / ldo rows must keep 16-byte alignment (ldw * element size % 16 == 0).
  *
  * Errors
  *   Arguments are validated on the host before anything is launched; on a

@@ -97,7 +97,7 @@ def _decode(lib, **kw):
     (dict(N=0), -1), (dict(d=-16), -1), (dict(K=1), -2), (dict(K=4097), -2), (dict(ldw=128), -1),
     (dict(W=None), -1), (dict(cb=None), -1), (dict(s=None), -1), (dict(packed=None), -1),
     (dict(W=MIS), -1), (dict(packed=MIS), -1), (dict(wdt=2), -2), (dict(ldw=260), -1),
-    (dict(ws=None), -4), (dict(ws_bytes=8), -4), (dict(ws=WS + 16), -4),
+    (dict(ws=None), -4), (dict(ws_bytes=8), -4), (dict(ws=WS + 16), -4), (dict(cb=MIS), -1),
 ])
 def test_encode_rejects(lib, kw, status):
     assert _encode(lib, **kw) == status
@@ -114,7 +114,7 @@ def test_calibrate_rejects(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(odt=3), -2), (dict(ldo=100), -1), (dict(out=MIS), -1), (dict(rn=None), -1),
-    (dict(K=5000), -2), (dict(block=64, d=96), -1), (dict(odt=1, ldo=260), -1),
+    (dict(K=5000), -2), (dict(block=64, d=96), -1), (dict(odt=1, ldo=260), -1), (dict(cb=MIS), -1),
 ])
 def test_decode_rejects(lib, kw, status):
     assert _decode(lib, **kw) == status

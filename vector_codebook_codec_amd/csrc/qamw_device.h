@@ -85,6 +85,20 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
 // complete in order, and the fences keep the compiler from reordering the
 // cross-lane accesses.
 // ---------------------------------------------------------------------------
+// Output stores stream through L2: non-temporal by default.
+#ifndef QAMW_NT_STORES
+#define QAMW_NT_STORES 1
+#endif
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16(void* dst, uint4 t) {
+#if QAMW_NT_STORES
+  const u32x4 v = {t.x, t.y, t.z, t.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+#else
+  *reinterpret_cast<uint4*>(dst) = t;
+#endif
+}
+
 __device__ __forceinline__ int stage_slot(int chunk, int q) {  // q: 16-byte piece of the chunk (0..3)
   return chunk * 4 + (q ^ ((chunk >> 2) & 3));
 }
@@ -106,11 +120,16 @@ __device__ __forceinline__ void store_window_f32(uint4* buf, int lane, int co_lo
     buf[stage_slot(co_local, q)] = make_uint4(__float_as_uint(x[4 * q]), __float_as_uint(x[4 * q + 1]),
                                               __float_as_uint(x[4 * q + 2]), __float_as_uint(x[4 * q + 3]));
   wave_lds_fence();
+  uint4 t[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {                 // all reads first: one LDS wait
+    const int e = v * 256 + lane * 4;          // first column of this lane's piece
+    t[v] = buf[stage_slot(e >> 4, (e >> 2) & 3)];
+  }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int e = v * 256 + lane * 4;          // first column of this lane's piece
-    const uint4 t = buf[stage_slot(e >> 4, (e >> 2) & 3)];
-    if (e < valid_cols) reinterpret_cast<uint4*>(dst + e)[0] = t;
+    const int e = v * 256 + lane * 4;
+    if (e < valid_cols) store16(dst + e, t[v]);
   }
 }
 
@@ -121,11 +140,16 @@ __device__ __forceinline__ void store_window_b16(uint4* buf, int lane, int co_lo
   buf[stage_slot(co_local, 0)] = make_uint4(w[0], w[1], w[2], w[3]);
   buf[stage_slot(co_local, 1)] = make_uint4(w[4], w[5], w[6], w[7]);
   wave_lds_fence();
+  uint4 t[2];
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
     const int e = v * 512 + lane * 8;          // first column of this lane's piece
-    const uint4 t = buf[stage_slot(e >> 4, (e >> 3) & 1)];
-    if (e < valid_cols) reinterpret_cast<uint4*>(dst + e)[0] = t;
+    t[v] = buf[stage_slot(e >> 4, (e >> 3) & 1)];
+  }
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int e = v * 512 + lane * 8;
+    if (e < valid_cols) store16(dst + e, t[v]);
   }
 }
 

@@ -31,7 +31,16 @@ namespace qamw {
 constexpr int kBlockThreads = 256;                   // 4 wavefronts per workgroup
 constexpr int kWavesPerBlock = kBlockThreads / kWave;
 constexpr int kCalibRowsPerTile = 16;                // rows per amplitude partial sum
-constexpr int kArgminChunk = 32;                     // centroids per min-tracking chunk
+
+// Decode tunables: rows whose packed words are loaded ahead, and wavefronts
+// of work per CU the launch aims for (each wave then walks several rows).
+#ifndef QAMW_DECODE_PREFETCH
+#define QAMW_DECODE_PREFETCH 4
+#endif
+#ifndef QAMW_DECODE_WAVES_PER_CU
+#define QAMW_DECODE_WAVES_PER_CU 16
+#endif
+constexpr int kDecodePrefetch = QAMW_DECODE_PREFETCH;
 
 // ---------------------------------------------------------------------------
 // s_j = r_j ^ alpha.  alpha = 0 gives exactly 1.
@@ -133,6 +142,12 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
 
   const int n0 = tile * kCalibRowsPerTile;
   const int n1 = min(N, n0 + kCalibRowsPerTile);
+  // 1 / (sqrt(b) rho_n) of the tile's rows, one per lane
+  float inv_lane = 0.0f;
+  if (lane < n1 - n0) {
+    const double r = rho[n0 + lane];
+    inv_lane = r > 0.0 ? (float)(1.0 / (sqrt_b * r)) : 0.0f;
+  }
   float nxt[16];
   if (active) load_chunk(W + (int64_t)n0 * ldw + c * kChunk, nxt);
   for (int n = n0; n < n1; ++n) {
@@ -141,8 +156,7 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
     for (int i = 0; i < 16; ++i) x[i] = active ? nxt[i] * f[i] : 0.0f;
     if (active && n + 1 < n1) load_chunk(W + (int64_t)(n + 1) * ldw + c * kChunk, nxt);
     fwht_block<L>(x, lane);
-    const double r = rho[n];
-    const float inv = r > 0.0 ? (float)(1.0 / (sqrt_b * r)) : 0.0f;
+    const float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv_lane), n - n0));
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const float a = x[2 * p], b = x[2 * p + 1];
@@ -180,22 +194,34 @@ __global__ __launch_bounds__(kBlockThreads) void sigma_kernel(const float* __res
 }
 
 // ---------------------------------------------------------------------------
-// Encode.  One wavefront per (row, window); 8 pairs per lane.
+// Encode.  One wavefront per (row, window): 512 pairs; eight wavefronts per
+// workgroup share one copy of the codebook in LDS.
 //
 // Nearest centroid on the expanded score S_c = |c|^2/2 - z.c, which orders
-// centroids exactly as |z - c|^2 does.  The codebook sits in LDS as three
-// arrays (-cx, -cy, |c|^2/2), padded to a multiple of kArgminChunk with
-// S = +inf; every lane reads the same centroid (broadcast), so each
-// (pair, centroid) costs two fp32 FMAs and half a v_min3.
+// centroids exactly as |z - c|^2 does.  The scores of 32 centroids x 32 pairs
+// are one v_mfma_f32_32x32x2_f32:  A[i][k] = (-cx_i, -cy_i),  B[k][j] =
+// (zx_j, zy_j),  C[i][j] = |c_i|^2 / 2.  That instruction computes
+// fma(A[i][1], B[1][j], fma(A[i][0], B[0][j], C[i][j])) in fp32 -- exactly
+// the VALU sequence fma(zy, -cy, fma(zx, -cx, h)) -- so every score is
+// reproducible on the VALU bit for bit.
 //
-// Lowest-index ties: a running minimum is kept per pair; at the end of each
-// chunk of kArgminChunk centroids the chunk is recorded if the minimum
-// dropped strictly.  Afterwards the recorded chunk is rescanned with the
-// identical FMA sequence and the first centroid whose score equals the
-// minimum bit for bit is taken.
+// Accumulator layout (32x32 fp32 MFMA): lane l, register r holds row
+// (r & 3) + 8 (r >> 2) + 4 (l >> 5), column l & 31.  Each lane therefore sees
+// 16 of a tile's 32 centroids for one pair, folds them into a running minimum
+// with v_min3, and records the tile whenever that minimum drops strictly.
+// Afterwards the two half-waves' minima are combined, and the recorded tile is
+// rescanned on the VALU to find the first centroid whose score equals the
+// minimum: exact ties go to the lowest index.
 // ---------------------------------------------------------------------------
+constexpr int kEncThreads = 512;                       // 8 wavefronts per workgroup
+constexpr int kEncWaves = kEncThreads / kWave;
+constexpr int kTile = 32;                              // centroids per MFMA tile
+constexpr int kPairSets = kWinPairs / 32;              // 16 MFMA columns blocks per window
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 template <int L, typename Tin>
-__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void encode_kernel(
+__global__ __launch_bounds__(kEncThreads) void encode_kernel(
     const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ s,
     const float* __restrict__ sigma, uint64_t seed, const float* __restrict__ codebook, int K, int Kpad,
     int B, int row_words, const double* __restrict__ rho, uint32_t* __restrict__ packed) {
@@ -203,9 +229,9 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
   float* cbx = reinterpret_cast<float*>(lds4);   // -cx
   float* cby = cbx + Kpad;                       // -cy
   float* cbh = cby + Kpad;                       // |c|^2 / 2
-  uint16_t* stage_all = reinterpret_cast<uint16_t*>(cbh + Kpad);
+  float2* zall = reinterpret_cast<float2*>(cbh + Kpad);
 
-  for (int c = threadIdx.x; c < Kpad; c += kBlockThreads) {
+  for (int c = threadIdx.x; c < Kpad; c += kEncThreads) {
     if (c < K) {
       const float cx = codebook[2 * c], cy = codebook[2 * c + 1];
       cbx[c] = -cx;
@@ -221,15 +247,15 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
-  uint16_t* stage = stage_all + wave * kWinPairs;
+  float2* zbuf = zall + wave * kWinPairs;         // the window's normalised pairs, window order
   const int nchunks = d >> 4;
   const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
-  const int gw = blockIdx.x * kWavesPerBlock + wave;
-  const bool has_work = (int64_t)gw < (int64_t)N * nwin;
-  const int n = has_work ? gw / nwin : 0;
-  const int win = has_work ? gw % nwin : 0;
+  const int gw = blockIdx.x * kEncWaves + wave;
+  if ((int64_t)gw >= (int64_t)N * nwin) return;   // no barriers follow
+  const int n = gw / nwin;
+  const int win = gw % nwin;
   const int c = win * kWinChunks + lane;
-  const bool active = has_work && c < nchunks;
+  const bool active = c < nchunks;
 
   // ---- rotate the lane's 16 columns: x = H_b (eps . s . w) (unnormalised)
   float x[16];
@@ -244,14 +270,12 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     for (int i = 0; i < 16; ++i) x[i] = 0.0f;
   }
   fwht_block<L>(x, lane);
-  // the lane now holds (sign * ) the rotated pairs of chunk co_local of the window
-  const int co_local = BlockOut<L>::chunk(lane);
+  const int co_local = BlockOut<L>::chunk(lane);   // the lane now holds (sign *) chunk co_local
   const int co = win * kWinChunks + co_local;
 
-  // ---- z~ = y / sigma_k with y = x / (sqrt(b) rho)
-  float zx[8], zy[8];
+  // ---- z~ = y / sigma_k with y = x / (sqrt(b) rho), into the wave's LDS buffer
   {
-    const double r = has_work ? rho[n] : 0.0;
+    const double r = rho[n];
     const double sqrt_b = sqrt((double)(1 << L));
     const float osign = BlockOut<L>::sign(lane);
     float sg[8];
@@ -267,60 +291,96 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const float inv = pair_normaliser(r, sg[p], sqrt_b) * osign;
-      zx[p] = x[2 * p] * inv;
-      zy[p] = x[2 * p + 1] * inv;
+      zbuf[co_local * kPairsPerLane + p] = make_float2(x[2 * p] * inv, x[2 * p + 1] * inv);
     }
   }
+  wave_lds_fence();
 
-  // ---- nearest centroid
-  float best[8];
-  int chunk_of_best[8];
+  // ---- MFMA operands: B column block ps = window pairs [32 ps, 32 ps + 32)
+  const int half = lane >> 5;                      // 0: k = 0 (x), 1: k = 1 (y)
+  const int jcol = lane & 31;
+  float bop[kPairSets];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) { best[p] = INFINITY; chunk_of_best[p] = 0; }
+  for (int ps = 0; ps < kPairSets; ++ps) {
+    const float2 z = zbuf[ps * 32 + jcol];
+    bop[ps] = half ? z.y : z.x;
+  }
+  const float* abase = (half ? cby : cbx) + jcol;  // A[i][k]: row i = jcol of the tile
+  const float* hbase = cbh + 4 * half;             // C rows of this half-wave
 
-  for (int c0 = 0; c0 < Kpad; c0 += kArgminChunk) {
-    float run[8];
+  float best[kPairSets];
+  int tile_of_best[kPairSets];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) run[p] = best[p];
-#pragma unroll 2
-    for (int cc = 0; cc < kArgminChunk; cc += 4) {
-      const float4 ax = *reinterpret_cast<const float4*>(cbx + c0 + cc);
-      const float4 ay = *reinterpret_cast<const float4*>(cby + c0 + cc);
-      const float4 ah = *reinterpret_cast<const float4*>(cbh + c0 + cc);
+  for (int ps = 0; ps < kPairSets; ++ps) { best[ps] = INFINITY; tile_of_best[ps] = 0; }
+
+  // Software pipeline: the MFMA of column block ps runs while the VALU folds
+  // the scores of block ps - 1 (two accumulator sets); the next tile's A and C
+  // operands are loaded during the current tile.
+  auto fold = [&](const f32x16& dsc, int ps, int c0) {
+    float m = best[ps];
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const float s0 = __builtin_fmaf(zy[p], ay.x, __builtin_fmaf(zx[p], ax.x, ah.x));
-        const float s1 = __builtin_fmaf(zy[p], ay.y, __builtin_fmaf(zx[p], ax.y, ah.y));
-        const float s2 = __builtin_fmaf(zy[p], ay.z, __builtin_fmaf(zx[p], ax.z, ah.z));
-        const float s3 = __builtin_fmaf(zy[p], ay.w, __builtin_fmaf(zx[p], ax.w, ah.w));
-        run[p] = fminf(fminf(run[p], s0), s1);  // v_min3_f32
-        run[p] = fminf(fminf(run[p], s2), s3);
-      }
+    for (int r = 0; r < 16; r += 2) m = fminf(fminf(m, dsc[r]), dsc[r + 1]);   // v_min3
+    tile_of_best[ps] = (m < best[ps]) ? c0 : tile_of_best[ps];
+    best[ps] = m;
+  };
+  auto load_c = [&](int c0, f32x16& cop) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 h4 = *reinterpret_cast<const float4*>(hbase + c0 + 8 * g);
+      cop[4 * g + 0] = h4.x; cop[4 * g + 1] = h4.y; cop[4 * g + 2] = h4.z; cop[4 * g + 3] = h4.w;
     }
+  };
+  float aop = abase[0];
+  f32x16 cop;
+  load_c(0, cop);
+  for (int c0 = 0; c0 < Kpad; c0 += kTile) {
+    const int cn = (c0 + kTile < Kpad) ? c0 + kTile : c0;
+    const float anext = abase[cn];
+    f32x16 cnext;
+    load_c(cn, cnext);
+    f32x16 dprev = __builtin_amdgcn_mfma_f32_32x32x2f32(aop, bop[0], cop, 0, 0, 0);
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      if (run[p] < best[p]) { best[p] = run[p]; chunk_of_best[p] = c0; }
+    for (int ps = 1; ps < kPairSets; ++ps) {
+      const f32x16 dcur = __builtin_amdgcn_mfma_f32_32x32x2f32(aop, bop[ps], cop, 0, 0, 0);
+      fold(dprev, ps - 1, c0);
+      dprev = dcur;
     }
+    fold(dprev, kPairSets - 1, c0);
+    aop = anext;
+    cop = cnext;
   }
 
-  int idx[8];
+  // ---- combine the half-waves: smaller minimum, then earlier tile
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int c0 = chunk_of_best[p];
-    int id = c0;
-    for (int cc = kArgminChunk - 1; cc >= 0; --cc) {
-      const int cidx = c0 + cc;
-      const float sc = __builtin_fmaf(zy[p], cby[cidx], __builtin_fmaf(zx[p], cbx[cidx], cbh[cidx]));
-      id = (sc == best[p]) ? cidx : id;
-    }
-    idx[p] = min(id, K - 1);
+  for (int ps = 0; ps < kPairSets; ++ps) {
+    const float ob = __shfl_xor(best[ps], 32);
+    const int ot = __shfl_xor(tile_of_best[ps], 32);
+    if (ob < best[ps] || (ob == best[ps] && ot < tile_of_best[ps])) { best[ps] = ob; tile_of_best[ps] = ot; }
   }
 
-  // ---- pack: the window's pairs own whole words [16*B*win, 16*B*(win+1))
+  // ---- lowest index: rescan the tile; lane handles column blocks 2m + half
+  uint32_t idxv[kPairSets / 2];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) stage[co_local * kPairsPerLane + p] = (uint16_t)idx[p];
-  __syncthreads();
-  if (!has_work) return;
+  for (int m2 = 0; m2 < kPairSets / 2; ++m2) {
+    const float bb = half ? best[2 * m2 + 1] : best[2 * m2];
+    const int t0 = half ? tile_of_best[2 * m2 + 1] : tile_of_best[2 * m2];
+    const float2 z = zbuf[(2 * m2 + half) * 32 + jcol];
+    int id = t0;
+    for (int cc = kTile - 1; cc >= 0; --cc) {
+      const int ci = t0 + cc;
+      const float sc = __builtin_fmaf(z.y, cby[ci], __builtin_fmaf(z.x, cbx[ci], cbh[ci]));
+      id = (sc == bb) ? ci : id;
+    }
+    idxv[m2] = (uint32_t)min(id, K - 1);
+  }
+
+  // ---- pack: stage the window's 512 indices (reusing the pair buffer), then
+  // build whole words; the window owns words [16*B*win, 16*B*(win+1))
+  uint16_t* stage = reinterpret_cast<uint16_t*>(zbuf);
+  wave_lds_fence();
+#pragma unroll
+  for (int m2 = 0; m2 < kPairSets / 2; ++m2) stage[(2 * m2 + half) * 32 + jcol] = (uint16_t)idxv[m2];
+  wave_lds_fence();
   const int half_d = d >> 1;
   const int npairs = min(kWinPairs, half_d - win * kWinPairs);
   const int word0 = win * 16 * B;
@@ -341,13 +401,15 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
 }
 
 // ---------------------------------------------------------------------------
-// Decode.  A workgroup owns one 1024-column window and 4 * rows_per_wave
-// rows; each wavefront walks rows_per_wave consecutive rows.  The workgroup
-// stages the codebook (K x float2) and the window's column factors
-// g_j = eps_j / (sqrt(b) s_j) in LDS once; each lane keeps its 8 sigma_k and
-// its 16 factors in registers, and prefetches the next row's packed words
-// while it decodes the current row.  BT > 0 fixes the index width at compile
-// time (BT = 0: width B from the argument).
+// Decode.  Each workgroup keeps one 1024-column window and walks rows with a
+// stride (row n goes to workgroup (n / 4) mod blocks_per_window of its
+// window, wave n mod 4), so the codebook (K x float2) and the window's column
+// factors g_j = eps_j / (sqrt(b) s_j) are staged in LDS once per workgroup,
+// with all prologue loads in flight together.  Each lane keeps its 8 sigma_k
+// and 16 factors in registers, holds the row norms of 64 rows at a time (one
+// per lane), and prefetches the packed words of the next rows while it
+// decodes the current one.  BT > 0 fixes the index width at compile time
+// (BT = 0: width B from the argument).
 // ---------------------------------------------------------------------------
 template <int BT>
 __device__ __forceinline__ void unpack8(const uint32_t w[4], uint32_t sh, int Bdyn, uint32_t idx[8]) {
@@ -370,7 +432,7 @@ template <int L, int BT, typename Out>
 __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
     const uint32_t* __restrict__ packed, const uint16_t* __restrict__ rho_f16, int N, int d,
     const float* __restrict__ s, const float* __restrict__ sigma, uint64_t seed,
-    const float* __restrict__ codebook, int K, int Bdyn, int row_words, int rows_per_wave,
+    const float* __restrict__ codebook, int K, int Bdyn, int row_words, int blocks_per_window,
     typename Out::T* __restrict__ out, int64_t ldo) {
   extern __shared__ float4 lds4[];
   uint4* stage_all = reinterpret_cast<uint4*>(lds4);    // 4 waves x 256 x 16 bytes
@@ -380,41 +442,39 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
   const int nchunks = d >> 4;
   const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
   const int win = blockIdx.x % nwin;
-  const int rblk = blockIdx.x / nwin;
-
-  for (int c = threadIdx.x; c < K; c += kBlockThreads)
-    cb[c] = make_float2(codebook[2 * c], codebook[2 * c + 1]);
-  {
-    const float inv_sqrt_b = (float)(1.0 / sqrt((double)(1 << L)));
-    for (int t = threadIdx.x; t < kWinChunks * kChunk; t += kBlockThreads) {
-      const int j = win * kWinChunks * kChunk + t;
-      gwin[t] = (j < d) ? sign_eps(seed, j) * (inv_sqrt_b / (s ? s[j] : 1.0f)) : 0.0f;
-    }
-  }
-  __syncthreads();
-
+  const int rblk = blockIdx.x / nwin;               // 0 .. blocks_per_window-1
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
-  uint4* stage = stage_all + wave * 256;
   const int c = win * kWinChunks + lane;
-  const int valid_cols = d - win * kWinChunks * kChunk;
   // Lanes past the row end hold zeros but stay: the window store reads back
   // columns for every lane of the wave.
   const bool active = c < nchunks;
-  const int co_local = BlockOut<L>::chunk(lane);
-  const int co = win * kWinChunks + co_local;
+  // rows of this wave: n = first + k * stride, k = 0 .. nrows-1
+  const int first = rblk * kWavesPerBlock + wave;
+  const int stride = blocks_per_window * kWavesPerBlock;
+  const int nrows = first < N ? (N - first + stride - 1) / stride : 0;
 
-  float g[16];
-  {
-    const float osign = BlockOut<L>::sign(lane);
-    const float4* gp = reinterpret_cast<const float4*>(gwin + co_local * kChunk);
+  // ---- the first rows' loads go out before the LDS prologue, so their
+  // latency overlaps it
+  const int B = BT ? BT : Bdyn;
+  const int64_t bitstart = (int64_t)c * kPairsPerLane * B;
+  const int wstart = (int)(bitstart >> 5);
+  const uint32_t sh = (uint32_t)(bitstart & 31);
+  int widx[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float4 t = gp[v];
-      g[4 * v + 0] = t.x * osign; g[4 * v + 1] = t.y * osign;
-      g[4 * v + 2] = t.z * osign; g[4 * v + 3] = t.w * osign;
+  for (int i = 0; i < 4; ++i) widx[i] = min(wstart + i, row_words - 1);
+  uint32_t ring[kDecodePrefetch][4];   // packed words of the next rows, in flight
+#pragma unroll
+  for (int q = 0; q < kDecodePrefetch; ++q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ring[q][i] = 0u;
+    if (active && q < nrows) {
+      const uint32_t* rw = packed + (int64_t)(first + q * stride) * row_words;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ring[q][i] = rw[widx[i]];
     }
   }
+  float rh_lane = (lane < nrows) ? f16_bits_to_f32(rho_f16[first + lane * stride]) : 0.0f;  // 64 rows at a time
   float sg[8];
   if (active) {
     const float4* sp = reinterpret_cast<const float4*>(sigma + c * kPairsPerLane);
@@ -426,29 +486,62 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
     for (int p = 0; p < 8; ++p) sg[p] = 0.0f;
   }
 
-  const int B = BT ? BT : Bdyn;
-  const int64_t bitstart = (int64_t)c * kPairsPerLane * B;
-  const int wstart = (int)(bitstart >> 5);
-  const uint32_t sh = (uint32_t)(bitstart & 31);
-  int widx[4];
+  // ---- LDS prologue: codebook and the window's column factors
+  {
+    const float4* cb4 = reinterpret_cast<const float4*>(codebook);   // two centroids per float4
+    float4* cbl = reinterpret_cast<float4*>(cb);
+    const int npairs4 = K >> 1;
+#pragma unroll 8
+    for (int cc = threadIdx.x; cc < npairs4; cc += kBlockThreads) cbl[cc] = cb4[cc];
+    if ((K & 1) && threadIdx.x == 0) cb[K - 1] = make_float2(codebook[2 * (K - 1)], codebook[2 * (K - 1) + 1]);
+    const float inv_sqrt_b = (float)(1.0 / sqrt((double)(1 << L)));
+    constexpr int kPer = kWinChunks * kChunk / kBlockThreads;   // 4
+    float sv[kPer];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) widx[i] = min(wstart + i, row_words - 1);
-
-  const int n0 = (rblk * kWavesPerBlock + wave) * rows_per_wave;
-  const int n1 = min(N, n0 + rows_per_wave);
-  if (n0 >= n1) return;
-  uint32_t wn[4] = {0u, 0u, 0u, 0u};
-  if (active) {
-    const uint32_t* rw = packed + (int64_t)n0 * row_words;
+    for (int q = 0; q < kPer; ++q) {
+      const int j = win * kWinChunks * kChunk + q * kBlockThreads + threadIdx.x;
+      sv[q] = (j < d) ? (s ? s[j] : 1.0f) : 1.0f;
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wn[i] = rw[widx[i]];
+    for (int q = 0; q < kPer; ++q) {
+      const int t = q * kBlockThreads + threadIdx.x;
+      const int j = win * kWinChunks * kChunk + t;
+      gwin[t] = (j < d) ? sign_eps(seed, j) * (inv_sqrt_b / sv[q]) : 0.0f;
+    }
   }
-  for (int n = n0; n < n1; ++n) {
-    uint32_t w[4] = {wn[0], wn[1], wn[2], wn[3]};
-    if (active && n + 1 < n1) {
-      const uint32_t* rw = packed + (int64_t)(n + 1) * row_words;
+  __syncthreads();
+  if (nrows == 0) return;                          // no barriers follow
+
+  uint4* stage = stage_all + wave * 256;
+  const int valid_cols = d - win * kWinChunks * kChunk;
+  const int co_local = BlockOut<L>::chunk(lane);
+  float g[16];
+  {
+    const float osign = BlockOut<L>::sign(lane);
+    const float4* gp = reinterpret_cast<const float4*>(gwin + co_local * kChunk);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wn[i] = rw[widx[i]];
+    for (int v = 0; v < 4; ++v) {
+      const float4 t = gp[v];
+      g[4 * v + 0] = t.x * osign; g[4 * v + 1] = t.y * osign;
+      g[4 * v + 2] = t.z * osign; g[4 * v + 3] = t.w * osign;
+    }
+  }
+
+  for (int k = 0; k < nrows; ++k) {
+    if (k > 0 && (k & (kWave - 1)) == 0) {
+      const int kk = k + lane;
+      rh_lane = (kk < nrows) ? f16_bits_to_f32(rho_f16[first + kk * stride]) : 0.0f;
+    }
+    const int n = first + k * stride;
+    uint32_t w[4] = {ring[0][0], ring[0][1], ring[0][2], ring[0][3]};
+#pragma unroll
+    for (int q = 0; q + 1 < kDecodePrefetch; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ring[q][i] = ring[q + 1][i];
+    if (active && k + kDecodePrefetch < nrows) {
+      const uint32_t* rw = packed + (int64_t)(n + kDecodePrefetch * stride) * row_words;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ring[kDecodePrefetch - 1][i] = rw[widx[i]];
     }
     uint32_t idx[8];
     unpack8<BT>(w, sh, Bdyn, idx);
@@ -460,7 +553,8 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
       x[2 * p + 1] = cc.y * sg[p];
     }
     fwht_block<L>(x, lane);
-    const float rh = f16_bits_to_f32(rho_f16[n]);
+    const float rh =
+        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rh_lane), k & (kWave - 1)));
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (x[i] * rh) * g[i];
     Out::store(stage, lane, co_local, x, out + (int64_t)n * ldo + win * kWinChunks * kChunk, valid_cols);
@@ -556,14 +650,15 @@ struct LaunchEncode {
                  uint32_t* packed, hipStream_t st) {
     const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
     const int64_t waves = (int64_t)N * nwin;
-    const int Kpad = (int)round_up((size_t)K, kArgminChunk);
-    const size_t lds = (size_t)Kpad * 3 * sizeof(float) + (size_t)kWavesPerBlock * kWinPairs * sizeof(uint16_t);
+    const int Kpad = (int)round_up((size_t)K, kTile);
+    const size_t lds = (size_t)Kpad * 3 * sizeof(float) + (size_t)kEncWaves * kWinPairs * sizeof(float2);
+    const dim3 grid((unsigned)((waves + kEncWaves - 1) / kEncWaves)), blk(kEncThreads);
     if (wdt == QAMW_F32)
-      hipLaunchKernelGGL((encode_kernel<L, float>), dim3(grid_for_waves(waves)), dim3(kBlockThreads), lds, st,
-                         (const float*)W, ldw, N, d, s, sigma, seed, cb, K, Kpad, B, row_words, rho, packed);
+      hipLaunchKernelGGL((encode_kernel<L, float>), grid, blk, lds, st, (const float*)W, ldw, N, d, s, sigma, seed,
+                         cb, K, Kpad, B, row_words, rho, packed);
     else
-      hipLaunchKernelGGL((encode_kernel<L, uint16_t>), dim3(grid_for_waves(waves)), dim3(kBlockThreads), lds, st,
-                         (const uint16_t*)W, ldw, N, d, s, sigma, seed, cb, K, Kpad, B, row_words, rho, packed);
+      hipLaunchKernelGGL((encode_kernel<L, uint16_t>), grid, blk, lds, st, (const uint16_t*)W, ldw, N, d, s, sigma,
+                         seed, cb, K, Kpad, B, row_words, rho, packed);
     return check_launch("encode_kernel");
   }
 };
@@ -573,24 +668,27 @@ int launch_decode_bt(const uint32_t* packed, const uint16_t* rho_f16, int N, int
                      const float* sigma, uint64_t seed, const float* cb, int K, int B, int row_words, void* out,
                      int32_t odt, int64_t ldo, hipStream_t st) {
   const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
-  // about 32 wavefronts of work per CU on 256 CUs; each walks rows_per_wave rows
-  const int64_t target = 256 * 32;
-  int rows_per_wave = (int)(((int64_t)N * nwin + target - 1) / target);
-  rows_per_wave = rows_per_wave < 1 ? 1 : (rows_per_wave > 64 ? 64 : rows_per_wave);
-  const int64_t rows_per_block = (int64_t)rows_per_wave * kWavesPerBlock;
-  const int64_t blocks = (int64_t)nwin * ((N + rows_per_block - 1) / rows_per_block);
+  // Persistent-style grid: every workgroup keeps one window (codebook and
+  // column factors loaded once) and walks rows with a stride; about
+  // QAMW_DECODE_WAVES_PER_CU / 4 workgroups per CU in total.
+  const int64_t target_blocks = 256 * QAMW_DECODE_WAVES_PER_CU / kWavesPerBlock;
+  int64_t bpw = target_blocks / nwin;
+  const int64_t need = (N + kWavesPerBlock - 1) / kWavesPerBlock;   // one row per wave at most
+  bpw = bpw < 1 ? 1 : (bpw > need ? need : bpw);
+  const int blocks_per_window = (int)bpw;
+  const int64_t blocks = (int64_t)nwin * blocks_per_window;
   const size_t lds = (size_t)kWavesPerBlock * 256 * 16 + (size_t)kWinChunks * kChunk * sizeof(float) +
                      (size_t)K * sizeof(float2);
   const dim3 grid((unsigned)blocks), blk(kBlockThreads);
   if (odt == QAMW_F32)
     hipLaunchKernelGGL((decode_kernel<L, BT, StageF32>), grid, blk, lds, st, packed, rho_f16, N, d, s, sigma, seed,
-                       cb, K, B, row_words, rows_per_wave, (float*)out, ldo);
+                       cb, K, B, row_words, blocks_per_window, (float*)out, ldo);
   else if (odt == QAMW_BF16)
     hipLaunchKernelGGL((decode_kernel<L, BT, StageBF16>), grid, blk, lds, st, packed, rho_f16, N, d, s, sigma,
-                       seed, cb, K, B, row_words, rows_per_wave, (uint16_t*)out, ldo);
+                       seed, cb, K, B, row_words, blocks_per_window, (uint16_t*)out, ldo);
   else
     hipLaunchKernelGGL((decode_kernel<L, BT, StageF16>), grid, blk, lds, st, packed, rho_f16, N, d, s, sigma, seed,
-                       cb, K, B, row_words, rows_per_wave, (uint16_t*)out, ldo);
+                       cb, K, B, row_words, blocks_per_window, (uint16_t*)out, ldo);
   return check_launch("decode_kernel");
 }
 
@@ -634,6 +732,7 @@ int check_weights(const void* W, int32_t wdt, int64_t d, int64_t ldw) {
 
 int check_codebook(const float* cb, int32_t K) {
   if (!cb) return fail(QAMW_EINVAL, "codebook is NULL");
+  if (!aligned16(cb)) return fail(QAMW_EINVAL, "codebook must be 16-byte aligned");
   if (K < 2 || K > 4096) return fail(QAMW_EUNSUPPORTED, "K=%d outside [2, 4096]", K);
   return QAMW_OK;
 }
