@@ -35,7 +35,7 @@ PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_kernel_4096x11008_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "vector_codebook_codec_amd", "csrc", f)
-                  for f in ("qamw_kernels.hip", "qamw_device.h")]
+                  for f in ("encode.hip", "qamw_device.h", "qamw_internal.h")]
 
 
 def measured_traffic(workload):
@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-decode-reps", type=int, default=10,
                     help="decode-only reps timed after overwriting a 1 GiB buffer")
+    ap.add_argument("--exhaustive-reps", type=int, default=5,
+                    help="encodes without a search plan timed after the steps (0 to skip)")
     ap.add_argument("--copy-reference", type=int, default=0,
                     help="also run N copies of a 1 GiB buffer (counter calibration)")
     return ap.parse_args()
@@ -117,7 +119,8 @@ def main():
     rn = torch.empty(N, dtype=torch.int16, device=dev)
     out = torch.empty((N, d), dtype=torch.float32, device=dev)
     ws_cal = torch.empty(q.qamw_calibrate_workspace_bytes(N, d, b), dtype=torch.uint8, device=dev)
-    ws_enc = torch.empty(max(256, q.qamw_encode_workspace_bytes(N)), dtype=torch.uint8, device=dev)
+    ws_enc = torch.empty(max(256, q.qamw_encode_workspace_bytes(N, d)), dtype=torch.uint8, device=dev)
+    plan = torch.empty(q.qamw_plan_bytes(K), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
@@ -128,19 +131,22 @@ def main():
         q.qamw_calibrate(W, r, wl.alpha, b, wl.sign_seed, s, sigma, ws_cal, stream)
         if marks is not None:
             marks[1].record(stream)
-        q.qamw_encode(W, s, sigma, b, wl.sign_seed, Ct, packed, rn, ws_enc, stream)
+        q.qamw_build_plan(Ct, plan, stream)
         if marks is not None:
             marks[2].record(stream)
-        q.qamw_decode(packed, rn, d, s, sigma, b, wl.sign_seed, Ct, out=out, stream=stream)
+        q.qamw_encode(W, s, sigma, b, wl.sign_seed, Ct, plan, packed, rn, ws_enc, stream)
         if marks is not None:
             marks[3].record(stream)
+        q.qamw_decode(packed, rn, d, s, sigma, b, wl.sign_seed, Ct, out=out, stream=stream)
+        if marks is not None:
+            marks[4].record(stream)
 
     for i in range(args.warmup):
         step()
         print(f"warmup step {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
 
-    marks = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    marks = [[ev() for _ in range(5)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(marks[i])
@@ -149,9 +155,25 @@ def main():
     print(f"timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
     cal_ms = float(np.mean([m[0].elapsed_time(m[1]) for m in marks]))
-    enc_ms = float(np.mean([m[1].elapsed_time(m[2]) for m in marks]))
-    dec_ms = float(np.mean([m[2].elapsed_time(m[3]) for m in marks]))
+    plan_ms = float(np.mean([m[1].elapsed_time(m[2]) for m in marks]))
+    enc_ms = float(np.mean([m[2].elapsed_time(m[3]) for m in marks]))
+    dec_ms = float(np.mean([m[3].elapsed_time(m[4]) for m in marks]))
     step_ms = wall * 1e3 / args.steps
+
+    # the exhaustive search (no plan) for comparison; same indices, bit for bit
+    packed_x = torch.empty_like(packed)
+    rn_x = torch.empty_like(rn)
+    exh = []
+    for _ in range(args.exhaustive_reps):
+        a, z = ev(), ev()
+        a.record(stream)
+        q.qamw_encode(W, s, sigma, b, wl.sign_seed, Ct, None, packed_x, rn_x, ws_enc, stream)
+        z.record(stream)
+        torch.cuda.synchronize()
+        exh.append(a.elapsed_time(z))
+    if exh and not (torch.equal(packed_x, packed) and torch.equal(rn_x, rn)):
+        raise RuntimeError("planned and exhaustive encodes disagree")
+    exh_ms = float(np.median(exh)) if exh else None
 
     # decode alone, with HBM caches (L2, MALL) flushed by a 1 GiB write before each rep
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -198,8 +220,9 @@ def main():
                      "achieved": achieved_tflops, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_tflops / PEAK_FP32_TFLOPS, "traffic": measured_traffic(wl.name),
                      "algorithmic": f"{P} pairs x {K} centroids x 4 flops = {enc_flops:.4g} per launch"},
-        "per_entry_ms": {"calibrate": cal_ms, "encode": enc_ms, "decode": dec_ms},
-        "encode_gweights_s": weights / ((cal_ms + enc_ms) * 1e-3) / 1e9,
+        "per_entry_ms": {"calibrate": cal_ms, "build_plan": plan_ms, "encode": enc_ms, "decode": dec_ms},
+        "encode_exhaustive_ms": exh_ms,
+        "encode_gweights_s": weights / ((cal_ms + plan_ms + enc_ms) * 1e-3) / 1e9,
         "decode_gweights_s": weights / (dec_ms * 1e-3) / 1e9,
         "decode_cold": None if dec_cold_ms is None else {
             "ms": dec_cold_ms, "algorithmic_bytes": dec_bytes,

@@ -40,7 +40,8 @@
  *     call only enqueues kernels on it and returns; results are valid once
  *     the stream has reached that point.  In-place calls are not supported
  *     (outputs must not alias inputs).
- *   - W, W_out, packed, codebook, s and sigma must be 16-byte aligned, and
+ *   - W, W_out, packed, codebook, s and sigma must be 16-byte aligned (a plan
+ *     256-byte aligned), and
  *     ldw / ldo rows must keep 16-byte alignment (ldw * element size % 16 == 0).
  *
  * Errors
@@ -84,8 +85,9 @@ int64_t qamw_packed_row_words(int64_t d, int32_t K);
  * (row norms in fp64 and per-row-tile partial sums of pair amplitudes). */
 size_t qamw_calibrate_workspace_bytes(int64_t N, int64_t d, int32_t block);
 
-/* Bytes of device workspace qamw_encode needs (fp64 row norms). */
-size_t qamw_encode_workspace_bytes(int64_t N);
+/* Bytes of device workspace qamw_encode needs for an N x d matrix (fp64 row
+ * norms, fp32 per-column factors eps_j s_j, fp64 1 / sigma_k). */
+size_t qamw_encode_workspace_bytes(int64_t N, int64_t d);
 
 const char* qamw_status_string(int32_t status);
 const char* qamw_last_error(void);
@@ -112,22 +114,48 @@ int32_t qamw_calibrate(const void* W, int32_t wdtype, int64_t N, int64_t d, int6
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Nearest-centroid search plan (QAM-W, Methodology: Joint 2D Quantization).
+ * An optional, codebook-specific acceleration structure for qamw_encode: a
+ * 512 x 512 grid over [-5, 5)^2 whose cells list, in ascending index order,
+ * every centroid that can be the nearest one (under qamw_encode's fp32
+ * scores) for some point of the cell.  Encoding with a plan gives the same
+ * indices, bit for bit, as encoding without one; pairs outside the grid and
+ * cells with too many candidates fall back to scanning all K centroids.
+ *
+ * qamw_plan_bytes(K): bytes of device memory a plan for K centroids takes
+ *   (0 for K outside [2, 4096]).  Host-only.
+ * qamw_build_plan: enqueue the plan's construction on `stream`.
+ *   codebook  [K][2] float32, the codebook later passed to qamw_encode
+ *   plan      device buffer of plan_size >= qamw_plan_bytes(K) bytes,
+ *             256-byte aligned; caller-owned, written entirely by the call
+ * A plan stays valid while the codebook's values do not change; it may be
+ * shared by concurrent encodes (they only read it).
+ */
+size_t qamw_plan_bytes(int32_t K);
+int32_t qamw_build_plan(const float* codebook, int32_t K, void* plan, size_t plan_size, void* stream);
+
+/*
  * Encode (QAM-W, Methodology: Separation of Scale and Direction; Deterministic
  * Rotation; Pairing and Calibration; Joint 2D Quantization).
  *   W, wdtype, N, d, ldw, block, sign_seed  as for qamw_calibrate
  *   s          [d] float32: channel scales (normally s_out of qamw_calibrate)
  *   sigma      [d/2] float32: pair scales; sigma_k = 0 codes z~ = 0
  *   codebook   [K][2] float32, 2 <= K <= 4096
+ *   plan       NULL (exhaustive search over the codebook) or a plan that
+ *              qamw_build_plan built for this codebook and K; same result.
+ *              A plan built for another K is detected on the device and the
+ *              whole codebook is scanned; one built for another codebook of
+ *              the same K gives unspecified (in-range) indices
  *   packed     [N][qamw_packed_row_words(d, K)] uint32 out
  *   rownorm_f16[N] uint16 out: binary16 bits of rho_n (RNE)
- *   workspace  >= qamw_encode_workspace_bytes(N), 256-byte aligned
+ *   workspace  >= qamw_encode_workspace_bytes(N, d), 256-byte aligned
  * The nearest centroid is decided in fp32 on the expanded score
  * |c|^2/2 - z~ . c (equal to |z~ - c|^2/2 - |z~|^2/2); equal scores go to the
  * lowest index.
  */
 int32_t qamw_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
                     const float* s, const float* sigma, int32_t block, uint64_t sign_seed,
-                    const float* codebook, int32_t K,
+                    const float* codebook, int32_t K, const void* plan,
                     uint32_t* packed, uint16_t* rownorm_f16,
                     void* workspace, size_t workspace_bytes, void* stream);
 

@@ -50,12 +50,19 @@ def test_host_helpers(lib):
     assert lib.qamw_packed_row_words(13824, 4096) == 2592
     assert lib.qamw_packed_row_words(12, 2048) == 4
     assert lib.qamw_packed_row_words(13, 2048) == -1
-    assert lib.qamw_encode_workspace_bytes(4096) == 4096 * 8
-    assert lib.qamw_encode_workspace_bytes(5) == 256
+    # rho (fp64) + column factors (fp32) + 1 / sigma (fp64), each 256-byte padded
+    assert lib.qamw_encode_workspace_bytes(4096, 11008) == 4096 * 8 + 11008 * 4 + 5504 * 8
+    assert lib.qamw_encode_workspace_bytes(5, 16) == 3 * 256
+    assert lib.qamw_encode_workspace_bytes(0, 16) == 0
     # rho (fp64, 256-byte padded) + ceil(N / 16) tiles x d/2 fp32
     assert lib.qamw_calibrate_workspace_bytes(4096, 11008, 256) == 4096 * 8 + 256 * 5504 * 4
     assert lib.qamw_calibrate_workspace_bytes(0, 16, 16) == 0
     assert lib.qamw_status_string(-4) == b"workspace missing or too small"
+    # header block + one uint16 record of lmax entries per cell of the 512 x 512 grid
+    assert lib.qamw_plan_bytes(256) == 256 + 512 ** 2 * 8 * 2
+    assert lib.qamw_plan_bytes(2048) == 256 + 512 ** 2 * 8 * 2
+    assert lib.qamw_plan_bytes(4096) == 256 + 512 ** 2 * 16 * 2
+    assert lib.qamw_plan_bytes(1) == 0 and lib.qamw_plan_bytes(4097) == 0
 
 
 # Fake, never-dereferenced device addresses: every call below must fail in
@@ -66,12 +73,12 @@ WS = 1 << 24
 
 
 def _encode(lib, **kw):
-    args = dict(W=A, wdt=1, N=8, d=256, ldw=256, s=A, sigma=A, block=128, seed=0, cb=A, K=256,
+    args = dict(W=A, wdt=1, N=8, d=256, ldw=256, s=A, sigma=A, block=128, seed=0, cb=A, K=256, plan=None,
                 packed=A, rn=A, ws=WS, ws_bytes=1 << 20, stream=None)
     args.update(kw)
     return lib.qamw_encode(args["W"], args["wdt"], args["N"], args["d"], args["ldw"], args["s"], args["sigma"],
-                           args["block"], args["seed"], args["cb"], args["K"], args["packed"], args["rn"],
-                           args["ws"], args["ws_bytes"], args["stream"])
+                           args["block"], args["seed"], args["cb"], args["K"], args["plan"], args["packed"],
+                           args["rn"], args["ws"], args["ws_bytes"], args["stream"])
 
 
 def _calibrate(lib, **kw):
@@ -98,6 +105,7 @@ def _decode(lib, **kw):
     (dict(W=None), -1), (dict(cb=None), -1), (dict(s=None), -1), (dict(packed=None), -1),
     (dict(W=MIS), -1), (dict(packed=MIS), -1), (dict(wdt=2), -2), (dict(ldw=260), -1),
     (dict(ws=None), -4), (dict(ws_bytes=8), -4), (dict(ws=WS + 16), -4), (dict(cb=MIS), -1),
+    (dict(plan=WS + 128), -1),
 ])
 def test_encode_rejects(lib, kw, status):
     assert _encode(lib, **kw) == status
@@ -118,6 +126,17 @@ def test_calibrate_rejects(lib, kw, status):
 ])
 def test_decode_rejects(lib, kw, status):
     assert _decode(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cb=None), -1), (dict(cb=MIS), -1), (dict(K=1), -2), (dict(K=5000), -2), (dict(plan=None), -1),
+    (dict(plan=WS + 16), -1), (dict(size=1000), -4), (dict(K=4096, size=256 + 512 ** 2 * 16), -4),
+])
+def test_build_plan_rejects(lib, kw, status):
+    args = dict(cb=A, K=2048, plan=WS, size=1 << 23, stream=None)
+    args.update(kw)
+    assert lib.qamw_build_plan(args["cb"], args["K"], args["plan"], args["size"], args["stream"]) == status
+    assert lib.qamw_last_error()
 
 
 def test_workspace_size_is_enforced(lib):

@@ -70,13 +70,25 @@ def f16_boundary_ok(gpu_bits, ora_bits, rho):
     return same | near
 
 
-def run_gpu(q, wl, C, stream_sync=True):
+def encode_both(q, W, s, sigma, block, seed, Ct):
+    """Encode with the exhaustive search and with a search plan; the two must
+    agree bit for bit (packed words and row norms)."""
+    packed, rn = q.qamw_encode(W, s, sigma, block, seed, Ct)
+    plan = q.qamw_build_plan(Ct)
+    packed_p, rn_p = q.qamw_encode(W, s, sigma, block, seed, Ct, plan=plan)
+    torch.cuda.synchronize()
+    n_bad = int((packed_p != packed).sum())
+    assert n_bad == 0, f"planned encode differs from exhaustive in {n_bad} words"
+    assert torch.equal(rn_p, rn)
+    return packed, rn
+
+
+def run_gpu(q, wl, C):
     W = to_dev(wl.W, wl.wdtype)
     r = torch.from_numpy(wl.r).to(DEV)
     Ct = torch.from_numpy(C).to(DEV)
     s, sigma = q.qamw_calibrate(W, r, wl.alpha, wl.block, wl.sign_seed)
-    packed, rn = q.qamw_encode(W, s, sigma, wl.block, wl.sign_seed, Ct)
-    torch.cuda.synchronize()
+    packed, rn = encode_both(q, W, s, sigma, wl.block, wl.sign_seed, Ct)
     return dict(W=W, r=r, C=Ct, s=s, sigma=sigma, packed=packed, rn=rn)
 
 
@@ -231,7 +243,7 @@ def test_zero_rows_and_zero_sigma(q):
     sigma = torch.from_numpy(sig_np).to(DEV)
     Ct = torch.from_numpy(C).to(DEV)
     say("case degenerate: zero row, sigma_k = 0")
-    packed, rn = q.qamw_encode(Wt, s, sigma, b, 9, Ct)
+    packed, rn = encode_both(q, Wt, s, sigma, b, 9, Ct)
     Wh = q.qamw_decode(packed, rn, d, s, sigma, b, 9, Ct)
     torch.cuda.synchronize()
     enc = O.encode(W, np.ones(d), sig_np, b, 9, C)
@@ -250,7 +262,7 @@ def test_all_zero_matrix(q):
     Wt = torch.zeros((N, d), device=DEV)
     C = q.load_codebook(K)
     s, sigma = q.qamw_calibrate(Wt, torch.ones(d, device=DEV), 0.5, b, 0)
-    packed, rn = q.qamw_encode(Wt, s, sigma, b, 0, torch.from_numpy(C).to(DEV))
+    packed, rn = encode_both(q, Wt, s, sigma, b, 0, torch.from_numpy(C).to(DEV))
     Wh = q.qamw_decode(packed, rn, d, s, sigma, b, 0, torch.from_numpy(C).to(DEV))
     torch.cuda.synchronize()
     assert torch.count_nonzero(sigma) == 0
@@ -285,7 +297,7 @@ def test_exact_ties_lowest_index(q):
     W = (rng.standard_normal((N, d)) * 0.02).astype(np.float32)
     dev = lambda a: torch.from_numpy(a).to(DEV)
     s, sigma = q.qamw_calibrate(dev(W), dev(np.ones(d, np.float32)), 0.0, b, 1)
-    packed, rn = q.qamw_encode(dev(W), s, sigma, b, 1, dev(C))
+    packed, rn = encode_both(q, dev(W), s, sigma, b, 1, dev(C))
     torch.cuda.synchronize()
     idx = O.unpack(packed.cpu().numpy().view(np.uint32), 32, d)
     assert idx.max() < 16
@@ -333,3 +345,110 @@ def test_full_size_sampled(q, name):
     check_decode_rows(q, wl, C, g, rows)
     if name.startswith("c3"):
         check_decode_rows(q, wl, C, g, rows, torch.float16)
+
+
+# ---------------------------------------------------------------- search plan
+PLAN_G, PLAN_R, PLAN_OVERFLOW = 512, 5.0, 255
+
+
+def read_plan(q, C):
+    """Build the plan on the GPU and decode its per-cell records: entry i is
+    16 c_i | nibble_i with nibble_0 = count - 1 and nibble_1 = overflow."""
+    K = C.shape[0]
+    plan = q.qamw_build_plan(torch.from_numpy(C).to(DEV))
+    torch.cuda.synchronize()
+    raw = plan.cpu().numpy()
+    lmax = 8 if K <= 2048 else 16
+    assert raw.size == q.qamw_plan_bytes(K) == 256 + PLAN_G ** 2 * lmax * 2
+    hdr_f = raw[:8].view(np.float32)
+    hdr_i = raw[8:20].view(np.int32)
+    assert hdr_f[0] == PLAN_R and hdr_f[1] == np.float32(PLAN_G / (2 * PLAN_R))
+    assert list(hdr_i) == [PLAN_G, lmax, K]
+    rec = raw[256:].view(np.uint16).reshape(PLAN_G ** 2, lmax).astype(np.int64)
+    nib = rec & 15
+    assert np.all(nib[:, 1] <= 1) and np.all(nib[:, 2:] == 0)
+    counts = np.where(nib[:, 1] == 1, PLAN_OVERFLOW, nib[:, 0] + 1)
+    return counts, rec >> 4, lmax
+
+
+def cell_of(z):
+    """Cell index of points inside [-R, R)^2 (fp32 arithmetic, as the kernel)."""
+    cpu = np.float32(PLAN_G / (2 * PLAN_R))
+    zf = z.astype(np.float32)
+    ix = np.minimum(((zf[:, 0] + np.float32(PLAN_R)) * cpu).astype(np.int64), PLAN_G - 1)
+    iy = np.minimum(((zf[:, 1] + np.float32(PLAN_R)) * cpu).astype(np.int64), PLAN_G - 1)
+    return ix * PLAN_G + iy
+
+
+@pytest.mark.parametrize("K", [2, 16, 256, 2048, 4096])
+def test_plan_lists_cover_near_minimisers(q, K):
+    """Every centroid within 1e-6 (1 + |z|^2) of a point's minimum squared
+    distance (fp64 brute force) is in that point's cell list; lists are
+    strictly ascending, in range and zero-padded."""
+    C = q.load_codebook(K)
+    counts, lists, lmax = read_plan(q, C)
+    say(f"case plan K={K}: {int((counts == PLAN_OVERFLOW).sum())} overflow cells, "
+        f"mean count {float(counts[counts != PLAN_OVERFLOW].mean()):.2f}")
+    ok_cells = counts != PLAN_OVERFLOW
+    assert np.all(counts[ok_cells] <= lmax) and np.all(counts[ok_cells] >= 1)
+    slot = np.arange(lmax)[None, :]
+    used = slot < counts[:, None]
+    # the unused tail repeats the last listed centroid
+    last = lists[np.arange(len(counts)), np.clip(counts, 1, lmax) - 1]
+    assert np.all((lists == last[:, None])[ok_cells][~used[ok_cells]])
+    assert np.all(lists[ok_cells] < K)
+    inc = np.diff(lists, axis=1) > 0
+    assert np.all(inc[ok_cells] | ~used[ok_cells][:, 1:])
+    rng = np.random.default_rng(K)
+    edges = -PLAN_R + np.arange(PLAN_G) * (2 * PLAN_R / PLAN_G)
+    z = np.concatenate([
+        rng.uniform(-PLAN_R, PLAN_R, (40000, 2)),
+        rng.standard_normal((40000, 2)),
+        # points on cell edges (both coordinates) and just inside the grid's far edge
+        np.stack([rng.choice(edges, 8000), rng.choice(edges, 8000)], 1),
+        np.stack([np.full(200, PLAN_R - 1e-6), rng.uniform(-PLAN_R, PLAN_R, 200)], 1),
+    ])
+    Cd = C.astype(np.float64)
+    for lo in range(0, len(z), 4000):
+        zz = z[lo:lo + 4000]
+        D = ((zz[:, None, :] - Cd[None, :, :]) ** 2).sum(-1)
+        near = D <= D.min(1, keepdims=True) + 1e-6 * (1 + (zz ** 2).sum(1, keepdims=True))
+        cells = cell_of(zz)
+        listed = np.zeros_like(near)
+        rows = np.repeat(np.arange(len(zz)), lmax)
+        cols = lists[cells].reshape(-1)
+        mask = used[cells].reshape(-1)
+        listed[rows[mask], cols[mask]] = True
+        listed[counts[cells] == PLAN_OVERFLOW] = True
+        assert not (near & ~listed).any(), "a near-minimising centroid is missing from its cell list"
+
+
+def test_plan_overflow_and_outside_grid(q):
+    """Clustered centroids overflow their cells' lists and tiny sigma_k push
+    pairs outside the grid: both fall back to the full scan, bit-identical
+    to the exhaustive search and accepted by the oracle."""
+    rng = np.random.default_rng(21)
+    base = q.load_codebook(16)
+    ang = rng.uniform(0, 2 * np.pi, 48)
+    cluster = np.stack([0.3 + 1e-3 * np.cos(ang), -0.2 + 1e-3 * np.sin(ang)], 1)
+    C = np.concatenate([base, cluster]).astype(np.float32)          # K = 64
+    counts, _, _ = read_plan(q, C)
+    assert (counts == PLAN_OVERFLOW).any()
+    N, d, b = 64, 4096, 256
+    W = (rng.standard_normal((N, d)) * 0.02).astype(np.float32)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    s, sigma = q.qamw_calibrate(dev(W), dev(np.ones(d, np.float32)), 0.0, b, 5)
+    sig_np = sigma.cpu().numpy().copy()
+    sig_np[::7] *= 1e-3                                                  # |z~| ~ 1e3: outside the grid
+    sigma = dev(sig_np)
+    say("case plan overflow / outside grid")
+    packed, rn = encode_both(q, dev(W), s, sigma, b, 5, dev(C))
+    enc = O.encode(W, s.cpu().numpy(), sig_np, b, 5, C)
+    zt = enc["zt"].reshape(-1, 2)
+    inside = (np.abs(zt) < PLAN_R).all(1)
+    in_overflow = inside.copy()
+    in_overflow[inside] = counts[cell_of(zt[inside])] == PLAN_OVERFLOW
+    say(f"  {int((~inside).sum())} pairs outside the grid, {int(in_overflow.sum())} in overflow cells")
+    assert (~inside).sum() > 1000 and in_overflow.sum() > 0
+    idx = O.unpack(packed.cpu().numpy().view(np.uint32), C.shape[0], d)
+    assert O.accept_index(zt, C, enc["idx"].reshape(-1), idx.reshape(-1)).all()

@@ -7,6 +7,7 @@ points ``qamw_calibrate``, ``qamw_encode`` and ``qamw_decode``.
 """
 from .codec import (  # noqa: F401
     load_codebook,
+    qamw_build_plan,
     qamw_calibrate,
     qamw_calibrate_workspace_bytes,
     qamw_decode,
@@ -14,6 +15,7 @@ from .codec import (  # noqa: F401
     qamw_encode_workspace_bytes,
     qamw_index_bits,
     qamw_packed_row_words,
+    qamw_plan_bytes,
 )
 
 __version__ = "0.1.0"

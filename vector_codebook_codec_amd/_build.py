@@ -16,8 +16,10 @@ import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "qamw_kernels.hip")]
-HEADERS = [os.path.join(PKG, "csrc", "qamw_device.h"), os.path.join(ROOT, "include", "qamw.h")]
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = [os.path.join(CSRC, f) for f in ("api.hip", "calibrate.hip", "encode.hip", "plan.hip", "decode.hip")]
+HEADERS = [os.path.join(CSRC, "qamw_device.h"), os.path.join(CSRC, "qamw_internal.h"),
+           os.path.join(ROOT, "include", "qamw.h")]
 LIB_PATH = os.path.join(PKG, "libqamw.so")
 ARCH = "gfx950"
 
@@ -29,35 +31,38 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def compile_command(out: str) -> list:
-    return [
-        hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
-        "-ffp-contract=off",
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", os.path.join(ROOT, "include"),
-        "-o", out, *SOURCES,
-    ]
+FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-ffp-contract=off",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every HIP source into libqamw.so (always recompiles)."""
-    fd, tmp = tempfile.mkstemp(prefix="libqamw.", suffix=".so.tmp", dir=PKG)
-    os.close(fd)
-    cmd = compile_command(tmp)
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l and l.strip()]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if msgs and verbose:
+        print("\n".join(msgs), flush=True)
+
+
+def build(verbose: bool = True, extra_flags=()) -> str:
+    """Compile every HIP source (in parallel) and link libqamw.so; always recompiles."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    tmpdir = tempfile.mkdtemp(prefix="qamw_build_", dir=PKG)
     try:
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        noise = "packed-fp32-ops"
-        msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l and l.strip()]
-        if res.returncode != 0:
-            raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-        if msgs and verbose:
-            print("\n".join(msgs), flush=True)
-        os.replace(tmp, LIB_PATH)
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
+        cmds = [[hipcc(), *FLAGS, *extra_flags, "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+        workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        tmp_lib = os.path.join(tmpdir, "libqamw.so")
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs], verbose)
+        os.replace(tmp_lib, LIB_PATH)
     finally:
-        if os.path.exists(tmp):
-            os.unlink(tmp)
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB_PATH
 
 

@@ -21,12 +21,14 @@ SIGNATURES = {
     "qamw_index_bits": (_i32, [_i32]),
     "qamw_packed_row_words": (_i64, [_i64, _i32]),
     "qamw_calibrate_workspace_bytes": (_sz, [_i64, _i64, _i32]),
-    "qamw_encode_workspace_bytes": (_sz, [_i64]),
+    "qamw_encode_workspace_bytes": (_sz, [_i64, _i64]),
     "qamw_status_string": (_c.c_char_p, [_i32]),
     "qamw_last_error": (_c.c_char_p, []),
     "qamw_version": (_c.c_char_p, []),
     "qamw_calibrate": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _f32, _i32, _u64, _p, _p, _p, _sz, _p]),
-    "qamw_encode": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _p, _p, _sz, _p]),
+    "qamw_plan_bytes": (_sz, [_i32]),
+    "qamw_build_plan": (_i32, [_p, _i32, _p, _sz, _p]),
+    "qamw_encode": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "qamw_decode": (_i32, [_p, _p, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _i32, _i64, _p]),
 }
 

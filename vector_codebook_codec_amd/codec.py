@@ -60,8 +60,19 @@ def qamw_calibrate_workspace_bytes(N: int, d: int, block: int) -> int:
     return int(_lib.load().qamw_calibrate_workspace_bytes(N, d, block))
 
 
-def qamw_encode_workspace_bytes(N: int) -> int:
-    return int(_lib.load().qamw_encode_workspace_bytes(N))
+def qamw_encode_workspace_bytes(N: int, d: int) -> int:
+    return int(_lib.load().qamw_encode_workspace_bytes(N, d))
+
+
+def qamw_plan_bytes(K: int) -> int:
+    return int(_lib.load().qamw_plan_bytes(K))
+
+
+def _codebook(codebook: torch.Tensor) -> int:
+    _dev(codebook, "codebook")
+    if codebook.dtype != torch.float32 or codebook.dim() != 2 or codebook.shape[1] != 2 or not codebook.is_contiguous():
+        raise ValueError("codebook must be a contiguous K x 2 float32 tensor")
+    return codebook.shape[0]
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
@@ -82,6 +93,22 @@ def load_codebook(K: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- entry points
+def qamw_build_plan(codebook: torch.Tensor, plan: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Nearest-centroid search plan for `codebook` (uint8 device buffer) for qamw_encode(plan=...)."""
+    K = _codebook(codebook)
+    need = qamw_plan_bytes(K)
+    if need <= 0:
+        raise ValueError(f"unsupported K={K}")
+    if plan is None:
+        plan = torch.empty(need, dtype=torch.uint8, device=codebook.device)
+    _dev(plan, "plan")
+    if plan.dtype != torch.uint8 or not plan.is_contiguous():
+        raise ValueError("plan must be a contiguous uint8 tensor")
+    _lib.check("qamw_build_plan", _lib.load().qamw_build_plan(
+        codebook.data_ptr(), K, plan.data_ptr(), plan.numel(), _stream(stream)))
+    return plan
+
+
 def qamw_calibrate(W: torch.Tensor, chan_rms: torch.Tensor, alpha: float, block: int, sign_seed: int,
                    s_out: Optional[torch.Tensor] = None, sigma_out: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None, stream=None):
@@ -107,22 +134,26 @@ def qamw_calibrate(W: torch.Tensor, chan_rms: torch.Tensor, alpha: float, block:
 
 
 def qamw_encode(W: torch.Tensor, s: torch.Tensor, sigma: torch.Tensor, block: int, sign_seed: int,
-                codebook: torch.Tensor, packed: Optional[torch.Tensor] = None,
-                rownorm_f16: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                stream=None):
-    """Returns (packed [N][row_words] int32 holding uint32 words, rownorm [N] int16 holding fp16 bits)."""
+                codebook: torch.Tensor, plan: Optional[torch.Tensor] = None,
+                packed: Optional[torch.Tensor] = None, rownorm_f16: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+    """Returns (packed [N][row_words] int32 holding uint32 words, rownorm [N] int16 holding fp16 bits).
+
+    `plan` (from qamw_build_plan for the same codebook) speeds up the nearest-centroid
+    search without changing the result; None searches the whole codebook."""
     N, d, ldw = _rows(W, "W")
     if W.dtype not in _WDT:
         raise ValueError("W must be float32 or bfloat16")
     _vec(s, "s", d)
     _vec(sigma, "sigma", d // 2)
-    _dev(codebook, "codebook")
-    if codebook.dtype != torch.float32 or codebook.dim() != 2 or codebook.shape[1] != 2 or not codebook.is_contiguous():
-        raise ValueError("codebook must be a contiguous K x 2 float32 tensor")
-    K = codebook.shape[0]
+    K = _codebook(codebook)
     rw = qamw_packed_row_words(d, K)
     if rw < 0:
         raise ValueError(f"unsupported K={K} or d={d}")
+    if plan is not None:
+        _dev(plan, "plan")
+        if plan.dtype != torch.uint8 or plan.numel() < qamw_plan_bytes(K):
+            raise ValueError("plan must be a uint8 tensor from qamw_build_plan for this K")
     if packed is None:
         packed = torch.empty((N, rw), dtype=torch.int32, device=W.device)
     if rownorm_f16 is None:
@@ -131,12 +162,13 @@ def qamw_encode(W: torch.Tensor, s: torch.Tensor, sigma: torch.Tensor, block: in
     if packed.dtype != torch.int32 or tuple(packed.shape) != (N, rw) or not packed.is_contiguous():
         raise ValueError(f"packed must be a contiguous int32 tensor of shape ({N}, {rw})")
     _vec(rownorm_f16, "rownorm_f16", N, torch.int16)
-    need = qamw_encode_workspace_bytes(N)
+    need = qamw_encode_workspace_bytes(N, d)
     if workspace is None:
         workspace = _workspace(need, W.device)
     _lib.check("qamw_encode", _lib.load().qamw_encode(
         W.data_ptr(), _WDT[W.dtype], N, d, ldw, s.data_ptr(), sigma.data_ptr(), int(block), int(sign_seed),
-        codebook.data_ptr(), K, packed.data_ptr(), rownorm_f16.data_ptr(), workspace.data_ptr(),
+        codebook.data_ptr(), K, None if plan is None else plan.data_ptr(), packed.data_ptr(),
+        rownorm_f16.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return packed, rownorm_f16
 
@@ -147,10 +179,7 @@ def qamw_decode(packed: torch.Tensor, rownorm_f16: torch.Tensor, d: int, s: Opti
     """Returns the decoded [N][d] matrix in out_dtype (fp32, bf16 or fp16)."""
     _dev(packed, "packed")
     N = packed.shape[0]
-    _dev(codebook, "codebook")
-    if codebook.dtype != torch.float32 or codebook.dim() != 2 or codebook.shape[1] != 2 or not codebook.is_contiguous():
-        raise ValueError("codebook must be a contiguous K x 2 float32 tensor")
-    K = codebook.shape[0]
+    K = _codebook(codebook)
     rw = qamw_packed_row_words(d, K)
     if packed.dtype != torch.int32 or tuple(packed.shape) != (N, rw) or not packed.is_contiguous():
         raise ValueError(f"packed must be a contiguous int32 tensor of shape ({N}, {rw})")

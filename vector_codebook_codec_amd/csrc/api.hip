@@ -1,0 +1,210 @@
+// C ABI of libqamw.so (declared in include/qamw.h): argument validation on
+// the host, then the stage launchers of calibrate.hip, encode.hip, plan.hip
+// and decode.hip on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+
+#include <cstdio>
+#include <string>
+
+#include "qamw.h"
+#include "qamw_internal.h"
+
+namespace qamw {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(QAMW_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return QAMW_OK;
+}
+
+int log2_exact(int64_t v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int l = 0;
+  while ((int64_t(1) << l) < v) ++l;
+  return l;
+}
+
+int check_matrix(int64_t N, int64_t d, int32_t block, int* L) {
+  if (N <= 0 || d <= 0) return fail(QAMW_EINVAL, "N and d must be positive (N=%lld d=%lld)", (long long)N, (long long)d);
+  // every wavefront index (rows x 1024-column windows) must fit in an int
+  if (N > kMaxDim || d > kMaxDim || N * ((d + 1023) / 1024) > (int64_t(1) << 30))
+    return fail(QAMW_EUNSUPPORTED, "matrix too large");
+  *L = log2_exact(block);
+  if (*L < 4 || *L > 10) return fail(QAMW_EUNSUPPORTED, "block must be a power of two in [16, 1024] (got %d)", block);
+  if (d % block) return fail(QAMW_EINVAL, "d=%lld is not a multiple of block=%d", (long long)d, block);
+  return QAMW_OK;
+}
+
+int check_weights(const void* W, int32_t wdt, int64_t d, int64_t ldw) {
+  if (!W) return fail(QAMW_EINVAL, "W is NULL");
+  if (wdt != QAMW_F32 && wdt != QAMW_BF16) return fail(QAMW_EUNSUPPORTED, "weight dtype %d not supported", wdt);
+  if (ldw < d) return fail(QAMW_EINVAL, "ldw=%lld < d=%lld", (long long)ldw, (long long)d);
+  if (!aligned16(W) || (ldw * elem_size(wdt)) % 16)
+    return fail(QAMW_EINVAL, "W must be 16-byte aligned with 16-byte aligned rows");
+  return QAMW_OK;
+}
+
+int check_codebook(const float* cb, int32_t K) {
+  if (!cb) return fail(QAMW_EINVAL, "codebook is NULL");
+  if (!aligned16(cb)) return fail(QAMW_EINVAL, "codebook must be 16-byte aligned");
+  if (K < 2 || K > 4096) return fail(QAMW_EUNSUPPORTED, "K=%d outside [2, 4096]", K);
+  return QAMW_OK;
+}
+
+}  // namespace qamw
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+using namespace qamw;
+
+extern "C" {
+
+int32_t qamw_index_bits(int32_t K) {
+  if (K < 2 || K > 4096) return -1;
+  int32_t b = 0;
+  while ((1 << b) < K) ++b;
+  return b;
+}
+
+int64_t qamw_packed_row_words(int64_t d, int32_t K) {
+  const int32_t B = qamw_index_bits(K);
+  if (B < 0 || d <= 0 || (d & 1) || d > kMaxDim) return -1;
+  const int64_t words = ((d / 2) * B + 31) / 32;
+  return (words + 3) / 4 * 4;
+}
+
+size_t qamw_calibrate_workspace_bytes(int64_t N, int64_t d, int32_t block) {
+  (void)block;
+  if (N <= 0 || d <= 0 || N > kMaxDim || d > kMaxDim) return 0;
+  return round_up((size_t)N * sizeof(double), 256) + calib_tiles(N) * (size_t)(d / 2) * sizeof(float);
+}
+
+size_t qamw_encode_workspace_bytes(int64_t N, int64_t d) {
+  if (N <= 0 || N > kMaxDim || d <= 0 || d > kMaxDim) return 0;
+  return round_up((size_t)N * sizeof(double), 256) + round_up((size_t)d * sizeof(float), 256) +
+         round_up((size_t)(d / 2) * sizeof(double), 256);
+}
+
+const char* qamw_status_string(int32_t status) {
+  switch (status) {
+    case QAMW_OK: return "ok";
+    case QAMW_EINVAL: return "invalid argument";
+    case QAMW_EUNSUPPORTED: return "unsupported argument";
+    case QAMW_EHIP: return "HIP runtime error";
+    case QAMW_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+const char* qamw_last_error(void) { return g_last_error.c_str(); }
+
+const char* qamw_version(void) { return "qamw 0.1 gfx950"; }
+
+int32_t qamw_calibrate(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, const float* chan_rms,
+                       float alpha, int32_t block, uint64_t sign_seed, float* s_out, float* sigma_out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int L = 0;
+  int rc = check_matrix(N, d, block, &L);
+  if (rc) return rc;
+  if ((rc = check_weights(W, wdtype, d, ldw))) return rc;
+  if (!chan_rms || !s_out || !sigma_out) return fail(QAMW_EINVAL, "chan_rms, s_out and sigma_out must be non-NULL");
+  if (!aligned16(s_out) || !aligned16(sigma_out)) return fail(QAMW_EINVAL, "s_out and sigma_out must be 16-byte aligned");
+  if (!isfinite(alpha)) return fail(QAMW_EINVAL, "alpha must be finite");
+  const size_t need = qamw_calibrate_workspace_bytes(N, d, block);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(QAMW_EWORKSPACE, "calibrate needs %zu bytes of 256-byte aligned workspace (got %zu)", need,
+                workspace_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  double* rho = (double*)workspace;
+  float* partial = (float*)((char*)workspace + round_up((size_t)N * sizeof(double), 256));
+  const int n = (int)N, dd = (int)d;
+  if ((rc = launch_scale(chan_rms, alpha, dd, s_out, st))) return rc;
+  if ((rc = launch_rownorm(W, wdtype, n, dd, ldw, s_out, rho, nullptr, st))) return rc;
+  if ((rc = launch_amplitude(L, W, wdtype, n, dd, ldw, s_out, sign_seed, rho, partial, st))) return rc;
+  return launch_sigma(partial, (int)calib_tiles(N), dd / 2, n, sigma_out, st);
+}
+
+size_t qamw_plan_bytes(int32_t K) {
+  if (K < 2 || K > 4096) return 0;
+  return plan_bytes(K);
+}
+
+int32_t qamw_build_plan(const float* codebook, int32_t K, void* plan, size_t plan_size, void* stream) {
+  int rc = check_codebook(codebook, K);
+  if (rc) return rc;
+  if (!plan || ((uintptr_t)plan & 255u)) return fail(QAMW_EINVAL, "plan must be non-NULL and 256-byte aligned");
+  if (plan_size < plan_bytes(K))
+    return fail(QAMW_EWORKSPACE, "plan needs %zu bytes (got %zu)", plan_bytes(K), plan_size);
+  return launch_build_plan(codebook, K, plan, (hipStream_t)stream);
+}
+
+int32_t qamw_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, const float* s,
+                    const float* sigma, int32_t block, uint64_t sign_seed, const float* codebook, int32_t K,
+                    const void* plan, uint32_t* packed, uint16_t* rownorm_f16, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int L = 0;
+  int rc = check_matrix(N, d, block, &L);
+  if (rc) return rc;
+  if ((rc = check_weights(W, wdtype, d, ldw))) return rc;
+  if ((rc = check_codebook(codebook, K))) return rc;
+  if (!s || !sigma || !packed || !rownorm_f16) return fail(QAMW_EINVAL, "s, sigma, packed and rownorm_f16 must be non-NULL");
+  if (!aligned16(s) || !aligned16(sigma) || !aligned16(packed))
+    return fail(QAMW_EINVAL, "s, sigma and packed must be 16-byte aligned");
+  if (plan && ((uintptr_t)plan & 255u)) return fail(QAMW_EINVAL, "plan must be 256-byte aligned");
+  const size_t need = qamw_encode_workspace_bytes(N, d);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(QAMW_EWORKSPACE, "encode needs %zu bytes of 256-byte aligned workspace (got %zu)", need, workspace_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  double* rho = (double*)ws;
+  ws += round_up((size_t)N * sizeof(double), 256);
+  float* f = (float*)ws;
+  ws += round_up((size_t)d * sizeof(float), 256);
+  double* isig = (double*)ws;
+  const int n = (int)N, dd = (int)d;
+  const int B = qamw_index_bits(K);
+  const int row_words = (int)qamw_packed_row_words(d, K);
+  if ((rc = launch_rownorm(W, wdtype, n, dd, ldw, s, rho, rownorm_f16, st))) return rc;
+  return launch_encode(L, W, wdtype, n, dd, ldw, s, sigma, sign_seed, codebook, (int)K, B, row_words, rho, f, isig,
+                       plan, packed, st);
+}
+
+int32_t qamw_decode(const uint32_t* packed, const uint16_t* rownorm_f16, int64_t N, int64_t d, const float* s,
+                    const float* sigma, int32_t block, uint64_t sign_seed, const float* codebook, int32_t K,
+                    void* W_out, int32_t out_dtype, int64_t ldo, void* stream) {
+  int L = 0;
+  int rc = check_matrix(N, d, block, &L);
+  if (rc) return rc;
+  if ((rc = check_codebook(codebook, K))) return rc;
+  if (!packed || !rownorm_f16 || !sigma || !W_out)
+    return fail(QAMW_EINVAL, "packed, rownorm_f16, sigma and W_out must be non-NULL");
+  if (out_dtype != QAMW_F32 && out_dtype != QAMW_BF16 && out_dtype != QAMW_F16)
+    return fail(QAMW_EUNSUPPORTED, "output dtype %d not supported", out_dtype);
+  if (ldo < d) return fail(QAMW_EINVAL, "ldo=%lld < d=%lld", (long long)ldo, (long long)d);
+  if (!aligned16(packed) || !aligned16(W_out) || (ldo * elem_size(out_dtype)) % 16 || !aligned16(sigma) ||
+      (s && !aligned16(s)))
+    return fail(QAMW_EINVAL, "packed, s, sigma and W_out must be 16-byte aligned with 16-byte aligned rows");
+  const int B = qamw_index_bits(K);
+  const int row_words = (int)qamw_packed_row_words(d, K);
+  return launch_decode(L, packed, rownorm_f16, (int)N, (int)d, s, sigma, sign_seed, codebook, (int)K, B, row_words,
+                       W_out, out_dtype, ldo, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,194 @@
+// Calibration kernels: channel scales, row norms, per-pair amplitude sums and
+// sigma ("QAM-W: Joint 2D Codebook Quantization for LLM Weights via Hadamard
+// Rotation and Activation-Aware Scaling"; Methodology: Activation-Aware
+// Scaling, Separation of Scale and Direction, Pairing and Calibration).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "qamw.h"
+#include "qamw_device.h"
+#include "qamw_internal.h"
+
+namespace qamw {
+
+// ---------------------------------------------------------------------------
+// s_j = r_j ^ alpha.  alpha = 0 gives exactly 1.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlockThreads) void scale_kernel(const float* __restrict__ r, float alpha,
+                                                              int d, float* __restrict__ s) {
+  const int j = blockIdx.x * kBlockThreads + threadIdx.x;
+  if (j < d) s[j] = (alpha == 0.0f) ? 1.0f : powf(r[j], alpha);
+}
+
+// ---------------------------------------------------------------------------
+// rho_n = sqrt(sum_j (W_nj s_j)^2), one wavefront per row.  W_nj s_j is exact
+// in fp64 (24-bit x 24-bit significands); squares and sums are fp64, reduced
+// in a fixed order, so rho is deterministic and accurate to ~1e-16.
+// Optionally writes the binary16 (RNE) row norm.
+// ---------------------------------------------------------------------------
+template <typename Tin>
+__global__ __launch_bounds__(kBlockThreads) void rownorm_kernel(const Tin* __restrict__ W, int64_t ldw,
+                                                                int N, int d, const float* __restrict__ s,
+                                                                double* __restrict__ rho,
+                                                                uint16_t* __restrict__ rho_f16) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const int nchunks = d >> 4;
+  const Tin* row = W + (int64_t)n * ldw;
+  double acc = 0.0;
+  for (int c = lane; c < nchunks; c += kWave) {
+    float x[16];
+    load_chunk(row + c * kChunk, x);
+    const float4* sp = reinterpret_cast<const float4*>(s + c * kChunk);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float4 sv = sp[v];
+      const float sc[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double w = (double)x[4 * v + i] * (double)sc[i];
+        acc = fma(w, w, acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) {
+    const double r = sqrt(acc);
+    rho[n] = r;
+    if (rho_f16) rho_f16[n] = f64_to_f16_bits(r);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Calibration, pass 2: per (window, row tile) wavefront, accumulate the pair
+// amplitudes |z_{n,k}| of the normalised rotated rows over the tile.
+// partial[t][k] = sum_{n in tile t} hypot(y_{n,2k}, y_{n,2k+1}) / (sqrt(b) rho_n)
+// ---------------------------------------------------------------------------
+template <int L, typename Tin>
+__global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
+    const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ s, uint64_t seed,
+    const double* __restrict__ rho, float* __restrict__ partial) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nchunks = d >> 4;
+  const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
+  const int ntiles = (N + kCalibRowsPerTile - 1) / kCalibRowsPerTile;
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (gw >= nwin * ntiles) return;
+  const int win = gw % nwin;
+  const int tile = gw / nwin;
+  const int c = win * kWinChunks + lane;
+  const bool active = c < nchunks;   // whole Hadamard blocks are active or not
+  const int co = win * kWinChunks + BlockOut<L>::chunk(lane);
+  const double sqrt_b = sqrt((double)(1 << L));
+
+  float f[16];
+  if (active) column_scale(s, seed, c * kChunk, f);
+  float acc[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) acc[p] = 0.0f;
+
+  const int n0 = tile * kCalibRowsPerTile;
+  const int n1 = min(N, n0 + kCalibRowsPerTile);
+  // 1 / (sqrt(b) rho_n) of the tile's rows, one per lane
+  float inv_lane = 0.0f;
+  if (lane < n1 - n0) {
+    const double r = rho[n0 + lane];
+    inv_lane = r > 0.0 ? (float)(1.0 / (sqrt_b * r)) : 0.0f;
+  }
+  float nxt[16];
+  if (active) load_chunk(W + (int64_t)n0 * ldw + c * kChunk, nxt);
+  for (int n = n0; n < n1; ++n) {
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = active ? nxt[i] * f[i] : 0.0f;
+    if (active && n + 1 < n1) load_chunk(W + (int64_t)(n + 1) * ldw + c * kChunk, nxt);
+    fwht_block<L>(x, lane);
+    const float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv_lane), n - n0));
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const float a = x[2 * p], b = x[2 * p + 1];
+      acc[p] += sqrtf(__builtin_fmaf(a, a, b * b)) * inv;
+    }
+  }
+  if (active) {
+    float4* out = reinterpret_cast<float4*>(partial + (int64_t)tile * (d >> 1) + co * kPairsPerLane);
+    out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
+// sigma_k = (sum over tiles, fp64, fixed order) / (N sqrt(pi/2)).  A
+// workgroup owns 16 columns; thread (column, slice) sums tiles slice,
+// slice + 16, ... and the 16 slice sums are then added in slice order.
+constexpr int kSigmaSlices = 16;
+__global__ __launch_bounds__(kBlockThreads) void sigma_kernel(const float* __restrict__ partial, int ntiles,
+                                                              int half_d, int N, float* __restrict__ sigma) {
+  __shared__ double part[kSigmaSlices][kBlockThreads / kSigmaSlices];
+  const int col_in = threadIdx.x % (kBlockThreads / kSigmaSlices);
+  const int slice = threadIdx.x / (kBlockThreads / kSigmaSlices);
+  const int k = blockIdx.x * (kBlockThreads / kSigmaSlices) + col_in;
+  double acc = 0.0;
+  if (k < half_d)
+    for (int t = slice; t < ntiles; t += kSigmaSlices) acc += (double)partial[(int64_t)t * half_d + k];
+  part[slice][col_in] = acc;
+  __syncthreads();
+  if (slice == 0 && k < half_d) {
+    double tot = 0.0;
+#pragma unroll
+    for (int q = 0; q < kSigmaSlices; ++q) tot += part[q][col_in];
+    sigma[k] = (float)(tot / ((double)N * 1.2533141373155002512078826));  // sqrt(pi/2)
+  }
+}
+
+// ===========================================================================
+// launchers
+// ===========================================================================
+int launch_scale(const float* r, float alpha, int d, float* s, hipStream_t st) {
+  hipLaunchKernelGGL(scale_kernel, dim3((d + kBlockThreads - 1) / kBlockThreads), dim3(kBlockThreads), 0, st, r,
+                     alpha, d, s);
+  return check_launch("scale_kernel");
+}
+
+int launch_rownorm(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, double* rho,
+                   uint16_t* rho_f16, hipStream_t st) {
+  const dim3 grid(grid_for_waves(N)), blk(kBlockThreads);
+  if (wdt == QAMW_F32)
+    hipLaunchKernelGGL(rownorm_kernel<float>, grid, blk, 0, st, (const float*)W, ldw, N, d, s, rho, rho_f16);
+  else
+    hipLaunchKernelGGL(rownorm_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)W, ldw, N, d, s, rho, rho_f16);
+  return check_launch("rownorm_kernel");
+}
+
+template <int L>
+struct LaunchAmplitude {
+  static int run(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, uint64_t seed,
+                 const double* rho, float* partial, hipStream_t st) {
+    const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
+    const int64_t waves = (int64_t)nwin * (int64_t)calib_tiles(N);
+    if (wdt == QAMW_F32)
+      hipLaunchKernelGGL((amplitude_kernel<L, float>), dim3(grid_for_waves(waves)), dim3(kBlockThreads), 0, st,
+                         (const float*)W, ldw, N, d, s, seed, rho, partial);
+    else
+      hipLaunchKernelGGL((amplitude_kernel<L, uint16_t>), dim3(grid_for_waves(waves)), dim3(kBlockThreads), 0,
+                         st, (const uint16_t*)W, ldw, N, d, s, seed, rho, partial);
+    return check_launch("amplitude_kernel");
+  }
+};
+
+int launch_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, uint64_t seed,
+                     const double* rho, float* partial, hipStream_t st) {
+  return dispatch_L<LaunchAmplitude>(L, W, wdt, N, d, ldw, s, seed, rho, partial, st);
+}
+
+int launch_sigma(const float* partial, int ntiles, int half_d, int N, float* sigma, hipStream_t st) {
+  const int cols = kBlockThreads / kSigmaSlices;
+  hipLaunchKernelGGL(sigma_kernel, dim3((half_d + cols - 1) / cols), dim3(kBlockThreads), 0, st, partial, ntiles,
+                     half_d, N, sigma);
+  return check_launch("sigma_kernel");
+}
+
+}  // namespace qamw

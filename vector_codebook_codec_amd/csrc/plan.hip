@@ -1,0 +1,229 @@
+// Nearest-centroid search plan: for a fixed codebook, a grid over the plane
+// whose every cell lists the centroids that can be the nearest one, under the
+// encode kernels' fp32 scores, for some point of the cell.  The encode kernel
+// then scores only a pair's cell list instead of all K centroids and returns
+// the same index as the exhaustive search ("QAM-W: Joint 2D Codebook
+// Quantization for LLM Weights via Hadamard Rotation and Activation-Aware
+// Scaling"; Methodology: Joint 2D Quantization -- the nearest centroid in one
+// 2D codebook).
+//
+// Why the lists are complete.  Let Q be a cell enlarged by eta, U(Q) =
+// min_c max_{z in Q} |z - c|^2.  For z in Q the exact nearest centroid c*
+// has |z - c*|^2 <= U(Q).  The kernels decide on fp32 scores S32(c) with
+// |S32(c) - (|c|^2/2 - z.c)| <= e(c), e(c) <= 2^-24 (2.5 |c|^2 + 2 |z||c|)
+// for the FMA sequence they use, so their choice c32 (and every centroid tied
+// with it) satisfies |z - c32|^2 <= |z - c*|^2 + 2 (e(c32) + e(c*)), hence
+// min_{z in Q} |z - c32|^2 <= U(Q) + delta whenever delta covers that slack.
+// A list holds exactly the centroids passing that test, in ascending index
+// order, so the first minimum met while scanning it is the lowest-index fp32
+// minimum over the whole codebook.  delta is 1e-5 (Cmax + R sqrt 2)^2, about
+// 10x the slack bound for points inside the grid; eta (1e-4) covers the fp32
+// rounding of the cell index.  Points outside the grid, and cells whose list
+// would exceed lmax entries, fall back to the exhaustive scan.
+//
+// Construction is two-level and gives the same lists as testing every
+// centroid against every cell.  A supercell SQ (16 x 16 cells) first keeps
+// the centroids with min_{z in SQ} |z - c|^2 <= U(SQ) + 2 delta.  Every
+// centroid of a cell's list passes that test (SQ contains Q, so its minimum
+// distances are smaller and U(SQ) >= U(Q)), and so does the centroid that
+// attains U(Q); the cells then test only the supercell's survivors.
+//
+// Layout (plan_bytes(K) bytes, 256-byte aligned):
+//   [0, 256)     PlanHeader (+ Cmax as fp64 at byte 128)
+//   [256, ...)   uint16 lists [G*G][lmax], one 16- or 32-byte record per cell.
+//                Entry i is 16 c_i | nibble_i: c_i the i-th listed centroid
+//                (16 c_i is its byte offset in the encode kernel's LDS copy of
+//                the codebook), nibble_0 = count - 1, nibble_1 = 1 when the
+//                cell overflows (scan the whole codebook), other nibbles 0;
+//                entries past the count repeat the last listed centroid.
+// Cell (ix, iy) covers [-R + ix s, -R + (ix+1) s) x [-R + iy s, ...), s = 2R/G;
+// its index is ix * G + iy.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qamw.h"
+#include "qamw_device.h"
+#include "qamw_internal.h"
+
+namespace qamw {
+
+struct PlanHeader {
+  float R;
+  float cells_per_unit;   // G / (2 R)
+  int G;
+  int lmax;
+  int K;
+};
+static_assert(offsetof(PlanHeader, K) == kPlanHeaderKOffset, "the encode kernel reads K at this offset");
+
+constexpr double kPlanEta = 1e-4;
+constexpr int kSuper = 16;                         // cells per supercell side
+constexpr int kSuperG = kPlanG / kSuper;           // supercells per axis
+constexpr int kSuperMax = 2048;                    // survivors kept; more -> test all K
+constexpr int kPlanThreads = 256;
+constexpr int kPlanWaves = kPlanThreads / kWave;
+
+// Largest centroid radius (one workgroup).
+__global__ __launch_bounds__(kBlockThreads) void codebook_radius_kernel(const float* __restrict__ cb, int K,
+                                                                        PlanHeader* hdr, double* cmax_out) {
+  __shared__ double part[kBlockThreads];
+  double m = 0.0;
+  for (int c = threadIdx.x; c < K; c += kBlockThreads) {
+    const double cx = cb[2 * c], cy = cb[2 * c + 1];
+    m = fmax(m, sqrt(cx * cx + cy * cy));
+  }
+  part[threadIdx.x] = m;
+  __syncthreads();
+  for (int off = kBlockThreads / 2; off > 0; off >>= 1) {
+    if (threadIdx.x < off) part[threadIdx.x] = fmax(part[threadIdx.x], part[threadIdx.x + off]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    *cmax_out = part[0];
+    hdr->R = kPlanR;
+    hdr->cells_per_unit = (float)kPlanG / (2.0f * kPlanR);
+    hdr->G = kPlanG;
+    hdr->lmax = plan_lmax(K);
+    hdr->K = K;
+  }
+}
+
+// Axis-aligned box [x0, x1] x [y0, y1] against centroid (cx, cy).
+struct Box {
+  double x0, x1, y0, y1;
+  __device__ double dmax2(double cx, double cy) const {
+    const double ax = fmax((cx - x0) * (cx - x0), (cx - x1) * (cx - x1));
+    const double ay = fmax((cy - y0) * (cy - y0), (cy - y1) * (cy - y1));
+    return ax + ay;
+  }
+  __device__ double dmin2(double cx, double cy) const {
+    const double dx = fmax(fmax(x0 - cx, cx - x1), 0.0);
+    const double dy = fmax(fmax(y0 - cy, cy - y1), 0.0);
+    return dx * dx + dy * dy;
+  }
+};
+
+__device__ __forceinline__ Box cell_box(int ix0, int iy0, int ncells) {
+  const double s = 2.0 * (double)kPlanR / kPlanG;
+  return Box{-(double)kPlanR + ix0 * s - kPlanEta, -(double)kPlanR + (ix0 + ncells) * s + kPlanEta,
+             -(double)kPlanR + iy0 * s - kPlanEta, -(double)kPlanR + (iy0 + ncells) * s + kPlanEta};
+}
+
+__device__ __forceinline__ double wave_min(double v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v = fmin(v, __shfl_xor(v, off));
+  return v;
+}
+
+// One workgroup per supercell: its survivors (ascending, with coordinates)
+// into LDS, then one lane per cell scans them.
+__global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* __restrict__ cb, int K, int lmax,
+                                                                  const double* __restrict__ cmax,
+                                                                  uint16_t* __restrict__ lists) {
+  static_assert(kSuper * kSuper == kPlanThreads, "one lane per cell of a supercell");
+  __shared__ uint16_t surv[kSuperMax];
+  __shared__ float2 survc[kSuperMax];
+  __shared__ uint16_t cell_list[kPlanThreads][16];
+  __shared__ double red[kPlanWaves];
+  __shared__ int wcount[kPlanWaves];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int sx = blockIdx.x / kSuperG, sy = blockIdx.x % kSuperG;
+  const double reach = *cmax + (double)kPlanR * 1.4142135623730951;
+  const double delta = 1e-5 * reach * reach;
+
+  // ---- supercell survivors
+  const Box sq = cell_box(sx * kSuper, sy * kSuper, kSuper);
+  double U = INFINITY;
+  for (int c = tid; c < K; c += kPlanThreads) U = fmin(U, sq.dmax2(cb[2 * c], cb[2 * c + 1]));
+  U = wave_min(U);
+  if (lane == 0) red[wave] = U;
+  __syncthreads();
+  U = red[0];
+#pragma unroll
+  for (int w = 1; w < kPlanWaves; ++w) U = fmin(U, red[w]);
+  const double slim = U + 2.0 * delta;
+  int nsurv = 0;
+  for (int c0 = 0; c0 < K; c0 += kPlanThreads) {
+    const int c = c0 + tid;
+    float cx = 0.0f, cy = 0.0f;
+    if (c < K) { cx = cb[2 * c]; cy = cb[2 * c + 1]; }
+    const bool pred = c < K && sq.dmin2(cx, cy) <= slim;
+    const uint64_t m = __ballot(pred);
+    __syncthreads();                        // previous round's wcount reads are done
+    if (lane == 0) wcount[wave] = __popcll(m);
+    __syncthreads();
+    int before = nsurv, total = nsurv;
+#pragma unroll
+    for (int w = 0; w < kPlanWaves; ++w) {
+      before += (w < wave) ? wcount[w] : 0;
+      total += wcount[w];
+    }
+    const int pos = before + __popcll(m & ((1ull << lane) - 1ull));
+    if (pred && pos < kSuperMax) { surv[pos] = (uint16_t)c; survc[pos] = make_float2(cx, cy); }
+    nsurv = total;
+  }
+  __syncthreads();
+  const bool all = nsurv > kSuperMax;       // too many survivors: test every centroid
+  const int ns = all ? K : nsurv;
+  auto survivor = [&](int j, double& x, double& y) -> int {
+    if (all) { x = cb[2 * j]; y = cb[2 * j + 1]; return j; }
+    const float2 v = survc[j];             // same address in every lane: broadcast
+    x = v.x; y = v.y;
+    return surv[j];
+  };
+
+  // ---- one lane per cell
+  const int ix = sx * kSuper + tid / kSuper, iy = sy * kSuper + tid % kSuper;
+  const Box cq = cell_box(ix, iy, 1);
+  double Uc = INFINITY;
+  for (int j = 0; j < ns; ++j) {
+    double x, y;
+    survivor(j, x, y);
+    Uc = fmin(Uc, cq.dmax2(x, y));
+  }
+  const double lim = Uc + delta;
+  uint16_t* mine = cell_list[tid];
+  int count = 0;
+  for (int j = 0; j < ns; ++j) {
+    double x, y;
+    const int c = survivor(j, x, y);
+    if (cq.dmin2(x, y) <= lim) {
+      if (count < lmax) mine[count] = (uint16_t)(c * 16);
+      ++count;
+    }
+  }
+  // ---- the record: tail repeats the last entry (rescoring it never wins a strict "<")
+  const bool overflow = count > lmax || count == 0;   // (a cell always lists at least one centroid)
+  uint32_t words[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t lo = 0, hi = 0;
+    if (2 * q < lmax && !overflow) {
+      lo = mine[min(2 * q, count - 1)];
+      hi = mine[min(2 * q + 1, count - 1)];
+    }
+    words[q] = lo | (hi << 16);
+  }
+  words[0] |= overflow ? (1u << 16) : (uint32_t)(count - 1);
+  uint4* out = reinterpret_cast<uint4*>(lists + ((size_t)ix * kPlanG + iy) * lmax);
+  out[0] = make_uint4(words[0], words[1], words[2], words[3]);
+  if (lmax == 16) out[1] = make_uint4(words[4], words[5], words[6], words[7]);
+}
+
+int launch_build_plan(const float* cb, int K, void* plan, hipStream_t st) {
+  char* base = (char*)plan;
+  PlanHeader* hdr = (PlanHeader*)base;
+  double* cmax = (double*)(base + 128);     // scratch inside the header block
+  uint16_t* lists = (uint16_t*)(base + kPlanHeaderBytes);
+  hipLaunchKernelGGL(codebook_radius_kernel, dim3(1), dim3(kBlockThreads), 0, st, cb, K, hdr, cmax);
+  int rc = check_launch("codebook_radius_kernel");
+  if (rc) return rc;
+  hipLaunchKernelGGL(build_plan_kernel, dim3(kSuperG * kSuperG), dim3(kPlanThreads), 0, st, cb, K, plan_lmax(K),
+                     (const double*)cmax, lists);
+  return check_launch("build_plan_kernel");
+}
+
+}  // namespace qamw

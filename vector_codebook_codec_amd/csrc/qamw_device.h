@@ -338,6 +338,26 @@ struct BlockOut {
   static __device__ __forceinline__ float sign(int lane) { return lane_out_sign<NB>(lane & ((1 << NB) - 1)); }
 };
 
+// Per-lane column factors f_j = s_j * eps_j for the lane's 16 columns.
+__device__ __forceinline__ void column_scale(const float* __restrict__ s, uint64_t seed, int col0,
+                                             float f[16]) {
+  const float4* sp = reinterpret_cast<const float4*>(s + col0);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float4 sv = sp[v];
+    f[4 * v + 0] = sv.x * sign_eps(seed, col0 + 4 * v + 0);
+    f[4 * v + 1] = sv.y * sign_eps(seed, col0 + 4 * v + 1);
+    f[4 * v + 2] = sv.z * sign_eps(seed, col0 + 4 * v + 2);
+    f[4 * v + 3] = sv.w * sign_eps(seed, col0 + 4 * v + 3);
+  }
+}
+
+// 1 / (sqrt(b) rho sigma) in fp64, rounded once to fp32; 0 when rho sigma == 0.
+__device__ __forceinline__ float pair_normaliser(double rho, float sigma, double sqrt_b) {
+  const double den = rho * (double)sigma * sqrt_b;
+  return den > 0.0 ? (float)(1.0 / den) : 0.0f;
+}
+
 // fp64 -> IEEE binary16 bits with one round-to-nearest-even step.
 __device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {
   const uint64_t u = (uint64_t)__double_as_longlong(x);

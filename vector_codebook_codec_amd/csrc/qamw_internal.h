@@ -1,0 +1,69 @@
+// Host-side interfaces shared by the translation units of libqamw.so:
+// launch helpers of each stage, argument checks and error reporting.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qamw.h"
+
+namespace qamw {
+
+constexpr int kBlockThreads = 256;                   // 4 wavefronts per workgroup (most kernels)
+constexpr int kWavesPerBlock = kBlockThreads / 64;
+constexpr int kCalibRowsPerTile = 16;                // rows per amplitude partial sum
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+// ---- errors (the message of the calling thread's last failure)
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int check_launch(const char* what);
+
+// ---- small helpers
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int elem_size(int32_t dt) { return dt == QAMW_F32 ? 4 : (dt == QAMW_BF16 || dt == QAMW_F16) ? 2 : 0; }
+inline size_t calib_tiles(int64_t N) { return (size_t)((N + kCalibRowsPerTile - 1) / kCalibRowsPerTile); }
+inline unsigned grid_for_waves(int64_t waves) { return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock); }
+
+// Call Launch<L>::run(args...) for the Hadamard block size 2^L, 16 <= b <= 1024.
+template <template <int> class Launch, typename... A>
+int dispatch_L(int L, A&&... args) {
+  switch (L) {
+    case 4: return Launch<4>::run(args...);
+    case 5: return Launch<5>::run(args...);
+    case 6: return Launch<6>::run(args...);
+    case 7: return Launch<7>::run(args...);
+    case 8: return Launch<8>::run(args...);
+    case 9: return Launch<9>::run(args...);
+    case 10: return Launch<10>::run(args...);
+    default: return fail(QAMW_EUNSUPPORTED, "block size");
+  }
+}
+
+// ---- nearest-centroid search plan (see plan.hip)
+constexpr int kPlanG = 512;                  // grid cells per axis over [-kPlanR, kPlanR)
+constexpr float kPlanR = 5.0f;
+constexpr size_t kPlanHeaderBytes = 256;
+constexpr size_t kPlanHeaderKOffset = 16;    // int32 K inside the header (plan.hip)
+__host__ __device__ inline int plan_lmax(int K) { return K <= 2048 ? 8 : 16; }
+inline size_t plan_bytes(int K) {
+  return kPlanHeaderBytes + (size_t)kPlanG * kPlanG * plan_lmax(K) * sizeof(uint16_t);
+}
+
+// ---- stage launchers (enqueue on `st`, return a qamw_status)
+int launch_scale(const float* r, float alpha, int d, float* s, hipStream_t st);
+int launch_rownorm(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, double* rho,
+                   uint16_t* rho_f16, hipStream_t st);
+int launch_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, uint64_t seed,
+                     const double* rho, float* partial, hipStream_t st);
+int launch_sigma(const float* partial, int ntiles, int half_d, int N, float* sigma, hipStream_t st);
+int launch_encode(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, const float* sigma,
+                  uint64_t seed, const float* cb, int K, int B, int row_words, const double* rho, float* f,
+                  double* isig, const void* plan, uint32_t* packed, hipStream_t st);
+int launch_build_plan(const float* cb, int K, void* plan, hipStream_t st);
+int launch_decode(int L, const uint32_t* packed, const uint16_t* rho_f16, int N, int d, const float* s,
+                  const float* sigma, uint64_t seed, const float* cb, int K, int B, int row_words, void* out,
+                  int32_t odt, int64_t ldo, hipStream_t st);
+
+}  // namespace qamw
