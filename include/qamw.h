@@ -116,11 +116,12 @@ int32_t qamw_calibrate(const void* W, int32_t wdtype, int64_t N, int64_t d, int6
 /*
  * Nearest-centroid search plan (QAM-W, Methodology: Joint 2D Quantization).
  * An optional, codebook-specific acceleration structure for qamw_encode: a
- * 512 x 512 grid over [-5, 5)^2 whose cells list, in ascending index order,
- * every centroid that can be the nearest one (under qamw_encode's fp32
- * scores) for some point of the cell.  Encoding with a plan gives the same
- * indices, bit for bit, as encoding without one; pairs outside the grid and
- * cells with too many candidates fall back to scanning all K centroids.
+ * 512 x 512 grid over [-5, 5)^2 and a 256 x 256 grid over [-40, 40)^2 whose
+ * cells list, in ascending index order, every centroid that can be the
+ * nearest one (under qamw_encode's fp32 scores) for some point of the cell.
+ * Encoding with a plan gives the same indices, bit for bit, as encoding
+ * without one; pairs beyond both grids and cells with too many candidates
+ * fall back to scanning all K centroids.
  *
  * qamw_plan_bytes(K): bytes of device memory a plan for K centroids takes
  *   (0 for K outside [2, 4096]).  Host-only.

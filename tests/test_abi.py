@@ -58,10 +58,11 @@ def test_host_helpers(lib):
     assert lib.qamw_calibrate_workspace_bytes(4096, 11008, 256) == 4096 * 8 + 256 * 5504 * 4
     assert lib.qamw_calibrate_workspace_bytes(0, 16, 16) == 0
     assert lib.qamw_status_string(-4) == b"workspace missing or too small"
-    # header block + one uint16 record of lmax entries per cell of the 512 x 512 grid
-    assert lib.qamw_plan_bytes(256) == 256 + 512 ** 2 * 8 * 2
-    assert lib.qamw_plan_bytes(2048) == 256 + 512 ** 2 * 8 * 2
-    assert lib.qamw_plan_bytes(4096) == 256 + 512 ** 2 * 16 * 2
+    # header block + one uint16 record of lmax entries per cell of the fine
+    # 512 x 512 grid and of the outer 256 x 256 grid
+    assert lib.qamw_plan_bytes(256) == 256 + (512 ** 2 + 256 ** 2) * 8 * 2
+    assert lib.qamw_plan_bytes(2048) == 256 + (512 ** 2 + 256 ** 2) * 8 * 2
+    assert lib.qamw_plan_bytes(4096) == 256 + (512 ** 2 + 256 ** 2) * 16 * 2
     assert lib.qamw_plan_bytes(1) == 0 and lib.qamw_plan_bytes(4097) == 0
 
 
@@ -130,7 +131,7 @@ def test_decode_rejects(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(cb=None), -1), (dict(cb=MIS), -1), (dict(K=1), -2), (dict(K=5000), -2), (dict(plan=None), -1),
-    (dict(plan=WS + 16), -1), (dict(size=1000), -4), (dict(K=4096, size=256 + 512 ** 2 * 16), -4),
+    (dict(plan=WS + 16), -1), (dict(size=1000), -4), (dict(K=4096, size=256 + (512 ** 2 + 256 ** 2) * 16), -4),
 ])
 def test_build_plan_rejects(lib, kw, status):
     args = dict(cb=A, K=2048, plan=WS, size=1 << 23, stream=None)

@@ -348,107 +348,133 @@ def test_full_size_sampled(q, name):
 
 
 # ---------------------------------------------------------------- search plan
-PLAN_G, PLAN_R, PLAN_OVERFLOW = 512, 5.0, 255
+PLAN_OVERFLOW = 255
+GRIDS = {"fine": (512, 5.0), "outer": (256, 40.0)}     # cells per axis, half-width R
 
 
 def read_plan(q, C):
-    """Build the plan on the GPU and decode its per-cell records: entry i is
-    16 c_i | nibble_i with nibble_0 = count - 1 and nibble_1 = overflow."""
+    """Build the plan on the GPU and decode each grid's per-cell records:
+    entry i is 16 c_i | nibble_i with nibble_0 = count - 1 and nibble_1 =
+    overflow.  Returns {grid: (counts, lists of centroid indices)}, lmax."""
     K = C.shape[0]
     plan = q.qamw_build_plan(torch.from_numpy(C).to(DEV))
     torch.cuda.synchronize()
     raw = plan.cpu().numpy()
     lmax = 8 if K <= 2048 else 16
-    assert raw.size == q.qamw_plan_bytes(K) == 256 + PLAN_G ** 2 * lmax * 2
-    hdr_f = raw[:8].view(np.float32)
-    hdr_i = raw[8:20].view(np.int32)
-    assert hdr_f[0] == PLAN_R and hdr_f[1] == np.float32(PLAN_G / (2 * PLAN_R))
-    assert list(hdr_i) == [PLAN_G, lmax, K]
-    rec = raw[256:].view(np.uint16).reshape(PLAN_G ** 2, lmax).astype(np.int64)
-    nib = rec & 15
-    assert np.all(nib[:, 1] <= 1) and np.all(nib[:, 2:] == 0)
-    counts = np.where(nib[:, 1] == 1, PLAN_OVERFLOW, nib[:, 0] + 1)
-    return counts, rec >> 4, lmax
+    G1, G2 = GRIDS["fine"][0], GRIDS["outer"][0]
+    assert raw.size == q.qamw_plan_bytes(K) == 256 + (G1 ** 2 + G2 ** 2) * lmax * 2
+    hdr_f = raw[:32].view(np.float32)
+    hdr_i = raw[:32].view(np.int32)
+    assert hdr_f[0] == 5.0 and hdr_f[1] == np.float32(G1 / 10.0) and list(hdr_i[2:5]) == [G1, lmax, K]
+    assert hdr_f[5] == 40.0 and hdr_f[6] == np.float32(G2 / 80.0) and hdr_i[7] == G2
+    out, off = {}, 256
+    for name in ("fine", "outer"):
+        G = GRIDS[name][0]
+        rec = raw[off:off + G * G * lmax * 2].view(np.uint16).reshape(G * G, lmax).astype(np.int64)
+        off += G * G * lmax * 2
+        nib = rec & 15
+        assert np.all(nib[:, 1] <= 1) and np.all(nib[:, 2:] == 0)
+        out[name] = (np.where(nib[:, 1] == 1, PLAN_OVERFLOW, nib[:, 0] + 1), rec >> 4)
+    return out, lmax
 
 
-def cell_of(z):
-    """Cell index of points inside [-R, R)^2 (fp32 arithmetic, as the kernel)."""
-    cpu = np.float32(PLAN_G / (2 * PLAN_R))
+def cell_of(z, grid):
+    """Cell index of points inside the grid (fp32 arithmetic, as the kernel)."""
+    G, R = GRIDS[grid]
+    cpu = np.float32(G / (2 * R))
     zf = z.astype(np.float32)
-    ix = np.minimum(((zf[:, 0] + np.float32(PLAN_R)) * cpu).astype(np.int64), PLAN_G - 1)
-    iy = np.minimum(((zf[:, 1] + np.float32(PLAN_R)) * cpu).astype(np.int64), PLAN_G - 1)
-    return ix * PLAN_G + iy
+    ix = np.minimum(((zf[:, 0] + np.float32(R)) * cpu).astype(np.int64), G - 1)
+    iy = np.minimum(((zf[:, 1] + np.float32(R)) * cpu).astype(np.int64), G - 1)
+    return ix * G + iy
+
+
+def grid_of(z):
+    """Which grid the encode kernel consults for each point (None: full scan)."""
+    zf = z.astype(np.float32)
+    fine = (zf >= -5).all(1) & (zf < 5).all(1)
+    outer = (zf >= -40).all(1) & (zf < 40).all(1)
+    return fine, outer & ~fine
 
 
 @pytest.mark.parametrize("K", [2, 16, 256, 2048, 4096])
 def test_plan_lists_cover_near_minimisers(q, K):
     """Every centroid within 1e-6 (1 + |z|^2) of a point's minimum squared
-    distance (fp64 brute force) is in that point's cell list; lists are
-    strictly ascending, in range and zero-padded."""
+    distance (fp64 brute force) is in the list of the cell the encode kernel
+    consults for that point; lists are strictly ascending, in range, and their
+    tails repeat the last entry."""
     C = q.load_codebook(K)
-    counts, lists, lmax = read_plan(q, C)
-    say(f"case plan K={K}: {int((counts == PLAN_OVERFLOW).sum())} overflow cells, "
-        f"mean count {float(counts[counts != PLAN_OVERFLOW].mean()):.2f}")
-    ok_cells = counts != PLAN_OVERFLOW
-    assert np.all(counts[ok_cells] <= lmax) and np.all(counts[ok_cells] >= 1)
-    slot = np.arange(lmax)[None, :]
-    used = slot < counts[:, None]
-    # the unused tail repeats the last listed centroid
-    last = lists[np.arange(len(counts)), np.clip(counts, 1, lmax) - 1]
-    assert np.all((lists == last[:, None])[ok_cells][~used[ok_cells]])
-    assert np.all(lists[ok_cells] < K)
-    inc = np.diff(lists, axis=1) > 0
-    assert np.all(inc[ok_cells] | ~used[ok_cells][:, 1:])
+    grids, lmax = read_plan(q, C)
+    for name, (counts, lists) in grids.items():
+        say(f"case plan K={K} {name}: {int((counts == PLAN_OVERFLOW).sum())} overflow cells, "
+            f"max count {int(counts[counts != PLAN_OVERFLOW].max())}")
+        ok_cells = counts != PLAN_OVERFLOW
+        assert np.all(counts[ok_cells] <= lmax) and np.all(counts[ok_cells] >= 1)
+        used = np.arange(lmax)[None, :] < counts[:, None]
+        last = lists[np.arange(len(counts)), np.clip(counts, 1, lmax) - 1]
+        assert np.all((lists == last[:, None])[ok_cells][~used[ok_cells]])
+        assert np.all(lists[ok_cells] < K)
+        inc = np.diff(lists, axis=1) > 0
+        assert np.all(inc[ok_cells] | ~used[ok_cells][:, 1:])
     rng = np.random.default_rng(K)
-    edges = -PLAN_R + np.arange(PLAN_G) * (2 * PLAN_R / PLAN_G)
+    fine_edges = -5 + np.arange(512) * (10 / 512)
+    outer_edges = -40 + np.arange(256) * (80 / 256)
     z = np.concatenate([
-        rng.uniform(-PLAN_R, PLAN_R, (40000, 2)),
-        rng.standard_normal((40000, 2)),
-        # points on cell edges (both coordinates) and just inside the grid's far edge
-        np.stack([rng.choice(edges, 8000), rng.choice(edges, 8000)], 1),
-        np.stack([np.full(200, PLAN_R - 1e-6), rng.uniform(-PLAN_R, PLAN_R, 200)], 1),
+        rng.uniform(-5, 5, (30000, 2)),
+        rng.standard_normal((30000, 2)),
+        np.stack([rng.choice(fine_edges, 6000), rng.choice(fine_edges, 6000)], 1),
+        np.stack([np.full(200, 5 - 1e-6), rng.uniform(-5, 5, 200)], 1),
+        rng.uniform(-40, 40, (20000, 2)),
+        rng.standard_normal((10000, 2)) * 8,
+        np.stack([rng.choice(outer_edges, 4000), rng.choice(outer_edges, 4000)], 1),
     ])
+    fine, outer = grid_of(z)
     Cd = C.astype(np.float64)
-    for lo in range(0, len(z), 4000):
-        zz = z[lo:lo + 4000]
-        D = ((zz[:, None, :] - Cd[None, :, :]) ** 2).sum(-1)
-        near = D <= D.min(1, keepdims=True) + 1e-6 * (1 + (zz ** 2).sum(1, keepdims=True))
-        cells = cell_of(zz)
-        listed = np.zeros_like(near)
-        rows = np.repeat(np.arange(len(zz)), lmax)
-        cols = lists[cells].reshape(-1)
-        mask = used[cells].reshape(-1)
-        listed[rows[mask], cols[mask]] = True
-        listed[counts[cells] == PLAN_OVERFLOW] = True
-        assert not (near & ~listed).any(), "a near-minimising centroid is missing from its cell list"
+    for name, sel in (("fine", fine), ("outer", outer)):
+        counts, lists = grids[name]
+        zs = z[sel]
+        for lo in range(0, len(zs), 4000):
+            zz = zs[lo:lo + 4000]
+            D = ((zz[:, None, :] - Cd[None, :, :]) ** 2).sum(-1)
+            near = D <= D.min(1, keepdims=True) + 1e-6 * (1 + (zz ** 2).sum(1, keepdims=True))
+            cells = cell_of(zz, name)
+            listed = np.zeros_like(near)
+            rows = np.repeat(np.arange(len(zz)), lmax)
+            cols = lists[cells].reshape(-1)
+            mask = (np.arange(lmax)[None, :] < counts[cells][:, None]).reshape(-1)
+            listed[rows[mask], cols[mask]] = True
+            listed[counts[cells] == PLAN_OVERFLOW] = True
+            assert not (near & ~listed).any(), f"a near-minimising centroid is missing from a {name} cell list"
 
 
 def test_plan_overflow_and_outside_grid(q):
-    """Clustered centroids overflow their cells' lists and tiny sigma_k push
-    pairs outside the grid: both fall back to the full scan, bit-identical
-    to the exhaustive search and accepted by the oracle."""
+    """Clustered centroids overflow their cells' lists, moderately small
+    sigma_k put pairs on the outer grid and tiny ones beyond it: every case is
+    bit-identical to the exhaustive search and accepted by the oracle."""
     rng = np.random.default_rng(21)
     base = q.load_codebook(16)
     ang = rng.uniform(0, 2 * np.pi, 48)
     cluster = np.stack([0.3 + 1e-3 * np.cos(ang), -0.2 + 1e-3 * np.sin(ang)], 1)
     C = np.concatenate([base, cluster]).astype(np.float32)          # K = 64
-    counts, _, _ = read_plan(q, C)
+    grids, _ = read_plan(q, C)
+    counts = grids["fine"][0]
     assert (counts == PLAN_OVERFLOW).any()
     N, d, b = 64, 4096, 256
     W = (rng.standard_normal((N, d)) * 0.02).astype(np.float32)
     dev = lambda a: torch.from_numpy(a).to(DEV)
     s, sigma = q.qamw_calibrate(dev(W), dev(np.ones(d, np.float32)), 0.0, b, 5)
     sig_np = sigma.cpu().numpy().copy()
-    sig_np[::7] *= 1e-3                                                  # |z~| ~ 1e3: outside the grid
+    sig_np[::7] *= 1e-3                                                  # |z~| ~ 1e3: beyond both grids
+    sig_np[3::7] *= 0.15                                                 # |z~| ~ 5..30: outer grid
     sigma = dev(sig_np)
-    say("case plan overflow / outside grid")
+    say("case plan overflow / outer grid / outside")
     packed, rn = encode_both(q, dev(W), s, sigma, b, 5, dev(C))
     enc = O.encode(W, s.cpu().numpy(), sig_np, b, 5, C)
     zt = enc["zt"].reshape(-1, 2)
-    inside = (np.abs(zt) < PLAN_R).all(1)
-    in_overflow = inside.copy()
-    in_overflow[inside] = counts[cell_of(zt[inside])] == PLAN_OVERFLOW
-    say(f"  {int((~inside).sum())} pairs outside the grid, {int(in_overflow.sum())} in overflow cells")
-    assert (~inside).sum() > 1000 and in_overflow.sum() > 0
+    fine, outer = grid_of(zt)
+    in_overflow = fine.copy()
+    in_overflow[fine] = counts[cell_of(zt[fine], "fine")] == PLAN_OVERFLOW
+    say(f"  {int(outer.sum())} pairs on the outer grid, {int((~fine & ~outer).sum())} beyond it, "
+        f"{int(in_overflow.sum())} in overflow cells")
+    assert outer.sum() > 1000 and (~fine & ~outer).sum() > 1000 and in_overflow.sum() > 0
     idx = O.unpack(packed.cpu().numpy().view(np.uint32), C.shape[0], d)
     assert O.accept_index(zt, C, enc["idx"].reshape(-1), idx.reshape(-1)).all()

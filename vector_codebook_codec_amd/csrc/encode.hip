@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
 // cell, in ascending index order, with the same fp32 FMA sequence and a strict
 // "<", which returns the exhaustive search's index (the plan's lists contain
 // every centroid that can be the fp32 minimum in the cell).  Pairs outside the
-// grid or in overflowing cells scan the whole codebook.
+// grids or in overflowing cells scan the whole codebook.
 //
 // The codebook sits in LDS as (-cx, -cy, |c|^2/2, 0) per centroid, one
 // ds_read_b128 per candidate at the byte offset the list stores.  A lane's
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
     const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ f,
     const double* __restrict__ isig, const float* __restrict__ codebook, int K, int B, int row_words,
     const double* __restrict__ rho, const int* __restrict__ plan_K, const uint16_t* __restrict__ lists,
-    uint32_t* __restrict__ packed) {
+    const uint16_t* __restrict__ lists2, uint32_t* __restrict__ packed) {
   static_assert(LMAX % 8 == 0 && LMAX <= 16 && kPairsPerLane % PG == 0, "list and group sizes");
   __shared__ float4 cb4[KMAX];                                      // (-cx, -cy, |c|^2/2, 0)
   __shared__ uint16_t stage_all[kEncWaves * kWinPairs];             // 8 waves x 512 indices
@@ -315,6 +315,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
       encode_transform<L, Tin>(W, ldw, n, win, nchunks, f, isig, row_normaliser(rho[n], L), lane, zx, zy);
 
   const float cells_per_unit = (float)kPlanG / (2.0f * kPlanR);
+  const float cells_per_unit2 = (float)kPlanG2 / (2.0f * kPlanR2);
   const bool plan_ok = *plan_K == K;   // a plan built for another K: scan the whole codebook
 #pragma unroll
   for (int g = 0; g < kPairsPerLane; g += PG) {
@@ -324,12 +325,17 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
     for (int p = 0; p < PG; ++p) {
       const float x = zx[g + p], y = zy[g + p];
-      inside[p] = plan_ok && x >= -kPlanR && x < kPlanR && y >= -kPlanR && y < kPlanR;   // false for NaN
-      // the clamps change nothing inside the grid and keep the conversion in range outside it
+      // fine grid, else outer grid (comparisons are false for NaN)
+      const bool fine = x >= -kPlanR && x < kPlanR && y >= -kPlanR && y < kPlanR;
+      inside[p] = plan_ok && x >= -kPlanR2 && x < kPlanR2 && y >= -kPlanR2 && y < kPlanR2;
+      // the clamps change nothing inside a grid and keep the conversion in range outside it
       const int ix = min((int)(fminf(fmaxf(x + kPlanR, 0.0f), 2.0f * kPlanR) * cells_per_unit), kPlanG - 1);
       const int iy = min((int)(fminf(fmaxf(y + kPlanR, 0.0f), 2.0f * kPlanR) * cells_per_unit), kPlanG - 1);
-      const int cell = inside[p] ? ix * kPlanG + iy : 0;
-      const uint4* lp = reinterpret_cast<const uint4*>(lists + (size_t)cell * LMAX);
+      const int jx = min((int)(fminf(fmaxf(x + kPlanR2, 0.0f), 2.0f * kPlanR2) * cells_per_unit2), kPlanG2 - 1);
+      const int jy = min((int)(fminf(fmaxf(y + kPlanR2, 0.0f), 2.0f * kPlanR2) * cells_per_unit2), kPlanG2 - 1);
+      const uint16_t* rec = fine ? lists + (size_t)(ix * kPlanG + iy) * LMAX
+                                 : lists2 + (size_t)(inside[p] ? jx * kPlanG2 + jy : 0) * LMAX;
+      const uint4* lp = reinterpret_cast<const uint4*>(rec);
 #pragma unroll
       for (int q = 0; q < LMAX / 8; ++q) {
         const uint4 t = lp[q];
@@ -407,9 +413,10 @@ struct LaunchEncode {
       const char* base = (const char*)plan;
       const int* plan_K = (const int*)(base + kPlanHeaderKOffset);
       const uint16_t* lists = (const uint16_t*)(base + kPlanHeaderBytes);
+      const uint16_t* lists2 = (const uint16_t*)(base + plan_outer_offset(K));
 #define QAMW_PLAN_LAUNCH(TIN, KM, LM, PG)                                                                      \
   hipLaunchKernelGGL((encode_plan_kernel<L, TIN, KM, LM, PG>), grid, blk, 0, st, (const TIN*)W, ldw, N, d, f, \
-                     isig, cb, K, B, row_words, rho, plan_K, lists, packed)
+                     isig, cb, K, B, row_words, rho, plan_K, lists, lists2, packed)
       if (plan_lmax(K) == 8) {
         if (wdt == QAMW_F32) QAMW_PLAN_LAUNCH(float, 2048, 8, 8); else QAMW_PLAN_LAUNCH(uint16_t, 2048, 8, 8);
       } else {

@@ -22,22 +22,29 @@
 // would exceed lmax entries, fall back to the exhaustive scan.
 //
 // Construction is two-level and gives the same lists as testing every
-// centroid against every cell.  A supercell SQ (16 x 16 cells) first keeps
+// centroid against every cell.  A supercell SQ (a square block of cells) first keeps
 // the centroids with min_{z in SQ} |z - c|^2 <= U(SQ) + 2 delta.  Every
 // centroid of a cell's list passes that test (SQ contains Q, so its minimum
 // distances are smaller and U(SQ) >= U(Q)), and so does the centroid that
 // attains U(Q); the cells then test only the supercell's survivors.
 //
+// Two grids: a fine one (G = 512 over [-5, 5)^2) where nearly all normalised
+// pairs fall, and a coarse outer one (256 over [-40, 40)^2) for the few pairs
+// beyond it -- rows dominated by one large weight put a whole Hadamard block
+// there.  Each has its own delta (R = 5 or 40 in the formula above).
+//
 // Layout (plan_bytes(K) bytes, 256-byte aligned):
 //   [0, 256)     PlanHeader (+ Cmax as fp64 at byte 128)
-//   [256, ...)   uint16 lists [G*G][lmax], one 16- or 32-byte record per cell.
+//   [256, ...)   fine grid: uint16 lists [G*G][lmax], then the outer grid's
+//                [G2*G2][lmax]; one 16- or 32-byte record per cell.
 //                Entry i is 16 c_i | nibble_i: c_i the i-th listed centroid
 //                (16 c_i is its byte offset in the encode kernel's LDS copy of
 //                the codebook), nibble_0 = count - 1, nibble_1 = 1 when the
 //                cell overflows (scan the whole codebook), other nibbles 0;
 //                entries past the count repeat the last listed centroid.
-// Cell (ix, iy) covers [-R + ix s, -R + (ix+1) s) x [-R + iy s, ...), s = 2R/G;
-// its index is ix * G + iy.
+// In a grid of G cells per axis over [-R, R)^2, cell (ix, iy) covers
+// [-R + ix s, -R + (ix+1) s) x [-R + iy s, ...), s = 2R/G; its index is
+// ix * G + iy.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -56,12 +63,15 @@ struct PlanHeader {
   int G;
   int lmax;
   int K;
+  float R2;               // outer grid
+  float cells_per_unit2;
+  int G2;
 };
 static_assert(offsetof(PlanHeader, K) == kPlanHeaderKOffset, "the encode kernel reads K at this offset");
 
 constexpr double kPlanEta = 1e-4;
-constexpr int kSuper = 16;                         // cells per supercell side
-constexpr int kSuperG = kPlanG / kSuper;           // supercells per axis
+constexpr int kSuperFine = 16;                     // cells per supercell side, fine grid
+constexpr int kSuperOuter = 4;                     // and outer grid
 constexpr int kSuperMax = 2048;                    // survivors kept; more -> test all K
 constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / kWave;
@@ -88,6 +98,9 @@ __global__ __launch_bounds__(kBlockThreads) void codebook_radius_kernel(const fl
     hdr->G = kPlanG;
     hdr->lmax = plan_lmax(K);
     hdr->K = K;
+    hdr->R2 = kPlanR2;
+    hdr->cells_per_unit2 = (float)kPlanG2 / (2.0f * kPlanR2);
+    hdr->G2 = kPlanG2;
   }
 }
 
@@ -106,10 +119,10 @@ struct Box {
   }
 };
 
-__device__ __forceinline__ Box cell_box(int ix0, int iy0, int ncells) {
-  const double s = 2.0 * (double)kPlanR / kPlanG;
-  return Box{-(double)kPlanR + ix0 * s - kPlanEta, -(double)kPlanR + (ix0 + ncells) * s + kPlanEta,
-             -(double)kPlanR + iy0 * s - kPlanEta, -(double)kPlanR + (iy0 + ncells) * s + kPlanEta};
+__device__ __forceinline__ Box cell_box(double R, int G, int ix0, int iy0, int ncells) {
+  const double s = 2.0 * R / G;
+  return Box{-R + ix0 * s - kPlanEta, -R + (ix0 + ncells) * s + kPlanEta,
+             -R + iy0 * s - kPlanEta, -R + (iy0 + ncells) * s + kPlanEta};
 }
 
 __device__ __forceinline__ double wave_min(double v) {
@@ -118,24 +131,29 @@ __device__ __forceinline__ double wave_min(double v) {
   return v;
 }
 
-// One workgroup per supercell: its survivors (ascending, with coordinates)
-// into LDS, then one lane per cell scans them.
+// One workgroup per supercell (S x S cells) of a G x G grid over [-R, R)^2:
+// the supercell's survivors (ascending, with coordinates) into LDS, then a
+// group of LPC = 256 / S^2 lanes per cell scans them.
+template <int S>
 __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* __restrict__ cb, int K, int lmax,
-                                                                  const double* __restrict__ cmax,
+                                                                  float Rf, int G, const double* __restrict__ cmax,
                                                                   uint16_t* __restrict__ lists) {
-  static_assert(kSuper * kSuper == kPlanThreads, "one lane per cell of a supercell");
+  constexpr int LPC = kPlanThreads / (S * S);
+  static_assert(LPC >= 1 && LPC * S * S == kPlanThreads && kWave % LPC == 0, "cell groups tile the wavefronts");
   __shared__ uint16_t surv[kSuperMax];
   __shared__ float2 survc[kSuperMax];
-  __shared__ uint16_t cell_list[kPlanThreads][16];
+  __shared__ uint16_t cell_list[S * S][16];
   __shared__ double red[kPlanWaves];
   __shared__ int wcount[kPlanWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int sx = blockIdx.x / kSuperG, sy = blockIdx.x % kSuperG;
-  const double reach = *cmax + (double)kPlanR * 1.4142135623730951;
+  const int nsuper = G / S;
+  const int sx = blockIdx.x / nsuper, sy = blockIdx.x % nsuper;
+  const double R = Rf;
+  const double reach = *cmax + R * 1.4142135623730951;
   const double delta = 1e-5 * reach * reach;
 
   // ---- supercell survivors
-  const Box sq = cell_box(sx * kSuper, sy * kSuper, kSuper);
+  const Box sq = cell_box(R, G, sx * S, sy * S, S);
   double U = INFINITY;
   for (int c = tid; c < K; c += kPlanThreads) U = fmin(U, sq.dmax2(cb[2 * c], cb[2 * c + 1]));
   U = wave_min(U);
@@ -170,31 +188,41 @@ __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* _
   const int ns = all ? K : nsurv;
   auto survivor = [&](int j, double& x, double& y) -> int {
     if (all) { x = cb[2 * j]; y = cb[2 * j + 1]; return j; }
-    const float2 v = survc[j];             // same address in every lane: broadcast
+    const float2 v = survc[j];
     x = v.x; y = v.y;
     return surv[j];
   };
 
-  // ---- one lane per cell
-  const int ix = sx * kSuper + tid / kSuper, iy = sy * kSuper + tid % kSuper;
-  const Box cq = cell_box(ix, iy, 1);
+  // ---- LPC lanes per cell: survivors j = sub, sub + LPC, ...
+  const int qc = tid / LPC, sub = tid % LPC;
+  const int ix = sx * S + qc / S, iy = sy * S + qc % S;
+  const Box cq = cell_box(R, G, ix, iy, 1);
   double Uc = INFINITY;
-  for (int j = 0; j < ns; ++j) {
+  for (int j = sub; j < ns; j += LPC) {
     double x, y;
     survivor(j, x, y);
     Uc = fmin(Uc, cq.dmax2(x, y));
   }
+#pragma unroll
+  for (int off = LPC / 2; off > 0; off >>= 1) Uc = fmin(Uc, __shfl_xor(Uc, off));   // within the group
   const double lim = Uc + delta;
-  uint16_t* mine = cell_list[tid];
+  uint16_t* mine = cell_list[qc];
+  const int gshift = lane & ~(LPC - 1);
+  const uint64_t gmask = (LPC == 64) ? ~0ull : ((1ull << LPC) - 1ull);
   int count = 0;
-  for (int j = 0; j < ns; ++j) {
-    double x, y;
-    const int c = survivor(j, x, y);
-    if (cq.dmin2(x, y) <= lim) {
-      if (count < lmax) mine[count] = (uint16_t)(c * 16);
-      ++count;
-    }
+  for (int j0 = 0; j0 < ns; j0 += LPC) {    // same trip count in every lane (ballot below)
+    const int j = j0 + sub;
+    double x = 0.0, y = 0.0;
+    int c = 0;
+    if (j < ns) c = survivor(j, x, y);
+    const bool pred = j < ns && cq.dmin2(x, y) <= lim;
+    const uint64_t gm = (__ballot(pred) >> gshift) & gmask;
+    const int pos = count + __popcll(gm & ((1ull << sub) - 1ull));
+    if (pred && pos < lmax) mine[pos] = (uint16_t)(c * 16);
+    count += __popcll(gm);
   }
+  __syncthreads();
+  if (sub != 0) return;                      // no barriers follow
   // ---- the record: tail repeats the last entry (rescoring it never wins a strict "<")
   const bool overflow = count > lmax || count == 0;   // (a cell always lists at least one centroid)
   uint32_t words[8];
@@ -208,7 +236,7 @@ __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* _
     words[q] = lo | (hi << 16);
   }
   words[0] |= overflow ? (1u << 16) : (uint32_t)(count - 1);
-  uint4* out = reinterpret_cast<uint4*>(lists + ((size_t)ix * kPlanG + iy) * lmax);
+  uint4* out = reinterpret_cast<uint4*>(lists + ((size_t)ix * G + iy) * lmax);
   out[0] = make_uint4(words[0], words[1], words[2], words[3]);
   if (lmax == 16) out[1] = make_uint4(words[4], words[5], words[6], words[7]);
 }
@@ -217,12 +245,19 @@ int launch_build_plan(const float* cb, int K, void* plan, hipStream_t st) {
   char* base = (char*)plan;
   PlanHeader* hdr = (PlanHeader*)base;
   double* cmax = (double*)(base + 128);     // scratch inside the header block
-  uint16_t* lists = (uint16_t*)(base + kPlanHeaderBytes);
   hipLaunchKernelGGL(codebook_radius_kernel, dim3(1), dim3(kBlockThreads), 0, st, cb, K, hdr, cmax);
   int rc = check_launch("codebook_radius_kernel");
   if (rc) return rc;
-  hipLaunchKernelGGL(build_plan_kernel, dim3(kSuperG * kSuperG), dim3(kPlanThreads), 0, st, cb, K, plan_lmax(K),
-                     (const double*)cmax, lists);
+  // fine grid: 16 x 16-cell supercells, one lane per cell; outer grid (larger
+  // cells, so more survivors per supercell): 4 x 4-cell supercells, 16 lanes per cell
+  static_assert(kPlanG % kSuperFine == 0 && kPlanG2 % kSuperOuter == 0, "grids are whole supercells");
+  hipLaunchKernelGGL(build_plan_kernel<kSuperFine>, dim3((kPlanG / kSuperFine) * (kPlanG / kSuperFine)),
+                     dim3(kPlanThreads), 0, st, cb, K, plan_lmax(K), kPlanR, kPlanG, (const double*)cmax,
+                     (uint16_t*)(base + kPlanHeaderBytes));
+  if ((rc = check_launch("build_plan_kernel"))) return rc;
+  hipLaunchKernelGGL(build_plan_kernel<kSuperOuter>, dim3((kPlanG2 / kSuperOuter) * (kPlanG2 / kSuperOuter)),
+                     dim3(kPlanThreads), 0, st, cb, K, plan_lmax(K), kPlanR2, kPlanG2, (const double*)cmax,
+                     (uint16_t*)(base + plan_outer_offset(K)));
   return check_launch("build_plan_kernel");
 }
 

@@ -41,14 +41,20 @@ int dispatch_L(int L, A&&... args) {
   }
 }
 
-// ---- nearest-centroid search plan (see plan.hip)
-constexpr int kPlanG = 512;                  // grid cells per axis over [-kPlanR, kPlanR)
+// ---- nearest-centroid search plan (see plan.hip): a fine grid and a coarse
+// outer grid, both square and centred on the origin
+constexpr int kPlanG = 512;                  // fine grid: cells per axis over [-kPlanR, kPlanR)
 constexpr float kPlanR = 5.0f;
+constexpr int kPlanG2 = 256;                 // outer grid: cells per axis over [-kPlanR2, kPlanR2)
+constexpr float kPlanR2 = 40.0f;
 constexpr size_t kPlanHeaderBytes = 256;
 constexpr size_t kPlanHeaderKOffset = 16;    // int32 K inside the header (plan.hip)
 __host__ __device__ inline int plan_lmax(int K) { return K <= 2048 ? 8 : 16; }
-inline size_t plan_bytes(int K) {
+inline size_t plan_outer_offset(int K) {
   return kPlanHeaderBytes + (size_t)kPlanG * kPlanG * plan_lmax(K) * sizeof(uint16_t);
+}
+inline size_t plan_bytes(int K) {
+  return plan_outer_offset(K) + (size_t)kPlanG2 * kPlanG2 * plan_lmax(K) * sizeof(uint16_t);
 }
 
 // ---- stage launchers (enqueue on `st`, return a qamw_status)
