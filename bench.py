@@ -3,15 +3,19 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 One step = the whole codec path over one matrix already resident in HBM:
-qamw_calibrate (s, sigma) -> qamw_encode (row norms, nearest centroid, pack)
--> qamw_decode (fp32 output).  The default workload is the 4096 x 11008 bf16
+qamw_calibrate (s, sigma) -> qamw_build_plan (search plan for the codebook)
+-> qamw_encode_prepare (row norms, column and pair factors) ->
+qamw_encode_indices (rotation, nearest centroid, packing) -> qamw_decode
+(fp32 output).  The default workload is the 4096 x 11008 bf16
 down-projection-shaped matrix (Student-t(5) entries, std 0.02; K = 2048,
 Hadamard block 256).  Prints one JSON line.
 
 value         weights per second of the whole step (Gweights/s)
-roofline      the dominant kernel (encode): algorithmic fp32 flops
-              (pairs x K x 4 per launch) / its mean launch time, against the
-              MI355X fp32 vector peak (157.3 TFLOP/s)
+roofline      the dominant kernel (encode_plan_kernel): algorithmic HBM bytes
+              (W read + packed write) / its mean launch time from HIP events
+              on the launch stream, against 8 TB/s
+valu_view     the same launch against the fp32 vector peak, counting the
+              exhaustive search's pairs x K x 4 flops
 cpu_baseline  the fp64 NumPy oracle, single-threaded, on a 160-row sample of
               the same workload (calibrate + encode + decode of those rows)
 """
@@ -33,9 +37,9 @@ import workloads  # noqa: E402
 
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_kernel_4096x11008_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "vector_codebook_codec_amd", "csrc", f)
                   for f in ("encode.hip", "qamw_device.h", "qamw_internal.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_plan_kernel_4096x11008_traffic.txt")
 
 
 def measured_traffic(workload):
@@ -126,27 +130,27 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     def step(marks=None):
-        if marks is not None:
-            marks[0].record(stream)
+        def mark(i):
+            if marks is not None:
+                marks[i].record(stream)
+        mark(0)
         q.qamw_calibrate(W, r, wl.alpha, b, wl.sign_seed, s, sigma, ws_cal, stream)
-        if marks is not None:
-            marks[1].record(stream)
+        mark(1)
         q.qamw_build_plan(Ct, plan, stream)
-        if marks is not None:
-            marks[2].record(stream)
-        q.qamw_encode(W, s, sigma, b, wl.sign_seed, Ct, plan, packed, rn, ws_enc, stream)
-        if marks is not None:
-            marks[3].record(stream)
+        mark(2)
+        q.qamw_encode_prepare(W, s, sigma, b, wl.sign_seed, rn, ws_enc, stream)
+        mark(3)
+        q.qamw_encode_indices(W, b, Ct, ws_enc, plan, packed, stream)
+        mark(4)
         q.qamw_decode(packed, rn, d, s, sigma, b, wl.sign_seed, Ct, out=out, stream=stream)
-        if marks is not None:
-            marks[4].record(stream)
+        mark(5)
 
     for i in range(args.warmup):
         step()
         print(f"warmup step {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
 
-    marks = [[ev() for _ in range(5)] for _ in range(args.steps)]
+    marks = [[ev() for _ in range(6)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(marks[i])
@@ -154,24 +158,22 @@ def main():
     wall = time.perf_counter() - t0
     print(f"timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
-    cal_ms = float(np.mean([m[0].elapsed_time(m[1]) for m in marks]))
-    plan_ms = float(np.mean([m[1].elapsed_time(m[2]) for m in marks]))
-    enc_ms = float(np.mean([m[2].elapsed_time(m[3]) for m in marks]))
-    dec_ms = float(np.mean([m[3].elapsed_time(m[4]) for m in marks]))
+    seg = lambda i: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in marks]))
+    cal_ms, plan_ms, prep_ms, idx_ms, dec_ms = (seg(i) for i in range(5))
+    enc_ms = prep_ms + idx_ms
     step_ms = wall * 1e3 / args.steps
 
     # the exhaustive search (no plan) for comparison; same indices, bit for bit
     packed_x = torch.empty_like(packed)
-    rn_x = torch.empty_like(rn)
     exh = []
     for _ in range(args.exhaustive_reps):
         a, z = ev(), ev()
         a.record(stream)
-        q.qamw_encode(W, s, sigma, b, wl.sign_seed, Ct, None, packed_x, rn_x, ws_enc, stream)
+        q.qamw_encode_indices(W, b, Ct, ws_enc, None, packed_x, stream)
         z.record(stream)
         torch.cuda.synchronize()
         exh.append(a.elapsed_time(z))
-    if exh and not (torch.equal(packed_x, packed) and torch.equal(rn_x, rn)):
+    if exh and not torch.equal(packed_x, packed):
         raise RuntimeError("planned and exhaustive encodes disagree")
     exh_ms = float(np.median(exh)) if exh else None
 
@@ -195,8 +197,10 @@ def main():
 
     B = q.qamw_index_bits(K)
     P = N * d // 2
-    enc_flops = P * K * 4.0
-    achieved_tflops = enc_flops / (enc_ms * 1e-3) / 1e12
+    in_bytes = 2 if wl.wdtype == "bf16" else 4
+    enc_bytes = N * d * in_bytes + N * rw * 4             # W read + packed write (qamw_encode_indices)
+    enc_gbs = enc_bytes / (idx_ms * 1e-3) / 1e9
+    exh_flops = P * K * 4.0                               # exhaustive search: K evaluations x 4 flops per pair
     dec_bytes = N * d * 4 + N * rw * 4 + N * 2            # fp32 out + packed + row norms
     weights = N * d
     res = {
@@ -216,12 +220,25 @@ def main():
                                f"r~LogNormal(0,1.2), alpha={wl.alpha}, block={b}, K={K}, fp32 decode",
                    "N": N, "d": d, "K": K, "block": b, "bits_per_index": B, "in_dtype": wl.wdtype,
                    "out_dtype": "f32"},
-        "roofline": {"bound": "alu", "kernel": "encode_kernel (qamw_encode; includes its row-norm pre-pass)",
-                     "achieved": achieved_tflops, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tflops / PEAK_FP32_TFLOPS, "traffic": measured_traffic(wl.name),
-                     "algorithmic": f"{P} pairs x {K} centroids x 4 flops = {enc_flops:.4g} per launch"},
-        "per_entry_ms": {"calibrate": cal_ms, "build_plan": plan_ms, "encode": enc_ms, "decode": dec_ms},
-        "encode_exhaustive_ms": exh_ms,
+        "roofline": {"bound": "hbm",
+                     "kernel": "encode_plan_kernel (qamw_encode_indices with a search plan)",
+                     "achieved": enc_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": enc_gbs / PEAK_HBM_GBS,
+                     "traffic": measured_traffic(wl.name),
+                     "algorithmic": f"W read {N * d * in_bytes} B + packed write {N * rw * 4} B "
+                                    f"= {enc_bytes} B per launch ({in_bytes} + {B}/16 B per weight)"},
+        "valu_view": {
+            "exhaustive_equivalent_flops": exh_flops,
+            "encode_indices_tflops": exh_flops / (idx_ms * 1e-3) / 1e12,
+            "encode_indices_frac_of_fp32_peak": exh_flops / (idx_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+            "calibrate_plan_encode_frac_of_fp32_peak":
+                exh_flops / ((cal_ms + plan_ms + enc_ms) * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+            "exhaustive_encode_indices_ms": exh_ms,
+            "exhaustive_frac_of_fp32_peak": None if exh_ms is None else
+                exh_flops / (exh_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+            "note": "pairs x K x 4 flops (the exhaustive nearest-centroid search) per unit time; the plan "
+                    "reaches the same indices with a few candidates per pair"},
+        "per_entry_ms": {"calibrate": cal_ms, "build_plan": plan_ms, "encode_prepare": prep_ms,
+                         "encode_indices": idx_ms, "decode": dec_ms},
         "encode_gweights_s": weights / ((cal_ms + plan_ms + enc_ms) * 1e-3) / 1e9,
         "decode_gweights_s": weights / (dec_ms * 1e-3) / 1e9,
         "decode_cold": None if dec_cold_ms is None else {

@@ -161,6 +161,31 @@ int32_t qamw_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qamw_encode in two phases, for callers that time or reuse them separately.
+ *
+ * qamw_encode_prepare (QAM-W, Methodology: Separation of Scale and Direction;
+ * Pairing and Calibration): row norms rho_n = ||W_n diag(s)||_2 (fp64 into
+ * the workspace, binary16 bits RNE into rownorm_f16 [N]), the per-column
+ * factors eps_j s_j and the pair factors 1 / sigma_k (into the workspace).
+ * Arguments as for qamw_encode.
+ *
+ * qamw_encode_indices (QAM-W, Methodology: Deterministic Rotation; Joint 2D
+ * Quantization): rotation, normalisation, nearest centroid and packing of W
+ * into packed, reading the factors from a workspace that qamw_encode_prepare
+ * filled for the same W, s, sigma, block and sign_seed, earlier on the same
+ * stream (or otherwise ordered before this call).  The workspace is only
+ * read.  Arguments as for qamw_encode.
+ *
+ * qamw_encode is exactly qamw_encode_prepare followed by qamw_encode_indices.
+ */
+int32_t qamw_encode_prepare(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
+                            const float* s, const float* sigma, int32_t block, uint64_t sign_seed,
+                            uint16_t* rownorm_f16, void* workspace, size_t workspace_bytes, void* stream);
+int32_t qamw_encode_indices(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, int32_t block,
+                            const float* codebook, int32_t K, const void* plan, uint32_t* packed,
+                            const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode (QAM-W, Methodology: Decoding).
  *   packed, rownorm_f16, N, d, block, sign_seed, codebook, K  as produced by
  *             qamw_encode; indices >= K (never produced) are clamped to K - 1

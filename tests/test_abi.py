@@ -82,6 +82,42 @@ def _encode(lib, **kw):
                            args["rn"], args["ws"], args["ws_bytes"], args["stream"])
 
 
+def _prepare(lib, **kw):
+    args = dict(W=A, wdt=1, N=8, d=256, ldw=256, s=A, sigma=A, block=128, seed=0, rn=A, ws=WS,
+                ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return lib.qamw_encode_prepare(args["W"], args["wdt"], args["N"], args["d"], args["ldw"], args["s"],
+                                   args["sigma"], args["block"], args["seed"], args["rn"], args["ws"],
+                                   args["ws_bytes"], args["stream"])
+
+
+def _indices(lib, **kw):
+    args = dict(W=A, wdt=1, N=8, d=256, ldw=256, block=128, cb=A, K=256, plan=None, packed=A, ws=WS,
+                ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return lib.qamw_encode_indices(args["W"], args["wdt"], args["N"], args["d"], args["ldw"], args["block"],
+                                   args["cb"], args["K"], args["plan"], args["packed"], args["ws"],
+                                   args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block=8), -2), (dict(N=0), -1), (dict(W=MIS), -1), (dict(s=None), -1), (dict(sigma=MIS), -1),
+    (dict(rn=None), -1), (dict(ws=None), -4), (dict(ws_bytes=8), -4), (dict(ws=WS + 16), -4), (dict(wdt=2), -2),
+])
+def test_encode_prepare_rejects(lib, kw, status):
+    assert _prepare(lib, **kw) == status
+    assert lib.qamw_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block=8), -2), (dict(K=1), -2), (dict(cb=MIS), -1), (dict(packed=None), -1), (dict(packed=MIS), -1),
+    (dict(plan=WS + 64), -1), (dict(ws=None), -4), (dict(ws_bytes=100), -4), (dict(ldw=100), -1),
+])
+def test_encode_indices_rejects(lib, kw, status):
+    assert _indices(lib, **kw) == status
+    assert lib.qamw_last_error()
+
+
 def _calibrate(lib, **kw):
     args = dict(W=A, wdt=0, N=8, d=256, ldw=256, r=A, alpha=0.5, block=128, seed=0, s=A, sigma=A,
                 ws=WS, ws_bytes=1 << 20, stream=None)

@@ -478,3 +478,20 @@ def test_plan_overflow_and_outside_grid(q):
     assert outer.sum() > 1000 and (~fine & ~outer).sum() > 1000 and in_overflow.sum() > 0
     idx = O.unpack(packed.cpu().numpy().view(np.uint32), C.shape[0], d)
     assert O.accept_index(zt, C, enc["idx"].reshape(-1), idx.reshape(-1)).all()
+
+
+def test_encode_phases_match_encode(q):
+    """qamw_encode_prepare + qamw_encode_indices give qamw_encode's outputs,
+    with and without a plan, and the workspace is reusable across codebooks."""
+    wl = workloads.get("c1_256x512")
+    W = to_dev(wl.W, wl.wdtype)
+    s, sigma = q.qamw_calibrate(W, torch.from_numpy(wl.r).to(DEV), wl.alpha, wl.block, wl.sign_seed)
+    rn, ws = q.qamw_encode_prepare(W, s, sigma, wl.block, wl.sign_seed)
+    for K in (wl.K, 16):
+        Ct = torch.from_numpy(q.load_codebook(K)).to(DEV)
+        packed, rn_ref = q.qamw_encode(W, s, sigma, wl.block, wl.sign_seed, Ct)
+        for plan in (None, q.qamw_build_plan(Ct)):
+            got = q.qamw_encode_indices(W, wl.block, Ct, ws, plan=plan)
+            torch.cuda.synchronize()
+            assert torch.equal(got, packed)
+        assert torch.equal(rn, rn_ref)

@@ -12,6 +12,8 @@ from .codec import (  # noqa: F401
     qamw_calibrate_workspace_bytes,
     qamw_decode,
     qamw_encode,
+    qamw_encode_indices,
+    qamw_encode_prepare,
     qamw_encode_workspace_bytes,
     qamw_index_bits,
     qamw_packed_row_words,

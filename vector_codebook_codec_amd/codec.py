@@ -173,6 +173,54 @@ def qamw_encode(W: torch.Tensor, s: torch.Tensor, sigma: torch.Tensor, block: in
     return packed, rownorm_f16
 
 
+def qamw_encode_prepare(W: torch.Tensor, s: torch.Tensor, sigma: torch.Tensor, block: int, sign_seed: int,
+                        rownorm_f16: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        stream=None):
+    """Encode phase 1: returns (rownorm [N] int16 holding fp16 bits, workspace for qamw_encode_indices)."""
+    N, d, ldw = _rows(W, "W")
+    if W.dtype not in _WDT:
+        raise ValueError("W must be float32 or bfloat16")
+    _vec(s, "s", d)
+    _vec(sigma, "sigma", d // 2)
+    if rownorm_f16 is None:
+        rownorm_f16 = torch.empty(N, dtype=torch.int16, device=W.device)
+    _vec(rownorm_f16, "rownorm_f16", N, torch.int16)
+    if workspace is None:
+        workspace = _workspace(qamw_encode_workspace_bytes(N, d), W.device)
+    _lib.check("qamw_encode_prepare", _lib.load().qamw_encode_prepare(
+        W.data_ptr(), _WDT[W.dtype], N, d, ldw, s.data_ptr(), sigma.data_ptr(), int(block), int(sign_seed),
+        rownorm_f16.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return rownorm_f16, workspace
+
+
+def qamw_encode_indices(W: torch.Tensor, block: int, codebook: torch.Tensor, workspace: torch.Tensor,
+                        plan: Optional[torch.Tensor] = None, packed: Optional[torch.Tensor] = None, stream=None):
+    """Encode phase 2 from a workspace filled by qamw_encode_prepare: returns packed [N][row_words] int32."""
+    N, d, ldw = _rows(W, "W")
+    if W.dtype not in _WDT:
+        raise ValueError("W must be float32 or bfloat16")
+    K = _codebook(codebook)
+    rw = qamw_packed_row_words(d, K)
+    if rw < 0:
+        raise ValueError(f"unsupported K={K} or d={d}")
+    if plan is not None:
+        _dev(plan, "plan")
+        if plan.dtype != torch.uint8 or plan.numel() < qamw_plan_bytes(K):
+            raise ValueError("plan must be a uint8 tensor from qamw_build_plan for this K")
+    if packed is None:
+        packed = torch.empty((N, rw), dtype=torch.int32, device=W.device)
+    _dev(packed, "packed")
+    if packed.dtype != torch.int32 or tuple(packed.shape) != (N, rw) or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous int32 tensor of shape ({N}, {rw})")
+    _dev(workspace, "workspace")
+    _lib.check("qamw_encode_indices", _lib.load().qamw_encode_indices(
+        W.data_ptr(), _WDT[W.dtype], N, d, ldw, int(block), codebook.data_ptr(), K,
+        None if plan is None else plan.data_ptr(), packed.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return packed
+
+
 def qamw_decode(packed: torch.Tensor, rownorm_f16: torch.Tensor, d: int, s: Optional[torch.Tensor],
                 sigma: torch.Tensor, block: int, sign_seed: int, codebook: torch.Tensor,
                 out_dtype=torch.float32, out: Optional[torch.Tensor] = None, stream=None):

@@ -155,10 +155,69 @@ int32_t qamw_build_plan(const float* codebook, int32_t K, void* plan, size_t pla
   return launch_build_plan(codebook, K, plan, (hipStream_t)stream);
 }
 
+struct EncodeWorkspace {
+  double* rho;    // [N] fp64 row norms
+  float* f;       // [d] eps_j s_j
+  double* isig;   // [d/2] 1 / sigma_k
+};
+
+static EncodeWorkspace encode_workspace(void* workspace, int64_t N, int64_t d) {
+  char* ws = (char*)workspace;
+  EncodeWorkspace e;
+  e.rho = (double*)ws;
+  ws += round_up((size_t)N * sizeof(double), 256);
+  e.f = (float*)ws;
+  ws += round_up((size_t)d * sizeof(float), 256);
+  e.isig = (double*)ws;
+  return e;
+}
+
+static int check_encode_workspace(const void* workspace, size_t workspace_bytes, int64_t N, int64_t d) {
+  const size_t need = qamw_encode_workspace_bytes(N, d);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(QAMW_EWORKSPACE, "encode needs %zu bytes of 256-byte aligned workspace (got %zu)", need,
+                workspace_bytes);
+  return QAMW_OK;
+}
+
+int32_t qamw_encode_prepare(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, const float* s,
+                            const float* sigma, int32_t block, uint64_t sign_seed, uint16_t* rownorm_f16,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  int L = 0;
+  int rc = check_matrix(N, d, block, &L);
+  if (rc) return rc;
+  if ((rc = check_weights(W, wdtype, d, ldw))) return rc;
+  if (!s || !sigma || !rownorm_f16) return fail(QAMW_EINVAL, "s, sigma and rownorm_f16 must be non-NULL");
+  if (!aligned16(s) || !aligned16(sigma)) return fail(QAMW_EINVAL, "s and sigma must be 16-byte aligned");
+  if ((rc = check_encode_workspace(workspace, workspace_bytes, N, d))) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const EncodeWorkspace e = encode_workspace(workspace, N, d);
+  if ((rc = launch_rownorm(W, wdtype, (int)N, (int)d, ldw, s, e.rho, rownorm_f16, st))) return rc;
+  return launch_encode_prep(s, sigma, sign_seed, (int)d, e.f, e.isig, st);
+}
+
+int32_t qamw_encode_indices(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, int32_t block,
+                            const float* codebook, int32_t K, const void* plan, uint32_t* packed,
+                            const void* workspace, size_t workspace_bytes, void* stream) {
+  int L = 0;
+  int rc = check_matrix(N, d, block, &L);
+  if (rc) return rc;
+  if ((rc = check_weights(W, wdtype, d, ldw))) return rc;
+  if ((rc = check_codebook(codebook, K))) return rc;
+  if (!packed) return fail(QAMW_EINVAL, "packed must be non-NULL");
+  if (!aligned16(packed)) return fail(QAMW_EINVAL, "packed must be 16-byte aligned");
+  if (plan && ((uintptr_t)plan & 255u)) return fail(QAMW_EINVAL, "plan must be 256-byte aligned");
+  if ((rc = check_encode_workspace(workspace, workspace_bytes, N, d))) return rc;
+  const EncodeWorkspace e = encode_workspace(const_cast<void*>(workspace), N, d);
+  return launch_encode(L, W, wdtype, (int)N, (int)d, ldw, e.f, e.isig, codebook, (int)K, qamw_index_bits(K),
+                       (int)qamw_packed_row_words(d, K), e.rho, plan, packed, (hipStream_t)stream);
+}
+
 int32_t qamw_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, const float* s,
                     const float* sigma, int32_t block, uint64_t sign_seed, const float* codebook, int32_t K,
                     const void* plan, uint32_t* packed, uint16_t* rownorm_f16, void* workspace,
                     size_t workspace_bytes, void* stream) {
+  // validate everything before the first launch
   int L = 0;
   int rc = check_matrix(N, d, block, &L);
   if (rc) return rc;
@@ -168,22 +227,12 @@ int32_t qamw_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t
   if (!aligned16(s) || !aligned16(sigma) || !aligned16(packed))
     return fail(QAMW_EINVAL, "s, sigma and packed must be 16-byte aligned");
   if (plan && ((uintptr_t)plan & 255u)) return fail(QAMW_EINVAL, "plan must be 256-byte aligned");
-  const size_t need = qamw_encode_workspace_bytes(N, d);
-  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
-    return fail(QAMW_EWORKSPACE, "encode needs %zu bytes of 256-byte aligned workspace (got %zu)", need, workspace_bytes);
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  double* rho = (double*)ws;
-  ws += round_up((size_t)N * sizeof(double), 256);
-  float* f = (float*)ws;
-  ws += round_up((size_t)d * sizeof(float), 256);
-  double* isig = (double*)ws;
-  const int n = (int)N, dd = (int)d;
-  const int B = qamw_index_bits(K);
-  const int row_words = (int)qamw_packed_row_words(d, K);
-  if ((rc = launch_rownorm(W, wdtype, n, dd, ldw, s, rho, rownorm_f16, st))) return rc;
-  return launch_encode(L, W, wdtype, n, dd, ldw, s, sigma, sign_seed, codebook, (int)K, B, row_words, rho, f, isig,
-                       plan, packed, st);
+  if ((rc = check_encode_workspace(workspace, workspace_bytes, N, d))) return rc;
+  if ((rc = qamw_encode_prepare(W, wdtype, N, d, ldw, s, sigma, block, sign_seed, rownorm_f16, workspace,
+                                workspace_bytes, stream)))
+    return rc;
+  return qamw_encode_indices(W, wdtype, N, d, ldw, block, codebook, K, plan, packed, workspace, workspace_bytes,
+                             stream);
 }
 
 int32_t qamw_decode(const uint32_t* packed, const uint16_t* rownorm_f16, int64_t N, int64_t d, const float* s,

@@ -5,6 +5,7 @@
 // Quantization).
 #include <hip/hip_runtime.h>
 
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -31,7 +32,7 @@ namespace qamw {
 // 16 of a tile's 32 centroids for one pair, folds them into a running minimum
 // with v_min3, and records the tile whenever that minimum drops strictly.
 // Afterwards the two half-waves' minima are combined, and the recorded tile is
-// rescanned on the VALU to find the first centroid whose score equals the
+// rescanned on the VALU for the smallest index whose score equals the
 // minimum: exact ties go to the lowest index.
 // ---------------------------------------------------------------------------
 constexpr int kEncThreads = 512;                       // 8 wavefronts per workgroup
@@ -249,11 +250,13 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
     const float bb = half ? best[2 * m2 + 1] : best[2 * m2];
     const int t0 = half ? tile_of_best[2 * m2 + 1] : tile_of_best[2 * m2];
     const float2 z = zbuf[(2 * m2 + half) * 32 + jcol];
-    int id = t0;
-    for (int cc = kTile - 1; cc >= 0; --cc) {
-      const int ci = t0 + cc;
+    // lane-rotated order keeps the lanes on different LDS banks (tiles start
+    // on multiples of 32 entries); the smallest matching index wins
+    int id = INT_MAX;
+    for (int cc = 0; cc < kTile; ++cc) {
+      const int ci = t0 + ((cc + lane) & (kTile - 1));
       const float sc = __builtin_fmaf(z.y, cby[ci], __builtin_fmaf(z.x, cbx[ci], cbh[ci]));
-      id = (sc == bb) ? ci : id;
+      id = (sc == bb) ? min(id, ci) : id;
     }
     idxv[m2] = (uint32_t)min(id, K - 1);
   }
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
 // repeats its last entry, which cannot win a strict "<" again).
 // ---------------------------------------------------------------------------
 template <int L, typename Tin, int KMAX, int LMAX, int PG>
-__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))) void encode_plan_kernel(
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(6))) void encode_plan_kernel(
     const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ f,
     const double* __restrict__ isig, const float* __restrict__ codebook, int K, int B, int row_words,
     const double* __restrict__ rho, const int* __restrict__ plan_K, const uint16_t* __restrict__ lists,
@@ -418,9 +421,9 @@ struct LaunchEncode {
   hipLaunchKernelGGL((encode_plan_kernel<L, TIN, KM, LM, PG>), grid, blk, 0, st, (const TIN*)W, ldw, N, d, f, \
                      isig, cb, K, B, row_words, rho, plan_K, lists, lists2, packed)
       if (plan_lmax(K) == 8) {
-        if (wdt == QAMW_F32) QAMW_PLAN_LAUNCH(float, 2048, 8, 8); else QAMW_PLAN_LAUNCH(uint16_t, 2048, 8, 8);
+        if (wdt == QAMW_F32) QAMW_PLAN_LAUNCH(float, 2048, 8, 4); else QAMW_PLAN_LAUNCH(uint16_t, 2048, 8, 4);
       } else {
-        if (wdt == QAMW_F32) QAMW_PLAN_LAUNCH(float, 4096, 16, 4); else QAMW_PLAN_LAUNCH(uint16_t, 4096, 16, 4);
+        if (wdt == QAMW_F32) QAMW_PLAN_LAUNCH(float, 4096, 16, 2); else QAMW_PLAN_LAUNCH(uint16_t, 4096, 16, 2);
       }
 #undef QAMW_PLAN_LAUNCH
       return check_launch("encode_plan_kernel");
@@ -437,15 +440,17 @@ struct LaunchEncode {
   }
 };
 
-int launch_encode(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, const float* sigma,
-                  uint64_t seed, const float* cb, int K, int B, int row_words, const double* rho, float* f,
-                  double* isig, const void* plan, uint32_t* packed, hipStream_t st) {
+int launch_encode_prep(const float* s, const float* sigma, uint64_t seed, int d, float* f, double* isig,
+                       hipStream_t st) {
   hipLaunchKernelGGL(encode_prep_kernel, dim3((unsigned)((d + kBlockThreads - 1) / kBlockThreads)),
                      dim3(kBlockThreads), 0, st, s, sigma, seed, d, f, isig);
-  const int rc = check_launch("encode_prep_kernel");
-  if (rc) return rc;
-  return dispatch_L<LaunchEncode>(L, W, wdt, N, d, ldw, (const float*)f, (const double*)isig, cb, K, B, row_words,
-                                  rho, plan, packed, st);
+  return check_launch("encode_prep_kernel");
+}
+
+int launch_encode(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const double* isig,
+                  const float* cb, int K, int B, int row_words, const double* rho, const void* plan, uint32_t* packed,
+                  hipStream_t st) {
+  return dispatch_L<LaunchEncode>(L, W, wdt, N, d, ldw, f, isig, cb, K, B, row_words, rho, plan, packed, st);
 }
 
 }  // namespace qamw

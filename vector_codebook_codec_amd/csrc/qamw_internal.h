@@ -64,9 +64,11 @@ int launch_rownorm(const void* W, int32_t wdt, int N, int d, int64_t ldw, const 
 int launch_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, uint64_t seed,
                      const double* rho, float* partial, hipStream_t st);
 int launch_sigma(const float* partial, int ntiles, int half_d, int N, float* sigma, hipStream_t st);
-int launch_encode(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, const float* sigma,
-                  uint64_t seed, const float* cb, int K, int B, int row_words, const double* rho, float* f,
-                  double* isig, const void* plan, uint32_t* packed, hipStream_t st);
+int launch_encode_prep(const float* s, const float* sigma, uint64_t seed, int d, float* f, double* isig,
+                       hipStream_t st);
+int launch_encode(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const double* isig,
+                  const float* cb, int K, int B, int row_words, const double* rho, const void* plan, uint32_t* packed,
+                  hipStream_t st);
 int launch_build_plan(const float* cb, int K, void* plan, hipStream_t st);
 int launch_decode(int L, const uint32_t* packed, const uint16_t* rho_f16, int N, int d, const float* s,
                   const float* sigma, uint64_t seed, const float* cb, int K, int B, int row_words, void* out,
