@@ -81,12 +81,13 @@ int32_t qamw_index_bits(int32_t K);
  * of 4; -1 for invalid d or K. */
 int64_t qamw_packed_row_words(int64_t d, int32_t K);
 
-/* Bytes of device workspace qamw_calibrate needs for an N x d matrix
- * (row norms in fp64 and per-row-tile partial sums of pair amplitudes). */
+/* Bytes of device workspace qamw_calibrate needs for an N x d matrix (row
+ * norms in fp64, column factors eps_j s_j and per-row-tile partial sums of
+ * pair amplitudes). */
 size_t qamw_calibrate_workspace_bytes(int64_t N, int64_t d, int32_t block);
 
 /* Bytes of device workspace qamw_encode needs for an N x d matrix (fp64 row
- * norms, fp32 per-column factors eps_j s_j, fp64 1 / sigma_k). */
+ * norms, fp32 per-column factors eps_j s_j, fp32 1 / sigma_k). */
 size_t qamw_encode_workspace_bytes(int64_t N, int64_t d);
 
 const char* qamw_status_string(int32_t status);

@@ -50,12 +50,12 @@ def test_host_helpers(lib):
     assert lib.qamw_packed_row_words(13824, 4096) == 2592
     assert lib.qamw_packed_row_words(12, 2048) == 4
     assert lib.qamw_packed_row_words(13, 2048) == -1
-    # rho (fp64) + column factors (fp32) + 1 / sigma (fp64), each 256-byte padded
-    assert lib.qamw_encode_workspace_bytes(4096, 11008) == 4096 * 8 + 11008 * 4 + 5504 * 8
+    # rho (fp64) + column factors (fp32) + 1 / sigma (fp32), each 256-byte padded
+    assert lib.qamw_encode_workspace_bytes(4096, 11008) == 4096 * 8 + 11008 * 4 + 5504 * 4
     assert lib.qamw_encode_workspace_bytes(5, 16) == 3 * 256
     assert lib.qamw_encode_workspace_bytes(0, 16) == 0
-    # rho (fp64, 256-byte padded) + ceil(N / 16) tiles x d/2 fp32
-    assert lib.qamw_calibrate_workspace_bytes(4096, 11008, 256) == 4096 * 8 + 256 * 5504 * 4
+    # rho (fp64) + column factors (fp32), each 256-byte padded, + ceil(N / 16) tiles x d/2 fp32
+    assert lib.qamw_calibrate_workspace_bytes(4096, 11008, 256) == 4096 * 8 + 11008 * 4 + 256 * 5504 * 4
     assert lib.qamw_calibrate_workspace_bytes(0, 16, 16) == 0
     assert lib.qamw_status_string(-4) == b"workspace missing or too small"
     # header block + one uint16 record of lmax entries per cell of the fine

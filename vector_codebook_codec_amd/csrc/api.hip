@@ -93,13 +93,14 @@ int64_t qamw_packed_row_words(int64_t d, int32_t K) {
 size_t qamw_calibrate_workspace_bytes(int64_t N, int64_t d, int32_t block) {
   (void)block;
   if (N <= 0 || d <= 0 || N > kMaxDim || d > kMaxDim) return 0;
-  return round_up((size_t)N * sizeof(double), 256) + calib_tiles(N) * (size_t)(d / 2) * sizeof(float);
+  return round_up((size_t)N * sizeof(double), 256) + round_up((size_t)d * sizeof(float), 256) +
+         calib_tiles(N) * (size_t)(d / 2) * sizeof(float);
 }
 
 size_t qamw_encode_workspace_bytes(int64_t N, int64_t d) {
   if (N <= 0 || N > kMaxDim || d <= 0 || d > kMaxDim) return 0;
   return round_up((size_t)N * sizeof(double), 256) + round_up((size_t)d * sizeof(float), 256) +
-         round_up((size_t)(d / 2) * sizeof(double), 256);
+         round_up((size_t)(d / 2) * sizeof(float), 256);
 }
 
 const char* qamw_status_string(int32_t status) {
@@ -133,11 +134,12 @@ int32_t qamw_calibrate(const void* W, int32_t wdtype, int64_t N, int64_t d, int6
                 workspace_bytes);
   hipStream_t st = (hipStream_t)stream;
   double* rho = (double*)workspace;
-  float* partial = (float*)((char*)workspace + round_up((size_t)N * sizeof(double), 256));
+  float* fcol = (float*)((char*)workspace + round_up((size_t)N * sizeof(double), 256));
+  float* partial = (float*)((char*)fcol + round_up((size_t)d * sizeof(float), 256));
   const int n = (int)N, dd = (int)d;
-  if ((rc = launch_scale(chan_rms, alpha, dd, s_out, st))) return rc;
+  if ((rc = launch_scale(chan_rms, alpha, sign_seed, dd, s_out, fcol, st))) return rc;
   if ((rc = launch_rownorm(W, wdtype, n, dd, ldw, s_out, rho, nullptr, st))) return rc;
-  if ((rc = launch_amplitude(L, W, wdtype, n, dd, ldw, s_out, sign_seed, rho, partial, st))) return rc;
+  if ((rc = launch_amplitude(L, W, wdtype, n, dd, ldw, fcol, rho, partial, st))) return rc;
   return launch_sigma(partial, (int)calib_tiles(N), dd / 2, n, sigma_out, st);
 }
 
@@ -158,7 +160,7 @@ int32_t qamw_build_plan(const float* codebook, int32_t K, void* plan, size_t pla
 struct EncodeWorkspace {
   double* rho;    // [N] fp64 row norms
   float* f;       // [d] eps_j s_j
-  double* isig;   // [d/2] 1 / sigma_k
+  float* isig;    // [d/2] 1 / sigma_k
 };
 
 static EncodeWorkspace encode_workspace(void* workspace, int64_t N, int64_t d) {
@@ -168,7 +170,7 @@ static EncodeWorkspace encode_workspace(void* workspace, int64_t N, int64_t d) {
   ws += round_up((size_t)N * sizeof(double), 256);
   e.f = (float*)ws;
   ws += round_up((size_t)d * sizeof(float), 256);
-  e.isig = (double*)ws;
+  e.isig = (float*)ws;
   return e;
 }
 

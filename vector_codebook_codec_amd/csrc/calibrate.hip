@@ -16,10 +16,16 @@ namespace qamw {
 // ---------------------------------------------------------------------------
 // s_j = r_j ^ alpha.  alpha = 0 gives exactly 1.
 // ---------------------------------------------------------------------------
+// Also f_j = eps_j s_j, the column factor the rotation pass applies.
 __global__ __launch_bounds__(kBlockThreads) void scale_kernel(const float* __restrict__ r, float alpha,
-                                                              int d, float* __restrict__ s) {
+                                                              uint64_t seed, int d, float* __restrict__ s,
+                                                              float* __restrict__ f) {
   const int j = blockIdx.x * kBlockThreads + threadIdx.x;
-  if (j < d) s[j] = (alpha == 0.0f) ? 1.0f : powf(r[j], alpha);
+  if (j < d) {
+    const float sj = (alpha == 0.0f) ? 1.0f : powf(r[j], alpha);
+    s[j] = sj;
+    f[j] = sj * sign_eps(seed, (uint32_t)j);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -39,20 +45,30 @@ __global__ __launch_bounds__(kBlockThreads) void rownorm_kernel(const Tin* __res
   const int nchunks = d >> 4;
   const Tin* row = W + (int64_t)n * ldw;
   double acc = 0.0;
-  for (int c = lane; c < nchunks; c += kWave) {
-    float x[16];
-    load_chunk(row + c * kChunk, x);
-    const float4* sp = reinterpret_cast<const float4*>(s + c * kChunk);
+  auto add_chunk = [&](const float x[16], const float* sc) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float4 sv = sp[v];
-      const float sc[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const double w = (double)x[4 * v + i] * (double)sc[i];
-        acc = fma(w, w, acc);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const double w = (double)x[i] * (double)sc[i];   // exact: a bf16/fp32 times an fp32
+      acc = fma(w, w, acc);
     }
+  };
+  // two chunks' loads in flight per lane, then the remainder
+  int c = lane;
+  for (; c + kWave < nchunks; c += 2 * kWave) {
+    float x[2][16], sc[2][16];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      load_chunk(row + (c + u * kWave) * kChunk, x[u]);
+      load_chunk(s + (c + u * kWave) * kChunk, sc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) add_chunk(x[u], sc[u]);
+  }
+  for (; c < nchunks; c += kWave) {
+    float x[16], sc[16];
+    load_chunk(row + c * kChunk, x);
+    load_chunk(s + c * kChunk, sc);
+    add_chunk(x, sc);
   }
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -70,7 +86,7 @@ __global__ __launch_bounds__(kBlockThreads) void rownorm_kernel(const Tin* __res
 // ---------------------------------------------------------------------------
 template <int L, typename Tin>
 __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
-    const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ s, uint64_t seed,
+    const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ fcol,
     const double* __restrict__ rho, float* __restrict__ partial) {
   const int lane = threadIdx.x & (kWave - 1);
   const int nchunks = d >> 4;
@@ -86,7 +102,7 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
   const double sqrt_b = sqrt((double)(1 << L));
 
   float f[16];
-  if (active) column_scale(s, seed, c * kChunk, f);
+  if (active) load_chunk(fcol + c * kChunk, f);
   float acc[8];
 #pragma unroll
   for (int p = 0; p < 8; ++p) acc[p] = 0.0f;
@@ -111,7 +127,8 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const float a = x[2 * p], b = x[2 * p + 1];
-      acc[p] += sqrtf(__builtin_fmaf(a, a, b * b)) * inv;
+      // v_sqrt_f32 (1 ulp) rather than the correctly rounded sqrtf expansion
+      acc[p] += __builtin_amdgcn_sqrtf(__builtin_fmaf(a, a, b * b)) * inv;
     }
   }
   if (active) {
@@ -147,9 +164,9 @@ __global__ __launch_bounds__(kBlockThreads) void sigma_kernel(const float* __res
 // ===========================================================================
 // launchers
 // ===========================================================================
-int launch_scale(const float* r, float alpha, int d, float* s, hipStream_t st) {
+int launch_scale(const float* r, float alpha, uint64_t seed, int d, float* s, float* f, hipStream_t st) {
   hipLaunchKernelGGL(scale_kernel, dim3((d + kBlockThreads - 1) / kBlockThreads), dim3(kBlockThreads), 0, st, r,
-                     alpha, d, s);
+                     alpha, seed, d, s, f);
   return check_launch("scale_kernel");
 }
 
@@ -165,23 +182,23 @@ int launch_rownorm(const void* W, int32_t wdt, int N, int d, int64_t ldw, const 
 
 template <int L>
 struct LaunchAmplitude {
-  static int run(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, uint64_t seed,
-                 const double* rho, float* partial, hipStream_t st) {
+  static int run(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const double* rho,
+                 float* partial, hipStream_t st) {
     const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
     const int64_t waves = (int64_t)nwin * (int64_t)calib_tiles(N);
     if (wdt == QAMW_F32)
       hipLaunchKernelGGL((amplitude_kernel<L, float>), dim3(grid_for_waves(waves)), dim3(kBlockThreads), 0, st,
-                         (const float*)W, ldw, N, d, s, seed, rho, partial);
+                         (const float*)W, ldw, N, d, f, rho, partial);
     else
       hipLaunchKernelGGL((amplitude_kernel<L, uint16_t>), dim3(grid_for_waves(waves)), dim3(kBlockThreads), 0,
-                         st, (const uint16_t*)W, ldw, N, d, s, seed, rho, partial);
+                         st, (const uint16_t*)W, ldw, N, d, f, rho, partial);
     return check_launch("amplitude_kernel");
   }
 };
 
-int launch_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, uint64_t seed,
-                     const double* rho, float* partial, hipStream_t st) {
-  return dispatch_L<LaunchAmplitude>(L, W, wdt, N, d, ldw, s, seed, rho, partial, st);
+int launch_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const double* rho,
+                     float* partial, hipStream_t st) {
+  return dispatch_L<LaunchAmplitude>(L, W, wdt, N, d, ldw, f, rho, partial, st);
 }
 
 int launch_sigma(const float* partial, int ntiles, int half_d, int N, float* sigma, hipStream_t st) {

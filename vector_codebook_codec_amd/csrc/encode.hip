@@ -9,6 +9,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "qamw.h"
 #include "qamw_device.h"
 #include "qamw_internal.h"
@@ -46,17 +48,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // Shared by both encode kernels.
 // ---------------------------------------------------------------------------
 // Per-matrix factors of the transform, computed once per call (prep kernel):
-// f_j = eps_j s_j (sign mask times channel scale, exact) and, in fp64,
-// 1 / sigma_k (0 where sigma_k <= 0, which codes z~ = 0).
+// f_j = eps_j s_j (sign mask times channel scale, exact) and 1 / sigma_k
+// (fp64 division rounded to fp32; 0 where sigma_k <= 0, which codes z~ = 0).
 __global__ __launch_bounds__(kBlockThreads) void encode_prep_kernel(const float* __restrict__ s,
                                                                     const float* __restrict__ sigma, uint64_t seed,
                                                                     int d, float* __restrict__ f,
-                                                                    double* __restrict__ isig) {
+                                                                    float* __restrict__ isig) {
   const int j = blockIdx.x * kBlockThreads + threadIdx.x;
   if (j < d) f[j] = s[j] * sign_eps(seed, (uint32_t)j);
   if (j < d / 2) {
     const float sg = sigma[j];
-    isig[j] = sg > 0.0f ? 1.0 / (double)sg : 0.0;
+    isig[j] = sg > 0.0f ? (float)(1.0 / (double)sg) : 0.0f;
   }
 }
 
@@ -64,19 +66,17 @@ __global__ __launch_bounds__(kBlockThreads) void encode_prep_kernel(const float*
 // holds the normalised pairs z~ of window chunk co_local (8 pairs),
 // z~ = y / sigma_k with y = H_b (f . w) / (sqrt(b) rho_n); inv_row is
 // 1 / (sqrt(b) rho_n) in fp64 (0 for rho_n = 0) and each pair's factor
-// inv_row / sigma_k is rounded once to fp32.
+// inv_row * (1 / sigma_k) is formed in fp64 and rounded once to fp32.
 template <int L, typename Tin>
-__device__ __forceinline__ int encode_transform(const Tin* __restrict__ W, int64_t ldw, int n, int win,
-                                                int nchunks, const float* __restrict__ f,
-                                                const double* __restrict__ isig, double inv_row, int lane,
-                                                float zx[8], float zy[8]) {
+__device__ __forceinline__ int encode_transform(const RawChunk<Tin>& raw, bool active, int win,
+                                                const float* __restrict__ f, const float* __restrict__ isig,
+                                                double inv_row, int lane, float zx[8], float zy[8]) {
   const int c = win * kWinChunks + lane;
-  const bool active = c < nchunks;   // whole Hadamard blocks are active or not
   float x[16];
   if (active) {
     float fc[16];
     load_chunk(f + c * kChunk, fc);
-    load_chunk(W + (int64_t)n * ldw + c * kChunk, x);
+    raw.unpack(x);
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] *= fc[i];
   } else {
@@ -87,22 +87,19 @@ __device__ __forceinline__ int encode_transform(const Tin* __restrict__ W, int64
   const int co_local = BlockOut<L>::chunk(lane);   // the lane now holds (sign *) chunk co_local
   const int co = win * kWinChunks + co_local;
   const float osign = BlockOut<L>::sign(lane);
-  double is[8];
+  float is[8];
   if (active) {
-    const double2* ip = reinterpret_cast<const double2*>(isig + co * kPairsPerLane);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const double2 t = ip[q];
-      is[2 * q] = t.x;
-      is[2 * q + 1] = t.y;
-    }
+    const float4* ip = reinterpret_cast<const float4*>(isig + co * kPairsPerLane);
+    const float4 t0 = ip[0], t1 = ip[1];
+    is[0] = t0.x; is[1] = t0.y; is[2] = t0.z; is[3] = t0.w;
+    is[4] = t1.x; is[5] = t1.y; is[6] = t1.z; is[7] = t1.w;
   } else {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) is[p] = 0.0;
+    for (int p = 0; p < 8; ++p) is[p] = 0.0f;
   }
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    const float inv = (float)(inv_row * is[p]) * osign;
+    const float inv = (float)(inv_row * (double)is[p]) * osign;
     zx[p] = x[2 * p] * inv;
     zy[p] = x[2 * p + 1] * inv;
   }
@@ -141,7 +138,7 @@ __device__ __forceinline__ void pack_window(const uint16_t* stage, int lane, int
 template <int L, typename Tin>
 __global__ __launch_bounds__(kEncThreads) void encode_kernel(
     const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ f,
-    const double* __restrict__ isig, const float* __restrict__ codebook, int K, int Kpad,
+    const float* __restrict__ isig, const float* __restrict__ codebook, int K, int Kpad,
     int B, int row_words, const double* __restrict__ rho, uint32_t* __restrict__ packed) {
   extern __shared__ float4 lds4[];
   float* cbx = reinterpret_cast<float*>(lds4);   // -cx
@@ -174,8 +171,10 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
   const int win = gw % nwin;
   {
     float zx[8], zy[8];
-    const int co_local =
-        encode_transform<L, Tin>(W, ldw, n, win, nchunks, f, isig, row_normaliser(rho[n], L), lane, zx, zy);
+    const bool active = win * kWinChunks + lane < nchunks;   // whole Hadamard blocks are active or not
+    RawChunk<Tin> raw;
+    if (active) raw.load(W + (int64_t)n * ldw + (win * kWinChunks + lane) * kChunk);
+    const int co_local = encode_transform<L, Tin>(raw, active, win, f, isig, row_normaliser(rho[n], L), lane, zx, zy);
 #pragma unroll
     for (int p = 0; p < 8; ++p) zbuf[co_local * kPairsPerLane + p] = make_float2(zx[p], zy[p]);
   }
@@ -286,10 +285,12 @@ __global__ __launch_bounds__(kEncThreads) void encode_kernel(
 // wavefront has a pair with more than i candidates (a list's unused tail
 // repeats its last entry, which cannot win a strict "<" again).
 // ---------------------------------------------------------------------------
+constexpr int kPlanWgPerCu = 2;   // 4 wavefronts per SIMD
+
 template <int L, typename Tin, int KMAX, int LMAX, int PG>
-__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(6))) void encode_plan_kernel(
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))) void encode_plan_kernel(
     const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ f,
-    const double* __restrict__ isig, const float* __restrict__ codebook, int K, int B, int row_words,
+    const float* __restrict__ isig, const float* __restrict__ codebook, int K, int B, int row_words,
     const double* __restrict__ rho, const int* __restrict__ plan_K, const uint16_t* __restrict__ lists,
     const uint16_t* __restrict__ lists2, uint32_t* __restrict__ packed) {
   static_assert(LMAX % 8 == 0 && LMAX <= 16 && kPairsPerLane % PG == 0, "list and group sizes");
@@ -308,97 +309,130 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(6))
   uint16_t* stage = stage_all + wave * kWinPairs;
   const int nchunks = d >> 4;
   const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
-  const int gw = blockIdx.x * kEncWaves + wave;
-  if ((int64_t)gw >= (int64_t)N * nwin) return;   // no barriers follow
-  const int n = gw / nwin;
-  const int win = gw % nwin;
+  const int total = N * nwin;                      // fits in int (checked on the host)
+  const int stride = gridDim.x * kEncWaves;
+  int gw = blockIdx.x * kEncWaves + wave;
+  if (gw >= total) return;                         // no barriers follow
 
-  float zx[8], zy[8];
-  const int co_local =
-      encode_transform<L, Tin>(W, ldw, n, win, nchunks, f, isig, row_normaliser(rho[n], L), lane, zx, zy);
+  // persistent wavefront: windows gw, gw + stride, ...; the next window's
+  // weights are loaded while the current one is searched
+  auto chunk_of = [&](int g, int& n, int& win) {
+    n = g / nwin;
+    win = g - n * nwin;
+    return win * kWinChunks + lane;
+  };
+  int n, win;
+  int c = chunk_of(gw, n, win);
+  RawChunk<Tin> raw;
+  if (c < nchunks) raw.load(W + (int64_t)n * ldw + c * kChunk);
 
   const float cells_per_unit = (float)kPlanG / (2.0f * kPlanR);
   const float cells_per_unit2 = (float)kPlanG2 / (2.0f * kPlanR2);
+  const float tmax = __uint_as_float(__float_as_uint((float)kPlanG) - 1u);     // largest float below G
+  const float tmax2 = __uint_as_float(__float_as_uint((float)kPlanG2) - 1u);
   const bool plan_ok = *plan_K == K;   // a plan built for another K: scan the whole codebook
-#pragma unroll
-  for (int g = 0; g < kPairsPerLane; g += PG) {
-    uint32_t words[PG][LMAX / 2];
-    bool inside[PG];
-    // ---- every record load of the group first
-#pragma unroll
-    for (int p = 0; p < PG; ++p) {
-      const float x = zx[g + p], y = zy[g + p];
-      // fine grid, else outer grid (comparisons are false for NaN)
-      const bool fine = x >= -kPlanR && x < kPlanR && y >= -kPlanR && y < kPlanR;
-      inside[p] = plan_ok && x >= -kPlanR2 && x < kPlanR2 && y >= -kPlanR2 && y < kPlanR2;
-      // the clamps change nothing inside a grid and keep the conversion in range outside it
-      const int ix = min((int)(fminf(fmaxf(x + kPlanR, 0.0f), 2.0f * kPlanR) * cells_per_unit), kPlanG - 1);
-      const int iy = min((int)(fminf(fmaxf(y + kPlanR, 0.0f), 2.0f * kPlanR) * cells_per_unit), kPlanG - 1);
-      const int jx = min((int)(fminf(fmaxf(x + kPlanR2, 0.0f), 2.0f * kPlanR2) * cells_per_unit2), kPlanG2 - 1);
-      const int jy = min((int)(fminf(fmaxf(y + kPlanR2, 0.0f), 2.0f * kPlanR2) * cells_per_unit2), kPlanG2 - 1);
-      const uint16_t* rec = fine ? lists + (size_t)(ix * kPlanG + iy) * LMAX
-                                 : lists2 + (size_t)(inside[p] ? jx * kPlanG2 + jy : 0) * LMAX;
-      const uint4* lp = reinterpret_cast<const uint4*>(rec);
-#pragma unroll
-      for (int q = 0; q < LMAX / 8; ++q) {
-        const uint4 t = lp[q];
-        words[p][4 * q + 0] = t.x; words[p][4 * q + 1] = t.y; words[p][4 * q + 2] = t.z; words[p][4 * q + 3] = t.w;
-      }
+
+  for (;;) {
+    const bool active = c < nchunks;   // whole Hadamard blocks are active or not
+    float zx[8], zy[8];
+    const int co_local = encode_transform<L, Tin>(raw, active, win, f, isig, row_normaliser(rho[n], L), lane, zx, zy);
+    const int n_cur = n, win_cur = win;
+    const int gnext = gw + stride;
+    if (gnext < total) {
+      c = chunk_of(gnext, n, win);
+      if (c < nchunks) raw.load(W + (int64_t)n * ldw + c * kChunk);
     }
-    // ---- record flags: nibble 0 = count - 1, nibble 1 = overflow
-    bool full[PG];
-    int maxc = 1;
+
 #pragma unroll
-    for (int p = 0; p < PG; ++p) {
-      const uint32_t w0 = words[p][0];
-      full[p] = !inside[p] || ((w0 >> 16) & 1u);
-      maxc = max(maxc, full[p] ? 1 : (int)(w0 & 15u) + 1);
-      words[p][0] = w0 & 0xfff0fff0u;
-    }
-    // ---- list slots, two per word
-    float best[PG];
-    uint32_t boff[PG];
+    for (int g = 0; g < kPairsPerLane; g += PG) {
+      uint32_t words[PG][LMAX / 2];
+      bool inside[PG];
+      // ---- every record load of the group first.  Cell coordinate t = x G/(2R) + G/2:
+      // its rounding error (< 1e-5 cell) is far inside the plan's eta margin;
+      // the clamp changes nothing inside the grid, so "unchanged" is the range test
 #pragma unroll
-    for (int p = 0; p < PG; ++p) { best[p] = INFINITY; boff[p] = 0; }
-#pragma unroll
-    for (int w = 0; w < LMAX / 2; ++w) {
-      if (w > 0 && !__any(2 * w < maxc)) continue;     // wave-uniform; later words are skipped too
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t off[PG];
-        float3 e[PG];
-#pragma unroll
-        for (int p = 0; p < PG; ++p) {
-          off[p] = h ? (words[p][w] >> 16) : (words[p][w] & 0xffffu);
-          const float4 t = *reinterpret_cast<const float4*>(cbytes + off[p]);
-          e[p] = make_float3(t.x, t.y, t.z);
+      for (int p = 0; p < PG; ++p) {
+        const float x = zx[g + p], y = zy[g + p];
+        const float tx = __builtin_fmaf(x, cells_per_unit, 0.5f * kPlanG);
+        const float ty = __builtin_fmaf(y, cells_per_unit, 0.5f * kPlanG);
+        const float cx = __builtin_amdgcn_fmed3f(tx, 0.0f, tmax);
+        const float cy = __builtin_amdgcn_fmed3f(ty, 0.0f, tmax);
+        const bool fine = cx == tx && cy == ty;      // false for NaN
+        const uint16_t* rec = lists + (size_t)((int)cx * kPlanG + (int)cy) * LMAX;
+        inside[p] = plan_ok;
+        if (!fine) {                                 // rare: the outer grid, else a full scan
+          const float ux = __builtin_fmaf(x, cells_per_unit2, 0.5f * kPlanG2);
+          const float uy = __builtin_fmaf(y, cells_per_unit2, 0.5f * kPlanG2);
+          const float vx = __builtin_amdgcn_fmed3f(ux, 0.0f, tmax2);
+          const float vy = __builtin_amdgcn_fmed3f(uy, 0.0f, tmax2);
+          inside[p] = plan_ok && vx == ux && vy == uy;
+          rec = lists2 + (size_t)(inside[p] ? (int)vx * kPlanG2 + (int)vy : 0) * LMAX;
         }
-        __builtin_amdgcn_sched_barrier(0);   // keep the group's LDS reads in flight together
+        const uint4* lp = reinterpret_cast<const uint4*>(rec);
 #pragma unroll
-        for (int p = 0; p < PG; ++p) {
-          const float sc = __builtin_fmaf(zy[g + p], e[p].y, __builtin_fmaf(zx[g + p], e[p].x, e[p].z));
-          if (sc < best[p]) { best[p] = sc; boff[p] = off[p]; }
+        for (int q = 0; q < LMAX / 8; ++q) {
+          const uint4 t = lp[q];
+          words[p][4 * q + 0] = t.x; words[p][4 * q + 1] = t.y; words[p][4 * q + 2] = t.z; words[p][4 * q + 3] = t.w;
         }
       }
-    }
-    // ---- pairs outside the grid or in overflowing cells: the whole codebook
+      // ---- record flags: nibble 0 = count - 1, nibble 1 = overflow
+      bool full[PG];
+      int maxc = 1;
 #pragma unroll
-    for (int p = 0; p < PG; ++p) {
-      if (__any(full[p])) {
-        float fb = INFINITY;
-        uint32_t fo = 0;
-        for (int c = 0; c < K; ++c) {
-          const float4 e = cb4[c];                 // same address in every lane: broadcast
-          const float sc = __builtin_fmaf(zy[g + p], e.y, __builtin_fmaf(zx[g + p], e.x, e.z));
-          if (sc < fb) { fb = sc; fo = (uint32_t)c * 16u; }
-        }
-        if (full[p]) boff[p] = fo;
+      for (int p = 0; p < PG; ++p) {
+        const uint32_t w0 = words[p][0];
+        full[p] = !inside[p] || ((w0 >> 16) & 1u);
+        maxc = max(maxc, full[p] ? 1 : (int)(w0 & 15u) + 1);
+        words[p][0] = w0 & 0xfff0fff0u;
       }
-      stage[co_local * kPairsPerLane + g + p] = (uint16_t)(boff[p] >> 4);
+      // ---- list slots, two per word
+      float best[PG];
+      uint32_t boff[PG];
+#pragma unroll
+      for (int p = 0; p < PG; ++p) { best[p] = INFINITY; boff[p] = 0; }
+#pragma unroll
+      for (int w = 0; w < LMAX / 2; ++w) {
+        if (w > 0 && !__any(2 * w < maxc)) continue;     // wave-uniform; later words are skipped too
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint32_t off[PG];
+          float3 e[PG];
+#pragma unroll
+          for (int p = 0; p < PG; ++p) {
+            off[p] = h ? (words[p][w] >> 16) : (words[p][w] & 0xffffu);
+            const float4 t = *reinterpret_cast<const float4*>(cbytes + off[p]);
+            e[p] = make_float3(t.x, t.y, t.z);
+          }
+          __builtin_amdgcn_sched_barrier(0);   // keep the group's LDS reads in flight together
+#pragma unroll
+          for (int p = 0; p < PG; ++p) {
+            const float sc = __builtin_fmaf(zy[g + p], e[p].y, __builtin_fmaf(zx[g + p], e[p].x, e[p].z));
+            if (sc < best[p]) { best[p] = sc; boff[p] = off[p]; }
+          }
+        }
+      }
+      // ---- pairs outside the grids or in overflowing cells: the whole codebook
+#pragma unroll
+      for (int p = 0; p < PG; ++p) {
+        if (__any(full[p])) {
+          float fb = INFINITY;
+          uint32_t fo = 0;
+          for (int cc = 0; cc < K; ++cc) {
+            const float4 e = cb4[cc];                // same address in every lane: broadcast
+            const float sc = __builtin_fmaf(zy[g + p], e.y, __builtin_fmaf(zx[g + p], e.x, e.z));
+            if (sc < fb) { fb = sc; fo = (uint32_t)cc * 16u; }
+          }
+          if (full[p]) boff[p] = fo;
+        }
+        stage[co_local * kPairsPerLane + g + p] = (uint16_t)(boff[p] >> 4);
+      }
     }
+    wave_lds_fence();
+    pack_window(stage, lane, win_cur, nwin, d >> 1, B, row_words, packed + (int64_t)n_cur * row_words);
+    gw = gnext;
+    if (gw >= total) break;
+    wave_lds_fence();                              // the stage is rewritten next round
   }
-  wave_lds_fence();
-  pack_window(stage, lane, win, nwin, d >> 1, B, row_words, packed + (int64_t)n * row_words);
 }
 
 // ===========================================================================
@@ -406,19 +440,25 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(6))
 // ===========================================================================
 template <int L>
 struct LaunchEncode {
-  static int run(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const double* isig,
+  static int run(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const float* isig,
                  const float* cb, int K, int B, int row_words, const double* rho, const void* plan, uint32_t* packed,
                  hipStream_t st) {
     const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
     const int64_t waves = (int64_t)N * nwin;
     const dim3 grid((unsigned)((waves + kEncWaves - 1) / kEncWaves)), blk(kEncThreads);
     if (plan) {
+      // persistent: as many workgroups as fit at once (2 of 8 wavefronts per CU)
+      int dev = 0, cus = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return fail(QAMW_EHIP, "cannot query the device's compute units");
+      const dim3 pgrid((unsigned)std::min<int64_t>(grid.x, (int64_t)cus * kPlanWgPerCu));
       const char* base = (const char*)plan;
       const int* plan_K = (const int*)(base + kPlanHeaderKOffset);
       const uint16_t* lists = (const uint16_t*)(base + kPlanHeaderBytes);
       const uint16_t* lists2 = (const uint16_t*)(base + plan_outer_offset(K));
 #define QAMW_PLAN_LAUNCH(TIN, KM, LM, PG)                                                                      \
-  hipLaunchKernelGGL((encode_plan_kernel<L, TIN, KM, LM, PG>), grid, blk, 0, st, (const TIN*)W, ldw, N, d, f, \
+  hipLaunchKernelGGL((encode_plan_kernel<L, TIN, KM, LM, PG>), pgrid, blk, 0, st, (const TIN*)W, ldw, N, d, f, \
                      isig, cb, K, B, row_words, rho, plan_K, lists, lists2, packed)
       if (plan_lmax(K) == 8) {
         if (wdt == QAMW_F32) QAMW_PLAN_LAUNCH(float, 2048, 8, 4); else QAMW_PLAN_LAUNCH(uint16_t, 2048, 8, 4);
@@ -440,14 +480,14 @@ struct LaunchEncode {
   }
 };
 
-int launch_encode_prep(const float* s, const float* sigma, uint64_t seed, int d, float* f, double* isig,
+int launch_encode_prep(const float* s, const float* sigma, uint64_t seed, int d, float* f, float* isig,
                        hipStream_t st) {
   hipLaunchKernelGGL(encode_prep_kernel, dim3((unsigned)((d + kBlockThreads - 1) / kBlockThreads)),
                      dim3(kBlockThreads), 0, st, s, sigma, seed, d, f, isig);
   return check_launch("encode_prep_kernel");
 }
 
-int launch_encode(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const double* isig,
+int launch_encode(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const float* isig,
                   const float* cb, int K, int B, int row_words, const double* rho, const void* plan, uint32_t* packed,
                   hipStream_t st) {
   return dispatch_L<LaunchEncode>(L, W, wdt, N, d, ldw, f, isig, cb, K, B, row_words, rho, plan, packed, st);

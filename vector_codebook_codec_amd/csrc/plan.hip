@@ -184,24 +184,34 @@ __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* _
     nsurv = total;
   }
   __syncthreads();
-  const bool all = nsurv > kSuperMax;       // too many survivors: test every centroid
-  const int ns = all ? K : nsurv;
-  auto survivor = [&](int j, double& x, double& y) -> int {
-    if (all) { x = cb[2 * j]; y = cb[2 * j + 1]; return j; }
-    const float2 v = survc[j];
-    x = v.x; y = v.y;
-    return surv[j];
-  };
+  const bool all = nsurv > kSuperMax;       // too many survivors: test every centroid (from global memory)
+  // pad the survivor list to whole unrolled rounds with a far-away dummy that
+  // neither lowers any U nor passes any test
+  constexpr int kRound = 4 * LPC;
+  static_assert(kSuperMax % kRound == 0, "padding stays inside the survivor arrays");
+  const int ns = all ? K : (nsurv + kRound - 1) / kRound * kRound;
+  if (!all)
+    for (int j = nsurv + tid; j < ns; j += kPlanThreads) {
+      survc[j] = make_float2(1e30f, 1e30f);
+      surv[j] = 0;
+    }
+  __syncthreads();
 
   // ---- LPC lanes per cell: survivors j = sub, sub + LPC, ...
   const int qc = tid / LPC, sub = tid % LPC;
   const int ix = sx * S + qc / S, iy = sy * S + qc % S;
   const Box cq = cell_box(R, G, ix, iy, 1);
   double Uc = INFINITY;
-  for (int j = sub; j < ns; j += LPC) {
-    double x, y;
-    survivor(j, x, y);
-    Uc = fmin(Uc, cq.dmax2(x, y));
+  if (all) {
+    for (int j = sub; j < ns; j += LPC) Uc = fmin(Uc, cq.dmax2(cb[2 * j], cb[2 * j + 1]));
+  } else {
+    for (int j0 = 0; j0 < ns; j0 += kRound) {
+      float2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = survc[j0 + u * LPC + sub];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Uc = fmin(Uc, cq.dmax2(v[u].x, v[u].y));
+    }
   }
 #pragma unroll
   for (int off = LPC / 2; off > 0; off >>= 1) Uc = fmin(Uc, __shfl_xor(Uc, off));   // within the group
@@ -210,16 +220,30 @@ __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* _
   const int gshift = lane & ~(LPC - 1);
   const uint64_t gmask = (LPC == 64) ? ~0ull : ((1ull << LPC) - 1ull);
   int count = 0;
-  for (int j0 = 0; j0 < ns; j0 += LPC) {    // same trip count in every lane (ballot below)
-    const int j = j0 + sub;
-    double x = 0.0, y = 0.0;
-    int c = 0;
-    if (j < ns) c = survivor(j, x, y);
-    const bool pred = j < ns && cq.dmin2(x, y) <= lim;
+  // survivors in index order: chunk t = [t LPC, (t+1) LPC), one per lane of the group
+  auto take = [&](bool pred, int c) {
     const uint64_t gm = (__ballot(pred) >> gshift) & gmask;
     const int pos = count + __popcll(gm & ((1ull << sub) - 1ull));
     if (pred && pos < lmax) mine[pos] = (uint16_t)(c * 16);
     count += __popcll(gm);
+  };
+  if (all) {
+    for (int j0 = 0; j0 < ns; j0 += LPC) {  // same trip count in every lane (ballot)
+      const int j = j0 + sub;
+      take(j < ns && cq.dmin2(cb[2 * min(j, ns - 1)], cb[2 * min(j, ns - 1) + 1]) <= lim, j);
+    }
+  } else {
+    for (int j0 = 0; j0 < ns; j0 += kRound) {
+      float2 v[4];
+      int c[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[u] = survc[j0 + u * LPC + sub];
+        c[u] = surv[j0 + u * LPC + sub];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) take(cq.dmin2(v[u].x, v[u].y) <= lim, c[u]);
+    }
   }
   __syncthreads();
   if (sub != 0) return;                      // no barriers follow

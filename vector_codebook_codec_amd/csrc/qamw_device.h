@@ -62,6 +62,43 @@ __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ p, float
   }
 }
 
+// A chunk as loaded, before conversion: lets a kernel issue the next chunk's
+// load early and convert it later.
+template <typename Tin> struct RawChunk;
+template <> struct RawChunk<float> {
+  float4 v[4];
+  __device__ void load(const float* __restrict__ p) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = q[i];
+  }
+  __device__ void unpack(float x[16]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[4 * i + 0] = v[i].x; x[4 * i + 1] = v[i].y; x[4 * i + 2] = v[i].z; x[4 * i + 3] = v[i].w;
+    }
+  }
+};
+template <> struct RawChunk<uint16_t> {
+  uint4 v[2];
+  __device__ void load(const uint16_t* __restrict__ p) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    v[0] = q[0];
+    v[1] = q[1];
+  }
+  __device__ void unpack(float x[16]) const {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t w[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[8 * h + 2 * i + 0] = bf16_bits_to_f32(w[i] & 0xffffu);
+        x[8 * h + 2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      }
+    }
+  }
+};
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
@@ -337,26 +374,6 @@ struct BlockOut {
   }
   static __device__ __forceinline__ float sign(int lane) { return lane_out_sign<NB>(lane & ((1 << NB) - 1)); }
 };
-
-// Per-lane column factors f_j = s_j * eps_j for the lane's 16 columns.
-__device__ __forceinline__ void column_scale(const float* __restrict__ s, uint64_t seed, int col0,
-                                             float f[16]) {
-  const float4* sp = reinterpret_cast<const float4*>(s + col0);
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const float4 sv = sp[v];
-    f[4 * v + 0] = sv.x * sign_eps(seed, col0 + 4 * v + 0);
-    f[4 * v + 1] = sv.y * sign_eps(seed, col0 + 4 * v + 1);
-    f[4 * v + 2] = sv.z * sign_eps(seed, col0 + 4 * v + 2);
-    f[4 * v + 3] = sv.w * sign_eps(seed, col0 + 4 * v + 3);
-  }
-}
-
-// 1 / (sqrt(b) rho sigma) in fp64, rounded once to fp32; 0 when rho sigma == 0.
-__device__ __forceinline__ float pair_normaliser(double rho, float sigma, double sqrt_b) {
-  const double den = rho * (double)sigma * sqrt_b;
-  return den > 0.0 ? (float)(1.0 / den) : 0.0f;
-}
 
 // fp64 -> IEEE binary16 bits with one round-to-nearest-even step.
 __device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {

@@ -58,15 +58,15 @@ inline size_t plan_bytes(int K) {
 }
 
 // ---- stage launchers (enqueue on `st`, return a qamw_status)
-int launch_scale(const float* r, float alpha, int d, float* s, hipStream_t st);
+int launch_scale(const float* r, float alpha, uint64_t seed, int d, float* s, float* f, hipStream_t st);
 int launch_rownorm(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, double* rho,
                    uint16_t* rho_f16, hipStream_t st);
-int launch_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, uint64_t seed,
-                     const double* rho, float* partial, hipStream_t st);
+int launch_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const double* rho,
+                     float* partial, hipStream_t st);
 int launch_sigma(const float* partial, int ntiles, int half_d, int N, float* sigma, hipStream_t st);
-int launch_encode_prep(const float* s, const float* sigma, uint64_t seed, int d, float* f, double* isig,
+int launch_encode_prep(const float* s, const float* sigma, uint64_t seed, int d, float* f, float* isig,
                        hipStream_t st);
-int launch_encode(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const double* isig,
+int launch_encode(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const float* isig,
                   const float* cb, int K, int B, int row_words, const double* rho, const void* plan, uint32_t* packed,
                   hipStream_t st);
 int launch_build_plan(const float* cb, int K, void* plan, hipStream_t st);
