@@ -194,8 +194,8 @@ int32_t qamw_encode_prepare(const void* W, int32_t wdtype, int64_t N, int64_t d,
   if ((rc = check_encode_workspace(workspace, workspace_bytes, N, d))) return rc;
   hipStream_t st = (hipStream_t)stream;
   const EncodeWorkspace e = encode_workspace(workspace, N, d);
-  if ((rc = launch_rownorm(W, wdtype, (int)N, (int)d, ldw, s, e.rho, rownorm_f16, st))) return rc;
-  return launch_encode_prep(s, sigma, sign_seed, (int)d, e.f, e.isig, st);
+  return launch_encode_prepare(W, wdtype, (int)N, (int)d, ldw, s, sigma, sign_seed, e.rho, rownorm_f16, e.f, e.isig,
+                               st);
 }
 
 int32_t qamw_encode_indices(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, int32_t block,

@@ -28,55 +28,14 @@ __global__ __launch_bounds__(kBlockThreads) void scale_kernel(const float* __res
   }
 }
 
-// ---------------------------------------------------------------------------
-// rho_n = sqrt(sum_j (W_nj s_j)^2), one wavefront per row.  W_nj s_j is exact
-// in fp64 (24-bit x 24-bit significands); squares and sums are fp64, reduced
-// in a fixed order, so rho is deterministic and accurate to ~1e-16.
-// Optionally writes the binary16 (RNE) row norm.
-// ---------------------------------------------------------------------------
+// rho_n = ||W_n diag(s)||, one wavefront per row (row_norm_wave).
 template <typename Tin>
 __global__ __launch_bounds__(kBlockThreads) void rownorm_kernel(const Tin* __restrict__ W, int64_t ldw,
                                                                 int N, int d, const float* __restrict__ s,
                                                                 double* __restrict__ rho,
                                                                 uint16_t* __restrict__ rho_f16) {
-  const int lane = threadIdx.x & (kWave - 1);
   const int n = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (n >= N) return;
-  const int nchunks = d >> 4;
-  const Tin* row = W + (int64_t)n * ldw;
-  double acc = 0.0;
-  auto add_chunk = [&](const float x[16], const float* sc) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const double w = (double)x[i] * (double)sc[i];   // exact: a bf16/fp32 times an fp32
-      acc = fma(w, w, acc);
-    }
-  };
-  // two chunks' loads in flight per lane, then the remainder
-  int c = lane;
-  for (; c + kWave < nchunks; c += 2 * kWave) {
-    float x[2][16], sc[2][16];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      load_chunk(row + (c + u * kWave) * kChunk, x[u]);
-      load_chunk(s + (c + u * kWave) * kChunk, sc[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) add_chunk(x[u], sc[u]);
-  }
-  for (; c < nchunks; c += kWave) {
-    float x[16], sc[16];
-    load_chunk(row + c * kChunk, x);
-    load_chunk(s + c * kChunk, sc);
-    add_chunk(x, sc);
-  }
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) {
-    const double r = sqrt(acc);
-    rho[n] = r;
-    if (rho_f16) rho_f16[n] = f64_to_f16_bits(r);
-  }
+  if (n < N) row_norm_wave(W, ldw, n, d, s, rho, rho_f16);
 }
 
 // ---------------------------------------------------------------------------
@@ -115,20 +74,30 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
     const double r = rho[n0 + lane];
     inv_lane = r > 0.0 ? (float)(1.0 / (sqrt_b * r)) : 0.0f;
   }
-  float nxt[16];
-  if (active) load_chunk(W + (int64_t)n0 * ldw + c * kChunk, nxt);
-  for (int n = n0; n < n1; ++n) {
-    float x[16];
+  // a ring of kAmpDepth rows in flight: row n + kAmpDepth is loaded while row n is processed
+  constexpr int kAmpDepth = 4;
+  RawChunk<Tin> ring[kAmpDepth];
+  const Tin* base = W + c * kChunk;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = active ? nxt[i] * f[i] : 0.0f;
-    if (active && n + 1 < n1) load_chunk(W + (int64_t)(n + 1) * ldw + c * kChunk, nxt);
-    fwht_block<L>(x, lane);
-    const float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv_lane), n - n0));
+  for (int u = 0; u < kAmpDepth; ++u)
+    if (active && n0 + u < n1) ring[u].load(base + (int64_t)(n0 + u) * ldw);
+  for (int n = n0; n < n1; n += kAmpDepth) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const float a = x[2 * p], b = x[2 * p + 1];
-      // v_sqrt_f32 (1 ulp) rather than the correctly rounded sqrtf expansion
-      acc[p] += __builtin_amdgcn_sqrtf(__builtin_fmaf(a, a, b * b)) * inv;
+    for (int u = 0; u < kAmpDepth; ++u) {
+      if (n + u >= n1) break;
+      float x[16];
+      ring[u].unpack(x);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = active ? x[i] * f[i] : 0.0f;
+      if (active && n + u + kAmpDepth < n1) ring[u].load(base + (int64_t)(n + u + kAmpDepth) * ldw);
+      fwht_block<L>(x, lane);
+      const float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv_lane), n + u - n0));
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const float a = x[2 * p], b = x[2 * p + 1];
+        // v_sqrt_f32 (1 ulp) rather than the correctly rounded sqrtf expansion
+        acc[p] += __builtin_amdgcn_sqrtf(__builtin_fmaf(a, a, b * b)) * inv;
+      }
     }
   }
   if (active) {

@@ -47,14 +47,22 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // ---------------------------------------------------------------------------
 // Shared by both encode kernels.
 // ---------------------------------------------------------------------------
-// Per-matrix factors of the transform, computed once per call (prep kernel):
-// f_j = eps_j s_j (sign mask times channel scale, exact) and 1 / sigma_k
-// (fp64 division rounded to fp32; 0 where sigma_k <= 0, which codes z~ = 0).
-__global__ __launch_bounds__(kBlockThreads) void encode_prep_kernel(const float* __restrict__ s,
-                                                                    const float* __restrict__ sigma, uint64_t seed,
-                                                                    int d, float* __restrict__ f,
-                                                                    float* __restrict__ isig) {
-  const int j = blockIdx.x * kBlockThreads + threadIdx.x;
+// Encode, phase 1, in one launch: workgroups [0, row_blocks) compute the row
+// norms (one wavefront per row); the rest compute the per-matrix factors of
+// the transform: f_j = eps_j s_j (sign mask times channel scale, exact) and
+// 1 / sigma_k (fp64 division rounded to fp32; 0 where sigma_k <= 0, which
+// codes z~ = 0).
+template <typename Tin>
+__global__ __launch_bounds__(kBlockThreads) void encode_prepare_kernel(
+    const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ s,
+    const float* __restrict__ sigma, uint64_t seed, int row_blocks, double* __restrict__ rho,
+    uint16_t* __restrict__ rho_f16, float* __restrict__ f, float* __restrict__ isig) {
+  if ((int)blockIdx.x < row_blocks) {
+    const int n = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    if (n < N) row_norm_wave(W, ldw, n, d, s, rho, rho_f16);
+    return;
+  }
+  const int j = (blockIdx.x - row_blocks) * kBlockThreads + threadIdx.x;
   if (j < d) f[j] = s[j] * sign_eps(seed, (uint32_t)j);
   if (j < d / 2) {
     const float sg = sigma[j];
@@ -480,11 +488,17 @@ struct LaunchEncode {
   }
 };
 
-int launch_encode_prep(const float* s, const float* sigma, uint64_t seed, int d, float* f, float* isig,
-                       hipStream_t st) {
-  hipLaunchKernelGGL(encode_prep_kernel, dim3((unsigned)((d + kBlockThreads - 1) / kBlockThreads)),
-                     dim3(kBlockThreads), 0, st, s, sigma, seed, d, f, isig);
-  return check_launch("encode_prep_kernel");
+int launch_encode_prepare(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, const float* sigma,
+                          uint64_t seed, double* rho, uint16_t* rho_f16, float* f, float* isig, hipStream_t st) {
+  const int row_blocks = grid_for_waves(N);
+  const dim3 grid((unsigned)(row_blocks + (d + kBlockThreads - 1) / kBlockThreads)), blk(kBlockThreads);
+  if (wdt == QAMW_F32)
+    hipLaunchKernelGGL(encode_prepare_kernel<float>, grid, blk, 0, st, (const float*)W, ldw, N, d, s, sigma, seed,
+                       row_blocks, rho, rho_f16, f, isig);
+  else
+    hipLaunchKernelGGL(encode_prepare_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)W, ldw, N, d, s, sigma,
+                       seed, row_blocks, rho, rho_f16, f, isig);
+  return check_launch("encode_prepare_kernel");
 }
 
 int launch_encode(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const float* isig,

@@ -34,7 +34,7 @@
 // there.  Each has its own delta (R = 5 or 40 in the formula above).
 //
 // Layout (plan_bytes(K) bytes, 256-byte aligned):
-//   [0, 256)     PlanHeader (+ Cmax as fp64 at byte 128)
+//   [0, 256)     PlanHeader
 //   [256, ...)   fine grid: uint16 lists [G*G][lmax], then the outer grid's
 //                [G2*G2][lmax]; one 16- or 32-byte record per cell.
 //                Entry i is 16 c_i | nibble_i: c_i the i-th listed centroid
@@ -70,39 +70,11 @@ struct PlanHeader {
 static_assert(offsetof(PlanHeader, K) == kPlanHeaderKOffset, "the encode kernel reads K at this offset");
 
 constexpr double kPlanEta = 1e-4;
-constexpr int kSuperFine = 16;                     // cells per supercell side, fine grid
-constexpr int kSuperOuter = 4;                     // and outer grid
 constexpr int kSuperMax = 2048;                    // survivors kept; more -> test all K
 constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / kWave;
 
-// Largest centroid radius (one workgroup).
-__global__ __launch_bounds__(kBlockThreads) void codebook_radius_kernel(const float* __restrict__ cb, int K,
-                                                                        PlanHeader* hdr, double* cmax_out) {
-  __shared__ double part[kBlockThreads];
-  double m = 0.0;
-  for (int c = threadIdx.x; c < K; c += kBlockThreads) {
-    const double cx = cb[2 * c], cy = cb[2 * c + 1];
-    m = fmax(m, sqrt(cx * cx + cy * cy));
-  }
-  part[threadIdx.x] = m;
-  __syncthreads();
-  for (int off = kBlockThreads / 2; off > 0; off >>= 1) {
-    if (threadIdx.x < off) part[threadIdx.x] = fmax(part[threadIdx.x], part[threadIdx.x + off]);
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    *cmax_out = part[0];
-    hdr->R = kPlanR;
-    hdr->cells_per_unit = (float)kPlanG / (2.0f * kPlanR);
-    hdr->G = kPlanG;
-    hdr->lmax = plan_lmax(K);
-    hdr->K = K;
-    hdr->R2 = kPlanR2;
-    hdr->cells_per_unit2 = (float)kPlanG2 / (2.0f * kPlanR2);
-    hdr->G2 = kPlanG2;
-  }
-}
+constexpr int kPerThread = kSuperMax / kPlanThreads;   // centroids one thread tests in the survivor pass
 
 // Axis-aligned box [x0, x1] x [y0, y1] against centroid (cx, cy).
 struct Box {
@@ -131,56 +103,89 @@ __device__ __forceinline__ double wave_min(double v) {
   return v;
 }
 
+__device__ __forceinline__ double wave_max(double v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+  return v;
+}
+
+struct PlanShared {
+  uint16_t surv[kSuperMax];
+  float2 survc[kSuperMax];
+  uint16_t cell_list[kPlanThreads][16];
+  double red[kPlanWaves];
+  double red2[kPlanWaves];
+  int wsum[kPlanWaves];
+};
+
 // One workgroup per supercell (S x S cells) of a G x G grid over [-R, R)^2:
 // the supercell's survivors (ascending, with coordinates) into LDS, then a
-// group of LPC = 256 / S^2 lanes per cell scans them.
+// group of LPC = 256 / S^2 lanes per cell scans them and writes the records.
 template <int S>
-__global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* __restrict__ cb, int K, int lmax,
-                                                                  float Rf, int G, const double* __restrict__ cmax,
-                                                                  uint16_t* __restrict__ lists) {
+__device__ void build_supercell(PlanShared& sh, const float* __restrict__ cb, int K, int lmax, double R, int G,
+                                int sidx, uint16_t* __restrict__ lists) {
   constexpr int LPC = kPlanThreads / (S * S);
   static_assert(LPC >= 1 && LPC * S * S == kPlanThreads && kWave % LPC == 0, "cell groups tile the wavefronts");
-  __shared__ uint16_t surv[kSuperMax];
-  __shared__ float2 survc[kSuperMax];
-  __shared__ uint16_t cell_list[S * S][16];
-  __shared__ double red[kPlanWaves];
-  __shared__ int wcount[kPlanWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int nsuper = G / S;
-  const int sx = blockIdx.x / nsuper, sy = blockIdx.x % nsuper;
-  const double R = Rf;
-  const double reach = *cmax + R * 1.4142135623730951;
-  const double delta = 1e-5 * reach * reach;
+  const int sx = sidx / nsuper, sy = sidx % nsuper;
 
-  // ---- supercell survivors
+  // ---- U(SQ) and the largest centroid radius Cmax in one pass over the codebook
   const Box sq = cell_box(R, G, sx * S, sy * S, S);
-  double U = INFINITY;
-  for (int c = tid; c < K; c += kPlanThreads) U = fmin(U, sq.dmax2(cb[2 * c], cb[2 * c + 1]));
+  double U = INFINITY, cmax = 0.0;
+  for (int c = tid; c < K; c += kPlanThreads) {
+    const double cx = cb[2 * c], cy = cb[2 * c + 1];
+    U = fmin(U, sq.dmax2(cx, cy));
+    cmax = fmax(cmax, sqrt(cx * cx + cy * cy));
+  }
   U = wave_min(U);
-  if (lane == 0) red[wave] = U;
+  cmax = wave_max(cmax);
+  if (lane == 0) { sh.red[wave] = U; sh.red2[wave] = cmax; }
   __syncthreads();
-  U = red[0];
+  U = sh.red[0];
+  cmax = sh.red2[0];
 #pragma unroll
-  for (int w = 1; w < kPlanWaves; ++w) U = fmin(U, red[w]);
+  for (int w = 1; w < kPlanWaves; ++w) { U = fmin(U, sh.red[w]); cmax = fmax(cmax, sh.red2[w]); }
+  const double reach = cmax + R * 1.4142135623730951;
+  const double delta = 1e-5 * reach * reach;
   const double slim = U + 2.0 * delta;
+
+  // ---- supercell survivors: thread t tests centroids [t P, t P + P), P = kPerThread
+  // (K <= 4096 = 2 kSuperMax, so two rounds at most), then one block-wide scan
   int nsurv = 0;
-  for (int c0 = 0; c0 < K; c0 += kPlanThreads) {
-    const int c = c0 + tid;
-    float cx = 0.0f, cy = 0.0f;
-    if (c < K) { cx = cb[2 * c]; cy = cb[2 * c + 1]; }
-    const bool pred = c < K && sq.dmin2(cx, cy) <= slim;
-    const uint64_t m = __ballot(pred);
-    __syncthreads();                        // previous round's wcount reads are done
-    if (lane == 0) wcount[wave] = __popcll(m);
+  for (int r0 = 0; r0 < K; r0 += kSuperMax) {
+    const int c0 = r0 + tid * kPerThread;
+    float2 v[kPerThread];
+    uint32_t mask = 0;
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int c = c0 + u;
+      v[u] = c < K ? make_float2(cb[2 * c], cb[2 * c + 1]) : make_float2(0.0f, 0.0f);
+      if (c < K && sq.dmin2(v[u].x, v[u].y) <= slim) mask |= 1u << u;
+    }
+    // exclusive prefix of the per-thread counts: wave scan, then across waves
+    const int mine = __popc(mask);
+    int incl = mine;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    __syncthreads();                        // the previous round's wsum reads are done
+    if (lane == kWave - 1) sh.wsum[wave] = incl;
     __syncthreads();
-    int before = nsurv, total = nsurv;
+    int before = nsurv + incl - mine, total = nsurv;
 #pragma unroll
     for (int w = 0; w < kPlanWaves; ++w) {
-      before += (w < wave) ? wcount[w] : 0;
-      total += wcount[w];
+      before += (w < wave) ? sh.wsum[w] : 0;
+      total += sh.wsum[w];
     }
-    const int pos = before + __popcll(m & ((1ull << lane) - 1ull));
-    if (pred && pos < kSuperMax) { surv[pos] = (uint16_t)c; survc[pos] = make_float2(cx, cy); }
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u)
+      if ((mask >> u) & 1u) {
+        if (before < kSuperMax) { sh.surv[before] = (uint16_t)(c0 + u); sh.survc[before] = v[u]; }
+        ++before;
+      }
     nsurv = total;
   }
   __syncthreads();
@@ -192,8 +197,8 @@ __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* _
   const int ns = all ? K : (nsurv + kRound - 1) / kRound * kRound;
   if (!all)
     for (int j = nsurv + tid; j < ns; j += kPlanThreads) {
-      survc[j] = make_float2(1e30f, 1e30f);
-      surv[j] = 0;
+      sh.survc[j] = make_float2(1e30f, 1e30f);
+      sh.surv[j] = 0;
     }
   __syncthreads();
 
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* _
     for (int j0 = 0; j0 < ns; j0 += kRound) {
       float2 v[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = survc[j0 + u * LPC + sub];
+      for (int u = 0; u < 4; ++u) v[u] = sh.survc[j0 + u * LPC + sub];
 #pragma unroll
       for (int u = 0; u < 4; ++u) Uc = fmin(Uc, cq.dmax2(v[u].x, v[u].y));
     }
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* _
 #pragma unroll
   for (int off = LPC / 2; off > 0; off >>= 1) Uc = fmin(Uc, __shfl_xor(Uc, off));   // within the group
   const double lim = Uc + delta;
-  uint16_t* mine = cell_list[qc];
+  uint16_t* mine = sh.cell_list[qc];
   const int gshift = lane & ~(LPC - 1);
   const uint64_t gmask = (LPC == 64) ? ~0ull : ((1ull << LPC) - 1ull);
   int count = 0;
@@ -238,15 +243,15 @@ __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* _
       int c[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        v[u] = survc[j0 + u * LPC + sub];
-        c[u] = surv[j0 + u * LPC + sub];
+        v[u] = sh.survc[j0 + u * LPC + sub];
+        c[u] = sh.surv[j0 + u * LPC + sub];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) take(cq.dmin2(v[u].x, v[u].y) <= lim, c[u]);
     }
   }
   __syncthreads();
-  if (sub != 0) return;                      // no barriers follow
+  if (sub != 0) return;
   // ---- the record: tail repeats the last entry (rescoring it never wins a strict "<")
   const bool overflow = count > lmax || count == 0;   // (a cell always lists at least one centroid)
   uint32_t words[8];
@@ -265,23 +270,43 @@ __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* _
   if (lmax == 16) out[1] = make_uint4(words[4], words[5], words[6], words[7]);
 }
 
+// One launch builds both grids: workgroups [0, nfine) are the fine grid's
+// 16 x 16-cell supercells (one lane per cell), the rest the outer grid's
+// 4 x 4-cell supercells (16 lanes per cell; its cells are larger, so a 16 x 16
+// supercell would keep most of the codebook).  Every workgroup computes the
+// largest centroid radius itself (with U of its supercell); workgroup 0 writes
+// the header.
+constexpr int kSuperFine = 16;
+constexpr int kSuperOuter = 4;
+constexpr int kFineSupercells = (kPlanG / kSuperFine) * (kPlanG / kSuperFine);
+constexpr int kOuterSupercells = (kPlanG2 / kSuperOuter) * (kPlanG2 / kSuperOuter);
+static_assert(kPlanG % kSuperFine == 0 && kPlanG2 % kSuperOuter == 0, "grids are whole supercells");
+
+__global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* __restrict__ cb, int K, int lmax,
+                                                                  char* __restrict__ plan, size_t outer_offset) {
+  __shared__ PlanShared sh;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    PlanHeader* hdr = reinterpret_cast<PlanHeader*>(plan);
+    hdr->R = kPlanR;
+    hdr->cells_per_unit = (float)kPlanG / (2.0f * kPlanR);
+    hdr->G = kPlanG;
+    hdr->lmax = lmax;
+    hdr->K = K;
+    hdr->R2 = kPlanR2;
+    hdr->cells_per_unit2 = (float)kPlanG2 / (2.0f * kPlanR2);
+    hdr->G2 = kPlanG2;
+  }
+  if (blockIdx.x < kFineSupercells)
+    build_supercell<kSuperFine>(sh, cb, K, lmax, kPlanR, kPlanG, blockIdx.x,
+                                reinterpret_cast<uint16_t*>(plan + kPlanHeaderBytes));
+  else
+    build_supercell<kSuperOuter>(sh, cb, K, lmax, kPlanR2, kPlanG2, blockIdx.x - kFineSupercells,
+                                 reinterpret_cast<uint16_t*>(plan + outer_offset));
+}
+
 int launch_build_plan(const float* cb, int K, void* plan, hipStream_t st) {
-  char* base = (char*)plan;
-  PlanHeader* hdr = (PlanHeader*)base;
-  double* cmax = (double*)(base + 128);     // scratch inside the header block
-  hipLaunchKernelGGL(codebook_radius_kernel, dim3(1), dim3(kBlockThreads), 0, st, cb, K, hdr, cmax);
-  int rc = check_launch("codebook_radius_kernel");
-  if (rc) return rc;
-  // fine grid: 16 x 16-cell supercells, one lane per cell; outer grid (larger
-  // cells, so more survivors per supercell): 4 x 4-cell supercells, 16 lanes per cell
-  static_assert(kPlanG % kSuperFine == 0 && kPlanG2 % kSuperOuter == 0, "grids are whole supercells");
-  hipLaunchKernelGGL(build_plan_kernel<kSuperFine>, dim3((kPlanG / kSuperFine) * (kPlanG / kSuperFine)),
-                     dim3(kPlanThreads), 0, st, cb, K, plan_lmax(K), kPlanR, kPlanG, (const double*)cmax,
-                     (uint16_t*)(base + kPlanHeaderBytes));
-  if ((rc = check_launch("build_plan_kernel"))) return rc;
-  hipLaunchKernelGGL(build_plan_kernel<kSuperOuter>, dim3((kPlanG2 / kSuperOuter) * (kPlanG2 / kSuperOuter)),
-                     dim3(kPlanThreads), 0, st, cb, K, plan_lmax(K), kPlanR2, kPlanG2, (const double*)cmax,
-                     (uint16_t*)(base + plan_outer_offset(K)));
+  hipLaunchKernelGGL(build_plan_kernel, dim3(kFineSupercells + kOuterSupercells), dim3(kPlanThreads), 0, st, cb, K,
+                     plan_lmax(K), (char*)plan, plan_outer_offset(K));
   return check_launch("build_plan_kernel");
 }
 

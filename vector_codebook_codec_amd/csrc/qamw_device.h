@@ -403,4 +403,53 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
+
+// ---------------------------------------------------------------------------
+// rho_n = sqrt(sum_j (W_nj s_j)^2) for one row, by one wavefront.  W_nj s_j
+// is exact in fp64 (24-bit x 24-bit significands); squares and sums are fp64,
+// reduced in a fixed order, so rho is deterministic and accurate to ~1e-16.
+// Lane 0 writes rho[n] and, when rho_f16 is given, its binary16 (RNE) bits.
+// ---------------------------------------------------------------------------
+template <typename Tin>
+__device__ __forceinline__ void row_norm_wave(const Tin* __restrict__ W, int64_t ldw, int n, int d,
+                                              const float* __restrict__ s, double* __restrict__ rho,
+                                              uint16_t* __restrict__ rho_f16) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nchunks = d >> 4;
+  const Tin* row = W + (int64_t)n * ldw;
+  double acc = 0.0;
+  auto add_chunk = [&](const float x[16], const float* sc) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const double w = (double)x[i] * (double)sc[i];   // exact: a bf16/fp32 times an fp32
+      acc = fma(w, w, acc);
+    }
+  };
+  // two chunks' loads in flight per lane, then the remainder
+  int c = lane;
+  for (; c + kWave < nchunks; c += 2 * kWave) {
+    float x[2][16], sc[2][16];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      load_chunk(row + (c + u * kWave) * kChunk, x[u]);
+      load_chunk(s + (c + u * kWave) * kChunk, sc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) add_chunk(x[u], sc[u]);
+  }
+  for (; c < nchunks; c += kWave) {
+    float x[16], sc[16];
+    load_chunk(row + c * kChunk, x);
+    load_chunk(s + c * kChunk, sc);
+    add_chunk(x, sc);
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) {
+    const double r = sqrt(acc);
+    rho[n] = r;
+    if (rho_f16) rho_f16[n] = f64_to_f16_bits(r);
+  }
+}
+
 }  // namespace qamw
