@@ -369,6 +369,45 @@ def decode(packed: np.ndarray, rho_hat_bits: np.ndarray, s, sigma: np.ndarray, b
 
 
 # ---------------------------------------------------------------------------
+# decoded weights times activations
+# ---------------------------------------------------------------------------
+def decode_matmul(X: np.ndarray, packed: np.ndarray, rho_hat_bits: np.ndarray, s, sigma: np.ndarray,
+                  b: int, sign_seed: int, C: np.ndarray, d: int) -> np.ndarray:
+    """Y = X W^^T, W^ the decoded matrix: the layer output that the pages'
+    pipeline computes after dequantising the weights (QAM-W, Methodology:
+    Decoding; the dequantise-then-matmul inference path).  X is (T, d), the
+    result (T, N), fp64: the plain definition, decode then multiply."""
+    Wh = decode(packed, rho_hat_bits, s, sigma, b, sign_seed, C, d)
+    return np.asarray(X, dtype=np.float64) @ Wh.T
+
+
+def rotate_activations(X: np.ndarray, s, b: int, sign_seed: int) -> np.ndarray:
+    """X~_t = R_fwd (X_t / s) for every activation row t (s = None means 1).
+
+    Because a decoded row is W^_n = rho^_n (R_fwd^T y^_n) / s and R_fwd is
+    orthogonal, <X_t, W^_n> = rho^_n <X~_t, y^_n>: a layer output can be
+    formed from the rotated activations and the looked-up pairs
+    y^_{n,2k:2k+2} = sigma_k C[idx_{n,k}] without undoing the rotation per
+    weight row.  fp64 (T, d)."""
+    X = np.asarray(X, dtype=np.float64)
+    if s is not None:
+        X = X / np.asarray(s, dtype=np.float64)[None, :]
+    return rotate_forward(X, sign_mask(sign_seed, X.shape[1]), b)
+
+
+def lookup_pairs(packed: np.ndarray, sigma: np.ndarray, C: np.ndarray, d: int) -> np.ndarray:
+    """y^_n: the looked-up pairs sigma_k C[idx_{n,k}], interleaved, fp64 (N, d)."""
+    C = np.asarray(C, dtype=np.float32).reshape(-1, 2).astype(np.float64)
+    K = C.shape[0]
+    idx = np.minimum(unpack(packed, K, d), K - 1)
+    sigma = np.asarray(sigma, dtype=np.float64)
+    Yh = np.empty((idx.shape[0], d))
+    Yh[:, 0::2] = sigma[None, :] * C[idx, 0]
+    Yh[:, 1::2] = sigma[None, :] * C[idx, 1]
+    return Yh
+
+
+# ---------------------------------------------------------------------------
 # layer-output error
 # ---------------------------------------------------------------------------
 def output_error_direct(X: np.ndarray, dW: np.ndarray) -> float:
