@@ -202,6 +202,40 @@ int32_t qamw_decode(const uint32_t* packed, const uint16_t* rownorm_f16, int64_t
                     const float* codebook, int32_t K,
                     void* W_out, int32_t out_dtype, int64_t ldo, void* stream);
 
+/*
+ * Decoded-weight matmul, Y = X W^^T, without materialising W^ (QAM-W,
+ * Methodology: Decoding; the pages dequantise to BF16 before the matmul and
+ * name the fused kernel as the missing piece).  A decoded row is
+ * W^_n = rho^_n (R_fwd^T y^_n) / s with y^_{n,2k:2k+2} = sigma_k C[idx_{n,k}],
+ * and R_fwd is orthogonal, so Y[t][n] = rho^_n <R_fwd (X_t / s), y^_n>:
+ * the activations are rotated once, and the matmul needs per weight only an
+ * index unpack, a codebook lookup and a scale by sigma_k.
+ *
+ * qamw_rotate_activations: Xr_bf16[t] = bf16_RNE(R_fwd (X[t] / s)).
+ *   X          [T][ldx] of xdtype (QAMW_F32 or QAMW_BF16), activations
+ *   s          [d] float32 channel scales of the matrix, or NULL (s = 1: use
+ *              with a matrix decoded as W diag(s), see qamw_decode)
+ *   block, sign_seed  those the matrix was encoded with
+ *   Xr_bf16    [T][ldr] bf16 bits out, rows 16-byte aligned (ldr % 8 == 0)
+ *
+ * qamw_decode_matmul: Y[t][n] = rho^_n sum_k Xr[t][k] y^_n[k].
+ *   Xr_bf16    [T][ldr] from qamw_rotate_activations
+ *   packed, rownorm_f16, N, sigma, codebook, K  as for qamw_decode
+ *   Y          [T][ldy] of ydtype (QAMW_F32 or QAMW_BF16), ldy >= N
+ * Products use bf16 operands (the looked-up y^ and Xr, rounded to nearest
+ * even) on bf16 MFMA with fp32 accumulation; each output is within
+ * 2^-7 rho^_n sum_k |Xr[t][k] y^_n[k]| of the exact product.  The sum over
+ * columns is split into a fixed number of parts added in a fixed order, so
+ * results are deterministic.
+ */
+int32_t qamw_rotate_activations(const void* X, int32_t xdtype, int64_t T, int64_t d, int64_t ldx,
+                                const float* s, int32_t block, uint64_t sign_seed,
+                                uint16_t* Xr_bf16, int64_t ldr, void* stream);
+int32_t qamw_decode_matmul(const uint16_t* Xr_bf16, int64_t T, int64_t d, int64_t ldr,
+                           const uint32_t* packed, const uint16_t* rownorm_f16, int64_t N,
+                           const float* sigma, const float* codebook, int32_t K,
+                           void* Y, int32_t ydtype, int64_t ldy, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -179,3 +179,31 @@ def test_build_plan_rejects(lib, kw, status):
 def test_workspace_size_is_enforced(lib):
     need = lib.qamw_calibrate_workspace_bytes(8, 256, 128)
     assert _calibrate(lib, ws_bytes=need - 1) == -4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block=8), -2), (dict(T=0), -1), (dict(X=None), -1), (dict(X=MIS), -1), (dict(xdt=2), -2),
+    (dict(out=None), -1), (dict(out=MIS), -1), (dict(ldr=260), -1), (dict(ldx=100), -1), (dict(s=MIS), -1),
+])
+def test_rotate_activations_rejects(lib, kw, status):
+    args = dict(X=A, xdt=1, T=4, d=256, ldx=256, s=A, block=128, seed=0, out=A, ldr=256, stream=None)
+    args.update(kw)
+    assert lib.qamw_rotate_activations(args["X"], args["xdt"], args["T"], args["d"], args["ldx"], args["s"],
+                                       args["block"], args["seed"], args["out"], args["ldr"],
+                                       args["stream"]) == status
+    assert lib.qamw_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), -1), (dict(N=0), -1), (dict(d=40), -1), (dict(K=1), -2), (dict(cb=MIS), -1), (dict(Xr=None), -1),
+    (dict(Xr=MIS), -1), (dict(packed=MIS), -1), (dict(ydt=2), -2), (dict(ldy=2), -1), (dict(ldr=100), -1),
+    (dict(ldr=260), -1), (dict(Y=None), -1),
+])
+def test_decode_matmul_rejects(lib, kw, status):
+    args = dict(Xr=A, T=4, d=256, ldr=256, packed=A, rn=A, N=8, sigma=A, cb=A, K=256, Y=A, ydt=0, ldy=8,
+                stream=None)
+    args.update(kw)
+    assert lib.qamw_decode_matmul(args["Xr"], args["T"], args["d"], args["ldr"], args["packed"], args["rn"],
+                                  args["N"], args["sigma"], args["cb"], args["K"], args["Y"], args["ydt"],
+                                  args["ldy"], args["stream"]) == status
+    assert lib.qamw_last_error()

@@ -11,6 +11,7 @@ from .codec import (  # noqa: F401
     qamw_calibrate,
     qamw_calibrate_workspace_bytes,
     qamw_decode,
+    qamw_decode_matmul,
     qamw_encode,
     qamw_encode_indices,
     qamw_encode_prepare,
@@ -18,6 +19,7 @@ from .codec import (  # noqa: F401
     qamw_index_bits,
     qamw_packed_row_words,
     qamw_plan_bytes,
+    qamw_rotate_activations,
 )
 
 __version__ = "0.1.0"

@@ -245,3 +245,48 @@ def qamw_decode(packed: torch.Tensor, rownorm_f16: torch.Tensor, d: int, s: Opti
         sigma.data_ptr(), int(block), int(sign_seed), codebook.data_ptr(), K, out.data_ptr(),
         _ODT[out.dtype], ldo, _stream(stream)))
     return out
+
+
+def qamw_rotate_activations(X: torch.Tensor, s: Optional[torch.Tensor], block: int, sign_seed: int,
+                            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Xr = bf16(R_fwd (X / s)) per activation row: the left operand of qamw_decode_matmul."""
+    T, d, ldx = _rows(X, "X")
+    if X.dtype not in _WDT:
+        raise ValueError("X must be float32 or bfloat16")
+    if s is not None:
+        _vec(s, "s", d)
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=X.device)
+    t2, d2, ldr = _rows(out, "out")
+    if (t2, d2) != (T, d) or out.dtype != torch.bfloat16:
+        raise ValueError("out must be a T x d bfloat16 tensor")
+    _lib.check("qamw_rotate_activations", _lib.load().qamw_rotate_activations(
+        X.data_ptr(), _WDT[X.dtype], T, d, ldx, None if s is None else s.data_ptr(), int(block), int(sign_seed),
+        out.data_ptr(), ldr, _stream(stream)))
+    return out
+
+
+def qamw_decode_matmul(Xr: torch.Tensor, packed: torch.Tensor, rownorm_f16: torch.Tensor, sigma: torch.Tensor,
+                       codebook: torch.Tensor, out_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Y = X W^^T [T][N] from rotated activations (qamw_rotate_activations) and the packed matrix."""
+    T, d, ldr = _rows(Xr, "Xr")
+    if Xr.dtype != torch.bfloat16:
+        raise ValueError("Xr must be bfloat16 (from qamw_rotate_activations)")
+    _dev(packed, "packed")
+    N = packed.shape[0]
+    K = _codebook(codebook)
+    rw = qamw_packed_row_words(d, K)
+    if packed.dtype != torch.int32 or tuple(packed.shape) != (N, rw) or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous int32 tensor of shape ({N}, {rw})")
+    _vec(rownorm_f16, "rownorm_f16", N, torch.int16)
+    _vec(sigma, "sigma", d // 2)
+    if out is None:
+        out = torch.empty((T, N), dtype=out_dtype, device=Xr.device)
+    t2, n2, ldy = _rows(out, "out")
+    if (t2, n2) != (T, N) or out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out must be T x N of float32 or bfloat16")
+    _lib.check("qamw_decode_matmul", _lib.load().qamw_decode_matmul(
+        Xr.data_ptr(), T, d, ldr, packed.data_ptr(), rownorm_f16.data_ptr(), N, sigma.data_ptr(),
+        codebook.data_ptr(), K, out.data_ptr(), _ODT[out.dtype], ldy, _stream(stream)))
+    return out

@@ -258,4 +258,38 @@ int32_t qamw_decode(const uint32_t* packed, const uint16_t* rownorm_f16, int64_t
                        W_out, out_dtype, ldo, (hipStream_t)stream);
 }
 
+int32_t qamw_rotate_activations(const void* X, int32_t xdtype, int64_t T, int64_t d, int64_t ldx, const float* s,
+                                int32_t block, uint64_t sign_seed, uint16_t* Xr_bf16, int64_t ldr, void* stream) {
+  int L = 0;
+  int rc = check_matrix(T, d, block, &L);
+  if (rc) return rc;
+  if (!X) return fail(QAMW_EINVAL, "X is NULL");
+  if (xdtype != QAMW_F32 && xdtype != QAMW_BF16) return fail(QAMW_EUNSUPPORTED, "activation dtype %d not supported", xdtype);
+  if (ldx < d || ldr < d) return fail(QAMW_EINVAL, "ldx and ldr must be >= d");
+  if (!Xr_bf16) return fail(QAMW_EINVAL, "Xr_bf16 is NULL");
+  if (!aligned16(X) || (ldx * elem_size(xdtype)) % 16 || !aligned16(Xr_bf16) || (ldr * 2) % 16 || (s && !aligned16(s)))
+    return fail(QAMW_EINVAL, "X, Xr_bf16 and s must be 16-byte aligned with 16-byte aligned rows");
+  return launch_rotate_act(L, X, xdtype, (int)T, (int)d, ldx, s, sign_seed, Xr_bf16, ldr, (hipStream_t)stream);
+}
+
+int32_t qamw_decode_matmul(const uint16_t* Xr_bf16, int64_t T, int64_t d, int64_t ldr, const uint32_t* packed,
+                           const uint16_t* rownorm_f16, int64_t N, const float* sigma, const float* codebook,
+                           int32_t K, void* Y, int32_t ydtype, int64_t ldy, void* stream) {
+  if (T <= 0 || N <= 0 || d <= 0) return fail(QAMW_EINVAL, "T, N and d must be positive");
+  if (T > kMaxDim || N > kMaxDim || d > kMaxDim) return fail(QAMW_EUNSUPPORTED, "matrix too large");
+  if (d % 16) return fail(QAMW_EINVAL, "d=%lld is not a multiple of 16", (long long)d);
+  int rc = check_codebook(codebook, K);
+  if (rc) return rc;
+  if (!Xr_bf16 || !packed || !rownorm_f16 || !sigma || !Y)
+    return fail(QAMW_EINVAL, "Xr_bf16, packed, rownorm_f16, sigma and Y must be non-NULL");
+  if (ydtype != QAMW_F32 && ydtype != QAMW_BF16) return fail(QAMW_EUNSUPPORTED, "output dtype %d not supported", ydtype);
+  if (ldr < d || ldy < N) return fail(QAMW_EINVAL, "ldr must be >= d and ldy >= N");
+  if (!aligned16(Xr_bf16) || (ldr * 2) % 16 || !aligned16(packed) || !aligned16(sigma))
+    return fail(QAMW_EINVAL, "Xr_bf16, packed and sigma must be 16-byte aligned, Xr rows too");
+  const int B = qamw_index_bits(K);
+  const int row_words = (int)qamw_packed_row_words(d, K);
+  return launch_decode_matmul(Xr_bf16, (int)T, (int)d, ldr, packed, row_words, rownorm_f16, (int)N, sigma, codebook,
+                              K, B, Y, ydtype, ldy, (hipStream_t)stream);
+}
+
 }  // extern "C"

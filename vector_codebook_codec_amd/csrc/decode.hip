@@ -33,23 +33,6 @@ constexpr int kDecodePrefetch = QAMW_DECODE_PREFETCH;
 // decodes the current one.  BT > 0 fixes the index width at compile time
 // (BT = 0: width B from the argument).
 // ---------------------------------------------------------------------------
-template <int BT>
-__device__ __forceinline__ void unpack8(const uint32_t w[4], uint32_t sh, int Bdyn, uint32_t idx[8]) {
-  const int B = BT ? BT : Bdyn;
-  const uint32_t mask = (1u << B) - 1u;
-  // the lane's 8*B bits, starting at bit 0 of a[0]
-  const uint32_t a[3] = {__builtin_amdgcn_alignbit(w[1], w[0], sh), __builtin_amdgcn_alignbit(w[2], w[1], sh),
-                         __builtin_amdgcn_alignbit(w[3], w[2], sh)};
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int o = p * B;
-    const int q = o >> 5;
-    const uint32_t lo = (q == 0) ? a[0] : ((q == 1) ? a[1] : a[2]);
-    const uint32_t hi = (q == 0) ? a[1] : ((q == 1) ? a[2] : 0u);
-    idx[p] = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(o & 31)) & mask;
-  }
-}
-
 template <int L, int BT, typename Out>
 __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
     const uint32_t* __restrict__ packed, const uint16_t* __restrict__ rho_f16, int N, int d,

@@ -452,4 +452,27 @@ __device__ __forceinline__ void row_norm_wave(const Tin* __restrict__ W, int64_t
   }
 }
 
+// ---------------------------------------------------------------------------
+// Eight B-bit indices from a lane's packed words: w[0..3] hold the bits from
+// word floor(bitstart / 32) on, sh = bitstart mod 32; index p is bits
+// [p B, p B + B) of the stream that starts at bit sh of w[0] (sh + 8 B <= 127
+// bits, gathered into three words by alignbit).  BT > 0 fixes B at compile time.
+// ---------------------------------------------------------------------------
+template <int BT>
+__device__ __forceinline__ void unpack8(const uint32_t w[4], uint32_t sh, int Bdyn, uint32_t idx[8]) {
+  const int B = BT ? BT : Bdyn;
+  const uint32_t mask = (1u << B) - 1u;
+  // the lane's 8*B bits, starting at bit 0 of a[0]
+  const uint32_t a[3] = {__builtin_amdgcn_alignbit(w[1], w[0], sh), __builtin_amdgcn_alignbit(w[2], w[1], sh),
+                         __builtin_amdgcn_alignbit(w[3], w[2], sh)};
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int o = p * B;
+    const int q = o >> 5;
+    const uint32_t lo = (q == 0) ? a[0] : ((q == 1) ? a[1] : a[2]);
+    const uint32_t hi = (q == 0) ? a[1] : ((q == 1) ? a[2] : 0u);
+    idx[p] = __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(o & 31)) & mask;
+  }
+}
+
 }  // namespace qamw
