@@ -18,6 +18,9 @@ valu_view     the same launch against the fp32 vector peak, counting the
               exhaustive search's pairs x K x 4 flops
 cpu_baseline  the fp64 NumPy oracle, single-threaded, on a 160-row sample of
               the same workload (calibrate + encode + decode of those rows)
+decode_matmul the fused decoded-weight matmul Y = X W^^T on the packed matrix
+              for T tokens, against decode-to-bf16 + torch.matmul (not part
+              of the step)
 """
 from __future__ import annotations
 
@@ -73,6 +76,9 @@ def parse():
                     help="decode-only reps timed after overwriting a 1 GiB buffer")
     ap.add_argument("--exhaustive-reps", type=int, default=5,
                     help="encodes without a search plan timed after the steps (0 to skip)")
+    ap.add_argument("--matmul-tokens", type=int, nargs="*", default=[1, 16, 64],
+                    help="token counts T of the fused decoded-weight matmul measurement")
+    ap.add_argument("--matmul-reps", type=int, default=10)
     ap.add_argument("--copy-reference", type=int, default=0,
                     help="also run N copies of a 1 GiB buffer (counter calibration)")
     return ap.parse_args()
@@ -190,6 +196,46 @@ def main():
         cold.append(a.elapsed_time(z))
     dec_cold_ms = float(np.median(cold)) if cold else None
 
+    # fused decoded-weight matmul Y = X W^^T for T tokens (not part of the step)
+    mm = {}
+    for T in args.matmul_tokens:
+        X = torch.randn((T, d), device=dev, dtype=torch.float32).to(torch.bfloat16)
+        Xr = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+        Y = torch.empty((T, N), dtype=torch.float32, device=dev)
+        Wbf = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
+
+        def fused():
+            q.qamw_rotate_activations(X, s, b, wl.sign_seed, Xr, stream)
+            q.qamw_decode_matmul(Xr, packed, rn, sigma, Ct, out=Y, stream=stream)
+
+        def unfused():
+            q.qamw_decode(packed, rn, d, s, sigma, b, wl.sign_seed, Ct, out=Wbf, stream=stream)
+            torch.matmul(X, Wbf.t())
+
+        res_t = {}
+        for name, fn in (("fused", fused), ("unfused", unfused)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(args.matmul_reps):
+                a, z = ev(), ev()
+                a.record(stream)
+                fn()
+                z.record(stream)
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(z))
+            res_t[name] = float(np.median(times))
+        # algorithmic bytes of the fused path: packed + row norms + sigma + X read + Xr write/read + Y write
+        mm_bytes = N * rw * 4 + N * 2 + d * 2 + T * d * 2 * 3 + T * N * 4
+        mm[str(T)] = {"fused_us": res_t["fused"] * 1e3, "unfused_us": res_t["unfused"] * 1e3,
+                      "algorithmic_bytes": mm_bytes,
+                      "GB_s": mm_bytes / (res_t["fused"] * 1e-3) / 1e9,
+                      "frac_hbm": mm_bytes / (res_t["fused"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                      "tflops": 2.0 * T * N * d / (res_t["fused"] * 1e-3) / 1e12}
+        print(f"decode_matmul T={T}: fused {res_t['fused'] * 1e3:.1f} us, "
+              f"decode-to-bf16 + torch.matmul {res_t['unfused'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+
     for _ in range(args.copy_reference):
         flush2 = torch.empty_like(flush)
         flush2.copy_(flush)
@@ -246,6 +292,9 @@ def main():
             "GB_s": dec_bytes / (dec_cold_ms * 1e-3) / 1e9,
             "frac_hbm": dec_bytes / (dec_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
         "achieved_bpw": B / 2 + 16.0 / d,
+        "decode_matmul": {"note": "Y = X W^^T over the packed matrix (qamw_rotate_activations + "
+                                  "qamw_decode_matmul) vs qamw_decode to bf16 + torch.matmul; per T",
+                          "by_tokens": mm},
     }
     if not args.no_cpu_baseline:
         print("timing the CPU oracle on a 160-row sample", file=sys.stderr, flush=True)

@@ -24,6 +24,7 @@ namespace qamw {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // Xr_t = R_fwd (X_t / s), rounded to bf16 (RNE).  One wavefront per window of
@@ -81,16 +82,17 @@ __global__ __launch_bounds__(kBlockThreads) void rotate_act_kernel(const Tin* __
 // ---------------------------------------------------------------------------
 // Y[t][n] = rho^_n sum_k Xr[t][k] y^[n][k] on v_mfma_f32_16x16x32_bf16.
 //
-// A workgroup (8 wavefronts) owns 16 output channels n0..n0+15 and 16 TT
+// A workgroup (16 wavefronts; 8 for more than one token tile) owns 16 output channels n0..n0+15 and 16 TT
 // tokens; its wavefronts split the columns in super-steps of 64 columns (32
-// pairs).  In a super-step lane l (g = l / 16) decodes the 8 pairs
+// pairs), each loading the next super-step's operands while it works on the
+// current one.  In a super-step lane l (g = l / 16) decodes the 8 pairs
 // [32 ss + 8 g, +8) of row n0 + l % 16 -- one byte-aligned run of 8 B bits --
 // into two bf16x8 B operands, and loads the matching 16 activation columns
 // as two bf16x8 A operands per 16-token tile.  The MFMA's k slots are thereby
 // a permutation of the columns, applied identically to A and B.  MFMA
 // layout (16x16x32 bf16): lane l holds A[l % 16][8 (l / 16) + e] and
 // B[8 (l / 16) + e][l % 16]; the result register r of lane l is
-// C[4 (l / 16) + r][l % 16].  Partial sums of the 8 wavefronts are added in
+// C[4 (l / 16) + r][l % 16].  Partial sums of the wavefronts are added in
 // a fixed order through LDS, so results are deterministic.
 // ---------------------------------------------------------------------------
 // output element types
@@ -103,81 +105,167 @@ struct OutBF16 {
   static __device__ void put(uint16_t* p, float v) { *p = (uint16_t)f32_to_bf16_bits(v); }
 };
 
-constexpr int kMmThreads = 512;
-constexpr int kMmWaves = kMmThreads / kWave;
+// wavefronts per workgroup: 16 for one token tile, 8 when more tiles need registers
+template <int TT> constexpr int mm_waves() { return TT == 1 ? 16 : 8; }
+
+// Global loads are coalesced: per super-step a wavefront loads the 16 rows'
+// packed bits (the 16-byte-aligned 64 bytes covering each row's 4 B bytes),
+// the 16 TT activation rows' 64 columns (128 bytes each) and the 32 sigma
+// values, into a ring of D super-steps in registers.  When a super-step is
+// consumed the wavefront moves it through a private LDS stage into the MFMA
+// lane layout.  All loads of a super-step are issued together, in the order
+// they are consumed, from clamped valid addresses (vector memory counters
+// complete in order; a conditional load would make them unknown).
+template <int TT>
+struct MmLoads {       // plain vector members so the slots stay in registers
+  u32x4 pk;            // packed row l / 4, 16-byte chunk l % 4 of the super-step's span
+  u32x4 a[TT][2];      // activation row l / 4 (of tile tt), columns 16 (l % 4) .. + 16
+  u32x4 sg;            // sigma of pairs 4 (l % 8) .. + 4
+};
+template <int TT> constexpr int mm_depth() { return TT == 1 ? 4 : 2; }
+// stage rows are padded (packed rows 72 bytes, activation rows 144) so that the
+// MFMA-layout reads of 16 rows fall in different LDS banks
+constexpr int kStPkRow = 18;      // dwords
+constexpr int kStARow = 144;      // bytes
+template <int TT> constexpr int mm_stage_bytes() { return 16 * kStPkRow * 4 + 16 * TT * kStARow + 128; }
 
 template <int BT, int TT, typename Out>
-__global__ __launch_bounds__(kMmThreads) void decode_matmul_kernel(
+__global__ __launch_bounds__(mm_waves<TT>() * kWave) void decode_matmul_kernel(
     const uint16_t* __restrict__ Xr, int T, int d, int64_t ldr, const uint32_t* __restrict__ packed,
     int row_words, const uint16_t* __restrict__ rho_f16, int N, const float* __restrict__ sigma,
     const float* __restrict__ codebook, int K, int Bdyn, typename Out::T* __restrict__ Y, int64_t ldy) {
+  constexpr int kMmWaves = mm_waves<TT>();
+  constexpr int kMmThreads = kMmWaves * kWave;
+  constexpr int D = mm_depth<TT>();
   extern __shared__ float4 lds4[];
   float2* cb = reinterpret_cast<float2*>(lds4);                    // K centroids
   float* red = reinterpret_cast<float*>(cb + ((K + 1) & ~1));       // kMmWaves x TT x 256 partial sums
+  char* stage_all = reinterpret_cast<char*>(red + kMmWaves * TT * 256);
 
   for (int c = threadIdx.x; c < K; c += kMmThreads) cb[c] = make_float2(codebook[2 * c], codebook[2 * c + 1]);
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
-  const int g = lane >> 4;                 // k-slot group
+  const int g = lane >> 4;                 // k-slot group (MFMA layout)
   const int nl = lane & 15;
+  const int lr = lane >> 2, lq = lane & 3; // row and 16/32-byte chunk (load layout)
   const int n0 = blockIdx.x * 16;
   const int t0 = blockIdx.y * 16 * TT;
-  const int n = n0 + nl;
   const int B = BT ? BT : Bdyn;
   const int half_d = d >> 1;
   const int nsteps = (half_d + 31) / 32;
-  const uint32_t* prow = packed + (int64_t)min(n, N - 1) * row_words;
+  char* stage = stage_all + wave * mm_stage_bytes<TT>();
+  uint32_t* st_pk = reinterpret_cast<uint32_t*>(stage);                         // [16 rows][kStPkRow dwords]
+  char* st_a = stage + 16 * kStPkRow * 4;                                       // [16 TT rows][kStARow bytes]
+  float* st_sg = reinterpret_cast<float*>(st_a + 16 * TT * kStARow);           // [32]
+  const u32x4* prow16 = reinterpret_cast<const u32x4*>(packed + (int64_t)min(n0 + lr, N - 1) * row_words);
+  const int row_chunks = row_words >> 2;   // row_words % 4 == 0
+
+  auto load = [&](int ss) __attribute__((always_inline)) {
+    MmLoads<TT> m;
+    const int abase16 = (ss * 4 * B) >> 4;                // first 16-byte chunk of the super-step's span
+    m.pk = prow16[min(abase16 + lq, row_chunks - 1)];
+#pragma clang loop unroll(full)
+    for (int tt = 0; tt < TT; ++tt) {
+      const int t = min(t0 + 16 * tt + lr, T - 1);
+      const int col = min(64 * ss + 16 * lq, d - 16);
+      const u32x4* ap = reinterpret_cast<const u32x4*>(Xr + (int64_t)t * ldr + col);
+      m.a[tt][0] = ap[0];
+      m.a[tt][1] = ap[1];
+    }
+    const int sp = min(32 * ss + 4 * (lane & 7), half_d - 4);
+    m.sg = *reinterpret_cast<const u32x4*>(sigma + sp);
+    return m;
+  };
 
   f32x4 acc[TT];
-#pragma unroll
+#pragma clang loop unroll(full)
   for (int tt = 0; tt < TT; ++tt) acc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int ss = wave; ss < nsteps; ss += kMmWaves) {
-    const int p0 = ss * 32 + 8 * g;        // first of the lane's 8 pairs
-    // ---- B: 8 looked-up pairs of row n (zeros past the row end or past N)
+  // one sub-step: stage super-step ss (held in `slot`), reload the slot for
+  // ss + D W, decode and multiply
+  auto step = [&](MmLoads<TT>& slot, int ss) __attribute__((always_inline)) {
+    // ---- through the stage into the MFMA layout
+    {
+      u32x2* pd = reinterpret_cast<u32x2*>(st_pk + lr * kStPkRow + 4 * lq);
+      pd[0] = u32x2{slot.pk.x, slot.pk.y};
+      pd[1] = u32x2{slot.pk.z, slot.pk.w};
+    }
+#pragma clang loop unroll(full)
+    for (int tt = 0; tt < TT; ++tt) {
+      u32x4* ad = reinterpret_cast<u32x4*>(st_a + (16 * tt + lr) * kStARow + 32 * lq);
+      ad[0] = slot.a[tt][0];
+      ad[1] = slot.a[tt][1];
+    }
+    if (lane < 8) reinterpret_cast<u32x4*>(st_sg)[lane] = slot.sg;
+    wave_lds_fence();
+    slot = load(ss + D * kMmWaves);
+
+    const int p0 = ss * 32 + 8 * g;
+    const int n = n0 + nl;
     float v[16];
     if (p0 < half_d && n < N) {
-      const int bitstart = p0 * B;
-      const int wstart = bitstart >> 5;
+      const int bit = p0 * B - ((ss * 4 * B) >> 4) * 128;   // bit offset inside the row's staged 64 bytes
+      const int w0 = bit >> 5;                               // <= 12 for B <= 12: w0 + 3 < 16
       uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = prow[min(wstart + i, row_words - 1)];
+#pragma clang loop unroll(full)
+      for (int i = 0; i < 4; ++i) w[i] = st_pk[nl * kStPkRow + w0 + i];
       uint32_t idx[8];
-      unpack8<BT>(w, (uint32_t)(bitstart & 31), Bdyn, idx);
-      const float4* sp = reinterpret_cast<const float4*>(sigma + p0);   // p0 % 8 == 0, half_d % 8 == 0
-      const float4 s0 = sp[0], s1 = sp[1];
+      unpack8<BT>(w, (uint32_t)(bit & 31), Bdyn, idx);
+      const float4 s0 = reinterpret_cast<const float4*>(st_sg)[2 * g];
+      const float4 s1 = reinterpret_cast<const float4*>(st_sg)[2 * g + 1];
       const float sg[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
+#pragma clang loop unroll(full)
       for (int p = 0; p < 8; ++p) {
         const float2 cc = cb[min((int)idx[p], K - 1)];
         v[2 * p] = cc.x * sg[p];
         v[2 * p + 1] = cc.y * sg[p];
       }
     } else {
-#pragma unroll
+#pragma clang loop unroll(full)
       for (int i = 0; i < 16; ++i) v[i] = 0.0f;
     }
     bf16x8 b0, b1;
-#pragma unroll
+#pragma clang loop unroll(full)
     for (int e = 0; e < 8; ++e) {
       b0[e] = (__bf16)v[e];
       b1[e] = (__bf16)v[8 + e];
     }
-    // ---- A: columns [2 p0, 2 p0 + 16) of token t0 + 16 tt + nl, for each tile
-#pragma unroll
+#pragma clang loop unroll(full)
     for (int tt = 0; tt < TT; ++tt) {
-      const int t = t0 + 16 * tt + nl;
-      uint4 a0 = make_uint4(0, 0, 0, 0), a1 = make_uint4(0, 0, 0, 0);
-      if (t < T && p0 < half_d) {
-        const uint4* ap = reinterpret_cast<const uint4*>(Xr + (int64_t)t * ldr + 2 * p0);
-        a0 = ap[0];
-        a1 = ap[1];
-      }
+      // activation rows past T contribute zeros (their loads read row T - 1)
+      const bool tin = t0 + 16 * tt + nl < T;
+      const u32x4* as = reinterpret_cast<const u32x4*>(st_a + (16 * tt + nl) * kStARow + 32 * g);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const u32x4 a0 = tin ? as[0] : z, a1 = tin ? as[1] : z;
       acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), b0, acc[tt], 0, 0, 0);
       acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), b1, acc[tt], 0, 0, 0);
     }
+    wave_lds_fence();                        // the stage is rewritten by the next sub-step
+  };
+
+  // D named ring slots: slot u holds super-step ss0 + u W.  Named variables
+  // keep each slot in its own registers (moving in-flight loads between
+  // registers would wait for them), and every path runs all D sub-steps (a
+  // super-step past the end multiplies zeros) so the counters agree on every
+  // path.
+  static_assert(D >= 2 && D <= 4, "ring depth");
+  // The prologue issues the slots' loads strictly in slot order (scheduling
+  // barriers), so that at the loop head the oldest loads are slot 0's.
+  MmLoads<TT> r0 = load(wave), r1, r2, r3;
+  __builtin_amdgcn_sched_barrier(0);
+  r1 = load(wave + kMmWaves);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (D > 2) r2 = load(wave + 2 * kMmWaves);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (D > 3) r3 = load(wave + 3 * kMmWaves);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int ss0 = wave; ss0 < nsteps; ss0 += D * kMmWaves) {
+    step(r0, ss0);
+    step(r1, ss0 + kMmWaves);
+    if constexpr (D > 2) step(r2, ss0 + 2 * kMmWaves);
+    if constexpr (D > 3) step(r3, ss0 + 3 * kMmWaves);
   }
 
   // ---- fixed-order sum over the wavefronts, scale by rho^_n, store
@@ -227,8 +315,9 @@ template <int BT, int TT>
 static int launch_mm(const uint16_t* Xr, int T, int d, int64_t ldr, const uint32_t* packed, int row_words,
                      const uint16_t* rn, int N, const float* sigma, const float* cb, int K, int B, void* Y,
                      int32_t ydt, int64_t ldy, hipStream_t st) {
-  const dim3 grid((unsigned)((N + 15) / 16), (unsigned)((T + 16 * TT - 1) / (16 * TT))), blk(kMmThreads);
-  const size_t lds = (size_t)((K + 1) & ~1) * sizeof(float2) + (size_t)kMmWaves * TT * 256 * sizeof(float);
+  const dim3 grid((unsigned)((N + 15) / 16), (unsigned)((T + 16 * TT - 1) / (16 * TT))), blk(mm_waves<TT>() * kWave);
+  const size_t lds = (size_t)((K + 1) & ~1) * sizeof(float2) + (size_t)mm_waves<TT>() * TT * 256 * sizeof(float) +
+                     (size_t)mm_waves<TT>() * mm_stage_bytes<TT>();
   if (ydt == QAMW_F32)
     hipLaunchKernelGGL((decode_matmul_kernel<BT, TT, OutF32>), grid, blk, lds, st, Xr, T, d, ldr, packed, row_words,
                        rn, N, sigma, cb, K, B, (float*)Y, ldy);
