@@ -21,6 +21,9 @@ cpu_baseline  the fp64 NumPy oracle, single-threaded, on a 160-row sample of
 decode_matmul the fused decoded-weight matmul Y = X W^^T on the packed matrix
               for T tokens, against decode-to-bf16 + torch.matmul (not part
               of the step)
+polar         the polar-code baseline encode (qamw_encode_polar, 8 amplitude
+              levels x 32 phases = 8 bits per pair) on the same matrix with
+              the step's s and sigma (not part of the step)
 """
 from __future__ import annotations
 
@@ -79,6 +82,8 @@ def parse():
     ap.add_argument("--matmul-tokens", type=int, nargs="*", default=[1, 16, 64],
                     help="token counts T of the fused decoded-weight matmul measurement")
     ap.add_argument("--matmul-reps", type=int, default=10)
+    ap.add_argument("--polar-reps", type=int, default=10,
+                    help="polar-code encodes (8 amplitudes x 32 phases) timed after the steps (0 to skip)")
     ap.add_argument("--copy-reference", type=int, default=0,
                     help="also run N copies of a 1 GiB buffer (counter calibration)")
     return ap.parse_args()
@@ -236,6 +241,35 @@ def main():
         print(f"decode_matmul T={T}: fused {res_t['fused'] * 1e3:.1f} us, "
               f"decode-to-bf16 + torch.matmul {res_t['unfused'] * 1e3:.1f} us", file=sys.stderr, flush=True)
 
+    # polar-code baseline encode at 8 bits per pair (not part of the step)
+    polar = None
+    if args.polar_reps > 0:
+        Ka, Kp = 8, 32
+        lv, dr, _ = q.load_polar(Ka, Kp)
+        lv_t, dr_t = torch.from_numpy(lv).to(dev), torch.from_numpy(dr).to(dev)
+        rw_p = q.qamw_packed_row_words(d, Ka * Kp)
+        packed_p = torch.empty((N, rw_p), dtype=torch.int32, device=dev)
+        rn_p = torch.empty(N, dtype=torch.int16, device=dev)
+        for _ in range(2):
+            q.qamw_encode_polar(W, s, sigma, b, wl.sign_seed, lv_t, dr_t, packed_p, rn_p, ws_enc, stream)
+        torch.cuda.synchronize()
+        pt = []
+        for _ in range(args.polar_reps):
+            a, z = ev(), ev()
+            a.record(stream)
+            q.qamw_encode_polar(W, s, sigma, b, wl.sign_seed, lv_t, dr_t, packed_p, rn_p, ws_enc, stream)
+            z.record(stream)
+            torch.cuda.synchronize()
+            pt.append(a.elapsed_time(z))
+        p_ms = float(np.median(pt))
+        in_b = 2 if wl.wdtype == "bf16" else 4
+        p_bytes = 2 * N * d * in_b + N * rw_p * 4 + N * 2     # W read twice (prepare, quantise) + packed + norms
+        polar = {"Ka": Ka, "Kp": Kp, "bits_per_index": q.qamw_index_bits(Ka * Kp), "ms": p_ms,
+                 "gweights_s": N * d / (p_ms * 1e-3) / 1e9, "algorithmic_bytes": p_bytes,
+                 "frac_hbm": p_bytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                 "note": "qamw_encode_polar = encode_prepare_kernel + encode_polar_kernel"}
+        print(f"polar encode {Ka}x{Kp}: {p_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+
     for _ in range(args.copy_reference):
         flush2 = torch.empty_like(flush)
         flush2.copy_(flush)
@@ -295,6 +329,7 @@ def main():
         "decode_matmul": {"note": "Y = X W^^T over the packed matrix (qamw_rotate_activations + "
                                   "qamw_decode_matmul) vs qamw_decode to bf16 + torch.matmul; per T",
                           "by_tokens": mm},
+        "polar": polar,
     }
     if not args.no_cpu_baseline:
         print("timing the CPU oracle on a 160-row sample", file=sys.stderr, flush=True)

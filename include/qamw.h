@@ -187,6 +187,27 @@ int32_t qamw_encode_indices(const void* W, int32_t wdtype, int64_t N, int64_t d,
                             const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Polar-code baseline (QAM-W, Methodology: Joint 2D Quantization, and the
+ * Experiments' joint-versus-polar ablation): the same transform as
+ * qamw_encode, but amplitude and phase of each normalised pair z~ = (x, y)
+ * are quantised independently.
+ *   levels  [Ka] float32 amplitude levels, >= 0 and strictly ascending
+ *   dirs    [Kp][2] float32 unit directions (cos, sin); 2 <= Ka Kp <= 4096
+ *   index   ia * Kp + ip, packed with B = ceil(log2(Ka Kp)) bits exactly as
+ *           qamw_encode packs (qamw_packed_row_words(d, Ka * Kp) words a row)
+ *   ia      the lowest i minimising |r - a_i|, r = sqrt(x*x + y*y), all fp32
+ *   ip      the lowest j maximising x c_j + y s_j in fp32
+ * Other arguments as for qamw_encode.  The result decodes with qamw_decode
+ * (and qamw_decode_matmul) given the Ka Kp-entry table whose entry
+ * ia * Kp + ip is a_ia (c_ip, s_ip).
+ */
+int32_t qamw_encode_polar(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
+                          const float* s, const float* sigma, int32_t block, uint64_t sign_seed,
+                          const float* levels, int32_t Ka, const float* dirs, int32_t Kp,
+                          uint32_t* packed, uint16_t* rownorm_f16,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode (QAM-W, Methodology: Decoding).
  *   packed, rownorm_f16, N, d, block, sign_seed, codebook, K  as produced by
  *             qamw_encode; indices >= K (never produced) are clamped to K - 1

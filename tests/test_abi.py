@@ -118,6 +118,26 @@ def test_encode_indices_rejects(lib, kw, status):
     assert lib.qamw_last_error()
 
 
+def _polar(lib, **kw):
+    args = dict(W=A, wdt=1, N=8, d=256, ldw=256, s=A, sigma=A, block=128, seed=0, lv=A, Ka=8, dirs=A, Kp=32,
+                packed=A, rn=A, ws=WS, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return lib.qamw_encode_polar(args["W"], args["wdt"], args["N"], args["d"], args["ldw"], args["s"],
+                                 args["sigma"], args["block"], args["seed"], args["lv"], args["Ka"], args["dirs"],
+                                 args["Kp"], args["packed"], args["rn"], args["ws"], args["ws_bytes"],
+                                 args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block=8), -2), (dict(Ka=0), -2), (dict(Kp=0), -2), (dict(Ka=1, Kp=1), -2), (dict(Ka=64, Kp=128), -2),
+    (dict(lv=None), -1), (dict(dirs=None), -1), (dict(packed=MIS), -1), (dict(s=None), -1), (dict(rn=None), -1),
+    (dict(ws=None), -4), (dict(ws_bytes=100), -4), (dict(ldw=100), -1), (dict(wdt=2), -2),
+])
+def test_encode_polar_rejects(lib, kw, status):
+    assert _polar(lib, **kw) == status
+    assert lib.qamw_last_error()
+
+
 def _calibrate(lib, **kw):
     args = dict(W=A, wdt=0, N=8, d=256, ldw=256, r=A, alpha=0.5, block=128, seed=0, s=A, sigma=A,
                 ws=WS, ws_bytes=1 << 20, stream=None)

@@ -7,6 +7,7 @@ points ``qamw_calibrate``, ``qamw_encode`` and ``qamw_decode``.
 """
 from .codec import (  # noqa: F401
     load_codebook,
+    load_polar,
     qamw_build_plan,
     qamw_calibrate,
     qamw_calibrate_workspace_bytes,
@@ -14,6 +15,7 @@ from .codec import (  # noqa: F401
     qamw_decode_matmul,
     qamw_encode,
     qamw_encode_indices,
+    qamw_encode_polar,
     qamw_encode_prepare,
     qamw_encode_workspace_bytes,
     qamw_index_bits,

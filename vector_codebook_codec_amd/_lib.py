@@ -31,6 +31,8 @@ SIGNATURES = {
     "qamw_encode": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "qamw_encode_prepare": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _p, _sz, _p]),
     "qamw_encode_indices": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _i32, _p, _p, _p, _sz, _p]),
+    "qamw_encode_polar": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _i32, _p, _p, _p,
+                                 _sz, _p]),
     "qamw_rotate_activations": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _i32, _u64, _p, _i64, _p]),
     "qamw_decode_matmul": (_i32, [_p, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _i32, _p, _i32, _i64, _p]),
     "qamw_decode": (_i32, [_p, _p, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _i32, _i64, _p]),

@@ -92,6 +92,23 @@ def load_codebook(K: int) -> np.ndarray:
     return C
 
 
+def load_polar(Ka: int, Kp: int):
+    """The stored polar code Ka x Kp: (levels [Ka], dirs [Kp][2], table [Ka Kp][2]), float32.
+
+    ``table`` is the decode codebook: entry ia * Kp + ip = levels[ia] * dirs[ip]."""
+    base = os.path.join(CODEBOOK_DIR, f"polar_A{Ka}_P{Kp}")
+    with open(base + ".json") as f:
+        meta = json.load(f)
+    if (meta["Ka"], meta["Kp"]) != (Ka, Kp):
+        raise ValueError(f"polar metadata mismatch for {Ka} x {Kp}")
+
+    def read(name, shape):
+        with open(name, "rb") as f:
+            return np.frombuffer(f.read(), dtype="<f4").reshape(shape).copy()
+
+    return read(base + "_levels.f32", (Ka,)), read(base + "_dirs.f32", (Kp, 2)), read(base + ".f32", (Ka * Kp, 2))
+
+
 # ---------------------------------------------------------------- entry points
 def qamw_build_plan(codebook: torch.Tensor, plan: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Nearest-centroid search plan for `codebook` (uint8 device buffer) for qamw_encode(plan=...)."""
@@ -219,6 +236,42 @@ def qamw_encode_indices(W: torch.Tensor, block: int, codebook: torch.Tensor, wor
         None if plan is None else plan.data_ptr(), packed.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return packed
+
+
+def qamw_encode_polar(W: torch.Tensor, s: torch.Tensor, sigma: torch.Tensor, block: int, sign_seed: int,
+                      levels: torch.Tensor, dirs: torch.Tensor, packed: Optional[torch.Tensor] = None,
+                      rownorm_f16: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None):
+    """Polar-code encode: returns (packed [N][row_words] int32, rownorm [N] int16 holding fp16 bits);
+    indices ia * Kp + ip decode with the Ka Kp-entry table of ``load_polar``."""
+    N, d, ldw = _rows(W, "W")
+    if W.dtype not in _WDT:
+        raise ValueError("W must be float32 or bfloat16")
+    _vec(s, "s", d)
+    _vec(sigma, "sigma", d // 2)
+    _dev(levels, "levels")
+    if levels.dtype != torch.float32 or levels.dim() != 1 or not levels.is_contiguous():
+        raise ValueError("levels must be a contiguous 1-D float32 tensor")
+    Ka = levels.shape[0]
+    Kp = _codebook(dirs)
+    rw = qamw_packed_row_words(d, Ka * Kp)
+    if rw < 0:
+        raise ValueError(f"unsupported Ka x Kp = {Ka} x {Kp} or d={d}")
+    if packed is None:
+        packed = torch.empty((N, rw), dtype=torch.int32, device=W.device)
+    if rownorm_f16 is None:
+        rownorm_f16 = torch.empty(N, dtype=torch.int16, device=W.device)
+    _dev(packed, "packed")
+    if packed.dtype != torch.int32 or tuple(packed.shape) != (N, rw) or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous int32 tensor of shape ({N}, {rw})")
+    _vec(rownorm_f16, "rownorm_f16", N, torch.int16)
+    if workspace is None:
+        workspace = _workspace(qamw_encode_workspace_bytes(N, d), W.device)
+    _lib.check("qamw_encode_polar", _lib.load().qamw_encode_polar(
+        W.data_ptr(), _WDT[W.dtype], N, d, ldw, s.data_ptr(), sigma.data_ptr(), int(block), int(sign_seed),
+        levels.data_ptr(), Ka, dirs.data_ptr(), Kp, packed.data_ptr(), rownorm_f16.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return packed, rownorm_f16
 
 
 def qamw_decode(packed: torch.Tensor, rownorm_f16: torch.Tensor, d: int, s: Optional[torch.Tensor],

@@ -237,6 +237,32 @@ int32_t qamw_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t
                              stream);
 }
 
+int32_t qamw_encode_polar(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, const float* s,
+                          const float* sigma, int32_t block, uint64_t sign_seed, const float* levels, int32_t Ka,
+                          const float* dirs, int32_t Kp, uint32_t* packed, uint16_t* rownorm_f16, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int L = 0;
+  int rc = check_matrix(N, d, block, &L);
+  if (rc) return rc;
+  if ((rc = check_weights(W, wdtype, d, ldw))) return rc;
+  if (!levels || !dirs) return fail(QAMW_EINVAL, "levels and dirs must be non-NULL");
+  if (Ka < 1 || Kp < 1 || (int64_t)Ka * Kp < 2 || (int64_t)Ka * Kp > 4096)
+    return fail(QAMW_EUNSUPPORTED, "polar code needs Ka, Kp >= 1 and 2 <= Ka * Kp <= 4096 (got %d x %d)", (int)Ka,
+                (int)Kp);
+  if (!s || !sigma || !packed || !rownorm_f16) return fail(QAMW_EINVAL, "s, sigma, packed and rownorm_f16 must be non-NULL");
+  if (!aligned16(s) || !aligned16(sigma) || !aligned16(packed))
+    return fail(QAMW_EINVAL, "s, sigma and packed must be 16-byte aligned");
+  if ((rc = check_encode_workspace(workspace, workspace_bytes, N, d))) return rc;
+  if ((rc = qamw_encode_prepare(W, wdtype, N, d, ldw, s, sigma, block, sign_seed, rownorm_f16, workspace,
+                                workspace_bytes, stream)))
+    return rc;
+  const int K = Ka * Kp;
+  const EncodeWorkspace e = encode_workspace(workspace, N, d);
+  return launch_encode_polar(L, W, wdtype, (int)N, (int)d, ldw, e.f, e.isig, levels, (int)Ka, dirs, (int)Kp,
+                             qamw_index_bits(K), (int)qamw_packed_row_words(d, K), e.rho, packed,
+                             (hipStream_t)stream);
+}
+
 int32_t qamw_decode(const uint32_t* packed, const uint16_t* rownorm_f16, int64_t N, int64_t d, const float* s,
                     const float* sigma, int32_t block, uint64_t sign_seed, const float* codebook, int32_t K,
                     void* W_out, int32_t out_dtype, int64_t ldo, void* stream) {

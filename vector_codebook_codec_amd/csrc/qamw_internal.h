@@ -69,6 +69,9 @@ int launch_encode_prepare(const void* W, int32_t wdt, int N, int d, int64_t ldw,
 int launch_encode(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const float* isig,
                   const float* cb, int K, int B, int row_words, const double* rho, const void* plan, uint32_t* packed,
                   hipStream_t st);
+int launch_encode_polar(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f,
+                        const float* isig, const float* levels, int Ka, const float* dirs, int Kp, int B,
+                        int row_words, const double* rho, uint32_t* packed, hipStream_t st);
 int launch_build_plan(const float* cb, int K, void* plan, hipStream_t st);
 int launch_rotate_act(int L, const void* X, int32_t xdt, int T, int d, int64_t ldx, const float* s, uint64_t seed,
                       uint16_t* Xr, int64_t ldr, hipStream_t st);
