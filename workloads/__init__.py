@@ -32,6 +32,7 @@ __all__ = [
     "gaussian_samples",
     "matrix",
     "channel_rms",
+    "activations",
     "get",
     "names",
     "stack_7b",
@@ -109,6 +110,17 @@ def matrix(rows: int, cols: int, *, dist: str, std: float, seed: int,
 def channel_rms(d: int, *, sigma_log: float, seed: int) -> np.ndarray:
     """Per-input-channel activation RMS r_j ~ LogNormal(0, sigma_log), fp32, all > 0."""
     return np.random.default_rng(seed).lognormal(0.0, sigma_log, size=d).astype(np.float32)
+
+
+def activations(T: int, r: np.ndarray, *, seed: int) -> np.ndarray:
+    """Synthetic layer inputs X (T, d) fp32: X[t, j] = r_j * g[t, j], g ~ N(0, 1).
+
+    Channel j's activations have RMS r_j in expectation (the pages calibrate
+    on real activations; these stand in for them with log-normal channel
+    scales, the heavy-channel structure activation-aware scaling targets).
+    """
+    g = np.random.default_rng(seed).standard_normal((T, np.asarray(r).size))
+    return (g * np.asarray(r, dtype=np.float64)[None, :]).astype(np.float32)
 
 
 # --------------------------------------------------------------------------
