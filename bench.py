@@ -24,6 +24,10 @@ decode_matmul the fused decoded-weight matmul Y = X W^^T on the packed matrix
 polar         the polar-code baseline encode (qamw_encode_polar, 8 amplitude
               levels x 32 phases = 8 bits per pair) on the same matrix with
               the step's s and sigma (not part of the step)
+alpha_sweep   channel RMS of synthetic activations X (qamw_channel_rms), then
+              for alpha in 0 .. 1: calibrate, encode, decode and the layer-
+              output error ||X dW^T||^2 (qamw_output_error, bf16 MFMA); the
+              times of the two metric kernels (not part of the step)
 """
 from __future__ import annotations
 
@@ -43,6 +47,7 @@ import workloads  # noqa: E402
 
 PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 KERNEL_SOURCES = [os.path.join(ROOT, "vector_codebook_codec_amd", "csrc", f)
                   for f in ("encode.hip", "qamw_device.h", "qamw_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_plan_kernel_4096x11008_traffic.txt")
@@ -82,6 +87,8 @@ def parse():
     ap.add_argument("--matmul-tokens", type=int, nargs="*", default=[1, 16, 64],
                     help="token counts T of the fused decoded-weight matmul measurement")
     ap.add_argument("--matmul-reps", type=int, default=10)
+    ap.add_argument("--sweep-tokens", type=int, default=1024,
+                    help="synthetic activation rows for the channel-RMS / output-error alpha sweep (0 to skip)")
     ap.add_argument("--polar-reps", type=int, default=10,
                     help="polar-code encodes (8 amplitudes x 32 phases) timed after the steps (0 to skip)")
     ap.add_argument("--copy-reference", type=int, default=0,
@@ -270,6 +277,55 @@ def main():
                  "note": "qamw_encode_polar = encode_prepare_kernel + encode_polar_kernel"}
         print(f"polar encode {Ka}x{Kp}: {p_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
+    # channel RMS from activations and the output error over alpha (not part of the step)
+    sweep = None
+    if args.sweep_tokens > 0:
+        Tt = args.sweep_tokens
+        Xs = torch.from_numpy(workloads.activations(Tt, wl.r, seed=2024)).to(dev).to(torch.bfloat16)
+        ws_rms = torch.empty(max(256, q.qamw_channel_rms_workspace_bytes(Tt, d)), dtype=torch.uint8, device=dev)
+        ws_oe = torch.empty(max(256, q.qamw_output_error_workspace_bytes(Tt, N)), dtype=torch.uint8, device=dev)
+        r_x = torch.empty(d, dtype=torch.float32, device=dev)
+        e_out = torch.empty(1, dtype=torch.float64, device=dev)
+        s_a = torch.empty_like(s)
+        sig_a = torch.empty_like(sigma)
+        packed_a = torch.empty_like(packed)
+        rn_a = torch.empty_like(rn)
+
+        def timed(fn, reps=5):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                a, z = ev(), ev()
+                a.record(stream)
+                fn()
+                z.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(z))
+            return float(np.median(ts))
+
+        rms_ms = timed(lambda: q.qamw_channel_rms(Xs, r_x, ws_rms, stream))
+        errs = {}
+        for alpha in (0.0, 0.25, 0.5, 0.75, 1.0):
+            q.qamw_calibrate(W, r_x, alpha, b, wl.sign_seed, s_a, sig_a, ws_cal, stream)
+            q.qamw_encode(W, s_a, sig_a, b, wl.sign_seed, Ct, packed=packed_a, rownorm_f16=rn_a,
+                          workspace=ws_enc, stream=stream, plan=plan)
+            q.qamw_decode(packed_a, rn_a, d, s_a, sig_a, b, wl.sign_seed, Ct, out=out, stream=stream)
+            q.qamw_output_error(Xs, W, out, e_out, ws_oe, stream)
+            errs[str(alpha)] = float(e_out.cpu()[0])
+        oe_ms = timed(lambda: q.qamw_output_error(Xs, W, out, e_out, ws_oe, stream))
+        oe_flops = 2.0 * Tt * N * d
+        rms_bytes = Tt * d * 2 + d * 4
+        sweep = {"tokens": Tt, "activations": "X[t][j] = r_j g, g ~ N(0, 1), bf16; r = the workload's channel RMS",
+                 "output_error_by_alpha": errs, "best_alpha": min(errs, key=errs.get),
+                 "channel_rms_us": rms_ms * 1e3,
+                 "channel_rms_frac_hbm": rms_bytes / (rms_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                 "output_error_us": oe_ms * 1e3,
+                 "output_error_tflops": oe_flops / (oe_ms * 1e-3) / 1e12,
+                 "output_error_frac_bf16_mfma": oe_flops / (oe_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        print(f"alpha sweep: {errs}; channel_rms {rms_ms * 1e3:.1f} us, output_error {oe_ms * 1e3:.1f} us",
+              file=sys.stderr, flush=True)
+
     for _ in range(args.copy_reference):
         flush2 = torch.empty_like(flush)
         flush2.copy_(flush)
@@ -330,6 +386,7 @@ def main():
                                   "qamw_decode_matmul) vs qamw_decode to bf16 + torch.matmul; per T",
                           "by_tokens": mm},
         "polar": polar,
+        "alpha_sweep": sweep,
     }
     if not args.no_cpu_baseline:
         print("timing the CPU oracle on a 160-row sample", file=sys.stderr, flush=True)

@@ -208,6 +208,42 @@ int32_t qamw_encode_polar(const void* W, int32_t wdtype, int64_t N, int64_t d, i
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Activation statistics and the layer-output error (QAM-W, Methodology:
+ * Activation-Aware Scaling; the trace identity of the composite bound
+ * chain, || X dW^T ||_F^2 = Tr(dW M dW^T) with M = X^T X).
+ *
+ * qamw_channel_rms: r_j = sqrt(sum_t X[t][j]^2 / T), the chan_rms input of
+ *   qamw_calibrate, from T activation rows.
+ *   X        [T][ldx] of xdtype (QAMW_F32 or QAMW_BF16), 16-byte aligned rows
+ *   d        a multiple of 8
+ *   r_out    [d] float32 out, 16-byte aligned
+ *   workspace >= qamw_channel_rms_workspace_bytes(T, d), 256-byte aligned
+ *   Squares are summed in fp32 over tiles of 64 rows and the tiles in fp64,
+ *   in a fixed order: deterministic.
+ *
+ * qamw_output_error: E = sum_{t, n} (sum_j X[t][j] (W[n][j] - W_hat[n][j]))^2,
+ *   the layer-output error of replacing W by W_hat for the activations X
+ *   (equal to Tr(dW X^T X dW^T)).
+ *   X        [T][ldx] as above; W [N][ldw] of wdtype and W_hat [N][ldh] of
+ *            hdtype (QAMW_F32 or QAMW_BF16 each), 16-byte aligned rows
+ *   d        a multiple of 16
+ *   err_out  one double on the device, written by the call
+ *   workspace >= qamw_output_error_workspace_bytes(T, N), 256-byte aligned
+ *   Arithmetic: dW = W - W_hat in fp32, then dW and X rounded to bf16 and
+ *   multiplied on bf16 MFMA with fp32 accumulation; squares summed in fp64 in
+ *   a fixed order (deterministic).  Relative error of E: about 2^-8 in the
+ *   worst case, far less for unstructured rounding errors.
+ */
+size_t qamw_channel_rms_workspace_bytes(int64_t T, int64_t d);
+int32_t qamw_channel_rms(const void* X, int32_t xdtype, int64_t T, int64_t d, int64_t ldx, float* r_out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+size_t qamw_output_error_workspace_bytes(int64_t T, int64_t N);
+int32_t qamw_output_error(const void* X, int32_t xdtype, int64_t T, int64_t d, int64_t ldx,
+                          const void* W, int32_t wdtype, int64_t N, int64_t ldw,
+                          const void* W_hat, int32_t hdtype, int64_t ldh,
+                          double* err_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Decode (QAM-W, Methodology: Decoding).
  *   packed, rownorm_f16, N, d, block, sign_seed, codebook, K  as produced by
  *             qamw_encode; indices >= K (never produced) are clamped to K - 1

@@ -138,6 +138,50 @@ def test_encode_polar_rejects(lib, kw, status):
     assert lib.qamw_last_error()
 
 
+def _rms(lib, **kw):
+    args = dict(X=A, xdt=1, T=100, d=64, ldx=64, r=A, ws=WS, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return lib.qamw_channel_rms(args["X"], args["xdt"], args["T"], args["d"], args["ldx"], args["r"], args["ws"],
+                                args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), -1), (dict(d=12, ldx=16), -1), (dict(X=None), -1), (dict(X=MIS), -1), (dict(ldx=60), -1),
+    (dict(ldx=68), -1), (dict(xdt=2), -2), (dict(r=None), -1), (dict(r=MIS), -1), (dict(ws=None), -4),
+    (dict(ws_bytes=16), -4), (dict(ws=WS + 32), -4),
+])
+def test_channel_rms_rejects(lib, kw, status):
+    assert _rms(lib, **kw) == status
+    assert lib.qamw_last_error()
+
+
+def _oe(lib, **kw):
+    args = dict(X=A, xdt=1, T=100, d=64, ldx=64, W=A, wdt=1, N=50, ldw=64, H=A, hdt=0, ldh=64, out=A,
+                ws=WS, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return lib.qamw_output_error(args["X"], args["xdt"], args["T"], args["d"], args["ldx"], args["W"], args["wdt"],
+                                 args["N"], args["ldw"], args["H"], args["hdt"], args["ldh"], args["out"],
+                                 args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), -1), (dict(d=40, ldx=40, ldw=40, ldh=40), -1), (dict(W=None), -1), (dict(H=MIS), -1),
+    (dict(ldh=32), -1), (dict(hdt=2), -2), (dict(wdt=5), -2), (dict(out=None), -1), (dict(out=A + 4), -1),
+    (dict(ws=None), -4), (dict(ws_bytes=8), -4),
+])
+def test_output_error_rejects(lib, kw, status):
+    assert _oe(lib, **kw) == status
+    assert lib.qamw_last_error()
+
+
+def test_metric_workspace_sizes(lib):
+    # one fp32 partial per (64-row tile, column); one fp64 partial per 128 x 128 block
+    assert lib.qamw_channel_rms_workspace_bytes(2048, 11008) == 32 * 11008 * 4
+    assert lib.qamw_channel_rms_workspace_bytes(65, 8) == 256
+    assert lib.qamw_output_error_workspace_bytes(2048, 4096) == 16 * 32 * 8
+    assert lib.qamw_output_error_workspace_bytes(0, 4) == 0
+
+
 def _calibrate(lib, **kw):
     args = dict(W=A, wdt=0, N=8, d=256, ldw=256, r=A, alpha=0.5, block=128, seed=0, s=A, sigma=A,
                 ws=WS, ws_bytes=1 << 20, stream=None)

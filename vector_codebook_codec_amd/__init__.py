@@ -11,6 +11,8 @@ from .codec import (  # noqa: F401
     qamw_build_plan,
     qamw_calibrate,
     qamw_calibrate_workspace_bytes,
+    qamw_channel_rms,
+    qamw_channel_rms_workspace_bytes,
     qamw_decode,
     qamw_decode_matmul,
     qamw_encode,
@@ -19,6 +21,8 @@ from .codec import (  # noqa: F401
     qamw_encode_prepare,
     qamw_encode_workspace_bytes,
     qamw_index_bits,
+    qamw_output_error,
+    qamw_output_error_workspace_bytes,
     qamw_packed_row_words,
     qamw_plan_bytes,
     qamw_rotate_activations,

@@ -33,6 +33,11 @@ SIGNATURES = {
     "qamw_encode_indices": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _i32, _p, _p, _p, _sz, _p]),
     "qamw_encode_polar": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _i32, _p, _p, _p,
                                  _sz, _p]),
+    "qamw_channel_rms_workspace_bytes": (_sz, [_i64, _i64]),
+    "qamw_channel_rms": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _sz, _p]),
+    "qamw_output_error_workspace_bytes": (_sz, [_i64, _i64]),
+    "qamw_output_error": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _i32, _i64, _i64, _p, _i32, _i64, _p, _p, _sz,
+                                 _p]),
     "qamw_rotate_activations": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _i32, _u64, _p, _i64, _p]),
     "qamw_decode_matmul": (_i32, [_p, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _i32, _p, _i32, _i64, _p]),
     "qamw_decode": (_i32, [_p, _p, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _i32, _i64, _p]),

@@ -274,6 +274,54 @@ def qamw_encode_polar(W: torch.Tensor, s: torch.Tensor, sigma: torch.Tensor, blo
     return packed, rownorm_f16
 
 
+def qamw_channel_rms_workspace_bytes(T: int, d: int) -> int:
+    return int(_lib.load().qamw_channel_rms_workspace_bytes(T, d))
+
+
+def qamw_output_error_workspace_bytes(T: int, N: int) -> int:
+    return int(_lib.load().qamw_output_error_workspace_bytes(T, N))
+
+
+def qamw_channel_rms(X: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """r_j = sqrt(mean_t X[t][j]^2) of T activation rows X [T][d]: the chan_rms input of qamw_calibrate."""
+    T, d, ldx = _rows(X, "X")
+    if X.dtype not in _WDT:
+        raise ValueError("X must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty(d, dtype=torch.float32, device=X.device)
+    _vec(out, "out", d)
+    if workspace is None:
+        workspace = _workspace(qamw_channel_rms_workspace_bytes(T, d), X.device)
+    _lib.check("qamw_channel_rms", _lib.load().qamw_channel_rms(
+        X.data_ptr(), _WDT[X.dtype], T, d, ldx, out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def qamw_output_error(X: torch.Tensor, W: torch.Tensor, W_hat: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """E = || X (W - W_hat)^T ||_F^2 = Tr(dW X^T X dW^T) as a one-element float64 device tensor."""
+    T, d, ldx = _rows(X, "X")
+    N, d2, ldw = _rows(W, "W")
+    N2, d3, ldh = _rows(W_hat, "W_hat")
+    if (d2, d3, N2) != (d, d, N):
+        raise ValueError("X [T][d], W [N][d] and W_hat [N][d] must agree")
+    for t, name in ((X, "X"), (W, "W"), (W_hat, "W_hat")):
+        if t.dtype not in _WDT:
+            raise ValueError(f"{name} must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float64, device=X.device)
+    _vec(out, "out", 1, torch.float64)
+    if workspace is None:
+        workspace = _workspace(qamw_output_error_workspace_bytes(T, N), X.device)
+    _lib.check("qamw_output_error", _lib.load().qamw_output_error(
+        X.data_ptr(), _WDT[X.dtype], T, d, ldx, W.data_ptr(), _WDT[W.dtype], N, ldw, W_hat.data_ptr(),
+        _WDT[W_hat.dtype], ldh, out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def qamw_decode(packed: torch.Tensor, rownorm_f16: torch.Tensor, d: int, s: Optional[torch.Tensor],
                 sigma: torch.Tensor, block: int, sign_seed: int, codebook: torch.Tensor,
                 out_dtype=torch.float32, out: Optional[torch.Tensor] = None, stream=None):

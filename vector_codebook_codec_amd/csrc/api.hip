@@ -263,6 +263,63 @@ int32_t qamw_encode_polar(const void* W, int32_t wdtype, int64_t N, int64_t d, i
                              (hipStream_t)stream);
 }
 
+size_t qamw_channel_rms_workspace_bytes(int64_t T, int64_t d) {
+  if (T <= 0 || T > kMaxDim || d <= 0 || d > kMaxDim) return 0;
+  return round_up((size_t)((T + kRmsRowsPerTile - 1) / kRmsRowsPerTile) * (size_t)d * sizeof(float), 256);
+}
+
+size_t qamw_output_error_workspace_bytes(int64_t T, int64_t N) {
+  if (T <= 0 || T > kMaxDim || N <= 0 || N > kMaxDim) return 0;
+  return round_up((size_t)((T + kOutputErrorTile - 1) / kOutputErrorTile) *
+                      (size_t)((N + kOutputErrorTile - 1) / kOutputErrorTile) * sizeof(double), 256);
+}
+
+static int check_rows16(const void* p, int32_t dt, int64_t d, int64_t ld, const char* name, bool allow_f16) {
+  if (!p) return fail(QAMW_EINVAL, "%s is NULL", name);
+  if (dt != QAMW_F32 && dt != QAMW_BF16 && !(allow_f16 && dt == QAMW_F16))
+    return fail(QAMW_EUNSUPPORTED, "%s dtype %d not supported", name, dt);
+  if (ld < d) return fail(QAMW_EINVAL, "%s: leading dimension %lld < d=%lld", name, (long long)ld, (long long)d);
+  if (!aligned16(p) || (ld * elem_size(dt)) % 16)
+    return fail(QAMW_EINVAL, "%s must be 16-byte aligned with 16-byte aligned rows", name);
+  return QAMW_OK;
+}
+
+int32_t qamw_channel_rms(const void* X, int32_t xdtype, int64_t T, int64_t d, int64_t ldx, float* r_out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (T <= 0 || d <= 0) return fail(QAMW_EINVAL, "T and d must be positive (T=%lld d=%lld)", (long long)T, (long long)d);
+  if (T > kMaxDim || d > kMaxDim) return fail(QAMW_EUNSUPPORTED, "activations too large");
+  if (d % 8) return fail(QAMW_EINVAL, "d=%lld is not a multiple of 8", (long long)d);
+  int rc = check_rows16(X, xdtype, d, ldx, "X", false);
+  if (rc) return rc;
+  if (!r_out || !aligned16(r_out)) return fail(QAMW_EINVAL, "r_out must be non-NULL and 16-byte aligned");
+  const size_t need = qamw_channel_rms_workspace_bytes(T, d);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(QAMW_EWORKSPACE, "channel RMS needs %zu bytes of 256-byte aligned workspace (got %zu)", need,
+                workspace_bytes);
+  return launch_channel_rms(X, xdtype, (int)T, (int)d, ldx, r_out, (float*)workspace, (hipStream_t)stream);
+}
+
+int32_t qamw_output_error(const void* X, int32_t xdtype, int64_t T, int64_t d, int64_t ldx, const void* W,
+                          int32_t wdtype, int64_t N, int64_t ldw, const void* W_hat, int32_t hdtype, int64_t ldh,
+                          double* err_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (T <= 0 || d <= 0 || N <= 0)
+    return fail(QAMW_EINVAL, "T, N and d must be positive (T=%lld N=%lld d=%lld)", (long long)T, (long long)N,
+                (long long)d);
+  if (T > kMaxDim || d > kMaxDim || N > kMaxDim) return fail(QAMW_EUNSUPPORTED, "operands too large");
+  if (d % 16) return fail(QAMW_EINVAL, "d=%lld is not a multiple of 16", (long long)d);
+  int rc;
+  if ((rc = check_rows16(X, xdtype, d, ldx, "X", false))) return rc;
+  if ((rc = check_rows16(W, wdtype, d, ldw, "W", false))) return rc;
+  if ((rc = check_rows16(W_hat, hdtype, d, ldh, "W_hat", false))) return rc;
+  if (!err_out || ((uintptr_t)err_out & 7u)) return fail(QAMW_EINVAL, "err_out must be non-NULL and 8-byte aligned");
+  const size_t need = qamw_output_error_workspace_bytes(T, N);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(QAMW_EWORKSPACE, "output error needs %zu bytes of 256-byte aligned workspace (got %zu)", need,
+                workspace_bytes);
+  return launch_output_error(X, xdtype, (int)T, (int)d, ldx, W, wdtype, (int)N, ldw, W_hat, hdtype, ldh, err_out,
+                             (double*)workspace, (hipStream_t)stream);
+}
+
 int32_t qamw_decode(const uint32_t* packed, const uint16_t* rownorm_f16, int64_t N, int64_t d, const float* s,
                     const float* sigma, int32_t block, uint64_t sign_seed, const float* codebook, int32_t K,
                     void* W_out, int32_t out_dtype, int64_t ldo, void* stream) {

@@ -99,6 +99,10 @@ template <> struct RawChunk<uint16_t> {
   }
 };
 
+// MFMA operand and accumulator vectors (v_mfma_f32_16x16x32_bf16)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
