@@ -3,10 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 One step = the whole codec path over one matrix already resident in HBM:
-qamw_calibrate (s, sigma) -> qamw_build_plan (search plan for the codebook)
--> qamw_encode_prepare (row norms, column and pair factors) ->
-qamw_encode_indices (rotation, nearest centroid, packing) -> qamw_decode
-(fp32 output).  The default workload is the 4096 x 11008 bf16
+qamw_build_plan (search plan for the codebook) -> qamw_calibrate_encode (s,
+sigma, row norms, rotation, nearest centroid, packing) -> qamw_decode (fp32
+output).  The same work is then timed as separate entry points (qamw_calibrate,
+qamw_encode_prepare, qamw_encode_indices) for per-kernel figures.  The default workload is the 4096 x 11008 bf16
 down-projection-shaped matrix (Student-t(5) entries, std 0.02; K = 2048,
 Hadamard block 256).  Prints one JSON line.
 
@@ -147,28 +147,26 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
+    ws_ce = torch.empty(q.qamw_calibrate_encode_workspace_bytes(N, d), dtype=torch.uint8, device=dev)
+
     def step(marks=None):
         def mark(i):
             if marks is not None:
                 marks[i].record(stream)
         mark(0)
-        q.qamw_calibrate(W, r, wl.alpha, b, wl.sign_seed, s, sigma, ws_cal, stream)
-        mark(1)
         q.qamw_build_plan(Ct, plan, stream)
+        mark(1)
+        q.qamw_calibrate_encode(W, r, wl.alpha, b, wl.sign_seed, Ct, plan, s, sigma, packed, rn, ws_ce, stream)
         mark(2)
-        q.qamw_encode_prepare(W, s, sigma, b, wl.sign_seed, rn, ws_enc, stream)
-        mark(3)
-        q.qamw_encode_indices(W, b, Ct, ws_enc, plan, packed, stream)
-        mark(4)
         q.qamw_decode(packed, rn, d, s, sigma, b, wl.sign_seed, Ct, out=out, stream=stream)
-        mark(5)
+        mark(3)
 
     for i in range(args.warmup):
         step()
         print(f"warmup step {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
 
-    marks = [[ev() for _ in range(6)] for _ in range(args.steps)]
+    marks = [[ev() for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(marks[i])
@@ -176,10 +174,31 @@ def main():
     wall = time.perf_counter() - t0
     print(f"timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
-    seg = lambda i: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in marks]))
-    cal_ms, plan_ms, prep_ms, idx_ms, dec_ms = (seg(i) for i in range(5))
-    enc_ms = prep_ms + idx_ms
+    seg = lambda mk, i: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in mk]))
+    plan_ms, ce_ms, dec_ms = (seg(marks, i) for i in range(3))
     step_ms = wall * 1e3 / args.steps
+
+    # the same work as separate entry points, for per-kernel times: the roofline's
+    # kernel (encode_plan_kernel, all of qamw_encode_indices) is timed here on its own
+    packed_c = torch.empty_like(packed)
+    rn_c = torch.empty_like(rn)
+    s_c = torch.empty_like(s)
+    sigma_c = torch.empty_like(sigma)
+    cmarks = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        m = cmarks[i]
+        m[0].record(stream)
+        q.qamw_calibrate(W, r, wl.alpha, b, wl.sign_seed, s_c, sigma_c, ws_cal, stream)
+        m[1].record(stream)
+        q.qamw_encode_prepare(W, s_c, sigma_c, b, wl.sign_seed, rn_c, ws_enc, stream)
+        m[2].record(stream)
+        q.qamw_encode_indices(W, b, Ct, ws_enc, plan, packed_c, stream)
+        m[3].record(stream)
+    torch.cuda.synchronize()
+    cal_ms, prep_ms, idx_ms = (seg(cmarks, i) for i in range(3))
+    if not (torch.equal(packed_c, packed) and torch.equal(rn_c, rn) and torch.equal(s_c, s)
+            and torch.equal(sigma_c, sigma)):
+        raise RuntimeError("qamw_calibrate_encode and the separate entry points disagree")
 
     # the exhaustive search (no plan) for comparison; same indices, bit for bit
     packed_x = torch.empty_like(packed)
@@ -367,15 +386,17 @@ def main():
             "encode_indices_tflops": exh_flops / (idx_ms * 1e-3) / 1e12,
             "encode_indices_frac_of_fp32_peak": exh_flops / (idx_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
             "calibrate_plan_encode_frac_of_fp32_peak":
-                exh_flops / ((cal_ms + plan_ms + enc_ms) * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+                exh_flops / ((plan_ms + ce_ms) * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
             "exhaustive_encode_indices_ms": exh_ms,
             "exhaustive_frac_of_fp32_peak": None if exh_ms is None else
                 exh_flops / (exh_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
             "note": "pairs x K x 4 flops (the exhaustive nearest-centroid search) per unit time; the plan "
                     "reaches the same indices with a few candidates per pair"},
-        "per_entry_ms": {"calibrate": cal_ms, "build_plan": plan_ms, "encode_prepare": prep_ms,
-                         "encode_indices": idx_ms, "decode": dec_ms},
-        "encode_gweights_s": weights / ((cal_ms + plan_ms + enc_ms) * 1e-3) / 1e9,
+        "per_entry_ms": {"build_plan": plan_ms, "calibrate_encode": ce_ms, "decode": dec_ms},
+        "separate_entry_ms": {"calibrate": cal_ms, "encode_prepare": prep_ms, "encode_indices": idx_ms,
+                              "note": "the step's calibrate_encode as separate calls (same results, bit for "
+                                      "bit); encode_prepare repeats the row-norm pass"},
+        "encode_gweights_s": weights / ((plan_ms + ce_ms) * 1e-3) / 1e9,
         "decode_gweights_s": weights / (dec_ms * 1e-3) / 1e9,
         "decode_cold": None if dec_cold_ms is None else {
             "ms": dec_cold_ms, "algorithmic_bytes": dec_bytes,

@@ -187,6 +187,24 @@ int32_t qamw_encode_indices(const void* W, int32_t wdtype, int64_t N, int64_t d,
                             const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Calibration and encode in one call (QAM-W, Methodology: Activation-Aware
+ * Scaling; Separation of Scale and Direction; Deterministic Rotation; Pairing
+ * and Calibration; Joint 2D Quantization): exactly qamw_calibrate followed by
+ * qamw_encode -- s_out, sigma_out, packed and rownorm_f16 are bit-identical
+ * to theirs -- but the row norms, column factors and 1 / sigma of the
+ * calibration pass are kept for the encode, which saves the encode's own pass
+ * over W for the row norms.
+ *   arguments  as for qamw_calibrate and qamw_encode
+ *   workspace  >= qamw_calibrate_encode_workspace_bytes(N, d), 256-byte aligned
+ */
+size_t qamw_calibrate_encode_workspace_bytes(int64_t N, int64_t d);
+int32_t qamw_calibrate_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
+                              const float* chan_rms, float alpha, int32_t block, uint64_t sign_seed,
+                              const float* codebook, int32_t K, const void* plan,
+                              float* s_out, float* sigma_out, uint32_t* packed, uint16_t* rownorm_f16,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Polar-code baseline (QAM-W, Methodology: Joint 2D Quantization, and the
  * Experiments' joint-versus-polar ablation): the same transform as
  * qamw_encode, but amplitude and phase of each normalised pair z~ = (x, y)

@@ -182,6 +182,33 @@ def test_metric_workspace_sizes(lib):
     assert lib.qamw_output_error_workspace_bytes(0, 4) == 0
 
 
+def _cal_enc(lib, **kw):
+    args = dict(W=A, wdt=1, N=8, d=256, ldw=256, r=A, alpha=0.5, block=128, seed=0, cb=A, K=256, plan=None,
+                s=A, sigma=A, packed=A, rn=A, ws=WS, ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return lib.qamw_calibrate_encode(args["W"], args["wdt"], args["N"], args["d"], args["ldw"], args["r"],
+                                     args["alpha"], args["block"], args["seed"], args["cb"], args["K"], args["plan"],
+                                     args["s"], args["sigma"], args["packed"], args["rn"], args["ws"],
+                                     args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block=8), -2), (dict(K=1), -2), (dict(r=None), -1), (dict(s=MIS), -1), (dict(packed=None), -1),
+    (dict(rn=None), -1), (dict(alpha=float("nan")), -1), (dict(plan=WS + 64), -1), (dict(ws=None), -4),
+    (dict(ws_bytes=1000), -4), (dict(ldw=100), -1), (dict(wdt=2), -2),
+])
+def test_calibrate_encode_rejects(lib, kw, status):
+    assert _cal_enc(lib, **kw) == status
+    assert lib.qamw_last_error()
+
+
+def test_calibrate_encode_workspace(lib):
+    # the encode workspace followed by the calibration's partial sums
+    assert lib.qamw_calibrate_encode_workspace_bytes(4096, 11008) == \
+        lib.qamw_encode_workspace_bytes(4096, 11008) + 256 * 5504 * 4
+    assert lib.qamw_calibrate_encode_workspace_bytes(0, 16) == 0
+
+
 def _calibrate(lib, **kw):
     args = dict(W=A, wdt=0, N=8, d=256, ldw=256, r=A, alpha=0.5, block=128, seed=0, s=A, sigma=A,
                 ws=WS, ws_bytes=1 << 20, stream=None)

@@ -495,3 +495,21 @@ def test_encode_phases_match_encode(q):
             torch.cuda.synchronize()
             assert torch.equal(got, packed)
         assert torch.equal(rn, rn_ref)
+
+
+# ---------------------------------------------------------------- calibrate + encode in one call
+@pytest.mark.parametrize("name", ["c1_256x512", "c3t_4096x11008"])
+def test_calibrate_encode_matches_separate_calls(q, name):
+    wl = workloads.get(name)
+    say(f"case calibrate_encode {name}")
+    W = to_dev(wl.W, wl.wdtype)
+    r = torch.from_numpy(wl.r).to(DEV)
+    Ct = torch.from_numpy(q.load_codebook(wl.K)).to(DEV)
+    plan = q.qamw_build_plan(Ct)
+    s, sigma = q.qamw_calibrate(W, r, wl.alpha, wl.block, wl.sign_seed)
+    packed, rn = q.qamw_encode(W, s, sigma, wl.block, wl.sign_seed, Ct, plan=plan)
+    for p in (plan, None):
+        s2, sig2, packed2, rn2 = q.qamw_calibrate_encode(W, r, wl.alpha, wl.block, wl.sign_seed, Ct, plan=p)
+        torch.cuda.synchronize()
+        assert torch.equal(s2, s) and torch.equal(sig2, sigma)
+        assert torch.equal(packed2, packed) and torch.equal(rn2, rn)

@@ -10,6 +10,8 @@ from .codec import (  # noqa: F401
     load_polar,
     qamw_build_plan,
     qamw_calibrate,
+    qamw_calibrate_encode,
+    qamw_calibrate_encode_workspace_bytes,
     qamw_calibrate_workspace_bytes,
     qamw_channel_rms,
     qamw_channel_rms_workspace_bytes,

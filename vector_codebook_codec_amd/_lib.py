@@ -31,6 +31,9 @@ SIGNATURES = {
     "qamw_encode": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "qamw_encode_prepare": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _p, _sz, _p]),
     "qamw_encode_indices": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _i32, _p, _p, _p, _sz, _p]),
+    "qamw_calibrate_encode_workspace_bytes": (_sz, [_i64, _i64]),
+    "qamw_calibrate_encode": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _f32, _i32, _u64, _p, _i32, _p, _p, _p, _p, _p,
+                                     _p, _sz, _p]),
     "qamw_encode_polar": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _i32, _p, _p, _p,
                                  _sz, _p]),
     "qamw_channel_rms_workspace_bytes": (_sz, [_i64, _i64]),

@@ -190,6 +190,53 @@ def qamw_encode(W: torch.Tensor, s: torch.Tensor, sigma: torch.Tensor, block: in
     return packed, rownorm_f16
 
 
+def qamw_calibrate_encode_workspace_bytes(N: int, d: int) -> int:
+    return int(_lib.load().qamw_calibrate_encode_workspace_bytes(N, d))
+
+
+def qamw_calibrate_encode(W: torch.Tensor, chan_rms: torch.Tensor, alpha: float, block: int, sign_seed: int,
+                          codebook: torch.Tensor, plan: Optional[torch.Tensor] = None,
+                          s_out: Optional[torch.Tensor] = None, sigma_out: Optional[torch.Tensor] = None,
+                          packed: Optional[torch.Tensor] = None, rownorm_f16: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """qamw_calibrate + qamw_encode in one call sharing the row norms:
+    returns (s, sigma, packed, rownorm_f16), bit-identical to the two calls."""
+    N, d, ldw = _rows(W, "W")
+    if W.dtype not in _WDT:
+        raise ValueError("W must be float32 or bfloat16")
+    _vec(chan_rms, "chan_rms", d)
+    K = _codebook(codebook)
+    rw = qamw_packed_row_words(d, K)
+    if rw < 0:
+        raise ValueError(f"unsupported K={K} or d={d}")
+    if plan is not None:
+        _dev(plan, "plan")
+        if plan.dtype != torch.uint8 or plan.numel() < qamw_plan_bytes(K):
+            raise ValueError("plan must be a uint8 tensor from qamw_build_plan for this K")
+    if s_out is None:
+        s_out = torch.empty(d, dtype=torch.float32, device=W.device)
+    if sigma_out is None:
+        sigma_out = torch.empty(d // 2, dtype=torch.float32, device=W.device)
+    if packed is None:
+        packed = torch.empty((N, rw), dtype=torch.int32, device=W.device)
+    if rownorm_f16 is None:
+        rownorm_f16 = torch.empty(N, dtype=torch.int16, device=W.device)
+    _vec(s_out, "s_out", d)
+    _vec(sigma_out, "sigma_out", d // 2)
+    _dev(packed, "packed")
+    if packed.dtype != torch.int32 or tuple(packed.shape) != (N, rw) or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous int32 tensor of shape ({N}, {rw})")
+    _vec(rownorm_f16, "rownorm_f16", N, torch.int16)
+    if workspace is None:
+        workspace = _workspace(qamw_calibrate_encode_workspace_bytes(N, d), W.device)
+    _lib.check("qamw_calibrate_encode", _lib.load().qamw_calibrate_encode(
+        W.data_ptr(), _WDT[W.dtype], N, d, ldw, chan_rms.data_ptr(), float(alpha), int(block), int(sign_seed),
+        codebook.data_ptr(), K, None if plan is None else plan.data_ptr(), s_out.data_ptr(), sigma_out.data_ptr(),
+        packed.data_ptr(), rownorm_f16.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return s_out, sigma_out, packed, rownorm_f16
+
+
 def qamw_encode_prepare(W: torch.Tensor, s: torch.Tensor, sigma: torch.Tensor, block: int, sign_seed: int,
                         rownorm_f16: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                         stream=None):

@@ -140,7 +140,7 @@ int32_t qamw_calibrate(const void* W, int32_t wdtype, int64_t N, int64_t d, int6
   if ((rc = launch_scale(chan_rms, alpha, sign_seed, dd, s_out, fcol, st))) return rc;
   if ((rc = launch_rownorm(W, wdtype, n, dd, ldw, s_out, rho, nullptr, st))) return rc;
   if ((rc = launch_amplitude(L, W, wdtype, n, dd, ldw, fcol, rho, partial, st))) return rc;
-  return launch_sigma(partial, (int)calib_tiles(N), dd / 2, n, sigma_out, st);
+  return launch_sigma(partial, (int)calib_tiles(N), dd / 2, n, sigma_out, nullptr, st);
 }
 
 size_t qamw_plan_bytes(int32_t K) {
@@ -235,6 +235,47 @@ int32_t qamw_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t
     return rc;
   return qamw_encode_indices(W, wdtype, N, d, ldw, block, codebook, K, plan, packed, workspace, workspace_bytes,
                              stream);
+}
+
+size_t qamw_calibrate_encode_workspace_bytes(int64_t N, int64_t d) {
+  const size_t e = qamw_encode_workspace_bytes(N, d);
+  if (!e) return 0;
+  return e + calib_tiles(N) * (size_t)(d / 2) * sizeof(float);
+}
+
+int32_t qamw_calibrate_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
+                              const float* chan_rms, float alpha, int32_t block, uint64_t sign_seed,
+                              const float* codebook, int32_t K, const void* plan, float* s_out, float* sigma_out,
+                              uint32_t* packed, uint16_t* rownorm_f16, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  int L = 0;
+  int rc = check_matrix(N, d, block, &L);
+  if (rc) return rc;
+  if ((rc = check_weights(W, wdtype, d, ldw))) return rc;
+  if ((rc = check_codebook(codebook, K))) return rc;
+  if (!chan_rms || !s_out || !sigma_out || !packed || !rownorm_f16)
+    return fail(QAMW_EINVAL, "chan_rms, s_out, sigma_out, packed and rownorm_f16 must be non-NULL");
+  if (!aligned16(s_out) || !aligned16(sigma_out) || !aligned16(packed))
+    return fail(QAMW_EINVAL, "s_out, sigma_out and packed must be 16-byte aligned");
+  if (!isfinite(alpha)) return fail(QAMW_EINVAL, "alpha must be finite");
+  if (plan && ((uintptr_t)plan & 255u)) return fail(QAMW_EINVAL, "plan must be 256-byte aligned");
+  const size_t need = qamw_calibrate_encode_workspace_bytes(N, d);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(QAMW_EWORKSPACE, "calibrate_encode needs %zu bytes of 256-byte aligned workspace (got %zu)", need,
+                workspace_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  const EncodeWorkspace e = encode_workspace(workspace, N, d);
+  float* partial = (float*)((char*)workspace + qamw_encode_workspace_bytes(N, d));
+  const int n = (int)N, dd = (int)d;
+  // the calibration pass leaves exactly what qamw_encode_prepare would compute:
+  // column factors (scale_kernel), row norms with their fp16 bits (rownorm_kernel)
+  // and 1 / sigma (sigma_kernel)
+  if ((rc = launch_scale(chan_rms, alpha, sign_seed, dd, s_out, e.f, st))) return rc;
+  if ((rc = launch_rownorm(W, wdtype, n, dd, ldw, s_out, e.rho, rownorm_f16, st))) return rc;
+  if ((rc = launch_amplitude(L, W, wdtype, n, dd, ldw, e.f, e.rho, partial, st))) return rc;
+  if ((rc = launch_sigma(partial, (int)calib_tiles(N), dd / 2, n, sigma_out, e.isig, st))) return rc;
+  return launch_encode(L, W, wdtype, n, dd, ldw, e.f, e.isig, codebook, (int)K, qamw_index_bits(K),
+                       (int)qamw_packed_row_words(d, K), e.rho, plan, packed, st);
 }
 
 int32_t qamw_encode_polar(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, const float* s,

@@ -111,8 +111,11 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
 // workgroup owns 16 columns; thread (column, slice) sums tiles slice,
 // slice + 16, ... and the 16 slice sums are then added in slice order.
 constexpr int kSigmaSlices = 16;
+// With isig non-NULL it also writes 1 / sigma_k (fp64 division of the stored
+// fp32 sigma, rounded once; 0 where sigma_k <= 0), the encode's pair factor.
 __global__ __launch_bounds__(kBlockThreads) void sigma_kernel(const float* __restrict__ partial, int ntiles,
-                                                              int half_d, int N, float* __restrict__ sigma) {
+                                                              int half_d, int N, float* __restrict__ sigma,
+                                                              float* __restrict__ isig) {
   __shared__ double part[kSigmaSlices][kBlockThreads / kSigmaSlices];
   const int col_in = threadIdx.x % (kBlockThreads / kSigmaSlices);
   const int slice = threadIdx.x / (kBlockThreads / kSigmaSlices);
@@ -126,7 +129,9 @@ __global__ __launch_bounds__(kBlockThreads) void sigma_kernel(const float* __res
     double tot = 0.0;
 #pragma unroll
     for (int q = 0; q < kSigmaSlices; ++q) tot += part[q][col_in];
-    sigma[k] = (float)(tot / ((double)N * 1.2533141373155002512078826));  // sqrt(pi/2)
+    const float sg = (float)(tot / ((double)N * 1.2533141373155002512078826));  // sqrt(pi/2)
+    sigma[k] = sg;
+    if (isig) isig[k] = sg > 0.0f ? (float)(1.0 / (double)sg) : 0.0f;
   }
 }
 
@@ -170,10 +175,10 @@ int launch_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ld
   return dispatch_L<LaunchAmplitude>(L, W, wdt, N, d, ldw, f, rho, partial, st);
 }
 
-int launch_sigma(const float* partial, int ntiles, int half_d, int N, float* sigma, hipStream_t st) {
+int launch_sigma(const float* partial, int ntiles, int half_d, int N, float* sigma, float* isig, hipStream_t st) {
   const int cols = kBlockThreads / kSigmaSlices;
   hipLaunchKernelGGL(sigma_kernel, dim3((half_d + cols - 1) / cols), dim3(kBlockThreads), 0, st, partial, ntiles,
-                     half_d, N, sigma);
+                     half_d, N, sigma, isig);
   return check_launch("sigma_kernel");
 }
 
