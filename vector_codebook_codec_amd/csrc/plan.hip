@@ -91,6 +91,38 @@ struct Box {
   }
 };
 
+// The same tests in fp32 on a box widened outward to the next floats: its
+// distances bound the fp64 box's from the safe side (dmax2 larger, dmin2
+// smaller) up to fp32 rounding (< 3 2^-24 relative), which the callers'
+// 1e-6 margins cover.
+struct BoxF {
+  float x0, x1, y0, y1;
+  __device__ float dmax2(float cx, float cy) const {
+    const float ax = fmaxf(fabsf(cx - x0), fabsf(cx - x1));
+    const float ay = fmaxf(fabsf(cy - y0), fabsf(cy - y1));
+    return ax * ax + ay * ay;
+  }
+  __device__ float dmin2(float cx, float cy) const {
+    const float dx = fmaxf(fmaxf(x0 - cx, cx - x1), 0.0f);
+    const float dy = fmaxf(fmaxf(y0 - cy, cy - y1), 0.0f);
+    return dx * dx + dy * dy;
+  }
+};
+
+// the next float above a finite f, and the largest float <= / smallest >= v
+__device__ __forceinline__ float float_next_up(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return f > 0.0f ? __uint_as_float(u + 1u) : (f < 0.0f ? __uint_as_float(u - 1u) : __uint_as_float(1u));
+}
+__device__ __forceinline__ float f32_down(double v) {
+  const float f = (float)v;
+  return (double)f > v ? -float_next_up(-f) : f;
+}
+__device__ __forceinline__ float f32_up(double v) {
+  const float f = (float)v;
+  return (double)f < v ? float_next_up(f) : f;
+}
+
 __device__ __forceinline__ Box cell_box(double R, int G, int ix0, int iy0, int ncells) {
   const double s = 2.0 * R / G;
   return Box{-R + ix0 * s - kPlanEta, -R + (ix0 + ncells) * s + kPlanEta,
@@ -130,40 +162,67 @@ __device__ void build_supercell(PlanShared& sh, const float* __restrict__ cb, in
   const int nsuper = G / S;
   const int sx = sidx / nsuper, sy = sidx % nsuper;
 
-  // ---- U(SQ) and the largest centroid radius Cmax in one pass over the codebook
-  const Box sq = cell_box(R, G, sx * S, sy * S, S);
-  double U = INFINITY, cmax = 0.0;
-  for (int c = tid; c < K; c += kPlanThreads) {
-    const double cx = cb[2 * c], cy = cb[2 * c + 1];
-    U = fmin(U, sq.dmax2(cx, cy));
-    cmax = fmax(cmax, sqrt(cx * cx + cy * cy));
-  }
-  U = wave_min(U);
-  cmax = wave_max(cmax);
-  if (lane == 0) { sh.red[wave] = U; sh.red2[wave] = cmax; }
-  __syncthreads();
-  U = sh.red[0];
-  cmax = sh.red2[0];
+  // ---- the codebook into registers once: thread t holds centroids
+  // r kSuperMax + t P + u (round r < 2 since K <= 4096, u < P = kPerThread),
+  // loaded as float4 pairs; past K a far-away dummy that never passes a test
+  constexpr int kRounds = 4096 / kSuperMax;
+  float2 v[kRounds][kPerThread];
 #pragma unroll
-  for (int w = 1; w < kPlanWaves; ++w) { U = fmin(U, sh.red[w]); cmax = fmax(cmax, sh.red2[w]); }
-  const double reach = cmax + R * 1.4142135623730951;
+  for (int r = 0; r < kRounds; ++r) {
+    const int c0 = r * kSuperMax + tid * kPerThread;
+    const float4* p4 = reinterpret_cast<const float4*>(cb + 2 * c0);
+#pragma unroll
+    for (int u = 0; u < kPerThread; u += 2) {
+      float4 t = make_float4(1e30f, 1e30f, 1e30f, 1e30f);
+      if (c0 + u + 1 < K) t = p4[u / 2];
+      else if (c0 + u < K) t = make_float4(cb[2 * (c0 + u)], cb[2 * (c0 + u) + 1], 1e30f, 1e30f);
+      v[r][u] = make_float2(t.x, t.y);
+      v[r][u + 1] = make_float2(t.z, t.w);
+    }
+  }
+  // ---- U(SQ) and the largest squared centroid radius, from the registers,
+  // in fp32 on the outward-widened supercell box: U is raised by 1e-6 and the
+  // survivor limit U + 2 delta by 1e-6 again, so the survivors can only be
+  // more.  They stay a superset of every cell's candidates: the widened cell
+  // boxes lie inside the widened supercell box, and the supercell limit's
+  // second delta exceeds the cells' relative fp32 slop (~3e-6 U) at every
+  // grid point.  delta (fp64) only needs to cover the scores' slack, which
+  // it does ten times over.
+  const Box sq64 = cell_box(R, G, sx * S, sy * S, S);
+  const BoxF sq{f32_down(sq64.x0), f32_up(sq64.x1), f32_down(sq64.y0), f32_up(sq64.y1)};
+  float U = INFINITY, cmax2 = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u)
+      if (r * kSuperMax + tid * kPerThread + u < K) {
+        const float cx = v[r][u].x, cy = v[r][u].y;
+        U = fminf(U, sq.dmax2(cx, cy));
+        cmax2 = fmaxf(cmax2, cx * cx + cy * cy);
+      }
+  U = (float)wave_min((double)U);
+  cmax2 = (float)wave_max((double)cmax2);
+  if (lane == 0) { sh.red[wave] = U; sh.red2[wave] = cmax2; }
+  __syncthreads();
+  U = (float)sh.red[0];
+  cmax2 = (float)sh.red2[0];
+#pragma unroll
+  for (int w = 1; w < kPlanWaves; ++w) { U = fminf(U, (float)sh.red[w]); cmax2 = fmaxf(cmax2, (float)sh.red2[w]); }
+  const double reach = sqrt((double)cmax2 * 1.000001) + R * 1.4142135623730951;
   const double delta = 1e-5 * reach * reach;
-  const double slim = U + 2.0 * delta;
+  const float slim = (U * 1.000001f + f32_up(2.0 * delta)) * 1.000001f;
 
-  // ---- supercell survivors: thread t tests centroids [t P, t P + P), P = kPerThread
-  // (K <= 4096 = 2 kSuperMax, so two rounds at most), then one block-wide scan
+  // ---- supercell survivors in ascending order: per round, each thread's
+  // passing centroids, placed by a block-wide exclusive scan of the counts
   int nsurv = 0;
-  for (int r0 = 0; r0 < K; r0 += kSuperMax) {
-    const int c0 = r0 + tid * kPerThread;
-    float2 v[kPerThread];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    if (r * kSuperMax >= K) break;                 // uniform
+    const int c0 = r * kSuperMax + tid * kPerThread;
     uint32_t mask = 0;
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      const int c = c0 + u;
-      v[u] = c < K ? make_float2(cb[2 * c], cb[2 * c + 1]) : make_float2(0.0f, 0.0f);
-      if (c < K && sq.dmin2(v[u].x, v[u].y) <= slim) mask |= 1u << u;
-    }
-    // exclusive prefix of the per-thread counts: wave scan, then across waves
+    for (int u = 0; u < kPerThread; ++u)
+      if (c0 + u < K && sq.dmin2(v[r][u].x, v[r][u].y) <= slim) mask |= 1u << u;
     const int mine = __popc(mask);
     int incl = mine;
 #pragma unroll
@@ -183,7 +242,7 @@ __device__ void build_supercell(PlanShared& sh, const float* __restrict__ cb, in
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u)
       if ((mask >> u) & 1u) {
-        if (before < kSuperMax) { sh.surv[before] = (uint16_t)(c0 + u); sh.survc[before] = v[u]; }
+        if (before < kSuperMax) { sh.surv[before] = (uint16_t)(c0 + u); sh.survc[before] = v[r][u]; }
         ++before;
       }
     nsurv = total;
@@ -202,25 +261,30 @@ __device__ void build_supercell(PlanShared& sh, const float* __restrict__ cb, in
     }
   __syncthreads();
 
-  // ---- LPC lanes per cell: survivors j = sub, sub + LPC, ...
+  // ---- LPC lanes per cell: survivors j = sub, sub + LPC, ...  The cell
+  // tests run in fp32 with margins that can only lengthen a list (a list with
+  // extra centroids still yields the exhaustive search's index, since it
+  // keeps every centroid tied with the winner): U(Q) from the widened box,
+  // raised by 1e-6, and the limit (U(Q) + delta) raised by 1e-6 again.
   const int qc = tid / LPC, sub = tid % LPC;
   const int ix = sx * S + qc / S, iy = sy * S + qc % S;
-  const Box cq = cell_box(R, G, ix, iy, 1);
-  double Uc = INFINITY;
+  const Box cq64 = cell_box(R, G, ix, iy, 1);
+  const BoxF cq{f32_down(cq64.x0), f32_up(cq64.x1), f32_down(cq64.y0), f32_up(cq64.y1)};
+  float Uc = INFINITY;
   if (all) {
-    for (int j = sub; j < ns; j += LPC) Uc = fmin(Uc, cq.dmax2(cb[2 * j], cb[2 * j + 1]));
+    for (int j = sub; j < ns; j += LPC) Uc = fminf(Uc, cq.dmax2(cb[2 * j], cb[2 * j + 1]));
   } else {
     for (int j0 = 0; j0 < ns; j0 += kRound) {
-      float2 v[4];
+      float2 v4[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = sh.survc[j0 + u * LPC + sub];
+      for (int u = 0; u < 4; ++u) v4[u] = sh.survc[j0 + u * LPC + sub];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) Uc = fmin(Uc, cq.dmax2(v[u].x, v[u].y));
+      for (int u = 0; u < 4; ++u) Uc = fminf(Uc, cq.dmax2(v4[u].x, v4[u].y));
     }
   }
 #pragma unroll
-  for (int off = LPC / 2; off > 0; off >>= 1) Uc = fmin(Uc, __shfl_xor(Uc, off));   // within the group
-  const double lim = Uc + delta;
+  for (int off = LPC / 2; off > 0; off >>= 1) Uc = fminf(Uc, __shfl_xor(Uc, off));   // within the group
+  const float lim = (Uc * 1.000001f + f32_up(delta)) * 1.000001f;
   uint16_t* mine = sh.cell_list[qc];
   const int gshift = lane & ~(LPC - 1);
   const uint64_t gmask = (LPC == 64) ? ~0ull : ((1ull << LPC) - 1ull);
@@ -239,15 +303,15 @@ __device__ void build_supercell(PlanShared& sh, const float* __restrict__ cb, in
     }
   } else {
     for (int j0 = 0; j0 < ns; j0 += kRound) {
-      float2 v[4];
+      float2 v4[4];
       int c[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        v[u] = sh.survc[j0 + u * LPC + sub];
+        v4[u] = sh.survc[j0 + u * LPC + sub];
         c[u] = sh.surv[j0 + u * LPC + sub];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) take(cq.dmin2(v[u].x, v[u].y) <= lim, c[u]);
+      for (int u = 0; u < 4; ++u) take(cq.dmin2(v4[u].x, v4[u].y) <= lim, c[u]);
     }
   }
   __syncthreads();
