@@ -69,3 +69,37 @@ def train(X: np.ndarray, K: int, iters: int = 50):
     _, dmin = assign(X, C)
     history.append(float(dmin.mean()))
     return C, history
+
+
+def refine_on_pairs(Zt: np.ndarray, C0: np.ndarray, iters: int):
+    """Lloyd rounds on a matrix's own normalised pairs, from a given codebook.
+
+    The pages train the codebook once on the unit circular Gaussian and
+    suggest that a codebook learned from a checkpoint's own pair
+    distribution could do better (QAM-W, Significance and Claims, on the
+    synthetic codebook).  Reading: start from the stored Gaussian codebook
+    and run Lloyd rounds on the pairs z~ the encoder quantises.  Each round
+    assigns every pair with the codec's own nearest-centroid rule -- decided
+    in fp32, lowest index on ties (``qamw_ref.nearest_centroid``) -- then
+    moves each centroid to the fp64 mean of its pairs, rounded to fp32; an
+    empty cell keeps its centroid.
+
+    Zt: (M, 2) fp64 pairs; C0: (K, 2) fp32.  Returns (C fp32 (K, 2) after
+    ``iters`` rounds, history) with history[t] the fp64 mean squared
+    distance of round t's assignment to round t's codebook.
+    """
+    from oracle import qamw_ref as O
+
+    Z = np.asarray(Zt, dtype=np.float64).reshape(-1, 2)
+    C = np.asarray(C0, dtype=np.float32).reshape(-1, 2).copy()
+    K = C.shape[0]
+    history = []
+    for _ in range(iters):
+        idx = np.empty(Z.shape[0], dtype=np.int64)
+        for a in range(0, Z.shape[0], 4096):
+            idx[a:a + 4096] = O.nearest_centroid(Z[a:a + 4096], C)[0]
+        C64 = C.astype(np.float64)
+        history.append(float(np.mean(np.sum((Z - C64[idx]) ** 2, axis=1))))
+        mean, cnt = cell_means(Z, idx, K)
+        C = np.where(cnt[:, None] > 0, mean, C64).astype(np.float32)
+    return C, history
