@@ -24,6 +24,10 @@ decode_matmul the fused decoded-weight matmul Y = X W^^T on the packed matrix
 polar         the polar-code baseline encode (qamw_encode_polar, 8 amplitude
               levels x 32 phases = 8 bits per pair) on the same matrix with
               the step's s and sigma (not part of the step)
+learned_codebook  Lloyd rounds of the codebook on the matrix's own normalised
+              pairs (qamw_learn_codebook: plan, encode, update per round) from
+              the Gaussian codebook: distortion per round, time per round,
+              reconstruction error before and after (not part of the step)
 alpha_sweep   channel RMS of synthetic activations X (qamw_channel_rms), then
               for alpha in 0 .. 1: calibrate, encode, decode and the layer-
               output error ||X dW^T||^2 (qamw_output_error, bf16 MFMA); the
@@ -89,6 +93,8 @@ def parse():
     ap.add_argument("--matmul-reps", type=int, default=10)
     ap.add_argument("--sweep-tokens", type=int, default=1024,
                     help="synthetic activation rows for the channel-RMS / output-error alpha sweep (0 to skip)")
+    ap.add_argument("--learn-iters", type=int, default=3,
+                    help="Lloyd rounds of the codebook refinement on the matrix's own pairs (0 to skip)")
     ap.add_argument("--polar-reps", type=int, default=10,
                     help="polar-code encodes (8 amplitudes x 32 phases) timed after the steps (0 to skip)")
     ap.add_argument("--copy-reference", type=int, default=0,
@@ -296,6 +302,36 @@ def main():
                  "note": "qamw_encode_polar = encode_prepare_kernel + encode_polar_kernel"}
         print(f"polar encode {Ka}x{Kp}: {p_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
+    # codebook refinement on the matrix's own pairs (not part of the step)
+    learned = None
+    if args.learn_iters > 0:
+        it = args.learn_iters
+        ws_l = torch.empty(q.qamw_lloyd_workspace_bytes(K), dtype=torch.uint8, device=dev)
+        C_l = torch.empty_like(Ct)
+        dist_l = torch.empty(it, dtype=torch.float64, device=dev)
+        packed_l = torch.empty_like(packed)
+        plan_l = torch.empty_like(plan)
+        q.qamw_calibrate_encode(W, r, wl.alpha, b, wl.sign_seed, Ct, plan, s, sigma, packed, rn, ws_ce, stream)
+        q.qamw_learn_codebook(W, b, ws_ce, Ct, it, C_l, dist_l, plan_l, packed_l, ws_l, stream)
+        torch.cuda.synchronize()
+        a, z = ev(), ev()
+        a.record(stream)
+        q.qamw_learn_codebook(W, b, ws_ce, Ct, it, C_l, dist_l, plan_l, packed_l, ws_l, stream)
+        z.record(stream)
+        torch.cuda.synchronize()
+        learn_ms = a.elapsed_time(z)
+        Wf = W.float()
+        q.qamw_decode(packed, rn, d, s, sigma, b, wl.sign_seed, Ct, out=out, stream=stream)
+        e0 = float(torch.linalg.norm(out - Wf) / torch.linalg.norm(Wf))
+        q.qamw_build_plan(C_l, plan_l, stream)
+        q.qamw_encode(W, s, sigma, b, wl.sign_seed, C_l, plan=plan_l, packed=packed_l, stream=stream)
+        q.qamw_decode(packed_l, rn, d, s, sigma, b, wl.sign_seed, C_l, out=out, stream=stream)
+        e1 = float(torch.linalg.norm(out - Wf) / torch.linalg.norm(Wf))
+        learned = {"rounds": it, "distortion_by_round": [float(v) for v in dist_l.cpu()],
+                   "ms_per_round": learn_ms / it, "relative_error_gaussian_codebook": e0,
+                   "relative_error_learned_codebook": e1}
+        print(f"learned codebook: {learned}", file=sys.stderr, flush=True)
+
     # channel RMS from activations and the output error over alpha (not part of the step)
     sweep = None
     if args.sweep_tokens > 0:
@@ -408,6 +444,7 @@ def main():
                           "by_tokens": mm},
         "polar": polar,
         "alpha_sweep": sweep,
+        "learned_codebook": learned,
     }
     if not args.no_cpu_baseline:
         print("timing the CPU oracle on a 160-row sample", file=sys.stderr, flush=True)

@@ -205,6 +205,43 @@ int32_t qamw_calibrate_encode(const void* W, int32_t wdtype, int64_t N, int64_t 
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Codebook refinement on a matrix's own pairs (QAM-W, Significance and
+ * Claims: the codebook is trained on the unit circular Gaussian, and a
+ * codebook learned from a checkpoint's own distribution may do better).
+ * Lloyd rounds on the normalised pairs z~ the encoder quantises.
+ *
+ * qamw_lloyd_update: one round's update.  packed must hold the indices that
+ *   qamw_encode (or qamw_encode_indices) produced for this W, codebook and
+ *   encode workspace (filled by qamw_encode_prepare or qamw_calibrate_encode,
+ *   only read here).  Writes codebook_out[c] = the mean of the pairs coded c
+ *   (sums in 64-bit fixed point of 2^-28, so independent of summation
+ *   order; the mean rounded to fp32), or codebook[c] when no pair is coded c,
+ *   and *distortion_out = the mean of |z~ - codebook[idx]|^2 (fp64, fixed
+ *   order) of the given assignment.  codebook_out must not alias codebook.
+ *   workspace >= qamw_lloyd_workspace_bytes(K), 256-byte aligned.
+ *   Deterministic.
+ *
+ * qamw_learn_codebook: iters >= 1 rounds of (qamw_build_plan for the current
+ *   codebook, the planned encode into packed, qamw_lloyd_update) from
+ *   codebook_init; the result goes to codebook_out and round t's distortion
+ *   (of its assignment to its starting codebook) to distortion_out[t].
+ *   plan (>= qamw_plan_bytes(K)) and packed ([N][qamw_packed_row_words(d, K)])
+ *   are scratch; the encode workspace as above.
+ */
+size_t qamw_lloyd_workspace_bytes(int32_t K);
+int32_t qamw_lloyd_update(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, int32_t block,
+                          const uint32_t* packed, const float* codebook, int32_t K,
+                          const void* enc_workspace, size_t enc_workspace_bytes,
+                          float* codebook_out, double* distortion_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int32_t qamw_learn_codebook(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, int32_t block,
+                            const void* enc_workspace, size_t enc_workspace_bytes,
+                            const float* codebook_init, int32_t K, int32_t iters,
+                            float* codebook_out, double* distortion_out,
+                            void* plan, size_t plan_size, uint32_t* packed,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Polar-code baseline (QAM-W, Methodology: Joint 2D Quantization, and the
  * Experiments' joint-versus-polar ablation): the same transform as
  * qamw_encode, but amplitude and phase of each normalised pair z~ = (x, y)

@@ -209,6 +209,43 @@ def test_calibrate_encode_workspace(lib):
     assert lib.qamw_calibrate_encode_workspace_bytes(0, 16) == 0
 
 
+def _lloyd(lib, **kw):
+    args = dict(W=A, wdt=1, N=8, d=256, ldw=256, block=128, packed=A, cb=A, K=256, enc=WS, enc_bytes=1 << 20,
+                out=A + 4096, dist=A, ws=WS + (1 << 21), ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return lib.qamw_lloyd_update(args["W"], args["wdt"], args["N"], args["d"], args["ldw"], args["block"],
+                                 args["packed"], args["cb"], args["K"], args["enc"], args["enc_bytes"], args["out"],
+                                 args["dist"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block=8), -2), (dict(K=1), -2), (dict(packed=None), -1), (dict(packed=MIS), -1), (dict(out=None), -1),
+    (dict(out=A), -1), (dict(dist=None), -1), (dict(dist=A + 4), -1), (dict(enc=None), -4), (dict(enc_bytes=64), -4),
+    (dict(ws=None), -4), (dict(ws_bytes=1024), -4), (dict(ldw=100), -1),
+])
+def test_lloyd_update_rejects(lib, kw, status):
+    assert _lloyd(lib, **kw) == status
+    assert lib.qamw_last_error()
+
+
+def test_learn_codebook_rejects(lib):
+    # one invalid argument each (a fully valid set would launch: never called here)
+    args = [A, 1, 8, 256, 256, 128, WS, 1 << 20, A, 256, 3, A + 4096, A, WS + (1 << 22), 1 << 24, A,
+            WS + (1 << 21), 1 << 20, None]
+    bad = list(args); bad[10] = 0                           # iters
+    assert lib.qamw_learn_codebook(*bad) == -1
+    bad = list(args); bad[11] = A                           # codebook_out aliases codebook_init
+    assert lib.qamw_learn_codebook(*bad) == -1
+    bad = list(args); bad[14] = 1000                        # plan too small
+    assert lib.qamw_learn_codebook(*bad) == -4
+
+
+def test_lloyd_workspace(lib):
+    # 3 x K int64 sums, 4096 fp64 partials, a spare K x 2 codebook; 256-byte padded each
+    assert lib.qamw_lloyd_workspace_bytes(2048) == 3 * 2048 * 8 + 4096 * 8 + 2048 * 8
+    assert lib.qamw_lloyd_workspace_bytes(1) == 0
+
+
 def _calibrate(lib, **kw):
     args = dict(W=A, wdt=0, N=8, d=256, ldw=256, r=A, alpha=0.5, block=128, seed=0, s=A, sigma=A,
                 ws=WS, ws_bytes=1 << 20, stream=None)

@@ -23,6 +23,9 @@ from .codec import (  # noqa: F401
     qamw_encode_prepare,
     qamw_encode_workspace_bytes,
     qamw_index_bits,
+    qamw_learn_codebook,
+    qamw_lloyd_update,
+    qamw_lloyd_workspace_bytes,
     qamw_output_error,
     qamw_output_error_workspace_bytes,
     qamw_packed_row_words,

@@ -285,6 +285,68 @@ def qamw_encode_indices(W: torch.Tensor, block: int, codebook: torch.Tensor, wor
     return packed
 
 
+def qamw_lloyd_workspace_bytes(K: int) -> int:
+    return int(_lib.load().qamw_lloyd_workspace_bytes(K))
+
+
+def qamw_lloyd_update(W: torch.Tensor, block: int, packed: torch.Tensor, codebook: torch.Tensor,
+                      enc_workspace: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      distortion: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None):
+    """One Lloyd update on the matrix's normalised pairs: returns (codebook' [K][2] fp32,
+    distortion [1] fp64 of the assignment in packed)."""
+    N, d, ldw = _rows(W, "W")
+    if W.dtype not in _WDT:
+        raise ValueError("W must be float32 or bfloat16")
+    K = _codebook(codebook)
+    rw = qamw_packed_row_words(d, K)
+    _dev(packed, "packed")
+    if packed.dtype != torch.int32 or tuple(packed.shape) != (N, rw) or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous int32 tensor of shape ({N}, {rw})")
+    _dev(enc_workspace, "enc_workspace")
+    if out is None:
+        out = torch.empty((K, 2), dtype=torch.float32, device=W.device)
+    if distortion is None:
+        distortion = torch.empty(1, dtype=torch.float64, device=W.device)
+    if workspace is None:
+        workspace = _workspace(qamw_lloyd_workspace_bytes(K), W.device)
+    _lib.check("qamw_lloyd_update", _lib.load().qamw_lloyd_update(
+        W.data_ptr(), _WDT[W.dtype], N, d, ldw, int(block), packed.data_ptr(), codebook.data_ptr(), K,
+        enc_workspace.data_ptr(), enc_workspace.numel() * enc_workspace.element_size(), out.data_ptr(),
+        distortion.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, distortion
+
+
+def qamw_learn_codebook(W: torch.Tensor, block: int, enc_workspace: torch.Tensor, codebook_init: torch.Tensor,
+                        iters: int, out: Optional[torch.Tensor] = None, distortion: Optional[torch.Tensor] = None,
+                        plan: Optional[torch.Tensor] = None, packed: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    """iters Lloyd rounds on the matrix's own pairs from codebook_init: returns (codebook [K][2] fp32,
+    distortion [iters] fp64, round t's mean squared distance)."""
+    N, d, ldw = _rows(W, "W")
+    if W.dtype not in _WDT:
+        raise ValueError("W must be float32 or bfloat16")
+    K = _codebook(codebook_init)
+    rw = qamw_packed_row_words(d, K)
+    _dev(enc_workspace, "enc_workspace")
+    if out is None:
+        out = torch.empty((K, 2), dtype=torch.float32, device=W.device)
+    if distortion is None:
+        distortion = torch.empty(int(iters), dtype=torch.float64, device=W.device)
+    if plan is None:
+        plan = torch.empty(qamw_plan_bytes(K), dtype=torch.uint8, device=W.device)
+    if packed is None:
+        packed = torch.empty((N, rw), dtype=torch.int32, device=W.device)
+    if workspace is None:
+        workspace = _workspace(qamw_lloyd_workspace_bytes(K), W.device)
+    _lib.check("qamw_learn_codebook", _lib.load().qamw_learn_codebook(
+        W.data_ptr(), _WDT[W.dtype], N, d, ldw, int(block), enc_workspace.data_ptr(),
+        enc_workspace.numel() * enc_workspace.element_size(), codebook_init.data_ptr(), K, int(iters),
+        out.data_ptr(), distortion.data_ptr(), plan.data_ptr(), plan.numel(), packed.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, distortion
+
+
 def qamw_encode_polar(W: torch.Tensor, s: torch.Tensor, sigma: torch.Tensor, block: int, sign_seed: int,
                       levels: torch.Tensor, dirs: torch.Tensor, packed: Optional[torch.Tensor] = None,
                       rownorm_f16: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,

@@ -278,6 +278,82 @@ int32_t qamw_calibrate_encode(const void* W, int32_t wdtype, int64_t N, int64_t 
                        (int)qamw_packed_row_words(d, K), e.rho, plan, packed, st);
 }
 
+size_t qamw_lloyd_workspace_bytes(int32_t K) {
+  if (K < 2 || K > 4096) return 0;
+  return round_up((size_t)3 * K * sizeof(unsigned long long), 256) + round_up((size_t)kLloydMaxParts * sizeof(double), 256) +
+         round_up((size_t)2 * K * sizeof(float), 256);
+}
+
+int32_t qamw_lloyd_update(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, int32_t block,
+                          const uint32_t* packed, const float* codebook, int32_t K, const void* enc_workspace,
+                          size_t enc_workspace_bytes, float* codebook_out, double* distortion_out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  int L = 0;
+  int rc = check_matrix(N, d, block, &L);
+  if (rc) return rc;
+  if ((rc = check_weights(W, wdtype, d, ldw))) return rc;
+  if ((rc = check_codebook(codebook, K))) return rc;
+  if (!packed || !aligned16(packed)) return fail(QAMW_EINVAL, "packed must be non-NULL and 16-byte aligned");
+  if (!codebook_out || !aligned16(codebook_out)) return fail(QAMW_EINVAL, "codebook_out must be non-NULL and 16-byte aligned");
+  if (codebook_out == codebook) return fail(QAMW_EINVAL, "codebook_out must not be the input codebook");
+  if (!distortion_out || ((uintptr_t)distortion_out & 7u)) return fail(QAMW_EINVAL, "distortion_out must be non-NULL and 8-byte aligned");
+  if ((rc = check_encode_workspace(enc_workspace, enc_workspace_bytes, N, d))) return rc;
+  const size_t need = qamw_lloyd_workspace_bytes(K);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(QAMW_EWORKSPACE, "lloyd update needs %zu bytes of 256-byte aligned workspace (got %zu)", need,
+                workspace_bytes);
+  const EncodeWorkspace e = encode_workspace(const_cast<void*>(enc_workspace), N, d);
+  unsigned long long* gacc = (unsigned long long*)workspace;
+  double* partial = (double*)((char*)workspace + round_up((size_t)3 * K * sizeof(unsigned long long), 256));
+  return launch_lloyd_update(L, W, wdtype, (int)N, (int)d, ldw, e.f, e.isig, e.rho, packed,
+                             (int)qamw_packed_row_words(d, K), qamw_index_bits(K), codebook, (int)K, codebook_out,
+                             distortion_out, gacc, partial, (hipStream_t)stream);
+}
+
+int32_t qamw_learn_codebook(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, int32_t block,
+                            const void* enc_workspace, size_t enc_workspace_bytes, const float* codebook_init,
+                            int32_t K, int32_t iters, float* codebook_out, double* distortion_out, void* plan,
+                            size_t plan_size, uint32_t* packed, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  int L = 0;
+  int rc = check_matrix(N, d, block, &L);
+  if (rc) return rc;
+  if ((rc = check_weights(W, wdtype, d, ldw))) return rc;
+  if ((rc = check_codebook(codebook_init, K))) return rc;
+  if (iters < 1) return fail(QAMW_EINVAL, "iters must be >= 1 (got %d)", (int)iters);
+  if (!codebook_out || !aligned16(codebook_out) || codebook_out == codebook_init)
+    return fail(QAMW_EINVAL, "codebook_out must be non-NULL, 16-byte aligned and not the initial codebook");
+  if (!distortion_out || ((uintptr_t)distortion_out & 7u)) return fail(QAMW_EINVAL, "distortion_out must be non-NULL and 8-byte aligned");
+  if (!packed || !aligned16(packed)) return fail(QAMW_EINVAL, "packed must be non-NULL and 16-byte aligned");
+  if (!plan || ((uintptr_t)plan & 255u) || plan_size < plan_bytes(K))
+    return fail(QAMW_EWORKSPACE, "plan must be 256-byte aligned with %zu bytes", plan_bytes(K));
+  if ((rc = check_encode_workspace(enc_workspace, enc_workspace_bytes, N, d))) return rc;
+  const size_t need = qamw_lloyd_workspace_bytes(K);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(QAMW_EWORKSPACE, "learn_codebook needs %zu bytes of 256-byte aligned workspace (got %zu)", need,
+                workspace_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  const EncodeWorkspace e = encode_workspace(const_cast<void*>(enc_workspace), N, d);
+  unsigned long long* gacc = (unsigned long long*)workspace;
+  double* partial = (double*)((char*)workspace + round_up((size_t)3 * K * sizeof(unsigned long long), 256));
+  float* spare = (float*)((char*)partial + round_up((size_t)kLloydMaxParts * sizeof(double), 256));
+  const int B = qamw_index_bits(K), rw = (int)qamw_packed_row_words(d, K);
+  // round t reads cur and writes dst; the last round writes codebook_out
+  const float* cur = codebook_init;
+  for (int t = 0; t < iters; ++t) {
+    float* dst = ((iters - 1 - t) % 2 == 0) ? codebook_out : spare;
+    if ((rc = launch_build_plan(cur, (int)K, plan, st))) return rc;
+    if ((rc = launch_encode(L, W, wdtype, (int)N, (int)d, ldw, e.f, e.isig, cur, (int)K, B, rw, e.rho, plan, packed,
+                            st)))
+      return rc;
+    if ((rc = launch_lloyd_update(L, W, wdtype, (int)N, (int)d, ldw, e.f, e.isig, e.rho, packed, rw, B, cur, (int)K,
+                                  dst, distortion_out + t, gacc, partial, st)))
+      return rc;
+    cur = dst;
+  }
+  return QAMW_OK;
+}
+
 int32_t qamw_encode_polar(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, const float* s,
                           const float* sigma, int32_t block, uint64_t sign_seed, const float* levels, int32_t Ka,
                           const float* dirs, int32_t Kp, uint32_t* packed, uint16_t* rownorm_f16, void* workspace,

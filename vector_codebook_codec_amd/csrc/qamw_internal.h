@@ -75,6 +75,11 @@ int launch_encode_polar(int L, const void* W, int32_t wdt, int N, int d, int64_t
                         const float* isig, const float* levels, int Ka, const float* dirs, int Kp, int B,
                         int row_words, const double* rho, uint32_t* packed, hipStream_t st);
 int launch_build_plan(const float* cb, int K, void* plan, hipStream_t st);
+constexpr int kLloydMaxParts = 4096;                 // workgroups (fp64 partial sums) of one refinement round
+int launch_lloyd_update(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f,
+                        const float* isig, const double* rho, const uint32_t* packed, int row_words, int B,
+                        const float* cb, int K, float* cb_out, double* distortion, unsigned long long* gacc,
+                        double* partial, hipStream_t st);
 int launch_channel_rms(const void* X, int32_t xdt, int T, int d, int64_t ldx, float* r, float* partial,
                        hipStream_t st);
 int launch_output_error(const void* X, int32_t xdt, int T, int d, int64_t ldx, const void* W, int32_t wdt, int N,
