@@ -53,7 +53,7 @@ PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 KERNEL_SOURCES = [os.path.join(ROOT, "vector_codebook_codec_amd", "csrc", f)
-                  for f in ("encode.hip", "qamw_device.h", "qamw_internal.h")]
+                  for f in ("encode.hip", "encode_window.h", "qamw_device.h", "qamw_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "encode_plan_kernel_4096x11008_traffic.txt")
 
 

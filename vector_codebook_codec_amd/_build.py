@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, f) for f in ("api.hip", "calibrate.hip", "encode.hip", "plan.hip", "decode.hip", "matmul.hip",
-                                                "metrics.hip")]
+                                                "metrics.hip", "polar.hip", "learn.hip")]
 HEADERS = [os.path.join(CSRC, "qamw_device.h"), os.path.join(CSRC, "qamw_internal.h"),
            os.path.join(ROOT, "include", "qamw.h")]
 LIB_PATH = os.path.join(PKG, "libqamw.so")

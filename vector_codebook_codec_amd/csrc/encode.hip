@@ -14,6 +14,7 @@
 #include "qamw.h"
 #include "qamw_device.h"
 #include "qamw_internal.h"
+#include "encode_window.h"
 
 namespace qamw {
 
@@ -37,8 +38,6 @@ namespace qamw {
 // rescanned on the VALU for the smallest index whose score equals the
 // minimum: exact ties go to the lowest index.
 // ---------------------------------------------------------------------------
-constexpr int kEncThreads = 512;                       // 8 wavefronts per workgroup
-constexpr int kEncWaves = kEncThreads / kWave;
 constexpr int kTile = 32;                              // centroids per MFMA tile
 constexpr int kPairSets = kWinPairs / 32;              // 16 MFMA columns blocks per window
 
@@ -67,93 +66,6 @@ __global__ __launch_bounds__(kBlockThreads) void encode_prepare_kernel(
   if (j < d / 2) {
     const float sg = sigma[j];
     isig[j] = sg > 0.0f ? (float)(1.0 / (double)sg) : 0.0f;
-  }
-}
-
-__device__ __forceinline__ double row_normaliser(double rho, int L) {
-  const double den = rho * sqrt((double)(1 << L));
-  return den > 0.0 ? 1.0 / den : 0.0;
-}
-
-// Everything one lane reads for one (row, window): its 16 weights, their
-// column factors eps_j s_j, 1 / sigma of the 8 pairs it holds after the
-// rotation, and the row norm.  load_window issues every load unconditionally
-// from clamped, valid addresses (lanes past the row's last chunk reload the
-// last chunk and are zeroed by the transform), so a wavefront can keep the
-// next window's loads in flight with exact wait counts.
-template <typename Tin>
-struct WinLoads {
-  RawChunk<Tin> raw;
-  float4 fc[4];
-  float4 is[2];
-  double rho;
-};
-
-template <int L, typename Tin>
-__device__ __forceinline__ void load_window(WinLoads<Tin>& w, const Tin* __restrict__ W, int64_t ldw,
-                                            const float* __restrict__ f, const float* __restrict__ isig,
-                                            const double* __restrict__ rho, int n, int win, int lane, int nchunks) {
-  const int c = min(win * kWinChunks + lane, nchunks - 1);
-  const int co = min(win * kWinChunks + BlockOut<L>::chunk(lane), nchunks - 1);
-  w.raw.load(W + (int64_t)n * ldw + c * kChunk);
-  const float4* fp = reinterpret_cast<const float4*>(f + c * kChunk);
-#pragma unroll
-  for (int v = 0; v < 4; ++v) w.fc[v] = fp[v];
-  const float4* ip = reinterpret_cast<const float4*>(isig + co * kPairsPerLane);
-  w.is[0] = ip[0];
-  w.is[1] = ip[1];
-  w.rho = rho[n];
-}
-
-// Rotate the lane's 16 columns and normalise: on return the lane holds the
-// normalised pairs z~ of window chunk co_local (8 pairs), z~ = y / sigma_k
-// with y = H_b (f . w) / (sqrt(b) rho_n); each pair's factor
-// (1 / (sqrt(b) rho_n)) * (1 / sigma_k) is formed in fp64 and rounded once to
-// fp32 (0 for rho_n = 0).  Inactive lanes (past the row's last chunk) give 0.
-template <int L, typename Tin>
-__device__ __forceinline__ int window_transform(const WinLoads<Tin>& w, bool active, int lane, float zx[8],
-                                                float zy[8]) {
-  float x[16];
-  w.raw.unpack(x);
-  const float fc[16] = {w.fc[0].x, w.fc[0].y, w.fc[0].z, w.fc[0].w, w.fc[1].x, w.fc[1].y, w.fc[1].z, w.fc[1].w,
-                        w.fc[2].x, w.fc[2].y, w.fc[2].z, w.fc[2].w, w.fc[3].x, w.fc[3].y, w.fc[3].z, w.fc[3].w};
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = active ? x[i] * fc[i] : 0.0f;
-  fwht_block<L>(x, lane);
-  const int co_local = BlockOut<L>::chunk(lane);   // the lane now holds (sign *) chunk co_local
-  const float osign = BlockOut<L>::sign(lane);
-  const double inv_row = row_normaliser(w.rho, L);
-  const float is[8] = {w.is[0].x, w.is[0].y, w.is[0].z, w.is[0].w, w.is[1].x, w.is[1].y, w.is[1].z, w.is[1].w};
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const float inv = (float)(inv_row * (double)(active ? is[p] : 0.0f)) * osign;
-    zx[p] = x[2 * p] * inv;
-    zy[p] = x[2 * p + 1] * inv;
-  }
-  return co_local;
-}
-
-// Pack the window's 512 indices (stage[k] = index of window pair k) into
-// whole words: a window owns words [16 B win, 16 B (win + 1)) of its row
-// because 512 B is a multiple of 32; the last window also writes the row's
-// zero padding.
-__device__ __forceinline__ void pack_window(const uint16_t* stage, int lane, int win, int nwin, int half_d, int B,
-                                            int row_words, uint32_t* __restrict__ row_out) {
-  const int npairs = min(kWinPairs, half_d - win * kWinPairs);
-  const int word0 = win * 16 * B;
-  const int nwords = (win == nwin - 1) ? row_words - word0 : 16 * B;
-  uint32_t* out = row_out + word0;
-  for (int q = lane; q < nwords; q += kWave) {
-    const int bit0 = q * 32;
-    const int k0 = bit0 / B;
-    const int k1 = min((bit0 + 31) / B, npairs - 1);
-    uint32_t word = 0;
-    for (int k = k0; k <= k1; ++k) {
-      const int off = k * B - bit0;
-      const uint32_t v = stage[k];
-      word |= (off >= 0) ? (v << off) : (v >> (-off));
-    }
-    out[q] = word;
   }
 }
 
@@ -455,337 +367,6 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
   }
 }
 
-// ---------------------------------------------------------------------------
-// Polar code (the pages' joint-versus-polar ablation): amplitude and phase of
-// each normalised pair quantised independently.  Same transform and packing
-// as the joint encode; index = ia * Kp + ip with
-//   r  = sqrt(x*x + y*y) in fp32, each operation rounded (sqrt correctly rounded)
-//   ia = the first i minimising |r - a_i| over the ascending fp32 levels
-//   ip = the first j maximising x c_j + y s_j over the fp32 unit directions.
-// ia: with both levels' fp32 rule folded into squared thresholds (one per
-// adjacent pair, computed by each workgroup), ia is the number of thresholds
-// below x*x + y*y -- no square root per pair.  That equals the first-minimum
-// rule while rounded differences to non-adjacent levels cannot tie, which
-// holds for r below 2^21 times the smallest level gap; larger r (never seen
-// from a normalised matrix) take the definition itself.  ip: an approximate
-// atan2 (error < 1.2e-5 rad, far below half a sector for Kp <= 4096) gives
-// q = phi Kp / 2 pi; the first maximum is sector j0 = round(q) or its
-// neighbour on the side of q - j0 (directions farther away score lower by
-// ~r (2 pi / Kp)^2, far above fp32 rounding).  Points with |z~|^2 < 1e-20,
-// where scores could underflow, scan every direction.
-// ---------------------------------------------------------------------------
-// Squared decision threshold between adjacent levels lo < hi (both >= 0):
-// the largest fp32 s such that r = sqrt(s) (correctly rounded) still picks
-// lo under the fp32 rule fl(r - lo) <= fl(hi - r).  That rule is monotone in
-// r, and sqrt is monotone in s, so for s = x^2 + y^2 the level index is the
-// number of thresholds below s.  Found by stepping one ulp at a time from
-// the midpoint and from its square (a few steps).
-__device__ __forceinline__ float ulp_up(float t) { return __uint_as_float(__float_as_uint(t) + 1u); }
-__device__ __forceinline__ float ulp_down(float t) { return t > 0.0f ? __uint_as_float(__float_as_uint(t) - 1u) : 0.0f; }
-__device__ float polar_threshold_sq(float lo, float hi) {
-  float t = (lo + hi) * 0.5f;
-  for (int it = 0; it < 64 && ulp_up(t) - lo <= hi - ulp_up(t); ++it) t = ulp_up(t);
-  for (int it = 0; it < 64 && !(t - lo <= hi - t); ++it) t = ulp_down(t);
-  float sv = t * t;
-  for (int it = 0; it < 64 && sqrtf(ulp_up(sv)) <= t; ++it) sv = ulp_up(sv);
-  for (int it = 0; it < 64 && sqrtf(sv) > t; ++it) sv = ulp_down(sv);
-  return sv;
-}
-
-constexpr int kPolarLinearLevels = 17;   // up to 16 thresholds are counted one by one
-
-// atan2(y, x) to within 1.2e-5 rad: octant reduction to a = min/max in [0, 1]
-// and the odd degree-9 polynomial of Abramowitz & Stegun, Handbook of
-// Mathematical Functions, formula 4.4.47 (|error| <= 1e-5 on [-1, 1]).  It
-// only places a point among the phase sectors; the decision itself is made
-// on exact fp32 inner products.
-__device__ __forceinline__ float approx_atan2(float y, float x) {
-  const float ax = fabsf(x), ay = fabsf(y);
-  const float mx = fmaxf(ax, ay), mn = fminf(ax, ay);
-  const float a = mx > 0.0f ? mn * __builtin_amdgcn_rcpf(mx) : 0.0f;
-  const float a2 = a * a;
-  float t = 0.0208351f;
-  t = t * a2 - 0.0851330f;
-  t = t * a2 + 0.1801410f;
-  t = t * a2 - 0.3302995f;
-  t = t * a2 + 0.9998660f;
-  t *= a;
-  t = (ay > ax) ? 1.5707963267948966f - t : t;
-  t = (x < 0.0f) ? 3.1415926535897932f - t : t;
-  return (y < 0.0f) ? -t : t;
-}
-
-constexpr int kPolarWgPerCu = 2;   // 4 wavefronts per SIMD
-
-template <int L, typename Tin>
-__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))) void encode_polar_kernel(
-    const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ f,
-    const float* __restrict__ isig, const float* __restrict__ levels, int Ka, const float* __restrict__ dirs,
-    int Kp, int B, int row_words, const double* __restrict__ rho, uint32_t* __restrict__ packed) {
-  extern __shared__ float4 lds4[];
-  float2* dv = reinterpret_cast<float2*>(lds4);                       // Kp directions
-  float* lv = reinterpret_cast<float*>(dv + Kp);                       // Ka levels
-  float* sq = lv + Ka;                                                 // Ka - 1 squared thresholds
-  uint16_t* stage_all = reinterpret_cast<uint16_t*>(sq + Ka);
-  __shared__ uint32_t gap_bits;                                        // smallest level gap (>= 0)
-  if (threadIdx.x == 0) gap_bits = 0x7f800000u;                        // +inf
-  for (int j = threadIdx.x; j < Kp; j += kEncThreads) dv[j] = make_float2(dirs[2 * j], dirs[2 * j + 1]);
-  for (int i = threadIdx.x; i < Ka; i += kEncThreads) lv[i] = levels[i];
-  __syncthreads();
-  for (int i = threadIdx.x + 1; i < Ka; i += kEncThreads) {
-    sq[i - 1] = polar_threshold_sq(lv[i - 1], lv[i]);
-    atomicMin(&gap_bits, __float_as_uint(fmaxf(lv[i] - lv[i - 1], 0.0f)));
-  }
-  __syncthreads();
-  // below r_safe = gap 2^21 the rounded differences r - a_j of non-adjacent
-  // levels cannot tie, so counting thresholds is the first-minimum rule
-  const float r_safe = __uint_as_float(gap_bits) * 2097152.0f;
-  const float s_safe = r_safe * r_safe;
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-  uint16_t* stage = stage_all + wave * kWinPairs;
-  const int nchunks = d >> 4;
-  const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
-  const int total = N * nwin;                      // fits in int (checked on the host)
-  const int stride = gridDim.x * kEncWaves;
-  int gw = blockIdx.x * kEncWaves + wave;
-  if (gw >= total) return;                         // no barriers follow
-
-  int n = gw / nwin, win = gw - (gw / nwin) * nwin;
-  WinLoads<Tin> wl;
-  load_window<L>(wl, W, ldw, f, isig, rho, n, win, lane, nchunks);
-  const float sectors_per_radian = (float)Kp * 0.15915494309189535f;   // Kp / (2 pi)
-  int ka_top = 1;                                  // largest power of two <= Ka - 1 thresholds
-  while (2 * ka_top <= Ka - 1) ka_top *= 2;
-
-  for (;;) {
-    const bool active = win * kWinChunks + lane < nchunks;   // whole Hadamard blocks are active or not
-    float zx[8], zy[8];
-    const int co_local = window_transform<L>(wl, active, lane, zx, zy);
-    const int n_cur = n, win_cur = win;
-    const int gnext = gw + stride;
-    {
-      // the next window's loads stay in flight during the search; past the
-      // end the last window is loaded again (unused), keeping them unconditional
-      const int gl = min(gnext, total - 1);
-      n = gl / nwin;
-      win = gl - n * nwin;
-      load_window<L>(wl, W, ldw, f, isig, rho, n, win, lane, nchunks);
-    }
-    // Each step below runs for all of the lane's pairs at once, LDS reads
-    // first, without branches; the rare cases are wave-uniform fallbacks.
-    float s2[kPairsPerLane];
-    int ia[kPairsPerLane];
-    bool big = false;
-#pragma unroll
-    for (int p = 0; p < kPairsPerLane; ++p) {
-      s2[p] = zx[p] * zx[p] + zy[p] * zy[p];
-      ia[p] = 0;
-      big |= !(s2[p] <= s_safe);
-    }
-    // ---- amplitude: ia = number of squared thresholds below x^2 + y^2
-    if (Ka <= kPolarLinearLevels) {
-      for (int t = 0; t < Ka - 1; ++t) {
-        const float th = sq[t];                    // same address in every lane: broadcast
-#pragma unroll
-        for (int p = 0; p < kPairsPerLane; ++p) ia[p] += (s2[p] > th) ? 1 : 0;
-      }
-    } else {
-      for (int h = ka_top; h > 0; h >>= 1) {       // thresholds ascend; same trip count in every lane
-        float th[kPairsPerLane];
-#pragma unroll
-        for (int p = 0; p < kPairsPerLane; ++p) th[p] = sq[min(ia[p] + h, Ka - 1) - 1];
-#pragma unroll
-        for (int p = 0; p < kPairsPerLane; ++p) {
-          const int t = ia[p] + h;
-          ia[p] = ((t <= Ka - 1) & (s2[p] > th[p])) ? t : ia[p];
-        }
-      }
-    }
-    if (__any(big)) {                              // |z~| dwarfs the level spacing: the definition itself
-#pragma unroll
-      for (int p = 0; p < kPairsPerLane; ++p) {
-        if (!(s2[p] <= s_safe)) {
-          const float r = sqrtf(s2[p]);
-          float best = INFINITY;
-          int bi = 0;
-          for (int i2 = 0; i2 < Ka; ++i2) {
-            const float dd = fabsf(r - lv[i2]);
-            if (dd < best) { best = dd; bi = i2; }
-          }
-          ia[p] = bi;
-        }
-      }
-    }
-    // ---- phase: the sector estimate j0 and its neighbour on the side the
-    // point leans to; the larger score wins, the lower index on a tie
-    int ip[kPairsPerLane];
-    bool tiny = false;
-    {
-      int ja[kPairsPerLane], jb[kPairsPerLane];
-      float2 ua[kPairsPerLane], ub[kPairsPerLane];
-#pragma unroll
-      for (int p = 0; p < kPairsPerLane; ++p) {
-        const float qv = approx_atan2(zy[p], zx[p]) * sectors_per_radian;   // in [-Kp/2, Kp/2]
-        const float qr = rintf(qv);
-        int j0 = (int)qr;
-        j0 += (j0 < 0) ? Kp : 0;
-        j0 = (j0 >= Kp) ? j0 - Kp : j0;
-        const int jup = (j0 == Kp - 1) ? 0 : j0 + 1;
-        const int jdn = (j0 == 0) ? Kp - 1 : j0 - 1;
-        ja[p] = j0;
-        jb[p] = (qv > qr) ? jup : jdn;
-        ua[p] = dv[ja[p]];
-        ub[p] = dv[jb[p]];
-      }
-#pragma unroll
-      for (int p = 0; p < kPairsPerLane; ++p) {
-        const float x = zx[p], y = zy[p];
-        const float sa = x * ua[p].x + y * ua[p].y;
-        const float sb = x * ub[p].x + y * ub[p].y;
-        const bool take = (sb > sa) | ((sb == sa) & (jb[p] < ja[p]));
-        ip[p] = take ? jb[p] : ja[p];
-        tiny |= !(s2[p] >= 1e-20f);
-      }
-    }
-    if (__any(tiny)) {                             // scores could underflow: every direction
-#pragma unroll
-      for (int p = 0; p < kPairsPerLane; ++p) {
-        if (!(s2[p] >= 1e-20f)) {
-          const float x = zx[p], y = zy[p];
-          float best = -INFINITY;
-          int bj = 0;
-          for (int j2 = 0; j2 < Kp; ++j2) {
-            const float2 uu = dv[j2];
-            const float sc = x * uu.x + y * uu.y;
-            if (sc > best) { best = sc; bj = j2; }
-          }
-          ip[p] = bj;
-        }
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < kPairsPerLane; ++p) stage[co_local * kPairsPerLane + p] = (uint16_t)(ia[p] * Kp + ip[p]);
-    wave_lds_fence();
-    pack_window(stage, lane, win_cur, nwin, d >> 1, B, row_words, packed + (int64_t)n_cur * row_words);
-    gw = gnext;
-    if (gw >= total) break;
-    wave_lds_fence();                              // the stage is rewritten next round
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Codebook refinement on the matrix's own pairs (the pages suggest a learned
-// codebook; Lloyd rounds on the normalised pairs z~).  One round = the encode
-// (assignment, any kernel above) followed by these two kernels:
-//   lloyd_accum_kernel   re-derives z~ with the encode's own transform, reads
-//                        each pair's index from the packed rows and adds z~
-//                        into its centroid's sums -- fixed point, 2^-28 units,
-//                        in 64-bit integers (LDS atomics per workgroup, then
-//                        global atomics), so the sums do not depend on the
-//                        order of the additions; |z~ - C[idx]|^2 is summed in
-//                        fp64 per lane, per wavefront and per workgroup in a
-//                        fixed order
-//   lloyd_update_kernel  C'[c] = sum / count rounded to fp32 (a centroid with no
-//                        pair keeps its place), and the mean squared distance.
-// Deterministic.
-// ---------------------------------------------------------------------------
-constexpr double kLloydScale = 268435456.0;      // 2^28
-constexpr int kLloydWgPerCu = 2;
-
-template <int L, typename Tin>
-__global__ __launch_bounds__(kEncThreads) void lloyd_accum_kernel(
-    const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ f,
-    const float* __restrict__ isig, const double* __restrict__ rho, const uint32_t* __restrict__ packed,
-    int row_words, int B, const float* __restrict__ codebook, int K, unsigned long long* __restrict__ gacc,
-    double* __restrict__ partial) {
-  extern __shared__ unsigned long long lacc[];     // K x (sum x, sum y, count)
-  __shared__ double red[kEncWaves];
-  for (int i = threadIdx.x; i < 3 * K; i += kEncThreads) lacc[i] = 0ull;
-  __syncthreads();
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-  const int nchunks = d >> 4;
-  const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
-  const int total = N * nwin;
-  const int stride = gridDim.x * kEncWaves;
-  double dsum = 0.0;
-  for (int gw = blockIdx.x * kEncWaves + wave; gw < total; gw += stride) {
-    const int n = gw / nwin, win = gw - (gw / nwin) * nwin;
-    WinLoads<Tin> wl;
-    load_window<L>(wl, W, ldw, f, isig, rho, n, win, lane, nchunks);
-    const bool active = win * kWinChunks + lane < nchunks;
-    float zx[8], zy[8];
-    const int co_local = window_transform<L>(wl, active, lane, zx, zy);
-    // the 8 indices of window pairs 8 co_local .. + 7: 8 B bits from bit
-    // (512 win + 8 co_local) B of the row (words past the row end only feed
-    // unused bits, so their loads are clamped into the row)
-    const int64_t bit0 = (int64_t)(win * kWinPairs + co_local * kPairsPerLane) * B;
-    const int w0 = (int)(bit0 >> 5);
-    const uint32_t* prow = packed + (int64_t)n * row_words;
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = prow[min(w0 + i, row_words - 1)];
-    uint32_t idx[8];
-    unpack8<0>(w, (uint32_t)(bit0 & 31), B, idx);
-    if (active) {
-#pragma unroll
-      for (int p = 0; p < kPairsPerLane; ++p) {
-        const int c = min((int)idx[p], K - 1);
-        const double cx = (double)codebook[2 * c], cy = (double)codebook[2 * c + 1];
-        const double dx = (double)zx[p] - cx, dy = (double)zy[p] - cy;
-        dsum += dx * dx + dy * dy;
-        atomicAdd(&lacc[3 * c + 0], (unsigned long long)__double2ll_rn((double)zx[p] * kLloydScale));
-        atomicAdd(&lacc[3 * c + 1], (unsigned long long)__double2ll_rn((double)zy[p] * kLloydScale));
-        atomicAdd(&lacc[3 * c + 2], 1ull);
-      }
-    }
-  }
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) dsum += __shfl_xor(dsum, off);
-  if (lane == 0) red[wave] = dsum;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double t = 0.0;
-#pragma unroll
-    for (int i = 0; i < kEncWaves; ++i) t += red[i];
-    partial[blockIdx.x] = t;
-  }
-  for (int i = threadIdx.x; i < 3 * K; i += kEncThreads)
-    if (lacc[i]) atomicAdd(&gacc[i], lacc[i]);
-}
-
-__global__ __launch_bounds__(256) void lloyd_zero_kernel(unsigned long long* __restrict__ gacc, int n) {
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) gacc[i] = 0ull;
-}
-
-__global__ __launch_bounds__(256) void lloyd_update_kernel(const unsigned long long* __restrict__ gacc,
-                                                           const float* __restrict__ codebook, int K,
-                                                           const double* __restrict__ partial, int nparts,
-                                                           double npairs, float* __restrict__ out,
-                                                           double* __restrict__ distortion) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c < K) {
-    const long long cnt = (long long)gacc[3 * c + 2];
-    if (cnt > 0) {
-      const double sx = (double)(long long)gacc[3 * c] / kLloydScale;
-      const double sy = (double)(long long)gacc[3 * c + 1] / kLloydScale;
-      out[2 * c] = (float)(sx / (double)cnt);
-      out[2 * c + 1] = (float)(sy / (double)cnt);
-    } else {
-      out[2 * c] = codebook[2 * c];
-      out[2 * c + 1] = codebook[2 * c + 1];
-    }
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    double t = 0.0;
-    for (int i = 0; i < nparts; ++i) t += partial[i];
-    *distortion = t / npairs;
-  }
-}
-
 // ===========================================================================
 // launcher
 // ===========================================================================
@@ -850,81 +431,5 @@ int launch_encode(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, 
   return dispatch_L<LaunchEncode>(L, W, wdt, N, d, ldw, f, isig, cb, K, B, row_words, rho, plan, packed, st);
 }
 
-
-template <int L>
-struct LaunchEncodePolar {
-  static int run(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const float* isig,
-                 const float* levels, int Ka, const float* dirs, int Kp, int B, int row_words, const double* rho,
-                 uint32_t* packed, hipStream_t st) {
-    const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
-    const int64_t waves = (int64_t)N * nwin;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      return fail(QAMW_EHIP, "cannot query the device's compute units");
-    const dim3 grid((unsigned)std::min<int64_t>((waves + kEncWaves - 1) / kEncWaves, (int64_t)cus * kPolarWgPerCu)),
-        blk(kEncThreads);
-    const size_t lds = (size_t)Kp * sizeof(float2) + (size_t)2 * Ka * sizeof(float) +
-                       (size_t)kEncWaves * kWinPairs * sizeof(uint16_t);
-    if (wdt == QAMW_F32)
-      hipLaunchKernelGGL((encode_polar_kernel<L, float>), grid, blk, lds, st, (const float*)W, ldw, N, d, f, isig,
-                         levels, Ka, dirs, Kp, B, row_words, rho, packed);
-    else
-      hipLaunchKernelGGL((encode_polar_kernel<L, uint16_t>), grid, blk, lds, st, (const uint16_t*)W, ldw, N, d, f,
-                         isig, levels, Ka, dirs, Kp, B, row_words, rho, packed);
-    return check_launch("encode_polar_kernel");
-  }
-};
-
-int launch_encode_polar(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f,
-                        const float* isig, const float* levels, int Ka, const float* dirs, int Kp, int B,
-                        int row_words, const double* rho, uint32_t* packed, hipStream_t st) {
-  return dispatch_L<LaunchEncodePolar>(L, W, wdt, N, d, ldw, f, isig, levels, Ka, dirs, Kp, B, row_words, rho,
-                                       packed, st);
-}
-
-
-template <int L>
-struct LaunchLloyd {
-  static int run(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const float* isig,
-                 const double* rho, const uint32_t* packed, int row_words, int B, const float* cb, int K,
-                 unsigned long long* gacc, double* partial, int nparts, hipStream_t st) {
-    const size_t lds = (size_t)3 * K * sizeof(unsigned long long);
-    if (wdt == QAMW_F32)
-      hipLaunchKernelGGL((lloyd_accum_kernel<L, float>), dim3(nparts), dim3(kEncThreads), lds, st, (const float*)W,
-                         ldw, N, d, f, isig, rho, packed, row_words, B, cb, K, gacc, partial);
-    else
-      hipLaunchKernelGGL((lloyd_accum_kernel<L, uint16_t>), dim3(nparts), dim3(kEncThreads), lds, st,
-                         (const uint16_t*)W, ldw, N, d, f, isig, rho, packed, row_words, B, cb, K, gacc, partial);
-    return check_launch("lloyd_accum_kernel");
-  }
-};
-
-int lloyd_parts(int N, int d) {
-  const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
-  const int64_t wgs = ((int64_t)N * nwin + kEncWaves - 1) / kEncWaves;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;
-  return (int)std::min<int64_t>(std::min<int64_t>(wgs, (int64_t)cus * kLloydWgPerCu), kLloydMaxParts);
-}
-
-int launch_lloyd_update(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f,
-                        const float* isig, const double* rho, const uint32_t* packed, int row_words, int B,
-                        const float* cb, int K, float* cb_out, double* distortion, unsigned long long* gacc,
-                        double* partial, hipStream_t st) {
-  hipLaunchKernelGGL(lloyd_zero_kernel, dim3((3 * K + 255) / 256), dim3(256), 0, st, gacc, 3 * K);
-  int rc = check_launch("lloyd_zero_kernel");
-  if (rc) return rc;
-  const int nparts = lloyd_parts(N, d);
-  if ((rc = dispatch_L<LaunchLloyd>(L, W, wdt, N, d, ldw, f, isig, rho, packed, row_words, B, cb, K, gacc, partial,
-                                    nparts, st)))
-    return rc;
-  const int64_t npairs = (int64_t)N * (d / 2);
-  hipLaunchKernelGGL(lloyd_update_kernel, dim3((K + 255) / 256), dim3(256), 0, st, gacc, cb, K, partial, nparts,
-                     (double)npairs, cb_out, distortion);
-  return check_launch("lloyd_update_kernel");
-}
 
 }  // namespace qamw
