@@ -241,28 +241,43 @@ def main():
         Y = torch.empty((T, N), dtype=torch.float32, device=dev)
         Wbf = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
 
-        def fused():
-            q.qamw_rotate_activations(X, s, b, wl.sign_seed, Xr, stream)
-            q.qamw_decode_matmul(Xr, packed, rn, sigma, Ct, out=Y, stream=stream)
+        def fused(st):
+            q.qamw_rotate_activations(X, s, b, wl.sign_seed, Xr, st)
+            q.qamw_decode_matmul(Xr, packed, rn, sigma, Ct, out=Y, stream=st)
 
-        def unfused():
-            q.qamw_decode(packed, rn, d, s, sigma, b, wl.sign_seed, Ct, out=Wbf, stream=stream)
+        def unfused(st):
+            q.qamw_decode(packed, rn, d, s, sigma, b, wl.sign_seed, Ct, out=Wbf, stream=st)
             torch.matmul(X, Wbf.t())
 
+        # GPU time per call: 20 calls captured in a HIP graph and replayed, so
+        # that host launch gaps (comparable to these kernels) are not counted
+        inner = 20
         res_t = {}
+        fused(stream)
+        torch.cuda.synchronize()
+        Y_eager = Y.clone()
         for name, fn in (("fused", fused), ("unfused", unfused)):
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for _ in range(3):
+                    fn(None)
+            torch.cuda.current_stream().wait_stream(side)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(inner):
+                    fn(None)
             times = []
-            for _ in range(args.matmul_reps):
+            for _ in range(max(1, args.matmul_reps)):
                 a, z = ev(), ev()
-                a.record(stream)
-                fn()
-                z.record(stream)
+                a.record()
+                g.replay()
+                z.record()
                 torch.cuda.synchronize()
-                times.append(a.elapsed_time(z))
+                times.append(a.elapsed_time(z) / inner)
             res_t[name] = float(np.median(times))
+            if name == "fused" and not torch.equal(Y, Y_eager):
+                raise RuntimeError("graph replays of the fused matmul differ from the eager result")
         # algorithmic bytes of the fused path: packed + row norms + sigma + X read + Xr write/read + Y write
         mm_bytes = N * rw * 4 + N * 2 + d * 2 + T * d * 2 * 3 + T * N * 4
         mm[str(T)] = {"fused_us": res_t["fused"] * 1e3, "unfused_us": res_t["unfused"] * 1e3,
