@@ -353,7 +353,7 @@ def main():
         Tt = args.sweep_tokens
         Xs = torch.from_numpy(workloads.activations(Tt, wl.r, seed=2024)).to(dev).to(torch.bfloat16)
         ws_rms = torch.empty(max(256, q.qamw_channel_rms_workspace_bytes(Tt, d)), dtype=torch.uint8, device=dev)
-        ws_oe = torch.empty(max(256, q.qamw_output_error_workspace_bytes(Tt, N)), dtype=torch.uint8, device=dev)
+        ws_oe = torch.empty(max(256, q.qamw_output_error_workspace_bytes(Tt, N, d)), dtype=torch.uint8, device=dev)
         r_x = torch.empty(d, dtype=torch.float32, device=dev)
         e_out = torch.empty(1, dtype=torch.float64, device=dev)
         s_a = torch.empty_like(s)

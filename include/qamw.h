@@ -283,7 +283,8 @@ int32_t qamw_encode_polar(const void* W, int32_t wdtype, int64_t N, int64_t d, i
  *            hdtype (QAMW_F32 or QAMW_BF16 each), 16-byte aligned rows
  *   d        a multiple of 16
  *   err_out  one double on the device, written by the call
- *   workspace >= qamw_output_error_workspace_bytes(T, N), 256-byte aligned
+ *   workspace >= qamw_output_error_workspace_bytes(T, N, d), 256-byte
+ *            aligned (holds bf16 copies of dW and, for fp32 X, of X)
  *   Arithmetic: dW = W - W_hat in fp32, then dW and X rounded to bf16 and
  *   multiplied on bf16 MFMA with fp32 accumulation; squares summed in fp64 in
  *   a fixed order (deterministic).  Relative error of E: about 2^-8 in the
@@ -292,7 +293,7 @@ int32_t qamw_encode_polar(const void* W, int32_t wdtype, int64_t N, int64_t d, i
 size_t qamw_channel_rms_workspace_bytes(int64_t T, int64_t d);
 int32_t qamw_channel_rms(const void* X, int32_t xdtype, int64_t T, int64_t d, int64_t ldx, float* r_out,
                          void* workspace, size_t workspace_bytes, void* stream);
-size_t qamw_output_error_workspace_bytes(int64_t T, int64_t N);
+size_t qamw_output_error_workspace_bytes(int64_t T, int64_t N, int64_t d);
 int32_t qamw_output_error(const void* X, int32_t xdtype, int64_t T, int64_t d, int64_t ldx,
                           const void* W, int32_t wdtype, int64_t N, int64_t ldw,
                           const void* W_hat, int32_t hdtype, int64_t ldh,

@@ -175,11 +175,14 @@ def test_output_error_rejects(lib, kw, status):
 
 
 def test_metric_workspace_sizes(lib):
-    # one fp32 partial per (64-row tile, column); one fp64 partial per 128 x 128 block
+    # one fp32 partial per (64-row tile, column)
     assert lib.qamw_channel_rms_workspace_bytes(2048, 11008) == 32 * 11008 * 4
     assert lib.qamw_channel_rms_workspace_bytes(65, 8) == 256
-    assert lib.qamw_output_error_workspace_bytes(2048, 4096) == 16 * 32 * 8
-    assert lib.qamw_output_error_workspace_bytes(0, 4) == 0
+    # one fp64 partial per 128 x 128 block of X dW^T (row blocks rounded up to a multiple
+    # of 8), bf16 dW [N][d] and bf16 X [T][d]
+    assert lib.qamw_output_error_workspace_bytes(2048, 4096, 11008) == 32 * 16 * 8 + 4096 * 11008 * 2 + 2048 * 11008 * 2
+    assert lib.qamw_output_error_workspace_bytes(64, 200, 16) == 256 + 200 * 16 * 2 + 64 * 16 * 2
+    assert lib.qamw_output_error_workspace_bytes(0, 4, 16) == 0
 
 
 def _cal_enc(lib, **kw):

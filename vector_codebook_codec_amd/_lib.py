@@ -42,7 +42,7 @@ SIGNATURES = {
                                  _sz, _p]),
     "qamw_channel_rms_workspace_bytes": (_sz, [_i64, _i64]),
     "qamw_channel_rms": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _sz, _p]),
-    "qamw_output_error_workspace_bytes": (_sz, [_i64, _i64]),
+    "qamw_output_error_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "qamw_output_error": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _i32, _i64, _i64, _p, _i32, _i64, _p, _p, _sz,
                                  _p]),
     "qamw_rotate_activations": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _i32, _u64, _p, _i64, _p]),

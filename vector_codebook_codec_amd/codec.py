@@ -387,8 +387,8 @@ def qamw_channel_rms_workspace_bytes(T: int, d: int) -> int:
     return int(_lib.load().qamw_channel_rms_workspace_bytes(T, d))
 
 
-def qamw_output_error_workspace_bytes(T: int, N: int) -> int:
-    return int(_lib.load().qamw_output_error_workspace_bytes(T, N))
+def qamw_output_error_workspace_bytes(T: int, N: int, d: int) -> int:
+    return int(_lib.load().qamw_output_error_workspace_bytes(T, N, d))
 
 
 def qamw_channel_rms(X: torch.Tensor, out: Optional[torch.Tensor] = None,
@@ -423,7 +423,7 @@ def qamw_output_error(X: torch.Tensor, W: torch.Tensor, W_hat: torch.Tensor, out
         out = torch.empty(1, dtype=torch.float64, device=X.device)
     _vec(out, "out", 1, torch.float64)
     if workspace is None:
-        workspace = _workspace(qamw_output_error_workspace_bytes(T, N), X.device)
+        workspace = _workspace(qamw_output_error_workspace_bytes(T, N, d), X.device)
     _lib.check("qamw_output_error", _lib.load().qamw_output_error(
         X.data_ptr(), _WDT[X.dtype], T, d, ldx, W.data_ptr(), _WDT[W.dtype], N, ldw, W_hat.data_ptr(),
         _WDT[W_hat.dtype], ldh, out.data_ptr(), workspace.data_ptr(),

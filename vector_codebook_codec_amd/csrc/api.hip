@@ -385,10 +385,16 @@ size_t qamw_channel_rms_workspace_bytes(int64_t T, int64_t d) {
   return round_up((size_t)((T + kRmsRowsPerTile - 1) / kRmsRowsPerTile) * (size_t)d * sizeof(float), 256);
 }
 
-size_t qamw_output_error_workspace_bytes(int64_t T, int64_t N) {
-  if (T <= 0 || T > kMaxDim || N <= 0 || N > kMaxDim) return 0;
-  return round_up((size_t)((T + kOutputErrorTile - 1) / kOutputErrorTile) *
-                      (size_t)((N + kOutputErrorTile - 1) / kOutputErrorTile) * sizeof(double), 256);
+static size_t oe_partials_bytes(int64_t T, int64_t N) {
+  // one per workgroup: row blocks rounded up to whole groups of 8 (one per XCD) x token blocks
+  const int64_t nb = (N + kOutputErrorRows - 1) / kOutputErrorRows;
+  return round_up((size_t)((nb + 7) / 8 * 8) * (size_t)((T + kOutputErrorTokens - 1) / kOutputErrorTokens) *
+                      sizeof(double), 256);
+}
+
+size_t qamw_output_error_workspace_bytes(int64_t T, int64_t N, int64_t d) {
+  if (T <= 0 || T > kMaxDim || N <= 0 || N > kMaxDim || d <= 0 || d > kMaxDim) return 0;
+  return oe_partials_bytes(T, N) + round_up((size_t)N * (size_t)d * 2, 256) + round_up((size_t)T * (size_t)d * 2, 256);
 }
 
 static int check_rows16(const void* p, int32_t dt, int64_t d, int64_t ld, const char* name, bool allow_f16) {
@@ -429,12 +435,16 @@ int32_t qamw_output_error(const void* X, int32_t xdtype, int64_t T, int64_t d, i
   if ((rc = check_rows16(W, wdtype, d, ldw, "W", false))) return rc;
   if ((rc = check_rows16(W_hat, hdtype, d, ldh, "W_hat", false))) return rc;
   if (!err_out || ((uintptr_t)err_out & 7u)) return fail(QAMW_EINVAL, "err_out must be non-NULL and 8-byte aligned");
-  const size_t need = qamw_output_error_workspace_bytes(T, N);
+  const size_t need = qamw_output_error_workspace_bytes(T, N, d);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
     return fail(QAMW_EWORKSPACE, "output error needs %zu bytes of 256-byte aligned workspace (got %zu)", need,
                 workspace_bytes);
+  char* ws = (char*)workspace;
+  double* partial = (double*)ws;
+  uint16_t* dWb = (uint16_t*)(ws + oe_partials_bytes(T, N));
+  uint16_t* Xb = (uint16_t*)((char*)dWb + round_up((size_t)N * (size_t)d * 2, 256));
   return launch_output_error(X, xdtype, (int)T, (int)d, ldx, W, wdtype, (int)N, ldw, W_hat, hdtype, ldh, err_out,
-                             (double*)workspace, (hipStream_t)stream);
+                             partial, dWb, Xb, (hipStream_t)stream);
 }
 
 int32_t qamw_decode(const uint32_t* packed, const uint16_t* rownorm_f16, int64_t N, int64_t d, const float* s,

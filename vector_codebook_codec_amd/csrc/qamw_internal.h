@@ -14,7 +14,8 @@ constexpr int kBlockThreads = 256;                   // 4 wavefronts per workgro
 constexpr int kWavesPerBlock = kBlockThreads / 64;
 constexpr int kCalibRowsPerTile = 16;                // rows per amplitude partial sum
 constexpr int kRmsRowsPerTile = 64;                  // activation rows per channel-RMS partial sum
-constexpr int kOutputErrorTile = 128;                // tokens and rows per output-error workgroup
+constexpr int kOutputErrorTokens = 128;              // tokens per output-error workgroup
+constexpr int kOutputErrorRows = 128;                // weight rows per output-error workgroup
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 
 // ---- errors (the message of the calling thread's last failure)
@@ -84,7 +85,7 @@ int launch_channel_rms(const void* X, int32_t xdt, int T, int d, int64_t ldx, fl
                        hipStream_t st);
 int launch_output_error(const void* X, int32_t xdt, int T, int d, int64_t ldx, const void* W, int32_t wdt, int N,
                         int64_t ldw, const void* Wh, int32_t hdt, int64_t ldh, double* out, double* partial,
-                        hipStream_t st);
+                        uint16_t* dWb, uint16_t* Xb, hipStream_t st);
 int launch_rotate_act(int L, const void* X, int32_t xdt, int T, int d, int64_t ldx, const float* s, uint64_t seed,
                       uint16_t* Xr, int64_t ldr, hipStream_t st);
 int launch_decode_matmul(const uint16_t* Xr, int T, int d, int64_t ldr, const uint32_t* packed, int row_words,
