@@ -109,6 +109,9 @@ def test_rotate_activations(q, T, d, b, wdtype):
 @pytest.mark.parametrize("N,d,b,K,T", [
     (37, 512, 128, 256, 1), (37, 512, 128, 256, 16), (16, 1088, 64, 2048, 17), (20, 96, 32, 16, 40),
     (9, 48, 16, 4, 65), (33, 3072, 256, 4096, 64), (8, 2048, 1024, 1024, 7),
+    # one token (the GEMV kernel): B = 12, a ragged single slice with B = 2, B = 10,
+    # more slices than wavefronts (d / 2 = 18432 pairs = 36 slices of 512)
+    (33, 3072, 256, 4096, 1), (9, 48, 16, 4, 1), (8, 2048, 1024, 1024, 1), (5, 36864, 256, 256, 1),
 ])
 def test_decode_matmul_shapes(q, N, d, b, K, T):
     rng = np.random.default_rng(N * 7 + d + T)
@@ -133,6 +136,9 @@ def test_decode_matmul_without_s_and_bf16_out(q):
     check_matmul(q, X, g, b, 3, C, d, use_s=False)
     say("case matmul bf16 out")
     check_matmul(q, X, g, b, 3, C, d, out_dtype=torch.bfloat16)
+    say("case matmul one token, s=None and bf16 out")
+    check_matmul(q, X[:1], g, b, 3, C, d, use_s=False)
+    check_matmul(q, X[:1], g, b, 3, C, d, out_dtype=torch.bfloat16)
 
 
 def test_decode_matmul_full_size_sampled(q):
@@ -150,3 +156,18 @@ def test_decode_matmul_full_size_sampled(q):
                               g["sigma"], g["C"])
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2)              # deterministic
+
+
+def test_decode_matmul_full_size_one_token(q):
+    """4096 x 11008 (K = 2048, block 256), one token (GEMV kernel), 96 sampled channels, deterministic."""
+    wl = workloads.get("c3t_4096x11008")
+    C = q.load_codebook(wl.K)
+    g = encode_gpu(q, wl.W_f32(), wl.r, wl.alpha, wl.block, wl.sign_seed, C, wdtype="bf16")
+    rng = np.random.default_rng(zlib.crc32(b"gemv"))
+    X = rng.standard_normal((1, wl.d)).astype(np.float32)
+    rows = np.sort(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, 94, replace=False)]))
+    say("case matmul c3t 4096x11008 T=1")
+    Y1, Xr = check_matmul(q, X, g, wl.block, wl.sign_seed, C, wl.d, rows=rows)
+    Y2 = q.qamw_decode_matmul(Xr, g["packed"], g["rn"], g["sigma"], g["C"])
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)

@@ -282,6 +282,101 @@ __global__ __launch_bounds__(mm_waves<TT>() * kWave) void decode_matmul_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// One token (T = 1): the same product as a GEMV, without MFMA.  y[n] =
+// rho^_n sum_k (u_k.x C[idx_nk].x + u_k.y C[idx_nk].y) with u_k = sigma_k
+// (xr_2k, xr_2k+1), all fp32.  Wavefront w of a workgroup owns the column
+// slices w, w + W, ... of 512 pairs (lane l: pairs 8 l .. 8 l + 7 of the
+// slice, one byte-aligned run of 8 B bits); its u stays in registers while it
+// walks the workgroup's 8 rows, whose packed bits it loads all at once
+// (clamped: words past a row end only feed unused bits, rows past N reload
+// the last one).  Per row the lane's fp32 dot product is summed across the
+// wavefront by a fixed butterfly; the slices' sums are added in wavefront
+// order through LDS.  Deterministic.
+// ---------------------------------------------------------------------------
+constexpr int kGvRows = 8;
+constexpr int kGvSlice = 512;
+constexpr int kGvMaxWaves = 16;
+
+template <int BT, typename Out>
+__global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_gemv_kernel(
+    const uint16_t* __restrict__ Xr, int d, const uint32_t* __restrict__ packed, int row_words,
+    const uint16_t* __restrict__ rho_f16, int N, const float* __restrict__ sigma,
+    const float* __restrict__ codebook, int K, int Bdyn, typename Out::T* __restrict__ Y) {
+  extern __shared__ float4 lds4[];
+  float2* cb = reinterpret_cast<float2*>(lds4);
+  float* part = reinterpret_cast<float*>(cb + ((K + 1) & ~1));      // [waves][kGvRows]
+  for (int c = threadIdx.x; c < K; c += blockDim.x) cb[c] = make_float2(codebook[2 * c], codebook[2 * c + 1]);
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int B = BT ? BT : Bdyn;
+  const int half_d = d >> 1;
+  const int nslices = (half_d + kGvSlice - 1) / kGvSlice;
+  const int n0 = blockIdx.x * kGvRows;
+  const uint32_t* prow[kGvRows];
+#pragma unroll
+  for (int r = 0; r < kGvRows; ++r) prow[r] = packed + (int64_t)min(n0 + r, N - 1) * row_words;
+  float rowacc[kGvRows];
+#pragma unroll
+  for (int r = 0; r < kGvRows; ++r) rowacc[r] = 0.0f;
+
+  for (int sl = wave; sl < nslices; sl += nw) {
+    const int p0 = sl * kGvSlice + 8 * lane;
+    const bool act = p0 < half_d;                  // half_d % 8 == 0: all 8 pairs in or out
+    const int pc = act ? p0 : 0;
+    float ux[8], uy[8];
+    {
+      const uint4 xa = *reinterpret_cast<const uint4*>(Xr + 2 * pc);
+      const uint4 xb = *reinterpret_cast<const uint4*>(Xr + 2 * pc + 8);
+      const float4 s0 = *reinterpret_cast<const float4*>(sigma + pc);
+      const float4 s1 = *reinterpret_cast<const float4*>(sigma + pc + 4);
+      const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+      const float sg[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        ux[p] = act ? sg[p] * bf16_bits_to_f32(xw[p] & 0xffffu) : 0.0f;
+        uy[p] = act ? sg[p] * bf16_bits_to_f32(xw[p] >> 16) : 0.0f;
+      }
+    }
+    const int64_t bit = (int64_t)pc * B;
+    const int w0 = (int)(bit >> 5);
+    const uint32_t sh = (uint32_t)(bit & 31);
+    uint32_t w[kGvRows][4];
+#pragma unroll
+    for (int r = 0; r < kGvRows; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[r][i] = prow[r][min(w0 + i, row_words - 1)];
+#pragma unroll
+    for (int r = 0; r < kGvRows; ++r) {
+      uint32_t idx[8];
+      unpack8<BT>(w[r], sh, Bdyn, idx);
+      float acc = 0.0f;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const float2 cc = cb[min((int)idx[p], K - 1)];
+        acc = __builtin_fmaf(ux[p], cc.x, acc);
+        acc = __builtin_fmaf(uy[p], cc.y, acc);
+      }
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+      rowacc[r] += acc;
+    }
+  }
+  if (lane == 0)
+#pragma unroll
+    for (int r = 0; r < kGvRows; ++r) part[wave * kGvRows + r] = rowacc[r];
+  __syncthreads();
+  if ((int)threadIdx.x < kGvRows) {
+    const int n = n0 + threadIdx.x;
+    if (n < N) {
+      float sum = 0.0f;
+      for (int ww = 0; ww < nw; ++ww) sum += part[ww * kGvRows + threadIdx.x];
+      Out::put(Y + n, sum * f16_bits_to_f32(rho_f16[n]));
+    }
+  }
+}
+
 // ===========================================================================
 // launchers
 // ===========================================================================
@@ -326,9 +421,27 @@ static int launch_mm(const uint16_t* Xr, int T, int d, int64_t ldr, const uint32
 }
 
 template <int BT>
+static int launch_gemv(const uint16_t* Xr, int d, const uint32_t* packed, int row_words, const uint16_t* rn, int N,
+                       const float* sigma, const float* cb, int K, int B, void* Y, int32_t ydt, hipStream_t st) {
+  const int nslices = (d / 2 + kGvSlice - 1) / kGvSlice;
+  const int nw = nslices < kGvMaxWaves ? nslices : kGvMaxWaves;
+  const dim3 grid((unsigned)((N + kGvRows - 1) / kGvRows)), blk((unsigned)(nw * kWave));
+  const size_t lds = (size_t)((K + 1) & ~1) * sizeof(float2) + (size_t)nw * kGvRows * sizeof(float);
+  if (ydt == QAMW_F32)
+    hipLaunchKernelGGL((decode_gemv_kernel<BT, OutF32>), grid, blk, lds, st, Xr, d, packed, row_words, rn, N, sigma,
+                       cb, K, B, (float*)Y);
+  else
+    hipLaunchKernelGGL((decode_gemv_kernel<BT, OutBF16>), grid, blk, lds, st, Xr, d, packed, row_words, rn, N, sigma,
+                       cb, K, B, (uint16_t*)Y);
+  return check_launch("decode_gemv_kernel");
+}
+
+template <int BT>
 static int launch_mm_tt(const uint16_t* Xr, int T, int d, int64_t ldr, const uint32_t* packed, int row_words,
                         const uint16_t* rn, int N, const float* sigma, const float* cb, int K, int B, void* Y,
                         int32_t ydt, int64_t ldy, hipStream_t st) {
+  // one token: the GEMV kernel
+  if (T == 1) return launch_gemv<BT>(Xr, d, packed, row_words, rn, N, sigma, cb, K, B, Y, ydt, st);
   // token tiles per workgroup: one for T <= 16, up to four (64 tokens) sharing each decoded operand
   if (T <= 16) return launch_mm<BT, 1>(Xr, T, d, ldr, packed, row_words, rn, N, sigma, cb, K, B, Y, ydt, ldy, st);
   if (T <= 32) return launch_mm<BT, 2>(Xr, T, d, ldr, packed, row_words, rn, N, sigma, cb, K, B, Y, ydt, ldy, st);
