@@ -278,15 +278,41 @@ def main():
             res_t[name] = float(np.median(times))
             if name == "fused" and not torch.equal(Y, Y_eager):
                 raise RuntimeError("graph replays of the fused matmul differ from the eager result")
+        if T == 1:                                  # the one-kernel path from raw activations
+            xv = X[0].contiguous()
+            yv = torch.empty(N, dtype=torch.float32, device=dev)
+            mv = lambda st: q.qamw_decode_matvec(xv, packed, rn, s, sigma, b, wl.sign_seed, Ct, out=yv, stream=st)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for _ in range(3):
+                    mv(None)
+            torch.cuda.current_stream().wait_stream(side)
+            gmv = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gmv):
+                for _ in range(inner):
+                    mv(None)
+            tms = []
+            for _ in range(max(1, args.matmul_reps)):
+                a, z = ev(), ev()
+                a.record()
+                gmv.replay()
+                z.record()
+                torch.cuda.synchronize()
+                tms.append(a.elapsed_time(z) / inner)
+            res_t["matvec"] = float(np.median(tms))
         # algorithmic bytes of the fused path: packed + row norms + sigma + X read + Xr write/read + Y write
         mm_bytes = N * rw * 4 + N * 2 + d * 2 + T * d * 2 * 3 + T * N * 4
         mm[str(T)] = {"fused_us": res_t["fused"] * 1e3, "unfused_us": res_t["unfused"] * 1e3,
+                      "matvec_us": res_t["matvec"] * 1e3 if "matvec" in res_t else None,
                       "algorithmic_bytes": mm_bytes,
                       "GB_s": mm_bytes / (res_t["fused"] * 1e-3) / 1e9,
                       "frac_hbm": mm_bytes / (res_t["fused"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                       "tflops": 2.0 * T * N * d / (res_t["fused"] * 1e-3) / 1e12}
         print(f"decode_matmul T={T}: fused {res_t['fused'] * 1e3:.1f} us, "
-              f"decode-to-bf16 + torch.matmul {res_t['unfused'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+              f"decode-to-bf16 + torch.matmul {res_t['unfused'] * 1e3:.1f} us"
+              + (f", one-kernel matvec {res_t['matvec'] * 1e3:.1f} us" if "matvec" in res_t else ""),
+              file=sys.stderr, flush=True)
 
     # polar-code baseline encode at 8 bits per pair (not part of the step)
     polar = None

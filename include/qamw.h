@@ -300,6 +300,25 @@ int32_t qamw_output_error(const void* X, int32_t xdtype, int64_t T, int64_t d, i
                           double* err_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One-token decoded-weight product from the raw activations (QAM-W,
+ * Significance and Claims: a fused kernel turns the bit savings into
+ * latency): y[n] = sum_j x[j] W^[n][j], W^ the decoded matrix (with s; with
+ * s = NULL the scaled W' = W diag(s), as qamw_decode), in one kernel that
+ * also performs the rotation of x.
+ *   x          [d] of xdtype (QAMW_F32 or QAMW_BF16), 16-byte aligned
+ *   s, block, sign_seed, packed, rownorm_f16, N, sigma, codebook, K
+ *              as for qamw_decode
+ *   y          [N] of ydtype (QAMW_F32 or QAMW_BF16, RNE from fp32)
+ * Equal to qamw_rotate_activations + qamw_decode_matmul with T = 1 except that
+ * the rotated activations stay fp32 (no bf16 rounding).  fp32 arithmetic;
+ * deterministic.
+ */
+int32_t qamw_decode_matvec(const void* x, int32_t xdtype, int64_t d, const float* s, int32_t block,
+                           uint64_t sign_seed, const uint32_t* packed, const uint16_t* rownorm_f16, int64_t N,
+                           const float* sigma, const float* codebook, int32_t K, void* y, int32_t ydtype,
+                           void* stream);
+
+/*
  * Decode (QAM-W, Methodology: Decoding).
  *   packed, rownorm_f16, N, d, block, sign_seed, codebook, K  as produced by
  *             qamw_encode; indices >= K (never produced) are clamped to K - 1

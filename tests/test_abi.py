@@ -249,6 +249,24 @@ def test_lloyd_workspace(lib):
     assert lib.qamw_lloyd_workspace_bytes(1) == 0
 
 
+def _mv(lib, **kw):
+    args = dict(x=A, xdt=0, d=256, s=A, block=128, seed=0, packed=A, rn=A, N=8, sigma=A, cb=A, K=256, y=A, ydt=0,
+                stream=None)
+    args.update(kw)
+    return lib.qamw_decode_matvec(args["x"], args["xdt"], args["d"], args["s"], args["block"], args["seed"],
+                                  args["packed"], args["rn"], args["N"], args["sigma"], args["cb"], args["K"],
+                                  args["y"], args["ydt"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block=8), -2), (dict(d=200), -1), (dict(N=0), -1), (dict(K=1), -2), (dict(x=None), -1), (dict(x=MIS), -1),
+    (dict(s=MIS), -1), (dict(packed=None), -1), (dict(y=None), -1), (dict(xdt=2), -2), (dict(ydt=2), -2),
+])
+def test_decode_matvec_rejects(lib, kw, status):
+    assert _mv(lib, **kw) == status
+    assert lib.qamw_last_error()
+
+
 def _calibrate(lib, **kw):
     args = dict(W=A, wdt=0, N=8, d=256, ldw=256, r=A, alpha=0.5, block=128, seed=0, s=A, sigma=A,
                 ws=WS, ws_bytes=1 << 20, stream=None)

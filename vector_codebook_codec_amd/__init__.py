@@ -17,6 +17,7 @@ from .codec import (  # noqa: F401
     qamw_channel_rms_workspace_bytes,
     qamw_decode,
     qamw_decode_matmul,
+    qamw_decode_matvec,
     qamw_encode,
     qamw_encode_indices,
     qamw_encode_polar,

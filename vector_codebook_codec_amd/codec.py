@@ -457,6 +457,36 @@ def qamw_decode(packed: torch.Tensor, rownorm_f16: torch.Tensor, d: int, s: Opti
     return out
 
 
+def qamw_decode_matvec(x: torch.Tensor, packed: torch.Tensor, rownorm_f16: torch.Tensor, s: Optional[torch.Tensor],
+                       sigma: torch.Tensor, block: int, sign_seed: int, codebook: torch.Tensor,
+                       out_dtype=torch.float32, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = x W^^T for one token x [d] (fp32 or bf16) from the packed matrix, rotation included: y [N]."""
+    _dev(x, "x")
+    if x.dim() != 1 or not x.is_contiguous() or x.dtype not in _WDT:
+        raise ValueError("x must be a contiguous 1-D float32 or bfloat16 tensor")
+    d = x.shape[0]
+    _dev(packed, "packed")
+    N = packed.shape[0]
+    K = _codebook(codebook)
+    rw = qamw_packed_row_words(d, K)
+    if packed.dtype != torch.int32 or tuple(packed.shape) != (N, rw) or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous int32 tensor of shape ({N}, {rw})")
+    _vec(rownorm_f16, "rownorm_f16", N, torch.int16)
+    if s is not None:
+        _vec(s, "s", d)
+    _vec(sigma, "sigma", d // 2)
+    if out is None:
+        out = torch.empty(N, dtype=out_dtype, device=x.device)
+    _dev(out, "out")
+    if out.dim() != 1 or out.shape[0] != N or not out.is_contiguous() or out.dtype not in _WDT:
+        raise ValueError("out must be a contiguous 1-D float32 or bfloat16 tensor of N elements")
+    _lib.check("qamw_decode_matvec", _lib.load().qamw_decode_matvec(
+        x.data_ptr(), _WDT[x.dtype], d, None if s is None else s.data_ptr(), int(block), int(sign_seed),
+        packed.data_ptr(), rownorm_f16.data_ptr(), N, sigma.data_ptr(), codebook.data_ptr(), K, out.data_ptr(),
+        _WDT[out.dtype], _stream(stream)))
+    return out
+
+
 def qamw_rotate_activations(X: torch.Tensor, s: Optional[torch.Tensor], block: int, sign_seed: int,
                             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Xr = bf16(R_fwd (X / s)) per activation row: the left operand of qamw_decode_matmul."""

@@ -502,4 +502,22 @@ int32_t qamw_decode_matmul(const uint16_t* Xr_bf16, int64_t T, int64_t d, int64_
                               K, B, Y, ydtype, ldy, (hipStream_t)stream);
 }
 
+int32_t qamw_decode_matvec(const void* x, int32_t xdtype, int64_t d, const float* s, int32_t block,
+                           uint64_t sign_seed, const uint32_t* packed, const uint16_t* rownorm_f16, int64_t N,
+                           const float* sigma, const float* codebook, int32_t K, void* y, int32_t ydtype,
+                           void* stream) {
+  int L = 0;
+  int rc = check_matrix(N, d, block, &L);
+  if (rc) return rc;
+  if ((rc = check_codebook(codebook, K))) return rc;
+  if (!x || !packed || !rownorm_f16 || !sigma || !y)
+    return fail(QAMW_EINVAL, "x, packed, rownorm_f16, sigma and y must be non-NULL");
+  if (xdtype != QAMW_F32 && xdtype != QAMW_BF16) return fail(QAMW_EUNSUPPORTED, "x dtype %d not supported", xdtype);
+  if (ydtype != QAMW_F32 && ydtype != QAMW_BF16) return fail(QAMW_EUNSUPPORTED, "y dtype %d not supported", ydtype);
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(sigma) || (s && !aligned16(s)))
+    return fail(QAMW_EINVAL, "x, packed, sigma and s must be 16-byte aligned");
+  return launch_decode_matvec(L, x, xdtype, (int)d, s, sign_seed, packed, (int)qamw_packed_row_words(d, K), rownorm_f16,
+                              (int)N, sigma, codebook, K, qamw_index_bits(K), y, ydtype, (hipStream_t)stream);
+}
+
 }  // extern "C"

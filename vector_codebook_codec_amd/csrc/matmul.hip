@@ -377,6 +377,110 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_gemv_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// One token from the raw activations: y = x W^^T with the rotation done in
+// the same kernel.  A GEMV slice of 512 pairs is exactly one 1024-column
+// rotation window, so wavefront w rotates window w (x_j eps_j / (sqrt(b)
+// s_j), the block FWHT) in registers; afterwards lane l holds the 8 pairs of
+// window chunk BlockOut(l) and decodes exactly those pairs -- the same
+// products as qamw_rotate_activations + qamw_decode_matmul, with the rotated
+// activations kept in fp32 instead of rounded to bf16.  Otherwise as
+// decode_gemv_kernel (index width at run time: this kernel waits on memory,
+// not on arithmetic).
+// ---------------------------------------------------------------------------
+template <int L, typename Tin, typename Out>
+__global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_matvec_kernel(
+    const Tin* __restrict__ X, int d, const float* __restrict__ s, uint64_t seed,
+    const uint32_t* __restrict__ packed, int row_words, const uint16_t* __restrict__ rho_f16, int N,
+    const float* __restrict__ sigma, const float* __restrict__ codebook, int K, int B,
+    typename Out::T* __restrict__ Y) {
+  extern __shared__ float4 lds4[];
+  float2* cb = reinterpret_cast<float2*>(lds4);
+  float* part = reinterpret_cast<float*>(cb + ((K + 1) & ~1));      // [waves][kGvRows]
+  for (int c = threadIdx.x; c < K; c += blockDim.x) cb[c] = make_float2(codebook[2 * c], codebook[2 * c + 1]);
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int nchunks = d >> 4;
+  const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
+  const int n0 = blockIdx.x * kGvRows;
+  const float inv_sqrt_b = (float)(1.0 / sqrt((double)(1 << L)));
+  const uint32_t* prow[kGvRows];
+#pragma unroll
+  for (int r = 0; r < kGvRows; ++r) prow[r] = packed + (int64_t)min(n0 + r, N - 1) * row_words;
+  float rowacc[kGvRows];
+#pragma unroll
+  for (int r = 0; r < kGvRows; ++r) rowacc[r] = 0.0f;
+
+  for (int win = wave; win < nwin; win += nw) {
+    const int c = win * kWinChunks + lane;
+    const bool active = c < nchunks;               // whole Hadamard blocks are active or not
+    const int cl = active ? c : 0;
+    float x[16];
+    {
+      RawChunk<Tin> raw;
+      raw.load(X + cl * kChunk);
+      raw.unpack(x);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = cl * kChunk + i;
+        const float g = sign_eps(seed, (uint32_t)j) * (inv_sqrt_b / (s ? s[j] : 1.0f));
+        x[i] = active ? x[i] * g : 0.0f;
+      }
+    }
+    fwht_block<L>(x, lane);
+    const int co = win * kWinChunks + BlockOut<L>::chunk(lane);   // the chunk this lane now holds
+    const float osign = BlockOut<L>::sign(lane);
+    const int pc = active ? co * kPairsPerLane : 0;
+    float ux[8], uy[8];
+    {
+      const float4 s0 = *reinterpret_cast<const float4*>(sigma + pc);
+      const float4 s1 = *reinterpret_cast<const float4*>(sigma + pc + 4);
+      const float sg[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        ux[p] = active ? sg[p] * (x[2 * p] * osign) : 0.0f;
+        uy[p] = active ? sg[p] * (x[2 * p + 1] * osign) : 0.0f;
+      }
+    }
+    const int64_t bit = (int64_t)pc * B;
+    const int w0 = (int)(bit >> 5);
+    const uint32_t sh = (uint32_t)(bit & 31);
+    uint32_t w[kGvRows][4];
+#pragma unroll
+    for (int r = 0; r < kGvRows; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[r][i] = prow[r][min(w0 + i, row_words - 1)];
+#pragma unroll
+    for (int r = 0; r < kGvRows; ++r) {
+      uint32_t idx[8];
+      unpack8<0>(w[r], sh, B, idx);
+      float acc = 0.0f;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const float2 cc = cb[min((int)idx[p], K - 1)];
+        acc = __builtin_fmaf(ux[p], cc.x, acc);
+        acc = __builtin_fmaf(uy[p], cc.y, acc);
+      }
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+      rowacc[r] += acc;
+    }
+  }
+  if (lane == 0)
+#pragma unroll
+    for (int r = 0; r < kGvRows; ++r) part[wave * kGvRows + r] = rowacc[r];
+  __syncthreads();
+  if ((int)threadIdx.x < kGvRows) {
+    const int n = n0 + threadIdx.x;
+    if (n < N) {
+      float sum = 0.0f;
+      for (int ww = 0; ww < nw; ++ww) sum += part[ww * kGvRows + threadIdx.x];
+      Out::put(Y + n, sum * f16_bits_to_f32(rho_f16[n]));
+    }
+  }
+}
+
 // ===========================================================================
 // launchers
 // ===========================================================================
@@ -446,6 +550,34 @@ static int launch_mm_tt(const uint16_t* Xr, int T, int d, int64_t ldr, const uin
   if (T <= 16) return launch_mm<BT, 1>(Xr, T, d, ldr, packed, row_words, rn, N, sigma, cb, K, B, Y, ydt, ldy, st);
   if (T <= 32) return launch_mm<BT, 2>(Xr, T, d, ldr, packed, row_words, rn, N, sigma, cb, K, B, Y, ydt, ldy, st);
   return launch_mm<BT, 4>(Xr, T, d, ldr, packed, row_words, rn, N, sigma, cb, K, B, Y, ydt, ldy, st);
+}
+
+template <int L>
+struct LaunchMatvec {
+  static int run(const void* X, int32_t xdt, int d, const float* s, uint64_t seed, const uint32_t* packed,
+                 int row_words, const uint16_t* rn, int N, const float* sigma, const float* cb, int K, int B, void* Y,
+                 int32_t ydt, hipStream_t st) {
+    const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
+    const int nw = nwin < kGvMaxWaves ? nwin : kGvMaxWaves;
+    const dim3 grid((unsigned)((N + kGvRows - 1) / kGvRows)), blk((unsigned)(nw * kWave));
+    const size_t lds = (size_t)((K + 1) & ~1) * sizeof(float2) + (size_t)nw * kGvRows * sizeof(float);
+#define QAMW_MV(TIN, OUT, YT)                                                                                    \
+  hipLaunchKernelGGL((decode_matvec_kernel<L, TIN, OUT>), grid, blk, lds, st, (const TIN*)X, d, s, seed, packed, \
+                     row_words, rn, N, sigma, cb, K, B, (YT*)Y)
+    if (xdt == QAMW_F32) {
+      if (ydt == QAMW_F32) QAMW_MV(float, OutF32, float); else QAMW_MV(float, OutBF16, uint16_t);
+    } else {
+      if (ydt == QAMW_F32) QAMW_MV(uint16_t, OutF32, float); else QAMW_MV(uint16_t, OutBF16, uint16_t);
+    }
+#undef QAMW_MV
+    return check_launch("decode_matvec_kernel");
+  }
+};
+
+int launch_decode_matvec(int L, const void* X, int32_t xdt, int d, const float* s, uint64_t seed,
+                         const uint32_t* packed, int row_words, const uint16_t* rn, int N, const float* sigma,
+                         const float* cb, int K, int B, void* Y, int32_t ydt, hipStream_t st) {
+  return dispatch_L<LaunchMatvec>(L, X, xdt, d, s, seed, packed, row_words, rn, N, sigma, cb, K, B, Y, ydt, st);
 }
 
 int launch_decode_matmul(const uint16_t* Xr, int T, int d, int64_t ldr, const uint32_t* packed, int row_words,
