@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "qamw.h"
 #include "qamw_device.h"
 #include "qamw_internal.h"
@@ -21,24 +23,37 @@ namespace qamw {
 #define QAMW_DECODE_WAVES_PER_CU 16
 #endif
 constexpr int kDecodePrefetch = QAMW_DECODE_PREFETCH;
+constexpr int kDecodeMaxRows = 16;   // rows per wavefront, at most
 
 // ---------------------------------------------------------------------------
 // Decode.  Each workgroup keeps one 1024-column window and walks rows with a
 // stride (row n goes to workgroup (n / 4) mod blocks_per_window of its
-// window, wave n mod 4), so the codebook (K x float2) and the window's column
-// factors g_j = eps_j / (sqrt(b) s_j) are staged in LDS once per workgroup,
-// with all prologue loads in flight together.  Each lane keeps its 8 sigma_k
-// and 16 factors in registers, holds the row norms of 64 rows at a time (one
-// per lane), and prefetches the packed words of the next rows while it
-// decodes the current one.  BT > 0 fixes the index width at compile time
-// (BT = 0: width B from the argument).
+// window, wave n mod 4), so the codebook and the window's column factors
+// g_j = eps_j / (sqrt(b) s_j) are staged in LDS once per workgroup, with all
+// prologue loads in flight together.  Each lane keeps its 8 sigma_k and 16
+// factors in registers, holds the row norms of 64 rows at a time (one per
+// lane), and keeps the packed words of the next kDecodePrefetch rows in
+// flight in a ring of named slots (the row loop is unrolled by the ring
+// length, so slots never move between registers).
+//
+// The LDS codebook holds each centroid as (c_x + c_y, c_x - c_y): the first
+// in-register butterfly of the inverse rotation acts on exactly the pair
+// (y_2k, y_2k+1), so it is folded into the table and the transform starts
+// at its second stage.  The row norm is folded into the pair scales.
+// BT > 0 fixes the index width at compile time and pads the table to 2^BT
+// entries (zeros past K), so any B-bit index reads inside it without a clamp;
+// BT = 0 takes the width B from the argument and clamps indices to K - 1.
 // ---------------------------------------------------------------------------
 template <int L, int BT, typename Out>
 __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
-    const uint32_t* __restrict__ packed, const uint16_t* __restrict__ rho_f16, int N, int d,
+    const uint32_t* packed, const uint16_t* rho_f16, int N, int d,
     const float* __restrict__ s, const float* __restrict__ sigma, uint64_t seed,
     const float* __restrict__ codebook, int K, int Bdyn, int row_words, int blocks_per_window,
     typename Out::T* __restrict__ out, int64_t ldo) {
+  // packed and rho_f16 are deliberately not __restrict__: the output stores
+  // then keep each ring-slot prefetch in the row that issues it (the compiler
+  // may not move a load past a store that could alias it), instead of letting
+  // it sink into the row that consumes it.
   extern __shared__ float4 lds4[];
   uint4* stage_all = reinterpret_cast<uint4*>(lds4);    // 4 waves x 256 x 16 bytes
   float* gwin = reinterpret_cast<float*>(stage_all + kWavesPerBlock * 256);  // kWinChunks * kChunk factors
@@ -49,7 +64,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
   const int win = blockIdx.x % nwin;
   const int rblk = blockIdx.x / nwin;               // 0 .. blocks_per_window-1
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = win * kWinChunks + lane;
   // Lanes past the row end hold zeros but stay: the window store reads back
   // columns for every lane of the wave.
@@ -58,28 +73,32 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
   const int first = rblk * kWavesPerBlock + wave;
   const int stride = blocks_per_window * kWavesPerBlock;
   const int nrows = first < N ? (N - first + stride - 1) / stride : 0;
+  const int last = nrows > 0 ? nrows - 1 : 0;
 
   // ---- the first rows' loads go out before the LDS prologue, so their
-  // latency overlaps it
+  // latency overlaps it.  Row loads are unconditional: rows past the wave's
+  // last reload its last row, and lanes past the row end read its last words.
+  // Each ring slot also carries its row's fp16 norm (a uniform load), so the
+  // row loop has no other global loads.
   const int B = BT ? BT : Bdyn;
   const int64_t bitstart = (int64_t)c * kPairsPerLane * B;
   const int wstart = (int)(bitstart >> 5);
   const uint32_t sh = (uint32_t)(bitstart & 31);
-  int widx[4];
+  uint32_t widx[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) widx[i] = min(wstart + i, row_words - 1);
+  for (int i = 0; i < 4; ++i) widx[i] = (uint32_t)min(wstart + i, row_words - 1);
   uint32_t ring[kDecodePrefetch][4];   // packed words of the next rows, in flight
+  uint16_t ring_rh[kDecodePrefetch];   // their row norms
+  if (nrows > 0) {
 #pragma unroll
-  for (int q = 0; q < kDecodePrefetch; ++q) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ring[q][i] = 0u;
-    if (active && q < nrows) {
-      const uint32_t* rw = packed + (int64_t)(first + q * stride) * row_words;
+    for (int q = 0; q < kDecodePrefetch; ++q) {
+      const int n = first + min(q, last) * stride;
+      const uint32_t* rw = packed + (int64_t)n * row_words;
 #pragma unroll
       for (int i = 0; i < 4; ++i) ring[q][i] = rw[widx[i]];
+      ring_rh[q] = rho_f16[n];
     }
   }
-  float rh_lane = (lane < nrows) ? f16_bits_to_f32(rho_f16[first + lane * stride]) : 0.0f;  // 64 rows at a time
   float sg[8];
   if (active) {
     const float4* sp = reinterpret_cast<const float4*>(sigma + c * kPairsPerLane);
@@ -91,14 +110,23 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
     for (int p = 0; p < 8; ++p) sg[p] = 0.0f;
   }
 
-  // ---- LDS prologue: codebook and the window's column factors
+  // ---- LDS prologue: codebook (sum/difference form, padded) and the
+  // window's column factors
   {
     const float4* cb4 = reinterpret_cast<const float4*>(codebook);   // two centroids per float4
     float4* cbl = reinterpret_cast<float4*>(cb);
     const int npairs4 = K >> 1;
 #pragma unroll 8
-    for (int cc = threadIdx.x; cc < npairs4; cc += kBlockThreads) cbl[cc] = cb4[cc];
-    if ((K & 1) && threadIdx.x == 0) cb[K - 1] = make_float2(codebook[2 * (K - 1)], codebook[2 * (K - 1) + 1]);
+    for (int cc = threadIdx.x; cc < npairs4; cc += kBlockThreads) {
+      const float4 t = cb4[cc];
+      cbl[cc] = make_float4(t.x + t.y, t.x - t.y, t.z + t.w, t.z - t.w);
+    }
+    if ((K & 1) && threadIdx.x == 0) {
+      const float cx = codebook[2 * (K - 1)], cy = codebook[2 * (K - 1) + 1];
+      cb[K - 1] = make_float2(cx + cy, cx - cy);
+    }
+    if constexpr (BT > 0)
+      for (int cc = K + (int)threadIdx.x; cc < (1 << BT); cc += kBlockThreads) cb[cc] = make_float2(0.0f, 0.0f);
     const float inv_sqrt_b = (float)(1.0 / sqrt((double)(1 << L)));
     constexpr int kPer = kWinChunks * kChunk / kBlockThreads;   // 4
     float sv[kPer];
@@ -132,38 +160,56 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
     }
   }
 
-  for (int k = 0; k < nrows; ++k) {
-    if (k > 0 && (k & (kWave - 1)) == 0) {
-      const int kk = k + lane;
-      rh_lane = (kk < nrows) ? f16_bits_to_f32(rho_f16[first + kk * stride]) : 0.0f;
-    }
-    const int n = first + k * stride;
-    uint32_t w[4] = {ring[0][0], ring[0][1], ring[0][2], ring[0][3]};
+  typename Out::T* out_win = out + win * kWinChunks * kChunk;
+  // One copy of the row walk for full windows (stores without a per-lane
+  // test) and one for the ragged last window, chosen once per workgroup.
+  // A wave has at most kDecodeMaxRows rows (the launcher picks the stride),
+  // and the walk is straight-line code: row k runs inside the test for row
+  // k - 1, so every row has one path to it and the compiler's memory-counter
+  // waits wait only for the ring slot being consumed, never for the stores
+  // and prefetches issued after it.
+  auto rows = [&](auto full) {
+    constexpr bool kFull = decltype(full)::value;
+    auto row = [&](int q, int k) {
+      const int n = first + k * stride;
+      uint32_t idx[8];
+      unpack8<BT>(ring[q], sh, Bdyn, idx);
+      const float rh = f16_bits_to_f32(ring_rh[q]);
+      {   // this slot now takes row k + kDecodePrefetch (or the last row again)
+        const int nn = first + min(k + kDecodePrefetch, last) * stride;
+        const uint32_t* rw = packed + (int64_t)nn * row_words;
 #pragma unroll
-    for (int q = 0; q + 1 < kDecodePrefetch; ++q)
+        for (int i = 0; i < 4; ++i) ring[q][i] = rw[widx[i]];
+        ring_rh[q] = rho_f16[nn];
+      }
+      float x[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ring[q][i] = ring[q + 1][i];
-    if (active && k + kDecodePrefetch < nrows) {
-      const uint32_t* rw = packed + (int64_t)(n + kDecodePrefetch * stride) * row_words;
+      for (int p = 0; p < 8; ++p) {
+        const float2 cc = cb[BT ? (int)idx[p] : min((int)idx[p], K - 1)];
+        const float f = sg[p] * rh;
+        x[2 * p] = cc.x * f;
+        x[2 * p + 1] = cc.y * f;
+      }
+      fwht_block<L, 2>(x, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ring[kDecodePrefetch - 1][i] = rw[widx[i]];
-    }
-    uint32_t idx[8];
-    unpack8<BT>(w, sh, Bdyn, idx);
-    float x[16];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const float2 cc = cb[min((int)idx[p], K - 1)];
-      x[2 * p] = cc.x * sg[p];
-      x[2 * p + 1] = cc.y * sg[p];
-    }
-    fwht_block<L>(x, lane);
-    const float rh =
-        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rh_lane), k & (kWave - 1)));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = (x[i] * rh) * g[i];
-    Out::store(stage, lane, co_local, x, out + (int64_t)n * ldo + win * kWinChunks * kChunk, valid_cols);
-  }
+      for (int i = 0; i < 16; ++i) x[i] *= g[i];
+      Out::template store<kFull>(stage, lane, co_local, x, out_win + (int64_t)n * ldo, valid_cols);
+    };
+    auto walk = [&](auto self, auto kc) {
+      constexpr int k = decltype(kc)::value;
+      if constexpr (k < kDecodeMaxRows) {
+        if (k < nrows) {
+          row(k % kDecodePrefetch, k);
+          self(self, std::integral_constant<int, k + 1>());
+        }
+      }
+    };
+    walk(walk, std::integral_constant<int, 0>());
+  };
+  if (valid_cols >= kWinChunks * kChunk)
+    rows(std::integral_constant<bool, true>());
+  else
+    rows(std::integral_constant<bool, false>());
 }
 
 // ===========================================================================
@@ -174,17 +220,26 @@ int launch_decode_bt(const uint32_t* packed, const uint16_t* rho_f16, int N, int
                      const float* sigma, uint64_t seed, const float* cb, int K, int B, int row_words, void* out,
                      int32_t odt, int64_t ldo, hipStream_t st) {
   const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
+  const size_t lds = (size_t)kWavesPerBlock * 256 * 16 + (size_t)kWinChunks * kChunk * sizeof(float) +
+                     (size_t)(BT ? (1 << BT) : K) * sizeof(float2);
   // Persistent-style grid: every workgroup keeps one window (codebook and
-  // column factors loaded once) and walks rows with a stride; about
-  // QAMW_DECODE_WAVES_PER_CU / 4 workgroups per CU in total.
-  const int64_t target_blocks = 256 * QAMW_DECODE_WAVES_PER_CU / kWavesPerBlock;
-  int64_t bpw = target_blocks / nwin;
+  // column factors loaded once) and walks rows with a stride.  Aim for the
+  // workgroups that fit on the chip at once (LDS-limited, at most
+  // QAMW_DECODE_WAVES_PER_CU / 4 per CU), unless that would give a wave more
+  // than kDecodeMaxRows rows: then the stride grows and the grid runs in
+  // several rounds.
+  int64_t per_cu = (int64_t)(160 * 1024 / lds);
+  const int64_t cap = QAMW_DECODE_WAVES_PER_CU / kWavesPerBlock;
+  per_cu = per_cu < 1 ? 1 : (per_cu > cap ? cap : per_cu);
+  int64_t bpw = 256 * per_cu / nwin;
   const int64_t need = (N + kWavesPerBlock - 1) / kWavesPerBlock;   // one row per wave at most
+  const int64_t min_bpw = (N + kWavesPerBlock * kDecodeMaxRows - 1) / (kWavesPerBlock * kDecodeMaxRows);
+  bpw = bpw < min_bpw ? min_bpw : bpw;
   bpw = bpw < 1 ? 1 : (bpw > need ? need : bpw);
+  if ((N + bpw * kWavesPerBlock - 1) / (bpw * kWavesPerBlock) > kDecodeMaxRows)
+    return fail(QAMW_EUNSUPPORTED, "decode: %d rows need more than %d rows per wavefront", N, kDecodeMaxRows);
   const int blocks_per_window = (int)bpw;
   const int64_t blocks = (int64_t)nwin * blocks_per_window;
-  const size_t lds = (size_t)kWavesPerBlock * 256 * 16 + (size_t)kWinChunks * kChunk * sizeof(float) +
-                     (size_t)K * sizeof(float2);
   const dim3 grid((unsigned)blocks), blk(kBlockThreads);
   if (odt == QAMW_F32)
     hipLaunchKernelGGL((decode_kernel<L, BT, StageF32>), grid, blk, lds, st, packed, rho_f16, N, d, s, sigma, seed,

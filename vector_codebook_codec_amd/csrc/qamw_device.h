@@ -153,6 +153,8 @@ __device__ __forceinline__ void wave_lds_fence() {
 // Stage 16 fp32 outputs of chunk `co_local`, store the window contiguously.
 // buf: 256 x 16 bytes of LDS private to the wave.  Columns at or beyond
 // `valid_cols` (relative to the window start) are not written.
+// kFull: the window is known to be whole (valid_cols >= 1024), no test.
+template <bool kFull = false>
 __device__ __forceinline__ void store_window_f32(uint4* buf, int lane, int co_local, const float x[16],
                                                 float* __restrict__ dst, int valid_cols) {
   wave_lds_fence();
@@ -167,14 +169,20 @@ __device__ __forceinline__ void store_window_f32(uint4* buf, int lane, int co_lo
     const int e = v * 256 + lane * 4;          // first column of this lane's piece
     t[v] = buf[stage_slot(e >> 4, (e >> 2) & 3)];
   }
+  if (kFull || valid_cols >= kWinChunks * kChunk) {      // a full window: no per-lane test
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int e = v * 256 + lane * 4;
-    if (e < valid_cols) store16(dst + e, t[v]);
+    for (int v = 0; v < 4; ++v) store16(dst + v * 256 + lane * 4, t[v]);
+  } else {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int e = v * 256 + lane * 4;
+      if (e < valid_cols) store16(dst + e, t[v]);
+    }
   }
 }
 
 // Same for 16-bit outputs (already packed two per word): 32 bytes per lane.
+template <bool kFull = false>
 __device__ __forceinline__ void store_window_b16(uint4* buf, int lane, int co_local, const uint32_t w[8],
                                                  uint16_t* __restrict__ dst, int valid_cols) {
   wave_lds_fence();
@@ -187,40 +195,48 @@ __device__ __forceinline__ void store_window_b16(uint4* buf, int lane, int co_lo
     const int e = v * 512 + lane * 8;          // first column of this lane's piece
     t[v] = buf[stage_slot(e >> 4, (e >> 3) & 1)];
   }
+  if (kFull || valid_cols >= kWinChunks * kChunk) {
 #pragma unroll
-  for (int v = 0; v < 2; ++v) {
-    const int e = v * 512 + lane * 8;
-    if (e < valid_cols) store16(dst + e, t[v]);
+    for (int v = 0; v < 2; ++v) store16(dst + v * 512 + lane * 8, t[v]);
+  } else {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int e = v * 512 + lane * 8;
+      if (e < valid_cols) store16(dst + e, t[v]);
+    }
   }
 }
 
 struct StageF32 {
   using T = float;
+  template <bool kFull = false>
   static __device__ __forceinline__ void store(uint4* buf, int lane, int co_local, const float x[16], float* dst,
                                                int valid_cols) {
-    store_window_f32(buf, lane, co_local, x, dst, valid_cols);
+    store_window_f32<kFull>(buf, lane, co_local, x, dst, valid_cols);
   }
 };
 
 struct StageBF16 {
   using T = uint16_t;
+  template <bool kFull = false>
   static __device__ __forceinline__ void store(uint4* buf, int lane, int co_local, const float x[16], uint16_t* dst,
                                                int valid_cols) {
     uint32_t w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = f32_to_bf16_bits(x[2 * i]) | (f32_to_bf16_bits(x[2 * i + 1]) << 16);
-    store_window_b16(buf, lane, co_local, w, dst, valid_cols);
+    store_window_b16<kFull>(buf, lane, co_local, w, dst, valid_cols);
   }
 };
 
 struct StageF16 {
   using T = uint16_t;
+  template <bool kFull = false>
   static __device__ __forceinline__ void store(uint4* buf, int lane, int co_local, const float x[16], uint16_t* dst,
                                                int valid_cols) {
     uint32_t w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = f32_to_f16_bits(x[2 * i]) | (f32_to_f16_bits(x[2 * i + 1]) << 16);
-    store_window_b16(buf, lane, co_local, w, dst, valid_cols);
+    store_window_b16<kFull>(buf, lane, co_local, w, dst, valid_cols);
   }
 };
 
@@ -349,12 +365,16 @@ __device__ __forceinline__ void lane_stage(float x[16], int a) {
 }
 
 // In-register stages plus the lane network; BlockOut says where each lane's
-// outputs land.  `lane` is the lane index in the wavefront.
-template <int L>
+// outputs land.  `lane` is the lane index in the wavefront.  The stages
+// commute, so a caller whose input already went through the in-register
+// stages below H0 (pairs (x[2p], x[2p+1]) already replaced by their sum and
+// difference, for H0 = 2) starts at H0.
+template <int L, int H0 = 1>
 __device__ __forceinline__ void fwht_block(float x[16], int lane) {
   static_assert(L >= 4 && L <= 10, "block size must be 16..1024");
+  static_assert(H0 == 1 || H0 == 2, "first in-register stage");
 #pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
+  for (int h = H0; h < 16; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if ((i & h) == 0) {
