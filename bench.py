@@ -220,11 +220,15 @@ def main():
         raise RuntimeError("planned and exhaustive encodes disagree")
     exh_ms = float(np.median(exh)) if exh else None
 
-    # decode alone, with HBM caches (L2, MALL) flushed by a 1 GiB write before each rep
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    # decode alone, with the caches (L2, MALL) holding other, clean data: a
+    # 1 GiB read before each rep (a write would leave dirty lines whose
+    # write-back the timed kernel would pay for)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_sum = torch.empty((), dtype=torch.float32, device=dev)
     cold = []
     for _ in range(args.cold_decode_reps):
-        flush.fill_(1.0)
+        torch.sum(flush, out=flush_sum)
+        torch.cuda.synchronize()
         a, z = ev(), ev()
         a.record(stream)
         q.qamw_decode(packed, rn, d, s, sigma, b, wl.sign_seed, Ct, out=out, stream=stream)

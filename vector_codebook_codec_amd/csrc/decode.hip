@@ -56,7 +56,8 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
   // it sink into the row that consumes it.
   extern __shared__ float4 lds4[];
   uint4* stage_all = reinterpret_cast<uint4*>(lds4);    // 4 waves x 256 x 16 bytes
-  float* gwin = reinterpret_cast<float*>(stage_all + kWavesPerBlock * 256);  // kWinChunks * kChunk factors
+  u32x4* pk_all = reinterpret_cast<u32x4*>(stage_all + kWavesPerBlock * 256);   // 4 waves x 64 x 16 bytes
+  float* gwin = reinterpret_cast<float*>(pk_all + kWavesPerBlock * kWave);  // kWinChunks * kChunk factors
   float2* cb = reinterpret_cast<float2*>(gwin + kWinChunks * kChunk);
 
   const int nchunks = d >> 4;
@@ -76,26 +77,30 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
   const int last = nrows > 0 ? nrows - 1 : 0;
 
   // ---- the first rows' loads go out before the LDS prologue, so their
-  // latency overlaps it.  Row loads are unconditional: rows past the wave's
-  // last reload its last row, and lanes past the row end read its last words.
-  // Each ring slot also carries its row's fp16 norm (a uniform load), so the
-  // row loop has no other global loads.
+  // latency overlaps it.  The window's packed bits are 16 B words
+  // (512 pairs x B bits) starting at word win * 16 B of the row, 64-byte
+  // aligned (rows are padded to 16 bytes): lane l loads the 16 bytes at word
+  // win * 16 B + 4 l with one aligned load (lanes past the row's end reload
+  // its last 16 bytes), and at its turn the slot goes through the wave's
+  // LDS slice so that each lane reads the 4 words holding its 8 indices.
+  // Row loads are unconditional: rows past the wave's last reload its last
+  // row.  Each ring slot also carries its row's fp16 norm (a uniform load),
+  // so the row walk has no other global loads.
   const int B = BT ? BT : Bdyn;
+  const int pbase = win * 16 * B;                   // first word of the window's bits
   const int64_t bitstart = (int64_t)c * kPairsPerLane * B;
-  const int wstart = (int)(bitstart >> 5);
   const uint32_t sh = (uint32_t)(bitstart & 31);
-  uint32_t widx[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) widx[i] = (uint32_t)min(wstart + i, row_words - 1);
-  uint32_t ring[kDecodePrefetch][4];   // packed words of the next rows, in flight
+  // this lane's first word, relative to the window; lanes past the row end
+  // read somewhere inside the slice (their results are never stored)
+  const int wl0 = min((int)(bitstart >> 5) - pbase, 4 * kWave - 4);
+  const int u4 = min(pbase / 4 + lane, row_words / 4 - 1);   // this lane's 16-byte load
+  u32x4 ring[kDecodePrefetch];         // packed words of the next rows, in flight
   uint16_t ring_rh[kDecodePrefetch];   // their row norms
   if (nrows > 0) {
 #pragma unroll
     for (int q = 0; q < kDecodePrefetch; ++q) {
       const int n = first + min(q, last) * stride;
-      const uint32_t* rw = packed + (int64_t)n * row_words;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ring[q][i] = rw[widx[i]];
+      ring[q] = reinterpret_cast<const u32x4*>(packed + (int64_t)n * row_words)[u4];
       ring_rh[q] = rho_f16[n];
     }
   }
@@ -170,16 +175,20 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
   // and prefetches issued after it.
   auto rows = [&](auto full) {
     constexpr bool kFull = decltype(full)::value;
+    u32x4* pk = pk_all + wave * kWave;
+    const uint32_t* pkw = reinterpret_cast<const uint32_t*>(pk) + wl0;
     auto row = [&](int q, int k) {
       const int n = first + k * stride;
+      wave_lds_fence();
+      pk[lane] = ring[q];
+      wave_lds_fence();
+      const uint32_t w[4] = {pkw[0], pkw[1], pkw[2], pkw[3]};
       uint32_t idx[8];
-      unpack8<BT>(ring[q], sh, Bdyn, idx);
+      unpack8<BT>(w, sh, Bdyn, idx);
       const float rh = f16_bits_to_f32(ring_rh[q]);
       {   // this slot now takes row k + kDecodePrefetch (or the last row again)
         const int nn = first + min(k + kDecodePrefetch, last) * stride;
-        const uint32_t* rw = packed + (int64_t)nn * row_words;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ring[q][i] = rw[widx[i]];
+        ring[q] = reinterpret_cast<const u32x4*>(packed + (int64_t)nn * row_words)[u4];
         ring_rh[q] = rho_f16[nn];
       }
       float x[16];
@@ -220,7 +229,7 @@ int launch_decode_bt(const uint32_t* packed, const uint16_t* rho_f16, int N, int
                      const float* sigma, uint64_t seed, const float* cb, int K, int B, int row_words, void* out,
                      int32_t odt, int64_t ldo, hipStream_t st) {
   const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
-  const size_t lds = (size_t)kWavesPerBlock * 256 * 16 + (size_t)kWinChunks * kChunk * sizeof(float) +
+  const size_t lds = (size_t)kWavesPerBlock * (256 + kWave) * 16 + (size_t)kWinChunks * kChunk * sizeof(float) +
                      (size_t)(BT ? (1 << BT) : K) * sizeof(float2);
   // Persistent-style grid: every workgroup keeps one window (codebook and
   // column factors loaded once) and walks rows with a stride.  Aim for the
