@@ -80,8 +80,8 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
   // latency overlaps it.  The window's packed bits are 16 B words
   // (512 pairs x B bits) starting at word win * 16 B of the row, 64-byte
   // aligned (rows are padded to 16 bytes): lane l loads the 16 bytes at word
-  // win * 16 B + 4 l with one aligned load (lanes past the row's end reload
-  // its last 16 bytes), and at its turn the slot goes through the wave's
+  // win * 16 B + 4 l with one aligned load (lanes past the window's words or
+  // the row's end reload its last 16 bytes), and at its turn the slot goes through the wave's
   // LDS slice so that each lane reads the 4 words holding its 8 indices.
   // Row loads are unconditional: rows past the wave's last reload its last
   // row.  Each ring slot also carries its row's fp16 norm (a uniform load),
@@ -93,7 +93,9 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
   // this lane's first word, relative to the window; lanes past the row end
   // read somewhere inside the slice (their results are never stored)
   const int wl0 = min((int)(bitstart >> 5) - pbase, 4 * kWave - 4);
-  const int u4 = min(pbase / 4 + lane, row_words / 4 - 1);   // this lane's 16-byte load
+  // this lane's 16-byte load; lanes past the window's 4 B words repeat the
+  // last one (same address: no extra traffic)
+  const int u4 = min(pbase / 4 + min(lane, 4 * B - 1), row_words / 4 - 1);
   u32x4 ring[kDecodePrefetch];         // packed words of the next rows, in flight
   uint16_t ring_rh[kDecodePrefetch];   // their row norms
   if (nrows > 0) {
