@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kBlockThreads) void encode_prepare_kernel(
 }
 
 template <int L, typename Tin>
-__global__ __launch_bounds__(kEncThreads) void encode_kernel(
+__global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))) void encode_kernel(
     const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ f,
     const float* __restrict__ isig, const float* __restrict__ codebook, int K, int Kpad,
     int B, int row_words, const double* __restrict__ rho, uint32_t* __restrict__ packed) {
