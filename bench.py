@@ -266,6 +266,40 @@ def main():
         cold.append(a.elapsed_time(z))
     dec_cold_ms = float(np.median(cold)) if cold else None
 
+    # decode to 16-bit outputs (the fused decode -> fp16 / bf16 of the
+    # 11008 x 4096 configuration's transpose), warm and cold
+    dec16 = {}
+    for name, tdt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
+        out16 = torch.empty((N, d), dtype=tdt, device=dev)
+        run16 = lambda: q.qamw_decode(packed, rn, d, s, sigma, b, wl.sign_seed, Ct, out=out16, stream=stream)
+        run16()
+        torch.cuda.synchronize()
+        # against the fp32 decode rounded (RNE) to 16 bits: the kernel rounds the
+        # last product straight to fp16 (one rounding), so at exact fp16 ties of
+        # the fp32 value the two may differ by one unit in the last place
+        ref16 = out.to(tdt)
+        dbits = (out16.view(torch.int16).int() - ref16.view(torch.int16).int()).abs()
+        if int(dbits.max()) > 1:
+            raise RuntimeError(f"{name} decode differs from the rounded fp32 decode by more than one ulp")
+        n_ulp = int((dbits != 0).sum())
+        warm16, cold16 = [], []
+        for rep in range(2 * max(1, args.cold_decode_reps)):
+            is_cold = rep % 2 == 1
+            if is_cold:
+                torch.sum(flush, dim=0, out=flush_sum)
+            torch.cuda.synchronize()
+            a, z = ev(), ev()
+            a.record(stream)
+            run16()
+            z.record(stream)
+            torch.cuda.synchronize()
+            (cold16 if is_cold else warm16).append(a.elapsed_time(z))
+        nb16 = N * d * 2 + N * rw * 4 + N * 2
+        dec16[name] = {"warm_ms": float(np.median(warm16)), "cold_ms": float(np.median(cold16)),
+                       "algorithmic_bytes": nb16, "one_ulp_from_rounded_f32": n_ulp,
+                       "frac_hbm_cold": nb16 / (np.median(cold16) * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del out16
+
     # fused decoded-weight matmul Y = X W^^T for T tokens (not part of the step)
     mm = {}
     for T in args.matmul_tokens:
@@ -509,6 +543,7 @@ def main():
                                       "bit); encode_prepare repeats the row-norm pass"},
         "encode_gweights_s": weights / ((plan_ms + ce_ms) * 1e-3) / 1e9,
         "decode_gweights_s": weights / (dec_ms * 1e-3) / 1e9,
+        "decode_16bit": dec16,
         "decode_cold": None if dec_cold_ms is None else {
             "ms": dec_cold_ms, "algorithmic_bytes": dec_bytes,
             "GB_s": dec_bytes / (dec_cold_ms * 1e-3) / 1e9,

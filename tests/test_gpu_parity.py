@@ -322,7 +322,8 @@ def test_repeatable_bitwise(q):
 
 # ---------------------------------------------------------------- full-size workloads
 FULL = ["c2_4096x4096", "c3_11008x4096", "c3t_4096x11008", "c4_5120x13824_K256_a0",
-        "c4_5120x13824_K4096_a0.5"]
+        "c4_5120x13824_K1024_a0.5", "c4_5120x13824_K2048_a0", "c4_5120x13824_K4096_a0.5",
+        "c5_l0_q", "c5_l17_down", "c5_l31_gate"]
 
 
 @pytest.mark.parametrize("name", FULL)
