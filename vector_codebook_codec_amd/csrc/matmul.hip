@@ -287,16 +287,69 @@ __global__ __launch_bounds__(mm_waves<TT>() * kWave) void decode_matmul_kernel(
 // rho^_n sum_k (u_k.x C[idx_nk].x + u_k.y C[idx_nk].y) with u_k = sigma_k
 // (xr_2k, xr_2k+1), all fp32.  Wavefront w of a workgroup owns the column
 // slices w, w + W, ... of 512 pairs (lane l: pairs 8 l .. 8 l + 7 of the
-// slice, one byte-aligned run of 8 B bits); its u stays in registers while it
-// walks the workgroup's 8 rows, whose packed bits it loads all at once
-// (clamped: words past a row end only feed unused bits, rows past N reload
-// the last one).  Per row the lane's fp32 dot product is summed across the
-// wavefront by a fixed butterfly; the slices' sums are added in wavefront
-// order through LDS.  Deterministic.
+// slice, one byte-aligned run of 8 B bits) for the workgroup's 8 rows.
+//
+// Memory: a slice's packed bits are 16 B words starting at word 16 B sl of
+// the row, 64-byte aligned (rows are padded to 16 bytes), so each row's slice
+// is fetched by one aligned 16-byte load per lane (lanes past the slice's
+// 4 B loads, or past the row end, repeat the last one), and handed to the
+// lanes through the wave's 1 KB LDS slice.  The first slice's packed loads
+// are issued before the codebook is staged in LDS, so the two latencies
+// overlap (rows longer than 16 slices load their later slices in turn); the
+// slice's activations and sigma, shared by all workgroups and cache-resident,
+// are loaded after the barrier, which keeps two workgroups per CU.  With
+// the index width fixed at compile time the table is padded to 2^B entries
+// (zeros past K), so lookups need no clamp.
+//
+// Sums: each lane keeps its 8 rows' fp32 partials over all its slices; a
+// reduce-scatter across the wavefront (halving the set of rows at each of
+// the first three exchange steps) leaves row r's total in lanes 8 r .. 8 r + 7
+// after 10 exchanges instead of 8 x 6; the wavefronts' totals are added in
+// wavefront order through LDS.  Deterministic.
 // ---------------------------------------------------------------------------
 constexpr int kGvRows = 8;
 constexpr int kGvSlice = 512;
 constexpr int kGvMaxWaves = 16;
+
+// Sum 8 per-lane values (one per row) across the wavefront: a reduce-scatter
+// that halves the set of rows at the exchanges at distances 32, 16 and 8,
+// then a butterfly over the last 8 lanes.  Returns row `row`'s total, which
+// lanes 8 row .. 8 row + 7 hold, row = lane bits 5, 4, 3.  10 exchanges
+// instead of 8 x 6; fixed order, deterministic.
+__device__ __forceinline__ float reduce_rows8(const float acc[8], int lane, int& row) {
+  float v4[4], v2[2];
+  {
+    const bool hi = (lane & 32) != 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float send = hi ? acc[i] : acc[i + 4];
+      const float keep = hi ? acc[i + 4] : acc[i];
+      v4[i] = keep + __shfl_xor(send, 32);
+    }
+  }
+  {
+    const bool hi = (lane & 16) != 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float send = hi ? v4[i] : v4[i + 2];
+      const float keep = hi ? v4[i + 2] : v4[i];
+      v2[i] = keep + __shfl_xor(send, 16);
+    }
+  }
+  const bool hi = (lane & 8) != 0;
+  float v1 = (hi ? v2[1] : v2[0]) + __shfl_xor(hi ? v2[0] : v2[1], 8);
+  v1 += __shfl_xor(v1, 4);
+  v1 += __shfl_xor(v1, 2);
+  v1 += __shfl_xor(v1, 1);
+  row = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+  return v1;
+}
+
+struct GvLoads {
+  uint4 xa, xb;            // 16 bf16 rotated activations
+  float4 s0, s1;           // 8 sigma_k
+  u32x4 rw[kGvRows];       // the rows' 16-byte pieces of the slice
+};
 
 template <int BT, typename Out>
 __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_gemv_kernel(
@@ -304,68 +357,93 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_gemv_kernel(
     const uint16_t* __restrict__ rho_f16, int N, const float* __restrict__ sigma,
     const float* __restrict__ codebook, int K, int Bdyn, typename Out::T* __restrict__ Y) {
   extern __shared__ float4 lds4[];
+  const int kp = BT ? (1 << BT) : K;                                 // table entries
   float2* cb = reinterpret_cast<float2*>(lds4);
-  float* part = reinterpret_cast<float*>(cb + ((K + 1) & ~1));      // [waves][kGvRows]
-  for (int c = threadIdx.x; c < K; c += blockDim.x) cb[c] = make_float2(codebook[2 * c], codebook[2 * c + 1]);
-  __syncthreads();
-
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  u32x4* pk_all = reinterpret_cast<u32x4*>(cb + ((kp + 1) & ~1));   // [waves][64] 16-byte slots
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  float* part = reinterpret_cast<float*>(pk_all + nw * kWave);       // [waves][kGvRows]
   const int B = BT ? BT : Bdyn;
   const int half_d = d >> 1;
   const int nslices = (half_d + kGvSlice - 1) / kGvSlice;
   const int n0 = blockIdx.x * kGvRows;
-  const uint32_t* prow[kGvRows];
+  const int lane_u4 = min(lane, 4 * B - 1);
+  const int last_u4 = row_words / 4 - 1;
+
+  // unconditional loads from clamped addresses: the rows' packed pieces
+  // (from HBM) and the slice's activations and sigma (small, cache-resident)
+  auto load_packed = [&](int sl, GvLoads& g) {
+    const int u4 = min(sl * 4 * B + lane_u4, last_u4);
 #pragma unroll
-  for (int r = 0; r < kGvRows; ++r) prow[r] = packed + (int64_t)min(n0 + r, N - 1) * row_words;
+    for (int r = 0; r < kGvRows; ++r)
+      g.rw[r] = reinterpret_cast<const u32x4*>(packed + (int64_t)min(n0 + r, N - 1) * row_words)[u4];
+  };
+  auto load_x = [&](int sl, GvLoads& g) {
+    const int p0 = min(sl * kGvSlice + 8 * lane, half_d - 8);
+    g.xa = *reinterpret_cast<const uint4*>(Xr + 2 * p0);
+    g.xb = *reinterpret_cast<const uint4*>(Xr + 2 * p0 + 8);
+    g.s0 = *reinterpret_cast<const float4*>(sigma + p0);
+    g.s1 = *reinterpret_cast<const float4*>(sigma + p0 + 4);
+  };
+
+  GvLoads cur;
+  load_packed(wave, cur);                // wave < nw <= nslices
+
+  {   // the codebook, padded: 2 centroids per float4
+    const float4* cb4 = reinterpret_cast<const float4*>(codebook);
+    float4* cbl = reinterpret_cast<float4*>(cb);
+    for (int c = threadIdx.x; c < (K >> 1); c += blockDim.x) cbl[c] = cb4[c];
+    if ((K & 1) && threadIdx.x == 0) cb[K - 1] = make_float2(codebook[2 * (K - 1)], codebook[2 * (K - 1) + 1]);
+    if constexpr (BT > 0)
+      for (int c = K + (int)threadIdx.x; c < kp; c += blockDim.x) cb[c] = make_float2(0.0f, 0.0f);
+  }
+  __syncthreads();
+
+  u32x4* pk = pk_all + wave * kWave;
+  const uint32_t lbit = (uint32_t)(8 * lane * B);        // the lane's first bit within the slice
+  const uint32_t sh = lbit & 31u;
+  const uint32_t* pkw = reinterpret_cast<const uint32_t*>(pk) + min((int)(lbit >> 5), 4 * kWave - 4);
   float rowacc[kGvRows];
 #pragma unroll
   for (int r = 0; r < kGvRows; ++r) rowacc[r] = 0.0f;
 
   for (int sl = wave; sl < nslices; sl += nw) {
-    const int p0 = sl * kGvSlice + 8 * lane;
-    const bool act = p0 < half_d;                  // half_d % 8 == 0: all 8 pairs in or out
-    const int pc = act ? p0 : 0;
+    if (sl != wave) load_packed(sl, cur);   // later slices (d > 16384 only): loaded in turn
+    load_x(sl, cur);
+    const bool act = sl * kGvSlice + 8 * lane < half_d;   // half_d % 8 == 0: all 8 pairs in or out
     float ux[8], uy[8];
     {
-      const uint4 xa = *reinterpret_cast<const uint4*>(Xr + 2 * pc);
-      const uint4 xb = *reinterpret_cast<const uint4*>(Xr + 2 * pc + 8);
-      const float4 s0 = *reinterpret_cast<const float4*>(sigma + pc);
-      const float4 s1 = *reinterpret_cast<const float4*>(sigma + pc + 4);
-      const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-      const float sg[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      const uint32_t xw[8] = {cur.xa.x, cur.xa.y, cur.xa.z, cur.xa.w, cur.xb.x, cur.xb.y, cur.xb.z, cur.xb.w};
+      const float sg[8] = {cur.s0.x, cur.s0.y, cur.s0.z, cur.s0.w, cur.s1.x, cur.s1.y, cur.s1.z, cur.s1.w};
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         ux[p] = act ? sg[p] * bf16_bits_to_f32(xw[p] & 0xffffu) : 0.0f;
         uy[p] = act ? sg[p] * bf16_bits_to_f32(xw[p] >> 16) : 0.0f;
       }
     }
-    const int64_t bit = (int64_t)pc * B;
-    const int w0 = (int)(bit >> 5);
-    const uint32_t sh = (uint32_t)(bit & 31);
-    uint32_t w[kGvRows][4];
-#pragma unroll
-    for (int r = 0; r < kGvRows; ++r)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[r][i] = prow[r][min(w0 + i, row_words - 1)];
 #pragma unroll
     for (int r = 0; r < kGvRows; ++r) {
+      wave_lds_fence();
+      pk[lane] = cur.rw[r];
+      wave_lds_fence();
+      const uint32_t w[4] = {pkw[0], pkw[1], pkw[2], pkw[3]};
       uint32_t idx[8];
-      unpack8<BT>(w[r], sh, Bdyn, idx);
+      unpack8<BT>(w, sh, Bdyn, idx);
       float acc = 0.0f;
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        const float2 cc = cb[min((int)idx[p], K - 1)];
+        const float2 cc = cb[BT ? (int)idx[p] : min((int)idx[p], K - 1)];
         acc = __builtin_fmaf(ux[p], cc.x, acc);
         acc = __builtin_fmaf(uy[p], cc.y, acc);
       }
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
       rowacc[r] += acc;
     }
   }
-  if (lane == 0)
-#pragma unroll
-    for (int r = 0; r < kGvRows; ++r) part[wave * kGvRows + r] = rowacc[r];
+
+  int myrow;
+  const float v1 = reduce_rows8(rowacc, lane, myrow);
+  if ((lane & 7) == 0) part[wave * kGvRows + myrow] = v1;
   __syncthreads();
   if ((int)threadIdx.x < kGvRows) {
     const int n = n0 + threadIdx.x;
@@ -384,7 +462,9 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_gemv_kernel(
 // s_j), the block FWHT) in registers; afterwards lane l holds the 8 pairs of
 // window chunk BlockOut(l) and decodes exactly those pairs -- the same
 // products as qamw_rotate_activations + qamw_decode_matmul, with the rotated
-// activations kept in fp32 instead of rounded to bf16.  Otherwise as
+// activations kept in fp32 instead of rounded to bf16.  The packed loads go
+// out first, so the codebook staging and the rotation of x (x, s and sigma
+// are small and cache-resident) overlap their latency.  Otherwise as
 // decode_gemv_kernel (index width at run time: this kernel waits on memory,
 // not on arithmetic).
 // ---------------------------------------------------------------------------
@@ -396,80 +476,101 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_matvec_kernel(
     typename Out::T* __restrict__ Y) {
   extern __shared__ float4 lds4[];
   float2* cb = reinterpret_cast<float2*>(lds4);
-  float* part = reinterpret_cast<float*>(cb + ((K + 1) & ~1));      // [waves][kGvRows]
-  for (int c = threadIdx.x; c < K; c += blockDim.x) cb[c] = make_float2(codebook[2 * c], codebook[2 * c + 1]);
-  __syncthreads();
-
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  u32x4* pk_all = reinterpret_cast<u32x4*>(cb + ((K + 1) & ~1));    // [waves][64] 16-byte slots
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  float* part = reinterpret_cast<float*>(pk_all + nw * kWave);       // [waves][kGvRows]
   const int nchunks = d >> 4;
   const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
   const int n0 = blockIdx.x * kGvRows;
   const float inv_sqrt_b = (float)(1.0 / sqrt((double)(1 << L)));
-  const uint32_t* prow[kGvRows];
+  const int lane_u4 = min(lane, 4 * B - 1);
+  const int last_u4 = row_words / 4 - 1;
+
+  // the window's packed pieces of the 8 rows (as in the GEMV), issued before
+  // the codebook is staged
+  u32x4 rw[kGvRows];
+  auto load_packed = [&](int win) {
+    const int u4 = min(win * 4 * B + lane_u4, last_u4);
 #pragma unroll
-  for (int r = 0; r < kGvRows; ++r) prow[r] = packed + (int64_t)min(n0 + r, N - 1) * row_words;
+    for (int r = 0; r < kGvRows; ++r)
+      rw[r] = reinterpret_cast<const u32x4*>(packed + (int64_t)min(n0 + r, N - 1) * row_words)[u4];
+  };
+  load_packed(wave);                     // wave < nw <= nwin
+  {
+    const float4* cb4 = reinterpret_cast<const float4*>(codebook);
+    float4* cbl = reinterpret_cast<float4*>(cb);
+    for (int c = threadIdx.x; c < (K >> 1); c += blockDim.x) cbl[c] = cb4[c];
+    if ((K & 1) && threadIdx.x == 0) cb[K - 1] = make_float2(codebook[2 * (K - 1)], codebook[2 * (K - 1) + 1]);
+  }
+  __syncthreads();
+
+  u32x4* pk = pk_all + wave * kWave;
+  const int co_local = BlockOut<L>::chunk(lane);   // the chunk this lane holds after the rotation
+  const float osign = BlockOut<L>::sign(lane);
+  const uint32_t lbit = (uint32_t)(co_local * kPairsPerLane * B);   // its first bit within the window
+  const uint32_t sh = lbit & 31u;
+  const uint32_t* pkw = reinterpret_cast<const uint32_t*>(pk) + min((int)(lbit >> 5), 4 * kWave - 4);
   float rowacc[kGvRows];
 #pragma unroll
   for (int r = 0; r < kGvRows; ++r) rowacc[r] = 0.0f;
 
   for (int win = wave; win < nwin; win += nw) {
+    if (win != wave) load_packed(win);   // rows longer than 16 windows: later windows in turn
     const int c = win * kWinChunks + lane;
     const bool active = c < nchunks;               // whole Hadamard blocks are active or not
-    const int cl = active ? c : 0;
+    const int cl = active ? c : nchunks - 1;
+    const int pc = (win * kWinChunks + co_local) * kPairsPerLane;
+    const int pcl = active ? pc : 0;
     float x[16];
     {
       RawChunk<Tin> raw;
       raw.load(X + cl * kChunk);
+      float sv[16];
+      if (s) {
+        load_chunk(s + cl * kChunk, sv);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[i] = 1.0f;
+      }
+      const float4 s0 = *reinterpret_cast<const float4*>(sigma + pcl);
+      const float4 s1 = *reinterpret_cast<const float4*>(sigma + pcl + 4);
       raw.unpack(x);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int j = cl * kChunk + i;
-        const float g = sign_eps(seed, (uint32_t)j) * (inv_sqrt_b / (s ? s[j] : 1.0f));
+        const float g = sign_eps(seed, (uint32_t)(cl * kChunk + i)) * (inv_sqrt_b / sv[i]);
         x[i] = active ? x[i] * g : 0.0f;
       }
-    }
-    fwht_block<L>(x, lane);
-    const int co = win * kWinChunks + BlockOut<L>::chunk(lane);   // the chunk this lane now holds
-    const float osign = BlockOut<L>::sign(lane);
-    const int pc = active ? co * kPairsPerLane : 0;
-    float ux[8], uy[8];
-    {
-      const float4 s0 = *reinterpret_cast<const float4*>(sigma + pc);
-      const float4 s1 = *reinterpret_cast<const float4*>(sigma + pc + 4);
+      fwht_block<L>(x, lane);
       const float sg[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        ux[p] = active ? sg[p] * (x[2 * p] * osign) : 0.0f;
-        uy[p] = active ? sg[p] * (x[2 * p + 1] * osign) : 0.0f;
+        x[2 * p] = active ? sg[p] * (x[2 * p] * osign) : 0.0f;
+        x[2 * p + 1] = active ? sg[p] * (x[2 * p + 1] * osign) : 0.0f;
       }
     }
-    const int64_t bit = (int64_t)pc * B;
-    const int w0 = (int)(bit >> 5);
-    const uint32_t sh = (uint32_t)(bit & 31);
-    uint32_t w[kGvRows][4];
-#pragma unroll
-    for (int r = 0; r < kGvRows; ++r)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[r][i] = prow[r][min(w0 + i, row_words - 1)];
 #pragma unroll
     for (int r = 0; r < kGvRows; ++r) {
+      wave_lds_fence();
+      pk[lane] = rw[r];
+      wave_lds_fence();
+      const uint32_t w[4] = {pkw[0], pkw[1], pkw[2], pkw[3]};
       uint32_t idx[8];
-      unpack8<0>(w[r], sh, B, idx);
+      unpack8<0>(w, sh, B, idx);
       float acc = 0.0f;
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         const float2 cc = cb[min((int)idx[p], K - 1)];
-        acc = __builtin_fmaf(ux[p], cc.x, acc);
-        acc = __builtin_fmaf(uy[p], cc.y, acc);
+        acc = __builtin_fmaf(x[2 * p], cc.x, acc);
+        acc = __builtin_fmaf(x[2 * p + 1], cc.y, acc);
       }
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
       rowacc[r] += acc;
     }
   }
-  if (lane == 0)
-#pragma unroll
-    for (int r = 0; r < kGvRows; ++r) part[wave * kGvRows + r] = rowacc[r];
+  int myrow;
+  const float v1 = reduce_rows8(rowacc, lane, myrow);
+  if ((lane & 7) == 0) part[wave * kGvRows + myrow] = v1;
   __syncthreads();
   if ((int)threadIdx.x < kGvRows) {
     const int n = n0 + threadIdx.x;
@@ -530,7 +631,9 @@ static int launch_gemv(const uint16_t* Xr, int d, const uint32_t* packed, int ro
   const int nslices = (d / 2 + kGvSlice - 1) / kGvSlice;
   const int nw = nslices < kGvMaxWaves ? nslices : kGvMaxWaves;
   const dim3 grid((unsigned)((N + kGvRows - 1) / kGvRows)), blk((unsigned)(nw * kWave));
-  const size_t lds = (size_t)((K + 1) & ~1) * sizeof(float2) + (size_t)nw * kGvRows * sizeof(float);
+  const int kp = BT ? (1 << BT) : K;
+  const size_t lds = (size_t)((kp + 1) & ~1) * sizeof(float2) + (size_t)nw * kWave * 16 +
+                     (size_t)nw * kGvRows * sizeof(float);
   if (ydt == QAMW_F32)
     hipLaunchKernelGGL((decode_gemv_kernel<BT, OutF32>), grid, blk, lds, st, Xr, d, packed, row_words, rn, N, sigma,
                        cb, K, B, (float*)Y);
@@ -560,7 +663,8 @@ struct LaunchMatvec {
     const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
     const int nw = nwin < kGvMaxWaves ? nwin : kGvMaxWaves;
     const dim3 grid((unsigned)((N + kGvRows - 1) / kGvRows)), blk((unsigned)(nw * kWave));
-    const size_t lds = (size_t)((K + 1) & ~1) * sizeof(float2) + (size_t)nw * kGvRows * sizeof(float);
+    const size_t lds = (size_t)((K + 1) & ~1) * sizeof(float2) + (size_t)nw * kWave * 16 +
+                       (size_t)nw * kGvRows * sizeof(float);
 #define QAMW_MV(TIN, OUT, YT)                                                                                    \
   hipLaunchKernelGGL((decode_matvec_kernel<L, TIN, OUT>), grid, blk, lds, st, (const TIN*)X, d, s, seed, packed, \
                      row_words, rn, N, sigma, cb, K, B, (YT*)Y)
