@@ -172,7 +172,7 @@ def main():
     # checks and launch calls are done once, at capture).  The same step
     # launched eagerly is timed too, for the per-entry split and as
     # `eager_ms_per_step`.
-    for i in range(args.warmup):
+    for i in range(max(1, args.warmup)):   # at least one eager step: the replays' reference
         step()
     torch.cuda.synchronize()
     ref_out = [t.clone() for t in (s, sigma, packed, rn, out)]
