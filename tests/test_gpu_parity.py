@@ -271,12 +271,15 @@ def test_all_zero_matrix(q):
     assert np.all(O.unpack(packed.cpu().numpy().view(np.uint32), K, d) == origin[0])
 
 
-def test_out_of_range_indices_clamp(q):
+@pytest.mark.parametrize("K", [5, 200, 1000])   # B = 3 (width at run time), 8 and 10 (compile time)
+def test_out_of_range_indices_clamp(q, K):
     """A hand-made stream with indices >= K decodes as K - 1."""
-    N, d, b, K = 2, 64, 32, 5          # B = 3, so 5..7 are representable
-    C = q.load_codebook(16)[:K].copy()
-    rng = np.random.default_rng(3)
-    idx = rng.integers(0, 8, size=(N, d // 2))
+    N, d, b = 2, 64, 32
+    C = q.load_codebook(1024 if K > 16 else 16)[:K].copy()
+    B = O.index_bits(K)
+    rng = np.random.default_rng(3 + K)
+    idx = rng.integers(0, 1 << B, size=(N, d // 2))
+    idx[:, :4] = (1 << B) - 1                                # the largest index is always present
     packed = O.pack(idx, K, d)
     rn = O.to_f16_bits(np.array([1.0, 0.5]))
     sig = np.full(d // 2, 0.1, np.float32)
@@ -286,6 +289,14 @@ def test_out_of_range_indices_clamp(q):
     torch.cuda.synchronize()
     ref = O.decode(packed, rn, s, sig, b, 4, C, d)
     assert float(np.max(np.abs(Wh.cpu().numpy() - ref))) <= 1e-6
+    # the one-token product reads the same stream: indices >= K act as K - 1
+    x = rng.standard_normal(d).astype(np.float32)
+    Xr = q.qamw_rotate_activations(dev(np.ascontiguousarray(x[None, :])), dev(s), b, 4)
+    y = q.qamw_decode_matmul(Xr, dev(packed.view(np.int32)), dev(rn.view(np.int16)), dev(sig), dev(C))
+    torch.cuda.synchronize()
+    y_ref = Wh.double() @ torch.from_numpy(x.astype(np.float64)).to(DEV)
+    S = float((Wh.abs().double() @ torch.from_numpy(np.abs(x).astype(np.float64)).to(DEV)).max())
+    assert float((y[0].double() - y_ref).abs().max()) <= 2.0 ** -7 * S + 1e-6
 
 
 def test_exact_ties_lowest_index(q):

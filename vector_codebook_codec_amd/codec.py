@@ -42,9 +42,11 @@ def _vec(t: torch.Tensor, name: str, n: int, dtype=torch.float32) -> None:
 
 def _rows(W: torch.Tensor, name: str):
     _dev(W, name)
-    if W.dim() != 2 or W.stride(1) != 1:
+    if W.dim() != 2 or (W.stride(1) != 1 and W.shape[1] > 1):
         raise ValueError(f"{name} must be 2-D with unit column stride")
-    return W.shape[0], W.shape[1], W.stride(0)
+    # a single row's leading stride is arbitrary (torch and NumPy leave it so):
+    # the row length is then its row pitch
+    return W.shape[0], W.shape[1], (W.stride(0) if W.shape[0] > 1 else W.shape[1])
 
 
 # ---------------------------------------------------------------- host helpers

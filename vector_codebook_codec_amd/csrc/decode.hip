@@ -41,7 +41,8 @@ constexpr int kDecodeMaxRows = 16;   // rows per wavefront, at most
 // (y_2k, y_2k+1), so it is folded into the table and the transform starts
 // at its second stage.  The row norm is folded into the pair scales.
 // BT > 0 fixes the index width at compile time and pads the table to 2^BT
-// entries (zeros past K), so any B-bit index reads inside it without a clamp;
+// entries, those past K repeating centroid K - 1, so any B-bit index reads
+// inside it and indices >= K decode as K - 1 without a clamp instruction;
 // BT = 0 takes the width B from the argument and clamps indices to K - 1.
 // ---------------------------------------------------------------------------
 template <int L, int BT, typename Out>
@@ -132,8 +133,10 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
       const float cx = codebook[2 * (K - 1)], cy = codebook[2 * (K - 1) + 1];
       cb[K - 1] = make_float2(cx + cy, cx - cy);
     }
-    if constexpr (BT > 0)
-      for (int cc = K + (int)threadIdx.x; cc < (1 << BT); cc += kBlockThreads) cb[cc] = make_float2(0.0f, 0.0f);
+    if constexpr (BT > 0) {   // entries past K repeat centroid K - 1: the clamp, without an instruction
+      const float cx = codebook[2 * (K - 1)], cy = codebook[2 * (K - 1) + 1];
+      for (int cc = K + (int)threadIdx.x; cc < (1 << BT); cc += kBlockThreads) cb[cc] = make_float2(cx + cy, cx - cy);
+    }
     const float inv_sqrt_b = (float)(1.0 / sqrt((double)(1 << L)));
     constexpr int kPer = kWinChunks * kChunk / kBlockThreads;   // 4
     float sv[kPer];

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(mm_waves<TT>() * kWave) void decode_matmul_kernel(
 // slice's activations and sigma, shared by all workgroups and cache-resident,
 // are loaded after the barrier, which keeps two workgroups per CU.  With
 // the index width fixed at compile time the table is padded to 2^B entries
-// (zeros past K), so lookups need no clamp.
+// repeating centroid K - 1, so indices >= K act as K - 1 without a clamp.
 //
 // Sums: each lane keeps its 8 rows' fp32 partials over all its slices; a
 // reduce-scatter across the wavefront (halving the set of rows at each of
@@ -395,8 +395,10 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_gemv_kernel(
     float4* cbl = reinterpret_cast<float4*>(cb);
     for (int c = threadIdx.x; c < (K >> 1); c += blockDim.x) cbl[c] = cb4[c];
     if ((K & 1) && threadIdx.x == 0) cb[K - 1] = make_float2(codebook[2 * (K - 1)], codebook[2 * (K - 1) + 1]);
-    if constexpr (BT > 0)
-      for (int c = K + (int)threadIdx.x; c < kp; c += blockDim.x) cb[c] = make_float2(0.0f, 0.0f);
+    if constexpr (BT > 0) {   // entries past K repeat centroid K - 1 (the clamp)
+      const float2 last = make_float2(codebook[2 * (K - 1)], codebook[2 * (K - 1) + 1]);
+      for (int c = K + (int)threadIdx.x; c < kp; c += blockDim.x) cb[c] = last;
+    }
   }
   __syncthreads();
 
