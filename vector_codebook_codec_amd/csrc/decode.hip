@@ -31,10 +31,10 @@ constexpr int kDecodeMaxRows = 16;   // rows per wavefront, at most
 // window, wave n mod 4), so the codebook and the window's column factors
 // g_j = eps_j / (sqrt(b) s_j) are staged in LDS once per workgroup, with all
 // prologue loads in flight together.  Each lane keeps its 8 sigma_k and 16
-// factors in registers, holds the row norms of 64 rows at a time (one per
-// lane), and keeps the packed words of the next kDecodePrefetch rows in
-// flight in a ring of named slots (the row loop is unrolled by the ring
-// length, so slots never move between registers).
+// factors in registers; the packed words (and fp16 norm) of the next
+// kDecodePrefetch rows stay in flight in a ring of named register slots.  A
+// wavefront has at most kDecodeMaxRows rows and walks them as straight-line
+// code (see the walk below).
 //
 // The LDS codebook holds each centroid as (c_x + c_y, c_x - c_y): the first
 // in-register butterfly of the inverse rotation acts on exactly the pair
