@@ -325,8 +325,10 @@ int32_t qamw_decode_matvec(const void* x, int32_t xdtype, int64_t d, const float
  *   s          [d] float32 or NULL.  With s the output approximates W; with
  *              NULL it approximates W' = W diag(s) (scales folded elsewhere)
  *   sigma      [d/2] float32
- *   W_out      [N][ldo] of out_dtype (QAMW_F32, QAMW_BF16 or QAMW_F16; the
- *              16-bit types are rounded to nearest even from fp32)
+ *   W_out      [N][ldo] of out_dtype (QAMW_F32, QAMW_BF16 or QAMW_F16; bf16
+ *              is rounded to nearest even from the fp32 value, fp16 from the
+ *              exact product of the last fp32 scale, in one rounding, which
+ *              can differ from rounding the fp32 value by one unit at ties)
  * Arithmetic is fp32.
  */
 int32_t qamw_decode(const uint32_t* packed, const uint16_t* rownorm_f16, int64_t N, int64_t d,
@@ -356,9 +358,10 @@ int32_t qamw_decode(const uint32_t* packed, const uint16_t* rownorm_f16, int64_t
  *   Y          [T][ldy] of ydtype (QAMW_F32 or QAMW_BF16), ldy >= N
  * Products use bf16 operands (the looked-up y^ and Xr, rounded to nearest
  * even) on bf16 MFMA with fp32 accumulation; each output is within
- * 2^-7 rho^_n sum_k |Xr[t][k] y^_n[k]| of the exact product.  The sum over
- * columns is split into a fixed number of parts added in a fixed order, so
- * results are deterministic.
+ * 2^-7 rho^_n sum_k |Xr[t][k] y^_n[k]| of the exact product.  With T = 1 the
+ * product runs as a GEMV in fp32 (y^ not rounded; Xr is bf16), inside the
+ * same bound.  The sum over columns is split into a fixed number of parts
+ * added in a fixed order, so results are deterministic.
  */
 int32_t qamw_rotate_activations(const void* X, int32_t xdtype, int64_t T, int64_t d, int64_t ldx,
                                 const float* s, int32_t block, uint64_t sign_seed,
