@@ -311,38 +311,34 @@ constexpr int kGvRows = 8;
 constexpr int kGvSlice = 512;
 constexpr int kGvMaxWaves = 16;
 
-// Sum 8 per-lane values (one per row) across the wavefront: a reduce-scatter
-// that halves the set of rows at the exchanges at distances 32, 16 and 8,
-// then a butterfly over the last 8 lanes.  Returns row `row`'s total, which
-// lanes 8 row .. 8 row + 7 hold, row = lane bits 5, 4, 3.  10 exchanges
-// instead of 8 x 6; fixed order, deterministic.
-__device__ __forceinline__ float reduce_rows8(const float acc[8], int lane, int& row) {
-  float v4[4], v2[2];
-  {
-    const bool hi = (lane & 32) != 0;
+// Sum R per-lane values (one per row, R = 8 or 16) across the wavefront: a
+// reduce-scatter that halves the set of rows at each exchange at distances
+// 32, 16, ... until one row is left, then a butterfly over the lanes that
+// share it.  Returns row `row`'s total, which lanes (64 / R) row .. + 64 / R
+// - 1 hold (row = the lane's top log2(R) bits, taken in that order).  R - 1
+// + log2(64 / R) exchanges instead of 6 R; fixed order, deterministic.
+template <int R>
+__device__ __forceinline__ float reduce_rows(const float acc[R], int lane, int& row) {
+  static_assert(R == 8 || R == 16, "rows per reduction");
+  float v[R];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float send = hi ? acc[i] : acc[i + 4];
-      const float keep = hi ? acc[i + 4] : acc[i];
-      v4[i] = keep + __shfl_xor(send, 32);
-    }
-  }
-  {
-    const bool hi = (lane & 16) != 0;
+  for (int i = 0; i < R; ++i) v[i] = acc[i];
+  row = 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float send = hi ? v4[i] : v4[i + 2];
-      const float keep = hi ? v4[i + 2] : v4[i];
-      v2[i] = keep + __shfl_xor(send, 16);
+  for (int half = R / 2, dist = 32; half >= 1; half >>= 1, dist >>= 1) {
+    const bool hi = (lane & dist) != 0;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float send = hi ? v[i] : v[i + half];
+      const float keep = hi ? v[i + half] : v[i];
+      v[i] = keep + __shfl_xor(send, dist);
     }
+    row = 2 * row + (hi ? 1 : 0);
   }
-  const bool hi = (lane & 8) != 0;
-  float v1 = (hi ? v2[1] : v2[0]) + __shfl_xor(hi ? v2[0] : v2[1], 8);
-  v1 += __shfl_xor(v1, 4);
-  v1 += __shfl_xor(v1, 2);
-  v1 += __shfl_xor(v1, 1);
-  row = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
-  return v1;
+  float t = v[0];
+#pragma unroll
+  for (int dist = 32 / R; dist >= 1; dist >>= 1) t += __shfl_xor(t, dist);
+  return t;
 }
 
 struct GvLoads {
@@ -444,8 +440,8 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_gemv_kernel(
   }
 
   int myrow;
-  const float v1 = reduce_rows8(rowacc, lane, myrow);
-  if ((lane & 7) == 0) part[wave * kGvRows + myrow] = v1;
+  const float v1 = reduce_rows<kGvRows>(rowacc, lane, myrow);
+  if ((lane & (kWave / kGvRows - 1)) == 0) part[wave * kGvRows + myrow] = v1;
   __syncthreads();
   if ((int)threadIdx.x < kGvRows) {
     const int n = n0 + threadIdx.x;
@@ -470,7 +466,7 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_gemv_kernel(
 // decode_gemv_kernel (index width at run time: this kernel waits on memory,
 // not on arithmetic).
 // ---------------------------------------------------------------------------
-template <int L, typename Tin, typename Out>
+template <int L, int R, typename Tin, typename Out>
 __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_matvec_kernel(
     const Tin* __restrict__ X, int d, const float* __restrict__ s, uint64_t seed,
     const uint32_t* __restrict__ packed, int row_words, const uint16_t* __restrict__ rho_f16, int N,
@@ -482,21 +478,21 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_matvec_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
-  float* part = reinterpret_cast<float*>(pk_all + nw * kWave);       // [waves][kGvRows]
+  float* part = reinterpret_cast<float*>(pk_all + nw * kWave);       // [waves][R]
   const int nchunks = d >> 4;
   const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
-  const int n0 = blockIdx.x * kGvRows;
+  const int n0 = blockIdx.x * R;
   const float inv_sqrt_b = (float)(1.0 / sqrt((double)(1 << L)));
   const int lane_u4 = min(lane, 4 * B - 1);
   const int last_u4 = row_words / 4 - 1;
 
   // the window's packed pieces of the 8 rows (as in the GEMV), issued before
   // the codebook is staged
-  u32x4 rw[kGvRows];
+  u32x4 rw[R];
   auto load_packed = [&](int win) {
     const int u4 = min(win * 4 * B + lane_u4, last_u4);
 #pragma unroll
-    for (int r = 0; r < kGvRows; ++r)
+    for (int r = 0; r < R; ++r)
       rw[r] = reinterpret_cast<const u32x4*>(packed + (int64_t)min(n0 + r, N - 1) * row_words)[u4];
   };
   load_packed(wave);                     // wave < nw <= nwin
@@ -514,9 +510,9 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_matvec_kernel(
   const uint32_t lbit = (uint32_t)(co_local * kPairsPerLane * B);   // its first bit within the window
   const uint32_t sh = lbit & 31u;
   const uint32_t* pkw = reinterpret_cast<const uint32_t*>(pk) + min((int)(lbit >> 5), 4 * kWave - 4);
-  float rowacc[kGvRows];
+  float rowacc[R];
 #pragma unroll
-  for (int r = 0; r < kGvRows; ++r) rowacc[r] = 0.0f;
+  for (int r = 0; r < R; ++r) rowacc[r] = 0.0f;
 
   for (int win = wave; win < nwin; win += nw) {
     if (win != wave) load_packed(win);   // rows longer than 16 windows: later windows in turn
@@ -553,7 +549,7 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_matvec_kernel(
       }
     }
 #pragma unroll
-    for (int r = 0; r < kGvRows; ++r) {
+    for (int r = 0; r < R; ++r) {
       wave_lds_fence();
       pk[lane] = rw[r];
       wave_lds_fence();
@@ -571,14 +567,14 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_matvec_kernel(
     }
   }
   int myrow;
-  const float v1 = reduce_rows8(rowacc, lane, myrow);
-  if ((lane & 7) == 0) part[wave * kGvRows + myrow] = v1;
+  const float v1 = reduce_rows<R>(rowacc, lane, myrow);
+  if ((lane & (kWave / R - 1)) == 0) part[wave * R + myrow] = v1;
   __syncthreads();
-  if ((int)threadIdx.x < kGvRows) {
+  if ((int)threadIdx.x < R) {
     const int n = n0 + threadIdx.x;
     if (n < N) {
       float sum = 0.0f;
-      for (int ww = 0; ww < nw; ++ww) sum += part[ww * kGvRows + threadIdx.x];
+      for (int ww = 0; ww < nw; ++ww) sum += part[ww * R + threadIdx.x];
       Out::put(Y + n, sum * f16_bits_to_f32(rho_f16[n]));
     }
   }
@@ -657,6 +653,12 @@ static int launch_mm_tt(const uint16_t* Xr, int T, int d, int64_t ldr, const uin
   return launch_mm<BT, 4>(Xr, T, d, ldr, packed, row_words, rn, N, sigma, cb, K, B, Y, ydt, ldy, st);
 }
 
+// Rows per workgroup of the one-kernel matvec.  (16 would let all
+// workgroups fit on the chip at once at the common sizes, but with
+// 1024-thread workgroups allowed the compiler keeps the kernel at 128 VGPRs
+// and it then spills.)
+constexpr int kMvRows = kGvRows;
+
 template <int L>
 struct LaunchMatvec {
   static int run(const void* X, int32_t xdt, int d, const float* s, uint64_t seed, const uint32_t* packed,
@@ -664,12 +666,12 @@ struct LaunchMatvec {
                  int32_t ydt, hipStream_t st) {
     const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
     const int nw = nwin < kGvMaxWaves ? nwin : kGvMaxWaves;
-    const dim3 grid((unsigned)((N + kGvRows - 1) / kGvRows)), blk((unsigned)(nw * kWave));
+    const dim3 grid((unsigned)((N + kMvRows - 1) / kMvRows)), blk((unsigned)(nw * kWave));
     const size_t lds = (size_t)((K + 1) & ~1) * sizeof(float2) + (size_t)nw * kWave * 16 +
-                       (size_t)nw * kGvRows * sizeof(float);
-#define QAMW_MV(TIN, OUT, YT)                                                                                    \
-  hipLaunchKernelGGL((decode_matvec_kernel<L, TIN, OUT>), grid, blk, lds, st, (const TIN*)X, d, s, seed, packed, \
-                     row_words, rn, N, sigma, cb, K, B, (YT*)Y)
+                       (size_t)nw * kMvRows * sizeof(float);
+#define QAMW_MV(TIN, OUT, YT)                                                                                 \
+  hipLaunchKernelGGL((decode_matvec_kernel<L, kMvRows, TIN, OUT>), grid, blk, lds, st, (const TIN*)X, d, s, seed, \
+                     packed, row_words, rn, N, sigma, cb, K, B, (YT*)Y)
     if (xdt == QAMW_F32) {
       if (ydt == QAMW_F32) QAMW_MV(float, OutF32, float); else QAMW_MV(float, OutBF16, uint16_t);
     } else {
