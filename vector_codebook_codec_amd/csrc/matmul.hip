@@ -45,10 +45,11 @@ __global__ __launch_bounds__(kBlockThreads) void rotate_act_kernel(const Tin* __
   const bool active = c < nchunks;   // whole Hadamard blocks are active or not
   const float inv_sqrt_b = (float)(1.0 / sqrt((double)(1 << L)));
   float g[16];
+  sign_eps16(seed, (uint32_t)(c * kChunk), g);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int j = c * kChunk + i;
-    g[i] = active ? sign_eps(seed, (uint32_t)j) * (inv_sqrt_b / (s ? s[j] : 1.0f)) : 0.0f;
+    g[i] = active ? g[i] * (inv_sqrt_b / (s ? s[j] : 1.0f)) : 0.0f;
   }
   const int co = win * kWinChunks + BlockOut<L>::chunk(lane);
   const float osign = BlockOut<L>::sign(lane);
@@ -535,9 +536,11 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_matvec_kernel(
       const float4 s0 = *reinterpret_cast<const float4*>(sigma + pcl);
       const float4 s1 = *reinterpret_cast<const float4*>(sigma + pcl + 4);
       raw.unpack(x);
+      float eps[16];
+      sign_eps16(seed, (uint32_t)(cl * kChunk), eps);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float g = sign_eps(seed, (uint32_t)(cl * kChunk + i)) * (inv_sqrt_b / sv[i]);
+        const float g = eps[i] * (inv_sqrt_b / sv[i]);
         x[i] = active ? x[i] * g : 0.0f;
       }
       fwht_block<L>(x, lane);

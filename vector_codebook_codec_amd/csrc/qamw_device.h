@@ -34,6 +34,25 @@ __device__ __forceinline__ float sign_eps(uint64_t seed, uint32_t j) {
   return (z >> 63) ? -1.0f : 1.0f;
 }
 
+// The same signs for the 16 consecutive columns j0 .. j0 + 15.  The counter
+// advances by gamma per column, so only the first needs a multiply; of the
+// last product only bit 63 is needed, the top bit of the high word of its low
+// 64 bits: hi(xl cl) + xl ch + xh cl (mod 2^32) for x = (xh, xl), c = (ch, cl).
+__device__ __forceinline__ void sign_eps16(uint64_t seed, uint32_t j0, float out[16]) {
+  constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+  constexpr uint32_t kC2lo = 0x133111EBu, kC2hi = 0x94D049BBu;
+  uint64_t ctr = seed + (uint64_t)(j0 + 1u) * kGamma;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint64_t z = (ctr ^ (ctr >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z ^= z >> 27;
+    const uint32_t xl = (uint32_t)z, xh = (uint32_t)(z >> 32);
+    const uint32_t hi = __umulhi(xl, kC2lo) + xl * kC2hi + xh * kC2lo;
+    out[i] = (hi >> 31) ? -1.0f : 1.0f;
+    ctr += kGamma;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Loads / stores of one 16-element chunk (16-byte aligned).
 // ---------------------------------------------------------------------------
