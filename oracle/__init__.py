@@ -20,7 +20,7 @@ Parity status: every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle_*.py`` against closed forms, textbook or library routines,
 published test vectors or brute force.  Agreement with the paper authors' own
 implementation is unpinned: the pages print no codebook, sigma values, test
-vectors or code, so the readings listed in the design doc (sign generator,
-Hadamard order, bit layout, sigma estimator, ...) cannot be checked against
-them.
+vectors or code, so the readings this oracle takes where the pages are
+silent (sign generator, Hadamard order, bit layout, sigma estimator, ...)
+cannot be checked against them.
 """
