@@ -17,10 +17,10 @@ namespace qamw {
 // Decode tunables: rows whose packed words are loaded ahead, and wavefronts
 // of work per CU the launch aims for (each wave then walks several rows).
 #ifndef QAMW_DECODE_PREFETCH
-#define QAMW_DECODE_PREFETCH 4
+#define QAMW_DECODE_PREFETCH 3
 #endif
 #ifndef QAMW_DECODE_WAVES_PER_CU
-#define QAMW_DECODE_WAVES_PER_CU 16
+#define QAMW_DECODE_WAVES_PER_CU 20
 #endif
 constexpr int kDecodePrefetch = QAMW_DECODE_PREFETCH;
 constexpr int kDecodeMaxRows = 16;   // rows per wavefront, at most
@@ -45,8 +45,11 @@ constexpr int kDecodeMaxRows = 16;   // rows per wavefront, at most
 // inside it and indices >= K decode as K - 1 without a clamp instruction;
 // BT = 0 takes the width B from the argument and clamps indices to K - 1.
 // ---------------------------------------------------------------------------
+// Five waves per SIMD (at most 102 VGPRs) with three rows in flight per wave
+// measured a little faster than four waves with four rows in flight (blocks up
+// to 256; the larger ones need more registers for their LDS-staged stores).
 template <int L, int BT, typename Out>
-__global__ __launch_bounds__(kBlockThreads) void decode_kernel(
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(L <= 8 ? 5 : 1))) void decode_kernel(
     const uint32_t* packed, const uint16_t* rho_f16, int N, int d,
     const float* __restrict__ s, const float* __restrict__ sigma, uint64_t seed,
     const float* __restrict__ codebook, int K, int Bdyn, int row_words, int blocks_per_window,
@@ -55,9 +58,12 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
   // then keep each ring-slot prefetch in the row that issues it (the compiler
   // may not move a load past a store that could alias it), instead of letting
   // it sink into the row that consumes it.
+  // Blocks of up to 256 columns store straight from registers; larger ones
+  // go through a 4 KB LDS buffer per wave.
+  constexpr bool kDirect = L <= 8;
   extern __shared__ float4 lds4[];
-  uint4* stage_all = reinterpret_cast<uint4*>(lds4);    // 4 waves x 256 x 16 bytes
-  u32x4* pk_all = reinterpret_cast<u32x4*>(stage_all + kWavesPerBlock * 256);   // 4 waves x 64 x 16 bytes
+  uint4* stage_all = reinterpret_cast<uint4*>(lds4);    // 4 waves x 256 x 16 bytes (LDS-staged stores only)
+  u32x4* pk_all = reinterpret_cast<u32x4*>(stage_all + (kDirect ? 0 : kWavesPerBlock * 256));   // 4 waves x 64 x 16 bytes
   float* gwin = reinterpret_cast<float*>(pk_all + kWavesPerBlock * kWave);  // kWinChunks * kChunk factors
   float2* cb = reinterpret_cast<float2*>(gwin + kWinChunks * kChunk);
 
@@ -158,6 +164,8 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
   uint4* stage = stage_all + wave * 256;
   const int valid_cols = d - win * kWinChunks * kChunk;
   const int co_local = BlockOut<L>::chunk(lane);
+  // first output column of this lane's direct stores
+  const int e0 = 16 * BlockOut<L>::chunk(lane & (Out::kGroup - 1)) + (lane / Out::kGroup) * Out::kPiece;
   float g[16];
   {
     const float osign = BlockOut<L>::sign(lane);
@@ -207,7 +215,10 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
       fwht_block<L, 2>(x, lane);
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[i] *= g[i];
-      Out::template store<kFull>(stage, lane, co_local, x, out_win + (int64_t)n * ldo, valid_cols);
+      if constexpr (kDirect)
+        Out::template direct<kFull>(x, e0, out_win + (int64_t)n * ldo, valid_cols);
+      else
+        Out::template store<kFull>(stage, lane, co_local, x, out_win + (int64_t)n * ldo, valid_cols);
     };
     auto walk = [&](auto self, auto kc) {
       constexpr int k = decltype(kc)::value;
@@ -234,7 +245,7 @@ int launch_decode_bt(const uint32_t* packed, const uint16_t* rho_f16, int N, int
                      const float* sigma, uint64_t seed, const float* cb, int K, int B, int row_words, void* out,
                      int32_t odt, int64_t ldo, hipStream_t st) {
   const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
-  const size_t lds = (size_t)kWavesPerBlock * (256 + kWave) * 16 + (size_t)kWinChunks * kChunk * sizeof(float) +
+  const size_t lds = (size_t)kWavesPerBlock * ((L <= 8 ? 0 : 256) + kWave) * 16 + (size_t)kWinChunks * kChunk * sizeof(float) +
                      (size_t)(BT ? (1 << BT) : K) * sizeof(float2);
   // Persistent-style grid: every workgroup keeps one window (codebook and
   // column factors loaded once) and walks rows with a stride.  Aim for the

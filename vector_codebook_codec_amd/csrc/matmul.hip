@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kBlockThreads) void rotate_act_kernel(const Tin* __
       uint32_t w[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        w[i] = f32_to_bf16_bits(x[2 * i] * osign) | (f32_to_bf16_bits(x[2 * i + 1] * osign) << 16);
+        w[i] = pack_bf16x2(x[2 * i] * osign, x[2 * i + 1] * osign);
       uint4* out = reinterpret_cast<uint4*>(Xr + (int64_t)t * ldr + co * kChunk);
       out[0] = make_uint4(w[0], w[1], w[2], w[3]);
       out[1] = make_uint4(w[4], w[5], w[6], w[7]);

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void oe_prep_kernel(const TX* __restrict__ X, 
     }
     uint32_t o[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16_bits(v[2 * e]) | (f32_to_bf16_bits(v[2 * e + 1]) << 16);
+    for (int e = 0; e < 8; ++e) o[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
     uint4* q = reinterpret_cast<uint4*>(dst);
     q[0] = make_uint4(o[0], o[1], o[2], o[3]);
     q[1] = make_uint4(o[4], o[5], o[6], o[7]);

@@ -122,11 +122,16 @@ template <> struct RawChunk<uint16_t> {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+// fp32 -> bf16 bits, round to nearest even: one v_cvt_pk_bf16_f32 per two
+// values (NaN stays a NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
@@ -226,8 +231,66 @@ __device__ __forceinline__ void store_window_b16(uint4* buf, int lane, int co_lo
   }
 }
 
+// Stores straight from registers, for blocks of at most 256 columns (the
+// lane network then stays inside lane bits 0..3).  Lane a holds columns
+// 16 co(a) + r, r = 0..15, co(a) its output chunk.  v_permlane16_swap and
+// v_permlane32_swap exchange halves of a register pair across lane bit 4 or
+// 5, i.e. transpose one lane bit with one register bit.  For fp32, swapping
+// lane bits 4, 5 with register bits 2, 3 leaves lane a holding, in registers
+// 4v .. 4v+3, the four columns from 256 v + 16 co(a & 15) + 4 (a >> 4): each
+// 16-byte store instruction writes 1 KB of the window contiguously.  For
+// 16-bit outputs (word i = columns 2i, 2i+1) one swap of lane bit 5 with word
+// bit 2 leaves words 4v .. 4v+3 holding the eight columns from
+// 512 v + 16 co(a & 31) + 8 (a >> 5).  `e0` is that first column for v = 0.
+__device__ __forceinline__ void swap_halves32(uint32_t& a, uint32_t& b) {
+  const auto t = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = t[0];
+  b = t[1];
+}
+__device__ __forceinline__ void swap_halves16(uint32_t& a, uint32_t& b) {
+  const auto t = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = t[0];
+  b = t[1];
+}
+
+template <bool kFull>
+__device__ __forceinline__ void store_direct_f32(const float x[16], int e0, float* __restrict__ dst, int valid_cols) {
+  uint32_t u[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) u[r] = __float_as_uint(x[r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if ((r & 4) == 0) swap_halves16(u[r], u[r + 4]);   // lane bit 4 <-> register bit 2
+#pragma unroll
+  for (int r = 0; r < 8; ++r) swap_halves32(u[r], u[r + 8]);   // lane bit 5 <-> register bit 3
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int e = v * 256 + e0;
+    if (kFull || e < valid_cols) store16(dst + e, make_uint4(u[4 * v], u[4 * v + 1], u[4 * v + 2], u[4 * v + 3]));
+  }
+}
+
+template <bool kFull>
+__device__ __forceinline__ void store_direct_b16(uint32_t w[8], int e0, uint16_t* __restrict__ dst, int valid_cols) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) swap_halves32(w[i], w[i + 4]);   // lane bit 5 <-> word bit 2
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int e = v * 512 + e0;
+    if (kFull || e < valid_cols) store16(dst + e, make_uint4(w[4 * v], w[4 * v + 1], w[4 * v + 2], w[4 * v + 3]));
+  }
+}
+
+// Output types of the decode: `store` goes through the wave's LDS buffer
+// (any block size), `direct` stores from registers (blocks up to 256).
+// kGroup / kPiece give e0 = 16 co(lane & (kGroup - 1)) + (lane / kGroup) kPiece.
 struct StageF32 {
   using T = float;
+  static constexpr int kGroup = 16, kPiece = 4;
+  template <bool kFull = false>
+  static __device__ __forceinline__ void direct(const float x[16], int e0, float* dst, int valid_cols) {
+    store_direct_f32<kFull>(x, e0, dst, valid_cols);
+  }
   template <bool kFull = false>
   static __device__ __forceinline__ void store(uint4* buf, int lane, int co_local, const float x[16], float* dst,
                                                int valid_cols) {
@@ -237,18 +300,34 @@ struct StageF32 {
 
 struct StageBF16 {
   using T = uint16_t;
+  static constexpr int kGroup = 32, kPiece = 8;
+  template <bool kFull = false>
+  static __device__ __forceinline__ void direct(const float x[16], int e0, uint16_t* dst, int valid_cols) {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    store_direct_b16<kFull>(w, e0, dst, valid_cols);
+  }
   template <bool kFull = false>
   static __device__ __forceinline__ void store(uint4* buf, int lane, int co_local, const float x[16], uint16_t* dst,
                                                int valid_cols) {
     uint32_t w[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = f32_to_bf16_bits(x[2 * i]) | (f32_to_bf16_bits(x[2 * i + 1]) << 16);
+    for (int i = 0; i < 8; ++i) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
     store_window_b16<kFull>(buf, lane, co_local, w, dst, valid_cols);
   }
 };
 
 struct StageF16 {
   using T = uint16_t;
+  static constexpr int kGroup = 32, kPiece = 8;
+  template <bool kFull = false>
+  static __device__ __forceinline__ void direct(const float x[16], int e0, uint16_t* dst, int valid_cols) {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = f32_to_f16_bits(x[2 * i]) | (f32_to_f16_bits(x[2 * i + 1]) << 16);
+    store_direct_b16<kFull>(w, e0, dst, valid_cols);
+  }
   template <bool kFull = false>
   static __device__ __forceinline__ void store(uint4* buf, int lane, int co_local, const float x[16], uint16_t* dst,
                                                int valid_cols) {
