@@ -229,6 +229,37 @@ def test_strided_rows(q):
     assert torch.count_nonzero(out_big[:, d:]) == 0
 
 
+@pytest.mark.parametrize("N,d,block,K,wdtype,alpha,seed", SHAPES)
+def test_decode_16bit_is_rounded_fp32(q, N, d, block, K, wdtype, alpha, seed):
+    """bf16 output = the fp32 decode rounded to nearest even, bit for bit; fp16
+    output within one unit in the last place of it (the last scale and the
+    rounding are one fused step); columns past d of a strided output untouched.
+    Covers every block size, ragged windows and single rows for the 16-bit
+    stores (the fp32 decode of the same shapes is checked against the oracle)."""
+    rng = np.random.default_rng(2000 + seed)
+    W = (rng.standard_normal((N, d)) * 0.02).astype(np.float32)
+    r = rng.lognormal(0.0, 1.0, d).astype(np.float32)
+    if wdtype == "bf16":
+        W = workloads.bf16_bits_from_f32(W)
+    wl = workloads.Workload(f"shape16_{seed}", W, wdtype, r, alpha, block, seed * 7919, K)
+    say(f"case decode16 N={N} d={d} b={block} K={K}")
+    g = run_gpu(q, wl, q.load_codebook(K))
+    args = (g["packed"], g["rn"], d, g["s"], g["sigma"], block, wl.sign_seed, g["C"])
+    ref32 = q.qamw_decode(*args)
+    pad = 40
+    for dt in (torch.bfloat16, torch.float16):
+        big = torch.full((N, d + pad), -3.0, dtype=dt, device=DEV)
+        q.qamw_decode(*args, out=big[:, :d])
+        torch.cuda.synchronize()
+        got = big[:, :d].contiguous().view(torch.int16).cpu().numpy().astype(np.int32)
+        want = ref32.to(dt).view(torch.int16).cpu().numpy().astype(np.int32)
+        if dt == torch.bfloat16:
+            assert np.array_equal(got, want)
+        else:
+            assert int(np.max(np.abs(got - want))) <= 1
+        assert torch.all(big[:, d:] == -3.0)
+
+
 # ---------------------------------------------------------------- degenerate inputs
 def test_zero_rows_and_zero_sigma(q):
     rng = np.random.default_rng(5)
