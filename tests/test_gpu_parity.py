@@ -183,6 +183,7 @@ SHAPES = [
     (4, 1536, 512, 4096, "f32", 0.5, 7),
     (3, 2048, 1024, 256, "bf16", 0.5, 8),
     (1, 1024, 1024, 2048, "f32", 0.5, 9),    # a single row
+    (3, 17408, 128, 256, "bf16", 0.5, 10),   # 17 windows: row norms and amplitudes in two passes
 ]
 
 

@@ -138,8 +138,7 @@ int32_t qamw_calibrate(const void* W, int32_t wdtype, int64_t N, int64_t d, int6
   float* partial = (float*)((char*)fcol + round_up((size_t)d * sizeof(float), 256));
   const int n = (int)N, dd = (int)d;
   if ((rc = launch_scale(chan_rms, alpha, sign_seed, dd, s_out, fcol, st))) return rc;
-  if ((rc = launch_rownorm(W, wdtype, n, dd, ldw, s_out, rho, nullptr, st))) return rc;
-  if ((rc = launch_amplitude(L, W, wdtype, n, dd, ldw, fcol, rho, partial, st))) return rc;
+  if ((rc = launch_norm_amplitude(L, W, wdtype, n, dd, ldw, s_out, fcol, rho, nullptr, partial, st))) return rc;
   return launch_sigma(partial, (int)calib_tiles(N), dd / 2, n, sigma_out, nullptr, st);
 }
 
@@ -271,8 +270,7 @@ int32_t qamw_calibrate_encode(const void* W, int32_t wdtype, int64_t N, int64_t 
   // column factors (scale_kernel), row norms with their fp16 bits (rownorm_kernel)
   // and 1 / sigma (sigma_kernel)
   if ((rc = launch_scale(chan_rms, alpha, sign_seed, dd, s_out, e.f, st))) return rc;
-  if ((rc = launch_rownorm(W, wdtype, n, dd, ldw, s_out, e.rho, rownorm_f16, st))) return rc;
-  if ((rc = launch_amplitude(L, W, wdtype, n, dd, ldw, e.f, e.rho, partial, st))) return rc;
+  if ((rc = launch_norm_amplitude(L, W, wdtype, n, dd, ldw, s_out, e.f, e.rho, rownorm_f16, partial, st))) return rc;
   if ((rc = launch_sigma(partial, (int)calib_tiles(N), dd / 2, n, sigma_out, e.isig, st))) return rc;
   return launch_encode(L, W, wdtype, n, dd, ldw, e.f, e.isig, codebook, (int)K, qamw_index_bits(K),
                        (int)qamw_packed_row_words(d, K), e.rho, plan, packed, st);

@@ -107,6 +107,111 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Passes 1 and 2 with one read of W (rows of up to kFuseMaxWin windows).  A
+// workgroup owns a tile of kCalibRowsPerTile rows across the whole width,
+// wavefront w = window w.  For each row every wavefront forms its window's
+// share of rho_n^2 (chunk_sumsq + window_sum, as row_norm_wave does) and the
+// pair amplitudes; the shares meet in LDS, every wavefront adds them in window
+// order (the same fp64 sum as row_norm_wave, so rho is identical), and the
+// amplitudes are scaled and accumulated exactly as amplitude_kernel does.  A
+// barrier per batch of rows; the share buffer alternates between batches.
+// ---------------------------------------------------------------------------
+constexpr int kFuseMaxWin = 16;   // 1024 threads
+
+template <int L, typename Tin>
+__global__ __launch_bounds__(kFuseMaxWin * kWave) void norm_amplitude_kernel(
+    const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ fcol,
+    double* __restrict__ rho, uint16_t* __restrict__ rho_f16, float* __restrict__ partial) {
+  constexpr int kBatch = sizeof(Tin) == 2 ? 2 : 1;   // rows per barrier (and loads in flight)
+  __shared__ double share[2][kBatch][kFuseMaxWin];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int win = threadIdx.x >> 6;
+  const int nwin = blockDim.x >> 6;
+  const int nchunks = d >> 4;
+  const int tile = blockIdx.x;
+  const int c = win * kWinChunks + lane;
+  const bool active = c < nchunks;   // whole Hadamard blocks are active or not
+  const int co = win * kWinChunks + BlockOut<L>::chunk(lane);
+  const double sqrt_b = sqrt((double)(1 << L));
+
+  float f[16];
+  if (active) {
+    load_chunk(fcol + c * kChunk, f);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) f[i] = 0.0f;
+  }
+  float acc[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) acc[p] = 0.0f;
+
+  const int n0 = tile * kCalibRowsPerTile;
+  const int n1 = min(N, n0 + kCalibRowsPerTile);
+  RawChunk<Tin> ring[kBatch];   // the batch's rows; each slot reloads the row kBatch ahead
+  const Tin* base = W + c * kChunk;
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u)
+    if (active && n0 + u < n1) ring[u].load(base + (int64_t)(n0 + u) * ldw);
+  int buf = 0;
+  for (int nb = n0; nb < n1; nb += kBatch) {     // uniform over the workgroup
+    float amp[kBatch][8];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int n = nb + u;
+      if (n >= n1) break;
+      float x[16];
+      if (active) {
+        ring[u].unpack(x);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = 0.0f;
+      }
+      if (active && n + kBatch < n1) ring[u].load(base + (int64_t)(n + kBatch) * ldw);
+      // an empty asm "redefines" f each row, so its fp64 conversions are redone
+      // here instead of being hoisted and held (32 registers) for the loop
+      asm volatile("" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]), "+v"(f[6]),
+                   "+v"(f[7]), "+v"(f[8]), "+v"(f[9]), "+v"(f[10]), "+v"(f[11]), "+v"(f[12]), "+v"(f[13]),
+                   "+v"(f[14]), "+v"(f[15]));
+      const double sh = window_sum(chunk_sumsq(x, f));   // f = eps s: the same squares as s
+      if (lane == 0) share[buf][u][win] = sh;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] *= f[i];
+      fwht_block<L>(x, lane);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const float a = x[2 * p], b = x[2 * p + 1];
+        // v_sqrt_f32 (1 ulp) rather than the correctly rounded sqrtf expansion
+        amp[u][p] = __builtin_amdgcn_sqrtf(__builtin_fmaf(a, a, b * b));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int n = nb + u;
+      if (n >= n1) break;
+      double t = 0.0;
+      for (int w = 0; w < nwin; ++w) t += share[buf][u][w];
+      const double r = sqrt(t);
+      const float inv = r > 0.0 ? (float)(1.0 / (sqrt_b * r)) : 0.0f;
+#pragma unroll
+      for (int p = 0; p < 8; ++p) acc[p] += amp[u][p] * inv;
+      if (threadIdx.x == 0) {
+        rho[n] = r;
+        if (rho_f16) rho_f16[n] = f64_to_f16_bits(r);
+      }
+    }
+    // the next batch writes the other buffer; the one after it has passed
+    // the next barrier, so every wavefront has read this one by then
+    buf ^= 1;
+  }
+  if (active) {
+    float4* out = reinterpret_cast<float4*>(partial + (int64_t)tile * (d >> 1) + co * kPairsPerLane);
+    out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
 // sigma_k = (sum over tiles, fp64, fixed order) / (N sqrt(pi/2)).  A
 // workgroup owns 16 columns; thread (column, slice) sums tiles slice,
 // slice + 16, ... and the 16 slice sums are then added in slice order.
@@ -173,6 +278,33 @@ struct LaunchAmplitude {
 int launch_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const double* rho,
                      float* partial, hipStream_t st) {
   return dispatch_L<LaunchAmplitude>(L, W, wdt, N, d, ldw, f, rho, partial, st);
+}
+
+template <int L>
+struct LaunchNormAmplitude {
+  static int run(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, double* rho,
+                 uint16_t* rho_f16, float* partial, hipStream_t st) {
+    const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
+    const dim3 grid((unsigned)calib_tiles(N)), blk((unsigned)(nwin * kWave));
+    if (wdt == QAMW_F32)
+      hipLaunchKernelGGL((norm_amplitude_kernel<L, float>), grid, blk, 0, st, (const float*)W, ldw, N, d, f, rho,
+                         rho_f16, partial);
+    else
+      hipLaunchKernelGGL((norm_amplitude_kernel<L, uint16_t>), grid, blk, 0, st, (const uint16_t*)W, ldw, N, d, f,
+                         rho, rho_f16, partial);
+    return check_launch("norm_amplitude_kernel");
+  }
+};
+
+// Row norms and amplitude partials: one fused pass when a row has at most
+// kFuseMaxWin windows, else the two passes (the results are the same).
+int launch_norm_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s,
+                          const float* f, double* rho, uint16_t* rho_f16, float* partial, hipStream_t st) {
+  const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
+  if (nwin <= kFuseMaxWin) return dispatch_L<LaunchNormAmplitude>(L, W, wdt, N, d, ldw, f, rho, rho_f16, partial, st);
+  int rc;
+  if ((rc = launch_rownorm(W, wdt, N, d, ldw, s, rho, rho_f16, st))) return rc;
+  return launch_amplitude(L, W, wdt, N, d, ldw, f, rho, partial, st);
 }
 
 int launch_sigma(const float* partial, int ntiles, int half_d, int N, float* sigma, float* isig, hipStream_t st) {

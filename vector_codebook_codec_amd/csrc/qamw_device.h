@@ -86,6 +86,10 @@ __device__ __forceinline__ void load_chunk(const uint16_t* __restrict__ p, float
 template <typename Tin> struct RawChunk;
 template <> struct RawChunk<float> {
   float4 v[4];
+  __device__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
   __device__ void load(const float* __restrict__ p) {
     const float4* q = reinterpret_cast<const float4*>(p);
 #pragma unroll
@@ -100,6 +104,7 @@ template <> struct RawChunk<float> {
 };
 template <> struct RawChunk<uint16_t> {
   uint4 v[2];
+  __device__ void zero() { v[0] = v[1] = make_uint4(0u, 0u, 0u, 0u); }
   __device__ void load(const uint16_t* __restrict__ p) {
     const uint4* q = reinterpret_cast<const uint4*>(p);
     v[0] = q[0];
@@ -528,47 +533,112 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
 
 // ---------------------------------------------------------------------------
 // rho_n = sqrt(sum_j (W_nj s_j)^2) for one row, by one wavefront.  W_nj s_j
-// is exact in fp64 (24-bit x 24-bit significands); squares and sums are fp64,
-// reduced in a fixed order, so rho is deterministic and accurate to ~1e-16.
+// is exact in fp64 (24-bit x 24-bit significands); squares and sums are fp64
+// in a fixed order, so rho is deterministic and accurate to ~1e-16.  The
+// order is by window (64 chunks, 1024 columns): lane l's share of window w is
+// the FMA chain over the 16 squares of chunk 64 w + l, the window's share is
+// their butterfly sum over the lanes (window_sum), and rho^2 adds the
+// windows' shares in window order.  The fused calibration kernel, which has
+// one wavefront per window, forms the same sum.
 // Lane 0 writes rho[n] and, when rho_f16 is given, its binary16 (RNE) bits.
 // ---------------------------------------------------------------------------
+// Sum over the wavefront, every lane getting the same bits, in VALU
+// instructions only: inside each 16-lane row, DPP pairs lane i with i ^ 1,
+// i ^ 2, then 7 - i within 8 lanes (half-row mirror) and 15 - i within 16
+// (row mirror) -- each time two lanes whose partial sums are already equal
+// across their groups, so a + b and b + a agree; then lane-half swaps
+// (v_permlane16_swap, v_permlane32_swap) bring in the partner across lane
+// bit 4 and 5.
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, kCtrl, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), kCtrl, 0xf, 0xf, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// v of lane l ^ 16 (kBit = 4) or l ^ 32 (kBit = 5)
+template <int kBit>
+__device__ __forceinline__ double partner_f64(double v, int lane) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  uint32_t lo2 = lo, hi2 = hi;
+  // swap(x, x): the first result holds the partner in the upper half of each
+  // pair of lane groups, the second in the lower half
+  if constexpr (kBit == 4) {
+    swap_halves16(lo, lo2);
+    swap_halves16(hi, hi2);
+  } else {
+    swap_halves32(lo, lo2);
+    swap_halves32(hi, hi2);
+  }
+  const bool upper = (lane >> kBit) & 1;
+  const uint64_t r = upper ? (((uint64_t)hi << 32) | lo) : (((uint64_t)hi2 << 32) | lo2);
+  return __longlong_as_double((long long)r);
+}
+
+__device__ __forceinline__ double window_sum(double v) {
+  const int lane = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  v += dpp_f64<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_f64<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_f64<0x141>(v);   // row_half_mirror
+  v += dpp_f64<0x140>(v);   // row_mirror
+  v += partner_f64<4>(v, lane);
+  v += partner_f64<5>(v, lane);
+  return v;
+}
+
+// One chunk's share: sum of (x_i s_i)^2, i = 0..15, as an FMA chain from 0.
+// The sign of s does not matter (the square of an exact product).
+__device__ __forceinline__ double chunk_sumsq(const float x[16], const float sc[16]) {
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const double w = (double)x[i] * (double)sc[i];   // exact: a bf16/fp32 times an fp32
+    acc = fma(w, w, acc);
+  }
+  return acc;
+}
+
 template <typename Tin>
 __device__ __forceinline__ void row_norm_wave(const Tin* __restrict__ W, int64_t ldw, int n, int d,
                                               const float* __restrict__ s, double* __restrict__ rho,
                                               uint16_t* __restrict__ rho_f16) {
   const int lane = threadIdx.x & (kWave - 1);
   const int nchunks = d >> 4;
+  const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
   const Tin* row = W + (int64_t)n * ldw;
-  double acc = 0.0;
-  auto add_chunk = [&](const float x[16], const float* sc) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const double w = (double)x[i] * (double)sc[i];   // exact: a bf16/fp32 times an fp32
-      acc = fma(w, w, acc);
+  // one window is summed while the next one's loads are in flight; lanes
+  // past the row end load nothing and add zero
+  RawChunk<Tin> rw[2];
+  RawChunk<float> rs[2];
+  auto load = [&](int slot, int w) {
+    const int c = w * kWinChunks + lane;
+    if (w < nwin && c < nchunks) {
+      rw[slot].load(row + c * kChunk);
+      rs[slot].load(s + c * kChunk);
+    } else {
+      rw[slot].zero();
+      rs[slot].zero();
     }
   };
-  // two chunks' loads in flight per lane, then the remainder
-  int c = lane;
-  for (; c + kWave < nchunks; c += 2 * kWave) {
-    float x[2][16], sc[2][16];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      load_chunk(row + (c + u * kWave) * kChunk, x[u]);
-      load_chunk(s + (c + u * kWave) * kChunk, sc[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) add_chunk(x[u], sc[u]);
-  }
-  for (; c < nchunks; c += kWave) {
+  auto add = [&](int slot, double& total) {
     float x[16], sc[16];
-    load_chunk(row + c * kChunk, x);
-    load_chunk(s + c * kChunk, sc);
-    add_chunk(x, sc);
+    rw[slot].unpack(x);
+    rs[slot].unpack(sc);
+    total += window_sum(chunk_sumsq(x, sc));
+  };
+  double total = 0.0;
+  load(0, 0);
+  for (int w = 0; w < nwin; w += 2) {
+    load(1, w + 1);
+    add(0, total);
+    if (w + 1 >= nwin) break;
+    load(0, w + 2);
+    add(1, total);
   }
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (lane == 0) {
-    const double r = sqrt(acc);
+    const double r = sqrt(total);
     rho[n] = r;
     if (rho_f16) rho_f16[n] = f64_to_f16_bits(r);
   }

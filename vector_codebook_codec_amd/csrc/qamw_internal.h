@@ -66,6 +66,8 @@ int launch_rownorm(const void* W, int32_t wdt, int N, int d, int64_t ldw, const 
                    uint16_t* rho_f16, hipStream_t st);
 int launch_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const double* rho,
                      float* partial, hipStream_t st);
+int launch_norm_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s,
+                          const float* f, double* rho, uint16_t* rho_f16, float* partial, hipStream_t st);
 int launch_sigma(const float* partial, int ntiles, int half_d, int N, float* sigma, float* isig, hipStream_t st);
 int launch_encode_prepare(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, const float* sigma,
                           uint64_t seed, double* rho, uint16_t* rho_f16, float* f, float* isig, hipStream_t st);
