@@ -122,7 +122,9 @@ int32_t qamw_calibrate(const void* W, int32_t wdtype, int64_t N, int64_t d, int6
  * nearest one (under qamw_encode's fp32 scores) for some point of the cell.
  * Encoding with a plan gives the same indices, bit for bit, as encoding
  * without one; pairs beyond both grids and cells with too many candidates
- * fall back to scanning all K centroids.
+ * fall back to scanning all K centroids.  The outer grid's cells that tile
+ * [-5, 5)^2 are never consulted (points there take the fine grid) and are
+ * marked "scan all".
  *
  * qamw_plan_bytes(K): bytes of device memory a plan for K centroids takes
  *   (0 for K outside [2, 4096]).  Host-only.

@@ -31,7 +31,9 @@
 // Two grids: a fine one (G = 512 over [-5, 5)^2) where nearly all normalised
 // pairs fall, and a coarse outer one (256 over [-40, 40)^2) for the few pairs
 // beyond it -- rows dominated by one large weight put a whole Hadamard block
-// there.  Each has its own delta (R = 5 or 40 in the formula above).
+// there.  Each has its own delta (R = 5 or 40 in the formula above).  The
+// outer cells that tile the fine grid's square are never consulted (points
+// there take the fine grid) and hold overflow records.
 //
 // Layout (plan_bytes(K) bytes, 256-byte aligned):
 //   [0, 256)     PlanHeader
@@ -346,6 +348,23 @@ constexpr int kFineSupercells = (kPlanG / kSuperFine) * (kPlanG / kSuperFine);
 constexpr int kOuterSupercells = (kPlanG2 / kSuperOuter) * (kPlanG2 / kSuperOuter);
 static_assert(kPlanG % kSuperFine == 0 && kPlanG2 % kSuperOuter == 0, "grids are whole supercells");
 
+// Outer-grid cells [kOuterFineLo, kOuterFineHi) per axis cover exactly the fine
+// grid's square [-R, R): a point there always takes the fine grid, so those
+// cells are never consulted.  Their supercells write overflow records (scan
+// the whole codebook, correct if ever read) instead of lists; near the centre
+// they are also the most expensive ones (thousands of survivors).
+constexpr int kOuterFineLo = (int)((kPlanR2 - kPlanR) * kPlanG2 / (2.0f * kPlanR2));
+constexpr int kOuterFineHi = kPlanG2 - kOuterFineLo;
+static_assert(kOuterFineLo * 2.0f * kPlanR2 == (kPlanR2 - kPlanR) * kPlanG2, "the fine square is whole outer cells");
+static_assert(kOuterFineLo % kSuperOuter == 0, "and whole outer supercells");
+
+__device__ __forceinline__ bool outer_supercell_unused(int sidx) {
+  constexpr int nsuper = kPlanG2 / kSuperOuter;
+  const int x0 = (sidx / nsuper) * kSuperOuter, y0 = (sidx % nsuper) * kSuperOuter;
+  return x0 >= kOuterFineLo && x0 + kSuperOuter <= kOuterFineHi && y0 >= kOuterFineLo &&
+         y0 + kSuperOuter <= kOuterFineHi;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* __restrict__ cb, int K, int lmax,
                                                                   char* __restrict__ plan, size_t outer_offset) {
   __shared__ PlanShared sh;
@@ -363,9 +382,18 @@ __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* _
   if (blockIdx.x < kFineSupercells)
     build_supercell<kSuperFine>(sh, cb, K, lmax, kPlanR, kPlanG, blockIdx.x,
                                 reinterpret_cast<uint16_t*>(plan + kPlanHeaderBytes));
-  else
+  else if (!outer_supercell_unused(blockIdx.x - kFineSupercells))
     build_supercell<kSuperOuter>(sh, cb, K, lmax, kPlanR2, kPlanG2, blockIdx.x - kFineSupercells,
                                  reinterpret_cast<uint16_t*>(plan + outer_offset));
+  else if (threadIdx.x < kSuperOuter * kSuperOuter) {   // one overflow record per cell
+    constexpr int nsuper = kPlanG2 / kSuperOuter;
+    const int sidx = blockIdx.x - kFineSupercells;
+    const int ix = (sidx / nsuper) * kSuperOuter + threadIdx.x / kSuperOuter;
+    const int iy = (sidx % nsuper) * kSuperOuter + threadIdx.x % kSuperOuter;
+    uint4* out = reinterpret_cast<uint4*>(plan + outer_offset + ((size_t)ix * kPlanG2 + iy) * lmax * sizeof(uint16_t));
+    out[0] = make_uint4(1u << 16, 0u, 0u, 0u);
+    if (lmax == 16) out[1] = make_uint4(0u, 0u, 0u, 0u);
+  }
 }
 
 int launch_build_plan(const float* cb, int K, void* plan, hipStream_t st) {
