@@ -226,8 +226,18 @@ __global__ __launch_bounds__(kBlockThreads) void sigma_kernel(const float* __res
   const int slice = threadIdx.x / (kBlockThreads / kSigmaSlices);
   const int k = blockIdx.x * (kBlockThreads / kSigmaSlices) + col_in;
   double acc = 0.0;
-  if (k < half_d)
-    for (int t = slice; t < ntiles; t += kSigmaSlices) acc += (double)partial[(int64_t)t * half_d + k];
+  if (k < half_d) {
+    // four loads in flight, added in tile order
+    int t = slice;
+    for (; t + 3 * kSigmaSlices < ntiles; t += 4 * kSigmaSlices) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = partial[(int64_t)(t + u * kSigmaSlices) * half_d + k];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += (double)v[u];
+    }
+    for (; t < ntiles; t += kSigmaSlices) acc += (double)partial[(int64_t)t * half_d + k];
+  }
   part[slice][col_in] = acc;
   __syncthreads();
   if (slice == 0 && k < half_d) {
