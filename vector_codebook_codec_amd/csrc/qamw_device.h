@@ -247,6 +247,10 @@ __device__ __forceinline__ void store_window_b16(uint4* buf, int lane, int co_lo
 // 16-bit outputs (word i = columns 2i, 2i+1) one swap of lane bit 5 with word
 // bit 2 leaves words 4v .. 4v+3 holding the eight columns from
 // 512 v + 16 co(a & 31) + 8 (a >> 5).  `e0` is that first column for v = 0.
+//
+// swap_halves32(a, b): lanes 32..63 of a and lanes 0..31 of b trade places
+// (a[l + 32] <-> b[l], l < 32); swap_halves16 does the same between the odd
+// 16-lane rows of a and the even rows of b (a[l + 16] <-> b[l], bit 4 of l clear).
 __device__ __forceinline__ void swap_halves32(uint32_t& a, uint32_t& b) {
   const auto t = __builtin_amdgcn_permlane32_swap(a, b, false, false);
   a = t[0];
