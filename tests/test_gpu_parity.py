@@ -448,6 +448,11 @@ def test_plan_lists_cover_near_minimisers(q, K):
     tails repeat the last entry."""
     C = q.load_codebook(K)
     grids, lmax = read_plan(q, C)
+    # the outer cells tiling the fine grid's square [-5, 5)^2 are never
+    # consulted (points there take the fine grid): "scan all" records
+    G2 = GRIDS["outer"][0]
+    lo = (G2 - G2 * 10 // 80) // 2
+    assert np.all(grids["outer"][0].reshape(G2, G2)[lo:G2 - lo, lo:G2 - lo] == PLAN_OVERFLOW)
     for name, (counts, lists) in grids.items():
         say(f"case plan K={K} {name}: {int((counts == PLAN_OVERFLOW).sum())} overflow cells, "
             f"max count {int(counts[counts != PLAN_OVERFLOW].max())}")
