@@ -393,7 +393,7 @@ struct LaunchEncode {
   hipLaunchKernelGGL((encode_plan_kernel<L, TIN, KM, LM, PG>), pgrid, blk, 0, st, (const TIN*)W, ldw, N, d, f, \
                      isig, cb, K, B, row_words, rho, plan_K, lists, lists2, packed)
       if (plan_lmax(K) == 8) {
-        if (wdt == QAMW_F32) QAMW_PLAN_LAUNCH(float, 2048, 8, 4); else QAMW_PLAN_LAUNCH(uint16_t, 2048, 8, 4);
+        if (wdt == QAMW_F32) QAMW_PLAN_LAUNCH(float, 2048, 8, 2); else QAMW_PLAN_LAUNCH(uint16_t, 2048, 8, 2);
       } else {
         if (wdt == QAMW_F32) QAMW_PLAN_LAUNCH(float, 4096, 16, 2); else QAMW_PLAN_LAUNCH(uint16_t, 4096, 16, 2);
       }
