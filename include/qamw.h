@@ -102,7 +102,9 @@ const char* qamw_version(void);
  *   W         [N][ldw] of wdtype (QAMW_F32 or QAMW_BF16)
  *   chan_rms  [d] float32, r_j > 0: RMS of input channel j's activations
  *   alpha     finite exponent; s_j = r_j ^ alpha (alpha = 0 gives s = 1)
- *   block     Hadamard block b: power of two, 16 <= b <= 1024, d % b == 0
+ *   block     Hadamard block b: power of two, 2 <= b <= 1024, d % b == 0; the
+ *             row length d must also be a multiple of 16 (QAMW_EUNSUPPORTED
+ *             otherwise: the kernels give each lane 16 columns)
  *   s_out     [d] float32 out: s_j
  *   sigma_out [d/2] float32 out: sigma_k = sum_n |z_{n,k}| / (N sqrt(pi/2)),
  *             |z_{n,k}| taken on the normalised rotated row u_n (0 for rho_n = 0)
@@ -117,14 +119,18 @@ int32_t qamw_calibrate(const void* W, int32_t wdtype, int64_t N, int64_t d, int6
 /*
  * Nearest-centroid search plan (QAM-W, Methodology: Joint 2D Quantization).
  * An optional, codebook-specific acceleration structure for qamw_encode: a
- * 512 x 512 grid over [-5, 5)^2 and a 256 x 256 grid over [-40, 40)^2 whose
- * cells list, in ascending index order, every centroid that can be the
- * nearest one (under qamw_encode's fp32 scores) for some point of the cell.
- * Encoding with a plan gives the same indices, bit for bit, as encoding
- * without one; pairs beyond both grids and cells with too many candidates
- * fall back to scanning all K centroids.  The outer grid's cells that tile
- * [-5, 5)^2 are never consulted (points there take the fine grid) and are
- * marked "scan all".
+ * grid over [-5, 5)^2 and a 256 x 256 grid over [-40, 40)^2 whose cells
+ * list, in ascending index order, every centroid that can be the nearest one
+ * (under qamw_encode's fp32 scores) for some point of the cell.  For
+ * K <= 2048 the inner grid is a table the encode keeps in LDS: cells narrow
+ * near the origin and wider away from it (edges on 2048 equal bins per axis),
+ * each listing exactly the centroids whose Voronoi region, widened by the fp32
+ * scores' error bound, meets the cell; equal lists are stored once.  For
+ * larger K it is a uniform 512 x 512 grid of per-cell records.  Encoding with
+ * a plan gives the same indices, bit for bit, as encoding without one; pairs
+ * beyond both grids and cells with too many candidates fall back to scanning
+ * all K centroids.  The outer grid's cells that tile [-5, 5)^2 are never
+ * consulted (points there take the inner grid) and are marked "scan all".
  *
  * qamw_plan_bytes(K): bytes of device memory a plan for K centroids takes
  *   (0 for K outside [2, 4096]).  Host-only.
@@ -150,6 +156,8 @@ int32_t qamw_build_plan(const float* codebook, int32_t K, void* plan, size_t pla
  *              A plan built for another K is detected on the device and the
  *              whole codebook is scanned; one built for another codebook of
  *              the same K gives unspecified (in-range) indices
+ *   plan_size  bytes of the plan buffer (ignored when plan is NULL); less than
+ *              qamw_plan_bytes(K) is rejected (QAMW_EWORKSPACE) before any launch
  *   packed     [N][qamw_packed_row_words(d, K)] uint32 out
  *   rownorm_f16[N] uint16 out: binary16 bits of rho_n (RNE)
  *   workspace  >= qamw_encode_workspace_bytes(N, d), 256-byte aligned
@@ -159,7 +167,7 @@ int32_t qamw_build_plan(const float* codebook, int32_t K, void* plan, size_t pla
  */
 int32_t qamw_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
                     const float* s, const float* sigma, int32_t block, uint64_t sign_seed,
-                    const float* codebook, int32_t K, const void* plan,
+                    const float* codebook, int32_t K, const void* plan, size_t plan_size,
                     uint32_t* packed, uint16_t* rownorm_f16,
                     void* workspace, size_t workspace_bytes, void* stream);
 
@@ -185,8 +193,8 @@ int32_t qamw_encode_prepare(const void* W, int32_t wdtype, int64_t N, int64_t d,
                             const float* s, const float* sigma, int32_t block, uint64_t sign_seed,
                             uint16_t* rownorm_f16, void* workspace, size_t workspace_bytes, void* stream);
 int32_t qamw_encode_indices(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, int32_t block,
-                            const float* codebook, int32_t K, const void* plan, uint32_t* packed,
-                            const void* workspace, size_t workspace_bytes, void* stream);
+                            const float* codebook, int32_t K, const void* plan, size_t plan_size,
+                            uint32_t* packed, const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Calibration and encode in one call (QAM-W, Methodology: Activation-Aware
@@ -202,7 +210,7 @@ int32_t qamw_encode_indices(const void* W, int32_t wdtype, int64_t N, int64_t d,
 size_t qamw_calibrate_encode_workspace_bytes(int64_t N, int64_t d);
 int32_t qamw_calibrate_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
                               const float* chan_rms, float alpha, int32_t block, uint64_t sign_seed,
-                              const float* codebook, int32_t K, const void* plan,
+                              const float* codebook, int32_t K, const void* plan, size_t plan_size,
                               float* s_out, float* sigma_out, uint32_t* packed, uint16_t* rownorm_f16,
                               void* workspace, size_t workspace_bytes, void* stream);
 

@@ -344,14 +344,26 @@ def encode(W: np.ndarray, s: np.ndarray, sigma: np.ndarray, b: int, sign_seed: i
     }
 
 
+def inverse_scale(s) -> np.ndarray:
+    """1 / s_j, taken as 0 where s_j = 0: a channel whose activations are all
+    zero (r_j = 0, so s_j = 0 for alpha > 0) contributes nothing to a layer
+    output, so its decoded weights and its activations are dropped."""
+    s = np.asarray(s, dtype=np.float64)
+    safe = np.where(s != 0.0, s, 1.0)
+    return np.where(s != 0.0, 1.0 / safe, 0.0)
+
+
 def decode(packed: np.ndarray, rho_hat_bits: np.ndarray, s, sigma: np.ndarray, b: int,
            sign_seed: int, C: np.ndarray, d: int) -> np.ndarray:
     """Decode (QAM-W, Methodology, Decoding): unpack, look up the centroids,
     multiply by sigma_k, undo the rotation, multiply by the stored row norm.
 
     Reading: decode also divides by s_j, returning an approximation of W; with
-    s = None it stops at W' = W diag(s).  Indices >= K (impossible from
-    ``encode``) are clamped to K - 1.  Returns fp64 (N, d).
+    s = None it stops at W' = W diag(s).  A column with s_j = 0 (an input
+    channel whose activations are all zero, so that W' holds zeros there and
+    its weights never reach the layer output) decodes as 0 rather than as a
+    division by zero.  Indices >= K (impossible from ``encode``) are clamped
+    to K - 1.  Returns fp64 (N, d).
     """
     C = np.asarray(C, dtype=np.float32).reshape(-1, 2).astype(np.float64)
     K = C.shape[0]
@@ -364,7 +376,7 @@ def decode(packed: np.ndarray, rho_hat_bits: np.ndarray, s, sigma: np.ndarray, b
     Uh = rotate_inverse(Yh, sign_mask(sign_seed, d), b)
     Wh = f16_bits_to_f64(rho_hat_bits)[:, None] * Uh
     if s is not None:
-        Wh = Wh / np.asarray(s, dtype=np.float64)[None, :]
+        Wh = Wh * inverse_scale(s)[None, :]
     return Wh
 
 
@@ -391,7 +403,7 @@ def rotate_activations(X: np.ndarray, s, b: int, sign_seed: int) -> np.ndarray:
     weight row.  fp64 (T, d)."""
     X = np.asarray(X, dtype=np.float64)
     if s is not None:
-        X = X / np.asarray(s, dtype=np.float64)[None, :]
+        X = X * inverse_scale(s)[None, :]
     return rotate_forward(X, sign_mask(sign_seed, X.shape[1]), b)
 
 

@@ -41,6 +41,31 @@ def test_every_declared_symbol_is_exported(lib):
         assert name in _lib.SIGNATURES, f"{name} has no Python binding"
 
 
+
+def lds_plan_layout(K):
+    """The plan layout for K <= 2048, written out: cell edges on 2048 bins over
+    [-5, 5) with widths round(7 sqrt(2048 / K) exp(t^2 / 8)) clamped to
+    [1, 255] bins (t: the inner edge's coordinate), mirrored about 0; an image
+    of the bin map, G x G 16-bit entries and as many 8-byte list records as fit
+    160 KB - 1 KB of LDS next to the codebook (16 K bytes) and 16 wavefronts'
+    64 B-byte packing stages."""
+    h, w0 = 10 / 2048, 7 * math.sqrt(2048 / K)
+    pos = [1024]
+    while pos[-1] < 2048:
+        t = (pos[-1] - 1024) * h
+        w = min(255, max(1, math.floor(w0 * math.exp(t * t / 8) + 0.5)))
+        pos.append(min(2048, pos[-1] + w))
+    edges = [2048 - p for p in reversed(pos[1:])] + pos
+    G = len(edges) - 1
+    B = math.ceil(math.log2(K))
+    up = lambda v, a: -(-v // a) * a
+    lists_off = 2048 + up(2 * G * G, 16)
+    cap = min((159 * 1024 - 16 * K - 16 * 64 * B - lists_off) // 8, 32767) & ~1
+    image = lists_off + 8 * cap
+    scratch = up(G * G * 16, 256) + 2 * up(G * G * 4, 256) + 256 + 256 * 4 + 32768 * 16
+    return dict(G=G, edges=edges, cap=cap, image_bytes=image,
+                plan_bytes=up(256 + 256 * 256 * 16 + image, 256) + scratch)
+
 def test_host_helpers(lib):
     for K in (2, 3, 4, 256, 257, 2048, 4096):
         assert lib.qamw_index_bits(K) == math.ceil(math.log2(K))
@@ -58,11 +83,14 @@ def test_host_helpers(lib):
     assert lib.qamw_calibrate_workspace_bytes(4096, 11008, 256) == 4096 * 8 + 11008 * 4 + 256 * 5504 * 4
     assert lib.qamw_calibrate_workspace_bytes(0, 16, 16) == 0
     assert lib.qamw_status_string(-4) == b"workspace missing or too small"
-    # header block + one uint16 record of lmax entries per cell of the fine
-    # 512 x 512 grid and of the outer 256 x 256 grid
-    assert lib.qamw_plan_bytes(256) == 256 + (512 ** 2 + 256 ** 2) * 8 * 2
-    assert lib.qamw_plan_bytes(2048) == 256 + (512 ** 2 + 256 ** 2) * 8 * 2
+    # K > 2048: header block + one uint16 record of 16 entries per cell of the
+    # uniform 512 x 512 grid and of the outer 256 x 256 grid; K <= 2048:
+    # header, outer grid (8 entries), the LDS table image and its build scratch
     assert lib.qamw_plan_bytes(4096) == 256 + (512 ** 2 + 256 ** 2) * 16 * 2
+    for K in (2, 16, 256, 1000, 2048):
+        assert lib.qamw_plan_bytes(K) == lds_plan_layout(K)["plan_bytes"], K
+    g = lds_plan_layout(2048)
+    assert g["G"] == 150 and g["image_bytes"] + 16 * 2048 + 16 * 64 * 11 <= 160 * 1024
     assert lib.qamw_plan_bytes(1) == 0 and lib.qamw_plan_bytes(4097) == 0
 
 
@@ -75,11 +103,11 @@ WS = 1 << 24
 
 def _encode(lib, **kw):
     args = dict(W=A, wdt=1, N=8, d=256, ldw=256, s=A, sigma=A, block=128, seed=0, cb=A, K=256, plan=None,
-                packed=A, rn=A, ws=WS, ws_bytes=1 << 20, stream=None)
+                plan_size=1 << 26, packed=A, rn=A, ws=WS, ws_bytes=1 << 20, stream=None)
     args.update(kw)
     return lib.qamw_encode(args["W"], args["wdt"], args["N"], args["d"], args["ldw"], args["s"], args["sigma"],
-                           args["block"], args["seed"], args["cb"], args["K"], args["plan"], args["packed"],
-                           args["rn"], args["ws"], args["ws_bytes"], args["stream"])
+                           args["block"], args["seed"], args["cb"], args["K"], args["plan"], args["plan_size"],
+                           args["packed"], args["rn"], args["ws"], args["ws_bytes"], args["stream"])
 
 
 def _prepare(lib, **kw):
@@ -92,16 +120,16 @@ def _prepare(lib, **kw):
 
 
 def _indices(lib, **kw):
-    args = dict(W=A, wdt=1, N=8, d=256, ldw=256, block=128, cb=A, K=256, plan=None, packed=A, ws=WS,
-                ws_bytes=1 << 20, stream=None)
+    args = dict(W=A, wdt=1, N=8, d=256, ldw=256, block=128, cb=A, K=256, plan=None, plan_size=1 << 26, packed=A,
+                ws=WS, ws_bytes=1 << 20, stream=None)
     args.update(kw)
     return lib.qamw_encode_indices(args["W"], args["wdt"], args["N"], args["d"], args["ldw"], args["block"],
-                                   args["cb"], args["K"], args["plan"], args["packed"], args["ws"],
+                                   args["cb"], args["K"], args["plan"], args["plan_size"], args["packed"], args["ws"],
                                    args["ws_bytes"], args["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(block=8), -2), (dict(N=0), -1), (dict(W=MIS), -1), (dict(s=None), -1), (dict(sigma=MIS), -1),
+    (dict(block=1), -2), (dict(N=0), -1), (dict(W=MIS), -1), (dict(s=None), -1), (dict(sigma=MIS), -1),
     (dict(rn=None), -1), (dict(ws=None), -4), (dict(ws_bytes=8), -4), (dict(ws=WS + 16), -4), (dict(wdt=2), -2),
 ])
 def test_encode_prepare_rejects(lib, kw, status):
@@ -110,8 +138,9 @@ def test_encode_prepare_rejects(lib, kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(block=8), -2), (dict(K=1), -2), (dict(cb=MIS), -1), (dict(packed=None), -1), (dict(packed=MIS), -1),
+    (dict(block=1), -2), (dict(K=1), -2), (dict(cb=MIS), -1), (dict(packed=None), -1), (dict(packed=MIS), -1),
     (dict(plan=WS + 64), -1), (dict(ws=None), -4), (dict(ws_bytes=100), -4), (dict(ldw=100), -1),
+    (dict(plan=WS, plan_size=1000), -4), (dict(plan=WS, K=2048, plan_size=1 << 20), -4),
 ])
 def test_encode_indices_rejects(lib, kw, status):
     assert _indices(lib, **kw) == status
@@ -129,7 +158,7 @@ def _polar(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(block=8), -2), (dict(Ka=0), -2), (dict(Kp=0), -2), (dict(Ka=1, Kp=1), -2), (dict(Ka=64, Kp=128), -2),
+    (dict(block=1), -2), (dict(Ka=0), -2), (dict(Kp=0), -2), (dict(Ka=1, Kp=1), -2), (dict(Ka=64, Kp=128), -2),
     (dict(lv=None), -1), (dict(dirs=None), -1), (dict(packed=MIS), -1), (dict(s=None), -1), (dict(rn=None), -1),
     (dict(ws=None), -4), (dict(ws_bytes=100), -4), (dict(ldw=100), -1), (dict(wdt=2), -2),
 ])
@@ -187,17 +216,18 @@ def test_metric_workspace_sizes(lib):
 
 def _cal_enc(lib, **kw):
     args = dict(W=A, wdt=1, N=8, d=256, ldw=256, r=A, alpha=0.5, block=128, seed=0, cb=A, K=256, plan=None,
-                s=A, sigma=A, packed=A, rn=A, ws=WS, ws_bytes=1 << 20, stream=None)
+                plan_size=1 << 26, s=A, sigma=A, packed=A, rn=A, ws=WS, ws_bytes=1 << 20, stream=None)
     args.update(kw)
     return lib.qamw_calibrate_encode(args["W"], args["wdt"], args["N"], args["d"], args["ldw"], args["r"],
                                      args["alpha"], args["block"], args["seed"], args["cb"], args["K"], args["plan"],
-                                     args["s"], args["sigma"], args["packed"], args["rn"], args["ws"],
-                                     args["ws_bytes"], args["stream"])
+                                     args["plan_size"], args["s"], args["sigma"], args["packed"], args["rn"],
+                                     args["ws"], args["ws_bytes"], args["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(block=8), -2), (dict(K=1), -2), (dict(r=None), -1), (dict(s=MIS), -1), (dict(packed=None), -1),
+    (dict(block=1), -2), (dict(K=1), -2), (dict(r=None), -1), (dict(s=MIS), -1), (dict(packed=None), -1),
     (dict(rn=None), -1), (dict(alpha=float("nan")), -1), (dict(plan=WS + 64), -1), (dict(ws=None), -4),
+    (dict(plan=WS, plan_size=4096), -4),
     (dict(ws_bytes=1000), -4), (dict(ldw=100), -1), (dict(wdt=2), -2),
 ])
 def test_calibrate_encode_rejects(lib, kw, status):
@@ -222,7 +252,7 @@ def _lloyd(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(block=8), -2), (dict(K=1), -2), (dict(packed=None), -1), (dict(packed=MIS), -1), (dict(out=None), -1),
+    (dict(block=1), -2), (dict(K=1), -2), (dict(packed=None), -1), (dict(packed=MIS), -1), (dict(out=None), -1),
     (dict(out=A), -1), (dict(dist=None), -1), (dict(dist=A + 4), -1), (dict(enc=None), -4), (dict(enc_bytes=64), -4),
     (dict(ws=None), -4), (dict(ws_bytes=1024), -4), (dict(ldw=100), -1),
 ])
@@ -259,7 +289,7 @@ def _mv(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(block=8), -2), (dict(d=200), -1), (dict(N=0), -1), (dict(K=1), -2), (dict(x=None), -1), (dict(x=MIS), -1),
+    (dict(block=1), -2), (dict(d=200), -1), (dict(N=0), -1), (dict(K=1), -2), (dict(x=None), -1), (dict(x=MIS), -1),
     (dict(s=MIS), -1), (dict(packed=None), -1), (dict(y=None), -1), (dict(xdt=2), -2), (dict(ydt=2), -2),
 ])
 def test_decode_matvec_rejects(lib, kw, status):
@@ -286,12 +316,12 @@ def _decode(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(block=3), -2), (dict(block=8), -2), (dict(block=2048), -2), (dict(block=128, d=320), -1),
+    (dict(block=3), -2), (dict(block=1), -2), (dict(block=8, d=264), -2), (dict(block=2048), -2), (dict(block=128, d=320), -1),
     (dict(N=0), -1), (dict(d=-16), -1), (dict(K=1), -2), (dict(K=4097), -2), (dict(ldw=128), -1),
     (dict(W=None), -1), (dict(cb=None), -1), (dict(s=None), -1), (dict(packed=None), -1),
     (dict(W=MIS), -1), (dict(packed=MIS), -1), (dict(wdt=2), -2), (dict(ldw=260), -1),
     (dict(ws=None), -4), (dict(ws_bytes=8), -4), (dict(ws=WS + 16), -4), (dict(cb=MIS), -1),
-    (dict(plan=WS + 128), -1),
+    (dict(plan=WS + 128), -1), (dict(plan=WS, plan_size=1000), -4),
 ])
 def test_encode_rejects(lib, kw, status):
     assert _encode(lib, **kw) == status
@@ -331,7 +361,7 @@ def test_workspace_size_is_enforced(lib):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(block=8), -2), (dict(T=0), -1), (dict(X=None), -1), (dict(X=MIS), -1), (dict(xdt=2), -2),
+    (dict(block=1), -2), (dict(T=0), -1), (dict(X=None), -1), (dict(X=MIS), -1), (dict(xdt=2), -2),
     (dict(out=None), -1), (dict(out=MIS), -1), (dict(ldr=260), -1), (dict(ldx=100), -1), (dict(s=MIS), -1),
 ])
 def test_rotate_activations_rejects(lib, kw, status):

@@ -248,6 +248,37 @@ def test_degenerate_rows_and_columns():
     assert np.array_equal(Wc, Wk)
 
 
+def test_dead_channel_decodes_as_zero():
+    """r_j = 0 (a channel whose activations are all zero) gives s_j = 0 for
+    alpha > 0: the channel is zeroed before quantisation, decodes as 0 instead
+    of dividing by zero, and its activations are dropped by the rotated-form
+    product, so X W^^T equals X~ W'^T on the other channels.  Pinned
+    independently of inverse_scale: the lossless codebook reproduces every
+    other column exactly up to rho_hat / rho, and the product is checked
+    against a plain matmul with column j removed."""
+    rng = np.random.default_rng(13)
+    N, d, b, seed, j = 4, 16, 8, 2, 5
+    W = rng.standard_normal((N, d))
+    r = rng.lognormal(0, 0.5, d)
+    r[j] = 0.0
+    s, sig, rho = Q.calibrate(W, r, 0.5, b, seed)
+    assert s[j] == 0.0 and np.all(np.isfinite(sig))
+    Zt, _ = Q.normalized_pairs(W, s, sig, b, seed)
+    C = Zt.reshape(-1, 2).astype(np.float32)
+    e = Q.encode(W, s, sig, b, seed, C)
+    Wh = Q.decode(e["packed"], e["rho_hat_bits"], s, sig, b, seed, C, d)
+    assert np.all(np.isfinite(Wh)) and np.all(Wh[:, j] == 0.0)
+    rho_hat = Q.f16_bits_to_f64(e["rho_hat_bits"])
+    keep = np.arange(d) != j
+    want = W * (rho_hat / rho)[:, None]
+    assert np.max(np.abs(Wh[:, keep] - want[:, keep])) < 1e-5 * np.max(np.abs(want))
+    X = rng.standard_normal((3, d))
+    Xr = Q.rotate_activations(X, s, b, seed)
+    assert np.all(np.isfinite(Xr))
+    Y = Q.decode_matmul(X, e["packed"], e["rho_hat_bits"], s, sig, b, seed, C, d)
+    assert np.allclose(Y, X[:, keep] @ Wh[:, keep].T, rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- fp16 / bf16 rounding
 def test_half_rounding_pins():
     one = 1.0

@@ -28,12 +28,13 @@ SIGNATURES = {
     "qamw_calibrate": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _f32, _i32, _u64, _p, _p, _p, _sz, _p]),
     "qamw_plan_bytes": (_sz, [_i32]),
     "qamw_build_plan": (_i32, [_p, _i32, _p, _sz, _p]),
-    "qamw_encode": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _p, _p, _p, _sz, _p]),
+    "qamw_encode": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _sz, _p, _p, _p, _sz,
+                         _p]),
     "qamw_encode_prepare": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _p, _sz, _p]),
-    "qamw_encode_indices": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _i32, _p, _p, _p, _sz, _p]),
+    "qamw_encode_indices": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _i32, _p, _sz, _p, _p, _sz, _p]),
     "qamw_calibrate_encode_workspace_bytes": (_sz, [_i64, _i64]),
-    "qamw_calibrate_encode": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _f32, _i32, _u64, _p, _i32, _p, _p, _p, _p, _p,
-                                     _p, _sz, _p]),
+    "qamw_calibrate_encode": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _f32, _i32, _u64, _p, _i32, _p, _sz, _p, _p, _p,
+                                     _p, _p, _sz, _p]),
     "qamw_lloyd_workspace_bytes": (_sz, [_i32]),
     "qamw_lloyd_update": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _p, _i32, _p, _sz, _p, _p, _p, _sz, _p]),
     "qamw_learn_codebook": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _sz, _p, _i32, _i32, _p, _p, _p, _sz, _p,

@@ -186,8 +186,8 @@ def qamw_encode(W: torch.Tensor, s: torch.Tensor, sigma: torch.Tensor, block: in
         workspace = _workspace(need, W.device)
     _lib.check("qamw_encode", _lib.load().qamw_encode(
         W.data_ptr(), _WDT[W.dtype], N, d, ldw, s.data_ptr(), sigma.data_ptr(), int(block), int(sign_seed),
-        codebook.data_ptr(), K, None if plan is None else plan.data_ptr(), packed.data_ptr(),
-        rownorm_f16.data_ptr(), workspace.data_ptr(),
+        codebook.data_ptr(), K, None if plan is None else plan.data_ptr(), 0 if plan is None else plan.numel(),
+        packed.data_ptr(), rownorm_f16.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return packed, rownorm_f16
 
@@ -233,7 +233,8 @@ def qamw_calibrate_encode(W: torch.Tensor, chan_rms: torch.Tensor, alpha: float,
         workspace = _workspace(qamw_calibrate_encode_workspace_bytes(N, d), W.device)
     _lib.check("qamw_calibrate_encode", _lib.load().qamw_calibrate_encode(
         W.data_ptr(), _WDT[W.dtype], N, d, ldw, chan_rms.data_ptr(), float(alpha), int(block), int(sign_seed),
-        codebook.data_ptr(), K, None if plan is None else plan.data_ptr(), s_out.data_ptr(), sigma_out.data_ptr(),
+        codebook.data_ptr(), K, None if plan is None else plan.data_ptr(), 0 if plan is None else plan.numel(),
+        s_out.data_ptr(), sigma_out.data_ptr(),
         packed.data_ptr(), rownorm_f16.data_ptr(), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return s_out, sigma_out, packed, rownorm_f16
@@ -282,7 +283,8 @@ def qamw_encode_indices(W: torch.Tensor, block: int, codebook: torch.Tensor, wor
     _dev(workspace, "workspace")
     _lib.check("qamw_encode_indices", _lib.load().qamw_encode_indices(
         W.data_ptr(), _WDT[W.dtype], N, d, ldw, int(block), codebook.data_ptr(), K,
-        None if plan is None else plan.data_ptr(), packed.data_ptr(), workspace.data_ptr(),
+        None if plan is None else plan.data_ptr(), 0 if plan is None else plan.numel(), packed.data_ptr(),
+        workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return packed
 

@@ -46,8 +46,10 @@ int check_matrix(int64_t N, int64_t d, int32_t block, int* L) {
   if (N > kMaxDim || d > kMaxDim || N * ((d + 1023) / 1024) > (int64_t(1) << 30))
     return fail(QAMW_EUNSUPPORTED, "matrix too large");
   *L = log2_exact(block);
-  if (*L < 4 || *L > 10) return fail(QAMW_EUNSUPPORTED, "block must be a power of two in [16, 1024] (got %d)", block);
+  if (*L < 1 || *L > 10) return fail(QAMW_EUNSUPPORTED, "block must be a power of two in [2, 1024] (got %d)", block);
   if (d % block) return fail(QAMW_EINVAL, "d=%lld is not a multiple of block=%d", (long long)d, block);
+  // a lane owns 16 columns: with blocks under 16 the row must still be whole 16-column chunks
+  if (d % 16) return fail(QAMW_EUNSUPPORTED, "d=%lld is not a multiple of 16", (long long)d);
   return QAMW_OK;
 }
 
@@ -64,6 +66,16 @@ int check_codebook(const float* cb, int32_t K) {
   if (!cb) return fail(QAMW_EINVAL, "codebook is NULL");
   if (!aligned16(cb)) return fail(QAMW_EINVAL, "codebook must be 16-byte aligned");
   if (K < 2 || K > 4096) return fail(QAMW_EUNSUPPORTED, "K=%d outside [2, 4096]", K);
+  return QAMW_OK;
+}
+
+// A search plan passed to an encode: NULL, or 256-byte aligned with at least
+// plan_bytes(K) bytes (the kernels read that much of it).
+int check_plan(const void* plan, size_t plan_size, int32_t K) {
+  if (!plan) return QAMW_OK;
+  if ((uintptr_t)plan & 255u) return fail(QAMW_EINVAL, "plan must be 256-byte aligned");
+  if (plan_size < plan_bytes(K))
+    return fail(QAMW_EWORKSPACE, "a plan for K=%d needs %zu bytes (got %zu)", (int)K, plan_bytes(K), plan_size);
   return QAMW_OK;
 }
 
@@ -198,7 +210,7 @@ int32_t qamw_encode_prepare(const void* W, int32_t wdtype, int64_t N, int64_t d,
 }
 
 int32_t qamw_encode_indices(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, int32_t block,
-                            const float* codebook, int32_t K, const void* plan, uint32_t* packed,
+                            const float* codebook, int32_t K, const void* plan, size_t plan_size, uint32_t* packed,
                             const void* workspace, size_t workspace_bytes, void* stream) {
   int L = 0;
   int rc = check_matrix(N, d, block, &L);
@@ -207,7 +219,7 @@ int32_t qamw_encode_indices(const void* W, int32_t wdtype, int64_t N, int64_t d,
   if ((rc = check_codebook(codebook, K))) return rc;
   if (!packed) return fail(QAMW_EINVAL, "packed must be non-NULL");
   if (!aligned16(packed)) return fail(QAMW_EINVAL, "packed must be 16-byte aligned");
-  if (plan && ((uintptr_t)plan & 255u)) return fail(QAMW_EINVAL, "plan must be 256-byte aligned");
+  if ((rc = check_plan(plan, plan_size, K))) return rc;
   if ((rc = check_encode_workspace(workspace, workspace_bytes, N, d))) return rc;
   const EncodeWorkspace e = encode_workspace(const_cast<void*>(workspace), N, d);
   return launch_encode(L, W, wdtype, (int)N, (int)d, ldw, e.f, e.isig, codebook, (int)K, qamw_index_bits(K),
@@ -216,7 +228,7 @@ int32_t qamw_encode_indices(const void* W, int32_t wdtype, int64_t N, int64_t d,
 
 int32_t qamw_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, const float* s,
                     const float* sigma, int32_t block, uint64_t sign_seed, const float* codebook, int32_t K,
-                    const void* plan, uint32_t* packed, uint16_t* rownorm_f16, void* workspace,
+                    const void* plan, size_t plan_size, uint32_t* packed, uint16_t* rownorm_f16, void* workspace,
                     size_t workspace_bytes, void* stream) {
   // validate everything before the first launch
   int L = 0;
@@ -227,13 +239,13 @@ int32_t qamw_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t
   if (!s || !sigma || !packed || !rownorm_f16) return fail(QAMW_EINVAL, "s, sigma, packed and rownorm_f16 must be non-NULL");
   if (!aligned16(s) || !aligned16(sigma) || !aligned16(packed))
     return fail(QAMW_EINVAL, "s, sigma and packed must be 16-byte aligned");
-  if (plan && ((uintptr_t)plan & 255u)) return fail(QAMW_EINVAL, "plan must be 256-byte aligned");
+  if ((rc = check_plan(plan, plan_size, K))) return rc;
   if ((rc = check_encode_workspace(workspace, workspace_bytes, N, d))) return rc;
   if ((rc = qamw_encode_prepare(W, wdtype, N, d, ldw, s, sigma, block, sign_seed, rownorm_f16, workspace,
                                 workspace_bytes, stream)))
     return rc;
-  return qamw_encode_indices(W, wdtype, N, d, ldw, block, codebook, K, plan, packed, workspace, workspace_bytes,
-                             stream);
+  return qamw_encode_indices(W, wdtype, N, d, ldw, block, codebook, K, plan, plan_size, packed, workspace,
+                             workspace_bytes, stream);
 }
 
 size_t qamw_calibrate_encode_workspace_bytes(int64_t N, int64_t d) {
@@ -244,9 +256,9 @@ size_t qamw_calibrate_encode_workspace_bytes(int64_t N, int64_t d) {
 
 int32_t qamw_calibrate_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
                               const float* chan_rms, float alpha, int32_t block, uint64_t sign_seed,
-                              const float* codebook, int32_t K, const void* plan, float* s_out, float* sigma_out,
-                              uint32_t* packed, uint16_t* rownorm_f16, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+                              const float* codebook, int32_t K, const void* plan, size_t plan_size, float* s_out,
+                              float* sigma_out, uint32_t* packed, uint16_t* rownorm_f16, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   int L = 0;
   int rc = check_matrix(N, d, block, &L);
   if (rc) return rc;
@@ -257,7 +269,7 @@ int32_t qamw_calibrate_encode(const void* W, int32_t wdtype, int64_t N, int64_t 
   if (!aligned16(s_out) || !aligned16(sigma_out) || !aligned16(packed))
     return fail(QAMW_EINVAL, "s_out, sigma_out and packed must be 16-byte aligned");
   if (!isfinite(alpha)) return fail(QAMW_EINVAL, "alpha must be finite");
-  if (plan && ((uintptr_t)plan & 255u)) return fail(QAMW_EINVAL, "plan must be 256-byte aligned");
+  if ((rc = check_plan(plan, plan_size, K))) return rc;
   const size_t need = qamw_calibrate_encode_workspace_bytes(N, d);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
     return fail(QAMW_EWORKSPACE, "calibrate_encode needs %zu bytes of 256-byte aligned workspace (got %zu)", need,

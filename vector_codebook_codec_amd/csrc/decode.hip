@@ -16,13 +16,8 @@ namespace qamw {
 
 // Decode tunables: rows whose packed words are loaded ahead, and wavefronts
 // of work per CU the launch aims for (each wave then walks several rows).
-#ifndef QAMW_DECODE_PREFETCH
-#define QAMW_DECODE_PREFETCH 3
-#endif
-#ifndef QAMW_DECODE_WAVES_PER_CU
-#define QAMW_DECODE_WAVES_PER_CU 20
-#endif
-constexpr int kDecodePrefetch = QAMW_DECODE_PREFETCH;
+constexpr int kDecodePrefetch = 3;
+constexpr int kDecodeWavesPerCu = 20;
 constexpr int kDecodeMaxRows = 16;   // rows per wavefront, at most
 
 // ---------------------------------------------------------------------------
@@ -155,7 +150,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(L
     for (int q = 0; q < kPer; ++q) {
       const int t = q * kBlockThreads + threadIdx.x;
       const int j = win * kWinChunks * kChunk + t;
-      gwin[t] = (j < d) ? sign_eps(seed, j) * (inv_sqrt_b / sv[q]) : 0.0f;
+      gwin[t] = (j < d) ? sign_eps(seed, j) * col_scale(inv_sqrt_b, sv[q]) : 0.0f;
     }
   }
   __syncthreads();
@@ -250,11 +245,11 @@ int launch_decode_bt(const uint32_t* packed, const uint16_t* rho_f16, int N, int
   // Persistent-style grid: every workgroup keeps one window (codebook and
   // column factors loaded once) and walks rows with a stride.  Aim for the
   // workgroups that fit on the chip at once (LDS-limited, at most
-  // QAMW_DECODE_WAVES_PER_CU / 4 per CU), unless that would give a wave more
+  // kDecodeWavesPerCu / 4 per CU), unless that would give a wave more
   // than kDecodeMaxRows rows: then the stride grows and the grid runs in
   // several rounds.
   int64_t per_cu = (int64_t)(160 * 1024 / lds);
-  const int64_t cap = QAMW_DECODE_WAVES_PER_CU / kWavesPerBlock;
+  const int64_t cap = kDecodeWavesPerCu / kWavesPerBlock;
   per_cu = per_cu < 1 ? 1 : (per_cu > cap ? cap : per_cu);
   int64_t bpw = 256 * per_cu / nwin;
   const int64_t need = (N + kWavesPerBlock - 1) / kWavesPerBlock;   // one row per wave at most

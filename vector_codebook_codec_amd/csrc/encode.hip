@@ -191,7 +191,19 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
       const float sc = __builtin_fmaf(z.y, cby[ci], __builtin_fmaf(z.x, cbx[ci], cbh[ci]));
       id = (sc == bb) ? min(id, ci) : id;
     }
-    idxv[m2] = (uint32_t)min(id, K - 1);
+    // no score of the tile equals the minimum (a NaN pair has no finite
+    // score): the whole codebook on the VALU, first strict minimum, as the
+    // planned search's scan does -- index 0 when no score is below +inf
+    if (__any(id == INT_MAX)) {
+      float fb = INFINITY;
+      int fo = 0;
+      for (int cc = 0; cc < K; ++cc) {                 // same address in every lane: broadcast
+        const float sc = __builtin_fmaf(z.y, cby[cc], __builtin_fmaf(z.x, cbx[cc], cbh[cc]));
+        if (sc < fb) { fb = sc; fo = cc; }
+      }
+      if (id == INT_MAX) id = fo;
+    }
+    idxv[m2] = (uint32_t)id;
   }
 
   // ---- pack: stage the window's 512 indices (reusing the pair buffer), then
@@ -367,6 +379,205 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
   }
 }
 
+// ---------------------------------------------------------------------------
+// Encode with the LDS search table (plan.hip, K <= kLdsMaxK).  One workgroup
+// of 16 wavefronts per CU keeps the codebook (-cx, -cy, |c|^2/2, 0) and the
+// plan's table image in LDS: a bin -> cell map shared by both axes, one
+// 16-bit entry per cell (16 c: the cell's only candidate; 0x8000 | r: list
+// record r; 0xFFFF: scan the whole codebook) and the list records (4 x 16 c,
+// ascending, the tail repeating the last; the top bit of the fourth entry
+// continues the list in record r + 1).  A pair looks its cell up, scores its
+// list with the same fp32 FMA sequence and strict "<" as the exhaustive
+// search, and so returns its index.  Pairs outside [-R, R)^2 take the outer
+// grid's record (global memory), or scan the whole codebook beyond it.
+// Indices are packed from registers through a byte stage per wavefront.
+// ---------------------------------------------------------------------------
+template <int L, typename Tin>
+__global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))) void encode_lds_kernel(
+    const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ f,
+    const float* __restrict__ isig, const float* __restrict__ codebook, int K, int B, int row_words,
+    const double* __restrict__ rho, const int* __restrict__ plan_K, const uint4* __restrict__ image, int image_bytes,
+    int G, int lists_off, const uint16_t* __restrict__ outer, uint32_t* __restrict__ packed) {
+  // LDS: the codebook at offset 0 (so a candidate's byte offset 16 c is its
+  // address), then the table image, then one packing stage per wavefront
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBudget];
+  float4* cb4 = reinterpret_cast<float4*>(lds);
+  const int cb_bytes = 16 * K;
+  const uint8_t* map = reinterpret_cast<const uint8_t*>(lds + cb_bytes);
+  const uint16_t* cells = reinterpret_cast<const uint16_t*>(lds + cb_bytes + kLdsBins);
+  const uint2* lists = reinterpret_cast<const uint2*>(lds + cb_bytes + lists_off);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int nchunks = d >> 4;
+  const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
+  const int total = N * nwin;                      // fits in int (checked on the host)
+  const int stride = gridDim.x * kLdsWaves;
+  int gw = blockIdx.x * kLdsWaves + wave;
+  // the first window's weights are in flight while the tables are staged
+  int n = min(gw, total - 1) / nwin, win = min(gw, total - 1) - (min(gw, total - 1) / nwin) * nwin;
+  WinLoads<Tin> wl;
+  load_window<L>(wl, W, ldw, f, isig, rho, n, win, lane, nchunks);
+  {
+    uint4* img = reinterpret_cast<uint4*>(lds + cb_bytes);
+    const int nv = image_bytes / 16;
+    constexpr int kU = 8;                          // loads in flight per thread (clamped, always valid)
+    for (int i0 = threadIdx.x; i0 < nv; i0 += kU * kLdsThreads) {
+      uint4 t[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) t[u] = image[min(i0 + u * kLdsThreads, nv - 1)];
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (i0 + u * kLdsThreads < nv) img[i0 + u * kLdsThreads] = t[u];
+    }
+  }
+  for (int c = threadIdx.x; c < K; c += kLdsThreads) {
+    const float cx = codebook[2 * c], cy = codebook[2 * c + 1];
+    cb4[c] = make_float4(-cx, -cy, 0.5f * __builtin_fmaf(cx, cx, cy * cy), 0.0f);
+  }
+  __syncthreads();
+  if (gw >= total) return;                         // no barriers follow
+  uint8_t* stage = reinterpret_cast<uint8_t*>(lds + cb_bytes + image_bytes + wave * 64 * B);
+  const bool plan_ok = *plan_K == K;               // a plan built for another K: scan the whole codebook
+
+  const float bins_per_unit = (float)kLdsBins / (2.0f * kPlanR);
+  const float bmax = __uint_as_float(__float_as_uint((float)kLdsBins) - 1u);   // largest float below kLdsBins
+  const float cells_per_unit2 = (float)kPlanG2 / (2.0f * kPlanR2);
+  const float tmax2 = __uint_as_float(__float_as_uint((float)kPlanG2) - 1u);
+
+  for (;;) {
+    const bool active = win * kWinChunks + lane < nchunks;   // whole Hadamard blocks are active or not
+    float zx[8], zy[8];
+    const int co_local = window_transform<L>(wl, active, lane, zx, zy);
+    const int n_cur = n, win_cur = win;
+    const int gnext = gw + stride;
+    {
+      const int gl = min(gnext, total - 1);
+      n = gl / nwin;
+      win = gl - n * nwin;
+      load_window<L>(wl, W, ldw, f, isig, rho, n, win, lane, nchunks);
+    }
+
+    uint32_t idx[8];
+#pragma unroll
+    for (int g = 0; g < 8; g += 4) {
+      uint32_t e[4];
+      // ---- cell lookups: bin t = x kLdsBins / (2R) + kLdsBins / 2 (its rounding,
+      // < 1e-3 bin, is inside the table's eta margin); the clamp changes nothing
+      // inside [-R, R), so "unchanged" is the range test (false for NaN)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float tx = __builtin_fmaf(zx[g + p], bins_per_unit, 0.5f * kLdsBins);
+        const float ty = __builtin_fmaf(zy[g + p], bins_per_unit, 0.5f * kLdsBins);
+        const float bx = __builtin_amdgcn_fmed3f(tx, 0.0f, bmax);
+        const float by = __builtin_amdgcn_fmed3f(ty, 0.0f, bmax);
+        const uint32_t ix = map[(int)bx], iy = map[(int)by];
+        const uint32_t ce = cells[__umul24(ix, (uint32_t)G) + iy];
+        e[p] = (plan_ok && bx == tx && by == ty) ? ce : (uint32_t)kLdsScanAll;
+      }
+      // ---- lists: the four slots' scores, their minimum, the first slot
+      // reaching it (as a strict "<" scan of the ascending list would)
+      uint32_t boff[4];
+      bool cont = false, wide = false;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        boff[p] = e[p];
+        wide |= e[p] == kLdsScanAll;
+        if (e[p] >= 0x8000u && e[p] != kLdsScanAll) {
+          const uint2 r = lists[e[p] & 0x7fffu];
+          const uint32_t o0 = r.x & 0xffffu, o1 = r.x >> 16, o2 = r.y & 0xffffu, o3 = (r.y >> 16) & 0x7fffu;
+          cont |= (r.y >> 31) != 0u;
+          const float4 t0 = cb4[o0 >> 4], t1 = cb4[o1 >> 4], t2 = cb4[o2 >> 4], t3 = cb4[o3 >> 4];
+          const float x = zx[g + p], y = zy[g + p];
+          const float s0 = __builtin_fmaf(y, t0.y, __builtin_fmaf(x, t0.x, t0.z));
+          const float s1 = __builtin_fmaf(y, t1.y, __builtin_fmaf(x, t1.x, t1.z));
+          const float s2 = __builtin_fmaf(y, t2.y, __builtin_fmaf(x, t2.x, t2.z));
+          const float s3 = __builtin_fmaf(y, t3.y, __builtin_fmaf(x, t3.x, t3.z));
+          const float m = fminf(fminf(s0, s1), fminf(s2, s3));
+          uint32_t o = o3;
+          o = (s2 == m) ? o2 : o;
+          o = (s1 == m) ? o1 : o;
+          o = (s0 == m) ? o0 : o;
+          boff[p] = o;
+        }
+      }
+      // ---- lists of 5..8: the continuation record (rare)
+      if (__any(cont)) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          if (e[p] >= 0x8000u && e[p] != kLdsScanAll) {
+            const uint2 r0 = lists[e[p] & 0x7fffu];
+            if (r0.y >> 31) {
+              const uint2 r = lists[(e[p] & 0x7fffu) + 1];
+              const uint32_t o[4] = {r.x & 0xffffu, r.x >> 16, r.y & 0xffffu, r.y >> 16};
+              const float4 tb = cb4[boff[p] >> 4];
+              float best = __builtin_fmaf(zy[g + p], tb.y, __builtin_fmaf(zx[g + p], tb.x, tb.z));
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float4 t = cb4[o[i] >> 4];
+                const float sc = __builtin_fmaf(zy[g + p], t.y, __builtin_fmaf(zx[g + p], t.x, t.z));
+                if (sc < best) { best = sc; boff[p] = o[i]; }
+              }
+            }
+          }
+        }
+      }
+      // ---- outside the table or a cell without a list: the outer grid's
+      // record, else the whole codebook (rare)
+      if (__any(wide)) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          if (!__any(e[p] == kLdsScanAll)) continue;
+          const float x = zx[g + p], y = zy[g + p];
+          const float ux = __builtin_fmaf(x, cells_per_unit2, 0.5f * kPlanG2);
+          const float uy = __builtin_fmaf(y, cells_per_unit2, 0.5f * kPlanG2);
+          const float vx = __builtin_amdgcn_fmed3f(ux, 0.0f, tmax2);
+          const float vy = __builtin_amdgcn_fmed3f(uy, 0.0f, tmax2);
+          // the outer grid is consulted only outside [-R, R)^2, where its
+          // records are lists (its cells inside the square say "scan all")
+          const bool full = e[p] == kLdsScanAll;
+          uint4 rec = make_uint4(1u << 16, 0u, 0u, 0u);
+          if (full && plan_ok && vx == ux && vy == uy)
+            rec = *reinterpret_cast<const uint4*>(outer + ((int)vx * kPlanG2 + (int)vy) * 8);
+          const uint32_t words[4] = {rec.x, rec.y, rec.z, rec.w};
+          const bool over = !full || ((words[0] >> 16) & 1u);
+          if (full && !over) {
+            const int cnt = (int)(words[0] & 15u) + 1;
+            float fb = INFINITY;
+            uint32_t fo = 0;
+            for (int i = 0; i < cnt; ++i) {
+              const uint32_t w = words[i >> 1];
+              const uint32_t off = ((i & 1) ? (w >> 16) : w) & 0xfff0u;
+              const float4 t = cb4[off >> 4];
+              const float sc = __builtin_fmaf(y, t.y, __builtin_fmaf(x, t.x, t.z));
+              if (sc < fb) { fb = sc; fo = off; }
+            }
+            boff[p] = fo;
+          }
+          if (__any(full && over)) {
+            float fb = INFINITY;
+            uint32_t fo = 0;
+            for (int cc = 0; cc < K; ++cc) {
+              const float4 t = cb4[cc];              // same address in every lane: broadcast
+              const float sc = __builtin_fmaf(y, t.y, __builtin_fmaf(x, t.x, t.z));
+              if (sc < fb) { fb = sc; fo = (uint32_t)cc * 16u; }
+            }
+            if (full && over) boff[p] = fo;
+          }
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) idx[g + p] = active ? (boff[p] & 0x7fffu) >> 4 : 0u;
+    }
+    stage_lane_bytes(stage, co_local, idx, B);
+    wave_lds_fence();
+    store_stage(stage, lane, win_cur, B, row_words, packed + (int64_t)n_cur * row_words);
+    gw = gnext;
+    if (gw >= total) break;
+    wave_lds_fence();                              // the stage is rewritten next round
+  }
+}
+
 // ===========================================================================
 // launcher
 // ===========================================================================
@@ -379,11 +590,31 @@ struct LaunchEncode {
     const int64_t waves = (int64_t)N * nwin;
     const dim3 grid((unsigned)((waves + kEncWaves - 1) / kEncWaves)), blk(kEncThreads);
     if (plan) {
-      // persistent: as many workgroups as fit at once (2 of 8 wavefronts per CU)
+      // persistent: as many workgroups as fit at once
       int dev = 0, cus = 0;
       if (hipGetDevice(&dev) != hipSuccess ||
           hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return fail(QAMW_EHIP, "cannot query the device's compute units");
+      LdsGeometry g;
+      if (lds_geometry(K, &g)) {                 // one 16-wavefront workgroup per CU
+        const char* base = (const char*)plan;
+        const int* plan_K = (const int*)(base + kPlanHeaderKOffset);
+        const uint4* image = (const uint4*)(base + plan_image_offset(K));
+        const uint16_t* outer = (const uint16_t*)(base + plan_outer_offset(K));
+        const int64_t wgs = (waves + kLdsWaves - 1) / kLdsWaves;
+        const dim3 lgrid((unsigned)std::min<int64_t>(wgs, (int64_t)cus)), lblk(kLdsThreads);
+        const size_t lds = (size_t)16 * K + g.image_bytes + (size_t)kLdsWaves * g.stage_bytes;
+        if (lds > kLdsBudget) return fail(QAMW_EUNSUPPORTED, "LDS table too large");
+        if (wdt == QAMW_F32)
+          hipLaunchKernelGGL((encode_lds_kernel<L, float>), lgrid, lblk, 0, st, (const float*)W, ldw, N, d, f, isig,
+                             cb, K, B, row_words, rho, plan_K, image, (int)g.image_bytes, g.G, (int)g.lists_off, outer,
+                             packed);
+        else
+          hipLaunchKernelGGL((encode_lds_kernel<L, uint16_t>), lgrid, lblk, 0, st, (const uint16_t*)W, ldw, N, d, f,
+                             isig, cb, K, B, row_words, rho, plan_K, image, (int)g.image_bytes, g.G, (int)g.lists_off,
+                             outer, packed);
+        return check_launch("encode_lds_kernel");
+      }
       const dim3 pgrid((unsigned)std::min<int64_t>(grid.x, (int64_t)cus * kPlanWgPerCu));
       const char* base = (const char*)plan;
       const int* plan_K = (const int*)(base + kPlanHeaderKOffset);

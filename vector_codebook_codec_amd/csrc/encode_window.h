@@ -105,4 +105,52 @@ __device__ __forceinline__ void pack_window(const uint16_t* stage, int lane, int
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Packing from registers.  A lane's 8 indices are those of the 8 consecutive
+// pairs of window chunk co, i.e. bits [8 B co, 8 B co + 8 B) of the window's
+// stream: exactly bytes [B co, B co + B).  stage_lane_bytes writes them into
+// the wavefront's 64 B-byte stage; store_stage then writes the window's
+// 16 B words from it with 16-byte stores (the last window of a row stops at
+// row_words; lanes past the row end must have staged zero indices, which are
+// the row's zero padding bits).
+// ---------------------------------------------------------------------------
+template <int BT>
+__device__ __forceinline__ void stage_lane_bytes_t(uint8_t* __restrict__ stage, int co, const uint32_t idx[8]) {
+  constexpr int B = BT;
+  uint32_t w[3] = {0u, 0u, 0u};
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int pos = p * B, wd = pos >> 5, sh = pos & 31;
+    w[wd] |= idx[p] << sh;
+    if (sh + B > 32) w[wd + 1] |= idx[p] >> (32 - sh);
+  }
+  uint8_t* dst = stage + B * co;
+#pragma unroll
+  for (int b = 0; b < B; ++b) dst[b] = (uint8_t)(w[b >> 2] >> (8 * (b & 3)));
+}
+
+__device__ __forceinline__ void stage_lane_bytes(uint8_t* __restrict__ stage, int co, const uint32_t idx[8], int B) {
+  switch (B) {
+    case 11: stage_lane_bytes_t<11>(stage, co, idx); return;
+    case 10: stage_lane_bytes_t<10>(stage, co, idx); return;
+    case 9: stage_lane_bytes_t<9>(stage, co, idx); return;
+    case 8: stage_lane_bytes_t<8>(stage, co, idx); return;
+    default: break;
+  }
+  // other widths (B <= 7): 8 B <= 56 bits fit one 64-bit word
+  uint64_t v = 0;
+  for (int p = 0; p < 8; ++p) v |= (uint64_t)idx[p] << (p * B);
+  uint8_t* dst = stage + B * co;
+  for (int b = 0; b < B; ++b) dst[b] = (uint8_t)(v >> (8 * b));
+}
+
+__device__ __forceinline__ void store_stage(const uint8_t* __restrict__ stage, int lane, int win, int B, int row_words,
+                                            uint32_t* __restrict__ row_out) {
+  const int word0 = win * 16 * B;                      // a multiple of 16 B: 16-byte aligned
+  const int nvec = min(4 * B, (row_words - word0) >> 2);
+  if (lane < nvec)
+    reinterpret_cast<uint4*>(row_out + word0)[lane] = reinterpret_cast<const uint4*>(stage)[lane];
+}
+
 }  // namespace qamw

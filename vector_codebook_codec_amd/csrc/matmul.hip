@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kBlockThreads) void rotate_act_kernel(const Tin* __
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int j = c * kChunk + i;
-    g[i] = active ? g[i] * (inv_sqrt_b / (s ? s[j] : 1.0f)) : 0.0f;
+    g[i] = active ? g[i] * col_scale(inv_sqrt_b, s ? s[j] : 1.0f) : 0.0f;
   }
   const int co = win * kWinChunks + BlockOut<L>::chunk(lane);
   const float osign = BlockOut<L>::sign(lane);
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_matvec_kernel(
       sign_eps16(seed, (uint32_t)(cl * kChunk), eps);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float g = eps[i] * (inv_sqrt_b / sv[i]);
+        const float g = eps[i] * col_scale(inv_sqrt_b, sv[i]);
         x[i] = active ? x[i] * g : 0.0f;
       }
       fwht_block<L>(x, lane);

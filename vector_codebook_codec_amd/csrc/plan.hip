@@ -61,13 +61,21 @@ namespace qamw {
 
 struct PlanHeader {
   float R;
-  float cells_per_unit;   // G / (2 R)
+  float cells_per_unit;   // G / (2 R) (uniform inner grid, K > kLdsMaxK)
   int G;
   int lmax;
   int K;
   float R2;               // outer grid
   float cells_per_unit2;
   int G2;
+  int lds_G;              // LDS table (K <= kLdsMaxK; 0 otherwise): cells per axis
+  int lds_bins;           // bins of the axis map over [-R, R)
+  int lds_lists_cap;      // list records the image holds
+  int lds_nlists;         // list records used (a cell over the capacity scans all)
+  int lds_image_bytes;
+  int lds_cells_off;      // byte offsets inside the image
+  int lds_lists_off;
+  int lds_image_off;      // byte offset of the image inside the plan
 };
 static_assert(offsetof(PlanHeader, K) == kPlanHeaderKOffset, "the encode kernel reads K at this offset");
 
@@ -152,18 +160,16 @@ struct PlanShared {
   int wsum[kPlanWaves];
 };
 
-// One workgroup per supercell (S x S cells) of a G x G grid over [-R, R)^2:
-// the supercell's survivors (ascending, with coordinates) into LDS, then a
-// group of LPC = 256 / S^2 lanes per cell scans them and writes the records.
-template <int S>
-__device__ void build_supercell(PlanShared& sh, const float* __restrict__ cb, int K, int lmax, double R, int G,
-                                int sidx, uint16_t* __restrict__ lists) {
-  constexpr int LPC = kPlanThreads / (S * S);
-  static_assert(LPC >= 1 && LPC * S * S == kPlanThreads && kWave % LPC == 0, "cell groups tile the wavefronts");
+// The survivors of a supercell box SQ: every centroid with
+// min_{z in SQ} |z - c|^2 <= U(SQ) + 2 delta, ascending, with coordinates, in
+// sh.surv / sh.survc, padded with far-away dummies to whole rounds of `round`
+// entries.  Returns their count (more than kSuperMax: `all` is set and the
+// callers test every centroid from global memory); *cmax2 is the largest
+// squared centroid radius and *delta the grid's score margin
+// 1e-5 (Cmax + R sqrt 2)^2 (R: the grid's half-width).
+__device__ int supercell_survivors(PlanShared& sh, const float* __restrict__ cb, int K, const Box& sq64, double R,
+                                   int round, float* cmax2_out, double* delta_out, bool* all_out, int* ns_out) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int nsuper = G / S;
-  const int sx = sidx / nsuper, sy = sidx % nsuper;
-
   // ---- the codebook into registers once: thread t holds centroids
   // r kSuperMax + t P + u (round r < 2 since K <= 4096, u < P = kPerThread),
   // loaded as float4 pairs; past K a far-away dummy that never passes a test
@@ -189,8 +195,7 @@ __device__ void build_supercell(PlanShared& sh, const float* __restrict__ cb, in
   // boxes lie inside the widened supercell box, and the supercell limit's
   // second delta exceeds the cells' relative fp32 slop (~3e-6 U) at every
   // grid point.  delta (fp64) only needs to cover the scores' slack, which
-  // it does ten times over.
-  const Box sq64 = cell_box(R, G, sx * S, sy * S, S);
+  // it does ten times over; a cell's own margin is never larger.
   const BoxF sq{f32_down(sq64.x0), f32_up(sq64.x1), f32_down(sq64.y0), f32_up(sq64.y1)};
   float U = INFINITY, cmax2 = 0.0f;
 #pragma unroll
@@ -251,17 +256,41 @@ __device__ void build_supercell(PlanShared& sh, const float* __restrict__ cb, in
   }
   __syncthreads();
   const bool all = nsurv > kSuperMax;       // too many survivors: test every centroid (from global memory)
-  // pad the survivor list to whole unrolled rounds with a far-away dummy that
-  // neither lowers any U nor passes any test
-  constexpr int kRound = 4 * LPC;
-  static_assert(kSuperMax % kRound == 0, "padding stays inside the survivor arrays");
-  const int ns = all ? K : (nsurv + kRound - 1) / kRound * kRound;
+  // pad the survivor list to whole rounds with a far-away dummy that neither
+  // lowers any U nor passes any test
+  const int ns = all ? K : (nsurv + round - 1) / round * round;
   if (!all)
     for (int j = nsurv + tid; j < ns; j += kPlanThreads) {
       sh.survc[j] = make_float2(1e30f, 1e30f);
       sh.surv[j] = 0;
     }
   __syncthreads();
+  *cmax2_out = cmax2;
+  *delta_out = delta;
+  *all_out = all;
+  *ns_out = ns;
+  return nsurv;
+}
+
+// One workgroup per supercell (S x S cells) of a G x G grid over [-R, R)^2:
+// the supercell's survivors (ascending, with coordinates) into LDS, then a
+// group of LPC = 256 / S^2 lanes per cell scans them and writes the records.
+template <int S>
+__device__ void build_supercell(PlanShared& sh, const float* __restrict__ cb, int K, int lmax, double R, int G,
+                                int sidx, uint16_t* __restrict__ lists) {
+  constexpr int LPC = kPlanThreads / (S * S);
+  static_assert(LPC >= 1 && LPC * S * S == kPlanThreads && kWave % LPC == 0, "cell groups tile the wavefronts");
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int nsuper = G / S;
+  const int sx = sidx / nsuper, sy = sidx % nsuper;
+  constexpr int kRound = 4 * LPC;
+  static_assert(kSuperMax % kRound == 0, "padding stays inside the survivor arrays");
+  float cmax2;
+  double delta;
+  bool all;
+  int ns;
+  supercell_survivors(sh, cb, K, cell_box(R, G, sx * S, sy * S, S), R, kRound, &cmax2, &delta, &all, &ns);
+  (void)cmax2;
 
   // ---- LPC lanes per cell: survivors j = sub, sub + LPC, ...  The cell
   // tests run in fp32 with margins that can only lengthen a list (a list with
@@ -336,26 +365,275 @@ __device__ void build_supercell(PlanShared& sh, const float* __restrict__ cb, in
   if (lmax == 16) out[1] = make_uint4(words[4], words[5], words[6], words[7]);
 }
 
-// One launch builds both grids: workgroups [0, nfine) are the fine grid's
-// 16 x 16-cell supercells (one lane per cell), the rest the outer grid's
-// 4 x 4-cell supercells (16 lanes per cell; its cells are larger, so a 16 x 16
-// supercell would keep most of the codebook).  Every workgroup computes the
-// largest centroid radius itself (with U of its supercell); workgroup 0 writes
-// the header.
+// ===========================================================================
+// LDS table (K <= kLdsMaxK): cell candidate sets decided exactly.
+//
+// A cell Q (its bins' box enlarged by eta) lists centroid c when some z in Q
+// has |z - c|^2 <= |z - c'|^2 + delta_Q for every centroid c': the fp32
+// winner c32 at z (and every centroid tied with it) qualifies, since
+// |z - c32|^2 <= |z - c*|^2 + slack(z) <= |z - c'|^2 + slack(z) for all c'.
+// slack(z) = 2 (e(c32) + e(c*)) <= 4 2^-24 (2.5 cm^2 + 2 zmax cm) with zmax
+// the largest |z| over Q and cm >= |c32|, |c*|: both lie within
+// sqrt(U(Q) + delta) of z (delta the grid's margin, >= slack everywhere), so
+// cm = min(Cmax, zmax + sqrt(U(Q) + delta)); delta_Q is ten times that bound.
+// The test for one c is the feasibility of a small 2D linear system (the box
+// and one half-plane 2 z.(c' - c) <= |c'|^2 - |c|^2 + delta_Q per c'): if the
+// feasible polygon is not empty, one of its vertices is the intersection of
+// two of the lines, so every such intersection point is tried (in fp64, with
+// a tolerance that errs towards listing).  Only the cell's loose candidates
+// (min_{z in Q} |z - c|^2 <= U(Q) + delta_Q) need testing or acting as c': any
+// other centroid is farther than the one attaining U(Q) everywhere in Q.
+// ===========================================================================
+constexpr int kLdsSuper = 8;           // LDS-table supercells: 8 x 8 cells, four lanes per cell
+constexpr int kLdsLoose = 16;          // loose candidates a cell may keep (more: scan all)
+constexpr int kLdsListMax = 8;         // exact candidates a cell may list (more: scan all)
+constexpr int kHashSlots = 32768;      // list dedup table (>= 1.4 x the cells of any geometry)
+static_assert(kHashSlots >= 2 * kLdsMaxG * kLdsMaxG / 4, "dedup table load factor");
+
+struct LdsEdges {
+  uint16_t e[kLdsMaxG + 1];
+};
+
+// dedup table entry: the list (4 x u16), the lowest cell holding it, its record id
+struct HashSlot {
+  unsigned long long key;
+  unsigned int owner;
+  unsigned int id;
+};
+
+struct LdsScratch {
+  uint4* cellset;         // [G*G] exact candidate sets: 8 x u16 16c, low nibble of entry 0 = count - 1,
+                          // of entry 1 = 1 when the cell must scan all
+  int* slot;              // [G*G] dedup slot of a 2..4 list, -1 otherwise
+  int* recid;             // [G*G] record id of a 5..8 list (two records), or of an owned 2..4 list
+  int* total;             // records used
+  int* blocksum;          // [kMaxScanBlocks] records needed per block of kScanBlock cells
+  HashSlot* table;        // [kHashSlots]
+};
+
+constexpr int kScanBlock = 256;                  // cells per block of the record-id scan
+constexpr int kMaxScanBlocks = kLdsMaxG * kLdsMaxG / kScanBlock;
+
+__host__ __device__ inline size_t lds_scratch_bytes(int G) {
+  const size_t cells = (size_t)G * G;
+  return round_up(cells * 16, 256) + 2 * round_up(cells * 4, 256) + 256 + kMaxScanBlocks * sizeof(int) +
+         (size_t)kHashSlots * sizeof(HashSlot);
+}
+
+__device__ __forceinline__ LdsScratch lds_scratch(char* base, int G) {
+  const size_t cells = (size_t)G * G;
+  LdsScratch s;
+  s.cellset = reinterpret_cast<uint4*>(base);
+  base += round_up(cells * 16, 256);
+  s.slot = reinterpret_cast<int*>(base);
+  base += round_up(cells * 4, 256);
+  s.recid = reinterpret_cast<int*>(base);
+  base += round_up(cells * 4, 256);
+  s.total = reinterpret_cast<int*>(base);
+  base += 256;
+  s.blocksum = reinterpret_cast<int*>(base);
+  base += kMaxScanBlocks * sizeof(int);
+  s.table = reinterpret_cast<HashSlot*>(base);
+  return s;
+}
+
+__device__ __forceinline__ Box lds_box(const LdsEdges& E, int x0, int x1, int y0, int y1) {
+  // cells [x0, x1) x [y0, y1) of the LDS table: bins of width 2 R / kLdsBins
+  const double h = 2.0 * kPlanR / kLdsBins;
+  return Box{-kPlanR + E.e[x0] * h - kPlanEta, -kPlanR + E.e[x1] * h + kPlanEta,
+             -kPlanR + E.e[y0] * h - kPlanEta, -kPlanR + E.e[y1] * h + kPlanEta};
+}
+
+// Candidate pruning inside one cell Q, for the loose candidates m[0..n) of
+// the cell (survivor slots).  f(z) = |z - c_i|^2 - |z - c_k|^2 is linear in z,
+// so its minimum over the box is at a corner: when it exceeds delta at all
+// four corners, c_k beats c_i by more than delta everywhere in Q and c_i is
+// never within delta of the minimum there ("k dominates i").  Such a c_i is
+// dropped, and its constraint on the others can be dropped too: whatever
+// satisfies |z - c_j|^2 <= |z - c_k|^2 + delta then satisfies it against c_i.
+__device__ __forceinline__ double corner_min_diff(const Box& q, double ix, double iy, double kx, double ky) {
+  // |z - c_i|^2 - |z - c_k|^2 = 2 z.(c_k - c_i) + |c_i|^2 - |c_k|^2, minimised over the corners
+  const double ax = 2.0 * (kx - ix), ay = 2.0 * (ky - iy), c0 = (ix * ix + iy * iy) - (kx * kx + ky * ky);
+  return fmin(ax * q.x0, ax * q.x1) + fmin(ay * q.y0, ay * q.y1) + c0;
+}
+
+// Is there a point z of q with |z - c_i|^2 <= |z - c_k|^2 + delta for every k
+// in the set `keep` (a bitmask over m[0..n))?  If that polygon is not empty
+// one of its vertices is the intersection of two of the lines (box edges and
+// the constraints' boundaries), so every such point is tried, in fp64, with a
+// tolerance that errs towards "feasible".
+__device__ bool lds_feasible(const PlanShared& sh, const uint16_t* m, int n, uint32_t keep, int i, const Box& q,
+                             double delta) {
+  const float2 fi = sh.survc[m[i]];
+  const double cix = fi.x, ciy = fi.y, ci2 = cix * cix + ciy * ciy;
+  auto cons = [&](int k, double& ax, double& ay, double& b) {
+    const float2 fk = sh.survc[m[k]];
+    const double kx = fk.x, ky = fk.y;
+    ax = 2.0 * (kx - cix);
+    ay = 2.0 * (ky - ciy);
+    b = (kx * kx + ky * ky) - ci2 + delta;
+  };
+  auto ok = [&](double px, double py) -> bool {
+    const double tb = 1e-12 * (1.0 + fabs(px) + fabs(py));
+    if (!(px >= q.x0 - tb && px <= q.x1 + tb && py >= q.y0 - tb && py <= q.y1 + tb)) return false;
+    for (int k = 0; k < n; ++k) {
+      if (k == i || !((keep >> k) & 1u)) continue;
+      double ax, ay, b;
+      cons(k, ax, ay, b);
+      if (ax * px + ay * py > b + 1e-12 * (fabs(ax * px) + fabs(ay * py) + fabs(b)) + 1e-15) return false;
+    }
+    return true;
+  };
+  if (ok(q.x0, q.y0) || ok(q.x0, q.y1) || ok(q.x1, q.y0) || ok(q.x1, q.y1)) return true;
+  for (int k = 0; k < n; ++k) {
+    if (k == i || !((keep >> k) & 1u)) continue;
+    double ax, ay, b;
+    cons(k, ax, ay, b);
+    if (ay != 0.0 && (ok(q.x0, (b - ax * q.x0) / ay) || ok(q.x1, (b - ax * q.x1) / ay))) return true;
+    if (ax != 0.0 && (ok((b - ay * q.y0) / ax, q.y0) || ok((b - ay * q.y1) / ax, q.y1))) return true;
+  }
+  for (int k = 0; k < n; ++k) {
+    if (k == i || !((keep >> k) & 1u)) continue;
+    double axk, ayk, bk;
+    cons(k, axk, ayk, bk);
+    for (int j = k + 1; j < n; ++j) {
+      if (j == i || !((keep >> j) & 1u)) continue;
+      double axj, ayj, bj;
+      cons(j, axj, ayj, bj);
+      const double det = axk * ayj - ayk * axj;
+      if (det == 0.0) continue;
+      if (ok((bk * ayj - bj * ayk) / det, (axk * bj - axj * bk) / det)) return true;
+    }
+  }
+  return false;
+}
+
+// One workgroup per 8 x 8-cell supercell of the LDS table: survivors, then
+// four lanes per cell: U(Q), delta_Q, the loose candidates (ascending), the
+// dominance pruning and the exact test of what is left, split over the lanes.
+constexpr int kLdsLanes = 4;
+__device__ void build_lds_supercell(PlanShared& sh, const float* __restrict__ cb, int K, const LdsEdges& E, int G,
+                                    int sidx, LdsScratch scr) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int nsuper = (G + kLdsSuper - 1) / kLdsSuper;
+  const int sx = sidx / nsuper, sy = sidx % nsuper;
+  const int x0 = sx * kLdsSuper, y0 = sy * kLdsSuper;
+  const int x1 = min(x0 + kLdsSuper, G), y1 = min(y0 + kLdsSuper, G);
+  constexpr int kRound = 4 * kLdsLanes;
+  float cmax2;
+  double delta;
+  bool all;
+  int ns;
+  supercell_survivors(sh, cb, K, lds_box(E, x0, x1, y0, y1), kPlanR, kRound, &cmax2, &delta, &all, &ns);
+  // K <= kSuperMax here, so the survivors always fit (all == false)
+  const int qc = tid / kLdsLanes, sub = tid % kLdsLanes;
+  const int ix = x0 + qc / kLdsSuper, iy = y0 + qc % kLdsSuper;
+  const bool real = ix < x1 && iy < y1;          // lanes of cells past the table's edge compute a copy of the last
+  const int cx_ = min(ix, G - 1), cy_ = min(iy, G - 1);
+  const Box cq64 = lds_box(E, cx_, cx_ + 1, cy_, cy_ + 1);
+  const BoxF cq{f32_down(cq64.x0), f32_up(cq64.x1), f32_down(cq64.y0), f32_up(cq64.y1)};
+  float Uc = INFINITY;
+  for (int j0 = 0; j0 < ns; j0 += kRound) {
+    float2 v4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v4[u] = sh.survc[j0 + u * kLdsLanes + sub];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Uc = fminf(Uc, cq.dmax2(v4[u].x, v4[u].y));
+  }
+#pragma unroll
+  for (int off = kLdsLanes / 2; off > 0; off >>= 1) Uc = fminf(Uc, __shfl_xor(Uc, off));
+  // the cell's margin: ten times the fp32 slack bound for its points
+  const double zx = fmax(fabs(cq64.x0), fabs(cq64.x1)), zy = fmax(fabs(cq64.y0), fabs(cq64.y1));
+  const double zmax = sqrt(zx * zx + zy * zy);
+  const double cm = fmin(sqrt((double)cmax2 * 1.000001), zmax + sqrt((double)Uc * 1.000001 + delta));
+  const double dq = 40.0 * 0x1p-24 * (2.5 * cm * cm + 2.0 * zmax * cm);
+  const float lim = (Uc * 1.000001f + f32_up(dq)) * 1.000001f;
+  // ---- loose candidates in ascending order: survivors j = sub, sub + 4, ...,
+  // one chunk of four per ballot
+  uint16_t* mine = sh.cell_list[qc];
+  const int gshift = lane & ~(kLdsLanes - 1);
+  int nl = 0;
+  for (int j0 = 0; j0 < ns; j0 += kLdsLanes) {
+    const float2 v = sh.survc[j0 + sub];
+    const bool pred = cq.dmin2(v.x, v.y) <= lim;
+    const uint64_t gm = (__ballot(pred) >> gshift) & ((1ull << kLdsLanes) - 1ull);
+    const int pos = nl + __popcll(gm & ((1ull << sub) - 1ull));
+    if (pred && pos < kLdsLoose) mine[pos] = (uint16_t)(j0 + sub);
+    nl += __popcll(gm);
+  }
+  __syncthreads();
+  // ---- dominance, then the exact test of the undominated candidates
+  // (lane sub decides candidates sub, sub + 4, ...; the four masks are or-ed)
+  const bool over_loose = nl > kLdsLoose || nl == 0;
+  const int n = over_loose ? 0 : nl;
+  uint32_t undom = 0;
+  for (int i = sub; i < n; i += kLdsLanes) {
+    const float2 fi = sh.survc[mine[i]];
+    bool dominated = false;
+    for (int k = 0; k < n && !dominated; ++k) {
+      if (k == i) continue;
+      const float2 fk = sh.survc[mine[k]];
+      dominated = corner_min_diff(cq64, fi.x, fi.y, fk.x, fk.y) > dq * (1.0 + 1e-9) + 1e-15;
+    }
+    if (!dominated) undom |= 1u << i;
+  }
+#pragma unroll
+  for (int off = kLdsLanes / 2; off > 0; off >>= 1) undom |= (uint32_t)__shfl_xor((int)undom, off);
+  uint32_t keep = 0;
+  for (int i = sub; i < n; i += kLdsLanes)
+    if (((undom >> i) & 1u) && (__popc(undom) == 1 || lds_feasible(sh, mine, n, undom, i, cq64, dq))) keep |= 1u << i;
+#pragma unroll
+  for (int off = kLdsLanes / 2; off > 0; off >>= 1) keep |= (uint32_t)__shfl_xor((int)keep, off);
+  if (sub != 0 || !real) return;
+  // ---- the cell's exact set, ascending (mine[] ascends)
+  const int count = __popc(keep);
+  const bool over = over_loose || count > kLdsListMax || count == 0;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (!over) {
+    uint32_t ent[kLdsListMax];
+    int c = 0;
+    uint32_t last = 0;
+#pragma unroll
+    for (int q = 0; q < kLdsListMax; ++q) ent[q] = 0;
+    for (int i = 0; i < n; ++i)
+      if ((keep >> i) & 1u) {
+        last = 16u * sh.surv[mine[i]];
+#pragma unroll
+        for (int q = 0; q < kLdsListMax; ++q) ent[q] = (q == c) ? last : ent[q];
+        ++c;
+      }
+#pragma unroll
+    for (int q = 0; q < kLdsListMax; ++q) ent[q] = (q >= count) ? last : ent[q];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = ent[2 * q] | (ent[2 * q + 1] << 16);
+  }
+  w[0] |= over ? (1u << 16) : (uint32_t)(count - 1);
+  scr.cellset[(size_t)ix * G + iy] = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Two launches build the grids: build_plan_kernel the inner grid's supercells
+// (the LDS table's 8 x 8 cells with four lanes per cell for K <= kLdsMaxK,
+// else the uniform 512 x 512 grid's 16 x 16 cells with one lane per cell),
+// build_outer_kernel the outer grid's 4 x 4-cell supercells (16 lanes per
+// cell; its cells are larger, so a 16 x 16 supercell would keep most of the
+// codebook).  Every workgroup computes the largest centroid radius itself
+// (with U of its supercell); workgroup 0 of the first writes the header, and
+// with the LDS table every workgroup of the first clears a stripe of the
+// dedup table.
 constexpr int kSuperFine = 16;
 constexpr int kSuperOuter = 4;
 constexpr int kFineSupercells = (kPlanG / kSuperFine) * (kPlanG / kSuperFine);
 constexpr int kOuterSupercells = (kPlanG2 / kSuperOuter) * (kPlanG2 / kSuperOuter);
 static_assert(kPlanG % kSuperFine == 0 && kPlanG2 % kSuperOuter == 0, "grids are whole supercells");
 
-// Outer-grid cells [kOuterFineLo, kOuterFineHi) per axis cover exactly the fine
-// grid's square [-R, R): a point there always takes the fine grid, so those
-// cells are never consulted.  Their supercells write overflow records (scan
-// the whole codebook, correct if ever read) instead of lists; near the centre
-// they are also the most expensive ones (thousands of survivors).
+// Outer-grid cells [kOuterFineLo, kOuterFineHi) per axis cover exactly the
+// inner grid's square [-R, R): a point there always takes the inner grid, so
+// those cells are never consulted.  Their supercells write overflow records
+// (scan the whole codebook, correct if ever read) instead of lists; near the
+// centre they are also the most expensive ones (thousands of survivors).
 constexpr int kOuterFineLo = (int)((kPlanR2 - kPlanR) * kPlanG2 / (2.0f * kPlanR2));
 constexpr int kOuterFineHi = kPlanG2 - kOuterFineLo;
-static_assert(kOuterFineLo * 2.0f * kPlanR2 == (kPlanR2 - kPlanR) * kPlanG2, "the fine square is whole outer cells");
+static_assert(kOuterFineLo * 2.0f * kPlanR2 == (kPlanR2 - kPlanR) * kPlanG2, "the inner square is whole outer cells");
 static_assert(kOuterFineLo % kSuperOuter == 0, "and whole outer supercells");
 
 __device__ __forceinline__ bool outer_supercell_unused(int sidx) {
@@ -366,28 +644,44 @@ __device__ __forceinline__ bool outer_supercell_unused(int sidx) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* __restrict__ cb, int K, int lmax,
-                                                                  char* __restrict__ plan, size_t outer_offset) {
+                                                                  char* __restrict__ plan, int lds_G, LdsEdges edges,
+                                                                  size_t scratch_offset) {
   __shared__ PlanShared sh;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     PlanHeader* hdr = reinterpret_cast<PlanHeader*>(plan);
     hdr->R = kPlanR;
-    hdr->cells_per_unit = (float)kPlanG / (2.0f * kPlanR);
-    hdr->G = kPlanG;
+    hdr->cells_per_unit = lds_G ? 0.0f : (float)kPlanG / (2.0f * kPlanR);
+    hdr->G = lds_G ? 0 : kPlanG;
     hdr->lmax = lmax;
     hdr->K = K;
     hdr->R2 = kPlanR2;
     hdr->cells_per_unit2 = (float)kPlanG2 / (2.0f * kPlanR2);
     hdr->G2 = kPlanG2;
+    // the LDS table's fields: lds_image_kernel fills them when there is one
+    hdr->lds_G = hdr->lds_bins = hdr->lds_lists_cap = hdr->lds_nlists = 0;
+    hdr->lds_image_bytes = hdr->lds_cells_off = hdr->lds_lists_off = hdr->lds_image_off = 0;
   }
-  if (blockIdx.x < kFineSupercells)
+  if (lds_G) {
+    LdsScratch scr = lds_scratch(plan + scratch_offset, lds_G);
+    for (int i = blockIdx.x * kPlanThreads + threadIdx.x; i < kHashSlots; i += gridDim.x * kPlanThreads)
+      scr.table[i] = HashSlot{0ull, 0xffffffffu, 0u};
+    build_lds_supercell(sh, cb, K, edges, lds_G, blockIdx.x, scr);
+  } else {
     build_supercell<kSuperFine>(sh, cb, K, lmax, kPlanR, kPlanG, blockIdx.x,
                                 reinterpret_cast<uint16_t*>(plan + kPlanHeaderBytes));
-  else if (!outer_supercell_unused(blockIdx.x - kFineSupercells))
-    build_supercell<kSuperOuter>(sh, cb, K, lmax, kPlanR2, kPlanG2, blockIdx.x - kFineSupercells,
+  }
+}
+
+// The outer grid, one workgroup per 4 x 4-cell supercell.
+__global__ __launch_bounds__(kPlanThreads) void build_outer_kernel(const float* __restrict__ cb, int K, int lmax,
+                                                                   char* __restrict__ plan, size_t outer_offset) {
+  __shared__ PlanShared sh;
+  const int sidx = blockIdx.x;
+  if (!outer_supercell_unused(sidx))
+    build_supercell<kSuperOuter>(sh, cb, K, lmax, kPlanR2, kPlanG2, sidx,
                                  reinterpret_cast<uint16_t*>(plan + outer_offset));
   else if (threadIdx.x < kSuperOuter * kSuperOuter) {   // one overflow record per cell
     constexpr int nsuper = kPlanG2 / kSuperOuter;
-    const int sidx = blockIdx.x - kFineSupercells;
     const int ix = (sidx / nsuper) * kSuperOuter + threadIdx.x / kSuperOuter;
     const int iy = (sidx % nsuper) * kSuperOuter + threadIdx.x % kSuperOuter;
     uint4* out = reinterpret_cast<uint4*>(plan + outer_offset + ((size_t)ix * kPlanG2 + iy) * lmax * sizeof(uint16_t));
@@ -396,10 +690,256 @@ __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* _
   }
 }
 
+// ---- list dedup.  A list of 2..4 candidates (4 x u16, tail repeated) is a
+// 64-bit key; equal lists share one record.  The record belongs to the lowest
+// cell holding the list, and records are numbered by a prefix sum over the
+// cells in order, so the image does not depend on the order of the atomics.
+__device__ __forceinline__ uint32_t cell_count(uint4 w) { return (w.x & 15u) + 1u; }
+__device__ __forceinline__ bool cell_over(uint4 w) { return (w.x >> 16) & 1u; }
+__device__ __forceinline__ unsigned long long list_key(uint4 w) {
+  return (unsigned long long)(w.x & 0xfff0fff0u) | ((unsigned long long)w.y << 32);
+}
+
+__global__ __launch_bounds__(256) void lds_insert_kernel(char* __restrict__ plan, size_t scratch_offset, int G) {
+  const int cell = blockIdx.x * 256 + threadIdx.x;
+  if (cell >= G * G) return;
+  LdsScratch scr = lds_scratch(plan + scratch_offset, G);
+  const uint4 w = scr.cellset[cell];
+  const uint32_t n = cell_count(w);
+  int slot = -1;
+  if (!cell_over(w) && n >= 2 && n <= 4) {
+    const unsigned long long key = list_key(w);
+    unsigned long long h = key * 0x9E3779B97F4A7C15ull;
+    h ^= h >> 29;
+    uint32_t at = (uint32_t)(h >> 17) & (kHashSlots - 1);
+    for (int probe = 0; probe < kHashSlots; ++probe) {      // bounded: every slot at most once
+      const unsigned long long prev = atomicCAS(&scr.table[at].key, 0ull, key);
+      if (prev == 0ull || prev == key) {
+        atomicMin(&scr.table[at].owner, (unsigned int)cell);
+        slot = (int)at;
+        break;
+      }
+      at = (at + 1) & (kHashSlots - 1);
+    }
+  }
+  scr.slot[cell] = slot;
+}
+
+// Block-wide inclusive scan of one int per thread (kScanBlock threads).
+__device__ __forceinline__ int block_scan(int v, int* sh) {
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = 1; off < kScanBlock; off <<= 1) {
+    const int t = threadIdx.x >= off ? sh[threadIdx.x - off] : 0;
+    __syncthreads();
+    sh[threadIdx.x] += t;
+    __syncthreads();
+  }
+  return sh[threadIdx.x];
+}
+
+// Records a cell needs: one for a 2..4 list it owns (it is the lowest cell
+// holding that list), two for a 5..8 list, none otherwise; and each block's
+// total.
+__global__ __launch_bounds__(kScanBlock) void lds_need_kernel(char* __restrict__ plan, size_t scratch_offset, int G) {
+  __shared__ int sh[kScanBlock];
+  const int cell = blockIdx.x * kScanBlock + threadIdx.x;
+  LdsScratch scr = lds_scratch(plan + scratch_offset, G);
+  int need = 0;
+  if (cell < G * G) {
+    const uint4 w = scr.cellset[cell];
+    if (!cell_over(w)) {
+      const uint32_t n = cell_count(w);
+      const int sl = scr.slot[cell];
+      if (n >= 5) need = 2;
+      else if (n >= 2 && sl >= 0 && scr.table[sl].owner == (unsigned int)cell) need = 1;
+    }
+    scr.recid[cell] = need;
+  }
+  const int incl = block_scan(need, sh);
+  if (threadIdx.x == kScanBlock - 1) scr.blocksum[blockIdx.x] = incl;
+}
+
+// Record ids: an exclusive prefix sum of the needs over the cells in order
+// (block offsets from the block totals, then a scan inside the block),
+// published to the dedup table for the owned 2..4 lists.
+__global__ __launch_bounds__(kScanBlock) void lds_ids_kernel(char* __restrict__ plan, size_t scratch_offset, int G) {
+  __shared__ int sh[kScanBlock];
+  LdsScratch scr = lds_scratch(plan + scratch_offset, G);
+  const int nblk = (G * G + kScanBlock - 1) / kScanBlock;
+  // this block's offset: the sum of the earlier blocks' totals
+  const int before = (int)threadIdx.x < (int)blockIdx.x ? scr.blocksum[threadIdx.x] : 0;
+  block_scan(before, sh);
+  const int block_off = sh[kScanBlock - 1];              // the scan's last entry: the whole sum
+  __syncthreads();
+  const int cell = blockIdx.x * kScanBlock + threadIdx.x;
+  const int need = cell < G * G ? scr.recid[cell] : 0;
+  const int incl = block_scan(need, sh);
+  if (cell < G * G) {
+    const int id = block_off + incl - need;
+    scr.recid[cell] = need ? id : -1;
+    if (need == 1) scr.table[scr.slot[cell]].id = (unsigned int)id;
+  }
+  if ((int)blockIdx.x == nblk - 1 && threadIdx.x == kScanBlock - 1) *scr.total = block_off + incl;
+}
+
+// The image: bin -> cell map, one entry per cell, the list records; the
+// header's table fields.  Records past the capacity are not written: their
+// cells scan the whole codebook.
+__global__ __launch_bounds__(256) void lds_image_kernel(char* __restrict__ plan, size_t scratch_offset,
+                                                        size_t image_offset, int G, int cells_off, int lists_off,
+                                                        int lists_cap, int image_bytes, LdsEdges E) {
+  LdsScratch scr = lds_scratch(plan + scratch_offset, G);
+  char* img = plan + image_offset;
+  uint16_t* cells = reinterpret_cast<uint16_t*>(img + cells_off);
+  uint2* lists = reinterpret_cast<uint2*>(img + lists_off);
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int used = min(*scr.total, lists_cap);
+  if (t == 0) {
+    PlanHeader* hdr = reinterpret_cast<PlanHeader*>(plan);
+    hdr->lds_G = G;
+    hdr->lds_bins = kLdsBins;
+    hdr->lds_lists_cap = lists_cap;
+    hdr->lds_nlists = used;
+    hdr->lds_image_bytes = image_bytes;
+    hdr->lds_cells_off = cells_off;
+    hdr->lds_lists_off = lists_off;
+    hdr->lds_image_off = (int)image_offset;
+  }
+  if (t < kLdsBins) {                                  // the bin -> cell map: the c with e[c] <= t < e[c + 1]
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (E.e[mid] <= t) lo = mid; else hi = mid;
+    }
+    reinterpret_cast<uint8_t*>(img)[t] = (uint8_t)lo;
+  }
+  // unused records and the cell padding are cleared, so the image is a pure
+  // function of the codebook
+  const int ncell = G * G;
+  const int pad_end = (lists_off - cells_off) / 2;
+  for (int i = ncell + t; i < pad_end; i += gridDim.x * 256) cells[i] = 0;
+  for (int i = used + t; i < lists_cap; i += gridDim.x * 256) lists[i] = make_uint2(0u, 0u);
+  if (t >= ncell) return;
+  const uint4 w = scr.cellset[t];
+  const uint32_t n = cell_count(w);
+  uint16_t entry = kLdsScanAll;
+  if (!cell_over(w)) {
+    if (n == 1) {
+      entry = (uint16_t)(w.x & 0xfff0u);
+    } else if (n <= 4) {
+      const int sl = scr.slot[t];
+      if (sl >= 0) {
+        const unsigned int id = scr.table[sl].id;
+        if ((int)id < used) {
+          entry = (uint16_t)(0x8000u | id);
+          if (scr.table[sl].owner == (unsigned int)t) lists[id] = make_uint2(w.x & 0xfff0fff0u, w.y);
+        }
+      }
+    } else {
+      const int id = scr.recid[t];
+      if (id >= 0 && id + 1 < used) {
+        entry = (uint16_t)(0x8000u | (unsigned)id);
+        lists[id] = make_uint2(w.x & 0xfff0fff0u, w.y | 0x80000000u);   // slot 3's top bit: continued
+        lists[id + 1] = make_uint2(w.z, w.w);
+      }
+    }
+  }
+  cells[t] = entry;
+}
+
+// ===========================================================================
+// host side
+// ===========================================================================
+bool lds_geometry(int K, LdsGeometry* g) {
+  if (!plan_has_lds(K)) return false;
+  // cell widths in bins grow as exp(t^2 / 8) away from the origin (centroid
+  // spacing of a Lloyd-Max codebook for N(0, I_2) grows like p(z)^(-1/4)), from
+  // 7 bins at the origin for K = 2048, scaled by sqrt(2048 / K)
+  const double h = 2.0 * kPlanR / kLdsBins;
+  const double w0 = 7.0 * sqrt(2048.0 / K);
+  int pos[kLdsBins + 1];
+  int np = 0;
+  pos[np++] = kLdsBins / 2;
+  while (pos[np - 1] < kLdsBins) {
+    const double t = (pos[np - 1] - kLdsBins / 2) * h;
+    const long w = lround(w0 * exp(t * t / 8.0));
+    const int wi = (int)(w < 1 ? 1 : (w > 255 ? 255 : w));
+    pos[np] = pos[np - 1] + wi > kLdsBins ? kLdsBins : pos[np - 1] + wi;
+    ++np;
+  }
+  // mirror: edges kLdsBins - pos[np-1] .. kLdsBins - pos[1], then pos[0..np)
+  if (2 * np - 1 > kLdsMaxG + 1) return false;
+  int G = 0;
+  for (int i = np - 1; i >= 1; --i) g->edges[G++] = (uint16_t)(kLdsBins - pos[i]);
+  for (int i = 0; i < np; ++i) g->edges[G++] = (uint16_t)pos[i];
+  G -= 1;
+  g->G = G;
+  const int B = qamw_index_bits(K);
+  g->stage_bytes = (size_t)64 * B;
+  g->cells_off = kLdsBins;
+  g->lists_off = g->cells_off + round_up((size_t)2 * G * G, 16);
+  const long avail = (long)kLdsBudget - 16L * K - (long)(kLdsWaves * g->stage_bytes) - (long)g->lists_off;
+  long cap = avail / 8;
+  cap = cap > 32767 ? 32767 : cap;
+  cap &= ~1L;                                   // whole 16-byte rows
+  if (cap < 2) return false;
+  g->lists_cap = (int)cap;
+  g->image_bytes = g->lists_off + (size_t)8 * cap;
+  return true;
+}
+
+size_t plan_outer_offset(int K) {
+  return plan_has_lds(K) ? kPlanHeaderBytes
+                         : kPlanHeaderBytes + (size_t)kPlanG * kPlanG * plan_lmax(K) * sizeof(uint16_t);
+}
+
+size_t plan_image_offset(int K) {
+  return plan_outer_offset(K) + (size_t)kPlanG2 * kPlanG2 * plan_lmax(K) * sizeof(uint16_t);
+}
+
+size_t plan_scratch_offset(int K) {
+  LdsGeometry g;
+  if (!lds_geometry(K, &g)) return plan_image_offset(K);
+  return round_up(plan_image_offset(K) + g.image_bytes, 256);
+}
+
+size_t plan_bytes(int K) {
+  LdsGeometry g;
+  if (!lds_geometry(K, &g)) return plan_image_offset(K);
+  return plan_scratch_offset(K) + lds_scratch_bytes(g.G);
+}
+
 int launch_build_plan(const float* cb, int K, void* plan, hipStream_t st) {
-  hipLaunchKernelGGL(build_plan_kernel, dim3(kFineSupercells + kOuterSupercells), dim3(kPlanThreads), 0, st, cb, K,
-                     plan_lmax(K), (char*)plan, plan_outer_offset(K));
-  return check_launch("build_plan_kernel");
+  LdsGeometry g;
+  LdsEdges E{};
+  int G = 0, ninner = kFineSupercells;
+  if (lds_geometry(K, &g)) {
+    G = g.G;
+    for (int i = 0; i <= G; ++i) E.e[i] = g.edges[i];
+    const int ns = (G + kLdsSuper - 1) / kLdsSuper;
+    ninner = ns * ns;
+  }
+  char* p = (char*)plan;
+  hipLaunchKernelGGL(build_plan_kernel, dim3(ninner), dim3(kPlanThreads), 0, st, cb, K, plan_lmax(K), p, G, E,
+                     plan_scratch_offset(K));
+  int rc = check_launch("build_plan_kernel");
+  if (rc) return rc;
+  hipLaunchKernelGGL(build_outer_kernel, dim3(kOuterSupercells), dim3(kPlanThreads), 0, st, cb, K, plan_lmax(K), p,
+                     plan_outer_offset(K));
+  if ((rc = check_launch("build_outer_kernel")) || !G) return rc;
+  const size_t so = plan_scratch_offset(K);
+  const int nblk = (G * G + kScanBlock - 1) / kScanBlock;
+  hipLaunchKernelGGL(lds_insert_kernel, dim3((G * G + 255) / 256), dim3(256), 0, st, p, so, G);
+  if ((rc = check_launch("lds_insert_kernel"))) return rc;
+  hipLaunchKernelGGL(lds_need_kernel, dim3(nblk), dim3(kScanBlock), 0, st, p, so, G);
+  if ((rc = check_launch("lds_need_kernel"))) return rc;
+  hipLaunchKernelGGL(lds_ids_kernel, dim3(nblk), dim3(kScanBlock), 0, st, p, so, G);
+  if ((rc = check_launch("lds_ids_kernel"))) return rc;
+  const int nthreads = G * G > kLdsBins ? G * G : kLdsBins;
+  hipLaunchKernelGGL(lds_image_kernel, dim3((nthreads + 255) / 256), dim3(256), 0, st, p, so, plan_image_offset(K), G,
+                     (int)g.cells_off, (int)g.lists_off, g.lists_cap, (int)g.image_bytes, E);
+  return check_launch("lds_image_kernel");
 }
 
 }  // namespace qamw

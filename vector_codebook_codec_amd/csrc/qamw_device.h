@@ -4,10 +4,11 @@
 // 16-column "chunks"; one lane of a 64-wide wavefront owns one chunk (16
 // consecutive elements = 8 consecutive pairs), and one wavefront owns a
 // "window" of 64 consecutive chunks (1024 columns, 512 pairs) of one row.  A
-// Hadamard block of b = 2^L columns therefore spans b/16 adjacent lanes, which
-// always sit inside one wavefront (16 <= b <= 1024), so the whole rotation is
+// Hadamard block of b = 2^L >= 16 columns therefore spans b/16 adjacent lanes,
+// which always sit inside one wavefront (b <= 1024), so the whole rotation is
 // done in registers: 4 butterfly stages inside each lane, then L-4 stages
-// across lanes.
+// across lanes; blocks of 2, 4 or 8 columns need only L in-lane stages (the
+// row length is then still a multiple of 16).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -52,6 +53,13 @@ __device__ __forceinline__ void sign_eps16(uint64_t seed, uint32_t j0, float out
     ctr += kGamma;
   }
 }
+
+// 1 / (sqrt(b) s_j), the per-column factor of the decode side (decoded weight
+// = rho^ (R_fwd^T y^) / s_j; rotated activations = R_fwd (x / s)).  A column
+// with s_j = 0 (an input channel whose activations are all zero, so its
+// weights never reach the output) gets 0: it decodes as 0 and its activations
+// are dropped, instead of dividing by zero.
+__device__ __forceinline__ float col_scale(float inv_sqrt_b, float s) { return s != 0.0f ? inv_sqrt_b / s : 0.0f; }
 
 // ---------------------------------------------------------------------------
 // Loads / stores of one 16-element chunk (16-byte aligned).
@@ -155,18 +163,11 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
 // complete in order, and the fences keep the compiler from reordering the
 // cross-lane accesses.
 // ---------------------------------------------------------------------------
-// Output stores stream through L2: non-temporal by default.
-#ifndef QAMW_NT_STORES
-#define QAMW_NT_STORES 1
-#endif
+// Output stores stream through L2: non-temporal.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store16(void* dst, uint4 t) {
-#if QAMW_NT_STORES
   const u32x4 v = {t.x, t.y, t.z, t.w};
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
-#else
-  *reinterpret_cast<uint4*>(dst) = t;
-#endif
 }
 
 __device__ __forceinline__ int stage_slot(int chunk, int q) {  // q: 16-byte piece of the chunk (0..3)
@@ -475,13 +476,16 @@ __device__ __forceinline__ void lane_stage(float x[16], int a) {
 // outputs land.  `lane` is the lane index in the wavefront.  The stages
 // commute, so a caller whose input already went through the in-register
 // stages below H0 (pairs (x[2p], x[2p+1]) already replaced by their sum and
-// difference, for H0 = 2) starts at H0.
+// difference, for H0 = 2) starts at H0.  Blocks of 2, 4 or 8 columns lie
+// inside one lane's 16 registers: only the in-register stages below b run,
+// and every lane keeps its own chunk.
 template <int L, int H0 = 1>
 __device__ __forceinline__ void fwht_block(float x[16], int lane) {
-  static_assert(L >= 4 && L <= 10, "block size must be 16..1024");
+  static_assert(L >= 1 && L <= 10, "block size must be 2..1024");
   static_assert(H0 == 1 || H0 == 2, "first in-register stage");
+  constexpr int kRegLimit = L < 4 ? (1 << L) : 16;   // in-register stages h < min(b, 16)
 #pragma unroll
-  for (int h = H0; h < 16; h <<= 1) {
+  for (int h = H0; h < kRegLimit; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if ((i & h) == 0) {
@@ -491,13 +495,13 @@ __device__ __forceinline__ void fwht_block(float x[16], int lane) {
       }
     }
   }
-  lane_stage<0, L - 4>(x, lane & ((1 << (L - 4)) - 1));
+  if constexpr (L > 4) lane_stage<0, L - 4>(x, lane & ((1 << (L - 4)) - 1));
 }
 
 // Block-relative placement of a lane's outputs after fwht_block<L>.
 template <int L>
 struct BlockOut {
-  static constexpr int NB = L - 4;
+  static constexpr int NB = L > 4 ? L - 4 : 0;
   // chunk index (within the wavefront window) holding this lane's outputs
   static __device__ __forceinline__ int chunk(int lane) {
     const int a = lane & ((1 << NB) - 1);

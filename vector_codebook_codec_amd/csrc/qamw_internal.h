@@ -24,15 +24,18 @@ int check_launch(const char* what);
 
 // ---- small helpers
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+__host__ __device__ inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int elem_size(int32_t dt) { return dt == QAMW_F32 ? 4 : (dt == QAMW_BF16 || dt == QAMW_F16) ? 2 : 0; }
 inline size_t calib_tiles(int64_t N) { return (size_t)((N + kCalibRowsPerTile - 1) / kCalibRowsPerTile); }
 inline unsigned grid_for_waves(int64_t waves) { return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock); }
 
-// Call Launch<L>::run(args...) for the Hadamard block size 2^L, 16 <= b <= 1024.
+// Call Launch<L>::run(args...) for the Hadamard block size 2^L, 2 <= b <= 1024.
 template <template <int> class Launch, typename... A>
 int dispatch_L(int L, A&&... args) {
   switch (L) {
+    case 1: return Launch<1>::run(args...);
+    case 2: return Launch<2>::run(args...);
+    case 3: return Launch<3>::run(args...);
     case 4: return Launch<4>::run(args...);
     case 5: return Launch<5>::run(args...);
     case 6: return Launch<6>::run(args...);
@@ -44,21 +47,45 @@ int dispatch_L(int L, A&&... args) {
   }
 }
 
-// ---- nearest-centroid search plan (see plan.hip): a fine grid and a coarse
-// outer grid, both square and centred on the origin
-constexpr int kPlanG = 512;                  // fine grid: cells per axis over [-kPlanR, kPlanR)
+// ---- nearest-centroid search plan (see plan.hip): a grid over [-kPlanR, kPlanR)^2
+// and a coarse outer grid over [-kPlanR2, kPlanR2)^2, both centred on the origin.
+// For K <= kLdsMaxK the inner grid is a table the encode kernel keeps in LDS
+// (non-uniform cells, one 16-bit entry per cell, shared candidate lists); for
+// larger K it is a uniform grid of per-cell records read from global memory.
+constexpr int kPlanG = 512;                  // global inner grid (K > kLdsMaxK): cells per axis
 constexpr float kPlanR = 5.0f;
 constexpr int kPlanG2 = 256;                 // outer grid: cells per axis over [-kPlanR2, kPlanR2)
 constexpr float kPlanR2 = 40.0f;
 constexpr size_t kPlanHeaderBytes = 256;
 constexpr size_t kPlanHeaderKOffset = 16;    // int32 K inside the header (plan.hip)
 __host__ __device__ inline int plan_lmax(int K) { return K <= 2048 ? 8 : 16; }
-inline size_t plan_outer_offset(int K) {
-  return kPlanHeaderBytes + (size_t)kPlanG * kPlanG * plan_lmax(K) * sizeof(uint16_t);
-}
-inline size_t plan_bytes(int K) {
-  return plan_outer_offset(K) + (size_t)kPlanG2 * kPlanG2 * plan_lmax(K) * sizeof(uint16_t);
-}
+
+// LDS table geometry.  Both axes share one map from kLdsBins equal bins over
+// [-kPlanR, kPlanR) to cell coordinates; cells are whole runs of bins, widest
+// far from the origin where centroids are sparse.  The image is copied to LDS
+// verbatim: [bin -> cell map, u8 x kLdsBins][cell entries, u16 x G x G, padded
+// to 16 bytes][candidate lists, 4 x u16 each, lists_cap of them].
+constexpr int kLdsMaxK = 2048;
+constexpr int kLdsBins = 2048;
+constexpr int kLdsMaxG = 256;
+constexpr int kLdsThreads = 1024;            // one 16-wavefront workgroup per CU
+constexpr int kLdsWaves = kLdsThreads / 64;
+constexpr size_t kLdsBudget = 160 * 1024 - 1024;   // LDS bytes one encode workgroup may take
+constexpr uint16_t kLdsScanAll = 0xFFFFu;    // cell entry: search the whole codebook
+struct LdsGeometry {
+  int G;                         // cells per axis (<= kLdsMaxG)
+  int lists_cap;                 // list records the image holds
+  size_t cells_off, lists_off;   // byte offsets inside the image
+  size_t image_bytes;            // multiple of 16
+  size_t stage_bytes;            // per-wavefront packing stage (64 B bytes)
+  uint16_t edges[kLdsMaxG + 1];  // cell c covers bins [edges[c], edges[c + 1])
+};
+bool lds_geometry(int K, LdsGeometry* g);    // false when K > kLdsMaxK
+inline bool plan_has_lds(int K) { return K >= 2 && K <= kLdsMaxK; }
+size_t plan_outer_offset(int K);             // outer grid records
+size_t plan_image_offset(int K);             // LDS image (K <= kLdsMaxK)
+size_t plan_scratch_offset(int K);           // construction scratch (K <= kLdsMaxK)
+size_t plan_bytes(int K);
 
 // ---- stage launchers (enqueue on `st`, return a qamw_status)
 int launch_scale(const float* r, float alpha, uint64_t seed, int d, float* s, float* f, hipStream_t st);
