@@ -172,6 +172,27 @@ int32_t qamw_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qamw_encode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The workspace lives in a device array of
+ * qamw_encode_noalloc_scratch_bytes() (1 MiB) inside the library, one per GPU,
+ * held until the process ends; the call allocates and frees nothing.
+ *   arguments  as for qamw_encode, less workspace and workspace_bytes
+ *   limit      qamw_encode_workspace_bytes(N, d) <= 1 MiB (every N <= 65536
+ *              with d <= 65536 fits); larger sizes return QAMW_EUNSUPPORTED
+ *              before anything runs
+ * Same results as qamw_encode, bit for bit.  All calls on one GPU share the
+ * array: calls that overlap on one GPU (other streams, other host threads)
+ * race, so the caller must order them.  Errors as for qamw_encode; QAMW_EHIP
+ * also when the array's device address cannot be looked up.
+ */
+size_t qamw_encode_noalloc_scratch_bytes(void);
+int32_t qamw_encode_noalloc(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
+                            const float* s, const float* sigma, int32_t block, uint64_t sign_seed,
+                            const float* codebook, int32_t K, const void* plan, size_t plan_size,
+                            uint32_t* packed, uint16_t* rownorm_f16, void* stream);
+
+/*
  * qamw_encode in two phases, for callers that time or reuse them separately.
  *
  * qamw_encode_prepare (QAM-W, Methodology: Separation of Scale and Direction;

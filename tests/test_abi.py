@@ -386,3 +386,23 @@ def test_decode_matmul_rejects(lib, kw, status):
                                   args["N"], args["sigma"], args["cb"], args["K"], args["Y"], args["ydt"],
                                   args["ldy"], args["stream"]) == status
     assert lib.qamw_last_error()
+
+
+def test_encode_noalloc_rejects_before_any_device_call(lib):
+    """The no-allocation encode refuses sizes beyond its 1 MiB per-GPU
+    workspace, and bad arguments, on the host before looking up the device."""
+    assert lib.qamw_encode_noalloc_scratch_bytes() == 1 << 20
+    args = [A, 1, 8, 256, 256, A, A, 128, 0, A, 256, None, 0, A, A, None]
+    big = list(args)
+    big[2] = 1 << 17                      # 2^17 fp64 row norms alone fill 1 MiB
+    assert lib.qamw_encode_noalloc(*big) == -2
+    assert b"no-allocation" in lib.qamw_last_error()
+    bad = list(args)
+    bad[7] = 3                            # block
+    assert lib.qamw_encode_noalloc(*bad) == -2
+    bad = list(args)
+    bad[13] = MIS                         # packed misaligned
+    assert lib.qamw_encode_noalloc(*bad) == -1
+    bad = list(args)
+    bad[11], bad[12] = WS, 100            # a plan too small for K
+    assert lib.qamw_encode_noalloc(*bad) == -4

@@ -19,6 +19,7 @@ from .codec import (  # noqa: F401
     qamw_decode_matmul,
     qamw_decode_matvec,
     qamw_encode,
+    qamw_encode_noalloc,
     qamw_encode_indices,
     qamw_encode_polar,
     qamw_encode_prepare,

@@ -30,6 +30,8 @@ SIGNATURES = {
     "qamw_build_plan": (_i32, [_p, _i32, _p, _sz, _p]),
     "qamw_encode": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _sz, _p, _p, _p, _sz,
                          _p]),
+    "qamw_encode_noalloc_scratch_bytes": (_sz, []),
+    "qamw_encode_noalloc": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _sz, _p, _p, _p]),
     "qamw_encode_prepare": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _p, _i32, _u64, _p, _p, _sz, _p]),
     "qamw_encode_indices": (_i32, [_p, _i32, _i64, _i64, _i64, _i32, _p, _i32, _p, _sz, _p, _p, _sz, _p]),
     "qamw_calibrate_encode_workspace_bytes": (_sz, [_i64, _i64]),

@@ -192,6 +192,40 @@ def qamw_encode(W: torch.Tensor, s: torch.Tensor, sigma: torch.Tensor, block: in
     return packed, rownorm_f16
 
 
+def qamw_encode_noalloc(W: torch.Tensor, s: torch.Tensor, sigma: torch.Tensor, block: int, sign_seed: int,
+                        codebook: torch.Tensor, plan: Optional[torch.Tensor] = None,
+                        packed: Optional[torch.Tensor] = None, rownorm_f16: Optional[torch.Tensor] = None,
+                        stream=None):
+    """qamw_encode with the library's own per-GPU workspace (no workspace argument; the C call
+    allocates nothing).  Returns (packed, rownorm_f16); pass both to avoid allocating them here."""
+    N, d, ldw = _rows(W, "W")
+    if W.dtype not in _WDT:
+        raise ValueError("W must be float32 or bfloat16")
+    _vec(s, "s", d)
+    _vec(sigma, "sigma", d // 2)
+    K = _codebook(codebook)
+    rw = qamw_packed_row_words(d, K)
+    if rw < 0:
+        raise ValueError(f"unsupported K={K} or d={d}")
+    if plan is not None:
+        _dev(plan, "plan")
+        if plan.dtype != torch.uint8 or plan.numel() < qamw_plan_bytes(K):
+            raise ValueError("plan must be a uint8 tensor from qamw_build_plan for this K")
+    if packed is None:
+        packed = torch.empty((N, rw), dtype=torch.int32, device=W.device)
+    if rownorm_f16 is None:
+        rownorm_f16 = torch.empty(N, dtype=torch.int16, device=W.device)
+    _dev(packed, "packed")
+    if packed.dtype != torch.int32 or tuple(packed.shape) != (N, rw) or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous int32 tensor of shape ({N}, {rw})")
+    _vec(rownorm_f16, "rownorm_f16", N, torch.int16)
+    _lib.check("qamw_encode_noalloc", _lib.load().qamw_encode_noalloc(
+        W.data_ptr(), _WDT[W.dtype], N, d, ldw, s.data_ptr(), sigma.data_ptr(), int(block), int(sign_seed),
+        codebook.data_ptr(), K, None if plan is None else plan.data_ptr(), 0 if plan is None else plan.numel(),
+        packed.data_ptr(), rownorm_f16.data_ptr(), _stream(stream)))
+    return packed, rownorm_f16
+
+
 def qamw_calibrate_encode_workspace_bytes(N: int, d: int) -> int:
     return int(_lib.load().qamw_calibrate_encode_workspace_bytes(N, d))
 

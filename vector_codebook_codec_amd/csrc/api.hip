@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "qamw.h"
@@ -246,6 +247,71 @@ int32_t qamw_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t
     return rc;
   return qamw_encode_indices(W, wdtype, N, d, ldw, block, codebook, K, plan, plan_size, packed, workspace,
                              workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The no-allocation encode keeps qamw_encode's workspace (row norms, column
+// factors, 1 / sigma) in this file-scope device array instead of a caller
+// buffer.  Each GPU holds its own copy until the process ends; its device
+// address is looked up once per device (hipGetSymbolAddress, with the device
+// current) and every later call on that device uses that address.  All calls
+// on one GPU share the array: calls that overlap on one GPU (different
+// streams, or host threads) race and must be ordered by the caller.  Nothing
+// in it has to start at zero: the encode writes every byte it reads.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(QAMW_EHIP, "cannot query the current device for the no-allocation scratch");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(QAMW_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QAMW_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t qamw_encode_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int32_t qamw_encode_noalloc(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw, const float* s,
+                            const float* sigma, int32_t block, uint64_t sign_seed, const float* codebook, int32_t K,
+                            const void* plan, size_t plan_size, uint32_t* packed, uint16_t* rownorm_f16,
+                            void* stream) {
+  // the size limit first (host only), then everything qamw_encode checks
+  const size_t need = qamw_encode_workspace_bytes(N, d);
+  if (need > kNoAllocScratchBytes)
+    return fail(QAMW_EUNSUPPORTED,
+                "the no-allocation encode holds %zu bytes of workspace per GPU; N=%lld d=%lld needs %zu "
+                "(use qamw_encode with a workspace)",
+                kNoAllocScratchBytes, (long long)N, (long long)d, need);
+  int L = 0;
+  int rc = check_matrix(N, d, block, &L);
+  if (rc) return rc;
+  if ((rc = check_weights(W, wdtype, d, ldw))) return rc;
+  if ((rc = check_codebook(codebook, K))) return rc;
+  if (!s || !sigma || !packed || !rownorm_f16) return fail(QAMW_EINVAL, "s, sigma, packed and rownorm_f16 must be non-NULL");
+  if (!aligned16(s) || !aligned16(sigma) || !aligned16(packed))
+    return fail(QAMW_EINVAL, "s, sigma and packed must be 16-byte aligned");
+  if ((rc = check_plan(plan, plan_size, K))) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_for_current_device(&ws))) return rc;
+  return qamw_encode(W, wdtype, N, d, ldw, s, sigma, block, sign_seed, codebook, K, plan, plan_size, packed,
+                     rownorm_f16, ws, kNoAllocScratchBytes, stream);
 }
 
 size_t qamw_calibrate_encode_workspace_bytes(int64_t N, int64_t d) {

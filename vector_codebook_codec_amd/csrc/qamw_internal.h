@@ -17,6 +17,7 @@ constexpr int kRmsRowsPerTile = 64;                  // activation rows per chan
 constexpr int kOutputErrorTokens = 128;              // tokens per output-error workgroup
 constexpr int kOutputErrorRows = 128;                // weight rows per output-error workgroup
 constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;   // per-GPU workspace of qamw_encode_noalloc
 
 // ---- errors (the message of the calling thread's last failure)
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
