@@ -119,7 +119,7 @@ int32_t qamw_calibrate(const void* W, int32_t wdtype, int64_t N, int64_t d, int6
 /*
  * Nearest-centroid search plan (QAM-W, Methodology: Joint 2D Quantization).
  * An optional, codebook-specific acceleration structure for qamw_encode: a
- * grid over [-5, 5)^2 and a 256 x 256 grid over [-40, 40)^2 whose cells
+ * grid over [-5, 5)^2 and a 128 x 128 grid over [-20, 20)^2 whose cells
  * list, in ascending index order, every centroid that can be the nearest one
  * (under qamw_encode's fp32 scores) for some point of the cell.  For
  * K <= 2048 the inner grid is a table the encode keeps in LDS: cells narrow

@@ -62,9 +62,10 @@ def lds_plan_layout(K):
     lists_off = 2048 + up(2 * G * G, 16)
     cap = min((159 * 1024 - 16 * K - 16 * 64 * B - lists_off) // 8, 32767) & ~1
     image = lists_off + 8 * cap
-    scratch = up(G * G * 16, 256) + 2 * up(G * G * 4, 256) + 256 + 256 * 4 + 32768 * 16
+    ns2 = (-(-G // 8)) * (-(-G // 4))       # 8 x 4-cell supercells
+    scratch = up(G * G * 4, 256) + up(ns2 * 4, 256) + ns2 * 64 * 8
     return dict(G=G, edges=edges, cap=cap, image_bytes=image,
-                plan_bytes=up(256 + 256 * 256 * 16 + image, 256) + scratch)
+                plan_bytes=up(256 + 128 * 128 * 16 + image, 256) + scratch)
 
 def test_host_helpers(lib):
     for K in (2, 3, 4, 256, 257, 2048, 4096):
@@ -84,9 +85,9 @@ def test_host_helpers(lib):
     assert lib.qamw_calibrate_workspace_bytes(0, 16, 16) == 0
     assert lib.qamw_status_string(-4) == b"workspace missing or too small"
     # K > 2048: header block + one uint16 record of 16 entries per cell of the
-    # uniform 512 x 512 grid and of the outer 256 x 256 grid; K <= 2048:
+    # uniform 512 x 512 grid and of the outer 128 x 128 grid; K <= 2048:
     # header, outer grid (8 entries), the LDS table image and its build scratch
-    assert lib.qamw_plan_bytes(4096) == 256 + (512 ** 2 + 256 ** 2) * 16 * 2
+    assert lib.qamw_plan_bytes(4096) == 256 + (512 ** 2 + 128 ** 2) * 16 * 2
     for K in (2, 16, 256, 1000, 2048):
         assert lib.qamw_plan_bytes(K) == lds_plan_layout(K)["plan_bytes"], K
     g = lds_plan_layout(2048)
@@ -140,7 +141,7 @@ def test_encode_prepare_rejects(lib, kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(block=1), -2), (dict(K=1), -2), (dict(cb=MIS), -1), (dict(packed=None), -1), (dict(packed=MIS), -1),
     (dict(plan=WS + 64), -1), (dict(ws=None), -4), (dict(ws_bytes=100), -4), (dict(ldw=100), -1),
-    (dict(plan=WS, plan_size=1000), -4), (dict(plan=WS, K=2048, plan_size=1 << 20), -4),
+    (dict(plan=WS, plan_size=1000), -4), (dict(plan=WS, K=2048, plan_size=1 << 19), -4),
 ])
 def test_encode_indices_rejects(lib, kw, status):
     assert _indices(lib, **kw) == status

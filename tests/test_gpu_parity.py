@@ -533,7 +533,7 @@ def read_plan(q, C):
     hdr_i = raw[:64].view(np.int32)
     lmax = 8 if K <= 2048 else 16
     assert hdr_f[0] == 5.0 and hdr_i[3] == lmax and hdr_i[4] == K
-    assert hdr_f[5] == 40.0 and hdr_f[6] == np.float32(256 / 80.0) and hdr_i[7] == 256
+    assert hdr_f[5] == 20.0 and hdr_f[6] == np.float32(128 / 40.0) and hdr_i[7] == 128
     grids = {}
     if K <= 2048:
         G, bins, cap, nlists, ib, co, lo, io = (int(v) for v in hdr_i[8:16])
@@ -549,8 +549,8 @@ def read_plan(q, C):
         counts, lists = _uniform_records(raw, 256, 512, lmax)
         grids["inner"] = ("uniform", (512, 5.0), counts, lists)
         outer_off = 256 + 512 * 512 * lmax * 2
-    counts, lists = _uniform_records(raw, outer_off, 256, lmax)
-    grids["outer"] = ("uniform", (256, 40.0), counts, lists)
+    counts, lists = _uniform_records(raw, outer_off, 128, lmax)
+    grids["outer"] = ("uniform", (128, 20.0), counts, lists)
     return grids, lmax
 
 
@@ -577,7 +577,7 @@ def grid_of(z):
     """Which grid the encode kernel consults for each point (None: full scan)."""
     zf = z.astype(np.float32)
     fine = (zf >= -5).all(1) & (zf < 5).all(1)
-    outer = (zf >= -40).all(1) & (zf < 40).all(1)
+    outer = (zf >= -20).all(1) & (zf < 20).all(1)
     return fine, outer & ~fine
 
 
@@ -605,8 +605,8 @@ def test_plan_lists_cover_near_minimisers(q, K):
     grids, lmax = read_plan(q, C)
     # the outer cells tiling the inner grid's square [-5, 5)^2 are never
     # consulted (points there take the inner grid): "scan all" records
-    G2 = 256
-    lo = (G2 - G2 * 10 // 80) // 2
+    G2 = 128
+    lo = (G2 - G2 * 10 // 40) // 2
     assert np.all(grids["outer"][2].reshape(G2, G2)[lo:G2 - lo, lo:G2 - lo] == PLAN_OVERFLOW)
     for name, (kind, geom, counts, lists) in grids.items():
         ok_cells = counts != PLAN_OVERFLOW
@@ -615,14 +615,14 @@ def test_plan_lists_cover_near_minimisers(q, K):
         assert np.all(lists[ok_cells] < K)
     rng = np.random.default_rng(K)
     fine_edges = -5 + np.arange(2048) * (10 / 2048)
-    outer_edges = -40 + np.arange(256) * (80 / 256)
+    outer_edges = -20 + np.arange(128) * (40 / 128)
     z = np.concatenate([
         rng.uniform(-5, 5, (30000, 2)),
         rng.standard_normal((30000, 2)),
         rng.standard_normal((10000, 2)) * 0.05,
         np.stack([rng.choice(fine_edges, 6000), rng.choice(fine_edges, 6000)], 1),
         np.stack([np.full(200, 5 - 1e-6), rng.uniform(-5, 5, 200)], 1),
-        rng.uniform(-40, 40, (20000, 2)),
+        rng.uniform(-20, 20, (20000, 2)),
         rng.standard_normal((10000, 2)) * 8,
         np.stack([rng.choice(outer_edges, 4000), rng.choice(outer_edges, 4000)], 1),
     ])
@@ -671,7 +671,7 @@ def test_plan_overflow_and_outside_grid(q):
     s, sigma = q.qamw_calibrate(dev(W), dev(np.ones(d, np.float32)), 0.0, b, 5)
     sig_np = sigma.cpu().numpy().copy()
     sig_np[::7] *= 1e-3                                                  # |z~| ~ 1e3: beyond both grids
-    sig_np[3::7] *= 0.15                                                 # |z~| ~ 5..30: outer grid
+    sig_np[3::7] *= 0.15                                                 # |z~| ~ 5..30: outer grid, some beyond
     sigma = dev(sig_np)
     say("case plan overflow / outer grid / outside")
     packed, rn = encode_both(q, dev(W), s, sigma, b, 5, dev(C))

@@ -29,9 +29,9 @@
 // attains U(Q); the cells then test only the supercell's survivors.
 //
 // Two grids: a fine one (G = 512 over [-5, 5)^2) where nearly all normalised
-// pairs fall, and a coarse outer one (256 over [-40, 40)^2) for the few pairs
+// pairs fall, and a coarse outer one (128 over [-20, 20)^2) for the few pairs
 // beyond it -- rows dominated by one large weight put a whole Hadamard block
-// there.  Each has its own delta (R = 5 or 40 in the formula above).  The
+// there.  Each has its own delta (R = 5 or 20 in the formula above).  The
 // outer cells that tile the fine grid's square are never consulted (points
 // there take the fine grid) and hold overflow records.
 //
@@ -85,6 +85,7 @@ constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / kWave;
 
 constexpr int kPerThread = kSuperMax / kPlanThreads;   // centroids one thread tests in the survivor pass
+constexpr int kLdsLanes = 8;                           // LDS table: lanes per cell
 
 // Axis-aligned box [x0, x1] x [y0, y1] against centroid (cx, cy).
 struct Box {
@@ -139,45 +140,31 @@ __device__ __forceinline__ Box cell_box(double R, int G, int ix0, int iy0, int n
              -R + iy0 * s - kPlanEta, -R + (iy0 + ncells) * s + kPlanEta};
 }
 
-__device__ __forceinline__ double wave_min(double v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v = fmin(v, __shfl_xor(v, off));
-  return v;
-}
-
-__device__ __forceinline__ double wave_max(double v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
-  return v;
-}
-
-struct PlanShared {
+// LDS of an inner-grid workgroup: the uniform grid (one lane per cell, 256
+// cells) or the LDS table (eight lanes per cell, 32 cells).
+template <bool kLdsTable>
+struct PlanSharedT {
+  static constexpr int kCells = kLdsTable ? kPlanThreads / kLdsLanes : kPlanThreads;
   uint16_t surv[kSuperMax];
   float2 survc[kSuperMax];
-  uint16_t cell_list[kPlanThreads][16];
-  double red[kPlanWaves];
-  double red2[kPlanWaves];
+  uint16_t cell_list[kCells][16];
+  float2 cand[kLdsTable ? kCells : 1][16];   // LDS table: a cell's loose candidates' coordinates
+  unsigned long long ckey[kCells];           // LDS table: a cell's list (4 x 11-bit index) and class,
+  int cneed[kCells];                         // records it needs, and its local record id
+  float red[kPlanWaves];
+  float red2[kPlanWaves];
   int wsum[kPlanWaves];
 };
 
-// The survivors of a supercell box SQ: every centroid with
-// min_{z in SQ} |z - c|^2 <= U(SQ) + 2 delta, ascending, with coordinates, in
-// sh.surv / sh.survc, padded with far-away dummies to whole rounds of `round`
-// entries.  Returns their count (more than kSuperMax: `all` is set and the
-// callers test every centroid from global memory); *cmax2 is the largest
-// squared centroid radius and *delta the grid's score margin
-// 1e-5 (Cmax + R sqrt 2)^2 (R: the grid's half-width).
-__device__ int supercell_survivors(PlanShared& sh, const float* __restrict__ cb, int K, const Box& sq64, double R,
-                                   int round, float* cmax2_out, double* delta_out, bool* all_out, int* ns_out) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  // ---- the codebook into registers once: thread t holds centroids
-  // r kSuperMax + t P + u (round r < 2 since K <= 4096, u < P = kPerThread),
-  // loaded as float4 pairs; past K a far-away dummy that never passes a test
-  constexpr int kRounds = 4096 / kSuperMax;
-  float2 v[kRounds][kPerThread];
+// The codebook in registers, once per workgroup: thread t holds centroids
+// r kSuperMax + t P + u (round r < 2 since K <= 4096, u < P = kPerThread),
+// loaded as float4 pairs; past K a far-away dummy that never passes a test.
+constexpr int kRounds = 4096 / kSuperMax;
+typedef float2 CbRegs[kRounds][kPerThread];
+__device__ __forceinline__ void load_cb_regs(const float* __restrict__ cb, int K, CbRegs& v) {
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
-    const int c0 = r * kSuperMax + tid * kPerThread;
+    const int c0 = r * kSuperMax + (int)threadIdx.x * kPerThread;
     const float4* p4 = reinterpret_cast<const float4*>(cb + 2 * c0);
 #pragma unroll
     for (int u = 0; u < kPerThread; u += 2) {
@@ -188,6 +175,19 @@ __device__ int supercell_survivors(PlanShared& sh, const float* __restrict__ cb,
       v[r][u + 1] = make_float2(t.z, t.w);
     }
   }
+}
+
+// The survivors of a supercell box SQ: every centroid with
+// min_{z in SQ} |z - c|^2 <= U(SQ) + 2 delta, ascending, with coordinates, in
+// sh.surv / sh.survc, padded with far-away dummies to whole rounds of `round`
+// entries.  Returns their count (more than kSuperMax: `all` is set and the
+// callers test every centroid from global memory); *cmax2 is the largest
+// squared centroid radius and *delta the grid's score margin
+// 1e-5 (Cmax + R sqrt 2)^2 (R: the grid's half-width).
+template <typename SH>
+__device__ int supercell_survivors(SH& sh, const CbRegs& v, int K, const Box& sq64, double R,
+                                   int round, float* cmax2_out, double* delta_out, bool* all_out, int* ns_out) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   // ---- U(SQ) and the largest squared centroid radius, from the registers,
   // in fp32 on the outward-widened supercell box: U is raised by 1e-6 and the
   // survivor limit U + 2 delta by 1e-6 again, so the survivors can only be
@@ -207,14 +207,17 @@ __device__ int supercell_survivors(PlanShared& sh, const float* __restrict__ cb,
         U = fminf(U, sq.dmax2(cx, cy));
         cmax2 = fmaxf(cmax2, cx * cx + cy * cy);
       }
-  U = (float)wave_min((double)U);
-  cmax2 = (float)wave_max((double)cmax2);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {     // the two reductions side by side
+    U = fminf(U, __shfl_xor(U, off));
+    cmax2 = fmaxf(cmax2, __shfl_xor(cmax2, off));
+  }
   if (lane == 0) { sh.red[wave] = U; sh.red2[wave] = cmax2; }
   __syncthreads();
-  U = (float)sh.red[0];
-  cmax2 = (float)sh.red2[0];
+  U = sh.red[0];
+  cmax2 = sh.red2[0];
 #pragma unroll
-  for (int w = 1; w < kPlanWaves; ++w) { U = fminf(U, (float)sh.red[w]); cmax2 = fmaxf(cmax2, (float)sh.red2[w]); }
+  for (int w = 1; w < kPlanWaves; ++w) { U = fminf(U, sh.red[w]); cmax2 = fmaxf(cmax2, sh.red2[w]); }
   const double reach = sqrt((double)cmax2 * 1.000001) + R * 1.4142135623730951;
   const double delta = 1e-5 * reach * reach;
   const float slim = (U * 1.000001f + f32_up(2.0 * delta)) * 1.000001f;
@@ -230,17 +233,19 @@ __device__ int supercell_survivors(PlanShared& sh, const float* __restrict__ cb,
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u)
       if (c0 + u < K && sq.dmin2(v[r][u].x, v[r][u].y) <= slim) mask |= 1u << u;
-    const int mine = __popc(mask);
-    int incl = mine;
+    // survivors in lower lanes of the wave, and in the wave: one ballot per slot u
+    const uint64_t below = (1ull << lane) - 1ull;
+    int in_wave_before = 0, in_wave = 0;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int t = __shfl_up(incl, off);
-      if (lane >= off) incl += t;
+    for (int u = 0; u < kPerThread; ++u) {
+      const uint64_t b = __ballot((mask >> u) & 1u);
+      in_wave_before += __popcll(b & below);
+      in_wave += __popcll(b);
     }
     __syncthreads();                        // the previous round's wsum reads are done
-    if (lane == kWave - 1) sh.wsum[wave] = incl;
+    if (lane == 0) sh.wsum[wave] = in_wave;
     __syncthreads();
-    int before = nsurv + incl - mine, total = nsurv;
+    int before = nsurv + in_wave_before, total = nsurv;
 #pragma unroll
     for (int w = 0; w < kPlanWaves; ++w) {
       before += (w < wave) ? sh.wsum[w] : 0;
@@ -275,9 +280,9 @@ __device__ int supercell_survivors(PlanShared& sh, const float* __restrict__ cb,
 // One workgroup per supercell (S x S cells) of a G x G grid over [-R, R)^2:
 // the supercell's survivors (ascending, with coordinates) into LDS, then a
 // group of LPC = 256 / S^2 lanes per cell scans them and writes the records.
-template <int S>
-__device__ void build_supercell(PlanShared& sh, const float* __restrict__ cb, int K, int lmax, double R, int G,
-                                int sidx, uint16_t* __restrict__ lists) {
+template <int S, typename SH>
+__device__ void build_supercell(SH& sh, const float* __restrict__ cb, const CbRegs& v, int K, int lmax,
+                                double R, int G, int sidx, uint16_t* __restrict__ lists) {
   constexpr int LPC = kPlanThreads / (S * S);
   static_assert(LPC >= 1 && LPC * S * S == kPlanThreads && kWave % LPC == 0, "cell groups tile the wavefronts");
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -289,7 +294,7 @@ __device__ void build_supercell(PlanShared& sh, const float* __restrict__ cb, in
   double delta;
   bool all;
   int ns;
-  supercell_survivors(sh, cb, K, cell_box(R, G, sx * S, sy * S, S), R, kRound, &cmax2, &delta, &all, &ns);
+  supercell_survivors(sh, v, K, cell_box(R, G, sx * S, sy * S, S), R, kRound, &cmax2, &delta, &all, &ns);
   (void)cmax2;
 
   // ---- LPC lanes per cell: survivors j = sub, sub + LPC, ...  The cell
@@ -377,63 +382,49 @@ __device__ void build_supercell(PlanShared& sh, const float* __restrict__ cb, in
 // sqrt(U(Q) + delta) of z (delta the grid's margin, >= slack everywhere), so
 // cm = min(Cmax, zmax + sqrt(U(Q) + delta)); delta_Q is ten times that bound.
 // The test for one c is the feasibility of a small 2D linear system (the box
-// and one half-plane 2 z.(c' - c) <= |c'|^2 - |c|^2 + delta_Q per c'): if the
-// feasible polygon is not empty, one of its vertices is the intersection of
-// two of the lines, so every such intersection point is tried (in fp64, with
-// a tolerance that errs towards listing).  Only the cell's loose candidates
+// and one half-plane 2 z.(c' - c) <= |c'|^2 - |c|^2 + delta_Q per c'),
+// decided by eliminating y (in fp64, with bounds that err towards listing).
+// Only the cell's loose candidates
 // (min_{z in Q} |z - c|^2 <= U(Q) + delta_Q) need testing or acting as c': any
 // other centroid is farther than the one attaining U(Q) everywhere in Q.
 // ===========================================================================
-constexpr int kLdsSuper = 8;           // LDS-table supercells: 8 x 8 cells, four lanes per cell
+constexpr int kLdsSuperX = 8;          // LDS-table supercells: 8 x 4 cells, eight lanes per cell
+constexpr int kLdsSuperY = 4;
 constexpr int kLdsLoose = 16;          // loose candidates a cell may keep (more: scan all)
 constexpr int kLdsListMax = 8;         // exact candidates a cell may list (more: scan all)
-constexpr int kHashSlots = 32768;      // list dedup table (>= 1.4 x the cells of any geometry)
-static_assert(kHashSlots >= 2 * kLdsMaxG * kLdsMaxG / 4, "dedup table load factor");
-
 struct LdsEdges {
   uint16_t e[kLdsMaxG + 1];
 };
 
-// dedup table entry: the list (4 x u16), the lowest cell holding it, its record id
-struct HashSlot {
-  unsigned long long key;
-  unsigned int owner;
-  unsigned int id;
-};
-
+// Global scratch of the build, per supercell of the LDS table (8 x 4 cells):
+// its cells' entries before numbering (u32 per cell: the final 16-bit entry,
+// or 1 << 16 | local record id, with 1 << 17 for a two-record list), its
+// count of records, and the records themselves (at most two per cell).  Equal
+// lists inside one supercell share a record; the table's record ids are the
+// local ones offset by the records of the supercells before it.
+constexpr int kLdsSuperCells = kLdsSuperX * kLdsSuperY;
+static_assert(kLdsSuperCells * kLdsLanes == kPlanThreads, "one workgroup per supercell");
+constexpr int kRecsPerSuper = 2 * kLdsSuperCells;
 struct LdsScratch {
-  uint4* cellset;         // [G*G] exact candidate sets: 8 x u16 16c, low nibble of entry 0 = count - 1,
-                          // of entry 1 = 1 when the cell must scan all
-  int* slot;              // [G*G] dedup slot of a 2..4 list, -1 otherwise
-  int* recid;             // [G*G] record id of a 5..8 list (two records), or of an owned 2..4 list
-  int* total;             // records used
-  int* blocksum;          // [kMaxScanBlocks] records needed per block of kScanBlock cells
-  HashSlot* table;        // [kHashSlots]
+  uint32_t* desc;         // [G*G]
+  int* nrec;              // [nsuper^2]
+  uint2* recs;            // [supercells][kRecsPerSuper]
 };
-
-constexpr int kScanBlock = 256;                  // cells per block of the record-id scan
-constexpr int kMaxScanBlocks = kLdsMaxG * kLdsMaxG / kScanBlock;
-
+__host__ __device__ inline int lds_nsuper_x(int G) { return (G + kLdsSuperX - 1) / kLdsSuperX; }
+__host__ __device__ inline int lds_nsuper_y(int G) { return (G + kLdsSuperY - 1) / kLdsSuperY; }
+__host__ __device__ inline int lds_nsupercells(int G) { return lds_nsuper_x(G) * lds_nsuper_y(G); }
 __host__ __device__ inline size_t lds_scratch_bytes(int G) {
-  const size_t cells = (size_t)G * G;
-  return round_up(cells * 16, 256) + 2 * round_up(cells * 4, 256) + 256 + kMaxScanBlocks * sizeof(int) +
-         (size_t)kHashSlots * sizeof(HashSlot);
+  const size_t ns2 = (size_t)lds_nsupercells(G);
+  return round_up((size_t)G * G * 4, 256) + round_up(ns2 * 4, 256) + ns2 * kRecsPerSuper * 8;
 }
-
 __device__ __forceinline__ LdsScratch lds_scratch(char* base, int G) {
-  const size_t cells = (size_t)G * G;
+  const size_t ns2 = (size_t)lds_nsupercells(G);
   LdsScratch s;
-  s.cellset = reinterpret_cast<uint4*>(base);
-  base += round_up(cells * 16, 256);
-  s.slot = reinterpret_cast<int*>(base);
-  base += round_up(cells * 4, 256);
-  s.recid = reinterpret_cast<int*>(base);
-  base += round_up(cells * 4, 256);
-  s.total = reinterpret_cast<int*>(base);
-  base += 256;
-  s.blocksum = reinterpret_cast<int*>(base);
-  base += kMaxScanBlocks * sizeof(int);
-  s.table = reinterpret_cast<HashSlot*>(base);
+  s.desc = reinterpret_cast<uint32_t*>(base);
+  base += round_up((size_t)G * G * 4, 256);
+  s.nrec = reinterpret_cast<int*>(base);
+  base += round_up(ns2 * 4, 256);
+  s.recs = reinterpret_cast<uint2*>(base);
   return s;
 }
 
@@ -458,76 +449,103 @@ __device__ __forceinline__ double corner_min_diff(const Box& q, double ix, doubl
 }
 
 // Is there a point z of q with |z - c_i|^2 <= |z - c_k|^2 + delta for every k
-// in the set `keep` (a bitmask over m[0..n))?  If that polygon is not empty
-// one of its vertices is the intersection of two of the lines (box edges and
-// the constraints' boundaries), so every such point is tried, in fp64, with a
-// tolerance that errs towards "feasible".
-__device__ bool lds_feasible(const PlanShared& sh, const uint16_t* m, int n, uint32_t keep, int i, const Box& q,
-                             double delta) {
-  const float2 fi = sh.survc[m[i]];
-  const double cix = fi.x, ciy = fi.y, ci2 = cix * cix + ciy * ciy;
-  auto cons = [&](int k, double& ax, double& ay, double& b) {
-    const float2 fk = sh.survc[m[k]];
-    const double kx = fk.x, ky = fk.y;
+// in the set `keep` (a bitmask over the cell's candidates cand[0..n))?  Each
+// such condition is the half-plane a_k . z <= b_k, a_k = 2 (c_k - c_i),
+// b_k = |c_k|^2 - |c_i|^2 + delta, and q adds y <= y1, -y <= -y0 and the
+// x-range [x0, x1].  Fourier-Motzkin elimination of y decides it exactly:
+// every pair of an upper row (a_y > 0) and a lower row (a_y < 0) implies
+// alpha x <= beta with alpha = ay_p ax_q - ay_q ax_p and beta = ay_p b_q -
+// ay_q b_p, rows with a_y = 0 bound x directly, and the system has a
+// solution iff the x-interval those bounds leave is not empty.  The a's are
+// differences of fp32 values, exact in fp64, so the sign of alpha is exact;
+// the b's and betas carry rounding, which every bound absorbs by moving
+// outward (by 1e-12 of the magnitudes involved), so the test errs towards
+// "feasible" (listing a centroid too many is harmless).  Bounds are kept as
+// fractions and compared by cross-multiplication (no division per pair).
+// The lanes of a cell share one test: lane sub takes the rows p = sub,
+// sub + kLdsLanes, ... and the lanes' intervals are intersected.
+__device__ bool lds_feasible(const float2* cand, int n, uint32_t keep, int i, const Box& q, double delta,
+                             int sub) {
+  const double cix = cand[i].x, ciy = cand[i].y, ci2 = cix * cix + ciy * ciy;
+  // row r < n: candidate r (when kept and not i); r == n: y <= y1; r == n + 1: -y <= -y0.
+  // s is the magnitude of b's terms, for its rounding bound.
+  auto row = [&](int r, double& ax, double& ay, double& b, double& s) -> bool {
+    if (r == n) { ax = 0.0; ay = 1.0; b = q.y1; s = fabs(q.y1); return true; }
+    if (r == n + 1) { ax = 0.0; ay = -1.0; b = -q.y0; s = fabs(q.y0); return true; }
+    if (r == i || !((keep >> r) & 1u)) return false;
+    const double kx = cand[r].x, ky = cand[r].y, k2 = kx * kx + ky * ky;
     ax = 2.0 * (kx - cix);
     ay = 2.0 * (ky - ciy);
-    b = (kx * kx + ky * ky) - ci2 + delta;
-  };
-  auto ok = [&](double px, double py) -> bool {
-    const double tb = 1e-12 * (1.0 + fabs(px) + fabs(py));
-    if (!(px >= q.x0 - tb && px <= q.x1 + tb && py >= q.y0 - tb && py <= q.y1 + tb)) return false;
-    for (int k = 0; k < n; ++k) {
-      if (k == i || !((keep >> k) & 1u)) continue;
-      double ax, ay, b;
-      cons(k, ax, ay, b);
-      if (ax * px + ay * py > b + 1e-12 * (fabs(ax * px) + fabs(ay * py) + fabs(b)) + 1e-15) return false;
-    }
+    b = k2 - ci2 + delta;
+    s = k2 + ci2 + delta;
     return true;
   };
-  if (ok(q.x0, q.y0) || ok(q.x0, q.y1) || ok(q.x1, q.y0) || ok(q.x1, q.y1)) return true;
-  for (int k = 0; k < n; ++k) {
-    if (k == i || !((keep >> k) & 1u)) continue;
-    double ax, ay, b;
-    cons(k, ax, ay, b);
-    if (ay != 0.0 && (ok(q.x0, (b - ax * q.x0) / ay) || ok(q.x1, (b - ax * q.x1) / ay))) return true;
-    if (ax != 0.0 && (ok((b - ay * q.y0) / ax, q.y0) || ok((b - ay * q.y1) / ax, q.y1))) return true;
-  }
-  for (int k = 0; k < n; ++k) {
-    if (k == i || !((keep >> k) & 1u)) continue;
-    double axk, ayk, bk;
-    cons(k, axk, ayk, bk);
-    for (int j = k + 1; j < n; ++j) {
-      if (j == i || !((keep >> j) & 1u)) continue;
-      double axj, ayj, bj;
-      cons(j, axj, ayj, bj);
-      const double det = axk * ayj - ayk * axj;
-      if (det == 0.0) continue;
-      if (ok((bk * ayj - bj * ayk) / det, (axk * bj - axj * bk) / det)) return true;
+  // the x-interval [lo_n / lo_d, hi_n / hi_d] (denominators > 0): a bound
+  // num / den replaces the current one when it is tighter, by cross-multiplying
+  double lo_n = q.x0, lo_d = 1.0, hi_n = q.x1, hi_d = 1.0;
+  bool bad = false;
+  auto upper = [&](double num, double den) {
+    if (num * hi_d < hi_n * den) { hi_n = num; hi_d = den; }
+  };
+  auto lower = [&](double num, double den) {
+    if (num * lo_d > lo_n * den) { lo_n = num; lo_d = den; }
+  };
+  auto bound = [&](double al, double be) {      // al x <= be
+    if (al > 0.0) upper(be, al);
+    else if (al < 0.0) lower(-be, -al);          // x >= be / al = -be / -al
+    else bad = bad || be < 0.0;
+  };
+  for (int p = sub; p < n + 2; p += kLdsLanes) {
+    double axp, ayp, bp, sp;
+    if (!row(p, axp, ayp, bp, sp)) continue;
+    if (ayp == 0.0) {
+      bound(axp, bp + 1e-12 * (fabs(bp) + sp));
+      continue;
+    }
+    if (ayp < 0.0) continue;
+    for (int r = 0; r < n + 2; ++r) {
+      double axq, ayq, bq, sq;
+      if (!row(r, axq, ayq, bq, sq) || !(ayq < 0.0)) continue;
+      const double al = ayp * axq - ayq * axp;
+      const double be = ayp * bq - ayq * bp;
+      bound(al, be + 1e-12 * (ayp * (fabs(bq) + sq) - ayq * (fabs(bp) + sp)));
     }
   }
-  return false;
+  // intersect the lanes' intervals
+#pragma unroll
+  for (int off = kLdsLanes / 2; off > 0; off >>= 1) {
+    const double ln = __shfl_xor(lo_n, off), ld = __shfl_xor(lo_d, off);
+    const double hn = __shfl_xor(hi_n, off), hd = __shfl_xor(hi_d, off);
+    bad = __shfl_xor((int)bad, off) != 0 || bad;
+    lower(ln, ld);
+    upper(hn, hd);
+  }
+  // lo <= hi, with a relative tolerance
+  const double lo = lo_n / lo_d, hi = hi_n / hi_d;
+  return !bad && lo <= hi + 1e-12 * (1.0 + fabs(lo) + fabs(hi));
 }
 
-// One workgroup per 8 x 8-cell supercell of the LDS table: survivors, then
-// four lanes per cell: U(Q), delta_Q, the loose candidates (ascending), the
+// One workgroup per 8 x 4-cell supercell of the LDS table: survivors, then
+// eight lanes per cell: U(Q), delta_Q, the loose candidates (ascending), the
 // dominance pruning and the exact test of what is left, split over the lanes.
-constexpr int kLdsLanes = 4;
-__device__ void build_lds_supercell(PlanShared& sh, const float* __restrict__ cb, int K, const LdsEdges& E, int G,
-                                    int sidx, LdsScratch scr) {
+static_assert(sizeof(PlanSharedT<true>::cand) / sizeof(PlanSharedT<true>::cand[0]) == kPlanThreads / kLdsLanes &&
+              sizeof(PlanSharedT<true>::cand[0]) / sizeof(float2) >= kLdsLoose, "one candidate row per cell");
+__device__ void build_lds_supercell(PlanSharedT<true>& sh, const CbRegs& v, int K, const LdsEdges& E, int G, int sidx,
+                                    LdsScratch scr) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int nsuper = (G + kLdsSuper - 1) / kLdsSuper;
-  const int sx = sidx / nsuper, sy = sidx % nsuper;
-  const int x0 = sx * kLdsSuper, y0 = sy * kLdsSuper;
-  const int x1 = min(x0 + kLdsSuper, G), y1 = min(y0 + kLdsSuper, G);
+  const int nsy = lds_nsuper_y(G);
+  const int sx = sidx / nsy, sy = sidx % nsy;
+  const int x0 = sx * kLdsSuperX, y0 = sy * kLdsSuperY;
+  const int x1 = min(x0 + kLdsSuperX, G), y1 = min(y0 + kLdsSuperY, G);
   constexpr int kRound = 4 * kLdsLanes;
   float cmax2;
   double delta;
   bool all;
   int ns;
-  supercell_survivors(sh, cb, K, lds_box(E, x0, x1, y0, y1), kPlanR, kRound, &cmax2, &delta, &all, &ns);
+  supercell_survivors(sh, v, K, lds_box(E, x0, x1, y0, y1), kPlanR, kRound, &cmax2, &delta, &all, &ns);
   // K <= kSuperMax here, so the survivors always fit (all == false)
   const int qc = tid / kLdsLanes, sub = tid % kLdsLanes;
-  const int ix = x0 + qc / kLdsSuper, iy = y0 + qc % kLdsSuper;
+  const int ix = x0 + qc / kLdsSuperY, iy = y0 + qc % kLdsSuperY;
   const bool real = ix < x1 && iy < y1;          // lanes of cells past the table's edge compute a copy of the last
   const int cx_ = min(ix, G - 1), cy_ = min(iy, G - 1);
   const Box cq64 = lds_box(E, cx_, cx_ + 1, cy_, cy_ + 1);
@@ -566,35 +584,72 @@ __device__ void build_lds_supercell(PlanShared& sh, const float* __restrict__ cb
   // (lane sub decides candidates sub, sub + 4, ...; the four masks are or-ed)
   const bool over_loose = nl > kLdsLoose || nl == 0;
   const int n = over_loose ? 0 : nl;
+  float2* cand = sh.cand[qc];
+  for (int k = sub; k < n; k += kLdsLanes) cand[k] = sh.survc[mine[k]];
+  __syncthreads();
   uint32_t undom = 0;
   for (int i = sub; i < n; i += kLdsLanes) {
-    const float2 fi = sh.survc[mine[i]];
+    const float2 fi = cand[i];
     bool dominated = false;
     for (int k = 0; k < n && !dominated; ++k) {
       if (k == i) continue;
-      const float2 fk = sh.survc[mine[k]];
+      const float2 fk = cand[k];
       dominated = corner_min_diff(cq64, fi.x, fi.y, fk.x, fk.y) > dq * (1.0 + 1e-9) + 1e-15;
     }
     if (!dominated) undom |= 1u << i;
   }
 #pragma unroll
   for (int off = kLdsLanes / 2; off > 0; off >>= 1) undom |= (uint32_t)__shfl_xor((int)undom, off);
+  // ---- a cheap sufficient test first: a candidate within dq of the minimum
+  // at one of 16 points of the cell (a 4 x 4 grid including the corners;
+  // lane sub takes column sub % 4 and two of its rows) qualifies.  fp32 here
+  // can only keep a candidate too many, which is harmless.
+  static_assert(kLdsLanes == 8, "two of the 16 points per lane");
   uint32_t keep = 0;
-  for (int i = sub; i < n; i += kLdsLanes)
-    if (((undom >> i) & 1u) && (__popc(undom) == 1 || lds_feasible(sh, mine, n, undom, i, cq64, dq))) keep |= 1u << i;
+  if (__popc(undom) > 1) {
+    const float px = cq.x0 + (cq.x1 - cq.x0) * (float)(sub & 3) * (1.0f / 3.0f);
+    float py[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) py[t] = cq.y0 + (cq.y1 - cq.y0) * (float)(2 * (sub >> 2) + t) * (1.0f / 3.0f);
+    const float dqf = (float)dq;
+    float dmin[2] = {INFINITY, INFINITY};
+    for (int k = 0; k < n; ++k) {
+      if (!((undom >> k) & 1u)) continue;
+      const float2 c = cand[k];
+      const float dx = px - c.x;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) dmin[t] = fminf(dmin[t], dx * dx + (py[t] - c.y) * (py[t] - c.y));
+    }
+    for (int k = 0; k < n; ++k) {
+      if (!((undom >> k) & 1u)) continue;
+      const float2 c = cand[k];
+      const float dx = px - c.x;
+      bool near = false;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) near = near || dx * dx + (py[t] - c.y) * (py[t] - c.y) <= dmin[t] + dqf;
+      if (near) keep |= 1u << k;
+    }
+  } else {
+    keep = undom;
+  }
 #pragma unroll
   for (int off = kLdsLanes / 2; off > 0; off >>= 1) keep |= (uint32_t)__shfl_xor((int)keep, off);
-  if (sub != 0 || !real) return;
-  // ---- the cell's exact set, ascending (mine[] ascends)
+  // ---- the exact test for the rest, each shared by the cell's lanes (the
+  // same trip count in them: `rest` is the same in them)
+  for (uint32_t rest = undom & ~keep; rest != 0u; rest &= rest - 1u) {
+    const int i = __ffs(rest) - 1;
+    if (lds_feasible(cand, n, undom, i, cq64, dq, sub)) keep |= 1u << i;
+  }
+  // ---- the cell's exact set, ascending (mine[] ascends): its class (0 scan
+  // all, 1 one centroid, 2 a 2..4 list, 3 a 5..8 list) and entries
   const int count = __popc(keep);
-  const bool over = over_loose || count > kLdsListMax || count == 0;
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  const bool over = over_loose || count > kLdsListMax || count == 0 || !real;
+  uint32_t ent[kLdsListMax];
+#pragma unroll
+  for (int q = 0; q < kLdsListMax; ++q) ent[q] = 0;
   if (!over) {
-    uint32_t ent[kLdsListMax];
     int c = 0;
     uint32_t last = 0;
-#pragma unroll
-    for (int q = 0; q < kLdsListMax; ++q) ent[q] = 0;
     for (int i = 0; i < n; ++i)
       if ((keep >> i) & 1u) {
         last = 16u * sh.surv[mine[i]];
@@ -604,22 +659,50 @@ __device__ void build_lds_supercell(PlanShared& sh, const float* __restrict__ cb
       }
 #pragma unroll
     for (int q = 0; q < kLdsListMax; ++q) ent[q] = (q >= count) ? last : ent[q];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = ent[2 * q] | (ent[2 * q + 1] << 16);
   }
-  w[0] |= over ? (1u << 16) : (uint32_t)(count - 1);
-  scr.cellset[(size_t)ix * G + iy] = make_uint4(w[0], w[1], w[2], w[3]);
+  const int cls = over ? 0 : (count == 1 ? 1 : (count <= 4 ? 2 : 3));
+  // ---- equal 2..4 lists share the record of the first cell holding them
+  if (sub == 0) {
+    const unsigned long long key = (unsigned long long)(ent[0] >> 4) | ((unsigned long long)(ent[1] >> 4) << 11) |
+                                   ((unsigned long long)(ent[2] >> 4) << 22) |
+                                   ((unsigned long long)(ent[3] >> 4) << 33);
+    sh.ckey[qc] = key | ((unsigned long long)cls << 60);
+  }
+  __syncthreads();
+  int owner = qc;
+  if (cls == 2)
+    for (int c = 0; c < qc; ++c)
+      if (sh.ckey[c] == sh.ckey[qc]) { owner = c; break; }
+  if (sub == 0) sh.cneed[qc] = cls == 3 ? 2 : (cls == 2 && owner == qc ? 1 : 0);
+  __syncthreads();
+  if (sub == 0 && real) {
+    int lid = 0;                                 // the owner's local record id
+    for (int c = 0; c < owner; ++c) lid += sh.cneed[c];
+    uint32_t desc = kLdsScanAll;
+    if (cls == 1) desc = ent[0];
+    else if (cls >= 2) desc = (1u << 16) | (cls == 3 ? 1u << 17 : 0u) | (uint32_t)lid;
+    scr.desc[(size_t)ix * G + iy] = desc;
+    uint2* recs = scr.recs + (size_t)sidx * kRecsPerSuper;
+    if (cls == 2 && owner == qc) recs[lid] = make_uint2(ent[0] | (ent[1] << 16), ent[2] | (ent[3] << 16));
+    if (cls == 3) {
+      recs[lid] = make_uint2(ent[0] | (ent[1] << 16), ent[2] | (ent[3] << 16) | 0x80000000u);   // continued
+      recs[lid + 1] = make_uint2(ent[4] | (ent[5] << 16), ent[6] | (ent[7] << 16));
+    }
+  }
+  if (threadIdx.x == 0) {
+    int tot = 0;
+    for (int c = 0; c < kLdsSuperCells; ++c) tot += sh.cneed[c];
+    scr.nrec[sidx] = tot;
+  }
 }
 
-// Two launches build the grids: build_plan_kernel the inner grid's supercells
-// (the LDS table's 8 x 8 cells with four lanes per cell for K <= kLdsMaxK,
-// else the uniform 512 x 512 grid's 16 x 16 cells with one lane per cell),
-// build_outer_kernel the outer grid's 4 x 4-cell supercells (16 lanes per
-// cell; its cells are larger, so a 16 x 16 supercell would keep most of the
-// codebook).  Every workgroup computes the largest centroid radius itself
-// (with U of its supercell); workgroup 0 of the first writes the header, and
-// with the LDS table every workgroup of the first clears a stripe of the
-// dedup table.
+// One launch builds both grids: the inner grid's supercells (the LDS table's
+// 8 x 4 cells with eight lanes per cell for K <= kLdsMaxK, else the uniform
+// 512 x 512 grid's 16 x 16 cells with one lane per cell), then the outer
+// grid's 4 x 4-cell supercells (16 lanes per cell; its cells are larger, so a
+// 16 x 16 supercell would keep most of the codebook), several per workgroup.  Every workgroup
+// computes the largest centroid radius itself (with U of its supercell);
+// workgroup 0 writes the header.
 constexpr int kSuperFine = 16;
 constexpr int kSuperOuter = 4;
 constexpr int kFineSupercells = (kPlanG / kSuperFine) * (kPlanG / kSuperFine);
@@ -643,10 +726,162 @@ __device__ __forceinline__ bool outer_supercell_unused(int sidx) {
          y0 + kSuperOuter <= kOuterFineHi;
 }
 
+// The outer grid: each workgroup builds a 2 x 2 block of 4 x 4-cell
+// supercells, one per wavefront.  The block's survivors (the supercell test
+// on the block's box, all 256 lanes) are a superset of each supercell's
+// (a larger box has smaller distances and a larger U), and contain the
+// centroid attaining each supercell's U; each wavefront then takes its
+// supercell's survivors from them by ballot, and its 16 cells' lists with
+// four lanes per cell, with no barrier.  The lists are the ones the
+// supercell test on the whole codebook gives.
+constexpr int kOuterPerWG = kPlanThreads / kWave;   // supercells per workgroup, 2 x 2
+constexpr int kOuterSurvMax = 128;                  // a supercell's survivors kept; more: its cells use the block's
+constexpr int kOuterLPC = kWave / (kSuperOuter * kSuperOuter);
+static_assert(kOuterPerWG == 4 && kOuterLPC == 4, "2 x 2 supercells per workgroup, four lanes per outer cell");
+struct OuterShared {
+  uint16_t surv[kSuperMax];                       // the block's survivors (supercell_survivors)
+  float2 survc[kSuperMax];
+  float red[kPlanWaves];
+  float red2[kPlanWaves];
+  int wsum[kPlanWaves];
+  float2 wsurvc[kOuterPerWG][kOuterSurvMax];      // each supercell's
+  uint16_t wsurv[kOuterPerWG][kOuterSurvMax];
+  uint16_t list[kOuterPerWG][kSuperOuter * kSuperOuter][16];
+};
+
+__device__ void build_outer_block(OuterShared& os, const float* __restrict__ cb, const CbRegs& v, int K, int lmax,
+                                  uint16_t* __restrict__ lists, int blk) {
+  constexpr int nsuper = kPlanG2 / kSuperOuter, nblk = nsuper / 2;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
+  const int bx = blk / nblk, by = blk % nblk;
+  // ---- the block's survivors (and the grid's delta), all lanes
+  float cmax2;
+  double delta;
+  bool ball;
+  int nb;
+  supercell_survivors(os, v, K, cell_box(kPlanR2, kPlanG2, bx * 2 * kSuperOuter, by * 2 * kSuperOuter, 2 * kSuperOuter),
+                      kPlanR2, kWave, &cmax2, &delta, &ball, &nb);
+  const int sx = 2 * bx + (w >> 1), sy = 2 * by + (w & 1), sidx = sx * nsuper + sy;
+  if (outer_supercell_unused(sidx)) {          // never consulted: one overflow record per cell
+    if (lane < kSuperOuter * kSuperOuter) {
+      const int ix = sx * kSuperOuter + lane / kSuperOuter, iy = sy * kSuperOuter + lane % kSuperOuter;
+      uint4* out = reinterpret_cast<uint4*>(lists + ((size_t)ix * kPlanG2 + iy) * lmax);
+      out[0] = make_uint4(1u << 16, 0u, 0u, 0u);
+      if (lmax == 16) out[1] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    return;
+  }
+  // the block's list (padded to whole wavefronts), or the whole codebook
+  auto bsurv = [&](int j, float2* c, int* idx) {
+    if (ball) { *c = make_float2(cb[2 * j], cb[2 * j + 1]); *idx = j; }
+    else { *c = os.survc[j]; *idx = os.surv[j]; }
+  };
+  const Box sq64 = cell_box(kPlanR2, kPlanG2, sx * kSuperOuter, sy * kSuperOuter, kSuperOuter);
+  const BoxF sq{f32_down(sq64.x0), f32_up(sq64.x1), f32_down(sq64.y0), f32_up(sq64.y1)};
+  // ---- U(SQ) (margins as in supercell_survivors): the block's list holds its minimiser
+  float U = INFINITY;
+  for (int j = lane; j < nb; j += kWave) {
+    float2 c;
+    int idx;
+    bsurv(j, &c, &idx);
+    U = fminf(U, sq.dmax2(c.x, c.y));
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) U = fminf(U, __shfl_xor(U, off));
+  const float slim = (U * 1.000001f + f32_up(2.0 * delta)) * 1.000001f;
+  // ---- the supercell's survivors, ascending, compacted by ballot
+  float2* survc = os.wsurvc[w];
+  uint16_t* surv = os.wsurv[w];
+  const uint64_t below = (1ull << lane) - 1ull;
+  int ns = 0;
+  for (int j0 = 0; j0 < nb; j0 += kWave) {      // nb is a whole number of wavefronts (or K)
+    const int j = j0 + lane;
+    float2 c = make_float2(1e30f, 1e30f);
+    int idx = 0;
+    if (j < nb) bsurv(j, &c, &idx);
+    const bool pred = j < nb && sq.dmin2(c.x, c.y) <= slim;
+    const uint64_t b = __ballot(pred);
+    const int pos = ns + __popcll(b & below);
+    if (pred && pos < kOuterSurvMax) { survc[pos] = c; surv[pos] = (uint16_t)idx; }
+    ns += __popcll(b);
+  }
+  const bool wall = ns > kOuterSurvMax;          // too many: the cells test the block's list
+  const int nsp = wall ? nb : (ns + kOuterLPC - 1) / kOuterLPC * kOuterLPC;
+  if (!wall && ns + lane < nsp) { survc[ns + lane] = make_float2(1e30f, 1e30f); surv[ns + lane] = 0; }
+  wave_lds_fence();
+  auto src = [&](int j, float2* c, int* idx) {
+    if (wall) bsurv(j, c, idx);
+    else { *c = survc[j]; *idx = surv[j]; }
+  };
+  // ---- four lanes per cell: U(Q), then the loose list in index order
+  const int qc = lane / kOuterLPC, sub = lane % kOuterLPC;
+  const int ix = sx * kSuperOuter + qc / kSuperOuter, iy = sy * kSuperOuter + qc % kSuperOuter;
+  const Box cq64 = cell_box(kPlanR2, kPlanG2, ix, iy, 1);
+  const BoxF cq{f32_down(cq64.x0), f32_up(cq64.x1), f32_down(cq64.y0), f32_up(cq64.y1)};
+  float Uc = INFINITY;
+  for (int j = sub; j < nsp; j += kOuterLPC) {
+    float2 c;
+    int idx;
+    src(j, &c, &idx);
+    Uc = fminf(Uc, cq.dmax2(c.x, c.y));
+  }
+#pragma unroll
+  for (int off = kOuterLPC / 2; off > 0; off >>= 1) Uc = fminf(Uc, __shfl_xor(Uc, off));
+  const float lim = (Uc * 1.000001f + f32_up(delta)) * 1.000001f;
+  uint16_t* mine = os.list[w][qc];
+  const int gshift = lane & ~(kOuterLPC - 1);
+  int count = 0;
+  for (int j0 = 0; j0 < nsp; j0 += kOuterLPC) {   // the same trip count in every lane
+    const int j = j0 + sub;
+    float2 c;
+    int idx;
+    src(min(j, nsp - 1), &c, &idx);
+    const bool pred = j < nsp && cq.dmin2(c.x, c.y) <= lim;
+    const uint64_t gm = (__ballot(pred) >> gshift) & ((1ull << kOuterLPC) - 1ull);
+    const int pos = count + __popcll(gm & ((1ull << sub) - 1ull));
+    if (pred && pos < lmax) mine[pos] = (uint16_t)(16 * idx);
+    count += __popcll(gm);
+  }
+  wave_lds_fence();
+  if (sub != 0) return;
+  // ---- the record: tail repeats the last entry (rescoring it never wins a strict "<")
+  const bool overflow = count > lmax || count == 0;
+  uint32_t words[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t lo = 0, hi = 0;
+    if (2 * q < lmax && !overflow) {
+      lo = mine[min(2 * q, count - 1)];
+      hi = mine[min(2 * q + 1, count - 1)];
+    }
+    words[q] = lo | (hi << 16);
+  }
+  words[0] |= overflow ? (1u << 16) : (uint32_t)(count - 1);
+  uint4* out = reinterpret_cast<uint4*>(lists + ((size_t)ix * kPlanG2 + iy) * lmax);
+  out[0] = make_uint4(words[0], words[1], words[2], words[3]);
+  if (lmax == 16) out[1] = make_uint4(words[4], words[5], words[6], words[7]);
+}
+
+// Both grids in one launch: workgroups [0, ninner) build the inner grid's
+// supercells (dispatched first: near the origin they hold the most work),
+// the rest the outer grid's.
+template <bool kLdsTable>
 __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* __restrict__ cb, int K, int lmax,
                                                                   char* __restrict__ plan, int lds_G, LdsEdges edges,
-                                                                  size_t scratch_offset) {
-  __shared__ PlanShared sh;
+                                                                  size_t scratch_offset, int ninner,
+                                                                  size_t outer_offset) {
+  __shared__ union {
+    PlanSharedT<kLdsTable> inner;
+    OuterShared outer;
+  } lds;
+  CbRegs v;
+  load_cb_regs(cb, K, v);
+  if ((int)blockIdx.x >= ninner) {
+    build_outer_block(lds.outer, cb, v, K, lmax, reinterpret_cast<uint16_t*>(plan + outer_offset),
+                      (int)blockIdx.x - ninner);
+    return;
+  }
+  auto& sh = lds.inner;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     PlanHeader* hdr = reinterpret_cast<PlanHeader*>(plan);
     hdr->R = kPlanR;
@@ -657,144 +892,93 @@ __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* _
     hdr->R2 = kPlanR2;
     hdr->cells_per_unit2 = (float)kPlanG2 / (2.0f * kPlanR2);
     hdr->G2 = kPlanG2;
-    // the LDS table's fields: lds_image_kernel fills them when there is one
+    // the LDS table's fields: lds_finish_kernel fills them when there is one
     hdr->lds_G = hdr->lds_bins = hdr->lds_lists_cap = hdr->lds_nlists = 0;
     hdr->lds_image_bytes = hdr->lds_cells_off = hdr->lds_lists_off = hdr->lds_image_off = 0;
   }
-  if (lds_G) {
-    LdsScratch scr = lds_scratch(plan + scratch_offset, lds_G);
-    for (int i = blockIdx.x * kPlanThreads + threadIdx.x; i < kHashSlots; i += gridDim.x * kPlanThreads)
-      scr.table[i] = HashSlot{0ull, 0xffffffffu, 0u};
-    build_lds_supercell(sh, cb, K, edges, lds_G, blockIdx.x, scr);
-  } else {
-    build_supercell<kSuperFine>(sh, cb, K, lmax, kPlanR, kPlanG, blockIdx.x,
+  if constexpr (kLdsTable)
+    build_lds_supercell(sh, v, K, edges, lds_G, blockIdx.x, lds_scratch(plan + scratch_offset, lds_G));
+  else
+    build_supercell<kSuperFine>(sh, cb, v, K, lmax, kPlanR, kPlanG, blockIdx.x,
                                 reinterpret_cast<uint16_t*>(plan + kPlanHeaderBytes));
-  }
 }
 
-// The outer grid, one workgroup per 4 x 4-cell supercell.
-__global__ __launch_bounds__(kPlanThreads) void build_outer_kernel(const float* __restrict__ cb, int K, int lmax,
-                                                                   char* __restrict__ plan, size_t outer_offset) {
-  __shared__ PlanShared sh;
-  const int sidx = blockIdx.x;
-  if (!outer_supercell_unused(sidx))
-    build_supercell<kSuperOuter>(sh, cb, K, lmax, kPlanR2, kPlanG2, sidx,
-                                 reinterpret_cast<uint16_t*>(plan + outer_offset));
-  else if (threadIdx.x < kSuperOuter * kSuperOuter) {   // one overflow record per cell
-    constexpr int nsuper = kPlanG2 / kSuperOuter;
-    const int ix = (sidx / nsuper) * kSuperOuter + threadIdx.x / kSuperOuter;
-    const int iy = (sidx % nsuper) * kSuperOuter + threadIdx.x % kSuperOuter;
-    uint4* out = reinterpret_cast<uint4*>(plan + outer_offset + ((size_t)ix * kPlanG2 + iy) * lmax * sizeof(uint16_t));
-    out[0] = make_uint4(1u << 16, 0u, 0u, 0u);
-    if (lmax == 16) out[1] = make_uint4(0u, 0u, 0u, 0u);
-  }
-}
-
-// ---- list dedup.  A list of 2..4 candidates (4 x u16, tail repeated) is a
-// 64-bit key; equal lists share one record.  The record belongs to the lowest
-// cell holding the list, and records are numbered by a prefix sum over the
-// cells in order, so the image does not depend on the order of the atomics.
-__device__ __forceinline__ uint32_t cell_count(uint4 w) { return (w.x & 15u) + 1u; }
-__device__ __forceinline__ bool cell_over(uint4 w) { return (w.x >> 16) & 1u; }
-__device__ __forceinline__ unsigned long long list_key(uint4 w) {
-  return (unsigned long long)(w.x & 0xfff0fff0u) | ((unsigned long long)w.y << 32);
-}
-
-__global__ __launch_bounds__(256) void lds_insert_kernel(char* __restrict__ plan, size_t scratch_offset, int G) {
-  const int cell = blockIdx.x * 256 + threadIdx.x;
-  if (cell >= G * G) return;
-  LdsScratch scr = lds_scratch(plan + scratch_offset, G);
-  const uint4 w = scr.cellset[cell];
-  const uint32_t n = cell_count(w);
-  int slot = -1;
-  if (!cell_over(w) && n >= 2 && n <= 4) {
-    const unsigned long long key = list_key(w);
-    unsigned long long h = key * 0x9E3779B97F4A7C15ull;
-    h ^= h >> 29;
-    uint32_t at = (uint32_t)(h >> 17) & (kHashSlots - 1);
-    for (int probe = 0; probe < kHashSlots; ++probe) {      // bounded: every slot at most once
-      const unsigned long long prev = atomicCAS(&scr.table[at].key, 0ull, key);
-      if (prev == 0ull || prev == key) {
-        atomicMin(&scr.table[at].owner, (unsigned int)cell);
-        slot = (int)at;
-        break;
-      }
-      at = (at + 1) & (kHashSlots - 1);
-    }
-  }
-  scr.slot[cell] = slot;
-}
-
-// Block-wide inclusive scan of one int per thread (kScanBlock threads).
-__device__ __forceinline__ int block_scan(int v, int* sh) {
-  sh[threadIdx.x] = v;
-  __syncthreads();
-  for (int off = 1; off < kScanBlock; off <<= 1) {
-    const int t = threadIdx.x >= off ? sh[threadIdx.x - off] : 0;
-    __syncthreads();
-    sh[threadIdx.x] += t;
-    __syncthreads();
-  }
-  return sh[threadIdx.x];
-}
-
-// Records a cell needs: one for a 2..4 list it owns (it is the lowest cell
-// holding that list), two for a 5..8 list, none otherwise; and each block's
-// total.
-__global__ __launch_bounds__(kScanBlock) void lds_need_kernel(char* __restrict__ plan, size_t scratch_offset, int G) {
-  __shared__ int sh[kScanBlock];
-  const int cell = blockIdx.x * kScanBlock + threadIdx.x;
-  LdsScratch scr = lds_scratch(plan + scratch_offset, G);
-  int need = 0;
-  if (cell < G * G) {
-    const uint4 w = scr.cellset[cell];
-    if (!cell_over(w)) {
-      const uint32_t n = cell_count(w);
-      const int sl = scr.slot[cell];
-      if (n >= 5) need = 2;
-      else if (n >= 2 && sl >= 0 && scr.table[sl].owner == (unsigned int)cell) need = 1;
-    }
-    scr.recid[cell] = need;
-  }
-  const int incl = block_scan(need, sh);
-  if (threadIdx.x == kScanBlock - 1) scr.blocksum[blockIdx.x] = incl;
-}
-
-// Record ids: an exclusive prefix sum of the needs over the cells in order
-// (block offsets from the block totals, then a scan inside the block),
-// published to the dedup table for the owned 2..4 lists.
-__global__ __launch_bounds__(kScanBlock) void lds_ids_kernel(char* __restrict__ plan, size_t scratch_offset, int G) {
-  __shared__ int sh[kScanBlock];
-  LdsScratch scr = lds_scratch(plan + scratch_offset, G);
-  const int nblk = (G * G + kScanBlock - 1) / kScanBlock;
-  // this block's offset: the sum of the earlier blocks' totals
-  const int before = (int)threadIdx.x < (int)blockIdx.x ? scr.blocksum[threadIdx.x] : 0;
-  block_scan(before, sh);
-  const int block_off = sh[kScanBlock - 1];              // the scan's last entry: the whole sum
-  __syncthreads();
-  const int cell = blockIdx.x * kScanBlock + threadIdx.x;
-  const int need = cell < G * G ? scr.recid[cell] : 0;
-  const int incl = block_scan(need, sh);
-  if (cell < G * G) {
-    const int id = block_off + incl - need;
-    scr.recid[cell] = need ? id : -1;
-    if (need == 1) scr.table[scr.slot[cell]].id = (unsigned int)id;
-  }
-  if ((int)blockIdx.x == nblk - 1 && threadIdx.x == kScanBlock - 1) *scr.total = block_off + incl;
-}
-
-// The image: bin -> cell map, one entry per cell, the list records; the
-// header's table fields.  Records past the capacity are not written: their
-// cells scan the whole codebook.
-__global__ __launch_bounds__(256) void lds_image_kernel(char* __restrict__ plan, size_t scratch_offset,
-                                                        size_t image_offset, int G, int cells_off, int lists_off,
-                                                        int lists_cap, int image_bytes, LdsEdges E) {
+// ---- the table image, one workgroup per supercell (at least eight): its record ids start
+// after the records of the supercells before it (in index order), so the
+// image is a pure function of the cells' sets.  Records past the capacity
+// are not written; their cells scan the whole codebook.  The first eight
+// workgroups also write the bin -> cell map, workgroup 0 the cell padding and
+// the header's table fields; every workgroup clears a stripe of the unused
+// records.
+constexpr int kFinishThreads = 256;
+__global__ __launch_bounds__(kFinishThreads) void lds_finish_kernel(char* __restrict__ plan, size_t scratch_offset,
+                                                                    size_t image_offset, int G, int cells_off,
+                                                                    int lists_off, int lists_cap, int image_bytes,
+                                                                    LdsEdges E) {
+  __shared__ int red[2][kFinishThreads / kWave];
+  __shared__ uint16_t edges[kLdsMaxG + 1];
+  static_assert(kLdsBins % kFinishThreads == 0, "whole workgroups of bins");
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t >> 6;
+  const int sidx = blockIdx.x, nsy = lds_nsuper_y(G), ns2 = lds_nsupercells(G);
   LdsScratch scr = lds_scratch(plan + scratch_offset, G);
   char* img = plan + image_offset;
   uint16_t* cells = reinterpret_cast<uint16_t*>(img + cells_off);
   uint2* lists = reinterpret_cast<uint2*>(img + lists_off);
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  const int used = min(*scr.total, lists_cap);
+  // this supercell's cell entries and records (workgroups past the last
+  // supercell have none), loaded before the wait for the counts
+  const bool real = sidx < ns2;
+  const int mine = real ? scr.nrec[sidx] : 0;
+  const int ix = (sidx / nsy) * kLdsSuperX + t / kLdsSuperY, iy = (sidx % nsy) * kLdsSuperY + t % kLdsSuperY;
+  const bool has_cell = real && t < kLdsSuperCells && ix < G && iy < G;
+  const uint32_t d = has_cell ? scr.desc[(size_t)ix * G + iy] : 0u;
+  static_assert(kRecsPerSuper <= kFinishThreads, "one record per thread");
+  const uint2 rec = t < mine ? scr.recs[(size_t)sidx * kRecsPerSuper + t] : make_uint2(0u, 0u);
+  // records before this supercell, and in all
+  int before = 0, total = 0;
+  for (int i = t; i < ns2; i += kFinishThreads) {
+    const int v = scr.nrec[i];
+    before += i < sidx ? v : 0;
+    total += v;
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    before += __shfl_xor(before, off);
+    total += __shfl_xor(total, off);
+  }
+  if (lane == 0) { red[0][wave] = before; red[1][wave] = total; }
+  __syncthreads();
+  before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kFinishThreads / kWave; ++w) { before += red[0][w]; total += red[1][w]; }
+  const int used = min(total, lists_cap);
+  if (t < mine && before + t < used) lists[before + t] = rec;
+  if (has_cell) {
+    uint16_t entry = (uint16_t)d;
+    if (d >> 16) {
+      const int id = before + (int)(d & 0xffffu);
+      entry = (id + ((d >> 17) & 1) < used) ? (uint16_t)(0x8000u | (unsigned)id) : kLdsScanAll;
+    }
+    cells[(size_t)ix * G + iy] = entry;
+  }
+  for (int i = used + sidx * kFinishThreads + t; i < lists_cap; i += (int)gridDim.x * kFinishThreads)
+    lists[i] = make_uint2(0u, 0u);
+  // the bin -> cell map, one bin per thread over the first workgroups: the c
+  // with e[c] <= bin < e[c + 1], by binary search over the edges (in LDS)
+  const int bin = sidx * kFinishThreads + t;
+  if (sidx < kLdsBins / kFinishThreads) {
+    for (int c = t; c <= G; c += kFinishThreads) edges[c] = E.e[c];
+    __syncthreads();
+    int lo = 0, hi = G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (edges[mid] <= bin) lo = mid; else hi = mid;
+    }
+    reinterpret_cast<uint8_t*>(img)[bin] = (uint8_t)lo;
+  }
+  if (sidx != 0) return;
+  const int pad_end = (lists_off - cells_off) / 2;
+  for (int i = G * G + t; i < pad_end; i += kFinishThreads) cells[i] = 0;
   if (t == 0) {
     PlanHeader* hdr = reinterpret_cast<PlanHeader*>(plan);
     hdr->lds_G = G;
@@ -806,46 +990,6 @@ __global__ __launch_bounds__(256) void lds_image_kernel(char* __restrict__ plan,
     hdr->lds_lists_off = lists_off;
     hdr->lds_image_off = (int)image_offset;
   }
-  if (t < kLdsBins) {                                  // the bin -> cell map: the c with e[c] <= t < e[c + 1]
-    int lo = 0, hi = G;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (E.e[mid] <= t) lo = mid; else hi = mid;
-    }
-    reinterpret_cast<uint8_t*>(img)[t] = (uint8_t)lo;
-  }
-  // unused records and the cell padding are cleared, so the image is a pure
-  // function of the codebook
-  const int ncell = G * G;
-  const int pad_end = (lists_off - cells_off) / 2;
-  for (int i = ncell + t; i < pad_end; i += gridDim.x * 256) cells[i] = 0;
-  for (int i = used + t; i < lists_cap; i += gridDim.x * 256) lists[i] = make_uint2(0u, 0u);
-  if (t >= ncell) return;
-  const uint4 w = scr.cellset[t];
-  const uint32_t n = cell_count(w);
-  uint16_t entry = kLdsScanAll;
-  if (!cell_over(w)) {
-    if (n == 1) {
-      entry = (uint16_t)(w.x & 0xfff0u);
-    } else if (n <= 4) {
-      const int sl = scr.slot[t];
-      if (sl >= 0) {
-        const unsigned int id = scr.table[sl].id;
-        if ((int)id < used) {
-          entry = (uint16_t)(0x8000u | id);
-          if (scr.table[sl].owner == (unsigned int)t) lists[id] = make_uint2(w.x & 0xfff0fff0u, w.y);
-        }
-      }
-    } else {
-      const int id = scr.recid[t];
-      if (id >= 0 && id + 1 < used) {
-        entry = (uint16_t)(0x8000u | (unsigned)id);
-        lists[id] = make_uint2(w.x & 0xfff0fff0u, w.y | 0x80000000u);   // slot 3's top bit: continued
-        lists[id + 1] = make_uint2(w.z, w.w);
-      }
-    }
-  }
-  cells[t] = entry;
 }
 
 // ===========================================================================
@@ -917,29 +1061,23 @@ int launch_build_plan(const float* cb, int K, void* plan, hipStream_t st) {
   if (lds_geometry(K, &g)) {
     G = g.G;
     for (int i = 0; i <= G; ++i) E.e[i] = g.edges[i];
-    const int ns = (G + kLdsSuper - 1) / kLdsSuper;
-    ninner = ns * ns;
+    ninner = lds_nsupercells(G);
   }
   char* p = (char*)plan;
-  hipLaunchKernelGGL(build_plan_kernel, dim3(ninner), dim3(kPlanThreads), 0, st, cb, K, plan_lmax(K), p, G, E,
-                     plan_scratch_offset(K));
+  const dim3 grid(ninner + kOuterSupercells / kOuterPerWG);
+  if (G)
+    hipLaunchKernelGGL(build_plan_kernel<true>, grid, dim3(kPlanThreads), 0, st, cb, K, plan_lmax(K), p, G, E,
+                       plan_scratch_offset(K), ninner, plan_outer_offset(K));
+  else
+    hipLaunchKernelGGL(build_plan_kernel<false>, grid, dim3(kPlanThreads), 0, st, cb, K, plan_lmax(K), p, G, E,
+                       plan_scratch_offset(K), ninner, plan_outer_offset(K));
   int rc = check_launch("build_plan_kernel");
-  if (rc) return rc;
-  hipLaunchKernelGGL(build_outer_kernel, dim3(kOuterSupercells), dim3(kPlanThreads), 0, st, cb, K, plan_lmax(K), p,
-                     plan_outer_offset(K));
-  if ((rc = check_launch("build_outer_kernel")) || !G) return rc;
-  const size_t so = plan_scratch_offset(K);
-  const int nblk = (G * G + kScanBlock - 1) / kScanBlock;
-  hipLaunchKernelGGL(lds_insert_kernel, dim3((G * G + 255) / 256), dim3(256), 0, st, p, so, G);
-  if ((rc = check_launch("lds_insert_kernel"))) return rc;
-  hipLaunchKernelGGL(lds_need_kernel, dim3(nblk), dim3(kScanBlock), 0, st, p, so, G);
-  if ((rc = check_launch("lds_need_kernel"))) return rc;
-  hipLaunchKernelGGL(lds_ids_kernel, dim3(nblk), dim3(kScanBlock), 0, st, p, so, G);
-  if ((rc = check_launch("lds_ids_kernel"))) return rc;
-  const int nthreads = G * G > kLdsBins ? G * G : kLdsBins;
-  hipLaunchKernelGGL(lds_image_kernel, dim3((nthreads + 255) / 256), dim3(256), 0, st, p, so, plan_image_offset(K), G,
-                     (int)g.cells_off, (int)g.lists_off, g.lists_cap, (int)g.image_bytes, E);
-  return check_launch("lds_image_kernel");
+  if (rc || !G) return rc;
+  const int nfin = lds_nsupercells(G) > kLdsBins / kFinishThreads ? lds_nsupercells(G) : kLdsBins / kFinishThreads;
+  hipLaunchKernelGGL(lds_finish_kernel, dim3(nfin), dim3(kFinishThreads), 0, st, p,
+                     plan_scratch_offset(K),
+                     plan_image_offset(K), G, (int)g.cells_off, (int)g.lists_off, g.lists_cap, (int)g.image_bytes, E);
+  return check_launch("lds_finish_kernel");
 }
 
 }  // namespace qamw

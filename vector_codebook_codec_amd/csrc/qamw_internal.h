@@ -55,8 +55,8 @@ int dispatch_L(int L, A&&... args) {
 // larger K it is a uniform grid of per-cell records read from global memory.
 constexpr int kPlanG = 512;                  // global inner grid (K > kLdsMaxK): cells per axis
 constexpr float kPlanR = 5.0f;
-constexpr int kPlanG2 = 256;                 // outer grid: cells per axis over [-kPlanR2, kPlanR2)
-constexpr float kPlanR2 = 40.0f;
+constexpr int kPlanG2 = 128;                 // outer grid: cells per axis over [-kPlanR2, kPlanR2)
+constexpr float kPlanR2 = 20.0f;
 constexpr size_t kPlanHeaderBytes = 256;
 constexpr size_t kPlanHeaderKOffset = 16;    // int32 K inside the header (plan.hip)
 __host__ __device__ inline int plan_lmax(int K) { return K <= 2048 ? 8 : 16; }
