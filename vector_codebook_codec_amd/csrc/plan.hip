@@ -180,13 +180,14 @@ __device__ __forceinline__ void load_cb_regs(const float* __restrict__ cb, int K
 // The survivors of a supercell box SQ: every centroid with
 // min_{z in SQ} |z - c|^2 <= U(SQ) + 2 delta, ascending, with coordinates, in
 // sh.surv / sh.survc, padded with far-away dummies to whole rounds of `round`
-// entries.  Returns their count (more than kSuperMax: `all` is set and the
+// entries.  Returns their count (more than sh holds: `all` is set and the
 // callers test every centroid from global memory); *cmax2 is the largest
 // squared centroid radius and *delta the grid's score margin
 // 1e-5 (Cmax + R sqrt 2)^2 (R: the grid's half-width).
 template <typename SH>
 __device__ int supercell_survivors(SH& sh, const CbRegs& v, int K, const Box& sq64, double R,
                                    int round, float* cmax2_out, double* delta_out, bool* all_out, int* ns_out) {
+  constexpr int kCap = sizeof(sh.surv) / sizeof(sh.surv[0]);   // survivors the LDS holds
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   // ---- U(SQ) and the largest squared centroid radius, from the registers,
   // in fp32 on the outward-widened supercell box: U is raised by 1e-6 and the
@@ -254,13 +255,13 @@ __device__ int supercell_survivors(SH& sh, const CbRegs& v, int K, const Box& sq
 #pragma unroll
     for (int u = 0; u < kPerThread; ++u)
       if ((mask >> u) & 1u) {
-        if (before < kSuperMax) { sh.surv[before] = (uint16_t)(c0 + u); sh.survc[before] = v[r][u]; }
+        if (before < kCap) { sh.surv[before] = (uint16_t)(c0 + u); sh.survc[before] = v[r][u]; }
         ++before;
       }
     nsurv = total;
   }
   __syncthreads();
-  const bool all = nsurv > kSuperMax;       // too many survivors: test every centroid (from global memory)
+  const bool all = nsurv > kCap;            // too many survivors: test every centroid (from global memory)
   // pad the survivor list to whole rounds with a far-away dummy that neither
   // lowers any U nor passes any test
   const int ns = all ? K : (nsurv + round - 1) / round * round;
@@ -735,12 +736,14 @@ __device__ __forceinline__ bool outer_supercell_unused(int sidx) {
 // four lanes per cell, with no barrier.  The lists are the ones the
 // supercell test on the whole codebook gives.
 constexpr int kOuterPerWG = kPlanThreads / kWave;   // supercells per workgroup, 2 x 2
-constexpr int kOuterSurvMax = 128;                  // a supercell's survivors kept; more: its cells use the block's
+// a supercell's survivors kept (more: its cells use the block's list); the
+// block's: up to K (more would mean the whole codebook from global memory)
 constexpr int kOuterLPC = kWave / (kSuperOuter * kSuperOuter);
 static_assert(kOuterPerWG == 4 && kOuterLPC == 4, "2 x 2 supercells per workgroup, four lanes per outer cell");
+template <int kBlockCap, int kOuterSurvMax>
 struct OuterShared {
-  uint16_t surv[kSuperMax];                       // the block's survivors (supercell_survivors)
-  float2 survc[kSuperMax];
+  uint16_t surv[kBlockCap];                       // the block's survivors (supercell_survivors)
+  float2 survc[kBlockCap];
   float red[kPlanWaves];
   float red2[kPlanWaves];
   int wsum[kPlanWaves];
@@ -749,8 +752,10 @@ struct OuterShared {
   uint16_t list[kOuterPerWG][kSuperOuter * kSuperOuter][16];
 };
 
-__device__ void build_outer_block(OuterShared& os, const float* __restrict__ cb, const CbRegs& v, int K, int lmax,
+template <typename OS>
+__device__ void build_outer_block(OS& os, const float* __restrict__ cb, const CbRegs& v, int K, int lmax,
                                   uint16_t* __restrict__ lists, int blk) {
+  constexpr int kOuterSurvMax = sizeof(os.wsurv[0]) / sizeof(os.wsurv[0][0]);
   constexpr int nsuper = kPlanG2 / kSuperOuter, nblk = nsuper / 2;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
   const int bx = blk / nblk, by = blk % nblk;
@@ -872,7 +877,7 @@ __global__ __launch_bounds__(kPlanThreads) void build_plan_kernel(const float* _
                                                                   size_t outer_offset) {
   __shared__ union {
     PlanSharedT<kLdsTable> inner;
-    OuterShared outer;
+    OuterShared<kLdsTable ? kLdsMaxK : 4096, kLdsTable ? 128 : 256> outer;
   } lds;
   CbRegs v;
   load_cb_regs(cb, K, v);
