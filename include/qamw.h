@@ -229,6 +229,19 @@ int32_t qamw_encode_indices(const void* W, int32_t wdtype, int64_t N, int64_t d,
  *   workspace  >= qamw_calibrate_encode_workspace_bytes(N, d), 256-byte aligned
  */
 size_t qamw_calibrate_encode_workspace_bytes(int64_t N, int64_t d);
+/*
+ * qamw_calibrate_prepare: the calibration half of qamw_calibrate_encode.
+ * Writes s_out, sigma_out and rownorm_f16 and leaves in the workspace (the
+ * same size and alignment as above) what qamw_encode_prepare would: a
+ * following qamw_encode_indices with this workspace gives qamw_calibrate_encode's
+ * packed words, bit for bit.  It does not read a codebook or a plan, so a
+ * caller may build the plan on another stream meanwhile and join before
+ * qamw_encode_indices.  Errors as for qamw_calibrate_encode.
+ */
+int32_t qamw_calibrate_prepare(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
+                               const float* chan_rms, float alpha, int32_t block, uint64_t sign_seed,
+                               float* s_out, float* sigma_out, uint16_t* rownorm_f16,
+                               void* workspace, size_t workspace_bytes, void* stream);
 int32_t qamw_calibrate_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
                               const float* chan_rms, float alpha, int32_t block, uint64_t sign_seed,
                               const float* codebook, int32_t K, const void* plan, size_t plan_size,

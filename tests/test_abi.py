@@ -236,6 +236,25 @@ def test_calibrate_encode_rejects(lib, kw, status):
     assert lib.qamw_last_error()
 
 
+def _cal_prep(lib, **kw):
+    args = dict(W=A, wdt=1, N=8, d=256, ldw=256, r=A, alpha=0.5, block=128, seed=0, s=A, sigma=A, rn=A, ws=WS,
+                ws_bytes=1 << 20, stream=None)
+    args.update(kw)
+    return lib.qamw_calibrate_prepare(args["W"], args["wdt"], args["N"], args["d"], args["ldw"], args["r"],
+                                      args["alpha"], args["block"], args["seed"], args["s"], args["sigma"],
+                                      args["rn"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block=1), -2), (dict(block=3), -2), (dict(block=8, d=264, ldw=264), -2), (dict(r=None), -1), (dict(s=MIS), -1),
+    (dict(sigma=None), -1), (dict(rn=None), -1), (dict(alpha=float("inf")), -1), (dict(ws=None), -4),
+    (dict(ws_bytes=1000), -4), (dict(ws=WS + 16), -4), (dict(wdt=7), -2), (dict(ldw=100), -1),
+])
+def test_calibrate_prepare_rejects(lib, kw, status):
+    assert _cal_prep(lib, **kw) == status
+    assert lib.qamw_last_error()
+
+
 def test_calibrate_encode_workspace(lib):
     # the encode workspace followed by the calibration's partial sums
     assert lib.qamw_calibrate_encode_workspace_bytes(4096, 11008) == \

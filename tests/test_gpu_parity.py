@@ -720,3 +720,22 @@ def test_calibrate_encode_matches_separate_calls(q, name):
         torch.cuda.synchronize()
         assert torch.equal(s2, s) and torch.equal(sig2, sigma)
         assert torch.equal(packed2, packed) and torch.equal(rn2, rn)
+    # the calibration half, then qamw_encode_indices on its workspace (the
+    # plan built on another stream meanwhile, joined before the encode)
+    side = torch.cuda.Stream()
+    plan2 = torch.empty_like(plan)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        q.qamw_build_plan(Ct, plan2)
+    s3, sig3, rn3, ws = q.qamw_calibrate_prepare(W, r, wl.alpha, wl.block, wl.sign_seed)
+    torch.cuda.current_stream().wait_stream(side)
+    packed3 = q.qamw_encode_indices(W, wl.block, Ct, ws, plan=plan2)
+    torch.cuda.synchronize()
+    assert torch.equal(s3, s) and torch.equal(sig3, sigma) and torch.equal(rn3, rn)
+    assert torch.equal(packed3, packed)
+    # the same plan: header fields, outer grid and table image (the build's
+    # scratch after the image, and the header block's unused tail, are not
+    # part of it)
+    hdr = plan[:64].cpu().numpy().view(np.int32)
+    end = int(hdr[15]) + int(hdr[12])
+    assert torch.equal(plan2[:64], plan[:64]) and torch.equal(plan2[256:end], plan[256:end])

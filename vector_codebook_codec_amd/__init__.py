@@ -11,6 +11,7 @@ from .codec import (  # noqa: F401
     qamw_build_plan,
     qamw_calibrate,
     qamw_calibrate_encode,
+    qamw_calibrate_prepare,
     qamw_calibrate_encode_workspace_bytes,
     qamw_calibrate_workspace_bytes,
     qamw_channel_rms,

@@ -230,6 +230,35 @@ def qamw_calibrate_encode_workspace_bytes(N: int, d: int) -> int:
     return int(_lib.load().qamw_calibrate_encode_workspace_bytes(N, d))
 
 
+def qamw_calibrate_prepare(W: torch.Tensor, chan_rms: torch.Tensor, alpha: float, block: int, sign_seed: int,
+                           s_out: Optional[torch.Tensor] = None, sigma_out: Optional[torch.Tensor] = None,
+                           rownorm_f16: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           stream=None):
+    """The calibration half of qamw_calibrate_encode: returns (s, sigma, rownorm_f16, workspace), the
+    workspace ready for qamw_encode_indices (same packed words as qamw_calibrate_encode)."""
+    N, d, ldw = _rows(W, "W")
+    if W.dtype not in _WDT:
+        raise ValueError("W must be float32 or bfloat16")
+    _vec(chan_rms, "chan_rms", d)
+    if s_out is None:
+        s_out = torch.empty(d, dtype=torch.float32, device=W.device)
+    if sigma_out is None:
+        sigma_out = torch.empty(d // 2, dtype=torch.float32, device=W.device)
+    if rownorm_f16 is None:
+        rownorm_f16 = torch.empty(N, dtype=torch.int16, device=W.device)
+    _vec(s_out, "s_out", d)
+    _vec(sigma_out, "sigma_out", d // 2)
+    _vec(rownorm_f16, "rownorm_f16", N, torch.int16)
+    if workspace is None:
+        workspace = _workspace(qamw_calibrate_encode_workspace_bytes(N, d), W.device)
+    _dev(workspace, "workspace")
+    _lib.check("qamw_calibrate_prepare", _lib.load().qamw_calibrate_prepare(
+        W.data_ptr(), _WDT[W.dtype], N, d, ldw, chan_rms.data_ptr(), float(alpha), int(block), int(sign_seed),
+        s_out.data_ptr(), sigma_out.data_ptr(), rownorm_f16.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return s_out, sigma_out, rownorm_f16, workspace
+
+
 def qamw_calibrate_encode(W: torch.Tensor, chan_rms: torch.Tensor, alpha: float, block: int, sign_seed: int,
                           codebook: torch.Tensor, plan: Optional[torch.Tensor] = None,
                           s_out: Optional[torch.Tensor] = None, sigma_out: Optional[torch.Tensor] = None,

@@ -320,6 +320,34 @@ size_t qamw_calibrate_encode_workspace_bytes(int64_t N, int64_t d) {
   return e + calib_tiles(N) * (size_t)(d / 2) * sizeof(float);
 }
 
+int32_t qamw_calibrate_prepare(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
+                               const float* chan_rms, float alpha, int32_t block, uint64_t sign_seed, float* s_out,
+                               float* sigma_out, uint16_t* rownorm_f16, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  int L = 0;
+  int rc = check_matrix(N, d, block, &L);
+  if (rc) return rc;
+  if ((rc = check_weights(W, wdtype, d, ldw))) return rc;
+  if (!chan_rms || !s_out || !sigma_out || !rownorm_f16)
+    return fail(QAMW_EINVAL, "chan_rms, s_out, sigma_out and rownorm_f16 must be non-NULL");
+  if (!aligned16(s_out) || !aligned16(sigma_out)) return fail(QAMW_EINVAL, "s_out and sigma_out must be 16-byte aligned");
+  if (!isfinite(alpha)) return fail(QAMW_EINVAL, "alpha must be finite");
+  const size_t need = qamw_calibrate_encode_workspace_bytes(N, d);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(QAMW_EWORKSPACE, "calibrate_prepare needs %zu bytes of 256-byte aligned workspace (got %zu)", need,
+                workspace_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  const EncodeWorkspace e = encode_workspace(workspace, N, d);
+  float* partial = (float*)((char*)workspace + qamw_encode_workspace_bytes(N, d));
+  const int n = (int)N, dd = (int)d;
+  // the calibration pass leaves exactly what qamw_encode_prepare would compute:
+  // column factors (scale_kernel), row norms with their fp16 bits
+  // (norm_amplitude_kernel) and 1 / sigma (sigma_kernel)
+  if ((rc = launch_scale(chan_rms, alpha, sign_seed, dd, s_out, e.f, st))) return rc;
+  if ((rc = launch_norm_amplitude(L, W, wdtype, n, dd, ldw, s_out, e.f, e.rho, rownorm_f16, partial, st))) return rc;
+  return launch_sigma(partial, (int)calib_tiles(N), dd / 2, n, sigma_out, e.isig, st);
+}
+
 int32_t qamw_calibrate_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
                               const float* chan_rms, float alpha, int32_t block, uint64_t sign_seed,
                               const float* codebook, int32_t K, const void* plan, size_t plan_size, float* s_out,
@@ -340,18 +368,12 @@ int32_t qamw_calibrate_encode(const void* W, int32_t wdtype, int64_t N, int64_t 
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
     return fail(QAMW_EWORKSPACE, "calibrate_encode needs %zu bytes of 256-byte aligned workspace (got %zu)", need,
                 workspace_bytes);
-  hipStream_t st = (hipStream_t)stream;
+  if ((rc = qamw_calibrate_prepare(W, wdtype, N, d, ldw, chan_rms, alpha, block, sign_seed, s_out, sigma_out,
+                                   rownorm_f16, workspace, workspace_bytes, stream)))
+    return rc;
   const EncodeWorkspace e = encode_workspace(workspace, N, d);
-  float* partial = (float*)((char*)workspace + qamw_encode_workspace_bytes(N, d));
-  const int n = (int)N, dd = (int)d;
-  // the calibration pass leaves exactly what qamw_encode_prepare would compute:
-  // column factors (scale_kernel), row norms with their fp16 bits (rownorm_kernel)
-  // and 1 / sigma (sigma_kernel)
-  if ((rc = launch_scale(chan_rms, alpha, sign_seed, dd, s_out, e.f, st))) return rc;
-  if ((rc = launch_norm_amplitude(L, W, wdtype, n, dd, ldw, s_out, e.f, e.rho, rownorm_f16, partial, st))) return rc;
-  if ((rc = launch_sigma(partial, (int)calib_tiles(N), dd / 2, n, sigma_out, e.isig, st))) return rc;
-  return launch_encode(L, W, wdtype, n, dd, ldw, e.f, e.isig, codebook, (int)K, qamw_index_bits(K),
-                       (int)qamw_packed_row_words(d, K), e.rho, plan, packed, st);
+  return launch_encode(L, W, wdtype, (int)N, (int)d, ldw, e.f, e.isig, codebook, (int)K, qamw_index_bits(K),
+                       (int)qamw_packed_row_words(d, K), e.rho, plan, packed, (hipStream_t)stream);
 }
 
 size_t qamw_lloyd_workspace_bytes(int32_t K) {
