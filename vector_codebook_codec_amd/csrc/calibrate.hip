@@ -113,18 +113,21 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
 // wavefront w = window w.  For each row every wavefront forms its window's
 // share of rho_n^2 (chunk_sumsq + window_sum, as row_norm_wave does) and the
 // pair amplitudes; the shares meet in LDS, every wavefront adds them in window
-// order (the same fp64 sum as row_norm_wave, so rho is identical), and the
-// amplitudes are scaled and accumulated exactly as amplitude_kernel does.  A
-// barrier per batch of rows; the share buffer alternates between batches.
+// order (the same fp64 sum as row_norm_wave, so rho is identical; one lane
+// per row of a batch), and the amplitudes are scaled and accumulated exactly
+// as amplitude_kernel does.  A barrier per batch of rows; the share buffer
+// alternates between batches.
 // ---------------------------------------------------------------------------
 constexpr int kFuseMaxWin = 16;   // 1024 threads
+constexpr int kFuseMidWin = 12;   // up to 768 threads: registers for more rows per barrier
 
-template <int L, typename Tin>
-__global__ __launch_bounds__(kFuseMaxWin * kWave) void norm_amplitude_kernel(
+template <int L, typename Tin, int kMaxWin>
+__global__ __launch_bounds__(kMaxWin * kWave) void norm_amplitude_kernel(
     const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ fcol,
     double* __restrict__ rho, uint16_t* __restrict__ rho_f16, float* __restrict__ partial) {
-  constexpr int kBatch = sizeof(Tin) == 2 ? 2 : 1;   // rows per barrier (and loads in flight)
-  __shared__ double share[2][kBatch][kFuseMaxWin];
+  // rows per barrier (and loads in flight)
+  constexpr int kBatch = sizeof(Tin) == 2 ? (kMaxWin <= kFuseMidWin ? 4 : 2) : (kMaxWin <= kFuseMidWin ? 2 : 1);
+  __shared__ double share[2][kBatch][kMaxWin];
   const int lane = threadIdx.x & (kWave - 1);
   const int win = threadIdx.x >> 6;
   const int nwin = blockDim.x >> 6;
@@ -186,20 +189,22 @@ __global__ __launch_bounds__(kFuseMaxWin * kWave) void norm_amplitude_kernel(
       }
     }
     __syncthreads();
+    // lane u sums row nb + u over the windows, in window order
+    double t = 0.0;
+    if (lane < kBatch)
+      for (int w = 0; w < nwin; ++w) t += share[buf][lane][w];
+    const double rn = sqrt(t);
+    const float inv_l = rn > 0.0 ? (float)(1.0 / (sqrt_b * rn)) : 0.0f;
+    if (win == 0 && lane < kBatch && nb + lane < n1) {
+      rho[nb + lane] = rn;
+      if (rho_f16) rho_f16[nb + lane] = f64_to_f16_bits(rn);
+    }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int n = nb + u;
-      if (n >= n1) break;
-      double t = 0.0;
-      for (int w = 0; w < nwin; ++w) t += share[buf][u][w];
-      const double r = sqrt(t);
-      const float inv = r > 0.0 ? (float)(1.0 / (sqrt_b * r)) : 0.0f;
+      if (nb + u >= n1) break;
+      const float inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv_l), u));
 #pragma unroll
       for (int p = 0; p < 8; ++p) acc[p] += amp[u][p] * inv;
-      if (threadIdx.x == 0) {
-        rho[n] = r;
-        if (rho_f16) rho_f16[n] = f64_to_f16_bits(r);
-      }
     }
     // the next batch writes the other buffer; the one after it has passed
     // the next barrier, so every wavefront has read this one by then
@@ -292,22 +297,28 @@ int launch_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ld
 
 template <int L>
 struct LaunchNormAmplitude {
+  template <typename Tin, int kMaxWin>
+  static void go(dim3 grid, dim3 blk, const void* W, int64_t ldw, int N, int d, const float* f, double* rho,
+                 uint16_t* rho_f16, float* partial, hipStream_t st) {
+    hipLaunchKernelGGL((norm_amplitude_kernel<L, Tin, kMaxWin>), grid, blk, 0, st, (const Tin*)W, ldw, N, d, f, rho,
+                       rho_f16, partial);
+  }
   static int run(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, double* rho,
                  uint16_t* rho_f16, float* partial, hipStream_t st) {
     const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
     const dim3 grid((unsigned)calib_tiles(N)), blk((unsigned)(nwin * kWave));
-    if (wdt == QAMW_F32)
-      hipLaunchKernelGGL((norm_amplitude_kernel<L, float>), grid, blk, 0, st, (const float*)W, ldw, N, d, f, rho,
-                         rho_f16, partial);
-    else
-      hipLaunchKernelGGL((norm_amplitude_kernel<L, uint16_t>), grid, blk, 0, st, (const uint16_t*)W, ldw, N, d, f,
-                         rho, rho_f16, partial);
+    const bool mid = nwin <= kFuseMidWin;
+    if (wdt == QAMW_F32) {
+      if (mid) go<float, kFuseMidWin>(grid, blk, W, ldw, N, d, f, rho, rho_f16, partial, st);
+      else go<float, kFuseMaxWin>(grid, blk, W, ldw, N, d, f, rho, rho_f16, partial, st);
+    } else {
+      if (mid) go<uint16_t, kFuseMidWin>(grid, blk, W, ldw, N, d, f, rho, rho_f16, partial, st);
+      else go<uint16_t, kFuseMaxWin>(grid, blk, W, ldw, N, d, f, rho, rho_f16, partial, st);
+    }
     return check_launch("norm_amplitude_kernel");
   }
 };
 
-// Row norms and amplitude partials: one fused pass when a row has at most
-// kFuseMaxWin windows, else the two passes (the results are the same).
 int launch_norm_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s,
                           const float* f, double* rho, uint16_t* rho_f16, float* partial, hipStream_t st) {
   const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
