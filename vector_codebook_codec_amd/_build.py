@@ -48,25 +48,49 @@ def _run(cmd, verbose):
         print("\n".join(msgs), flush=True)
 
 
-def build(verbose: bool = True, extra_flags=()) -> str:
-    """Compile every HIP source (in parallel) and link libqamw.so; always recompiles."""
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (the
+# device code is built as usual); for CPU-side checks of the C ABI's argument
+# validation, with the sanitizer runtime preloaded into the checking process.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZED_LIB_PATH = os.path.join(PKG, "libqamw_hostsan.so")
+
+
+def build(verbose: bool = True, extra_flags=(), sanitize: bool = False) -> str:
+    """Compile every HIP source (in parallel) and link libqamw.so; always recompiles.
+    With sanitize, the host code is instrumented (ASan + UBSan) and the library
+    goes to libqamw_hostsan.so instead."""
     from concurrent.futures import ThreadPoolExecutor
 
+    flags = [*FLAGS, *extra_flags, *(SANITIZE_FLAGS if sanitize else [])]
+    out = SANITIZED_LIB_PATH if sanitize else LIB_PATH
     tmpdir = tempfile.mkdtemp(prefix="qamw_build_", dir=PKG)
     try:
         objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
-        cmds = [[hipcc(), *FLAGS, *extra_flags, "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+        cmds = [[hipcc(), *flags, "-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
         workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
         with ThreadPoolExecutor(workers) as ex:
             list(ex.map(lambda c: _run(c, verbose), cmds))
         tmp_lib = os.path.join(tmpdir, "libqamw.so")
-        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs], verbose)
-        os.replace(tmp_lib, LIB_PATH)
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"]
+        if sanitize:
+            link += ["-fsanitize=address,undefined", "-shared-libsan"]
+        _run([*link, "-o", tmp_lib, *objs], verbose)
+        os.replace(tmp_lib, out)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
-    return LIB_PATH
+    return out
+
+
+def sanitizer_runtime() -> str:
+    """Path of the ASan runtime the sanitized library needs preloaded."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the ASan runtime of the HIP toolchain was not found")
+    return path
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--sanitize" in sys.argv[1:])
     sys.exit(0)

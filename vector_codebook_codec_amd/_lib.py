@@ -64,11 +64,14 @@ class QamwError(RuntimeError):
         self.status = status
 
 
-def load(path: str = LIB_PATH):
-    """Load libqamw.so once and attach the prototypes."""
+def load(path: str = ""):
+    """Load libqamw.so once and attach the prototypes.  The path defaults to
+    the in-tree build; the environment variable QAMW_LIBRARY can name another
+    build of the same sources (for instance the host-sanitized one)."""
     global _LIB
     if _LIB is not None:
         return _LIB
+    path = path or os.environ.get("QAMW_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it first (python -m vector_codebook_codec_amd._build "
                            "or __graft_entry__.build())")
