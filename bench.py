@@ -16,7 +16,8 @@ cold_step     the same replays after a 1 GiB read each (L2 and MALL cold)
 roofline      the dominant kernel (encode_lds_kernel, all of
               qamw_encode_indices with a plan): algorithmic HBM bytes (W read
               + packed write) / its mean launch time from HIP events on the
-              launch stream, against 8 TB/s; traffic from the committed
+              launch stream (10 launches in a HIP graph, mean per launch),
+              against 8 TB/s; traffic from the committed
               counter passes when they match the kernel sources
 valu_view     the exhaustive search (no plan) against the fp32 vector peak,
               and the planned search's speedup over it in those units
@@ -479,10 +480,39 @@ def main():
         q.qamw_encode_indices(W, b, Ct, ws_enc, plan, packed_c, stream)
         m[3].record(stream)
     torch.cuda.synchronize()
-    cal_ms, prep_ms, idx_ms = (seg(cmarks, i) for i in range(3))
+    cal_ms, prep_ms, idx_ms_eager = (seg(cmarks, i) for i in range(3))
     if not (torch.equal(packed_c, packed) and torch.equal(rn_c, rn) and torch.equal(s_c, s)
             and torch.equal(sigma_c, sigma)):
         raise RuntimeError("qamw_calibrate_encode and the separate entry points disagree")
+
+    # The roofline kernel's launch time: 10 back-to-back qamw_encode_indices
+    # launches captured in a HIP graph, replayed between HIP events on the
+    # replay stream (the per-launch event pairs above also count each
+    # launch's start latency); mean per launch over the replays.
+    roof_launches = 10
+    roof_graph = torch.cuda.CUDAGraph()
+    rs = torch.cuda.Stream()
+    rs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(rs):
+        q.qamw_encode_indices(W, b, Ct, ws_enc, plan, packed_c)
+    torch.cuda.current_stream().wait_stream(rs)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(roof_graph):
+        for _ in range(roof_launches):
+            q.qamw_encode_indices(W, b, Ct, ws_enc, plan, packed_c)
+    roof_graph.replay()
+    torch.cuda.synchronize()
+    roof = []
+    for _ in range(max(3, args.steps // 4)):
+        a_ev, z_ev = ev(), ev()
+        a_ev.record()
+        roof_graph.replay()
+        z_ev.record()
+        torch.cuda.synchronize()
+        roof.append(a_ev.elapsed_time(z_ev) / roof_launches)
+    idx_ms = float(np.mean(roof))
+    if not torch.equal(packed_c, packed):
+        raise RuntimeError("graph replays of qamw_encode_indices differ from the step's encode")
 
     # the exhaustive search (no plan) for comparison; same indices, bit for bit
     packed_x = torch.empty_like(packed)
@@ -570,8 +600,13 @@ def main():
                            N * d * 2 / (fill16_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
         del out16
 
-    # fused decoded-weight matmul Y = X W^^T for T tokens (not part of the step)
+    # fused decoded-weight matmul Y = X W^^T for T tokens (not part of the step).
+    # Cold: the graph cycles through 12 copies of the packed matrix (372 MB, more
+    # than the 256 MB Infinity Cache), so each call's weights come from HBM, as
+    # in a model whose layers stream through.
     mm = {}
+    n_copies = 12
+    pk_copies = [packed.clone() for _ in range(n_copies)] if args.matmul_tokens else []
     for T in args.matmul_tokens:
         X = torch.randn((T, d), device=dev, dtype=torch.float32).to(torch.bfloat16)
         Xr = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
@@ -615,40 +650,43 @@ def main():
             res_t[name] = float(np.median(times))
             if name == "fused" and not torch.equal(Y, Y_eager):
                 raise RuntimeError("graph replays of the fused matmul differ from the eager result")
-        if T == 1:                                  # the one-kernel path from raw activations
-            xv = X[0].contiguous()
-            yv = torch.empty(N, dtype=torch.float32, device=dev)
-            mv = lambda st: q.qamw_decode_matvec(xv, packed, rn, s, sigma, b, wl.sign_seed, Ct, out=yv, stream=st)
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                for _ in range(3):
-                    mv(None)
-            torch.cuda.current_stream().wait_stream(side)
-            gmv = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gmv):
-                for _ in range(inner):
-                    mv(None)
-            tms = []
-            for _ in range(max(1, args.matmul_reps)):
-                a, z = ev(), ev()
-                a.record()
-                gmv.replay()
-                z.record()
-                torch.cuda.synchronize()
-                tms.append(a.elapsed_time(z) / inner)
-            res_t["matvec"] = float(np.median(tms))
+        def cold_fused(st, pk):
+            q.qamw_rotate_activations(X, s, b, wl.sign_seed, Xr, st)
+            q.qamw_decode_matmul(Xr, pk, rn, sigma, Ct, out=Y, stream=st)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            cold_fused(None, pk_copies[0])
+        torch.cuda.current_stream().wait_stream(side)
+        gc = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gc):
+            for pk in pk_copies:
+                cold_fused(None, pk)
+        gc.replay()
+        torch.cuda.synchronize()
+        tc = []
+        for _ in range(max(1, args.matmul_reps)):
+            a, z = ev(), ev()
+            a.record()
+            gc.replay()
+            z.record()
+            torch.cuda.synchronize()
+            tc.append(a.elapsed_time(z) / n_copies)
+        res_t["fused_cold"] = float(np.median(tc))
+        if not torch.equal(Y, Y_eager):
+            raise RuntimeError("the fused matmul over a copy of the packed matrix differs")
         # algorithmic bytes of the fused path: packed + row norms + sigma + X read + Xr write/read + Y write
         mm_bytes = N * rw * 4 + N * 2 + d * 2 + T * d * 2 * 3 + T * N * 4
         mm[str(T)] = {"fused_us": res_t["fused"] * 1e3, "unfused_us": res_t["unfused"] * 1e3,
-                      "matvec_us": res_t["matvec"] * 1e3 if "matvec" in res_t else None,
+                      "fused_cold_us": res_t["fused_cold"] * 1e3,
+                      "frac_hbm_cold": mm_bytes / (res_t["fused_cold"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                       "algorithmic_bytes": mm_bytes,
                       "GB_s": mm_bytes / (res_t["fused"] * 1e-3) / 1e9,
                       "frac_hbm": mm_bytes / (res_t["fused"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
                       "tflops": 2.0 * T * N * d / (res_t["fused"] * 1e-3) / 1e12}
-        print(f"decode_matmul T={T}: fused {res_t['fused'] * 1e3:.1f} us, "
-              f"decode-to-bf16 + torch.matmul {res_t['unfused'] * 1e3:.1f} us"
-              + (f", one-kernel matvec {res_t['matvec'] * 1e3:.1f} us" if "matvec" in res_t else ""),
+        print(f"decode_matmul T={T}: fused {res_t['fused'] * 1e3:.1f} us (cold {res_t['fused_cold'] * 1e3:.1f}), "
+              f"decode-to-bf16 + torch.matmul {res_t['unfused'] * 1e3:.1f} us",
               file=sys.stderr, flush=True)
 
     # polar-code baseline encode at 8 bits per pair (not part of the step)
@@ -815,7 +853,8 @@ def main():
                          "decode": dec_ms, "encode_total": enc_ms,
                          "note": "eager launches; build_plan runs on a second stream beside calibrate_prepare; "
                                  "encode_total is the step's start to the end of its encode"},
-        "separate_entry_ms": {"calibrate": cal_ms, "encode_prepare": prep_ms, "encode_indices": idx_ms,
+        "separate_entry_ms": {"calibrate": cal_ms, "encode_prepare": prep_ms, "encode_indices": idx_ms_eager,
+                              "encode_indices_graph": idx_ms,
                               "note": "the step's calibrate_encode as separate calls (same results, bit for "
                                       "bit); encode_prepare repeats the row-norm pass"},
         "encode_gweights_s": weights / (enc_ms * 1e-3) / 1e9,

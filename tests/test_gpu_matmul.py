@@ -171,65 +171,3 @@ def test_decode_matmul_full_size_one_token(q):
     Y2 = q.qamw_decode_matmul(Xr, g["packed"], g["rn"], g["sigma"], g["C"])
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2)
-
-
-@pytest.mark.parametrize("N,d,b,K,xdtype,use_s,out_dtype", [
-    (37, 512, 128, 256, "f32", True, torch.float32),
-    (9, 48, 16, 4, "bf16", True, torch.float32),        # ragged window, B = 2
-    (8, 2048, 1024, 1024, "f32", False, torch.bfloat16),
-    (5, 36864, 256, 256, "bf16", True, torch.float32),  # 36 windows: several per wavefront
-])
-def test_decode_matvec(q, N, d, b, K, xdtype, use_s, out_dtype):
-    """One token from raw activations, rotation in the kernel (fp32), against the oracle."""
-    rng = np.random.default_rng(N + d)
-    W = (rng.standard_normal((N, d)) * 0.02).astype(np.float32)
-    r = rng.lognormal(0, 1.0, d).astype(np.float32)
-    C = q.load_codebook(K)
-    g = encode_gpu(q, W, r, 0.5, b, 13, C)
-    x = rng.standard_normal(d).astype(np.float32)
-    if xdtype == "bf16":
-        x = workloads.bf16_bits_to_f32(workloads.bf16_bits_from_f32(x))
-        xt = torch.from_numpy(workloads.bf16_bits_from_f32(x).view(np.int16)).to(DEV).view(torch.bfloat16)
-    else:
-        xt = torch.from_numpy(x).to(DEV)
-    say(f"case matvec N={N} d={d} b={b} K={K} x {xdtype} s={'yes' if use_s else 'None'} out {out_dtype}")
-    y = q.qamw_decode_matvec(xt, g["packed"], g["rn"], g["s"] if use_s else None, g["sigma"], b, 13, g["C"],
-                             out_dtype=out_dtype)
-    y2 = q.qamw_decode_matvec(xt, g["packed"], g["rn"], g["s"] if use_s else None, g["sigma"], b, 13, g["C"],
-                              out_dtype=out_dtype)
-    torch.cuda.synchronize()
-    assert torch.equal(y, y2)
-    packed = g["packed"].cpu().numpy().view(np.uint32)
-    rn = g["rn"].cpu().numpy().view(np.uint16)
-    s_np = g["s"].cpu().numpy() if use_s else None
-    sig = g["sigma"].cpu().numpy()
-    ref = O.decode_matmul(x[None, :], packed, rn, s_np, sig, b, 13, C, d)[0]
-    Xr_ex = O.rotate_activations(x[None, :], s_np, b, 13)
-    S = (np.abs(Xr_ex) @ np.abs(O.lookup_pairs(packed, sig, C, d)).T)[0] * O.f16_bits_to_f64(rn)
-    got = y.float().cpu().numpy().astype(np.float64)
-    err = np.abs(got - ref)
-    tol = 1e-5 * S
-    if out_dtype == torch.bfloat16:
-        tol = tol + 0.5 * bf16_ulp(ref) * (1 + 1e-5)
-    say(f"  max |err|/S = {float(np.max(err / np.maximum(S, 1e-300))):.3e}")
-    assert np.all(err <= tol + 1e-30)
-
-
-def test_decode_matvec_full_size(q):
-    wl = workloads.get("c3t_4096x11008")
-    C = q.load_codebook(wl.K)
-    g = encode_gpu(q, wl.W_f32(), wl.r, wl.alpha, wl.block, wl.sign_seed, C, wdtype="bf16")
-    x = np.random.default_rng(zlib.crc32(b"matvec")).standard_normal(wl.d).astype(np.float32)
-    say("case matvec c3t 4096x11008")
-    y = q.qamw_decode_matvec(torch.from_numpy(x).to(DEV), g["packed"], g["rn"], g["s"], g["sigma"], wl.block,
-                             wl.sign_seed, g["C"])
-    torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(3).choice(wl.N, 96, replace=False))
-    packed = g["packed"].cpu().numpy().view(np.uint32)[rows]
-    rn = g["rn"].cpu().numpy().view(np.uint16)[rows]
-    ref = O.decode_matmul(x[None, :], packed, rn, g["s"].cpu().numpy(), g["sigma"].cpu().numpy(), wl.block,
-                          wl.sign_seed, C, wl.d)[0]
-    got = y.cpu().numpy()[rows].astype(np.float64)
-    rel = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
-    say(f"  max |err| / max |y| = {rel:.2e}")
-    assert rel <= 1e-5

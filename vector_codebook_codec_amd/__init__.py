@@ -18,7 +18,6 @@ from .codec import (  # noqa: F401
     qamw_channel_rms_workspace_bytes,
     qamw_decode,
     qamw_decode_matmul,
-    qamw_decode_matvec,
     qamw_encode,
     qamw_encode_noalloc,
     qamw_encode_indices,

@@ -51,7 +51,6 @@ SIGNATURES = {
                                  _p]),
     "qamw_rotate_activations": (_i32, [_p, _i32, _i64, _i64, _i64, _p, _i32, _u64, _p, _i64, _p]),
     "qamw_decode_matmul": (_i32, [_p, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _i32, _p, _i32, _i64, _p]),
-    "qamw_decode_matvec": (_i32, [_p, _i32, _i64, _p, _i32, _u64, _p, _p, _i64, _p, _p, _i32, _p, _i32, _p]),
     "qamw_decode": (_i32, [_p, _p, _i64, _i64, _p, _p, _i32, _u64, _p, _i32, _p, _i32, _i64, _p]),
 }
 

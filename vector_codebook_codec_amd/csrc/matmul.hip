@@ -454,135 +454,6 @@ __global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_gemv_kernel(
   }
 }
 
-// ---------------------------------------------------------------------------
-// One token from the raw activations: y = x W^^T with the rotation done in
-// the same kernel.  A GEMV slice of 512 pairs is exactly one 1024-column
-// rotation window, so wavefront w rotates window w (x_j eps_j / (sqrt(b)
-// s_j), the block FWHT) in registers; afterwards lane l holds the 8 pairs of
-// window chunk BlockOut(l) and decodes exactly those pairs -- the same
-// products as qamw_rotate_activations + qamw_decode_matmul, with the rotated
-// activations kept in fp32 instead of rounded to bf16.  The packed loads go
-// out first, so the codebook staging and the rotation of x (x, s and sigma
-// are small and cache-resident) overlap their latency.  Otherwise as
-// decode_gemv_kernel (index width at run time: this kernel waits on memory,
-// not on arithmetic).
-// ---------------------------------------------------------------------------
-template <int L, int R, typename Tin, typename Out>
-__global__ __launch_bounds__(kGvMaxWaves * kWave) void decode_matvec_kernel(
-    const Tin* __restrict__ X, int d, const float* __restrict__ s, uint64_t seed,
-    const uint32_t* __restrict__ packed, int row_words, const uint16_t* __restrict__ rho_f16, int N,
-    const float* __restrict__ sigma, const float* __restrict__ codebook, int K, int B,
-    typename Out::T* __restrict__ Y) {
-  extern __shared__ float4 lds4[];
-  float2* cb = reinterpret_cast<float2*>(lds4);
-  u32x4* pk_all = reinterpret_cast<u32x4*>(cb + ((K + 1) & ~1));    // [waves][64] 16-byte slots
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nw = blockDim.x >> 6;
-  float* part = reinterpret_cast<float*>(pk_all + nw * kWave);       // [waves][R]
-  const int nchunks = d >> 4;
-  const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
-  const int n0 = blockIdx.x * R;
-  const float inv_sqrt_b = (float)(1.0 / sqrt((double)(1 << L)));
-  const int lane_u4 = min(lane, 4 * B - 1);
-  const int last_u4 = row_words / 4 - 1;
-
-  // the window's packed pieces of the 8 rows (as in the GEMV), issued before
-  // the codebook is staged
-  u32x4 rw[R];
-  auto load_packed = [&](int win) {
-    const int u4 = min(win * 4 * B + lane_u4, last_u4);
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      rw[r] = reinterpret_cast<const u32x4*>(packed + (int64_t)min(n0 + r, N - 1) * row_words)[u4];
-  };
-  load_packed(wave);                     // wave < nw <= nwin
-  {
-    const float4* cb4 = reinterpret_cast<const float4*>(codebook);
-    float4* cbl = reinterpret_cast<float4*>(cb);
-    for (int c = threadIdx.x; c < (K >> 1); c += blockDim.x) cbl[c] = cb4[c];
-    if ((K & 1) && threadIdx.x == 0) cb[K - 1] = make_float2(codebook[2 * (K - 1)], codebook[2 * (K - 1) + 1]);
-  }
-  __syncthreads();
-
-  u32x4* pk = pk_all + wave * kWave;
-  const int co_local = BlockOut<L>::chunk(lane);   // the chunk this lane holds after the rotation
-  const float osign = BlockOut<L>::sign(lane);
-  const uint32_t lbit = (uint32_t)(co_local * kPairsPerLane * B);   // its first bit within the window
-  const uint32_t sh = lbit & 31u;
-  const uint32_t* pkw = reinterpret_cast<const uint32_t*>(pk) + min((int)(lbit >> 5), 4 * kWave - 4);
-  float rowacc[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) rowacc[r] = 0.0f;
-
-  for (int win = wave; win < nwin; win += nw) {
-    if (win != wave) load_packed(win);   // rows longer than 16 windows: later windows in turn
-    const int c = win * kWinChunks + lane;
-    const bool active = c < nchunks;               // whole Hadamard blocks are active or not
-    const int cl = active ? c : nchunks - 1;
-    const int pc = (win * kWinChunks + co_local) * kPairsPerLane;
-    const int pcl = active ? pc : 0;
-    float x[16];
-    {
-      RawChunk<Tin> raw;
-      raw.load(X + cl * kChunk);
-      float sv[16];
-      if (s) {
-        load_chunk(s + cl * kChunk, sv);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sv[i] = 1.0f;
-      }
-      const float4 s0 = *reinterpret_cast<const float4*>(sigma + pcl);
-      const float4 s1 = *reinterpret_cast<const float4*>(sigma + pcl + 4);
-      raw.unpack(x);
-      float eps[16];
-      sign_eps16(seed, (uint32_t)(cl * kChunk), eps);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float g = eps[i] * col_scale(inv_sqrt_b, sv[i]);
-        x[i] = active ? x[i] * g : 0.0f;
-      }
-      fwht_block<L>(x, lane);
-      const float sg[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        x[2 * p] = active ? sg[p] * (x[2 * p] * osign) : 0.0f;
-        x[2 * p + 1] = active ? sg[p] * (x[2 * p + 1] * osign) : 0.0f;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      wave_lds_fence();
-      pk[lane] = rw[r];
-      wave_lds_fence();
-      const uint32_t w[4] = {pkw[0], pkw[1], pkw[2], pkw[3]};
-      uint32_t idx[8];
-      unpack8<0>(w, sh, B, idx);
-      float acc = 0.0f;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const float2 cc = cb[min((int)idx[p], K - 1)];
-        acc = __builtin_fmaf(x[2 * p], cc.x, acc);
-        acc = __builtin_fmaf(x[2 * p + 1], cc.y, acc);
-      }
-      rowacc[r] += acc;
-    }
-  }
-  int myrow;
-  const float v1 = reduce_rows<R>(rowacc, lane, myrow);
-  if ((lane & (kWave / R - 1)) == 0) part[wave * R + myrow] = v1;
-  __syncthreads();
-  if ((int)threadIdx.x < R) {
-    const int n = n0 + threadIdx.x;
-    if (n < N) {
-      float sum = 0.0f;
-      for (int ww = 0; ww < nw; ++ww) sum += part[ww * R + threadIdx.x];
-      Out::put(Y + n, sum * f16_bits_to_f32(rho_f16[n]));
-    }
-  }
-}
-
 // ===========================================================================
 // launchers
 // ===========================================================================
@@ -654,41 +525,6 @@ static int launch_mm_tt(const uint16_t* Xr, int T, int d, int64_t ldr, const uin
   if (T <= 16) return launch_mm<BT, 1>(Xr, T, d, ldr, packed, row_words, rn, N, sigma, cb, K, B, Y, ydt, ldy, st);
   if (T <= 32) return launch_mm<BT, 2>(Xr, T, d, ldr, packed, row_words, rn, N, sigma, cb, K, B, Y, ydt, ldy, st);
   return launch_mm<BT, 4>(Xr, T, d, ldr, packed, row_words, rn, N, sigma, cb, K, B, Y, ydt, ldy, st);
-}
-
-// Rows per workgroup of the one-kernel matvec.  (16 would let all
-// workgroups fit on the chip at once at the common sizes, but with
-// 1024-thread workgroups allowed the compiler keeps the kernel at 128 VGPRs
-// and it then spills.)
-constexpr int kMvRows = kGvRows;
-
-template <int L>
-struct LaunchMatvec {
-  static int run(const void* X, int32_t xdt, int d, const float* s, uint64_t seed, const uint32_t* packed,
-                 int row_words, const uint16_t* rn, int N, const float* sigma, const float* cb, int K, int B, void* Y,
-                 int32_t ydt, hipStream_t st) {
-    const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
-    const int nw = nwin < kGvMaxWaves ? nwin : kGvMaxWaves;
-    const dim3 grid((unsigned)((N + kMvRows - 1) / kMvRows)), blk((unsigned)(nw * kWave));
-    const size_t lds = (size_t)((K + 1) & ~1) * sizeof(float2) + (size_t)nw * kWave * 16 +
-                       (size_t)nw * kMvRows * sizeof(float);
-#define QAMW_MV(TIN, OUT, YT)                                                                                 \
-  hipLaunchKernelGGL((decode_matvec_kernel<L, kMvRows, TIN, OUT>), grid, blk, lds, st, (const TIN*)X, d, s, seed, \
-                     packed, row_words, rn, N, sigma, cb, K, B, (YT*)Y)
-    if (xdt == QAMW_F32) {
-      if (ydt == QAMW_F32) QAMW_MV(float, OutF32, float); else QAMW_MV(float, OutBF16, uint16_t);
-    } else {
-      if (ydt == QAMW_F32) QAMW_MV(uint16_t, OutF32, float); else QAMW_MV(uint16_t, OutBF16, uint16_t);
-    }
-#undef QAMW_MV
-    return check_launch("decode_matvec_kernel");
-  }
-};
-
-int launch_decode_matvec(int L, const void* X, int32_t xdt, int d, const float* s, uint64_t seed,
-                         const uint32_t* packed, int row_words, const uint16_t* rn, int N, const float* sigma,
-                         const float* cb, int K, int B, void* Y, int32_t ydt, hipStream_t st) {
-  return dispatch_L<LaunchMatvec>(L, X, xdt, d, s, seed, packed, row_words, rn, N, sigma, cb, K, B, Y, ydt, st);
 }
 
 int launch_decode_matmul(const uint16_t* Xr, int T, int d, int64_t ldr, const uint32_t* packed, int row_words,

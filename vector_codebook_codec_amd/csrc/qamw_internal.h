@@ -121,9 +121,6 @@ int launch_rotate_act(int L, const void* X, int32_t xdt, int T, int d, int64_t l
 int launch_decode_matmul(const uint16_t* Xr, int T, int d, int64_t ldr, const uint32_t* packed, int row_words,
                          const uint16_t* rn, int N, const float* sigma, const float* cb, int K, int B, void* Y,
                          int32_t ydt, int64_t ldy, hipStream_t st);
-int launch_decode_matvec(int L, const void* X, int32_t xdt, int d, const float* s, uint64_t seed,
-                         const uint32_t* packed, int row_words, const uint16_t* rn, int N, const float* sigma,
-                         const float* cb, int K, int B, void* Y, int32_t ydt, hipStream_t st);
 int launch_decode(int L, const uint32_t* packed, const uint16_t* rho_f16, int N, int d, const float* s,
                   const float* sigma, uint64_t seed, const float* cb, int K, int B, int row_words, void* out,
                   int32_t odt, int64_t ldo, hipStream_t st);
