@@ -132,8 +132,10 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
   for (int ps = 0; ps < kPairSets; ++ps) { best[ps] = INFINITY; tile_of_best[ps] = 0; }
 
   // Software pipeline: the MFMA of column block ps runs while the VALU folds
-  // the scores of block ps - 1 (two accumulator sets); the next tile's A and C
-  // operands are loaded during the current tile.
+  // the scores of block ps - 1 (two accumulator sets).  Tiles go in pairs
+  // with their own A and C operand registers: each register set is reloaded
+  // for the tile after next as soon as its tile's MFMAs are issued, so no
+  // operand is copied and every load has a whole tile to land.
   auto fold = [&](const f32x16& dsc, int ps, int c0) {
     float m = best[ps];
 #pragma unroll
@@ -148,25 +150,28 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
       cop[4 * g + 0] = h4.x; cop[4 * g + 1] = h4.y; cop[4 * g + 2] = h4.z; cop[4 * g + 3] = h4.w;
     }
   };
-  float aop = abase[0];
-  f32x16 cop;
-  load_c(0, cop);
-  for (int c0 = 0; c0 < Kpad; c0 += kTile) {
-    const int cn = (c0 + kTile < Kpad) ? c0 + kTile : c0;
-    const float anext = abase[cn];
-    f32x16 cnext;
-    load_c(cn, cnext);
-    f32x16 dprev = __builtin_amdgcn_mfma_f32_32x32x2f32(aop, bop[0], cop, 0, 0, 0);
+  auto tile = [&](float aop, const f32x16& cop, int c0) {
 #pragma unroll
-    for (int ps = 1; ps < kPairSets; ++ps) {
-      const f32x16 dcur = __builtin_amdgcn_mfma_f32_32x32x2f32(aop, bop[ps], cop, 0, 0, 0);
-      fold(dprev, ps - 1, c0);
-      dprev = dcur;
-    }
-    fold(dprev, kPairSets - 1, c0);
-    aop = anext;
-    cop = cnext;
+    for (int ps = 0; ps < kPairSets; ++ps)
+      fold(__builtin_amdgcn_mfma_f32_32x32x2f32(aop, bop[ps], cop, 0, 0, 0), ps, c0);
+  };
+  // tiles in pairs, then an odd last tile; padded centroids score +inf
+  float a0 = abase[0], a1 = abase[min(kTile, Kpad - kTile)];
+  f32x16 c0v, c1v;
+  load_c(0, c0v);
+  load_c(min(kTile, Kpad - kTile), c1v);
+  int c0 = 0;
+  for (; c0 + 2 * kTile <= Kpad; c0 += 2 * kTile) {
+    const int cn0 = c0 + 2 * kTile < Kpad ? c0 + 2 * kTile : 0;   // past the end: any valid tile
+    const int cn1 = c0 + 3 * kTile < Kpad ? c0 + 3 * kTile : 0;
+    tile(a0, c0v, c0);
+    a0 = abase[cn0];
+    load_c(cn0, c0v);
+    tile(a1, c1v, c0 + kTile);
+    a1 = abase[cn1];
+    load_c(cn1, c1v);
   }
+  if (c0 < Kpad) tile(a0, c0v, c0);
 
   // ---- combine the half-waves: smaller minimum, then earlier tile
 #pragma unroll
