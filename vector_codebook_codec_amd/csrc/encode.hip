@@ -492,7 +492,13 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
           const uint2 r = lists[e[p] & 0x7fffu];
           const uint32_t o0 = r.x & 0xffffu, o1 = r.x >> 16, o2 = r.y & 0xffffu, o3 = (r.y >> 16) & 0x7fffu;
           cont |= (r.y >> 31) != 0u;
-          const float4 t0 = cb4[o0 >> 4], t1 = cb4[o1 >> 4], t2 = cb4[o2 >> 4], t3 = cb4[o3 >> 4];
+          // a list's tail repeats its last entry: those lanes skip the gather
+          // (fewer active lanes, fewer bank conflicts) and reuse the operand
+          const float4 t0 = cb4[o0 >> 4], t1 = cb4[o1 >> 4];
+          float4 t2 = t1, t3;
+          if (o2 != o1) t2 = cb4[o2 >> 4];
+          t3 = t2;
+          if (o3 != o2) t3 = cb4[o3 >> 4];
           const float x = zx[g + p], y = zy[g + p];
           const float s0 = __builtin_fmaf(y, t0.y, __builtin_fmaf(x, t0.x, t0.z));
           const float s1 = __builtin_fmaf(y, t1.y, __builtin_fmaf(x, t1.x, t1.z));
