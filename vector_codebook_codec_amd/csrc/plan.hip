@@ -28,22 +28,28 @@
 // distances are smaller and U(SQ) >= U(Q)), and so does the centroid that
 // attains U(Q); the cells then test only the supercell's survivors.
 //
-// Two grids: a fine one (G = 512 over [-5, 5)^2) where nearly all normalised
-// pairs fall, and a coarse outer one (128 over [-20, 20)^2) for the few pairs
-// beyond it -- rows dominated by one large weight put a whole Hadamard block
-// there.  Each has its own delta (R = 5 or 20 in the formula above).  The
-// outer cells that tile the fine grid's square are never consulted (points
-// there take the fine grid) and hold overflow records.
+// Two levels: an inner square [-5, 5)^2 where nearly all normalised pairs
+// fall, and a coarse outer grid (128 cells per axis over [-20, 20)^2) for the
+// few pairs beyond it -- rows dominated by one large weight put a whole
+// Hadamard block there.  For K <= kLdsMaxK the inner square is the LDS table
+// (non-uniform cells with exact candidate sets, below); for larger K it is a
+// uniform 512 x 512 grid of supercell lists.  Each level has its own delta
+// (R = 5 or 20 in the formula above).  The outer cells that tile the inner
+// square are never consulted (points there take the inner level) and hold
+// overflow records.
 //
 // Layout (plan_bytes(K) bytes, 256-byte aligned):
 //   [0, 256)     PlanHeader
-//   [256, ...)   fine grid: uint16 lists [G*G][lmax], then the outer grid's
-//                [G2*G2][lmax]; one 16- or 32-byte record per cell.
-//                Entry i is 16 c_i | nibble_i: c_i the i-th listed centroid
-//                (16 c_i is its byte offset in the encode kernel's LDS copy of
-//                the codebook), nibble_0 = count - 1, nibble_1 = 1 when the
-//                cell overflows (scan the whole codebook), other nibbles 0;
-//                entries past the count repeat the last listed centroid.
+//   K > kLdsMaxK:  uniform inner grid, uint16 records [512*512][lmax], then
+//                  the outer grid's [G2*G2][lmax]
+//   K <= kLdsMaxK: the outer grid's records, then the LDS table image (bin
+//                  map, cell entries, list records: qamw_internal.h), then the
+//                  construction scratch of build_plan_kernel / lds_finish_kernel
+// A uniform-grid record is 16 (lmax 8) or 32 (lmax 16) bytes: entry i is
+// 16 c_i | nibble_i, c_i the i-th listed centroid (16 c_i is its byte offset in
+// the encode kernel's LDS copy of the codebook), nibble_0 = count - 1,
+// nibble_1 = 1 when the cell overflows (scan the whole codebook), other
+// nibbles 0; entries past the count repeat the last listed centroid.
 // In a grid of G cells per axis over [-R, R)^2, cell (ix, iy) covers
 // [-R + ix s, -R + (ix+1) s) x [-R + iy s, ...), s = 2R/G; its index is
 // ix * G + iy.
@@ -567,8 +573,8 @@ __device__ void build_lds_supercell(PlanSharedT<true>& sh, const CbRegs& v, int 
   const double cm = fmin(sqrt((double)cmax2 * 1.000001), zmax + sqrt((double)Uc * 1.000001 + delta));
   const double dq = 40.0 * 0x1p-24 * (2.5 * cm * cm + 2.0 * zmax * cm);
   const float lim = (Uc * 1.000001f + f32_up(dq)) * 1.000001f;
-  // ---- loose candidates in ascending order: survivors j = sub, sub + 4, ...,
-  // one chunk of four per ballot
+  // ---- loose candidates in ascending order: survivors j = sub, sub + 8, ...,
+  // one chunk of eight per ballot
   uint16_t* mine = sh.cell_list[qc];
   const int gshift = lane & ~(kLdsLanes - 1);
   int nl = 0;
@@ -582,7 +588,7 @@ __device__ void build_lds_supercell(PlanSharedT<true>& sh, const CbRegs& v, int 
   }
   __syncthreads();
   // ---- dominance, then the exact test of the undominated candidates
-  // (lane sub decides candidates sub, sub + 4, ...; the four masks are or-ed)
+  // (lane sub decides candidates sub, sub + 8, ...; the eight masks are or-ed)
   const bool over_loose = nl > kLdsLoose || nl == 0;
   const int n = over_loose ? 0 : nl;
   float2* cand = sh.cand[qc];
