@@ -403,17 +403,19 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
     const float* __restrict__ isig, const float* __restrict__ codebook, int K, int B, int row_words,
     const double* __restrict__ rho, const int* __restrict__ plan_K, const uint4* __restrict__ image, int image_bytes,
     int G, int lists_off, const uint16_t* __restrict__ outer, uint32_t* __restrict__ packed) {
-  // LDS: the codebook at offset 0 (so a candidate's byte offset 16 c is its
-  // address), then the table image, then one packing stage per wavefront
+  // LDS: the image's bin -> cell map at offset 0 and the codebook right
+  // after it (fixed offsets: the lookups and a candidate's byte offset 16 c
+  // need no base register), then the rest of the table image, then one
+  // packing stage per wavefront
   __shared__ __attribute__((aligned(16))) char lds[kLdsBudget];
-  float4* cb4 = reinterpret_cast<float4*>(lds);
+  const uint8_t* map = reinterpret_cast<const uint8_t*>(lds);
+  float4* cb4 = reinterpret_cast<float4*>(lds + kLdsBins);
   const int cb_bytes = 16 * K;
-  const uint8_t* map = reinterpret_cast<const uint8_t*>(lds + cb_bytes);
-  const uint16_t* cells = reinterpret_cast<const uint16_t*>(lds + cb_bytes + kLdsBins);
+  const uint16_t* cells = reinterpret_cast<const uint16_t*>(lds + kLdsBins + cb_bytes);
   const uint2* lists = reinterpret_cast<const uint2*>(lds + cb_bytes + lists_off);
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: window bookkeeping stays scalar
   const int nchunks = d >> 4;
   const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
   const int total = N * nwin;                      // fits in int (checked on the host)
@@ -424,8 +426,11 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
   WinLoads<Tin> wl;
   load_window<L>(wl, W, ldw, f, isig, rho, n, win, lane, nchunks);
   {
-    uint4* img = reinterpret_cast<uint4*>(lds + cb_bytes);
+    // image chunk i: the map (i < kLdsBins / 16) to offset 16 i, the rest
+    // after the codebook
+    uint4* img = reinterpret_cast<uint4*>(lds);
     const int nv = image_bytes / 16;
+    constexpr int kMapChunks = kLdsBins / 16;
     constexpr int kU = 8;                          // loads in flight per thread (clamped, always valid)
     for (int i0 = threadIdx.x; i0 < nv; i0 += kU * kLdsThreads) {
       uint4 t[kU];
@@ -433,7 +438,8 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
       for (int u = 0; u < kU; ++u) t[u] = image[min(i0 + u * kLdsThreads, nv - 1)];
 #pragma unroll
       for (int u = 0; u < kU; ++u)
-        if (i0 + u * kLdsThreads < nv) img[i0 + u * kLdsThreads] = t[u];
+        if (i0 + u * kLdsThreads < nv)
+          img[i0 + u * kLdsThreads + (i0 + u * kLdsThreads < kMapChunks ? 0 : K)] = t[u];
     }
   }
   for (int c = threadIdx.x; c < K; c += kLdsThreads) {
@@ -483,7 +489,8 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
       // ---- lists: the four slots' scores, their minimum, the first slot
       // reaching it (as a strict "<" scan of the ascending list would)
       uint32_t boff[4];
-      bool cont = false, wide = false;
+      bool wide = false;
+      uint64_t cont = 0;                           // lanes whose list continues (wave-uniform mask)
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         boff[p] = e[p];
@@ -491,19 +498,22 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
         if (e[p] >= 0x8000u && e[p] != kLdsScanAll) {
           const uint2 r = lists[e[p] & 0x7fffu];
           const uint32_t o0 = r.x & 0xffffu, o1 = r.x >> 16, o2 = r.y & 0xffffu, o3 = (r.y >> 16) & 0x7fffu;
-          cont |= (r.y >> 31) != 0u;
+          cont |= __ballot((r.y >> 31) != 0u);
           // a list's tail repeats its last entry: those lanes skip the gather
-          // (fewer active lanes, fewer bank conflicts) and reuse the operand
+          // (fewer active lanes, fewer bank conflicts) and take the previous
+          // slot's score
+          const bool n2 = o2 != o1, n3 = o3 != o2;
           const float4 t0 = cb4[o0 >> 4], t1 = cb4[o1 >> 4];
-          float4 t2 = t1, t3;
-          if (o2 != o1) t2 = cb4[o2 >> 4];
-          t3 = t2;
-          if (o3 != o2) t3 = cb4[o3 >> 4];
+          float4 t2, t3;
+          if (n2) t2 = cb4[o2 >> 4];
+          if (n3) t3 = cb4[o3 >> 4];
           const float x = zx[g + p], y = zy[g + p];
           const float s0 = __builtin_fmaf(y, t0.y, __builtin_fmaf(x, t0.x, t0.z));
           const float s1 = __builtin_fmaf(y, t1.y, __builtin_fmaf(x, t1.x, t1.z));
-          const float s2 = __builtin_fmaf(y, t2.y, __builtin_fmaf(x, t2.x, t2.z));
-          const float s3 = __builtin_fmaf(y, t3.y, __builtin_fmaf(x, t3.x, t3.z));
+          const float s2r = __builtin_fmaf(y, t2.y, __builtin_fmaf(x, t2.x, t2.z));
+          const float s2 = n2 ? s2r : s1;
+          const float s3r = __builtin_fmaf(y, t3.y, __builtin_fmaf(x, t3.x, t3.z));
+          const float s3 = n3 ? s3r : s2;
           const float m = fminf(fminf(s0, s1), fminf(s2, s3));
           uint32_t o = o3;
           o = (s2 == m) ? o2 : o;
@@ -513,7 +523,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
         }
       }
       // ---- lists of 5..8: the continuation record (rare)
-      if (__any(cont)) {
+      if (cont != 0) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           if (e[p] >= 0x8000u && e[p] != kLdsScanAll) {

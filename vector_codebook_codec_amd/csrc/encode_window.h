@@ -70,11 +70,13 @@ __device__ __forceinline__ int window_transform(const WinLoads<Tin>& w, bool act
   fwht_block<L>(x, lane);
   const int co_local = BlockOut<L>::chunk(lane);   // the lane now holds (sign *) chunk co_local
   const float osign = BlockOut<L>::sign(lane);
-  const double inv_row = row_normaliser(w.rho, L);
+  // the lane's sign and activity folded into the row factor once: a sign
+  // flip commutes with the rounding, and inactive lanes get 0
+  const double inv_row = active ? row_normaliser(w.rho, L) * (double)osign : 0.0;
   const float is[8] = {w.is[0].x, w.is[0].y, w.is[0].z, w.is[0].w, w.is[1].x, w.is[1].y, w.is[1].z, w.is[1].w};
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    const float inv = (float)(inv_row * (double)(active ? is[p] : 0.0f)) * osign;
+    const float inv = (float)(inv_row * (double)is[p]);
     zx[p] = x[2 * p] * inv;
     zy[p] = x[2 * p + 1] * inv;
   }
