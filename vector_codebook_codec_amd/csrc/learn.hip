@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kEncThreads) void lloyd_accum_kernel(
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: window bookkeeping stays scalar
   const int nchunks = d >> 4;
   const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
   const int total = N * nwin;

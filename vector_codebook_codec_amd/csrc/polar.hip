@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
   const float s_safe = r_safe * r_safe;
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: window bookkeeping stays scalar
   uint16_t* stage = stage_all + wave * kWinPairs;
   const int nchunks = d >> 4;
   const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
