@@ -125,8 +125,10 @@ template <int L, typename Tin, int kMaxWin>
 __global__ __launch_bounds__(kMaxWin * kWave) void norm_amplitude_kernel(
     const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ fcol,
     double* __restrict__ rho, uint16_t* __restrict__ rho_f16, float* __restrict__ partial) {
-  // rows per barrier (and loads in flight)
-  constexpr int kBatch = sizeof(Tin) == 2 ? (kMaxWin <= kFuseMidWin ? 4 : 2) : (kMaxWin <= kFuseMidWin ? 2 : 1);
+  // rows per barrier (and loads in flight); blocks below 32 or above 256
+  // columns need more registers for their lane stages, and take two
+  constexpr bool kWide = sizeof(Tin) == 2 && kMaxWin <= kFuseMidWin && L >= 5 && L <= 8;
+  constexpr int kBatch = kWide ? 4 : (sizeof(Tin) == 2 || kMaxWin <= kFuseMidWin ? 2 : 1);
   __shared__ double share[2][kBatch][kMaxWin];
   const int lane = threadIdx.x & (kWave - 1);
   const int win = threadIdx.x >> 6;
