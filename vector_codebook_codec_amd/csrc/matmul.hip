@@ -145,7 +145,7 @@ __global__ __launch_bounds__(mm_waves<TT>() * kWave) void decode_matmul_kernel(
   __syncthreads();
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: step bookkeeping stays scalar
   const int g = lane >> 4;                 // k-slot group (MFMA layout)
   const int nl = lane & 15;
   const int lr = lane >> 2, lq = lane & 3; // row and 16/32-byte chunk (load layout)
