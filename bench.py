@@ -22,7 +22,9 @@ roofline      the dominant kernel (encode_lds_kernel, all of
 valu_view     the exhaustive search (no plan) against the fp32 vector peak,
               and the planned search's speedup over it in those units
 decode_cold   decode alone after a 1 GiB read, next to a plain fill of the
-              same output bytes under the same protocol (also for 16 bits)
+              same output bytes under the same protocol (also for 16 bits):
+              one eager launch, and per launch of a graph of 8 decodes over
+              distinct buffers (no launch latency, every byte from/to HBM)
 c4_sweep      the 5120 x 13824 bf16 matrix at K = 256 / 1024 / 2048 / 4096
               and alpha = 0 / 0.5: plan, calibrate + encode, decode per variant
 c5_stack      the 7B-shaped stack (32 layers x q, k, v, o, gate, up, down):
@@ -562,6 +564,50 @@ def main():
     fill_buf = torch.empty_like(out)      # not `out`: it holds the step's decode
     fill32_ms = cold_fill(fill_buf, args.cold_decode_reps)
 
+    # The same two without the launch latency of a single eager launch: a
+    # HIP graph of 8 decodes (or fills), each over its own copy of the packed
+    # matrix and its own output (1.7 GB in all, far more than the 256 MB
+    # Infinity Cache, so every launch reads and writes HBM), replayed after
+    # the 1 GiB read; per launch = graph time / 8.
+    n_dc = 8
+    dc_pk = [packed.clone() for _ in range(n_dc)] if args.cold_decode_reps else []
+
+    def graph_cold(outs, reps, fill):
+        gst = torch.cuda.Stream()
+        gst.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gst):
+            def body():
+                for i, o in enumerate(outs):
+                    if fill:
+                        o.fill_(1.0)
+                    else:
+                        q.qamw_decode(dc_pk[i], rn, d, s, sigma, b, wl.sign_seed, Ct, out=o, stream=gst)
+            body()                      # pages touched once before capture
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=gst):
+                body()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            torch.sum(flush, dim=0, out=flush_sum)
+            torch.cuda.synchronize()
+            a, z = ev(), ev()
+            a.record()                  # a graph replays on the current stream
+            gr.replay()
+            z.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(z) / len(outs))
+        return float(np.median(ts)) if ts else None
+
+    dec_graph_cold_ms = fill32_graph_ms = None
+    if args.cold_decode_reps:
+        dc_out = [torch.empty_like(out) for _ in range(n_dc)]
+        dec_graph_cold_ms = graph_cold(dc_out, args.cold_decode_reps, False)
+        if not all(torch.equal(o, out) for o in dc_out):
+            raise RuntimeError("graph-replayed decodes differ from the step's decode")
+        fill32_graph_ms = graph_cold(dc_out, args.cold_decode_reps, True)
+        del dc_out
+
     # decode to 16-bit outputs (the fused decode -> fp16 / bf16 of the
     # 11008 x 4096 configuration's transpose), warm and cold
     dec16 = {}
@@ -592,12 +638,25 @@ def main():
             (cold16 if is_cold else warm16).append(a.elapsed_time(z))
         nb16 = N * d * 2 + N * rw * 4 + N * 2
         fill16_ms = cold_fill(fill_buf.view(-1).view(tdt)[:N * d], args.cold_decode_reps)
+        g16 = f16g = None
+        if args.cold_decode_reps:
+            outs16 = [torch.empty((N, d), dtype=tdt, device=dev) for _ in range(n_dc)]
+            g16 = graph_cold(outs16, args.cold_decode_reps, False)
+            if not all(torch.equal(o, out16) for o in outs16):
+                raise RuntimeError(f"graph-replayed {name} decodes differ")
+            f16g = graph_cold(outs16, args.cold_decode_reps, True)
+            del outs16
         dec16[name] = {"warm_ms": float(np.median(warm16)), "cold_ms": float(np.median(cold16)),
                        "algorithmic_bytes": nb16, "one_ulp_from_rounded_f32": n_ulp,
                        "frac_hbm_cold": nb16 / (np.median(cold16) * 1e-3) / 1e9 / PEAK_HBM_GBS,
                        "plain_fill_cold_ms": fill16_ms,
                        "plain_fill_frac_hbm_cold": None if fill16_ms is None else
-                           N * d * 2 / (fill16_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+                           N * d * 2 / (fill16_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                       "graph_cold_ms": g16,
+                       "frac_hbm_graph_cold": None if g16 is None else nb16 / (g16 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                       "plain_fill_graph_cold_ms": f16g,
+                       "plain_fill_frac_hbm_graph_cold": None if f16g is None else
+                           N * d * 2 / (f16g * 1e-3) / 1e9 / PEAK_HBM_GBS}
         del out16
 
     # fused decoded-weight matmul Y = X W^^T for T tokens (not part of the step).
@@ -867,8 +926,16 @@ def main():
             "plain_fill_cold_ms": fill32_ms,
             "plain_fill_frac_hbm_cold": None if fill32_ms is None else
                 N * d * 4 / (fill32_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "note": "1 GiB read before each rep; plain_fill is torch's fill of the same output under the "
-                    "same protocol"},
+            "graph_cold_ms": dec_graph_cold_ms,
+            "frac_hbm_graph_cold": None if dec_graph_cold_ms is None else
+                dec_bytes / (dec_graph_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "plain_fill_graph_cold_ms": fill32_graph_ms,
+            "plain_fill_frac_hbm_graph_cold": None if fill32_graph_ms is None else
+                N * d * 4 / (fill32_graph_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "note": "1 GiB read before each rep; ms: one eager launch (its launch latency included); "
+                    "graph_cold_ms: per launch of a HIP graph of 8 decodes, each over its own copy of the "
+                    "packed matrix and its own output (1.7 GB, all from and to HBM); plain_fill: torch's fill "
+                    "of the same outputs under the same two protocols"},
         "achieved_bpw": B / 2 + 16.0 / d,
         "decode_matmul": {"note": "Y = X W^^T over the packed matrix (qamw_rotate_activations + "
                                   "qamw_decode_matmul) vs qamw_decode to bf16 + torch.matmul; per T",
