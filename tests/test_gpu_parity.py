@@ -346,19 +346,23 @@ def test_out_of_range_indices_clamp(q, K):
     assert float((y[0].double() - y_ref).abs().max()) <= 2.0 ** -7 * S + 1e-6
 
 
-def test_exact_ties_lowest_index(q):
-    """Duplicated centroids: every index must be the first copy."""
+@pytest.mark.parametrize("Kb", [4, 16, 32])
+def test_exact_ties_lowest_index(q, Kb):
+    """Duplicated centroids: every index must be the first copy.  The
+    exhaustive kernel's MFMA tiles hold 32 centroids, rows 8 g + 4 h + k in
+    half-wave h: copies 4 apart tie across the half-waves of one tile, 16
+    apart inside one half-wave, 32 apart across tiles."""
     rng = np.random.default_rng(11)
     N, d, b = 4, 256, 64
-    base = q.load_codebook(16)
-    C = np.concatenate([base, base]).astype(np.float32)          # K = 32, second half duplicates
+    base = q.load_codebook(4) if Kb == 4 else (q.load_codebook(16) if Kb == 16 else q.load_codebook(256)[:32].copy())
+    C = np.concatenate([base, base]).astype(np.float32)          # K = 2 Kb, second half duplicates
     W = (rng.standard_normal((N, d)) * 0.02).astype(np.float32)
     dev = lambda a: torch.from_numpy(a).to(DEV)
     s, sigma = q.qamw_calibrate(dev(W), dev(np.ones(d, np.float32)), 0.0, b, 1)
     packed, rn = encode_both(q, dev(W), s, sigma, b, 1, dev(C))
     torch.cuda.synchronize()
-    idx = O.unpack(packed.cpu().numpy().view(np.uint32), 32, d)
-    assert idx.max() < 16
+    idx = O.unpack(packed.cpu().numpy().view(np.uint32), 2 * Kb, d)
+    assert idx.max() < Kb
     enc = O.encode(W, s.cpu().numpy(), sigma.cpu().numpy(), b, 1, C)
     assert O.accept_index(enc["zt"].reshape(-1, 2), C, enc["idx"].reshape(-1), idx.reshape(-1)).all()
 

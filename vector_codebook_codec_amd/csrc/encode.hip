@@ -173,26 +173,38 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
   }
   if (c0 < Kpad) tile(a0, c0v, c0);
 
-  // ---- combine the half-waves: smaller minimum, then earlier tile
+  // ---- combine the half-waves: smaller minimum, then earlier tile.  A
+  // half-wave holds rows 8 g + 4 half + k (g, k < 4) of every tile, so the
+  // rescan below needs only the 16 rows of the half that holds the minimum
+  // in the recorded tile -- both halves when they tie in the same tile.
+  uint32_t from_other = 0, both_halves = 0;
 #pragma unroll
   for (int ps = 0; ps < kPairSets; ++ps) {
     const float ob = __shfl_xor(best[ps], 32);
     const int ot = __shfl_xor(tile_of_best[ps], 32);
-    if (ob < best[ps] || (ob == best[ps] && ot < tile_of_best[ps])) { best[ps] = ob; tile_of_best[ps] = ot; }
+    const bool take = ob < best[ps] || (ob == best[ps] && ot < tile_of_best[ps]);
+    both_halves |= (ob == best[ps] && ot == tile_of_best[ps]) ? 1u << ps : 0u;
+    from_other |= take ? 1u << ps : 0u;
+    if (take) { best[ps] = ob; tile_of_best[ps] = ot; }
   }
 
   // ---- lowest index: rescan the tile; lane handles column blocks 2m + half
   uint32_t idxv[kPairSets / 2];
 #pragma unroll
   for (int m2 = 0; m2 < kPairSets / 2; ++m2) {
+    const int ps = 2 * m2 + half;
     const float bb = half ? best[2 * m2 + 1] : best[2 * m2];
     const int t0 = half ? tile_of_best[2 * m2 + 1] : tile_of_best[2 * m2];
-    const float2 z = zbuf[(2 * m2 + half) * 32 + jcol];
+    const float2 z = zbuf[ps * 32 + jcol];
+    const int src = ((from_other >> ps) & 1u) ? (half ^ 1) : half;
+    const bool both = (both_halves >> ps) & 1u;
     // lane-rotated order keeps the lanes on different LDS banks (tiles start
     // on multiples of 32 entries); the smallest matching index wins
     int id = INT_MAX;
-    for (int cc = 0; cc < kTile; ++cc) {
-      const int ci = t0 + ((cc + lane) & (kTile - 1));
+    const int span = both ? kTile : kTile / 2;
+    for (int cc = 0; cc < span; ++cc) {
+      const int q = (cc + lane) & (span - 1);
+      const int ci = t0 + (both ? q : 8 * (q >> 2) + 4 * src + (q & 3));
       const float sc = __builtin_fmaf(z.y, cby[ci], __builtin_fmaf(z.x, cbx[ci], cbh[ci]));
       id = (sc == bb) ? min(id, ci) : id;
     }
