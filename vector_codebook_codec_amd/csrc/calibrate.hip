@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kMaxWin * kWave) void norm_amplitude_kernel(
   constexpr int kBatch = kWide ? 4 : (sizeof(Tin) == 2 || kMaxWin <= kFuseMidWin ? 2 : 1);
   __shared__ double share[2][kBatch][kMaxWin];
   const int lane = threadIdx.x & (kWave - 1);
-  const int win = threadIdx.x >> 6;
+  const int win = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wavefront
   const int nwin = blockDim.x >> 6;
   const int nchunks = d >> 4;
   const int tile = blockIdx.x;
@@ -158,6 +158,7 @@ __global__ __launch_bounds__(kMaxWin * kWave) void norm_amplitude_kernel(
 #pragma unroll
   for (int u = 0; u < kBatch; ++u)
     if (active && n0 + u < n1) ring[u].load(base + (int64_t)(n0 + u) * ldw);
+    else ring[u].zero();                         // lanes past the row end keep zeros: no per-row select
   int buf = 0;
   for (int nb = n0; nb < n1; nb += kBatch) {     // uniform over the workgroup
     float amp[kBatch][8];
@@ -166,12 +167,7 @@ __global__ __launch_bounds__(kMaxWin * kWave) void norm_amplitude_kernel(
       const int n = nb + u;
       if (n >= n1) break;
       float x[16];
-      if (active) {
-        ring[u].unpack(x);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = 0.0f;
-      }
+      ring[u].unpack(x);                        // zeros in lanes past the row end
       if (active && n + kBatch < n1) ring[u].load(base + (int64_t)(n + kBatch) * ldw);
       // an empty asm "redefines" f each row, so its fp64 conversions are redone
       // here instead of being hoisted and held (32 registers) for the loop

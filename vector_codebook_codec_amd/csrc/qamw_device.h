@@ -560,8 +560,10 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
 template <int kCtrl>
 __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, kCtrl, 0xf, 0xf, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), kCtrl, 0xf, 0xf, false);
+  // every lane reads a lane of its own row (quad permutes and mirrors), so
+  // bound_ctrl never applies and the old value is not needed: no init move
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, kCtrl, 0xf, 0xf, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), kCtrl, 0xf, 0xf, true);
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
