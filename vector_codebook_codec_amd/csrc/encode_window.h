@@ -57,7 +57,8 @@ __device__ __forceinline__ void load_window(WinLoads<Tin>& w, const Tin* __restr
 // normalised pairs z~ of window chunk co_local (8 pairs), z~ = y / sigma_k
 // with y = H_b (f . w) / (sqrt(b) rho_n); each pair's factor
 // (1 / (sqrt(b) rho_n)) * (1 / sigma_k) is formed in fp64 and rounded once to
-// fp32 (0 for rho_n = 0).  Inactive lanes (past the row's last chunk) give 0.
+// fp32 (0 for rho_n = 0).  Inactive lanes (past the row's last chunk) give 0
+// (NaN where the chunk they copied holds a non-finite weight).
 template <int L, typename Tin>
 __device__ __forceinline__ int window_transform(const WinLoads<Tin>& w, bool active, int lane, float zx[8],
                                                 float zy[8]) {
@@ -66,12 +67,15 @@ __device__ __forceinline__ int window_transform(const WinLoads<Tin>& w, bool act
   const float fc[16] = {w.fc[0].x, w.fc[0].y, w.fc[0].z, w.fc[0].w, w.fc[1].x, w.fc[1].y, w.fc[1].z, w.fc[1].w,
                         w.fc[2].x, w.fc[2].y, w.fc[2].z, w.fc[2].w, w.fc[3].x, w.fc[3].y, w.fc[3].z, w.fc[3].w};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = active ? x[i] * fc[i] : 0.0f;
+  for (int i = 0; i < 16; ++i) x[i] *= fc[i];   // lanes past the row end: a copy of the last chunk, zeroed below
   fwht_block<L>(x, lane);
   const int co_local = BlockOut<L>::chunk(lane);   // the lane now holds (sign *) chunk co_local
   const float osign = BlockOut<L>::sign(lane);
   // the lane's sign and activity folded into the row factor once: a sign
-  // flip commutes with the rounding, and inactive lanes get 0
+  // flip commutes with the rounding, and inactive lanes get 0 (their pairs
+  // are 0, or NaN where the copied chunk holds Inf or NaN; whole Hadamard
+  // blocks are active or not, so they never mix with active lanes, and every
+  // caller discards their indices)
   const double inv_row = active ? row_normaliser(w.rho, L) * (double)osign : 0.0;
   const float is[8] = {w.is[0].x, w.is[0].y, w.is[0].z, w.is[0].w, w.is[1].x, w.is[1].y, w.is[1].z, w.is[1].w};
 #pragma unroll
