@@ -131,11 +131,12 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
   for (int ps = 0; ps < kPairSets; ++ps) { best[ps] = INFINITY; tile_of_best[ps] = 0; }
 
-  // Software pipeline: the MFMA of column block ps runs while the VALU folds
-  // the scores of block ps - 1 (two accumulator sets).  Tiles go in pairs
-  // with their own A and C operand registers: each register set is reloaded
-  // for the tile after next as soon as its tile's MFMAs are issued, so no
-  // operand is copied and every load has a whole tile to land.
+  // Each column block's scores are folded right after its MFMA (on this chip
+  // the fp32 MFMAs and the VALU do not overlap, so deferring the fold under
+  // the next MFMA gains nothing and costs an accumulator set).  Tiles go in
+  // pairs with their own A and C operand registers: each register set is
+  // reloaded for the tile after next as soon as its tile's MFMAs are issued,
+  // so no operand is copied and every load has a whole tile to land.
   auto fold = [&](const f32x16& dsc, int ps, int c0) {
     float m = best[ps];
 #pragma unroll
