@@ -188,6 +188,8 @@ SHAPES = [
     (5, 272, 4, 200, "bf16", 0.5, 12),       # K not a power of two (B = 8), 17 chunks
     (6, 1040, 8, 1000, "f32", 0.5, 13),      # two windows, the second one chunk wide; B = 10
     (3, 2048, 128, 3000, "bf16", 0.5, 14),   # K = 3000: the uniform grid of per-cell records, B = 12
+    (2, 262144, 256, 256, "bf16", 0.5, 15),  # 256 windows per row: the widest rows tested
+    (20000, 32, 16, 16, "f32", 0.5, 16),     # 20000 one-window rows: every grid walks many rows
 ]
 
 
