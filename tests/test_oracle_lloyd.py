@@ -37,7 +37,7 @@ def test_live_training_invariants():
     C50, h50 = lloyd.train(X, K, 50)
     assert h50[:49] == h49[:49]
     assert all(b <= a + 1e-15 for a, b in zip(h50, h50[1:]))      # non-increasing
-    # centroid condition: round 50 moves every centroid to its cell mean
+    # centroid condition: iteration 50 moves every centroid to its cell mean
     idx, _ = lloyd.assign(X, C49)
     mean, cnt = lloyd.cell_means(X, idx, K)
     assert np.all(cnt > 0)
