@@ -47,8 +47,11 @@ def lds_plan_layout(K):
     [-5, 5) with widths round(7 sqrt(2048 / K) exp(t^2 / 8)) clamped to
     [1, 255] bins (t: the inner edge's coordinate), mirrored about 0; an image
     of the bin map, G x G 16-bit entries and as many 8-byte list records as fit
-    160 KB - 1 KB of LDS next to the codebook (16 K bytes) and 16 wavefronts'
-    64 B-byte packing stages."""
+    160 KB - 1 KB of LDS next to the codebook (8 K bytes), 16 wavefronts'
+    64 B-byte packing stages and the encode kernel's own copy of the map and
+    cells (the map with a guard bin at each end, 2050 bytes padded to 2064;
+    the cells with a guard row and column, (G + 1)^2 16-bit entries padded to
+    16 bytes)."""
     h, w0 = 10 / 2048, 7 * math.sqrt(2048 / K)
     pos = [1024]
     while pos[-1] < 2048:
@@ -60,7 +63,7 @@ def lds_plan_layout(K):
     B = math.ceil(math.log2(K))
     up = lambda v, a: -(-v // a) * a
     lists_off = 2048 + up(2 * G * G, 16)
-    cap = min((159 * 1024 - 16 * K - 16 * 64 * B - lists_off) // 8, 32767) & ~1
+    cap = min((159 * 1024 - 8 * K - 16 * 64 * B - 2064 - up(2 * (G + 1) ** 2, 16)) // 8, 32767) & ~1
     image = lists_off + 8 * cap
     ns2 = (-(-G // 8)) * (-(-G // 4))       # 8 x 4-cell supercells
     scratch = up(G * G * 4, 256) + up(ns2 * 4, 256) + ns2 * 64 * 8
@@ -91,7 +94,10 @@ def test_host_helpers(lib):
     for K in (2, 16, 256, 1000, 2048):
         assert lib.qamw_plan_bytes(K) == lds_plan_layout(K)["plan_bytes"], K
     g = lds_plan_layout(2048)
-    assert g["G"] == 150 and g["image_bytes"] + 16 * 2048 + 16 * 64 * 11 <= 160 * 1024
+    # the encode kernel's LDS: map with guards, codebook (-cx, -cy), cells with
+    # a guard row and column, records, 16 packing stages
+    lds = 2064 + 8 * 2048 + -(-2 * 151 ** 2 // 16) * 16 + 8 * g["cap"] + 16 * 64 * 11
+    assert g["G"] == 150 and lds <= 159 * 1024
     assert lib.qamw_plan_bytes(1) == 0 and lib.qamw_plan_bytes(4097) == 0
 
 

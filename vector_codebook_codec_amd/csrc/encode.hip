@@ -399,16 +399,26 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
 
 // ---------------------------------------------------------------------------
 // Encode with the LDS search table (plan.hip, K <= kLdsMaxK).  One workgroup
-// of 16 wavefronts per CU keeps the codebook (-cx, -cy, |c|^2/2, 0) and the
-// plan's table image in LDS: a bin -> cell map shared by both axes, one
-// 16-bit entry per cell (16 c: the cell's only candidate; 0x8000 | r: list
-// record r; 0xFFFF: scan the whole codebook) and the list records (4 x 16 c,
-// ascending, the tail repeating the last; the top bit of the fourth entry
-// continues the list in record r + 1).  A pair looks its cell up, scores its
-// list with the same fp32 FMA sequence and strict "<" as the exhaustive
-// search, and so returns its index.  Pairs outside [-R, R)^2 take the outer
-// grid's record (global memory), or scan the whole codebook beyond it.
-// Indices are packed from registers through a byte stage per wavefront.
+// of 16 wavefronts per CU keeps the codebook (-cx, -cy) and the plan's table
+// in LDS: the bin -> cell map shared by both axes, one 16-bit
+// entry per cell (16 c: the cell's only candidate; 0x8000 | r: list record r;
+// 0xFFFF: scan the whole codebook) and the list records (4 x 16 c, ascending,
+// the tail repeating the last; the top bit of the fourth entry continues the
+// list in record r + 1).  A pair looks its cell up, scores its list with the
+// same fp32 FMA sequence and strict "<" as the exhaustive search, and so
+// returns its index.  Pairs outside [-R, R)^2 take the outer grid's record
+// (global memory), or scan the whole codebook beyond it.  Indices are packed
+// from registers through a byte stage per wavefront.
+//
+// LDS layout (the kernel's own, staged from the plan's image): the map with a
+// guard bin at each end, kLdsMapBytes; the codebook at kLdsMapBytes, 8 bytes
+// per centroid (a 64-lane gather of 8-byte entries meets far fewer bank
+// conflicts than one of 16-byte entries, whose starting banks are a quarter
+// as many); the cells as a (G + 1) x (G + 1) array whose last row and column ("cell G",
+// where the guard bins point) say "scan all"; the records; the stages.  A bin
+// outside [-R, R), an infinite or a NaN coordinate (the clamp and the
+// conversion send NaN to bin 0) lands in a guard bin, so the lookup needs no
+// range test.  A plan built for another K points every bin at the guard.
 // ---------------------------------------------------------------------------
 template <int L, typename Tin>
 __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))) void encode_lds_kernel(
@@ -416,16 +426,13 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
     const float* __restrict__ isig, const float* __restrict__ codebook, int K, int B, int row_words,
     const double* __restrict__ rho, const int* __restrict__ plan_K, const uint4* __restrict__ image, int image_bytes,
     int G, int lists_off, const uint16_t* __restrict__ outer, uint32_t* __restrict__ packed) {
-  // LDS: the image's bin -> cell map at offset 0 and the codebook right
-  // after it (fixed offsets: the lookups and a candidate's byte offset 16 c
-  // need no base register), then the rest of the table image, then one
-  // packing stage per wavefront
   __shared__ __attribute__((aligned(16))) char lds[kLdsBudget];
   const uint8_t* map = reinterpret_cast<const uint8_t*>(lds);
-  float4* cb4 = reinterpret_cast<float4*>(lds + kLdsBins);
-  const int cb_bytes = 16 * K;
-  const uint16_t* cells = reinterpret_cast<const uint16_t*>(lds + kLdsBins + cb_bytes);
-  const uint2* lists = reinterpret_cast<const uint2*>(lds + cb_bytes + lists_off);
+  const char* cbase = lds + kLdsMapBytes;          // codebook: centroid c at byte 8 c
+  const int cb_bytes = 8 * K;
+  const int cells_lds = kLdsMapBytes + cb_bytes;
+  const int lists_lds = cells_lds + (int)lds_cell_bytes(G);
+  const int rec_bytes = image_bytes - lists_off;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: window bookkeeping stays scalar
@@ -438,36 +445,88 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
   int n = min(gw, total - 1) / nwin, win = min(gw, total - 1) - (min(gw, total - 1) / nwin) * nwin;
   WinLoads<Tin> wl;
   load_window<L>(wl, W, ldw, f, isig, rho, n, win, lane, nchunks);
+  const bool plan_ok = *plan_K == K;               // a plan built for another K: scan the whole codebook
   {
-    // image chunk i: the map (i < kLdsBins / 16) to offset 16 i, the rest
-    // after the codebook
-    uint4* img = reinterpret_cast<uint4*>(lds);
-    const int nv = image_bytes / 16;
-    constexpr int kMapChunks = kLdsBins / 16;
+    // records: verbatim 16-byte chunks of the image
+    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(image) + lists_off);
+    uint4* dst = reinterpret_cast<uint4*>(lds + lists_lds);
+    const int nv = rec_bytes / 16;
     constexpr int kU = 8;                          // loads in flight per thread (clamped, always valid)
     for (int i0 = threadIdx.x; i0 < nv; i0 += kU * kLdsThreads) {
       uint4 t[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) t[u] = image[min(i0 + u * kLdsThreads, nv - 1)];
+      for (int u = 0; u < kU; ++u) t[u] = src[min(i0 + u * kLdsThreads, nv - 1)];
 #pragma unroll
       for (int u = 0; u < kU; ++u)
-        if (i0 + u * kLdsThreads < nv)
-          img[i0 + u * kLdsThreads + (i0 + u * kLdsThreads < kMapChunks ? 0 : K)] = t[u];
+        if (i0 + u * kLdsThreads < nv) dst[i0 + u * kLdsThreads] = t[u];
     }
+    // the cells, 16-byte chunks of the image's G x G array re-strided to
+    // G + 1 (element i of the image goes to i + i / G), then the guard row
+    // and column; the map one chunk per thread, shifted by the low guard bin
+    const uint4* gcells = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(image) + kLdsBins);
+    uint16_t* lcells = reinterpret_cast<uint16_t*>(lds + cells_lds);
+    const int ncv = (G * G + 7) / 8;
+    constexpr int kC = 4;
+    for (int i0 = threadIdx.x; i0 < ncv; i0 += kC * kLdsThreads) {
+      uint4 t[kC];
+#pragma unroll
+      for (int u = 0; u < kC; ++u) t[u] = gcells[min(i0 + u * kLdsThreads, ncv - 1)];
+#pragma unroll
+      for (int u = 0; u < kC; ++u) {
+        const int v = i0 + u * kLdsThreads;
+        const uint32_t w[4] = {t[u].x, t[u].y, t[u].z, t[u].w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int i = 8 * v + k;
+          if (v < ncv && i < G * G) lcells[i + i / G] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+        }
+      }
+    }
+    for (int i = threadIdx.x; i < 2 * G + 1; i += kLdsThreads)
+      lcells[i < G + 1 ? i * (G + 1) + G : G * (G + 1) + (i - (G + 1))] = kLdsScanAll;
+    uint8_t* lmap = reinterpret_cast<uint8_t*>(lds);
+    if (threadIdx.x < kLdsBins / 16) {
+      const uint4 m = reinterpret_cast<const uint4*>(image)[threadIdx.x];
+      const uint32_t w[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        lmap[1 + 16 * threadIdx.x + k] = plan_ok ? (uint8_t)(w[k >> 2] >> (8 * (k & 3))) : (uint8_t)G;
+    }
+    if (threadIdx.x < 2) lmap[threadIdx.x ? kLdsBins + 1 : 0] = (uint8_t)G;
   }
   for (int c = threadIdx.x; c < K; c += kLdsThreads) {
     const float cx = codebook[2 * c], cy = codebook[2 * c + 1];
-    cb4[c] = make_float4(-cx, -cy, 0.5f * __builtin_fmaf(cx, cx, cy * cy), 0.0f);
+    reinterpret_cast<float2*>(lds + kLdsMapBytes)[c] = make_float2(-cx, -cy);
   }
   __syncthreads();
   if (gw >= total) return;                         // no barriers follow
-  uint8_t* stage = reinterpret_cast<uint8_t*>(lds + cb_bytes + image_bytes + wave * 64 * B);
-  const bool plan_ok = *plan_K == K;               // a plan built for another K: scan the whole codebook
+  uint8_t* stage = reinterpret_cast<uint8_t*>(lds + lists_lds + rec_bytes + wave * 64 * B);
+  // Twice the score of centroid c at byte h8 = 8 c, from (x2, y2) = 2 z~:
+  // fma(y2, -cy, fma(x2, -cx, |c|^2)) with |c|^2 = fma(cx, cx, cy cy).  Every
+  // step is exactly twice that of fma(y, -cy, fma(x, -cx, |c|^2 / 2)) (a
+  // power-of-two scaling commutes with the rounding), so the scores order
+  // and tie exactly as the exhaustive search's.  The codebook holds only
+  // (-cx, -cy): 8-byte gathers, half the LDS bytes of (-cx, -cy, |c|^2 / 2).
+  auto cand = [&](uint32_t h8) -> float2 {
+    return *reinterpret_cast<const float2*>(__builtin_assume_aligned(cbase + h8, 8));
+  };
+  auto score2c = [](float x2, float y2, float2 c) -> float {
+    return __builtin_fmaf(y2, c.y, __builtin_fmaf(x2, c.x, __builtin_fmaf(c.x, c.x, c.y * c.y)));
+  };
+  auto score2 = [&](float x2, float y2, uint32_t h8) -> float { return score2c(x2, y2, cand(h8)); };
+  // record r of an entry 0x8000 | r sits at lists_lds + 8 r = 8 e + (lists_lds - 0x40000)
+  const uint32_t rec_bias = (uint32_t)lists_lds - 0x40000u;
+  auto record = [&](uint32_t e) -> uint2 {
+    return *reinterpret_cast<const uint2*>(__builtin_assume_aligned(lds + ((e << 3) + rec_bias), 8));
+  };
 
+  // bin t = x kLdsBins / (2R) + kLdsBins / 2 + 1 (its rounding, < 1e-3 bin,
+  // is inside the table's eta margin); bins 0 and kLdsBins + 1 are the guards
   const float bins_per_unit = (float)kLdsBins / (2.0f * kPlanR);
-  const float bmax = __uint_as_float(__float_as_uint((float)kLdsBins) - 1u);   // largest float below kLdsBins
+  const float bmax = __uint_as_float(__float_as_uint((float)(kLdsBins + 2)) - 1u);   // largest float below kLdsBins + 2
   const float cells_per_unit2 = (float)kPlanG2 / (2.0f * kPlanR2);
   const float tmax2 = __uint_as_float(__float_as_uint((float)kPlanG2) - 1u);
+  const uint32_t gstride = (uint32_t)(G + 1);
 
   for (;;) {
     const bool active = win * kWinChunks + lane < nchunks;   // whole Hadamard blocks are active or not
@@ -486,53 +545,52 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
     for (int g = 0; g < 8; g += 4) {
       uint32_t e[4];
-      // ---- cell lookups: bin t = x kLdsBins / (2R) + kLdsBins / 2 (its rounding,
-      // < 1e-3 bin, is inside the table's eta margin); the clamp changes nothing
-      // inside [-R, R), so "unchanged" is the range test (false for NaN)
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const float tx = __builtin_fmaf(zx[g + p], bins_per_unit, 0.5f * kLdsBins);
-        const float ty = __builtin_fmaf(zy[g + p], bins_per_unit, 0.5f * kLdsBins);
-        const float bx = __builtin_amdgcn_fmed3f(tx, 0.0f, bmax);
-        const float by = __builtin_amdgcn_fmed3f(ty, 0.0f, bmax);
-        const uint32_t ix = map[(int)bx], iy = map[(int)by];
-        const uint32_t ce = cells[__umul24(ix, (uint32_t)G) + iy];
-        e[p] = (plan_ok && bx == tx && by == ty) ? ce : (uint32_t)kLdsScanAll;
+        const float tx = __builtin_fmaf(zx[g + p], bins_per_unit, 0.5f * kLdsBins + 1.0f);
+        const float ty = __builtin_fmaf(zy[g + p], bins_per_unit, 0.5f * kLdsBins + 1.0f);
+        const uint32_t ix = map[(int)__builtin_amdgcn_fmed3f(tx, 0.0f, bmax)];
+        const uint32_t iy = map[(int)__builtin_amdgcn_fmed3f(ty, 0.0f, bmax)];
+        const uint32_t cell = __umul24(ix, gstride) + iy;
+        e[p] = *reinterpret_cast<const uint16_t*>(lds + cells_lds + 2u * cell);
       }
-      // ---- lists: the four slots' scores, their minimum, the first slot
-      // reaching it (as a strict "<" scan of the ascending list would)
+      // ---- lists: scan the record's distinct slots in ascending order with a
+      // strict "<" (the first of equal scores wins, as in the exhaustive
+      // search).  The four pairs' records are read together (other lanes read
+      // record 0, unused); a list's repeated tail slots skip the gather (fewer
+      // bank conflicts) and the comparison.
       uint32_t boff[4];
-      bool wide = false;
+      bool wide = false, lst[4];
+      uint2 rr[4];
       uint64_t cont = 0;                           // lanes whose list continues (wave-uniform mask)
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        boff[p] = e[p];
+        lst[p] = e[p] >= 0x8000u && e[p] != kLdsScanAll;
         wide |= e[p] == kLdsScanAll;
-        if (e[p] >= 0x8000u && e[p] != kLdsScanAll) {
-          const uint2 r = lists[e[p] & 0x7fffu];
-          const uint32_t o0 = r.x & 0xffffu, o1 = r.x >> 16, o2 = r.y & 0xffffu, o3 = (r.y >> 16) & 0x7fffu;
-          cont |= __ballot((r.y >> 31) != 0u);
-          // a list's tail repeats its last entry: those lanes skip the gather
-          // (fewer active lanes, fewer bank conflicts) and take the previous
-          // slot's score
+        rr[p] = record(lst[p] ? e[p] : 0x8000u);
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        boff[p] = e[p];
+        if (lst[p]) {
+          // slots as byte offsets 8 c (the record holds 16 c)
+          const uint32_t o0 = (rr[p].x & 0xffffu) >> 1, o1 = rr[p].x >> 17, o2 = (rr[p].y & 0xffffu) >> 1,
+                         o3 = (rr[p].y >> 17) & 0x3fffu;
+          cont |= __ballot((rr[p].y >> 31) != 0u);
           const bool n2 = o2 != o1, n3 = o3 != o2;
-          const float4 t0 = cb4[o0 >> 4], t1 = cb4[o1 >> 4];
-          float4 t2, t3;
-          if (n2) t2 = cb4[o2 >> 4];
-          if (n3) t3 = cb4[o3 >> 4];
-          const float x = zx[g + p], y = zy[g + p];
-          const float s0 = __builtin_fmaf(y, t0.y, __builtin_fmaf(x, t0.x, t0.z));
-          const float s1 = __builtin_fmaf(y, t1.y, __builtin_fmaf(x, t1.x, t1.z));
-          const float s2r = __builtin_fmaf(y, t2.y, __builtin_fmaf(x, t2.x, t2.z));
-          const float s2 = n2 ? s2r : s1;
-          const float s3r = __builtin_fmaf(y, t3.y, __builtin_fmaf(x, t3.x, t3.z));
-          const float s3 = n3 ? s3r : s2;
-          const float m = fminf(fminf(s0, s1), fminf(s2, s3));
-          uint32_t o = o3;
-          o = (s2 == m) ? o2 : o;
-          o = (s1 == m) ? o1 : o;
-          o = (s0 == m) ? o0 : o;
-          boff[p] = o;
+          const float x2 = 2.0f * zx[g + p], y2 = 2.0f * zy[g + p];
+          const float2 c0 = cand(o0), c1 = cand(o1);
+          float2 c2, c3;                           // gathered only where the slot is new
+          if (n2) c2 = cand(o2);
+          if (n3) c3 = cand(o3);
+          const float s0 = score2c(x2, y2, c0), s1 = score2c(x2, y2, c1);
+          const float s2 = score2c(x2, y2, c2), s3 = score2c(x2, y2, c3);
+          float best = s0;
+          uint32_t o = o0;
+          if (s1 < best) { best = s1; o = o1; }
+          if (n2 && s2 < best) { best = s2; o = o2; }
+          if (n3 && s3 < best) o = o3;
+          boff[p] = 2u * o;
         }
       }
       // ---- lists of 5..8: the continuation record (rare)
@@ -540,17 +598,16 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           if (e[p] >= 0x8000u && e[p] != kLdsScanAll) {
-            const uint2 r0 = lists[e[p] & 0x7fffu];
+            const uint2 r0 = record(e[p]);
             if (r0.y >> 31) {
-              const uint2 r = lists[(e[p] & 0x7fffu) + 1];
+              const uint2 r = record(e[p] + 1u);
               const uint32_t o[4] = {r.x & 0xffffu, r.x >> 16, r.y & 0xffffu, r.y >> 16};
-              const float4 tb = cb4[boff[p] >> 4];
-              float best = __builtin_fmaf(zy[g + p], tb.y, __builtin_fmaf(zx[g + p], tb.x, tb.z));
+              const float x2 = 2.0f * zx[g + p], y2 = 2.0f * zy[g + p];
+              float best = score2(x2, y2, boff[p] >> 1);
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const float4 t = cb4[o[i] >> 4];
-                const float sc = __builtin_fmaf(zy[g + p], t.y, __builtin_fmaf(zx[g + p], t.x, t.z));
-                if (sc < best) { best = sc; boff[p] = o[i]; }
+                const float sc = score2(x2, y2, (o[i] & 0x7ff0u) >> 1);
+                if (sc < best) { best = sc; boff[p] = o[i] & 0x7ff0u; }
               }
             }
           }
@@ -563,6 +620,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
         for (int p = 0; p < 4; ++p) {
           if (!__any(e[p] == kLdsScanAll)) continue;
           const float x = zx[g + p], y = zy[g + p];
+          const float x2 = 2.0f * x, y2 = 2.0f * y;
           const float ux = __builtin_fmaf(x, cells_per_unit2, 0.5f * kPlanG2);
           const float uy = __builtin_fmaf(y, cells_per_unit2, 0.5f * kPlanG2);
           const float vx = __builtin_amdgcn_fmed3f(ux, 0.0f, tmax2);
@@ -582,8 +640,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
             for (int i = 0; i < cnt; ++i) {
               const uint32_t w = words[i >> 1];
               const uint32_t off = ((i & 1) ? (w >> 16) : w) & 0xfff0u;
-              const float4 t = cb4[off >> 4];
-              const float sc = __builtin_fmaf(y, t.y, __builtin_fmaf(x, t.x, t.z));
+              const float sc = score2(x2, y2, off >> 1);
               if (sc < fb) { fb = sc; fo = off; }
             }
             boff[p] = fo;
@@ -592,8 +649,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
             float fb = INFINITY;
             uint32_t fo = 0;
             for (int cc = 0; cc < K; ++cc) {
-              const float4 t = cb4[cc];              // same address in every lane: broadcast
-              const float sc = __builtin_fmaf(y, t.y, __builtin_fmaf(x, t.x, t.z));
+              const float sc = score2(x2, y2, (uint32_t)cc * 8u);   // same address in every lane: broadcast
               if (sc < fb) { fb = sc; fo = (uint32_t)cc * 16u; }
             }
             if (full && over) boff[p] = fo;
@@ -601,7 +657,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
         }
       }
 #pragma unroll
-      for (int p = 0; p < 4; ++p) idx[g + p] = active ? (boff[p] & 0x7fffu) >> 4 : 0u;
+      for (int p = 0; p < 4; ++p) idx[g + p] = active ? boff[p] >> 4 : 0u;
     }
     stage_lane_bytes(stage, co_local, idx, B);
     wave_lds_fence();
@@ -637,7 +693,8 @@ struct LaunchEncode {
         const uint16_t* outer = (const uint16_t*)(base + plan_outer_offset(K));
         const int64_t wgs = (waves + kLdsWaves - 1) / kLdsWaves;
         const dim3 lgrid((unsigned)std::min<int64_t>(wgs, (int64_t)cus)), lblk(kLdsThreads);
-        const size_t lds = (size_t)16 * K + g.image_bytes + (size_t)kLdsWaves * g.stage_bytes;
+        const size_t lds = kLdsMapBytes + (size_t)8 * K + lds_cell_bytes(g.G) + (g.image_bytes - g.lists_off) +
+                           (size_t)kLdsWaves * g.stage_bytes;
         if (lds > kLdsBudget) return fail(QAMW_EUNSUPPORTED, "LDS table too large");
         if (wdt == QAMW_F32)
           hipLaunchKernelGGL((encode_lds_kernel<L, float>), lgrid, lblk, 0, st, (const float*)W, ldw, N, d, f, isig,

@@ -1034,7 +1034,10 @@ bool lds_geometry(int K, LdsGeometry* g) {
   g->stage_bytes = (size_t)64 * B;
   g->cells_off = kLdsBins;
   g->lists_off = g->cells_off + round_up((size_t)2 * G * G, 16);
-  const long avail = (long)kLdsBudget - 16L * K - (long)(kLdsWaves * g->stage_bytes) - (long)g->lists_off;
+  // the encode kernel holds the map and cells in its own layout (guard bins,
+  // a guard row and column): the records get what is left of its LDS
+  const long avail = (long)kLdsBudget - 8L * K - (long)(kLdsWaves * g->stage_bytes) - (long)kLdsMapBytes -
+                     (long)lds_cell_bytes(G);
   long cap = avail / 8;
   cap = cap > 32767 ? 32767 : cap;
   cap &= ~1L;                                   // whole 16-byte rows

@@ -63,16 +63,24 @@ __host__ __device__ inline int plan_lmax(int K) { return K <= 2048 ? 8 : 16; }
 
 // LDS table geometry.  Both axes share one map from kLdsBins equal bins over
 // [-kPlanR, kPlanR) to cell coordinates; cells are whole runs of bins, widest
-// far from the origin where centroids are sparse.  The image is copied to LDS
-// verbatim: [bin -> cell map, u8 x kLdsBins][cell entries, u16 x G x G, padded
-// to 16 bytes][candidate lists, 4 x u16 each, lists_cap of them].
+// far from the origin where centroids are sparse.  The plan's image is
+// [bin -> cell map, u8 x kLdsBins][cell entries, u16 x G x G, padded to 16
+// bytes][candidate lists, 4 x u16 each, lists_cap of them]; the encode kernel
+// stages it into LDS in a layout of its own (below), and lists_cap is what
+// fits there.
 constexpr int kLdsMaxK = 2048;
 constexpr int kLdsBins = 2048;
-constexpr int kLdsMaxG = 256;
+constexpr int kLdsMaxG = 255;                // the guard cell index G fits the u8 map
 constexpr int kLdsThreads = 1024;            // one 16-wavefront workgroup per CU
 constexpr int kLdsWaves = kLdsThreads / 64;
 constexpr size_t kLdsBudget = 160 * 1024 - 1024;   // LDS bytes one encode workgroup may take
 constexpr uint16_t kLdsScanAll = 0xFFFFu;    // cell entry: search the whole codebook
+// The encode kernel's own LDS copy of the table: the map with one guard bin
+// at each end (padded to 16 bytes), then the codebook (-cx, -cy) at 8 bytes
+// per centroid, then the cells as a (G + 1) x (G + 1) array with a "scan all"
+// guard row and column, then the records, then 16 packing stages.
+constexpr size_t kLdsMapBytes = (kLdsBins + 2 + 15) / 16 * 16;
+__host__ __device__ inline size_t lds_cell_bytes(int G) { return ((size_t)2 * (G + 1) * (G + 1) + 15) / 16 * 16; }
 struct LdsGeometry {
   int G;                         // cells per axis (<= kLdsMaxG)
   int lists_cap;                 // list records the image holds
