@@ -116,7 +116,7 @@ __device__ __forceinline__ void pack_window(const uint16_t* stage, int lane, int
 // Packing from registers.  A lane's 8 indices are those of the 8 consecutive
 // pairs of window chunk co, i.e. bits [8 B co, 8 B co + 8 B) of the window's
 // stream: exactly bytes [B co, B co + B).  stage_lane_bytes writes them into
-// the wavefront's 64 B-byte stage; store_stage then writes the window's
+// the wavefront's 64 B-byte stage (dword writes for B = 8..11, bytes below); store_stage then writes the window's
 // 16 B words from it with 16-byte stores (the last window of a row stops at
 // row_words; lanes past the row end must have staged zero indices, which are
 // the row's zero padding bits).
@@ -124,6 +124,7 @@ __device__ __forceinline__ void pack_window(const uint16_t* stage, int lane, int
 template <int BT>
 __device__ __forceinline__ void stage_lane_bytes_t(uint8_t* __restrict__ stage, int co, const uint32_t idx[8]) {
   constexpr int B = BT;
+  static_assert(B >= 8 && B <= 11, "8 B bits span at most four dwords");
   uint32_t w[3] = {0u, 0u, 0u};
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
@@ -131,9 +132,23 @@ __device__ __forceinline__ void stage_lane_bytes_t(uint8_t* __restrict__ stage, 
     w[wd] |= idx[p] << sh;
     if (sh + B > 32) w[wd + 1] |= idx[p] >> (32 - sh);
   }
-  uint8_t* dst = stage + B * co;
-#pragma unroll
-  for (int b = 0; b < B; ++b) dst[b] = (uint8_t)(w[b >> 2] >> (8 * (b & 3)));
+  // The lane's bits start at byte B co: byte t of dword j0.  Shifted into
+  // place they are d0..d3 (v_perm selects the bytes of (w_k : w_(k-1)) >>
+  // (32 - 8 t)).  A dword shared with the previous lane (t > 0: that lane
+  // wrote its low bytes, zeros above) is OR-ed in after every lane's plain
+  // writes; every other dword the lane touches it owns alone.
+  const uint32_t bc = (uint32_t)(B * co), t = bc & 3u, j0 = bc >> 2;
+  const uint32_t sel = 0x07060504u - t * 0x01010101u;
+  const uint32_t d0 = __builtin_amdgcn_perm(w[0], 0u, sel), d1 = __builtin_amdgcn_perm(w[1], w[0], sel),
+                 d2 = __builtin_amdgcn_perm(w[2], w[1], sel), d3 = __builtin_amdgcn_perm(0u, w[2], sel);
+  const uint32_t last = (8u * t + 8u * B - 1u) >> 5;   // the last dword touched, relative to j0 (1..3)
+  uint32_t* s32 = reinterpret_cast<uint32_t*>(stage) + j0;
+  s32[1] = d1;
+  if (last >= 2u) s32[2] = d2;
+  if (last == 3u) s32[3] = d3;
+  if (t == 0u) s32[0] = d0;
+  wave_lds_fence();                                  // the plain writes of every lane first
+  if (t != 0u) __hip_atomic_fetch_or(s32, d0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
 }
 
 __device__ __forceinline__ void stage_lane_bytes(uint8_t* __restrict__ stage, int co, const uint32_t idx[8], int B) {
