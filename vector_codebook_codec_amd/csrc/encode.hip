@@ -560,9 +560,10 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
       // record 0, unused); a list's repeated tail slots skip the gather (fewer
       // bank conflicts) and the comparison.
       uint32_t boff[4];
-      bool wide = false, lst[4];
+      float bsc[4];                                // the list's best (doubled) score so far
+      bool wide = false, lst[4], more[4];          // more: the list continues in the next record
       uint2 rr[4];
-      uint64_t cont = 0;                           // lanes whose list continues (wave-uniform mask)
+      uint64_t cont = 0;                           // lanes with some list that continues (wave-uniform mask)
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         lst[p] = e[p] >= 0x8000u && e[p] != kLdsScanAll;
@@ -572,11 +573,12 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         boff[p] = e[p];
+        more[p] = lst[p] && (rr[p].y >> 31) != 0u;
+        cont |= __ballot(more[p]);
         if (lst[p]) {
           // slots as byte offsets 8 c (the record holds 16 c)
           const uint32_t o0 = (rr[p].x & 0xffffu) >> 1, o1 = rr[p].x >> 17, o2 = (rr[p].y & 0xffffu) >> 1,
                          o3 = (rr[p].y >> 17) & 0x3fffu;
-          cont |= __ballot((rr[p].y >> 31) != 0u);
           const bool n2 = o2 != o1, n3 = o3 != o2;
           const float x2 = 2.0f * zx[g + p], y2 = 2.0f * zy[g + p];
           const float2 c0 = cand(o0), c1 = cand(o1);
@@ -589,26 +591,30 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
           uint32_t o = o0;
           if (s1 < best) { best = s1; o = o1; }
           if (n2 && s2 < best) { best = s2; o = o2; }
-          if (n3 && s3 < best) o = o3;
+          if (n3 && s3 < best) { best = s3; o = o3; }
           boff[p] = 2u * o;
+          bsc[p] = best;
         }
       }
-      // ---- lists of 5..8: the continuation record (rare)
+      // ---- lists of 5..8: the continuation record, for the pairs of the
+      // group where some lane needs it (rare per pair, but a group of 256
+      // pairs holds one often); its entries all follow the first record's
       if (cont != 0) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          if (e[p] >= 0x8000u && e[p] != kLdsScanAll) {
-            const uint2 r0 = record(e[p]);
-            if (r0.y >> 31) {
-              const uint2 r = record(e[p] + 1u);
-              const uint32_t o[4] = {r.x & 0xffffu, r.x >> 16, r.y & 0xffffu, r.y >> 16};
-              const float x2 = 2.0f * zx[g + p], y2 = 2.0f * zy[g + p];
-              float best = score2(x2, y2, boff[p] >> 1);
+          if (!__any(more[p])) continue;
+          if (more[p]) {
+            const uint2 r = record(e[p] + 1u);
+            const uint32_t o[4] = {(r.x & 0xffffu) >> 1, r.x >> 17, (r.y & 0xffffu) >> 1, (r.y >> 17) & 0x3fffu};
+            const float x2 = 2.0f * zx[g + p], y2 = 2.0f * zy[g + p];
+            float2 c[4];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const float sc = score2(x2, y2, (o[i] & 0x7ff0u) >> 1);
-                if (sc < best) { best = sc; boff[p] = o[i] & 0x7ff0u; }
-              }
+            for (int i = 0; i < 4; ++i) c[i] = cand(o[i]);
+            float best = bsc[p];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float sc = score2c(x2, y2, c[i]);
+              if (sc < best) { best = sc; boff[p] = 2u * o[i]; }
             }
           }
         }
