@@ -521,17 +521,19 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
   };
 
   // bin t = x kLdsBins / (2R) + kLdsBins / 2 + 1 (its rounding, < 1e-3 bin,
-  // is inside the table's eta margin); bins 0 and kLdsBins + 1 are the guards
-  const float bins_per_unit = (float)kLdsBins / (2.0f * kPlanR);
+  // is inside the table's eta margin); bins 0 and kLdsBins + 1 are the guards.
+  // The lanes hold 2 z~: the factors below are halved (exactly), so every
+  // product is that of z~ with the full factor.
+  const float bins_per_unit = 0.5f * ((float)kLdsBins / (2.0f * kPlanR));
   const float bmax = __uint_as_float(__float_as_uint((float)(kLdsBins + 2)) - 1u);   // largest float below kLdsBins + 2
-  const float cells_per_unit2 = (float)kPlanG2 / (2.0f * kPlanR2);
+  const float cells_per_unit2 = 0.5f * ((float)kPlanG2 / (2.0f * kPlanR2));
   const float tmax2 = __uint_as_float(__float_as_uint((float)kPlanG2) - 1u);
   const uint32_t gstride = (uint32_t)(G + 1);
 
   for (;;) {
     const bool active = win * kWinChunks + lane < nchunks;   // whole Hadamard blocks are active or not
-    float zx[8], zy[8];
-    const int co_local = window_transform<L>(wl, active, lane, zx, zy);
+    float zx[8], zy[8];                            // 2 z~ (see score2c)
+    const int co_local = window_transform<L, Tin, 2>(wl, active, lane, zx, zy);
     const int n_cur = n, win_cur = win;
     const int gnext = gw + stride;
     {
@@ -580,7 +582,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
           const uint32_t o0 = (rr[p].x & 0xffffu) >> 1, o1 = rr[p].x >> 17, o2 = (rr[p].y & 0xffffu) >> 1,
                          o3 = (rr[p].y >> 17) & 0x3fffu;
           const bool n2 = o2 != o1, n3 = o3 != o2;
-          const float x2 = 2.0f * zx[g + p], y2 = 2.0f * zy[g + p];
+          const float x2 = zx[g + p], y2 = zy[g + p];
           const float2 c0 = cand(o0), c1 = cand(o1);
           float2 c2, c3;                           // gathered only where the slot is new
           if (n2) c2 = cand(o2);
@@ -606,7 +608,7 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
           if (more[p]) {
             const uint2 r = record(e[p] + 1u);
             const uint32_t o[4] = {(r.x & 0xffffu) >> 1, r.x >> 17, (r.y & 0xffffu) >> 1, (r.y >> 17) & 0x3fffu};
-            const float x2 = 2.0f * zx[g + p], y2 = 2.0f * zy[g + p];
+            const float x2 = zx[g + p], y2 = zy[g + p];
             float2 c[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) c[i] = cand(o[i]);
@@ -625,10 +627,9 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           if (!__any(e[p] == kLdsScanAll)) continue;
-          const float x = zx[g + p], y = zy[g + p];
-          const float x2 = 2.0f * x, y2 = 2.0f * y;
-          const float ux = __builtin_fmaf(x, cells_per_unit2, 0.5f * kPlanG2);
-          const float uy = __builtin_fmaf(y, cells_per_unit2, 0.5f * kPlanG2);
+          const float x2 = zx[g + p], y2 = zy[g + p];
+          const float ux = __builtin_fmaf(x2, cells_per_unit2, 0.5f * kPlanG2);
+          const float uy = __builtin_fmaf(y2, cells_per_unit2, 0.5f * kPlanG2);
           const float vx = __builtin_amdgcn_fmed3f(ux, 0.0f, tmax2);
           const float vy = __builtin_amdgcn_fmed3f(uy, 0.0f, tmax2);
           // the outer grid is consulted only outside [-R, R)^2, where its

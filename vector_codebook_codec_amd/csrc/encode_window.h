@@ -58,8 +58,10 @@ __device__ __forceinline__ void load_window(WinLoads<Tin>& w, const Tin* __restr
 // with y = H_b (f . w) / (sqrt(b) rho_n); each pair's factor
 // (1 / (sqrt(b) rho_n)) * (1 / sigma_k) is formed in fp64 and rounded once to
 // fp32 (0 for rho_n = 0).  Inactive lanes (past the row's last chunk) give 0
-// (NaN where the chunk they copied holds a non-finite weight).
-template <int L, typename Tin>
+// (NaN where the chunk they copied holds a non-finite weight).  With
+// kScale = 2 the lane gets 2 z~ instead, exactly (the factor is doubled in
+// fp64 before its one rounding; doubling commutes with every rounding).
+template <int L, typename Tin, int kScale = 1>
 __device__ __forceinline__ int window_transform(const WinLoads<Tin>& w, bool active, int lane, float zx[8],
                                                 float zy[8]) {
   float x[16];
@@ -80,7 +82,7 @@ __device__ __forceinline__ int window_transform(const WinLoads<Tin>& w, bool act
   const float is[8] = {w.is[0].x, w.is[0].y, w.is[0].z, w.is[0].w, w.is[1].x, w.is[1].y, w.is[1].z, w.is[1].w};
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    const float inv = (float)(inv_row * (double)is[p]);
+    const float inv = (float)(inv_row * (double)is[p] * (double)kScale);
     zx[p] = x[2 * p] * inv;
     zy[p] = x[2 * p + 1] * inv;
   }
