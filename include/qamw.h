@@ -82,12 +82,13 @@ int32_t qamw_index_bits(int32_t K);
 int64_t qamw_packed_row_words(int64_t d, int32_t K);
 
 /* Bytes of device workspace qamw_calibrate needs for an N x d matrix (row
- * norms in fp64, column factors eps_j s_j and per-row-tile partial sums of
- * pair amplitudes). */
+ * factors 1 / (sqrt(block) rho_n) in fp64, column factors eps_j s_j and
+ * per-row-tile partial sums of pair amplitudes). */
 size_t qamw_calibrate_workspace_bytes(int64_t N, int64_t d, int32_t block);
 
 /* Bytes of device workspace qamw_encode needs for an N x d matrix (fp64 row
- * norms, fp32 per-column factors eps_j s_j, fp32 1 / sigma_k). */
+ * factors 1 / (sqrt(block) rho_n), 0 for rho_n = 0; fp32 per-column factors
+ * eps_j s_j; fp32 1 / sigma_k). */
 size_t qamw_encode_workspace_bytes(int64_t N, int64_t d);
 
 const char* qamw_status_string(int32_t status);
@@ -196,9 +197,10 @@ int32_t qamw_encode_noalloc(const void* W, int32_t wdtype, int64_t N, int64_t d,
  * qamw_encode in two phases, for callers that time or reuse them separately.
  *
  * qamw_encode_prepare (QAM-W, Methodology: Separation of Scale and Direction;
- * Pairing and Calibration): row norms rho_n = ||W_n diag(s)||_2 (fp64 into
- * the workspace, binary16 bits RNE into rownorm_f16 [N]), the per-column
- * factors eps_j s_j and the pair factors 1 / sigma_k (into the workspace).
+ * Pairing and Calibration): row norms rho_n = ||W_n diag(s)||_2 (binary16
+ * bits RNE into rownorm_f16 [N]; into the workspace the fp64 row factors
+ * 1 / (sqrt(block) rho_n)), the per-column factors eps_j s_j and the pair
+ * factors 1 / sigma_k (into the workspace).
  * Arguments as for qamw_encode.
  *
  * qamw_encode_indices (QAM-W, Methodology: Deterministic Rotation; Joint 2D

@@ -170,7 +170,7 @@ int32_t qamw_build_plan(const float* codebook, int32_t K, void* plan, size_t pla
 }
 
 struct EncodeWorkspace {
-  double* rho;    // [N] fp64 row norms
+  double* rho;    // [N] fp64 row factors 1 / (sqrt(b) rho_n) (0 for rho_n = 0)
   float* f;       // [d] eps_j s_j
   float* isig;    // [d/2] 1 / sigma_k
 };
@@ -206,7 +206,7 @@ int32_t qamw_encode_prepare(const void* W, int32_t wdtype, int64_t N, int64_t d,
   if ((rc = check_encode_workspace(workspace, workspace_bytes, N, d))) return rc;
   hipStream_t st = (hipStream_t)stream;
   const EncodeWorkspace e = encode_workspace(workspace, N, d);
-  return launch_encode_prepare(W, wdtype, (int)N, (int)d, ldw, s, sigma, sign_seed, e.rho, rownorm_f16, e.f, e.isig,
+  return launch_encode_prepare(L, W, wdtype, (int)N, (int)d, ldw, s, sigma, sign_seed, e.rho, rownorm_f16, e.f, e.isig,
                                st);
 }
 

@@ -28,20 +28,22 @@ __global__ __launch_bounds__(kBlockThreads) void scale_kernel(const float* __res
   }
 }
 
-// rho_n = ||W_n diag(s)||, one wavefront per row (row_norm_wave).
+// rho_n = ||W_n diag(s)||, one wavefront per row (row_norm_wave): its
+// binary16 bits and the row factor 1 / (sqrt(b) rho_n).
 template <typename Tin>
 __global__ __launch_bounds__(kBlockThreads) void rownorm_kernel(const Tin* __restrict__ W, int64_t ldw,
                                                                 int N, int d, const float* __restrict__ s,
-                                                                double* __restrict__ rho,
+                                                                double sqrt_b, double* __restrict__ rowf,
                                                                 uint16_t* __restrict__ rho_f16) {
   const int n = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (n < N) row_norm_wave(W, ldw, n, d, s, rho, rho_f16);
+  if (n < N) row_norm_wave(W, ldw, n, d, s, sqrt_b, rowf, rho_f16);
 }
 
 // ---------------------------------------------------------------------------
 // Calibration, pass 2: per (window, row tile) wavefront, accumulate the pair
 // amplitudes |z_{n,k}| of the normalised rotated rows over the tile.
-// partial[t][k] = sum_{n in tile t} hypot(y_{n,2k}, y_{n,2k+1}) / (sqrt(b) rho_n)
+// partial[t][k] = sum_{n in tile t} hypot(y_{n,2k}, y_{n,2k+1}) / (sqrt(b) rho_n),
+// the divisor read as the row factor rownorm_kernel wrote.
 // ---------------------------------------------------------------------------
 template <int L, typename Tin>
 __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
@@ -68,12 +70,9 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
 
   const int n0 = tile * kCalibRowsPerTile;
   const int n1 = min(N, n0 + kCalibRowsPerTile);
-  // 1 / (sqrt(b) rho_n) of the tile's rows, one per lane
+  // 1 / (sqrt(b) rho_n) of the tile's rows (the row factors), one per lane
   float inv_lane = 0.0f;
-  if (lane < n1 - n0) {
-    const double r = rho[n0 + lane];
-    inv_lane = r > 0.0 ? (float)(1.0 / (sqrt_b * r)) : 0.0f;
-  }
+  if (lane < n1 - n0) inv_lane = (float)rho[n0 + lane];
   // a ring of kAmpDepth rows in flight: row n + kAmpDepth is loaded while row n is processed
   constexpr int kAmpDepth = 4;
   RawChunk<Tin> ring[kAmpDepth];
@@ -114,8 +113,9 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
 // share of rho_n^2 (chunk_sumsq + window_sum, as row_norm_wave does) and the
 // pair amplitudes; the shares meet in LDS, every wavefront adds them in window
 // order (the same fp64 sum as row_norm_wave, so rho is identical; one lane
-// per row of a batch), and the amplitudes are scaled and accumulated exactly
-// as amplitude_kernel does.  A barrier per batch of rows; the share buffer
+// per row of a batch, which also writes the row factor 1 / (sqrt(b) rho_n)),
+// and the amplitudes are scaled and accumulated exactly as amplitude_kernel
+// does.  A barrier per batch of rows; the share buffer
 // alternates between batches.
 // ---------------------------------------------------------------------------
 constexpr int kFuseMaxWin = 16;   // 1024 threads
@@ -192,9 +192,10 @@ __global__ __launch_bounds__(kMaxWin * kWave) void norm_amplitude_kernel(
     if (lane < kBatch)
       for (int w = 0; w < nwin; ++w) t += share[buf][lane][w];
     const double rn = sqrt(t);
-    const float inv_l = rn > 0.0 ? (float)(1.0 / (sqrt_b * rn)) : 0.0f;
+    const double rowf = row_factor(rn, sqrt_b);
+    const float inv_l = (float)rowf;
     if (win == 0 && lane < kBatch && nb + lane < n1) {
-      rho[nb + lane] = rn;
+      rho[nb + lane] = rowf;
       if (rho_f16) rho_f16[nb + lane] = f64_to_f16_bits(rn);
     }
 #pragma unroll
@@ -262,13 +263,16 @@ int launch_scale(const float* r, float alpha, uint64_t seed, int d, float* s, fl
   return check_launch("scale_kernel");
 }
 
-int launch_rownorm(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, double* rho,
+int launch_rownorm(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, double* rho,
                    uint16_t* rho_f16, hipStream_t st) {
   const dim3 grid(grid_for_waves(N)), blk(kBlockThreads);
+  const double sqrt_b = sqrt((double)(1 << L));
   if (wdt == QAMW_F32)
-    hipLaunchKernelGGL(rownorm_kernel<float>, grid, blk, 0, st, (const float*)W, ldw, N, d, s, rho, rho_f16);
+    hipLaunchKernelGGL(rownorm_kernel<float>, grid, blk, 0, st, (const float*)W, ldw, N, d, s, sqrt_b, rho,
+                       rho_f16);
   else
-    hipLaunchKernelGGL(rownorm_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)W, ldw, N, d, s, rho, rho_f16);
+    hipLaunchKernelGGL(rownorm_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)W, ldw, N, d, s, sqrt_b, rho,
+                       rho_f16);
   return check_launch("rownorm_kernel");
 }
 
@@ -322,7 +326,7 @@ int launch_norm_amplitude(int L, const void* W, int32_t wdt, int N, int d, int64
   const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
   if (nwin <= kFuseMaxWin) return dispatch_L<LaunchNormAmplitude>(L, W, wdt, N, d, ldw, f, rho, rho_f16, partial, st);
   int rc;
-  if ((rc = launch_rownorm(W, wdt, N, d, ldw, s, rho, rho_f16, st))) return rc;
+  if ((rc = launch_rownorm(L, W, wdt, N, d, ldw, s, rho, rho_f16, st))) return rc;
   return launch_amplitude(L, W, wdt, N, d, ldw, f, rho, partial, st);
 }
 

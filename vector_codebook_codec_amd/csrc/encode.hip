@@ -54,11 +54,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 template <typename Tin>
 __global__ __launch_bounds__(kBlockThreads) void encode_prepare_kernel(
     const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ s,
-    const float* __restrict__ sigma, uint64_t seed, int row_blocks, double* __restrict__ rho,
+    const float* __restrict__ sigma, uint64_t seed, int row_blocks, double sqrt_b, double* __restrict__ rho,
     uint16_t* __restrict__ rho_f16, float* __restrict__ f, float* __restrict__ isig) {
   if ((int)blockIdx.x < row_blocks) {
     const int n = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (n < N) row_norm_wave(W, ldw, n, d, s, rho, rho_f16);
+    if (n < N) row_norm_wave(W, ldw, n, d, s, sqrt_b, rho, rho_f16);
     return;
   }
   const int j = (blockIdx.x - row_blocks) * kBlockThreads + threadIdx.x;
@@ -741,16 +741,18 @@ struct LaunchEncode {
   }
 };
 
-int launch_encode_prepare(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s, const float* sigma,
-                          uint64_t seed, double* rho, uint16_t* rho_f16, float* f, float* isig, hipStream_t st) {
+int launch_encode_prepare(int L, const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* s,
+                          const float* sigma, uint64_t seed, double* rho, uint16_t* rho_f16, float* f, float* isig,
+                          hipStream_t st) {
   const int row_blocks = grid_for_waves(N);
   const dim3 grid((unsigned)(row_blocks + (d + kBlockThreads - 1) / kBlockThreads)), blk(kBlockThreads);
+  const double sqrt_b = sqrt((double)(1 << L));
   if (wdt == QAMW_F32)
     hipLaunchKernelGGL(encode_prepare_kernel<float>, grid, blk, 0, st, (const float*)W, ldw, N, d, s, sigma, seed,
-                       row_blocks, rho, rho_f16, f, isig);
+                       row_blocks, sqrt_b, rho, rho_f16, f, isig);
   else
     hipLaunchKernelGGL(encode_prepare_kernel<uint16_t>, grid, blk, 0, st, (const uint16_t*)W, ldw, N, d, s, sigma,
-                       seed, row_blocks, rho, rho_f16, f, isig);
+                       seed, row_blocks, sqrt_b, rho, rho_f16, f, isig);
   return check_launch("encode_prepare_kernel");
 }
 

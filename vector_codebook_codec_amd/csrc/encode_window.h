@@ -18,11 +18,6 @@ namespace qamw {
 constexpr int kEncThreads = 512;                       // 8 wavefronts per workgroup
 constexpr int kEncWaves = kEncThreads / kWave;
 
-__device__ __forceinline__ double row_normaliser(double rho, int L) {
-  const double den = rho * sqrt((double)(1 << L));
-  return den > 0.0 ? 1.0 / den : 0.0;
-}
-
 // Everything one lane reads for one (row, window): its 16 weights, their
 // column factors eps_j s_j, 1 / sigma of the 8 pairs it holds after the
 // rotation, and the row norm.  load_window issues every load unconditionally
@@ -34,7 +29,7 @@ struct WinLoads {
   RawChunk<Tin> raw;
   float4 fc[4];
   float4 is[2];
-  double rho;
+  double rho;   // the row factor 1 / (sqrt(b) rho_n) (0 for rho_n = 0)
 };
 
 template <int L, typename Tin>
@@ -78,7 +73,7 @@ __device__ __forceinline__ int window_transform(const WinLoads<Tin>& w, bool act
   // are 0, or NaN where the copied chunk holds Inf or NaN; whole Hadamard
   // blocks are active or not, so they never mix with active lanes, and every
   // caller discards their indices)
-  const double inv_row = active ? row_normaliser(w.rho, L) * (double)osign : 0.0;
+  const double inv_row = active ? w.rho * (double)osign : 0.0;
   const float is[8] = {w.is[0].x, w.is[0].y, w.is[0].z, w.is[0].w, w.is[1].x, w.is[1].y, w.is[1].z, w.is[1].w};
 #pragma unroll
   for (int p = 0; p < 8; ++p) {

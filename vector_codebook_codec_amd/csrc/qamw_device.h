@@ -548,7 +548,8 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
 // their butterfly sum over the lanes (window_sum), and rho^2 adds the
 // windows' shares in window order.  The fused calibration kernel, which has
 // one wavefront per window, forms the same sum.
-// Lane 0 writes rho[n] and, when rho_f16 is given, its binary16 (RNE) bits.
+// Lane 0 writes the row factor (row_factor, below) and, when rho_f16 is
+// given, rho_n's binary16 (RNE) bits.
 // ---------------------------------------------------------------------------
 // Sum over the wavefront, every lane getting the same bits, in VALU
 // instructions only: inside each 16-lane row, DPP pairs lane i with i ^ 1,
@@ -598,6 +599,14 @@ __device__ __forceinline__ double window_sum(double v) {
   return v;
 }
 
+// The factor every pair of row n is scaled by before its nearest-centroid
+// search: 1 / (sqrt(b) rho_n) in fp64 (0 for rho_n = 0), formed once per row
+// by the kernel that computes rho_n.
+__device__ __forceinline__ double row_factor(double rho, double sqrt_b) {
+  const double den = rho * sqrt_b;
+  return den > 0.0 ? 1.0 / den : 0.0;
+}
+
 // One chunk's share: sum of (x_i s_i)^2, i = 0..15, as an FMA chain from 0.
 // The sign of s does not matter (the square of an exact product).
 __device__ __forceinline__ double chunk_sumsq(const float x[16], const float sc[16]) {
@@ -610,10 +619,12 @@ __device__ __forceinline__ double chunk_sumsq(const float x[16], const float sc[
   return acc;
 }
 
+// Lane 0 writes the row factor 1 / (sqrt(b) rho_n) (fp64; 0 for rho_n = 0)
+// that the transform scales the row's pairs by, and rho_n's binary16 bits.
 template <typename Tin>
 __device__ __forceinline__ void row_norm_wave(const Tin* __restrict__ W, int64_t ldw, int n, int d,
-                                              const float* __restrict__ s, double* __restrict__ rho,
-                                              uint16_t* __restrict__ rho_f16) {
+                                              const float* __restrict__ s, double sqrt_b,
+                                              double* __restrict__ rowf, uint16_t* __restrict__ rho_f16) {
   const int lane = threadIdx.x & (kWave - 1);
   const int nchunks = d >> 4;
   const int nwin = (nchunks + kWinChunks - 1) / kWinChunks;
@@ -649,7 +660,7 @@ __device__ __forceinline__ void row_norm_wave(const Tin* __restrict__ W, int64_t
   }
   if (lane == 0) {
     const double r = sqrt(total);
-    rho[n] = r;
+    rowf[n] = row_factor(r, sqrt_b);
     if (rho_f16) rho_f16[n] = f64_to_f16_bits(r);
   }
 }
