@@ -562,10 +562,8 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
       // record 0, unused); a list's repeated tail slots skip the gather (fewer
       // bank conflicts) and the comparison.
       uint32_t boff[4];
-      float bsc[4];                                // the list's best (doubled) score so far
       bool wide = false, lst[4], more[4];          // more: the list continues in the next record
       uint2 rr[4];
-      uint64_t cont = 0;                           // lanes with some list that continues (wave-uniform mask)
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         lst[p] = e[p] >= 0x8000u && e[p] != kLdsScanAll;
@@ -576,13 +574,16 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
       for (int p = 0; p < 4; ++p) {
         boff[p] = e[p];
         more[p] = lst[p] && (rr[p].y >> 31) != 0u;
-        cont |= __ballot(more[p]);
         if (lst[p]) {
           // slots as byte offsets 8 c (the record holds 16 c)
           const uint32_t o0 = (rr[p].x & 0xffffu) >> 1, o1 = rr[p].x >> 17, o2 = (rr[p].y & 0xffffu) >> 1,
                          o3 = (rr[p].y >> 17) & 0x3fffu;
           const bool n2 = o2 != o1, n3 = o3 != o2;
           const float x2 = zx[g + p], y2 = zy[g + p];
+          // lists of 5..8 (rare per pair, but a group of 256 pairs holds one
+          // often): the continuation record is read with the first gathers
+          uint2 rc;
+          if (more[p]) rc = record(e[p] + 1u);
           const float2 c0 = cand(o0), c1 = cand(o1);
           float2 c2, c3;                           // gathered only where the slot is new
           if (n2) c2 = cand(o2);
@@ -594,31 +595,27 @@ __global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4))
           if (s1 < best) { best = s1; o = o1; }
           if (n2 && s2 < best) { best = s2; o = o2; }
           if (n3 && s3 < best) { best = s3; o = o3; }
-          boff[p] = 2u * o;
-          bsc[p] = best;
-        }
-      }
-      // ---- lists of 5..8: the continuation record, for the pairs of the
-      // group where some lane needs it (rare per pair, but a group of 256
-      // pairs holds one often); its entries all follow the first record's
-      if (cont != 0) {
+          // its entries all follow the first record's; a list of 5 has one
+          // (the others repeat it), longer lists take the other three slots
+          if (__any(more[p])) {
+            if (more[p]) {
+              const uint32_t oc[4] = {(rc.x & 0xffffu) >> 1, rc.x >> 17, (rc.y & 0xffffu) >> 1,
+                                      (rc.y >> 17) & 0x3fffu};
+              const float sc0 = score2c(x2, y2, cand(oc[0]));
+              if (sc0 < best) { best = sc0; o = oc[0]; }
+              if (__any(oc[1] != oc[0])) {
+                float2 c[3];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          if (!__any(more[p])) continue;
-          if (more[p]) {
-            const uint2 r = record(e[p] + 1u);
-            const uint32_t o[4] = {(r.x & 0xffffu) >> 1, r.x >> 17, (r.y & 0xffffu) >> 1, (r.y >> 17) & 0x3fffu};
-            const float x2 = zx[g + p], y2 = zy[g + p];
-            float2 c[4];
+                for (int i = 0; i < 3; ++i) c[i] = cand(oc[i + 1]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) c[i] = cand(o[i]);
-            float best = bsc[p];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float sc = score2c(x2, y2, c[i]);
-              if (sc < best) { best = sc; boff[p] = 2u * o[i]; }
+                for (int i = 0; i < 3; ++i) {
+                  const float sc = score2c(x2, y2, c[i]);
+                  if (sc < best) { best = sc; o = oc[i + 1]; }
+                }
+              }
             }
           }
+          boff[p] = 2u * o;
         }
       }
       // ---- outside the table or a cell without a list: the outer grid's
