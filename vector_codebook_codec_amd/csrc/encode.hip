@@ -242,8 +242,8 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
 // every centroid that can be the fp32 minimum in the cell).  Pairs outside the
 // grids or in overflowing cells scan the whole codebook.
 //
-// The codebook sits in LDS as (-cx, -cy, |c|^2/2, 0) per centroid, one
-// ds_read_b128 per candidate at the byte offset the list stores.  A lane's
+// The codebook sits in LDS as (-cx, -cy) per centroid, one 8-byte gather per
+// candidate at half the byte offset 16 c the list stores.  A lane's
 // pairs are scored in groups of PG with all their record loads issued
 // together; list slot i is scored for the whole group while any lane of the
 // wavefront has a pair with more than i candidates (a list's unused tail
@@ -258,15 +258,22 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
     const double* __restrict__ rho, const int* __restrict__ plan_K, const uint16_t* __restrict__ lists,
     const uint16_t* __restrict__ lists2, uint32_t* __restrict__ packed) {
   static_assert(LMAX % 8 == 0 && LMAX <= 16 && kPairsPerLane % PG == 0, "list and group sizes");
-  __shared__ float4 cb4[KMAX];                                      // (-cx, -cy, |c|^2/2, 0)
+  __shared__ float2 cb2[KMAX];                                      // (-cx, -cy)
   __shared__ uint16_t stage_all[kEncWaves * kWinPairs];             // 8 waves x 512 indices
-  const char* cbytes = reinterpret_cast<const char*>(cb4);
+  const char* cbytes = reinterpret_cast<const char*>(cb2);
 
   for (int c = threadIdx.x; c < K; c += kEncThreads) {
     const float cx = codebook[2 * c], cy = codebook[2 * c + 1];
-    cb4[c] = make_float4(-cx, -cy, 0.5f * __builtin_fmaf(cx, cx, cy * cy), 0.0f);
+    cb2[c] = make_float2(-cx, -cy);
   }
   __syncthreads();
+  // Twice the score of centroid c from (x2, y2) = 2 z~: fma(y2, -cy, fma(x2,
+  // -cx, |c|^2)), |c|^2 = fma(cx, cx, cy cy) -- every step exactly twice the
+  // exhaustive search's fma(y, -cy, fma(x, -cx, |c|^2 / 2)), so the order and
+  // the ties are the same; 8-byte gathers meet far fewer bank conflicts.
+  auto score2 = [](float x2, float y2, float2 c) -> float {
+    return __builtin_fmaf(y2, c.y, __builtin_fmaf(x2, c.x, __builtin_fmaf(c.x, c.x, c.y * c.y)));
+  };
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: window bookkeeping stays scalar
@@ -284,16 +291,17 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
   WinLoads<Tin> wl;
   load_window<L>(wl, W, ldw, f, isig, rho, n, win, lane, nchunks);
 
-  const float cells_per_unit = (float)kPlanG / (2.0f * kPlanR);
-  const float cells_per_unit2 = (float)kPlanG2 / (2.0f * kPlanR2);
+  // the lanes hold 2 z~: the cell factors are halved (exactly)
+  const float cells_per_unit = 0.5f * ((float)kPlanG / (2.0f * kPlanR));
+  const float cells_per_unit2 = 0.5f * ((float)kPlanG2 / (2.0f * kPlanR2));
   const float tmax = __uint_as_float(__float_as_uint((float)kPlanG) - 1u);     // largest float below G
   const float tmax2 = __uint_as_float(__float_as_uint((float)kPlanG2) - 1u);
   const bool plan_ok = *plan_K == K;   // a plan built for another K: scan the whole codebook
 
   for (;;) {
     const bool active = win * kWinChunks + lane < nchunks;   // whole Hadamard blocks are active or not
-    float zx[8], zy[8];
-    const int co_local = window_transform<L>(wl, active, lane, zx, zy);
+    float zx[8], zy[8];                            // 2 z~ (see score2)
+    const int co_local = window_transform<L, Tin, 2>(wl, active, lane, zx, zy);
     const int n_cur = n, win_cur = win;
     const int gnext = gw + stride;
     {
@@ -309,6 +317,7 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
     for (int g = 0; g < kPairsPerLane; g += PG) {
       uint32_t words[PG][LMAX / 2];
       bool inside[PG];
+      const uint4* recp[PG];
       // ---- every record load of the group first.  Cell coordinate t = x G/(2R) + G/2:
       // its rounding error (< 1e-5 cell) is far inside the plan's eta margin;
       // the clamp changes nothing inside the grid, so "unchanged" is the range test
@@ -330,22 +339,42 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
           inside[p] = plan_ok && vx == ux && vy == uy;
           rec = lists2 + (size_t)(inside[p] ? (int)vx * kPlanG2 + (int)vy : 0) * LMAX;
         }
-        const uint4* lp = reinterpret_cast<const uint4*>(rec);
-#pragma unroll
-        for (int q = 0; q < LMAX / 8; ++q) {
-          const uint4 t = lp[q];
-          words[p][4 * q + 0] = t.x; words[p][4 * q + 1] = t.y; words[p][4 * q + 2] = t.z; words[p][4 * q + 3] = t.w;
-        }
+        // the record's first 16 bytes (entries 0..7); the rest only for
+        // lists of more than 8, below
+        recp[p] = reinterpret_cast<const uint4*>(rec);
+        const uint4 t = recp[p][0];
+        words[p][0] = t.x; words[p][1] = t.y; words[p][2] = t.z; words[p][3] = t.w;
       }
       // ---- record flags: nibble 0 = count - 1, nibble 1 = overflow
       bool full[PG];
-      int maxc = 1;
+      int maxc = 1, cnt[PG];
 #pragma unroll
       for (int p = 0; p < PG; ++p) {
         const uint32_t w0 = words[p][0];
         full[p] = !inside[p] || ((w0 >> 16) & 1u);
-        maxc = max(maxc, full[p] ? 1 : (int)(w0 & 15u) + 1);
+        cnt[p] = full[p] ? 1 : (int)(w0 & 15u) + 1;
+        maxc = max(maxc, cnt[p]);
         words[p][0] = w0 & 0xfff0fff0u;
+      }
+      if constexpr (LMAX > 8) {
+        // entries 8..15 for the lanes whose list is longer than 8 (rare);
+        // the others repeat their entry 7, which cannot win a strict "<" again
+        bool longer[PG];
+        bool any_longer = false;
+#pragma unroll
+        for (int p = 0; p < PG; ++p) {
+          longer[p] = cnt[p] > 8;
+          any_longer |= longer[p];
+        }
+        if (__any(any_longer)) {
+#pragma unroll
+          for (int p = 0; p < PG; ++p) {
+            const uint32_t rep = (words[p][3] >> 16) * 0x10001u;
+            uint4 t = make_uint4(rep, rep, rep, rep);
+            if (longer[p]) t = recp[p][1];
+            words[p][4] = t.x; words[p][5] = t.y; words[p][6] = t.z; words[p][7] = t.w;
+          }
+        }
       }
       // ---- list slots, two per word
       float best[PG];
@@ -357,18 +386,17 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
         if (w > 0 && !__any(2 * w < maxc)) continue;     // wave-uniform; later words are skipped too
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          uint32_t off[PG];
-          float3 e[PG];
+          uint32_t off[PG];                    // 8 c: the entry's 16 c halved
+          float2 e[PG];
 #pragma unroll
           for (int p = 0; p < PG; ++p) {
-            off[p] = h ? (words[p][w] >> 16) : (words[p][w] & 0xffffu);
-            const float4 t = *reinterpret_cast<const float4*>(cbytes + off[p]);
-            e[p] = make_float3(t.x, t.y, t.z);
+            off[p] = h ? (words[p][w] >> 17) : ((words[p][w] & 0xffffu) >> 1);
+            e[p] = *reinterpret_cast<const float2*>(__builtin_assume_aligned(cbytes + off[p], 8));
           }
           __builtin_amdgcn_sched_barrier(0);   // keep the group's LDS reads in flight together
 #pragma unroll
           for (int p = 0; p < PG; ++p) {
-            const float sc = __builtin_fmaf(zy[g + p], e[p].y, __builtin_fmaf(zx[g + p], e[p].x, e[p].z));
+            const float sc = score2(zx[g + p], zy[g + p], e[p]);
             if (sc < best[p]) { best[p] = sc; boff[p] = off[p]; }
           }
         }
@@ -380,13 +408,12 @@ __global__ __launch_bounds__(kEncThreads) __attribute__((amdgpu_waves_per_eu(4))
           float fb = INFINITY;
           uint32_t fo = 0;
           for (int cc = 0; cc < K; ++cc) {
-            const float4 e = cb4[cc];                // same address in every lane: broadcast
-            const float sc = __builtin_fmaf(zy[g + p], e.y, __builtin_fmaf(zx[g + p], e.x, e.z));
-            if (sc < fb) { fb = sc; fo = (uint32_t)cc * 16u; }
+            const float sc = score2(zx[g + p], zy[g + p], cb2[cc]);   // same address in every lane: broadcast
+            if (sc < fb) { fb = sc; fo = (uint32_t)cc * 8u; }
           }
           if (full[p]) boff[p] = fo;
         }
-        stage[co_local * kPairsPerLane + g + p] = (uint16_t)(boff[p] >> 4);
+        stage[co_local * kPairsPerLane + g + p] = (uint16_t)(boff[p] >> 3);
       }
     }
     wave_lds_fence();
