@@ -467,9 +467,11 @@ def test_full_size_sampled(q, name):
     say(f"  sigma max rel err {err:.3e}")
     assert err <= 1e-5
     rng = np.random.default_rng(zlib.crc32(name.encode()))
-    rows = np.sort(np.concatenate([[0, wl.N - 1], rng.choice(wl.N, 10, replace=False)]))
+    # the headline matrix gets a larger sample (48 rows) than the other shapes (12)
+    extra = 46 if name == "c3t_4096x11008" else 10
+    rows = np.sort(np.concatenate([[0, wl.N - 1], rng.choice(np.arange(1, wl.N - 1), extra, replace=False)]))
     check_encode_rows(wl, C, g, rows, "C")
-    check_encode_rows(wl, C, g, rows[:4], "I", s_o, sig_o)
+    check_encode_rows(wl, C, g, rows, "I", s_o, sig_o)
     say(f"case {name}: GPU decode")
     check_decode_rows(q, wl, C, g, rows)
     if name.startswith("c3"):
