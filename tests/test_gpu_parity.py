@@ -451,7 +451,7 @@ def test_repeatable_bitwise(q):
 # ---------------------------------------------------------------- full-size workloads
 FULL = ["c2_4096x4096", "c3_11008x4096", "c3t_4096x11008"] + \
     [f"c4_5120x13824_K{K}_a{a}" for K in (256, 1024, 2048, 4096) for a in ("0", "0.5")] + \
-    ["c5_l0_q", "c5_l17_down", "c5_l31_gate"]
+    ["c5_l0_q", "c5_l5_k", "c5_l9_v", "c5_l13_o", "c5_l31_gate", "c5_l22_up", "c5_l17_down"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -472,6 +472,13 @@ def test_full_size_sampled(q, name):
     rows = np.sort(np.concatenate([[0, wl.N - 1], rng.choice(np.arange(1, wl.N - 1), extra, replace=False)]))
     check_encode_rows(wl, C, g, rows, "C")
     check_encode_rows(wl, C, g, rows, "I", s_o, sig_o)
+    # the stored fp16 row norm of every row, against the oracle's rho with the
+    # GPU's s (the products formed in fp64: fp32 products would round them)
+    rho_all = O.row_split(wl.W_f32().astype(np.float64) * s_g.astype(np.float64)[None, :])[0]
+    rn_all = g["rn"].cpu().numpy().view(np.uint16)
+    ok_rn = f16_boundary_ok(rn_all, O.to_f16_bits(rho_all), rho_all)
+    say(f"  row norms: {int((~ok_rn).sum())} of {wl.N} rows differ")
+    assert ok_rn.all()
     say(f"case {name}: GPU decode")
     check_decode_rows(q, wl, C, g, rows)
     if name.startswith("c3"):
