@@ -708,6 +708,33 @@ def test_plan_overflow_and_outside_grid(q):
     assert O.accept_index(zt, C, enc["idx"].reshape(-1), idx.reshape(-1)).all()
 
 
+@pytest.mark.parametrize("K_plan,K_use", [(2048, 1024), (4096, 2048), (4096, 3000)])
+def test_plan_built_for_another_k(q, K_plan, K_use):
+    """A plan built for another codebook size (its buffer at least as large as
+    qamw_plan_bytes of the K in use, so the host accepts it) is detected on
+    the device: every pair then scans the whole codebook, and the words equal
+    the exhaustive search's bit for bit.  A plan buffer smaller than
+    qamw_plan_bytes(K) is refused before any launch."""
+    assert q.qamw_plan_bytes(K_plan) >= q.qamw_plan_bytes(K_use)
+    rng = np.random.default_rng(K_plan + K_use)
+    N, d, b = 48, 2048, 128
+    W = (rng.standard_normal((N, d)) * 0.02).astype(np.float32)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    s, sigma = q.qamw_calibrate(dev(W), dev(rng.lognormal(0.0, 1.0, d).astype(np.float32)), 0.5, b, 9)
+    C_plan, C_use = dev(codebook_for(q, K_plan)), dev(codebook_for(q, K_use))
+    plan = q.qamw_build_plan(C_plan)
+    say(f"case plan built for K={K_plan} used with K={K_use}")
+    ref, rn_ref = q.qamw_encode(dev(W), s, sigma, b, 9, C_use)
+    got, rn = q.qamw_encode(dev(W), s, sigma, b, 9, C_use, plan=plan)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref) and torch.equal(rn, rn_ref)
+    # the other way round the buffer is too small: refused on the host
+    small = q.qamw_build_plan(C_use)
+    if q.qamw_plan_bytes(K_use) < q.qamw_plan_bytes(K_plan):
+        with pytest.raises(ValueError):
+            q.qamw_encode(dev(W), s, sigma, b, 9, C_plan, plan=small)
+
+
 def test_encode_phases_match_encode(q):
     """qamw_encode_prepare + qamw_encode_indices give qamw_encode's outputs,
     with and without a plan, and the workspace is reusable across codebooks."""
