@@ -85,6 +85,11 @@ def test_host_helpers(lib):
     assert lib.qamw_encode_workspace_bytes(0, 16) == 0
     # rho (fp64) + column factors (fp32), each 256-byte padded, + ceil(N / 16) tiles x d/2 fp32
     assert lib.qamw_calibrate_workspace_bytes(4096, 11008, 256) == 4096 * 8 + 11008 * 4 + 256 * 5504 * 4
+    # rows of 5 to 16 windows: tiles of ceil(N / 256) rows (a multiple of 4, at least 16)
+    assert lib.qamw_calibrate_workspace_bytes(5120, 13824, 128) == 5120 * 8 + 13824 * 4 + 256 * 6912 * 4
+    assert lib.qamw_calibrate_workspace_bytes(5000, 8192, 128) == 40192 + 8192 * 4 + 250 * 4096 * 4   # rho padded to 256 B
+    # up to 4 windows, or more than 16: 16-row tiles
+    assert lib.qamw_calibrate_workspace_bytes(11008, 4096, 128) == 11008 * 8 + 4096 * 4 + 688 * 2048 * 4
     assert lib.qamw_calibrate_workspace_bytes(0, 16, 16) == 0
     assert lib.qamw_status_string(-4) == b"workspace missing or too small"
     # K > 2048: header block + one uint16 record of 16 entries per cell of the

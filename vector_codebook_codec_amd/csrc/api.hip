@@ -107,7 +107,7 @@ size_t qamw_calibrate_workspace_bytes(int64_t N, int64_t d, int32_t block) {
   (void)block;
   if (N <= 0 || d <= 0 || N > kMaxDim || d > kMaxDim) return 0;
   return round_up((size_t)N * sizeof(double), 256) + round_up((size_t)d * sizeof(float), 256) +
-         calib_tiles(N) * (size_t)(d / 2) * sizeof(float);
+         calib_tiles(N, d) * (size_t)(d / 2) * sizeof(float);
 }
 
 size_t qamw_encode_workspace_bytes(int64_t N, int64_t d) {
@@ -152,7 +152,7 @@ int32_t qamw_calibrate(const void* W, int32_t wdtype, int64_t N, int64_t d, int6
   const int n = (int)N, dd = (int)d;
   if ((rc = launch_scale(chan_rms, alpha, sign_seed, dd, s_out, fcol, st))) return rc;
   if ((rc = launch_norm_amplitude(L, W, wdtype, n, dd, ldw, s_out, fcol, rho, nullptr, partial, st))) return rc;
-  return launch_sigma(partial, (int)calib_tiles(N), dd / 2, n, sigma_out, nullptr, st);
+  return launch_sigma(partial, (int)calib_tiles(N, d), dd / 2, n, sigma_out, nullptr, st);
 }
 
 size_t qamw_plan_bytes(int32_t K) {
@@ -317,7 +317,7 @@ int32_t qamw_encode_noalloc(const void* W, int32_t wdtype, int64_t N, int64_t d,
 size_t qamw_calibrate_encode_workspace_bytes(int64_t N, int64_t d) {
   const size_t e = qamw_encode_workspace_bytes(N, d);
   if (!e) return 0;
-  return e + calib_tiles(N) * (size_t)(d / 2) * sizeof(float);
+  return e + calib_tiles(N, d) * (size_t)(d / 2) * sizeof(float);
 }
 
 int32_t qamw_calibrate_prepare(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,
@@ -345,7 +345,7 @@ int32_t qamw_calibrate_prepare(const void* W, int32_t wdtype, int64_t N, int64_t
   // (norm_amplitude_kernel) and 1 / sigma (sigma_kernel)
   if ((rc = launch_scale(chan_rms, alpha, sign_seed, dd, s_out, e.f, st))) return rc;
   if ((rc = launch_norm_amplitude(L, W, wdtype, n, dd, ldw, s_out, e.f, e.rho, rownorm_f16, partial, st))) return rc;
-  return launch_sigma(partial, (int)calib_tiles(N), dd / 2, n, sigma_out, e.isig, st);
+  return launch_sigma(partial, (int)calib_tiles(N, d), dd / 2, n, sigma_out, e.isig, st);
 }
 
 int32_t qamw_calibrate_encode(const void* W, int32_t wdtype, int64_t N, int64_t d, int64_t ldw,

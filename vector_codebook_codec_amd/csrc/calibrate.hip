@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kBlockThreads) void amplitude_kernel(
 
 // ---------------------------------------------------------------------------
 // Passes 1 and 2 with one read of W (rows of up to kFuseMaxWin windows).  A
-// workgroup owns a tile of kCalibRowsPerTile rows across the whole width,
+// workgroup owns a tile of rows_per_tile rows across the whole width,
 // wavefront w = window w.  For each row every wavefront forms its window's
 // share of rho_n^2 (chunk_sumsq + window_sum, as row_norm_wave does) and the
 // pair amplitudes; the shares meet in LDS, every wavefront adds them in window
@@ -124,7 +124,7 @@ constexpr int kFuseMidWin = 12;   // up to 768 threads: registers for more rows 
 template <int L, typename Tin, int kMaxWin>
 __global__ __launch_bounds__(kMaxWin * kWave) void norm_amplitude_kernel(
     const Tin* __restrict__ W, int64_t ldw, int N, int d, const float* __restrict__ fcol,
-    double* __restrict__ rho, uint16_t* __restrict__ rho_f16, float* __restrict__ partial) {
+    double* __restrict__ rho, uint16_t* __restrict__ rho_f16, float* __restrict__ partial, int rows_per_tile) {
   // rows per barrier (and loads in flight); blocks below 32 or above 256
   // columns need more registers for their lane stages, and take two
   constexpr bool kWide = sizeof(Tin) == 2 && kMaxWin <= kFuseMidWin && L >= 5 && L <= 8;
@@ -151,8 +151,8 @@ __global__ __launch_bounds__(kMaxWin * kWave) void norm_amplitude_kernel(
 #pragma unroll
   for (int p = 0; p < 8; ++p) acc[p] = 0.0f;
 
-  const int n0 = tile * kCalibRowsPerTile;
-  const int n1 = min(N, n0 + kCalibRowsPerTile);
+  const int n0 = tile * rows_per_tile;
+  const int n1 = min(N, n0 + rows_per_tile);
   RawChunk<Tin> ring[kBatch];   // the batch's rows; each slot reloads the row kBatch ahead
   const Tin* base = W + c * kChunk;
 #pragma unroll
@@ -281,7 +281,7 @@ struct LaunchAmplitude {
   static int run(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, const double* rho,
                  float* partial, hipStream_t st) {
     const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
-    const int64_t waves = (int64_t)nwin * (int64_t)calib_tiles(N);
+    const int64_t waves = (int64_t)nwin * (int64_t)calib_tiles(N, d);
     if (wdt == QAMW_F32)
       hipLaunchKernelGGL((amplitude_kernel<L, float>), dim3(grid_for_waves(waves)), dim3(kBlockThreads), 0, st,
                          (const float*)W, ldw, N, d, f, rho, partial);
@@ -303,12 +303,12 @@ struct LaunchNormAmplitude {
   static void go(dim3 grid, dim3 blk, const void* W, int64_t ldw, int N, int d, const float* f, double* rho,
                  uint16_t* rho_f16, float* partial, hipStream_t st) {
     hipLaunchKernelGGL((norm_amplitude_kernel<L, Tin, kMaxWin>), grid, blk, 0, st, (const Tin*)W, ldw, N, d, f, rho,
-                       rho_f16, partial);
+                       rho_f16, partial, calib_rows_per_tile(N, d));
   }
   static int run(const void* W, int32_t wdt, int N, int d, int64_t ldw, const float* f, double* rho,
                  uint16_t* rho_f16, float* partial, hipStream_t st) {
     const int nwin = (d / 16 + kWinChunks - 1) / kWinChunks;
-    const dim3 grid((unsigned)calib_tiles(N)), blk((unsigned)(nwin * kWave));
+    const dim3 grid((unsigned)calib_tiles(N, d)), blk((unsigned)(nwin * kWave));
     const bool mid = nwin <= kFuseMidWin;
     if (wdt == QAMW_F32) {
       if (mid) go<float, kFuseMidWin>(grid, blk, W, ldw, N, d, f, rho, rho_f16, partial, st);

@@ -27,7 +27,24 @@ int check_launch(const char* what);
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 __host__ __device__ inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int elem_size(int32_t dt) { return dt == QAMW_F32 ? 4 : (dt == QAMW_BF16 || dt == QAMW_F16) ? 2 : 0; }
-inline size_t calib_tiles(int64_t N) { return (size_t)((N + kCalibRowsPerTile - 1) / kCalibRowsPerTile); }
+// Rows per calibration tile (one amplitude partial sum each).  Rows of 5 to
+// 16 windows of 1024 columns are calibrated by one workgroup per CU (one
+// wavefront per window), so more than kCalibTileTarget tiles would run in a
+// second, mostly idle round of workgroups: there a tile grows to
+// ceil(N / kCalibTileTarget) rows, a multiple of 4.  Every entry point takes
+// its tiles from this one rule, so the fp32 partial sums, and sigma, agree
+// bit for bit between them.
+constexpr int64_t kCalibTileTarget = 256;
+inline int calib_rows_per_tile(int64_t N, int64_t d) {
+  const int64_t nwin = (d / 16 + 63) / 64;
+  if (nwin <= 4 || nwin > 16) return kCalibRowsPerTile;
+  const int64_t t = (N + kCalibTileTarget - 1) / kCalibTileTarget;
+  return t <= kCalibRowsPerTile ? kCalibRowsPerTile : (int)((t + 3) / 4 * 4);
+}
+inline size_t calib_tiles(int64_t N, int64_t d) {
+  const int64_t r = calib_rows_per_tile(N, d);
+  return (size_t)((N + r - 1) / r);
+}
 inline unsigned grid_for_waves(int64_t waves) { return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock); }
 
 // Call Launch<L>::run(args...) for the Hadamard block size 2^L, 2 <= b <= 1024.
